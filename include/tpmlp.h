@@ -1,0 +1,199 @@
+/*
+ * tpmlp.h -- C ABI of the tensor-parallel MLP shard library for AMD MI355X
+ * (gfx950).  Every entry point enqueues HIP kernels on the caller's stream and
+ * returns; nothing here allocates, keeps a pointer after returning, or holds
+ * global mutable state.  The library is thread-safe.
+ *
+ * Sources (page title, section):
+ *   [TUT]   "024｜Megatron-LM：按矩阵结构切分 Transformer，减少模型并行通信",
+ *           §二 "前向少通信，反向为何仍要一次归约？" -- the shard forward
+ *           Z_i = X·A_i, Y_i = φ(Z_i), O = Σ_i Y_i·B_i and the shard backward
+ *           D_i = (G·B_iᵀ)⊙φ'(Z_i), ∂ℓ/∂A_i = Xᵀ·D_i, ∂ℓ/∂B_i = Y_iᵀ·G,
+ *           ∂ℓ/∂X = Σ_i D_i·A_iᵀ.
+ *   [SENSE] SenseParrots 模型并行 (xujun.org), §2.1 Eq.(1)/(2): column split
+ *           of the first weight, row split of the second; splits are even.
+ *   [SP]    "Megatron-SP 机制", sections on the f/g operator table, the layer
+ *           placement diagram and the RNG-domain table: LayerNorm, dropout and
+ *           residual run on the rank's s/t rows; AllGather before fc1,
+ *           ReduceScatter after fc2.
+ *   [TRAIN] "Megatron 训练" (lovelonelytime), LayerNorm and Dropout sections.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers to row-major, contiguous tensors.  Shapes
+ *     are given in elements.  A tensor of dtype bf16 is IEEE bfloat16; f32 is
+ *     IEEE binary32.
+ *   - Shards: t_local shards are resident together and processed by the same
+ *     launch; per-shard tensors are stacked along a leading shard axis.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Validation happens before any launch.  A negative status means nothing
+ *     was enqueued, except TPMLP_ERR_HIP, which reports a failed launch
+ *     (earlier kernels of the same call may have been enqueued).
+ *   - The caller owns every buffer and keeps it alive until the stream work
+ *     completes.  Inputs and outputs must not overlap.
+ *   - bf16 operands need 16-byte aligned base pointers and row lengths that
+ *     are multiples of 8 elements (d % 8 == 0, m_i % 8 == 0); f32 operands
+ *     need 4-byte alignment only.  Each per-shard operand must be smaller
+ *     than 2^31 bytes.
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPMLP_ABI_VERSION 1
+
+typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
+
+enum {
+  TPMLP_OK = 0,
+  TPMLP_ERR_NULLPTR = -1,   /* a required pointer is NULL                        */
+  TPMLP_ERR_SHAPE = -2,     /* negative/zero size, shard split not even, t < 2 for SP */
+  TPMLP_ERR_DTYPE = -3,     /* unknown dtype or unsupported dtype combination    */
+  TPMLP_ERR_ALIGN = -4,     /* bf16 base pointer not 16-B aligned or row length % 8 */
+  TPMLP_ERR_HIP = -5,       /* a kernel launch failed (tpmlp_last_hip_error)     */
+  TPMLP_ERR_WORKSPACE = -6, /* workspace missing or smaller than required        */
+  TPMLP_ERR_ARG = -7        /* other invalid argument (phase, probability, eps)  */
+};
+
+/*
+ * tpmlp_fwd -- forward of t_local MLP shards ([TUT] §二; [SENSE] Eq.(1)/(2)).
+ *
+ *   Z_i = X·A_i          [n, m_i]   (stored: the backward needs it)
+ *   Y_i = GeLU(Z_i)      [n, m_i]   exact erf GeLU, evaluated on the fp32
+ *                                   accumulator before Z_i is rounded
+ *   P_i = Y_i·B_i        [n, d]     row-parallel partial output; O = Σ_i P_i
+ *                                   is formed by tpmlp_reduce_partials
+ *
+ *   dt      TPMLP_BF16 (fp32 accumulation) or TPMLP_F32 (fp32 throughout)
+ *   n       tokens (b·s), n >= 0; n == 0 enqueues nothing
+ *   d       model width, d >= 1
+ *   m_i     hidden columns per shard (m / t), m_i >= 1
+ *   t_local shards processed by this call, >= 1
+ *   X [n, d]; A [t_local, d, m_i] (shard i = column block i of the full
+ *   first weight); B [t_local, m_i, d] (shard i = row block i of the full
+ *   second weight); Z, Y [t_local, n, m_i]; P [t_local, n, d]; all of dt.
+ */
+int tpmlp_fwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+              const void* X, const void* A, const void* B, void* Z, void* Y, void* P);
+
+/*
+ * tpmlp_bwd -- backward of t_local MLP shards ([TUT] §二).
+ *
+ *   D_i   = (G·B_iᵀ) ⊙ GeLU'(Z_i)   [n, m_i]  dt; GeLU' is evaluated on the
+ *                                            stored Z_i
+ *   dA_i  = Xᵀ·D_i                  [d, m_i]  fp32
+ *   dB_i  = Y_iᵀ·G                  [m_i, d]  fp32
+ *   dX_i  = D_i·A_iᵀ                [n, d]    dt, partial input gradient;
+ *                                            dX = Σ_i dX_i is formed by
+ *                                            tpmlp_reduce_partials
+ *
+ *   Inputs X, A, B as for tpmlp_fwd; Z, Y from tpmlp_fwd; G [n, d] the
+ *   upstream gradient ∂ℓ/∂O.  With n == 0, dA and dB are set to zero.
+ *   ws / ws_bytes: workspace, at least tpmlp_bwd_workspace_bytes(...) bytes
+ *   (may be NULL when that is 0).
+ */
+size_t tpmlp_bwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local);
+int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+              const void* X, const void* A, const void* B, const void* Z, const void* Y,
+              const void* G, void* D, float* dA, float* dB, void* dXp, void* ws, size_t ws_bytes);
+
+/*
+ * tpmlp_reduce_partials -- out = Σ_{i=0}^{t-1} partials[i]  (the one-GPU
+ * stand-in for the all-reduce after the row-parallel GEMM and for the
+ * all-reduce of the column-parallel input gradient: [TRAIN] RowParallelLinear
+ * forward / ColumnParallelLinear backward; a sum, never a mean, [TUT] §三).
+ * Accumulation is fp32 in the fixed order i = 0, 1, ..., t-1, so results are
+ * bit-reproducible.
+ *
+ *   in_dt, out_dt  TPMLP_BF16 or TPMLP_F32 each
+ *   partials [t, rows, cols] of in_dt; out [rows, cols] of out_dt
+ *   t >= 1, rows >= 0, cols >= 1
+ */
+int tpmlp_reduce_partials(hipStream_t stream, int in_dt, int out_dt, int32_t t, int64_t rows,
+                          int64_t cols, const void* partials, void* out);
+
+/*
+ * tpmlp_ln_sp -- the sequence-parallel region around one MLP block
+ * ([SP] placement diagram; [TRAIN] LayerNorm and Dropout sections):
+ *     out = x + dropout_p( Σ_i P_i ),   the MLP input being LN(x)
+ * The t sequence shards of s/t rows each are all resident (s rows in total);
+ * the AllGather before fc1 is the row-block layout of ln_out itself, and the
+ * ReduceScatter after fc2 is a sum over the t partials whose row blocks are
+ * the shards.  The dropout keep-mask is regenerated, never stored: element
+ * (r, c) with global index e = (row0 + r)·h + c is dropped iff word (e mod 4)
+ * of Philox-4x32-10(counter = (e div 4) as two 32-bit words + two zero words,
+ * key = seed as two 32-bit words) is below floor(p·2^32); survivors are scaled
+ * by 1/(1-p).  Every sequence shard therefore draws its own mask.
+ *
+ * Phases (a->phase):
+ *   TPMLP_SP_LN_FWD      x, gamma, beta -> ln_out [s,h] (dt), mean, rstd [s] (f32)
+ *   TPMLP_SP_DROPRES_FWD partials [t,s,h] (the MLP's P_i), x -> out [s,h]
+ *   TPMLP_SP_DROPRES_BWD g_out [s,h] -> dS [s,h] = g_out⊙mask/(1-p)
+ *                        (the MLP's upstream gradient G)
+ *   TPMLP_SP_LN_BWD      dU_partials [t,s,h] (the MLP's dX_i), g_out, x,
+ *                        gamma, mean, rstd -> dx = g_out + LN'(Σ_i dU_i) [s,h],
+ *                        dgamma, dbeta [h] (f32, summed over all s rows in a
+ *                        fixed order; needs ws)
+ * LayerNorm: biased variance over h, eps inside the square root, statistics
+ * in fp32.  Requirements: t >= 2 (sequence parallelism needs tensor
+ * parallelism, [SP] 工程约束), s % t == 0, 0 <= p < 1, eps > 0, bf16 needs
+ * h % 8 == 0.
+ */
+typedef enum {
+  TPMLP_SP_LN_FWD = 0,
+  TPMLP_SP_DROPRES_FWD = 1,
+  TPMLP_SP_DROPRES_BWD = 2,
+  TPMLP_SP_LN_BWD = 3
+} tpmlp_sp_phase;
+
+typedef struct {
+  int32_t phase;            /* tpmlp_sp_phase                                   */
+  int32_t dt;               /* dtype of x, gamma, beta, ln_out, partials, out,
+                               g_out, dS, dU_partials, dx                       */
+  int32_t t;                /* SP degree = TP degree = number of partials       */
+  int32_t reserved;
+  int64_t s;                /* rows on this GPU (all t shards)                  */
+  int64_t h;                /* hidden width                                     */
+  int64_t row0;             /* global index of row 0 (mask counter offset)      */
+  float eps;
+  float p_drop;
+  uint64_t seed;
+  const void* x;
+  const void* gamma;
+  const void* beta;
+  void* ln_out;
+  float* mean;
+  float* rstd;
+  const void* partials;
+  void* out;
+  const void* g_out;
+  void* dS;
+  const void* dU_partials;
+  void* dx;
+  float* dgamma;
+  float* dbeta;
+  void* ws;
+  size_t ws_bytes;
+} tpmlp_sp_args;
+
+size_t tpmlp_sp_workspace_bytes(int64_t s, int64_t h);
+int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a);
+
+/* Status text for a return code; never NULL. */
+const char* tpmlp_status_string(int status);
+/* The hipError_t of the most recent TPMLP_ERR_HIP on the calling thread. */
+int tpmlp_last_hip_error(void);
+int tpmlp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPMLP_H */

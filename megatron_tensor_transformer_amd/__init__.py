@@ -1,0 +1,225 @@
+"""Python binding of libtpmlp.so, the MI355X (gfx950) tensor-parallel MLP shard
+library.  Argument marshalling only: every step runs in the library's HIP
+kernels; torch supplies device memory and the current stream.
+
+The functions named tpmlp_* mirror the C entry points of include/tpmlp.h one to
+one; mlp_fwd / mlp_bwd / reduce_partials / sp_* allocate their outputs with
+torch and then call them.  A missing library or a non-zero status raises; there
+is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtpmlp.so")
+
+F32, BF16 = 0, 1
+SP_LN_FWD, SP_DROPRES_FWD, SP_DROPRES_BWD, SP_LN_BWD = 0, 1, 2, 3
+
+ERR_NULLPTR, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_HIP, ERR_WORKSPACE, ERR_ARG = -1, -2, -3, -4, -5, -6, -7
+
+
+class TpmlpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"tpmlp status {status}: {msg}")
+        self.status = status
+
+
+class TpmlpValueError(ValueError):
+    def __init__(self, status, msg):
+        super().__init__(f"tpmlp status {status}: {msg}")
+        self.status = status
+
+
+class SpArgs(ctypes.Structure):
+    """Mirror of tpmlp_sp_args."""
+    _fields_ = [
+        ("phase", ctypes.c_int32), ("dt", ctypes.c_int32), ("t", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("s", ctypes.c_int64), ("h", ctypes.c_int64),
+        ("row0", ctypes.c_int64), ("eps", ctypes.c_float), ("p_drop", ctypes.c_float),
+        ("seed", ctypes.c_uint64), ("x", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("ln_out", ctypes.c_void_p), ("mean", ctypes.c_void_p),
+        ("rstd", ctypes.c_void_p), ("partials", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("g_out", ctypes.c_void_p), ("dS", ctypes.c_void_p), ("dU_partials", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p), ("dgamma", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+# exported C symbols and their ctypes signatures
+_P, _I, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "tpmlp_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "tpmlp_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I32]),
+    "tpmlp_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
+    "tpmlp_reduce_partials": (_I, [_P, _I, _I, _I32, _I64, _I64, _P, _P]),
+    "tpmlp_sp_workspace_bytes": (_SZ, [_I64, _I64]),
+    "tpmlp_ln_sp": (_I, [_P, ctypes.POINTER(SpArgs)]),
+    "tpmlp_status_string": (ctypes.c_char_p, [_I]),
+    "tpmlp_last_hip_error": (_I, []),
+    "tpmlp_abi_version": (_I, []),
+}
+
+
+def lib():
+    """Load libtpmlp.so (built by megatron_tensor_transformer_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m megatron_tensor_transformer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status == 0:
+        return
+    msg = lib().tpmlp_status_string(status).decode()
+    if status == ERR_HIP:
+        raise TpmlpError(status, f"{msg} (hipError {lib().tpmlp_last_hip_error()})")
+    raise TpmlpValueError(status, msg)
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TpmlpValueError(ERR_DTYPE, f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TpmlpValueError(ERR_ARG, "tensor is not on a GPU")
+    if not t.is_contiguous():
+        raise TpmlpValueError(ERR_ARG, "tensor is not contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ---------------------------------------------------------------- raw entry points
+def tpmlp_fwd(X, A, B, Z, Y, P, stream=None):
+    """X [n,d]; A [t,d,m_i]; B [t,m_i,d]; Z, Y [t,n,m_i]; P [t,n,d] (all one dtype)."""
+    t, d, mi = A.shape
+    n = X.shape[0]
+    _check(lib().tpmlp_fwd(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B),
+                           _ptr(Z), _ptr(Y), _ptr(P)))
+
+
+def tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, ws=None, stream=None):
+    """Gradients of t_local shards; dA [t,d,m_i] and dB [t,m_i,d] are fp32."""
+    t, d, mi = A.shape
+    n = X.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().tpmlp_bwd(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B), _ptr(Z),
+                           _ptr(Y), _ptr(G), _ptr(D), _ptr(dA), _ptr(dB), _ptr(dXp), _ptr(ws), ws_bytes))
+
+
+def tpmlp_reduce_partials(partials, out, stream=None):
+    """out [rows, cols] = Σ_i partials[i]."""
+    t = partials.shape[0]
+    rows = out.shape[0]
+    cols = out.numel() // rows if rows else (out.shape[1] if out.dim() > 1 else 1)
+    _check(lib().tpmlp_reduce_partials(_stream(stream), _dt(partials), _dt(out), t, rows, cols,
+                                       _ptr(partials), _ptr(out)))
+
+
+def tpmlp_ln_sp(args, stream=None):
+    _check(lib().tpmlp_ln_sp(_stream(stream), ctypes.byref(args)))
+
+
+# ---------------------------------------------------------------- allocating wrappers
+def mlp_fwd(X, A, B, stream=None):
+    t, d, mi = A.shape
+    n = X.shape[0]
+    Z = torch.empty((t, n, mi), dtype=X.dtype, device=X.device)
+    Y = torch.empty_like(Z)
+    P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
+    tpmlp_fwd(X, A, B, Z, Y, P, stream)
+    return Z, Y, P
+
+
+def bwd_workspace_bytes(X, A):
+    t, d, mi = A.shape
+    return lib().tpmlp_bwd_workspace_bytes(_dt(X), X.shape[0], d, mi, t)
+
+
+def mlp_bwd(X, A, B, Z, Y, G, stream=None):
+    t, d, mi = A.shape
+    n = X.shape[0]
+    D = torch.empty((t, n, mi), dtype=X.dtype, device=X.device)
+    dA = torch.empty((t, d, mi), dtype=torch.float32, device=X.device)
+    dB = torch.empty((t, mi, d), dtype=torch.float32, device=X.device)
+    dXp = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
+    nb = bwd_workspace_bytes(X, A)
+    ws = torch.empty(nb, dtype=torch.uint8, device=X.device) if nb else None
+    tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, ws, stream)
+    return D, dA, dB, dXp
+
+
+def reduce_partials(partials, out_dtype=None, stream=None):
+    out = torch.empty(partials.shape[1:], dtype=out_dtype or partials.dtype, device=partials.device)
+    tpmlp_reduce_partials(partials, out, stream)
+    return out
+
+
+def sp_ln_fwd(x, gamma, beta, t, eps=1e-5, stream=None):
+    s, h = x.shape
+    U = torch.empty_like(x)
+    mean = torch.empty(s, dtype=torch.float32, device=x.device)
+    rstd = torch.empty_like(mean)
+    a = SpArgs(phase=SP_LN_FWD, dt=_dt(x), t=t, s=s, h=h, eps=eps, x=_ptr(x), gamma=_ptr(gamma),
+               beta=_ptr(beta), ln_out=_ptr(U), mean=_ptr(mean), rstd=_ptr(rstd))
+    tpmlp_ln_sp(a, stream)
+    return U, mean, rstd
+
+
+def sp_dropres_fwd(partials, x, p, seed, row0=0, stream=None):
+    t = partials.shape[0]
+    s, h = x.shape
+    out = torch.empty_like(x)
+    a = SpArgs(phase=SP_DROPRES_FWD, dt=_dt(x), t=t, s=s, h=h, row0=row0, eps=1.0, p_drop=p, seed=seed,
+               partials=_ptr(partials), x=_ptr(x), out=_ptr(out))
+    tpmlp_ln_sp(a, stream)
+    return out
+
+
+def sp_dropres_bwd(g_out, t, p, seed, row0=0, stream=None):
+    s, h = g_out.shape
+    dS = torch.empty_like(g_out)
+    a = SpArgs(phase=SP_DROPRES_BWD, dt=_dt(g_out), t=t, s=s, h=h, row0=row0, eps=1.0, p_drop=p,
+               seed=seed, g_out=_ptr(g_out), dS=_ptr(dS))
+    tpmlp_ln_sp(a, stream)
+    return dS
+
+
+def sp_ln_bwd(dU_partials, g_out, x, gamma, mean, rstd, stream=None):
+    t = dU_partials.shape[0]
+    s, h = x.shape
+    dx = torch.empty_like(x)
+    dgamma = torch.empty(h, dtype=torch.float32, device=x.device)
+    dbeta = torch.empty_like(dgamma)
+    nb = lib().tpmlp_sp_workspace_bytes(s, h)
+    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=x.device)
+    a = SpArgs(phase=SP_LN_BWD, dt=_dt(x), t=t, s=s, h=h, eps=1.0, dU_partials=_ptr(dU_partials),
+               g_out=_ptr(g_out), x=_ptr(x), gamma=_ptr(gamma), mean=_ptr(mean), rstd=_ptr(rstd),
+               dx=_ptr(dx), dgamma=_ptr(dgamma), dbeta=_ptr(dbeta), ws=_ptr(ws), ws_bytes=nb)
+    tpmlp_ln_sp(a, stream)
+    return dx, dgamma, dbeta

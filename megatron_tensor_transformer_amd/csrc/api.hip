@@ -1,0 +1,325 @@
+// C ABI of the tensor-parallel MLP shard library: argument validation and the
+// mapping of each step onto the kernels.  Validation never touches the GPU, so
+// every error status is returned with nothing enqueued.
+#include <math.h>
+#include <initializer_list>
+#include <stdint.h>
+
+#include "../../include/tpmlp.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxOperandBytes = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+int elem_size(int dt) { return dt == TPMLP_BF16 ? 2 : 4; }
+bool valid_dt(int dt) { return dt == TPMLP_BF16 || dt == TPMLP_F32; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool fits(int64_t rows, int64_t cols, int es) {
+  if (rows < 0 || cols < 0) return false;
+  if (cols != 0 && rows > kMaxOperandBytes / cols) return false;
+  return rows * cols * es <= kMaxOperandBytes;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return TPMLP_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return TPMLP_ERR_HIP;
+}
+
+// Shared checks of tpmlp_fwd / tpmlp_bwd dimensions.
+int check_mlp_dims(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  if (!valid_dt(dt)) return TPMLP_ERR_DTYPE;
+  if (n < 0 || d < 1 || m_i < 1 || t_local < 1) return TPMLP_ERR_SHAPE;
+  if (n > kMaxDim || d > kMaxDim || m_i > kMaxDim) return TPMLP_ERR_SHAPE;
+  const int es = elem_size(dt);
+  if (!fits(n, d, es) || !fits(d, m_i, es) || !fits(n, m_i, es) || !fits(d, m_i, 4))
+    return TPMLP_ERR_SHAPE;
+  if (dt == TPMLP_BF16 && (d % 8 != 0 || m_i % 8 != 0)) return TPMLP_ERR_ALIGN;
+  return TPMLP_OK;
+}
+
+int check_ptrs(int dt, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr) return TPMLP_ERR_NULLPTR;
+  const uintptr_t a = dt == TPMLP_BF16 ? 16 : 4;
+  for (const void* p : ps)
+    if (!aligned(p, a)) return TPMLP_ERR_ALIGN;
+  return TPMLP_OK;
+}
+
+hipError_t gemm(int dt, const tpmlp::GemmProblem& p, int ao, int bo, int epi, hipStream_t s) {
+  return dt == TPMLP_BF16 ? tpmlp::launch_gemm_bf16(p, ao, bo, epi, s)
+                          : tpmlp::launch_gemm_f32(p, ao, bo, epi, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpmlp_abi_version(void) { return TPMLP_ABI_VERSION; }
+
+int tpmlp_last_hip_error(void) { return g_last_hip_error; }
+
+const char* tpmlp_status_string(int status) {
+  switch (status) {
+    case TPMLP_OK: return "ok";
+    case TPMLP_ERR_NULLPTR: return "a required pointer is NULL";
+    case TPMLP_ERR_SHAPE: return "invalid shape (non-positive size, uneven shard split, size limit, or t < 2 for sequence parallelism)";
+    case TPMLP_ERR_DTYPE: return "unsupported dtype";
+    case TPMLP_ERR_ALIGN: return "misaligned pointer or row length (bf16 needs 16-byte bases and rows of a multiple of 8 elements)";
+    case TPMLP_ERR_HIP: return "a HIP kernel launch failed";
+    case TPMLP_ERR_WORKSPACE: return "workspace missing or too small";
+    case TPMLP_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int tpmlp_fwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+              const void* X, const void* A, const void* B, void* Z, void* Y, void* P) {
+  int st = check_mlp_dims(dt, n, d, m_i, t_local);
+  if (st) return st;
+  if (n == 0) return TPMLP_OK;
+  st = check_ptrs(dt, {X, A, B, Z, Y, P});
+  if (st) return st;
+
+  // Z_i = X·A_i and Y_i = GeLU(Z_i): A = X [n,d] (K-major), B = A_i [d,m_i]
+  // (N-major), batched over shards with X shared.
+  tpmlp::GemmProblem g1{};
+  g1.M = static_cast<int>(n);
+  g1.N = static_cast<int>(m_i);
+  g1.K = static_cast<int>(d);
+  g1.batch = t_local;
+  g1.A = X;
+  g1.B = A;
+  g1.C = Z;
+  g1.C2 = Y;
+  g1.lda = d;
+  g1.ldb = m_i;
+  g1.ldc = m_i;
+  g1.sA = 0;
+  g1.sB = d * m_i;
+  g1.sC = n * m_i;
+  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_GELU_ZY, stream));
+  if (st) return st;
+
+  // P_i = Y_i·B_i: A = Y_i [n,m_i] (K-major), B = B_i [m_i,d] (N-major).
+  tpmlp::GemmProblem g2{};
+  g2.M = static_cast<int>(n);
+  g2.N = static_cast<int>(d);
+  g2.K = static_cast<int>(m_i);
+  g2.batch = t_local;
+  g2.A = Y;
+  g2.B = B;
+  g2.C = P;
+  g2.lda = m_i;
+  g2.ldb = d;
+  g2.ldc = d;
+  g2.sA = n * m_i;
+  g2.sB = m_i * d;
+  g2.sC = n * d;
+  return hip_status(gemm(dt, g2, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+}
+
+size_t tpmlp_bwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  (void)dt, (void)n, (void)d, (void)m_i, (void)t_local;
+  return 0;
+}
+
+int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+              const void* X, const void* A, const void* B, const void* Z, const void* Y,
+              const void* G, void* D, float* dA, float* dB, void* dXp, void* ws, size_t ws_bytes) {
+  int st = check_mlp_dims(dt, n, d, m_i, t_local);
+  if (st) return st;
+  if (ws_bytes < tpmlp_bwd_workspace_bytes(dt, n, d, m_i, t_local)) return TPMLP_ERR_WORKSPACE;
+  (void)ws;
+  if (dA == nullptr || dB == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(dA, 4) || !aligned(dB, 4)) return TPMLP_ERR_ALIGN;
+  if (n > 0) {
+    st = check_ptrs(dt, {X, A, B, Z, Y, G, D, dXp});
+    if (st) return st;
+  }
+  const int es = elem_size(dt);
+  (void)es;
+
+  if (n > 0) {
+    // D_i = (G·B_iᵀ) ⊙ GeLU'(Z_i): A = G [n,d] (K-major), B(k,j) = B_i[j][k]
+    // (K-major, ld = d).
+    tpmlp::GemmProblem e{};
+    e.M = static_cast<int>(n);
+    e.N = static_cast<int>(m_i);
+    e.K = static_cast<int>(d);
+    e.batch = t_local;
+    e.A = G;
+    e.B = B;
+    e.C = D;
+    e.Zin = Z;
+    e.lda = d;
+    e.ldb = d;
+    e.ldc = m_i;
+    e.sA = 0;
+    e.sB = m_i * d;
+    e.sC = n * m_i;
+    st = hip_status(gemm(dt, e, tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_GELU_GRAD, stream));
+    if (st) return st;
+  }
+
+  // dB_i = Y_iᵀ·G: M = m_i, N = d, K = n; A(m,k) = Y_i[k][m] (M-major),
+  // B(k,j) = G[k][j] (N-major).  With n == 0 this writes zeros.
+  tpmlp::GemmProblem wb{};
+  wb.M = static_cast<int>(m_i);
+  wb.N = static_cast<int>(d);
+  wb.K = static_cast<int>(n);
+  wb.batch = t_local;
+  wb.A = Y;
+  wb.B = G;
+  wb.C = dB;
+  wb.lda = m_i;
+  wb.ldb = d;
+  wb.ldc = d;
+  wb.sA = n * m_i;
+  wb.sB = 0;
+  wb.sC = m_i * d;
+  st = hip_status(gemm(dt, wb, tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32, stream));
+  if (st) return st;
+
+  // dA_i = Xᵀ·D_i: M = d, N = m_i, K = n; A(m,k) = X[k][m], B(k,j) = D_i[k][j].
+  tpmlp::GemmProblem wa{};
+  wa.M = static_cast<int>(d);
+  wa.N = static_cast<int>(m_i);
+  wa.K = static_cast<int>(n);
+  wa.batch = t_local;
+  wa.A = X;
+  wa.B = D;
+  wa.C = dA;
+  wa.lda = d;
+  wa.ldb = m_i;
+  wa.ldc = m_i;
+  wa.sA = 0;
+  wa.sB = n * m_i;
+  wa.sC = d * m_i;
+  st = hip_status(gemm(dt, wa, tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32, stream));
+  if (st) return st;
+
+  if (n > 0) {
+    // dX_i = D_i·A_iᵀ: M = n, N = d, K = m_i; A = D_i (K-major),
+    // B(k,j) = A_i[j][k] (K-major, ld = m_i).
+    tpmlp::GemmProblem dx{};
+    dx.M = static_cast<int>(n);
+    dx.N = static_cast<int>(d);
+    dx.K = static_cast<int>(m_i);
+    dx.batch = t_local;
+    dx.A = D;
+    dx.B = A;
+    dx.C = dXp;
+    dx.lda = m_i;
+    dx.ldb = m_i;
+    dx.ldc = d;
+    dx.sA = n * m_i;
+    dx.sB = d * m_i;
+    dx.sC = n * d;
+    st = hip_status(gemm(dt, dx, tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE, stream));
+    if (st) return st;
+  }
+  return TPMLP_OK;
+}
+
+int tpmlp_reduce_partials(hipStream_t stream, int in_dt, int out_dt, int32_t t, int64_t rows,
+                          int64_t cols, const void* partials, void* out) {
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return TPMLP_ERR_DTYPE;
+  if (t < 1 || rows < 0 || cols < 1) return TPMLP_ERR_SHAPE;
+  if (rows > 0 && cols > (int64_t{1} << 62) / rows) return TPMLP_ERR_SHAPE;
+  const int64_t count = rows * cols;
+  if (count > (int64_t{1} << 62) / t) return TPMLP_ERR_SHAPE;
+  if (count == 0) return TPMLP_OK;
+  if (partials == nullptr || out == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(partials, elem_size(in_dt)) || !aligned(out, elem_size(out_dt))) return TPMLP_ERR_ALIGN;
+  return hip_status(tpmlp::launch_reduce_partials(in_dt, out_dt, t, count, partials, out, stream));
+}
+
+size_t tpmlp_sp_workspace_bytes(int64_t s, int64_t h) {
+  if (s <= 0 || h <= 0) return 0;
+  return static_cast<size_t>(tpmlp::sp_ln_bwd_row_blocks(s)) * 2 * static_cast<size_t>(h) * sizeof(float);
+}
+
+int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
+  if (a == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!valid_dt(a->dt)) return TPMLP_ERR_DTYPE;
+  if (a->phase < TPMLP_SP_LN_FWD || a->phase > TPMLP_SP_LN_BWD) return TPMLP_ERR_ARG;
+  if (a->t < 2) return TPMLP_ERR_SHAPE;  // sequence parallelism needs TP > 1
+  if (a->s < 0 || a->h < 8 || a->h > 4096 || a->row0 < 0) return TPMLP_ERR_SHAPE;
+  if (a->s % a->t != 0) return TPMLP_ERR_SHAPE;
+  if (a->h % 8 != 0) return TPMLP_ERR_ALIGN;
+  if (!(a->p_drop >= 0.0f && a->p_drop < 1.0f)) return TPMLP_ERR_ARG;
+  if (!(a->eps > 0.0f)) return TPMLP_ERR_ARG;
+  if (a->s == 0) return TPMLP_OK;
+  const int es = elem_size(a->dt);
+  if (!fits(a->s, a->h, es) || !fits(a->s * a->t, a->h, es)) return TPMLP_ERR_SHAPE;
+
+  tpmlp::SpProblem p{};
+  p.phase = a->phase;
+  p.dt = a->dt;
+  p.t = a->t;
+  p.s = a->s;
+  p.h = a->h;
+  p.row0 = a->row0;
+  p.eps = a->eps;
+  p.drop_threshold = static_cast<uint32_t>(floor(static_cast<double>(a->p_drop) * 4294967296.0));
+  p.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(a->p_drop)));
+  p.seed = a->seed;
+  p.x = a->x;
+  p.gamma = a->gamma;
+  p.beta = a->beta;
+  p.ln_out = a->ln_out;
+  p.mean = a->mean;
+  p.rstd = a->rstd;
+  p.partials = a->partials;
+  p.out = a->out;
+  p.g_out = a->g_out;
+  p.dS = a->dS;
+  p.dU_partials = a->dU_partials;
+  p.dx = a->dx;
+  p.dgamma = a->dgamma;
+  p.dbeta = a->dbeta;
+  p.ws = static_cast<float*>(a->ws);
+
+  const uintptr_t al = 16;
+  auto ok = [&](std::initializer_list<const void*> ps) {
+    for (const void* q : ps)
+      if (q == nullptr) return TPMLP_ERR_NULLPTR;
+    for (const void* q : ps)
+      if (!aligned(q, al)) return TPMLP_ERR_ALIGN;
+    return TPMLP_OK;
+  };
+  int st = TPMLP_OK;
+  switch (a->phase) {
+    case TPMLP_SP_LN_FWD:
+      st = ok({a->x, a->gamma, a->beta, a->ln_out});
+      if (!st && (a->mean == nullptr || a->rstd == nullptr)) st = TPMLP_ERR_NULLPTR;
+      break;
+    case TPMLP_SP_DROPRES_FWD:
+      st = ok({a->partials, a->x, a->out});
+      break;
+    case TPMLP_SP_DROPRES_BWD:
+      st = ok({a->g_out, a->dS});
+      break;
+    default:
+      st = ok({a->dU_partials, a->g_out, a->x, a->gamma, a->dx});
+      if (!st && (a->mean == nullptr || a->rstd == nullptr || a->dgamma == nullptr ||
+                  a->dbeta == nullptr))
+        st = TPMLP_ERR_NULLPTR;
+      if (!st && (a->ws == nullptr || a->ws_bytes < tpmlp_sp_workspace_bytes(a->s, a->h)))
+        st = TPMLP_ERR_WORKSPACE;
+      if (!st && !aligned(a->ws, 4)) st = TPMLP_ERR_ALIGN;
+      break;
+  }
+  if (st) return st;
+  return hip_status(tpmlp::launch_sp(p, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+// Operand storage order of a GEMM operand, seen from C = A·B with A (M×K) and
+// B (K×N).
+//   KMAJ : the K index is contiguous.  A: A[m*ld + k]; B: B[n*ld + k].
+//   MNMAJ: the M (or N) index is contiguous.  A: A[k*ld + m]; B: B[k*ld + n].
+enum OperandOrder { KMAJ = 0, MNMAJ = 1 };
+
+// What the GEMM writes.
+enum Epilogue {
+  EPI_STORE = 0,      // C = acc (dtype of the path)
+  EPI_STORE_F32 = 1,  // C = acc as fp32 (weight gradients)
+  EPI_GELU_ZY = 2,    // C = acc (Z), C2 = GeLU(acc) (Y)
+  EPI_GELU_GRAD = 3   // C = acc ⊙ GeLU'(Zin) (D)
+};
+
+struct GemmProblem {
+  int M, N, K;
+  int batch;
+  const void* A;
+  const void* B;
+  void* C;
+  void* C2;          // EPI_GELU_ZY: Y
+  const void* Zin;   // EPI_GELU_GRAD: stored Z, same layout as C
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;  // per-batch strides in elements (0 = shared operand)
+};
+
+// bf16 inputs, fp32 accumulation (MFMA).  Returns a hipError_t.
+hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int epi,
+                            hipStream_t stream);
+// fp32 throughout.
+hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int epi,
+                           hipStream_t stream);
+
+// out = Σ_i partials[i]; dtypes: 0 = f32, 1 = bf16.
+hipError_t launch_reduce_partials(int in_dt, int out_dt, int t, int64_t count,
+                                  const void* partials, void* out, hipStream_t stream);
+
+struct SpProblem {
+  int phase, dt, t;
+  int64_t s, h, row0;
+  float eps;
+  uint32_t drop_threshold;
+  float keep_scale;
+  uint64_t seed;
+  const void* x;
+  const void* gamma;
+  const void* beta;
+  void* ln_out;
+  float* mean;
+  float* rstd;
+  const void* partials;
+  void* out;
+  const void* g_out;
+  void* dS;
+  const void* dU_partials;
+  void* dx;
+  float* dgamma;
+  float* dbeta;
+  float* ws;
+};
+
+int64_t sp_ln_bwd_row_blocks(int64_t s);
+hipError_t launch_sp(const SpProblem& p, hipStream_t stream);
+
+}  // namespace tpmlp

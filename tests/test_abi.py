@@ -1,0 +1,141 @@
+"""The C-ABI library loads, exports every function include/tpmlp.h declares, and
+rejects invalid arguments with the documented status before touching the GPU.
+Runs without a GPU: every call here fails validation, so no kernel is
+launched."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import megatron_tensor_transformer_amd as tp
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "tpmlp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(tpmlp_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return tp.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("tpmlp_fwd", "tpmlp_bwd", "tpmlp_reduce_partials", "tpmlp_ln_sp"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in tp.SIGNATURES, f"binding lacks {name}"
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.tpmlp_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+        assert L.tpmlp_status_string(s)
+
+
+def _fwd(L, dt=1, n=64, d=64, mi=64, t=2, ptr=0x1000):
+    p = ctypes.c_void_p(ptr)
+    return L.tpmlp_fwd(None, dt, n, d, mi, t, p, p, p, p, p, p)
+
+
+def test_fwd_validation(L):
+    assert _fwd(L, dt=7) == tp.ERR_DTYPE
+    assert _fwd(L, n=-1) == tp.ERR_SHAPE
+    assert _fwd(L, d=0) == tp.ERR_SHAPE
+    assert _fwd(L, mi=0) == tp.ERR_SHAPE
+    assert _fwd(L, t=0) == tp.ERR_SHAPE
+    assert _fwd(L, d=12) == tp.ERR_ALIGN          # bf16 rows must be multiples of 8
+    assert _fwd(L, mi=20) == tp.ERR_ALIGN
+    assert _fwd(L, ptr=0x1008) == tp.ERR_ALIGN     # bf16 needs 16-byte bases
+    assert _fwd(L, ptr=0) == tp.ERR_NULLPTR
+    assert _fwd(L, n=1 << 20, d=1 << 12) == tp.ERR_SHAPE  # 2^33 bytes per operand
+    assert _fwd(L, n=0) == 0                        # empty input: nothing to do
+    # fp32 accepts any row length and 4-byte alignment
+    assert _fwd(L, dt=0, d=3, mi=5, ptr=0) == tp.ERR_NULLPTR
+    assert _fwd(L, dt=0, d=3, mi=5, ptr=0x1002) == tp.ERR_ALIGN
+
+
+def test_bwd_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    z = ctypes.c_void_p(0)
+    args = [p] * 10
+    assert L.tpmlp_bwd(None, 3, 64, 64, 64, 2, *args, None, 0) == tp.ERR_DTYPE
+    assert L.tpmlp_bwd(None, 1, 64, 60, 64, 2, *args, None, 0) == tp.ERR_ALIGN
+    # dA missing
+    a = [p] * 10
+    a[7] = z
+    assert L.tpmlp_bwd(None, 1, 64, 64, 64, 2, *a, None, 0) == tp.ERR_NULLPTR
+    a = [p] * 10
+    a[6] = z  # D missing
+    assert L.tpmlp_bwd(None, 1, 64, 64, 64, 2, *a, None, 0) == tp.ERR_NULLPTR
+    assert L.tpmlp_bwd_workspace_bytes(1, 8192, 3072, 1536, 8) == 0
+
+
+def test_reduce_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    assert L.tpmlp_reduce_partials(None, 2, 1, 8, 16, 16, p, p) == tp.ERR_DTYPE
+    assert L.tpmlp_reduce_partials(None, 1, 1, 0, 16, 16, p, p) == tp.ERR_SHAPE
+    assert L.tpmlp_reduce_partials(None, 1, 1, 8, -1, 16, p, p) == tp.ERR_SHAPE
+    assert L.tpmlp_reduce_partials(None, 1, 1, 8, 16, 0, p, p) == tp.ERR_SHAPE
+    assert L.tpmlp_reduce_partials(None, 1, 1, 8, 16, 16, None, p) == tp.ERR_NULLPTR
+    assert L.tpmlp_reduce_partials(None, 0, 0, 8, 16, 16, ctypes.c_void_p(0x1001), p) == tp.ERR_ALIGN
+    assert L.tpmlp_reduce_partials(None, 1, 1, 8, 0, 16, None, None) == 0
+
+
+def _sp(**kw):
+    base = dict(phase=tp.SP_LN_FWD, dt=1, t=8, s=64, h=64, eps=1e-5, p_drop=0.1, seed=0,
+                x=0x1000, gamma=0x1000, beta=0x1000, ln_out=0x1000, mean=0x1000, rstd=0x1000)
+    base.update(kw)
+    return tp.SpArgs(**base)
+
+
+def test_sp_validation(L):
+    call = lambda a: L.tpmlp_ln_sp(None, ctypes.byref(a))
+    assert L.tpmlp_ln_sp(None, None) == tp.ERR_NULLPTR
+    assert call(_sp(t=1)) == tp.ERR_SHAPE          # SP requires TP > 1
+    assert call(_sp(s=60)) == tp.ERR_SHAPE         # s % t
+    assert call(_sp(h=8200)) == tp.ERR_SHAPE       # h limit
+    assert call(_sp(h=36)) == tp.ERR_ALIGN
+    assert call(_sp(phase=9)) == tp.ERR_ARG
+    assert call(_sp(p_drop=1.0)) == tp.ERR_ARG
+    assert call(_sp(p_drop=-0.1)) == tp.ERR_ARG
+    assert call(_sp(eps=0.0)) == tp.ERR_ARG
+    assert call(_sp(dt=5)) == tp.ERR_DTYPE
+    assert call(_sp(ln_out=0)) == tp.ERR_NULLPTR
+    assert call(_sp(x=0x1004)) == tp.ERR_ALIGN
+    assert call(_sp(s=0)) == 0
+    assert call(_sp(phase=tp.SP_LN_BWD, dU_partials=0x1000, g_out=0x1000, dx=0x1000,
+                    dgamma=0x1000, dbeta=0x1000, ws=0x1000, ws_bytes=16)) == tp.ERR_WORKSPACE
+    assert L.tpmlp_sp_workspace_bytes(4096, 4096) == (4096 // 32) * 2 * 4096 * 4
+
+
+def test_sp_args_layout_matches_header(tmp_path):
+    """The ctypes mirror of tpmlp_sp_args has the C compiler's size and offsets."""
+    fields = [f for f, _ in tp.SpArgs._fields_]
+    prog = tmp_path / "layout.c"
+    prog.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "tpmlp.h"\nint main(void){\n'
+        '  printf("%zu\\n", sizeof(tpmlp_sp_args));\n'
+        + "".join(f'  printf("%zu\\n", offsetof(tpmlp_sp_args, {f}));\n' for f in fields)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(prog), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(tp.SpArgs)
+    for f, off in zip(fields, out[1:]):
+        assert getattr(tp.SpArgs, f).offset == off, f

@@ -1,0 +1,192 @@
+"""GPU parity of the MLP shard (tpmlp_fwd, tpmlp_bwd, tpmlp_reduce_partials)
+against the fp64 oracle on the same seeded inputs, through the C ABI.
+
+Bars (relative Frobenius error, fp64): fp32 path 1e-5, bf16 path 8e-3, for
+every output and gradient (O, dX, each dA_i, each dB_i) and for the stored
+intermediates (Z_i, Y_i, P_i, D_i, dX_i).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import megatron_tensor_transformer_amd as tp
+from oracle import mlp as om
+from tpmlp_inputs import config_inputs, mlp_inputs
+
+from gpu_util import dev, f64, relerr, run_step, say, shard_cols, shard_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 8e-3}
+
+
+def compare_full(inp, t, dtype, extra=""):
+    X, A, B, G = (dev(inp[k]) for k in "XABG")
+    A_s, B_s = shard_cols(A, t), shard_rows(B, t)
+    say(f"[gpu] step {dtype} n={X.shape[0]} d={X.shape[1]} m={A.shape[1]} t={t} {extra}")
+    r = run_step(X, A_s, B_s, G)
+    Xo, Ao, Bo, Go = (inp[k].f64 for k in "XABG")
+    fwd = om.tp_forward(Xo, Ao, Bo, t)
+    bwd = om.tp_backward(Xo, Ao, Bo, fwd, Go)
+    tol = TOL[dtype]
+    errs = {"O": relerr(r["O"], fwd["O"]), "dX": relerr(r["dX"], bwd["dX"])}
+    for i in range(t):
+        errs[f"dA{i}"] = relerr(r["dA"][i], bwd["dA"][i])
+        errs[f"dB{i}"] = relerr(r["dB"][i], bwd["dB"][i])
+        errs[f"Z{i}"] = relerr(r["Z"][i], fwd["Z"][i])
+        errs[f"Y{i}"] = relerr(r["Y"][i], fwd["Y"][i])
+        errs[f"P{i}"] = relerr(r["P"][i], fwd["P"][i])
+        errs[f"D{i}"] = relerr(r["D"][i], bwd["D"][i])
+        errs[f"dXp{i}"] = relerr(r["dXp"][i], bwd["dXp"][i])
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    assert not bad, f"over {tol}: {bad}"
+    return errs
+
+
+def test_worked_example_fp32():
+    inp = config_inputs("worked_example", seed=0)
+    errs = compare_full(inp, 2, "f32", "worked example")
+    # the sharded GPU result also equals the unsharded layer
+    X, A, B, G = (inp[k].f64 for k in "XABG")
+    O = om.dense_forward(X, A, B)
+    r = run_step(dev(inp["X"]), shard_cols(dev(inp["A"]), 2), shard_rows(dev(inp["B"]), 2),
+                 dev(inp["G"]))
+    assert relerr(r["O"], O) <= 1e-5
+    assert max(errs.values()) <= 1e-5
+
+
+@pytest.mark.parametrize("n,d,m,t", [(1, 4, 8, 2), (17, 36, 40, 2), (130, 72, 400, 2), (65, 100, 300, 3)])
+def test_fp32_ragged(n, d, m, t):
+    inp = mlp_inputs(n, d, m, t, dtype="f32", seed=11, x_std=1.0, w_std=0.2, g_std=1.0)
+    compare_full(inp, t, "f32")
+
+
+@pytest.mark.parametrize("n,d,m,t", [
+    (1, 8, 16, 2),          # single token, smallest legal widths
+    (3, 264, 272, 2),       # ragged N and K tails
+    (17, 520, 528, 2),
+    (1000, 264, 272, 2),    # ragged M; wgrad K = 1000 (16 K steps, ragged)
+    (520, 520, 1584, 3),    # several tiles in every dimension, t = 3
+    (256, 256, 256, 1),     # exactly one tile, t = 1 (the reduce is a copy)
+])
+def test_bf16_ragged(n, d, m, t):
+    inp = mlp_inputs(n, d, m, t, dtype="bf16", seed=5)
+    compare_full(inp, t, "bf16")
+
+
+def test_single_shard_config():
+    """t = 1, n = 4·512, d = 1024, m = 4096, bf16: full comparison."""
+    compare_full(config_inputs("single_shard", seed=0), 1, "bf16", "single-shard config")
+
+
+def test_empty_batch_gives_zero_weight_grads():
+    d, m, t = 64, 128, 2
+    inp = mlp_inputs(4, d, m, t, dtype="bf16", seed=1)
+    A_s, B_s = shard_cols(dev(inp["A"]), t), shard_rows(dev(inp["B"]), t)
+    X = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    Z, Y, P = tp.mlp_fwd(X, A_s, B_s)
+    assert Z.shape == (t, 0, m // t) and P.shape == (t, 0, d)
+    D, dA, dB, dXp = tp.mlp_bwd(X, A_s, B_s, Z, Y, X)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) == 0
+
+
+def test_deterministic_bitwise():
+    inp = mlp_inputs(600, 520, 1056, 2, dtype="bf16", seed=9)
+    X, A, B, G = (dev(inp[k]) for k in "XABG")
+    A_s, B_s = shard_cols(A, 2), shard_rows(B, 2)
+    r1 = run_step(X, A_s, B_s, G)
+    r2 = run_step(X, A_s, B_s, G)
+    for k in r1:
+        assert torch.equal(r1[k].view(torch.int16) if r1[k].dtype == torch.bfloat16 else r1[k],
+                           r2[k].view(torch.int16) if r2[k].dtype == torch.bfloat16 else r2[k]), k
+
+
+def test_bf16_store_rounds_to_nearest_even():
+    """Z = X·A with exact fp32 accumulators that sit halfway between two bf16
+    values: the stored Z must be the round-to-nearest-even result."""
+    from tpmlp_inputs import f32_to_bf16_bits
+    n, d, mi = 8, 8, 8
+    X = np.zeros((n, d), np.float32)
+    X[:, 0] = 1.0
+    X[:, 1] = np.arange(n, dtype=np.float32)    # row r: 1 + r·A[1, j]
+    A = np.zeros((d, mi), np.float32)
+    A[0, :] = 1.0
+    A[1, :] = 2.0 ** -8                         # 1 + r·2^-8: halfway cases for odd r
+    exact = X @ A                               # exact in fp32
+    tX = torch.from_numpy(f32_to_bf16_bits(X).view(np.int16)).view(torch.bfloat16).cuda()
+    tA = torch.from_numpy(f32_to_bf16_bits(A).view(np.int16)).view(torch.bfloat16).cuda()
+    tB = torch.zeros((1, mi, d), dtype=torch.bfloat16, device="cuda")
+    Z, Y, P = tp.mlp_fwd(tX, tA.reshape(1, d, mi).contiguous(), tB)
+    torch.cuda.synchronize()
+    got = Z[0].cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, f32_to_bf16_bits(exact))
+
+
+def test_nan_propagates_to_its_row_only():
+    inp = mlp_inputs(300, 264, 528, 2, dtype="bf16", seed=4)
+    X, A, B, G = (dev(inp[k]) for k in "XABG")
+    X[7, 3] = float("nan")
+    r = run_step(X, shard_cols(A, 2), shard_rows(B, 2), G)
+    O = r["O"].float()
+    assert torch.isnan(O[7]).all()
+    assert torch.isfinite(torch.cat([O[:7], O[8:]])).all()
+
+
+# ------------------------------------------------------------------ full-size, sampled
+def _sampled_check(inp, t, shards, rng_seed, n_rows, n_cols, label):
+    """Full-size GPU run; the oracle computes sampled rows (tokens) and sampled
+    hidden columns one by one: rows of O, Z_i, Y_i, P_i, D_i, dX_i, dX depend
+    only on the same rows of X and G; columns H of A_i give D_i[:, H],
+    dA_i[:, H] and dB_i[H, :] exactly (the hidden units decompose)."""
+    X, A, B, G = (dev(inp[k]) for k in "XABG")
+    say(f"[gpu] {label}: n={X.shape[0]} d={X.shape[1]} shards={shards}")
+    if A.shape[1] == B.shape[0] and shards > 1:
+        A_s, B_s = shard_cols(A, shards), shard_rows(B, shards)
+    else:
+        A_s, B_s = A.reshape(1, *A.shape).contiguous(), B.reshape(1, *B.shape).contiguous()
+    r = run_step(X, A_s, B_s, G)
+    n, d = X.shape
+    mi = A_s.shape[2]
+    rng = np.random.default_rng(rng_seed)
+    rows = np.sort(rng.choice(n, size=min(n_rows, n), replace=False))
+    Xf, Gf = inp["X"].f32, inp["G"].f32
+    Af = inp["A"].f32
+    Bf = inp["B"].f32
+    tol = TOL["bf16"]
+    errs = {}
+    O_rows = np.zeros((rows.size, d))
+    dX_rows = np.zeros((rows.size, d))
+    for i in range(A_s.shape[0]):
+        Ai = Af[:, i * mi:(i + 1) * mi]
+        Bi = Bf[i * mi:(i + 1) * mi, :]
+        Z, Y, P = om.shard_forward(Xf[rows], Ai, Bi)
+        D, _, _, dXi = om.shard_backward(Xf[rows], Ai, Bi, Z, Y, Gf[rows])
+        O_rows += P
+        dX_rows += dXi
+        for k, ref in (("Z", Z), ("Y", Y), ("P", P), ("D", D), ("dXp", dXi)):
+            errs[f"{k}{i}[rows]"] = relerr(f64(r[k][i][rows]), ref)
+        cols = np.sort(rng.choice(mi, size=min(n_cols, mi), replace=False))
+        Zc, Yc, _ = om.shard_forward(Xf, Ai[:, cols], Bi[cols, :])
+        Dc, dAc, dBc, _ = om.shard_backward(Xf, Ai[:, cols], Bi[cols, :], Zc, Yc, Gf)
+        errs[f"dA{i}[:,H]"] = relerr(f64(r["dA"][i][:, cols]), dAc)
+        errs[f"dB{i}[H,:]"] = relerr(f64(r["dB"][i][cols, :]), dBc)
+        errs[f"D{i}[:,H]"] = relerr(f64(r["D"][i][:, cols]), Dc)
+    errs["O[rows]"] = relerr(f64(r["O"][rows]), O_rows)
+    errs["dX[rows]"] = relerr(f64(r["dX"][rows]), dX_rows)
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    say(f"[gpu] {label}: worst {max(errs.values()):.3e}")
+    assert not bad, f"over {tol}: {bad}"
+    del r
+    torch.cuda.empty_cache()
+
+
+def test_gpt8p3b_shard_config_sampled():
+    """h = 3072, m = 4h, t = 8, n = 8192, all 8 shards resident (the bench workload)."""
+    _sampled_check(config_inputs("gpt8p3b_t8", seed=0), 8, 8, 0, 64, 48, "8.3B-shaped, 8 shards")
+
+
+def test_gpt1t_shard_config_sampled():
+    """h = 25600, m = 4h, t = 8 -> one shard A_0 25600×12800, B_0 12800×25600, n = 2048."""
+    _sampled_check(config_inputs("gpt1t_t8_shard0", seed=0), 8, 1, 1, 12, 24, "1T-shaped, shard 0")

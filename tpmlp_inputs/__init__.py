@@ -42,32 +42,48 @@ CONFIGS = {
 
 
 def f32_to_bf16_bits(x):
-    """Round fp32 values to bf16 (nearest-even); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
-    return (u >> np.uint64(16)).astype(np.uint16)
+    """Round finite fp32 values to bf16 (nearest-even); returns uint16 bit
+    patterns.  (No finite input can overflow the 32-bit sum.)"""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    u = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (u >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-class Tensor:
-    """One synthetic tensor: the stored values (fp32 or bf16 bits) and the
-    same values upcast exactly to fp64 for the oracle."""
+_CHUNK = 1 << 22  # elements drawn per step (the stream does not depend on it)
 
-    def __init__(self, values64, dtype):
-        v32 = np.asarray(values64, dtype=np.float64).astype(np.float32)
-        self.dtype = dtype
-        if dtype == "bf16":
-            self.bits = f32_to_bf16_bits(v32)
-            self.f32 = bf16_bits_to_f32(self.bits)
-        elif dtype == "f32":
-            self.bits = None
-            self.f32 = v32
-        else:
+
+def _draw(rng, shape, std, dtype):
+    """standard_normal fp64 × std, rounded to the storage dtype chunk by chunk;
+    returns fp32 values or bf16 bit patterns."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for b in range(0, n, _CHUNK):
+        v32 = (rng.standard_normal(min(_CHUNK, n - b)) * std).astype(np.float32)
+        out[b:b + v32.size] = f32_to_bf16_bits(v32) if dtype == "bf16" else v32
+    return out.reshape(shape)
+
+
+class Tensor:
+    """One synthetic tensor: the stored values (fp32, or bf16 bit patterns)
+    and, on demand, the same values upcast exactly to fp32 / fp64."""
+
+    def __init__(self, stored, dtype):
+        if dtype not in ("bf16", "f32"):
             raise ValueError(dtype)
-        self.shape = self.f32.shape
+        self.dtype = dtype
+        self.bits = stored if dtype == "bf16" else None
+        self._f32 = None if dtype == "bf16" else stored
+        self.shape = stored.shape
+
+    @property
+    def f32(self):
+        if self._f32 is None:
+            self._f32 = bf16_bits_to_f32(self.bits)
+        return self._f32
 
     @property
     def f64(self):
@@ -80,15 +96,11 @@ def mlp_inputs(n, d, m, t, dtype="bf16", seed=0, x_std=X_STD, w_std=W_STD,
     if m % t:
         raise ValueError("m must be divisible by t")
     rng = np.random.default_rng(seed)
-    X = rng.standard_normal((n, d)) * x_std
-    if shards is None:
-        A = rng.standard_normal((d, m)) * w_std
-        B = rng.standard_normal((m, d)) * w_std
-    else:
-        mi = m // t
-        A = rng.standard_normal((d, mi)) * w_std
-        B = rng.standard_normal((mi, d)) * w_std
-    G = rng.standard_normal((n, d)) * g_std
+    mw = m if shards is None else m // t
+    X = _draw(rng, (n, d), x_std, dtype)
+    A = _draw(rng, (d, mw), w_std, dtype)
+    B = _draw(rng, (mw, d), w_std, dtype)
+    G = _draw(rng, (n, d), g_std, dtype)
     return {"X": Tensor(X, dtype), "A": Tensor(A, dtype), "B": Tensor(B, dtype),
             "G": Tensor(G, dtype)}
 
@@ -97,12 +109,14 @@ def sp_inputs(s, h, m, t, dtype="bf16", seed=0, x_std=X_STD, w_std=W_STD,
               g_std=G_STD, gamma_std=0.1, beta_std=0.1):
     """x [s, h], A [h, m], B [m, h], G_out [s, h], γ = 1 + N(0, σ²), β = N(0, σ²)."""
     rng = np.random.default_rng(seed)
-    x = rng.standard_normal((s, h)) * x_std
-    A = rng.standard_normal((h, m)) * w_std
-    B = rng.standard_normal((m, h)) * w_std
-    G = rng.standard_normal((s, h)) * g_std
-    gamma = 1.0 + rng.standard_normal(h) * gamma_std
-    beta = rng.standard_normal(h) * beta_std
+    x = _draw(rng, (s, h), x_std, dtype)
+    A = _draw(rng, (h, m), w_std, dtype)
+    B = _draw(rng, (m, h), w_std, dtype)
+    G = _draw(rng, (s, h), g_std, dtype)
+    g32 = (1.0 + rng.standard_normal(h) * gamma_std).astype(np.float32)
+    b32 = (rng.standard_normal(h) * beta_std).astype(np.float32)
+    gamma = f32_to_bf16_bits(g32) if dtype == "bf16" else g32
+    beta = f32_to_bf16_bits(b32) if dtype == "bf16" else b32
     return {"x": Tensor(x, dtype), "A": Tensor(A, dtype), "B": Tensor(B, dtype),
             "G": Tensor(G, dtype), "gamma": Tensor(gamma, dtype), "beta": Tensor(beta, dtype)}
 
