@@ -12,18 +12,26 @@
 //
 // Tiling: 256×256 macro tile, K step 64, 4 waves (2×2), each wave owning a
 // 128×128 sub-tile as 4×4 MFMA blocks of 32×32 (256 fp32 accumulators per
-// lane, held in AGPRs).  Global→LDS traffic uses buffer_load … lds (16 B per
-// lane) into two LDS stages (2 × 64 KiB); edges are zero-filled by the buffer
-// descriptor's range check, so one code path serves every shape.  One
-// workgroup barrier per K step: it both publishes the next stage and frees the
-// current one.
+// lane, in AGPRs).  The B fragment is the MFMA's first operand, so each lane
+// ends up holding 4 consecutive output columns of one row.
 //
-// LDS fragment reads are issued as inline asm with explicit lgkmcnt waits that
-// carry the fragment registers as operands, so (a) reads for the next 16-wide
-// K slice are in flight while the current slice's 16 MFMAs run, and (b) the
-// compiler's conservative "wait for every LDS DMA" before a transposing read
-// is never inserted (the DMA completion is awaited once per stage, before the
-// barrier).
+// Global→LDS: buffer_load … lds (16 B per lane; edges zero-filled by the
+// buffer descriptor's range check, so one code path serves every shape).  The
+// A operand has 3 LDS stages and is fetched two K steps ahead, the B operand
+// has 2 stages and is fetched one step ahead: 5 × 32 KiB = all 160 KiB of LDS.
+// One workgroup barrier per K step publishes the stages that just landed and
+// frees the ones just consumed.
+//
+// The K-step body is a fixed interleaving written as inline asm, so that the
+// compiler keeps it: each of the 64 MFMAs of a step is followed by at most one
+// memory instruction (a fragment read for the next 16-wide K slice, or a DMA
+// load for a later step), so no burst of memory instructions stalls the
+// in-order MFMA issue of the single wave per SIMD.  Fragment registers are
+// double-buffered across K slices; the lgkmcnt waits carry them as operands.
+//
+// Epilogue: bf16 outputs are staged through LDS (each wave its own 128×128
+// quadrant) and written with coalesced 16-B stores; fp32 outputs are written
+// straight from the accumulators as 16-B stores.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,8 +39,10 @@ namespace tpmlp {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
-constexpr int OP_TILE_BYTES = 256 * BK * 2;  // one operand tile, 32 KiB
-constexpr int STAGE_BYTES = 2 * OP_TILE_BYTES;
+constexpr int TILE_BYTES = 256 * BK * 2;  // one operand stage, 32 KiB
+constexpr int A_STAGES = 3, B_STAGES = 2;
+constexpr int B_BASE = A_STAGES * TILE_BYTES;
+constexpr int LDS_BYTES = (A_STAGES + B_STAGES) * TILE_BYTES;  // 160 KiB
 constexpr uint32_t OOB = 0x80000000u;  // past every descriptor's range (< 2^31)
 
 struct KArgs {
@@ -45,69 +55,106 @@ struct KArgs {
   int tiles_m, tiles_n, batch;
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;
-  uint32_t a_bytes, b_bytes;
+  uint32_t a_bytes, b_bytes, c_bytes;
 };
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------------------
-// LDS tile layouts (one 256-row × 64-k operand tile = 32 KiB).
+// LDS operand tile layouts (256 rows of M or N × 64 k = 32 KiB).
 //
-// KMAJ: [256 rows][64 k], 128 B per row.  The 16-B chunk c (8 k values) of
-//   row r sits at chunk slot c ^ (r & 7): the 8 lanes that read one chunk of 8
-//   consecutive rows hit 8 different bank groups.
+// KMAJ: [256 rows][64 k], 128 B per row.  Chunk c (8 k values) of row r sits
+//   at chunk slot c ^ ((r >> 1) & 7).  The LDS serves 256 B per clock (64
+//   banks), i.e. 16 lanes of a 16-B read: those lanes read one chunk of 16
+//   consecutive rows, even rows in one 128-B half of the bank line and odd rows
+//   in the other, and the swizzle gives the 8 rows of each half 8 slots.
 // MNMAJ: [8 column blocks][64 k][32 columns], 64 B per (block, k) row.  Chunk
-//   c (0..3) of k-row k sits at slot c ^ (((k >> 1) & 1) << 1): a 16-lane
-//   transposing read of 4 consecutive k-rows × 32 B then covers the 8 distinct
-//   16-B slots of a 128-B bank line.
+//   c (0..3) of k-row k sits at slot c ^ (((k >> 1) & 1) << 1): the 32 lanes
+//   of two 16-lane transposing reads then cover 4 k-rows × 64 B = 256 B once.
 // ---------------------------------------------------------------------------
 
+// Per-lane DMA offsets for one operand: the 8 loads a wave issues per stage.
+// base[j] is the byte offset of the lane's 16-B chunk at k0 = 0 (OOB when the
+// row lies past the matrix edge); the k part is added per step.  kq / kq_odd
+// are the lane's k offset inside the step, for the K-edge test.
+struct LoadPlan {
+  uint32_t base[8];
+  uint32_t kstep;  // bytes to add per K step (64 k)
+  int kq;
+  int kq_odd;
+};
+
 template <int ORDER>
-__device__ __forceinline__ void issue_tile(i32x4 rsrc, TPMLP_LDS char* tile, int r0, int k0, int R,
-                                           int K, int64_t ld, int wave, int lane) {
+__device__ __forceinline__ LoadPlan make_plan(int r0, int R, int64_t ld, int wave, int lane) {
+  LoadPlan p;
   if constexpr (ORDER == KMAJ) {
-    // 8 instructions per wave, each 8 rows × 128 B.
+    // load j: rows wave·64 + 8j .. +7; lane: row + lane/8, slot lane%8
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = wave * 64 + j * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (lane >> 3);  // row & 7 == lane >> 3
-      const int gr = r0 + row, gk = k0 + c * 8;
-      const bool ok = gr < R && gk < K;
-      const uint32_t voff =
-          ok ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + gk) * 2) : OOB;
-      buffer_load_lds16(rsrc, tile + (wave * 64 + j * 8) * 128, voff);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      const int gr = r0 + row;
+      p.base[j] = gr < R ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + c * 8) * 2) : OOB;
     }
+    p.kstep = BK * 2;
+    // (row >> 1) & 7 = (4j + lane/16) & 7 only depends on the parity of j
+    p.kq = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
+    p.kq_odd = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
   } else {
-    // 8 instructions per wave, each one column block × 16 k-rows × 64 B.
+    // load j: column block (wave·8+j)/4, k-rows 16·(j%4) + lane/4
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int seg = wave * 8 + j;  // 32 segments of 1 KiB
-      const int blk = seg >> 2;      // column block 0..7
+      const int seg = wave * 8 + j;
+      const int blk = seg >> 2;
       const int kr = (seg & 3) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ (((kr >> 1) & 1) << 1);
-      const int gk = k0 + kr, gr = r0 + blk * 32 + c * 8;
-      const bool ok = gk < K && gr < R;
-      const uint32_t voff =
-          ok ? static_cast<uint32_t>((static_cast<int64_t>(gk) * ld + gr) * 2) : OOB;
-      buffer_load_lds16(rsrc, tile + seg * 1024, voff);
+      const int gr = r0 + blk * 32 + c * 8;
+      p.base[j] = gr < R ? static_cast<uint32_t>((static_cast<int64_t>(kr) * ld + gr) * 2) : OOB;
     }
+    p.kstep = static_cast<uint32_t>(BK * ld * 2);
+    p.kq = lane >> 2;
+    p.kq_odd = 0;
+  }
+  return p;
+}
+
+// DMA load J of one operand for the K step at byte offset koff (krem = K minus
+// the step's first k) into stage `tile`.
+template <int ORDER, int J>
+__device__ __forceinline__ void dma(i32x4 rsrc, TPMLP_LDS char* tile, const LoadPlan& p, uint32_t koff,
+                                    int krem, int wave) {
+  bool ok;
+  if constexpr (ORDER == KMAJ)
+    ok = ((J & 1) ? p.kq_odd : p.kq) < krem;
+  else
+    ok = (J & 3) * 16 + p.kq < krem;
+  const uint32_t voff = ok ? p.base[J] + koff : OOB;
+  if constexpr (ORDER == KMAJ)
+    buffer_load_lds16(rsrc, tile + (wave * 64 + J * 8) * 128, voff);
+  else
+    buffer_load_lds16(rsrc, tile + (wave * 8 + J) * 1024, voff);
+}
+
+template <int ORDER, int J = 0>
+__device__ __forceinline__ void dma_all(i32x4 rsrc, TPMLP_LDS char* tile, const LoadPlan& p, uint32_t koff,
+                                        int krem, int wave) {
+  if constexpr (J < 8) {
+    dma<ORDER, J>(rsrc, tile, p, koff, krem, wave);
+    dma_all<ORDER, J + 1>(rsrc, tile, p, koff, krem, wave);
   }
 }
 
-// Per-lane LDS byte offsets (relative to the operand tile) of the fragment
-// reads.  A fragment covers 32 rows (of M or N) × one 16-wide K slice; lane L
-// receives row L%32, k = 8·(L/32) + 0..7 of the slice.
-struct FragAddr {
-  uint32_t a[4];  // KMAJ: one base per K slice; MNMAJ: a[0] only
-};
-
+// Per-lane LDS byte offsets of the fragment reads (relative to a stage).  A
+// fragment covers 32 rows (of M or N) × one 16-wide K slice; lane L receives
+// row L%32, k = 8·(L/32) + 0..7 of the slice.
 template <int ORDER>
-__device__ __forceinline__ FragAddr frag_addr(int rbase, int lane) {
-  FragAddr f;
+__device__ __forceinline__ void frag_addr(uint32_t (&f)[4], int rbase, int lane) {
   if constexpr (ORDER == KMAJ) {
     const int rr = rbase + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = ks * 2 + (lane >> 5);
-      f.a[ks] = rr * 128 + ((c ^ (rr & 7)) << 4);
+      f[ks] = rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4);
     }
   } else {
     // ds_read_b64_tr_b16: in each 16-lane group, lane i reads 4 elements of
@@ -115,106 +162,154 @@ __device__ __forceinline__ FragAddr frag_addr(int rbase, int lane) {
     // lane i holds column i of the block for k-rows 0..3.  Groups: g&1 picks
     // columns 0-15 / 16-31 of the fragment, g>>1 picks k 0-7 / 8-15.
     const int g = lane >> 4, i = lane & 15;
-    const int col = (g & 1) * 16 + (i & 3) * 4;  // within the 32-column block
+    const int col = (g & 1) * 16 + (i & 3) * 4;
     const int kq = (g >> 1) * 8 + (i >> 2);
     const int c = (col >> 3) ^ (((kq >> 1) & 1) << 1);
-    f.a[0] = (rbase >> 5) * 4096 + kq * 64 + (c << 4) + (col & 7) * 2;
-    f.a[1] = f.a[2] = f.a[3] = 0;
-  }
-  return f;
-}
-
-#define TPMLP_DS_READ_B128(dst, addr, OFF) \
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF))
-#define TPMLP_DS_READ_TR(dst, addr, OFF) \
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF))
-
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-// Issue the 4 fragment reads of one operand for K slice KS.  TILE_OFF is the
-// operand tile's byte offset inside the stage; `base` already includes the
-// stage offset.
-template <int ORDER, int KS, int TILE_OFF>
-__device__ __forceinline__ void read_frags(i32x4 (&fr)[4], const FragAddr& fa, uint32_t stage) {
-  if constexpr (ORDER == KMAJ) {
-    const uint32_t a = fa.a[KS] + stage;
-    TPMLP_DS_READ_B128(fr[0], a, TILE_OFF + 0 * 4096);
-    TPMLP_DS_READ_B128(fr[1], a, TILE_OFF + 1 * 4096);
-    TPMLP_DS_READ_B128(fr[2], a, TILE_OFF + 2 * 4096);
-    TPMLP_DS_READ_B128(fr[3], a, TILE_OFF + 3 * 4096);
-  } else {
-    const uint32_t a = fa.a[0] + stage;
-    i32x2 lo[4], hi[4];
-    TPMLP_DS_READ_TR(lo[0], a, TILE_OFF + 0 * 4096 + KS * 1024);
-    TPMLP_DS_READ_TR(hi[0], a, TILE_OFF + 0 * 4096 + KS * 1024 + 256);
-    TPMLP_DS_READ_TR(lo[1], a, TILE_OFF + 1 * 4096 + KS * 1024);
-    TPMLP_DS_READ_TR(hi[1], a, TILE_OFF + 1 * 4096 + KS * 1024 + 256);
-    TPMLP_DS_READ_TR(lo[2], a, TILE_OFF + 2 * 4096 + KS * 1024);
-    TPMLP_DS_READ_TR(hi[2], a, TILE_OFF + 2 * 4096 + KS * 1024 + 256);
-    TPMLP_DS_READ_TR(lo[3], a, TILE_OFF + 3 * 4096 + KS * 1024);
-    TPMLP_DS_READ_TR(hi[3], a, TILE_OFF + 3 * 4096 + KS * 1024 + 256);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) fr[q] = __builtin_shufflevector(lo[q], hi[q], 0, 1, 2, 3);
+    f[0] = (rbase >> 5) * 4096 + kq * 64 + (c << 4) + (col & 7) * 2;
+    f[1] = f[2] = f[3] = 0;
   }
 }
 
 template <int ORDER>
-constexpr int reads_per_operand() {
+constexpr int reads_per_slice() {
   return ORDER == KMAJ ? 4 : 8;
 }
 
-// Wait until at most N LDS reads are outstanding; the fragment registers are
-// in/out operands so no use of them can be scheduled above the wait.
-template <int N>
+// Read op T of one operand for K slice KS.  KMAJ: op T is fragment T.  MNMAJ:
+// op T is half T&1 (k 0-3 / 4-7 of the lane's 8) of fragment T>>1.
+template <int ORDER, int KS, int T>
+__device__ __forceinline__ void read_op(i32x4 (&fr)[4], const uint32_t (&f)[4], uint32_t stage) {
+  if constexpr (ORDER == KMAJ) {
+    const uint32_t a = f[KS] + stage;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fr[T]) : "v"(a), "i"(T * 4096));
+  } else {
+    const uint32_t a = f[0] + stage;
+    i32x2 h;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(h)
+                 : "v"(a), "i"((T >> 1) * 4096 + KS * 1024 + (T & 1) * 256));
+    if constexpr (T & 1) {
+      fr[T >> 1][2] = h[0];
+      fr[T >> 1][3] = h[1];
+    } else {
+      fr[T >> 1][0] = h[0];
+      fr[T >> 1][1] = h[1];
+    }
+  }
+}
+
+// Wait until no LDS read is outstanding; the fragment registers are in/out
+// operands so no use of them can be placed above the wait.
 __device__ __forceinline__ void wait_frags(i32x4 (&a)[4], i32x4 (&b)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
-                 "+v"(b[2]), "+v"(b[3])
-               : "i"(N));
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
+                 "+v"(b[3]));
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+#define TPMLP_MFMA(ACC, BF, AF) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(ACC) : "v"(BF), "v"(AF))
 
-__device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const i32x4 (&a)[4], const i32x4 (&b)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[j]),
-                                                          acc[i][j], 0, 0, 0);
+// One read op for the next slice, from the merged A-then-B op list.
+template <int AO, int BO, int KS, int T>
+__device__ __forceinline__ void next_read(i32x4 (&fa)[4], i32x4 (&fb)[4], const uint32_t (&pa)[4],
+                                          const uint32_t (&pb)[4], uint32_t sa, uint32_t sb) {
+  constexpr int NA = reads_per_slice<AO>();
+  if constexpr (T < NA)
+    read_op<AO, KS, T>(fa, pa, sa);
+  else
+    read_op<BO, KS, T - NA>(fb, pb, sb);
 }
 
-// Map the linear workgroup id to a tile so that the tiles one XCD works on
-// form one contiguous range (workgroups are dealt to the 8 XCDs round-robin;
-// each XCD has its own L2).
-__device__ __forceinline__ int xcd_tile(int wg, int total) {
+template <int AO, int BO, int KS, int T = 0>
+__device__ __forceinline__ void read_slice(i32x4 (&fa)[4], i32x4 (&fb)[4], const uint32_t (&pa)[4],
+                                           const uint32_t (&pb)[4], uint32_t sa, uint32_t sb) {
+  if constexpr (T < reads_per_slice<AO>() + reads_per_slice<BO>()) {
+    next_read<AO, BO, KS, T>(fa, fb, pa, pb, sa, sb);
+    read_slice<AO, BO, KS, T + 1>(fa, fb, pa, pb, sa, sb);
+  }
+}
+
+struct StepCtx {
+  i32x4 rA, rB;
+  TPMLP_LDS char* dA;
+  TPMLP_LDS char* dB;
+  uint32_t sa, sb, koA, koB;
+  int kremA, kremB, wave;
+};
+
+// The 16 MFMAs of slice S, each followed by at most one memory instruction:
+// the reads of slice S+1 (S < 3) and, in slices 0 and 1, the DMA loads of the
+// B operand (next step) and the A operand (the step after).
+template <int AO, int BO, int S, int Q = 0>
+__device__ __forceinline__ void slice_body(f32x16 (&acc)[4][4], i32x4 (&ca)[4], i32x4 (&cb)[4],
+                                           i32x4 (&na)[4], i32x4 (&nb)[4], const uint32_t (&pa)[4],
+                                           const uint32_t (&pb)[4], const LoadPlan& la, const LoadPlan& lb,
+                                           const StepCtx& s) {
+  if constexpr (Q < 16) {
+    TPMLP_MFMA(acc[Q >> 2][Q & 3], cb[Q & 3], ca[Q >> 2]);
+    constexpr int NR = reads_per_slice<AO>() + reads_per_slice<BO>();
+    if constexpr (S < 3 && Q < NR) next_read<AO, BO, S + 1, Q>(na, nb, pa, pb, s.sa, s.sb);
+    if constexpr (S == 0 && (Q & 1)) dma<BO, (Q >> 1)>(s.rB, s.dB, lb, s.koB, s.kremB, s.wave);
+    if constexpr (S == 1 && (Q & 1)) dma<AO, (Q >> 1)>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
+    slice_body<AO, BO, S, Q + 1>(acc, ca, cb, na, nb, pa, pb, la, lb, s);
+  }
+}
+
+// Tile order: the tiles one XCD works on form one contiguous range
+// (workgroups are dealt to the 8 XCDs round-robin and each XCD has its own
+// L2), and inside a range tiles go in groups of 4 tile rows so that the 32
+// tiles an XCD runs at once share 4 A panels and 8 B panels.
+__device__ __forceinline__ void tile_coords(int wg, const KArgs& a, int& batch, int& tm, int& tn) {
+  const int per_batch = a.tiles_m * a.tiles_n;
+  const int total = per_batch * a.batch;
   const int q = total >> 3, r = total & 7;
   const int xcd = wg & 7, local = wg >> 3;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int tile = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  batch = tile / per_batch;
+  const int t2 = tile - batch * per_batch;
+  constexpr int GM = 4;
+  const int grp = t2 / (GM * a.tiles_n);
+  const int fm = grp * GM;
+  const int gm = a.tiles_m - fm < GM ? a.tiles_m - fm : GM;
+  const int rem = t2 - grp * GM * a.tiles_n;
+  tm = fm + rem % gm;
+  tn = rem / gm;
+}
+
+__device__ __forceinline__ i32x2 pack4_bf16(float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = f2bf(a);
+  v[1] = f2bf(b);
+  v[2] = f2bf(c);
+  v[3] = f2bf(d);
+  return __builtin_bit_cast(i32x2, v);
+}
+
+// Epilogue staging quadrant (per wave, 128 rows × 128 columns of bf16, 256 B
+// per row): chunk c (8 columns) of row r sits at slot c ^ (r & 15).
+__device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk, int half) {
+  return qbase + row * 256 + ((chunk ^ (row & 15)) << 4) + half * 8;
 }
 
 template <int AO, int BO, int EPI>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
-  const int per_batch = a.tiles_m * a.tiles_n;
-  const int tile = xcd_tile(blockIdx.x, per_batch * a.batch);
-  const int batch = tile / per_batch;
-  const int t2 = tile - batch * per_batch;
-  const int tm = t2 / a.tiles_n, tn = t2 - (t2 / a.tiles_n) * a.tiles_n;
+  int batch, tm, tn;
+  tile_coords(blockIdx.x, a, batch, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const i32x4 ra = make_rsrc(a.A + batch * a.sA, a.a_bytes);
-  const i32x4 rb = make_rsrc(a.B + batch * a.sB, a.b_bytes);
-
-  const FragAddr fa = frag_addr<AO>(wm * 128, lane);
-  const FragAddr fb = frag_addr<BO>(wn * 128, lane);
-  constexpr int NR = reads_per_operand<AO>() + reads_per_operand<BO>();
-  constexpr int NRW = NR > 15 ? 15 : NR;
+  const i32x4 rA = make_rsrc(a.A + batch * a.sA, a.a_bytes);
+  const i32x4 rB = make_rsrc(a.B + batch * a.sB, a.b_bytes);
+  const LoadPlan la = make_plan<AO>(m0, a.M, a.lda, wave, lane);
+  const LoadPlan lb = make_plan<BO>(n0, a.N, a.ldb, wave, lane);
+  uint32_t pa[4], pb[4];
+  frag_addr<AO>(pa, wm * 128, lane);
+  frag_addr<BO>(pb, wn * 128, lane);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -226,66 +321,170 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KArgs a) {
 
   const int KT = (a.K + BK - 1) / BK;
   if (KT > 0) {
-    issue_tile<AO>(ra, lds, m0, 0, a.M, a.K, a.lda, wave, lane);
-    issue_tile<BO>(rb, lds + OP_TILE_BYTES, n0, 0, a.N, a.K, a.ldb, wave, lane);
-    wait_vmcnt<0>();
-    block_barrier();
-  }
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) {
-      TPMLP_LDS char* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-      issue_tile<AO>(ra, nxt, m0, (kt + 1) * BK, a.M, a.K, a.lda, wave, lane);
-      issue_tile<BO>(rb, nxt + OP_TILE_BYTES, n0, (kt + 1) * BK, a.N, a.K, a.ldb, wave, lane);
-    }
-    const uint32_t st = lds_base + (kt & 1) * STAGE_BYTES;
-    i32x4 a0[4], b0[4], a1[4], b1[4];
-    read_frags<AO, 0, 0>(a0, fa, st);
-    read_frags<BO, 0, OP_TILE_BYTES>(b0, fb, st);
-    read_frags<AO, 1, 0>(a1, fa, st);
-    read_frags<BO, 1, OP_TILE_BYTES>(b1, fb, st);
-    wait_frags<NRW>(a0, b0);
-    mma16(acc, a0, b0);
-    read_frags<AO, 2, 0>(a0, fa, st);
-    read_frags<BO, 2, OP_TILE_BYTES>(b0, fb, st);
-    wait_frags<NRW>(a1, b1);
-    mma16(acc, a1, b1);
-    read_frags<AO, 3, 0>(a1, fa, st);
-    read_frags<BO, 3, OP_TILE_BYTES>(b1, fb, st);
-    wait_frags<NRW>(a0, b0);
-    mma16(acc, a0, b0);
-    wait_frags<0>(a1, b1);
-    mma16(acc, a1, b1);
-    // The next stage's loads have landed (this wave's share) and this wave is
-    // done reading the current stage; the barrier makes both hold for all.
-    wait_vmcnt<0>();
+    // prologue: A(0), B(0), then A(1); wait for the first two
+    dma_all<AO>(rA, lds, la, 0, a.K, wave);
+    dma_all<BO>(rB, lds + B_BASE, lb, 0, a.K, wave);
+    dma_all<AO>(rA, lds + TILE_BYTES, la, la.kstep, a.K - BK, wave);
+    wait_vmcnt<8>();
     block_barrier();
   }
 
-  // Epilogue.  32×32 block (i, j), accumulator v of lane L holds
-  // row 8·(v/4) + 4·(L/32) + v%4, column L%32.
-  const int64_t cb = static_cast<int64_t>(batch) * a.sC;
+  int sA = 0;  // A stage of step kt (= kt % 3)
+  for (int kt = 0; kt < KT; ++kt) {
+    const int sA2 = sA == 0 ? 2 : sA - 1;  // (kt + 2) % 3
+    StepCtx s;
+    s.rA = rA;
+    s.rB = rB;
+    s.sa = lds_base + sA * TILE_BYTES;
+    s.sb = lds_base + B_BASE + (kt & 1) * TILE_BYTES;
+    s.dA = lds + sA2 * TILE_BYTES;
+    s.dB = lds + B_BASE + ((kt + 1) & 1) * TILE_BYTES;
+    s.koA = static_cast<uint32_t>(kt + 2) * la.kstep;
+    s.koB = static_cast<uint32_t>(kt + 1) * lb.kstep;
+    s.kremA = a.K - (kt + 2) * BK;
+    s.kremB = a.K - (kt + 1) * BK;
+    s.wave = wave;
+
+    i32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+    read_slice<AO, BO, 0>(fa0, fb0, pa, pb, s.sa, s.sb);
+    wait_frags(fa0, fb0);
+    slice_body<AO, BO, 0>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
+    wait_frags(fa1, fb1);
+    slice_body<AO, BO, 1>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
+    wait_frags(fa0, fb0);
+    slice_body<AO, BO, 2>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
+    wait_frags(fa1, fb1);
+    slice_body<AO, BO, 3>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
+    // B(kt+1) and A(kt+1) have landed (this wave's share); A(kt+2) may still
+    // be in flight.  The barrier publishes them and frees this step's stages.
+    wait_vmcnt<8>();
+    block_barrier();
+    sA = sA == 2 ? 0 : sA + 1;
+  }
+  wait_vmcnt<0>();
+  // The accumulators were last written by inline-asm MFMAs: give the MFMA
+  // pipeline its passes before they are read.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // ------------------------------------------------------------------ epilogue
+  // Accumulator v of block (i, j) of lane L: row wm·128 + 32i + L%32,
+  // columns wn·128 + 32j + 8·(v/4) + 4·(L/32) + v%4.
+  const int row_l = lane & 31, half = lane >> 5;
+  if constexpr (EPI == EPI_STORE_F32) {
+    float* C = static_cast<float*>(a.C) + static_cast<int64_t>(batch) * a.sC;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * 128 + i * 32 + row_l;
+      if (row >= a.M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= a.N) continue;
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        if (row >= a.M) continue;
-        const int64_t off = cb + static_cast<int64_t>(row) * a.ldc + col;
-        const float x = acc[i][j][v];
-        if constexpr (EPI == EPI_STORE) {
-          static_cast<bf16*>(a.C)[off] = f2bf(x);
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          static_cast<float*>(a.C)[off] = x;
-        } else if constexpr (EPI == EPI_GELU_ZY) {
-          static_cast<bf16*>(a.C)[off] = f2bf(x);
-          static_cast<bf16*>(a.C2)[off] = f2bf(gelu_fast(x));
-        } else {
-          const float z = bf2f(a.Zin[off]);
-          static_cast<bf16*>(a.C)[off] = f2bf(x * gelu_grad_fast(z));
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * 128 + j * 32 + q * 8 + half * 4;
+          if (col < a.N) {
+            f32x4 v;
+            v[0] = acc[i][j][4 * q + 0];
+            v[1] = acc[i][j][4 * q + 1];
+            v[2] = acc[i][j][4 * q + 2];
+            v[3] = acc[i][j][4 * q + 3];
+            *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row) * a.ldc + col) = v;
+          }
+        }
+      }
+    }
+  } else {
+    block_barrier();  // every wave is done with the main-loop stages
+    const uint32_t qbase = lds_base + wave * 32768;
+    const int64_t cbase = static_cast<int64_t>(batch) * a.sC;
+    const int qm0 = m0 + wm * 128, qn0 = n0 + wn * 128;
+    constexpr int PASSES = EPI == EPI_GELU_ZY ? 2 : 1;
+
+    if constexpr (EPI == EPI_GELU_GRAD) {
+      // Stage this quadrant's stored Z (same layout) with 16-B DMA loads:
+      // load j covers rows 4j..4j+3; lane: row 4j + L/16, slot L%16.
+      const i32x4 rZ = make_rsrc(a.Zin + cbase, a.c_bytes);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int row = j * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ (row & 15);
+        const int gr = qm0 + row, gc = qn0 + c * 8;
+        const uint32_t voff = (gr < a.M && gc < a.N)
+                                  ? static_cast<uint32_t>((static_cast<int64_t>(gr) * a.ldc + gc) * 2)
+                                  : OOB;
+        buffer_load_lds16(rZ, lds + wave * 32768 + j * 1024, voff);
+      }
+      wait_vmcnt<0>();
+    }
+
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      // accumulators -> bf16 -> staging quadrant, one 32-row block at a time
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        i32x2 zr[4][4];
+        if constexpr (EPI == EPI_GELU_GRAD) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              asm volatile("ds_read_b64 %0, %1"
+                           : "=v"(zr[j][q])
+                           : "v"(quad_addr(qbase, i * 32 + row_l, j * 4 + q, half)));
+          // the Z registers are operands of the wait: no use moves above it
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(zr[0][0]), "+v"(zr[0][1]), "+v"(zr[0][2]), "+v"(zr[0][3]), "+v"(zr[1][0]),
+                         "+v"(zr[1][1]), "+v"(zr[1][2]), "+v"(zr[1][3]), "+v"(zr[2][0]), "+v"(zr[2][1]),
+                         "+v"(zr[2][2]), "+v"(zr[2][3]), "+v"(zr[3][0]), "+v"(zr[3][1]), "+v"(zr[3][2]),
+                         "+v"(zr[3][3])::"memory");
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+            float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+            if constexpr (EPI == EPI_GELU_ZY) {
+              if (pass == 1) {
+                v0 = gelu_fast(v0);
+                v1 = gelu_fast(v1);
+                v2 = gelu_fast(v2);
+                v3 = gelu_fast(v3);
+              }
+            } else if constexpr (EPI == EPI_GELU_GRAD) {
+              const bf16x4 z = __builtin_bit_cast(bf16x4, zr[j][q]);
+              v0 *= gelu_grad_fast(bf2f(z[0]));
+              v1 *= gelu_grad_fast(bf2f(z[1]));
+              v2 *= gelu_grad_fast(bf2f(z[2]));
+              v3 *= gelu_grad_fast(bf2f(z[3]));
+            }
+            const i32x2 pk = pack4_bf16(v0, v1, v2, v3);
+            asm volatile("ds_write_b64 %0, %1" ::"v"(quad_addr(qbase, i * 32 + row_l, j * 4 + q, half)),
+                         "v"(pk)
+                         : "memory");
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // staging quadrant -> global: 4 rows × 256 B per wave-wide 16-B access
+      bf16* C = static_cast<bf16*>(pass == 0 ? a.C : a.C2) + cbase;
+#pragma unroll
+      for (int it0 = 0; it0 < 32; it0 += 8) {
+        i32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = (it0 + u) * 4 + (lane >> 4);
+          const uint32_t ad = qbase + row * 256 + (((lane & 15) ^ (row & 15)) << 4);
+          asm volatile("ds_read_b128 %0, %1" : "=v"(v[u]) : "v"(ad) : "memory");
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                       "+v"(v[7])::"memory");
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = (it0 + u) * 4 + (lane >> 4);
+          const int gr = qm0 + row, gc = qn0 + (lane & 15) * 8;
+          if (gr < a.M && gc < a.N)
+            *reinterpret_cast<i32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc) = v[u];
         }
       }
     }
@@ -332,6 +531,7 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int 
   k.sC = p.sC;
   k.a_bytes = extent_bytes(a_order, p.M, p.K, p.lda);
   k.b_bytes = extent_bytes(b_order, p.N, p.K, p.ldb);
+  k.c_bytes = static_cast<uint32_t>(((static_cast<int64_t>(p.M) - 1) * p.ldc + p.N) * 2);
   if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_GELU_ZY)
     return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY>(k, stream);
   if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_STORE)
