@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing on the host")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain device copy of 512 MiB (read 512 MiB, write 512 MiB), "
+                         "the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -57,9 +60,10 @@ def cpu_baseline(inp, t, budget_s):
     info = threadpoolctl.threadpool_info()
     threads = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"), default=1)
     shards, t0 = 0, time.perf_counter()
-    while shards < t:
-        Ai = A[:, shards * mi:(shards + 1) * mi].astype(np.float64)
-        Bi = B[shards * mi:(shards + 1) * mi, :].astype(np.float64)
+    while shards < 4 * t:  # whole shards, cycling, until the budget is used
+        i = shards % t
+        Ai = A[:, i * mi:(i + 1) * mi].astype(np.float64)
+        Bi = B[i * mi:(i + 1) * mi, :].astype(np.float64)
         Z, Y, P = om.shard_forward(X, Ai, Bi)
         om.shard_backward(X, Ai, Bi, Z, Y, G)
         shards += 1
@@ -69,9 +73,31 @@ def cpu_baseline(inp, t, budget_s):
     flops = 12.0 * n * d * mi * shards
     return {"value": round(flops / el / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{shards} of {t} shards, full n={n}: fp64 NumPy forward + backward "
-                      f"({flops:.3e} FLOP in {el:.1f} s); host logical CPUs {os.cpu_count()}, "
+            "sample": f"{shards} whole-shard passes (of {t} shards), full n={n}: fp64 NumPy forward + "
+                      f"backward ({flops:.3e} FLOP in {el:.1f} s); host logical CPUs {os.cpu_count()}, "
                       f"affinity {len(os.sched_getaffinity(0))}"}
+
+
+def recorded_traffic(kernel_file, summary):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    in a profiles/ summary, or None when the summary is missing or the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].strip() in ("source_sha256", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    src = open(os.path.join(ROOT, "megatron_tensor_transformer_amd", "csrc", kernel_file), "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -135,6 +161,12 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # timed region: K whole steps, events around each entry point
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -181,13 +213,15 @@ def main():
         "gemm_only": {"tflops": round(gemm_tflops, 2),
                       "pct_of_peak": round(100.0 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
                       "fwd_ms": round(float(np.mean(fwd_ms)), 4), "bwd_ms": round(float(np.mean(bwd_ms)), 4)},
-        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (6 launches per step)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel, average over the 6 launches of a step",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic("gemm_bf16.hip", "gemm_bf16_gpt8p3b_t8_traffic.md"),
                      "flop_per_launch": per_launch_flop, "avg_launch_ms": round(avg_launch_ms, 4)},
         "roofline_reduce": {"bound": "hbm", "kernel": "reduce_vec8_kernel",
                             "achieved": round(red_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(red_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                            "frac": round(red_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": recorded_traffic("reduce.hip", "reduce_gpt8p3b_t8_traffic.md"),
                             "bytes_per_launch": red_bytes, "avg_launch_ms": round(red_ms, 4)},
         "wall_s_timed": round(wall, 3),
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
