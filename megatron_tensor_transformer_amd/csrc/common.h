@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gelu_poly.h"  // GeLU / GeLU' of the bf16 epilogues
+
 namespace tpmlp {
 
 typedef __bf16 bf16;
@@ -53,41 +55,6 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 }
 
 __device__ __forceinline__ void block_barrier() { __builtin_amdgcn_s_barrier(); }
-
-// ---------------------------------------------------------------------------
-// GeLU for the bf16 path.  Φ(z) comes from the Abramowitz & Stegun 7.1.26
-// rational approximation of erf (|error| <= 1.5e-7, far below bf16's 2^-9
-// resolution): erf(x) = 1 - (a1 s + ... + a5 s^5) e^{-x^2}, s = 1/(1 + p x).
-// With x = |z|/√2, e^{-x^2} = e^{-z^2/2} is also the normal density's kernel,
-// so GeLU'(z) = Φ(z) + z·e^{-z^2/2}/√(2π) costs two more operations.
-struct NormalParts {
-  float cdf;   // Φ(z)
-  float expo;  // e^{-z²/2}
-};
-
-__device__ __forceinline__ NormalParts normal_parts_fast(float z) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float s = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float poly = fmaf(1.061405429f, s, -1.453152027f);
-  poly = fmaf(poly, s, 1.421413741f);
-  poly = fmaf(poly, s, -0.284496736f);
-  poly = fmaf(poly, s, 0.254829592f);
-  poly *= s;
-  // e^{-z²/2} = 2^{-z²·log2(e)/2}
-  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170f);
-  const float q = 0.5f * poly * e;  // = 1 - Φ(|z|)
-  NormalParts r;
-  r.cdf = (z >= 0.0f) ? 1.0f - q : q;
-  r.expo = e;
-  return r;
-}
-
-__device__ __forceinline__ float gelu_fast(float z) { return z * normal_parts_fast(z).cdf; }
-
-__device__ __forceinline__ float gelu_grad_fast(float z) {
-  NormalParts p = normal_parts_fast(z);
-  return fmaf(z * 0.39894228040143268f, p.expo, p.cdf);
-}
 
 // fp32 path: the device library's erf / exp, for ≤1e-5 parity in fp32.
 __device__ __forceinline__ float gelu_precise(float z) {

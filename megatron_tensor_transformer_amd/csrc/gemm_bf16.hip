@@ -58,6 +58,13 @@ struct KArgs {
   uint32_t a_bytes, b_bytes, c_bytes;
 };
 
+// One launch runs one or two problems of the same operand orders and
+// epilogue: tiles [0, tiles0) belong to p0, [tiles0, total) to p1.
+struct KGroup {
+  KArgs p0, p1;
+  int tiles0, total;
+};
+
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
@@ -233,13 +240,16 @@ struct StepCtx {
   i32x4 rA, rB;
   TPMLP_LDS char* dA;
   TPMLP_LDS char* dB;
-  uint32_t sa, sb, koA, koB;
+  uint32_t sa, sb;    // this step's A and B stages
+  uint32_t nsa, nsb;  // the next step's
+  uint32_t koA, koB;
   int kremA, kremB, wave;
 };
 
 // The 16 MFMAs of slice S, each followed by at most one memory instruction:
-// the reads of slice S+1 (S < 3) and, in slices 0 and 1, the DMA loads of the
-// B operand (next step) and the A operand (the step after).
+// the fragment reads of the next slice (for S = 3, slice 0 of the next step,
+// from its stages), in slice 1 the DMA loads of A two steps ahead and in
+// slice 3 those of B two steps ahead.
 template <int AO, int BO, int S, int Q = 0>
 __device__ __forceinline__ void slice_body(f32x16 (&acc)[4][4], i32x4 (&ca)[4], i32x4 (&cb)[4],
                                            i32x4 (&na)[4], i32x4 (&nb)[4], const uint32_t (&pa)[4],
@@ -249,8 +259,9 @@ __device__ __forceinline__ void slice_body(f32x16 (&acc)[4][4], i32x4 (&ca)[4], 
     TPMLP_MFMA(acc[Q >> 2][Q & 3], cb[Q & 3], ca[Q >> 2]);
     constexpr int NR = reads_per_slice<AO>() + reads_per_slice<BO>();
     if constexpr (S < 3 && Q < NR) next_read<AO, BO, S + 1, Q>(na, nb, pa, pb, s.sa, s.sb);
-    if constexpr (S == 0 && (Q & 1)) dma<BO, (Q >> 1)>(s.rB, s.dB, lb, s.koB, s.kremB, s.wave);
+    if constexpr (S == 3 && Q < NR) next_read<AO, BO, 0, Q>(na, nb, pa, pb, s.nsa, s.nsb);
     if constexpr (S == 1 && (Q & 1)) dma<AO, (Q >> 1)>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
+    if constexpr (S == 3 && (Q & 1)) dma<BO, (Q >> 1)>(s.rB, s.dB, lb, s.koB, s.kremB, s.wave);
     slice_body<AO, BO, S, Q + 1>(acc, ca, cb, na, nb, pa, pb, la, lb, s);
   }
 }
@@ -259,12 +270,18 @@ __device__ __forceinline__ void slice_body(f32x16 (&acc)[4][4], i32x4 (&ca)[4], 
 // (workgroups are dealt to the 8 XCDs round-robin and each XCD has its own
 // L2), and inside a range tiles go in groups of 4 tile rows so that the 32
 // tiles an XCD runs at once share 4 A panels and 8 B panels.
-__device__ __forceinline__ void tile_coords(int wg, const KArgs& a, int& batch, int& tm, int& tn) {
-  const int per_batch = a.tiles_m * a.tiles_n;
-  const int total = per_batch * a.batch;
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
+// workgroup w runs on XCD w % 8.  Each XCD is given a contiguous range of the
+// logical tile order, and within a problem's batch the tiles go in groups of GM
+// tile rows, so the workgroups resident on one XCD share operand panels in its L2.
+__device__ __forceinline__ int logical_tile(int wg, int total) {
   const int q = total >> 3, r = total & 7;
   const int xcd = wg & 7, local = wg >> 3;
-  const int tile = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+__device__ __forceinline__ void tile_coords(int tile, const KArgs& a, int& batch, int& tm, int& tn) {
+  const int per_batch = a.tiles_m * a.tiles_n;
   batch = tile / per_batch;
   const int t2 = tile - batch * per_batch;
   constexpr int GM = 4;
@@ -292,13 +309,16 @@ __device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk
 }
 
 template <int AO, int BO, int EPI>
-__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KArgs a) {
+__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
+  const int tile = logical_tile(blockIdx.x, g.total);
+  const bool second = tile >= g.tiles0;
+  const KArgs& a = second ? g.p1 : g.p0;
   int batch, tm, tn;
-  tile_coords(blockIdx.x, a, batch, tm, tn);
+  tile_coords(second ? tile - g.tiles0 : tile, a, batch, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -320,46 +340,61 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int KT = (a.K + BK - 1) / BK;
+  // Stages: A is triple-buffered (step kt in A stage kt % 3), B double-buffered
+  // (B stage kt % 2).  The DMA loads run two steps ahead: A(kt+2) is issued in
+  // slice 1 of step kt, into the stage step kt-1 used; B(kt+2) in slice 3 of
+  // step kt, into the stage step kt used.  Each step has one barrier, between
+  // slices 2 and 3: every fragment of the step is in registers by then, so
+  // the barrier both frees the step's stages and (after this wave's wait for
+  // B(kt+1), A(kt+1)) publishes the next step's, whose slice 0 is read while
+  // slice 3's MFMAs run.
+  i32x4 fa0[4], fb0[4], fa1[4], fb1[4];
   if (KT > 0) {
-    // prologue: A(0), B(0), then A(1); wait for the first two
+    // prologue: A(0), B(0), A(1), B(1); wait for the first two
     dma_all<AO>(rA, lds, la, 0, a.K, wave);
     dma_all<BO>(rB, lds + B_BASE, lb, 0, a.K, wave);
     dma_all<AO>(rA, lds + TILE_BYTES, la, la.kstep, a.K - BK, wave);
-    wait_vmcnt<8>();
+    dma_all<BO>(rB, lds + B_BASE + TILE_BYTES, lb, lb.kstep, a.K - BK, wave);
+    wait_vmcnt<16>();
     block_barrier();
+    read_slice<AO, BO, 0>(fa0, fb0, pa, pb, lds_base, lds_base + B_BASE);
+    wait_frags(fa0, fb0);
   }
 
   int sA = 0;  // A stage of step kt (= kt % 3)
   for (int kt = 0; kt < KT; ++kt) {
+    const int sA1 = sA == 2 ? 0 : sA + 1;  // (kt + 1) % 3
     const int sA2 = sA == 0 ? 2 : sA - 1;  // (kt + 2) % 3
     StepCtx s;
     s.rA = rA;
     s.rB = rB;
     s.sa = lds_base + sA * TILE_BYTES;
     s.sb = lds_base + B_BASE + (kt & 1) * TILE_BYTES;
+    s.nsa = lds_base + sA1 * TILE_BYTES;
+    s.nsb = lds_base + B_BASE + ((kt + 1) & 1) * TILE_BYTES;
     s.dA = lds + sA2 * TILE_BYTES;
-    s.dB = lds + B_BASE + ((kt + 1) & 1) * TILE_BYTES;
+    s.dB = lds + B_BASE + (kt & 1) * TILE_BYTES;
     s.koA = static_cast<uint32_t>(kt + 2) * la.kstep;
-    s.koB = static_cast<uint32_t>(kt + 1) * lb.kstep;
+    s.koB = static_cast<uint32_t>(kt + 2) * lb.kstep;
     s.kremA = a.K - (kt + 2) * BK;
-    s.kremB = a.K - (kt + 1) * BK;
+    s.kremB = a.K - (kt + 2) * BK;
     s.wave = wave;
 
-    i32x4 fa0[4], fb0[4], fa1[4], fb1[4];
-    read_slice<AO, BO, 0>(fa0, fb0, pa, pb, s.sa, s.sb);
-    wait_frags(fa0, fb0);
     slice_body<AO, BO, 0>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
     wait_frags(fa1, fb1);
     slice_body<AO, BO, 1>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
     wait_frags(fa0, fb0);
     slice_body<AO, BO, 2>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
     wait_frags(fa1, fb1);
-    slice_body<AO, BO, 3>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
     // B(kt+1) and A(kt+1) have landed (this wave's share); A(kt+2) may still
-    // be in flight.  The barrier publishes them and frees this step's stages.
+    // be in flight.
     wait_vmcnt<8>();
     block_barrier();
-    sA = sA == 2 ? 0 : sA + 1;
+    slice_body<AO, BO, 3>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
+    // the next step's slice-0 fragments (unused after the last step) must
+    // have landed before their registers are touched again
+    wait_frags(fa0, fb0);
+    sA = sA1;
   }
   wait_vmcnt<0>();
   // The accumulators were last written by inline-asm MFMAs: give the MFMA
@@ -418,7 +453,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KArgs a) {
 
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-      // accumulators -> bf16 -> staging quadrant, one 32-row block at a time
+      // accumulators -> bf16 -> staging quadrant, one 32×32 block at a time
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         i32x2 zr[4][4];
@@ -439,25 +474,29 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // The block's 16 accumulators are read in program order (volatile
+          // asm keeps them behind the previous block's LDS writes), so only
+          // one block is live in VGPRs and its 16 independent GeLU chains
+          // interleave to cover the VALU latency.
+          float v[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[i][j][e]));
+          if constexpr (EPI == EPI_GELU_ZY) {
+            if (pass == 1) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) v[e] = gelu_fast(v[e]);
+            }
+          } else if constexpr (EPI == EPI_GELU_GRAD) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bf16x4 z = __builtin_bit_cast(bf16x4, zr[j][q]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[4 * q + e] *= gelu_grad_fast(bf2f(z[e]));
+            }
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-            float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-            if constexpr (EPI == EPI_GELU_ZY) {
-              if (pass == 1) {
-                v0 = gelu_fast(v0);
-                v1 = gelu_fast(v1);
-                v2 = gelu_fast(v2);
-                v3 = gelu_fast(v3);
-              }
-            } else if constexpr (EPI == EPI_GELU_GRAD) {
-              const bf16x4 z = __builtin_bit_cast(bf16x4, zr[j][q]);
-              v0 *= gelu_grad_fast(bf2f(z[0]));
-              v1 *= gelu_grad_fast(bf2f(z[1]));
-              v2 *= gelu_grad_fast(bf2f(z[2]));
-              v3 *= gelu_grad_fast(bf2f(z[3]));
-            }
-            const i32x2 pk = pack4_bf16(v0, v1, v2, v3);
+            const i32x2 pk = pack4_bf16(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
             asm volatile("ds_write_b64 %0, %1" ::"v"(quad_addr(qbase, i * 32 + row_l, j * 4 + q, half)),
                          "v"(pk)
                          : "memory");
@@ -492,9 +531,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KArgs a) {
 }
 
 template <int AO, int BO, int EPI>
-hipError_t launch_t(const KArgs& k, hipStream_t stream) {
-  dim3 grid(k.tiles_m * k.tiles_n * k.batch);
-  hipLaunchKernelGGL((gemm_bf16_kernel<AO, BO, EPI>), grid, dim3(NTHR), 0, stream, k);
+hipError_t launch_t(const KGroup& g, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<AO, BO, EPI>), dim3(g.total), dim3(NTHR), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -506,11 +544,8 @@ uint32_t extent_bytes(int order, int rows, int K, int64_t ld) {
   return static_cast<uint32_t>(elems * 2);
 }
 
-}  // namespace
 
-hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int epi,
-                            hipStream_t stream) {
-  if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
+KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
   KArgs k;
   k.A = static_cast<const bf16*>(p.A);
   k.B = static_cast<const bf16*>(p.B);
@@ -532,17 +567,47 @@ hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int 
   k.a_bytes = extent_bytes(a_order, p.M, p.K, p.lda);
   k.b_bytes = extent_bytes(b_order, p.N, p.K, p.ldb);
   k.c_bytes = static_cast<uint32_t>(((static_cast<int64_t>(p.M) - 1) * p.ldc + p.N) * 2);
+  return k;
+}
+
+bool empty(const GemmProblem& p) { return p.M <= 0 || p.N <= 0 || p.batch <= 0; }
+
+int64_t tiles_of(const GemmProblem& p) {
+  return empty(p) ? 0 : static_cast<int64_t>((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_group(const GemmProblem* probs, int count, int a_order, int b_order, int epi,
+                                  hipStream_t stream) {
+  if (probs == nullptr || count < 1 || count > 2) return hipErrorInvalidValue;
+  const GemmProblem* live[2];
+  int nlive = 0;
+  for (int i = 0; i < count; ++i)
+    if (!empty(probs[i])) live[nlive++] = &probs[i];
+  if (nlive == 0) return hipSuccess;
+  const int64_t t0 = tiles_of(*live[0]), t1 = nlive > 1 ? tiles_of(*live[1]) : 0;
+  if (t0 + t1 > 0x7fffffff) return hipErrorInvalidValue;
+  KGroup g;
+  g.p0 = kargs(*live[0], a_order, b_order);
+  g.p1 = nlive > 1 ? kargs(*live[1], a_order, b_order) : g.p0;
+  g.tiles0 = static_cast<int>(t0);
+  g.total = static_cast<int>(t0 + t1);
   if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_GELU_ZY)
-    return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY>(k, stream);
+    return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
   if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_STORE)
-    return launch_t<KMAJ, MNMAJ, EPI_STORE>(k, stream);
+    return launch_t<KMAJ, MNMAJ, EPI_STORE>(g, stream);
   if (a_order == KMAJ && b_order == KMAJ && epi == EPI_GELU_GRAD)
-    return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD>(k, stream);
+    return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
   if (a_order == KMAJ && b_order == KMAJ && epi == EPI_STORE)
-    return launch_t<KMAJ, KMAJ, EPI_STORE>(k, stream);
+    return launch_t<KMAJ, KMAJ, EPI_STORE>(g, stream);
   if (a_order == MNMAJ && b_order == MNMAJ && epi == EPI_STORE_F32)
-    return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32>(k, stream);
+    return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int epi, hipStream_t stream) {
+  return launch_gemm_bf16_group(&p, 1, a_order, b_order, epi, stream);
 }
 
 }  // namespace tpmlp

@@ -36,6 +36,11 @@ struct GemmProblem {
 // bf16 inputs, fp32 accumulation (MFMA).  Returns a hipError_t.
 hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int epi,
                             hipStream_t stream);
+// Two problems with the same operand orders and epilogue in one launch (their
+// tiles share one grid, so the tail of one fills the machine with the other).
+// Empty problems are skipped; count is 1 or 2.
+hipError_t launch_gemm_bf16_group(const GemmProblem* probs, int count, int a_order, int b_order, int epi,
+                                  hipStream_t stream);
 // fp32 throughout.
 hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int epi,
                            hipStream_t stream);
