@@ -10,10 +10,12 @@
 //   gfx950 transposing LDS read (ds_read_b64_tr_b16), so no operand is ever
 //   transposed in HBM.
 //
-// Tiling: 256×256 macro tile, K step 64, 4 waves (2×2), each wave owning a
-// 128×128 sub-tile as 4×4 MFMA blocks of 32×32 (256 fp32 accumulators per
-// lane, in AGPRs).  The B fragment is the MFMA's first operand, so each lane
-// ends up holding 4 consecutive output columns of one row.
+// Tiling: 256×256 macro tile, K step 64, 8 waves (2×4), each wave owning a
+// 128×64 sub-tile as 4×2 MFMA blocks of 32×32 (128 fp32 accumulators per
+// lane, in AGPRs).  Two waves share each SIMD, so when one waits (an LDS read,
+// a DMA issue held up by a full address queue, the barrier) the other keeps
+// the matrix core busy.  The B fragment is the MFMA's first operand, so each
+// lane ends up holding 4 consecutive output columns of one row.
 //
 // Global→LDS: buffer_load … lds (16 B per lane; edges zero-filled by the
 // buffer descriptor's range check, so one code path serves every shape).  The
@@ -23,14 +25,13 @@
 // frees the ones just consumed.
 //
 // The K-step body is a fixed interleaving written as inline asm, so that the
-// compiler keeps it: each of the 64 MFMAs of a step is followed by at most one
-// memory instruction (a fragment read for the next 16-wide K slice, or a DMA
-// load for a later step), so no burst of memory instructions stalls the
-// in-order MFMA issue of the single wave per SIMD.  Fragment registers are
+// compiler keeps it: the 32 MFMAs of a wave's step are each followed by at most
+// a fragment read for the next 16-wide K slice and a DMA load for a later
+// step, so memory instructions never come in bursts.  Fragment registers are
 // double-buffered across K slices; the lgkmcnt waits carry them as operands.
 //
-// Epilogue: bf16 outputs are staged through LDS (each wave its own 128×128
-// quadrant) and written with coalesced 16-B stores; fp32 outputs are written
+// Epilogue: bf16 outputs are staged through LDS (each wave its own 128×64
+// region) and written with coalesced 16-B stores; fp32 outputs are written
 // straight from the accumulators as 16-B stores.
 #include "common.h"
 #include "kernels.h"
@@ -38,7 +39,9 @@
 namespace tpmlp {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
+constexpr int BM = 256, BN = 256, BK = 64, NWAVE = 8, NTHR = NWAVE * 64;
+constexpr int FA = 4, FB = 2;           // 32-row fragments per wave: 128 rows of A, 64 columns of B
+constexpr int NLOAD = 32 / NWAVE;      // 1-KiB DMA loads per wave per operand stage
 constexpr int TILE_BYTES = 256 * BK * 2;  // one operand stage, 32 KiB
 constexpr int A_STAGES = 3, B_STAGES = 2;
 constexpr int B_BASE = A_STAGES * TILE_BYTES;
@@ -80,12 +83,12 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 //   of two 16-lane transposing reads then cover 4 k-rows × 64 B = 256 B once.
 // ---------------------------------------------------------------------------
 
-// Per-lane DMA offsets for one operand: the 8 loads a wave issues per stage.
-// base[j] is the byte offset of the lane's 16-B chunk at k0 = 0 (OOB when the
-// row lies past the matrix edge); the k part is added per step.  kq / kq_odd
-// are the lane's k offset inside the step, for the K-edge test.
+// Per-lane DMA offsets for one operand: the NLOAD loads a wave issues per
+// stage.  base[j] is the byte offset of the lane's 16-B chunk at k0 = 0 (OOB
+// when the row lies past the matrix edge); the k part is added per step.
+// kq / kq_odd are the lane's k offset inside the step, for the K-edge test.
 struct LoadPlan {
-  uint32_t base[8];
+  uint32_t base[NLOAD];
   uint32_t kstep;  // bytes to add per K step (64 k)
   int kq;
   int kq_odd;
@@ -95,23 +98,24 @@ template <int ORDER>
 __device__ __forceinline__ LoadPlan make_plan(int r0, int R, int64_t ld, int wave, int lane) {
   LoadPlan p;
   if constexpr (ORDER == KMAJ) {
-    // load j: rows wave·64 + 8j .. +7; lane: row + lane/8, slot lane%8
+    // load j: rows (NLOAD·wave + j)·8 .. +7; lane: row + lane/8, slot lane%8
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = wave * 64 + j * 8 + (lane >> 3);
+    for (int j = 0; j < NLOAD; ++j) {
+      const int row = (wave * NLOAD + j) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((row >> 1) & 7);
       const int gr = r0 + row;
       p.base[j] = gr < R ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + c * 8) * 2) : OOB;
     }
     p.kstep = BK * 2;
-    // (row >> 1) & 7 = (4j + lane/16) & 7 only depends on the parity of j
+    // (row >> 1) & 7 = (4·(NLOAD·wave + j) + lane/16) & 7 only depends on
+    // the parity of j (NLOAD is even)
     p.kq = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
     p.kq_odd = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
   } else {
-    // load j: column block (wave·8+j)/4, k-rows 16·(j%4) + lane/4
+    // load j: column block seg/4, k-rows 16·(seg%4) + lane/4, seg = NLOAD·wave + j
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int seg = wave * 8 + j;
+    for (int j = 0; j < NLOAD; ++j) {
+      const int seg = wave * NLOAD + j;
       const int blk = seg >> 2;
       const int kr = (seg & 3) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ (((kr >> 1) & 1) << 1);
@@ -136,16 +140,14 @@ __device__ __forceinline__ void dma(i32x4 rsrc, TPMLP_LDS char* tile, const Load
   else
     ok = (J & 3) * 16 + p.kq < krem;
   const uint32_t voff = ok ? p.base[J] + koff : OOB;
-  if constexpr (ORDER == KMAJ)
-    buffer_load_lds16(rsrc, tile + (wave * 64 + J * 8) * 128, voff);
-  else
-    buffer_load_lds16(rsrc, tile + (wave * 8 + J) * 1024, voff);
+  // both layouts: load (NLOAD·wave + J) fills the tile's 1-KiB segment of that index
+  buffer_load_lds16(rsrc, tile + (wave * NLOAD + J) * 1024, voff);
 }
 
 template <int ORDER, int J = 0>
 __device__ __forceinline__ void dma_all(i32x4 rsrc, TPMLP_LDS char* tile, const LoadPlan& p, uint32_t koff,
                                         int krem, int wave) {
-  if constexpr (J < 8) {
+  if constexpr (J < NLOAD) {
     dma<ORDER, J>(rsrc, tile, p, koff, krem, wave);
     dma_all<ORDER, J + 1>(rsrc, tile, p, koff, krem, wave);
   }
@@ -177,15 +179,16 @@ __device__ __forceinline__ void frag_addr(uint32_t (&f)[4], int rbase, int lane)
   }
 }
 
-template <int ORDER>
+// LDS read instructions per K slice for NF fragments
+template <int ORDER, int NF>
 constexpr int reads_per_slice() {
-  return ORDER == KMAJ ? 4 : 8;
+  return ORDER == KMAJ ? NF : 2 * NF;
 }
 
 // Read op T of one operand for K slice KS.  KMAJ: op T is fragment T.  MNMAJ:
 // op T is half T&1 (k 0-3 / 4-7 of the lane's 8) of fragment T>>1.
-template <int ORDER, int KS, int T>
-__device__ __forceinline__ void read_op(i32x4 (&fr)[4], const uint32_t (&f)[4], uint32_t stage) {
+template <int ORDER, int KS, int T, int NF>
+__device__ __forceinline__ void read_op(i32x4 (&fr)[NF], const uint32_t (&f)[4], uint32_t stage) {
   if constexpr (ORDER == KMAJ) {
     const uint32_t a = f[KS] + stage;
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fr[T]) : "v"(a), "i"(T * 4096));
@@ -207,20 +210,22 @@ __device__ __forceinline__ void read_op(i32x4 (&fr)[4], const uint32_t (&f)[4], 
 
 // Wait until no LDS read is outstanding; the fragment registers are in/out
 // operands so no use of them can be placed above the wait.
-__device__ __forceinline__ void wait_frags(i32x4 (&a)[4], i32x4 (&b)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
-                 "+v"(b[3]));
+__device__ __forceinline__ void wait_frags(i32x4 (&a)[FA], i32x4 (&b)[FB]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
 }
 
 #define TPMLP_MFMA(ACC, BF, AF) \
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(ACC) : "v"(BF), "v"(AF))
 
+constexpr int n_reads(int ao, int bo) {
+  return (ao == KMAJ ? FA : 2 * FA) + (bo == KMAJ ? FB : 2 * FB);
+}
+
 // One read op for the next slice, from the merged A-then-B op list.
 template <int AO, int BO, int KS, int T>
-__device__ __forceinline__ void next_read(i32x4 (&fa)[4], i32x4 (&fb)[4], const uint32_t (&pa)[4],
+__device__ __forceinline__ void next_read(i32x4 (&fa)[FA], i32x4 (&fb)[FB], const uint32_t (&pa)[4],
                                           const uint32_t (&pb)[4], uint32_t sa, uint32_t sb) {
-  constexpr int NA = reads_per_slice<AO>();
+  constexpr int NA = reads_per_slice<AO, FA>();
   if constexpr (T < NA)
     read_op<AO, KS, T>(fa, pa, sa);
   else
@@ -228,9 +233,9 @@ __device__ __forceinline__ void next_read(i32x4 (&fa)[4], i32x4 (&fb)[4], const 
 }
 
 template <int AO, int BO, int KS, int T = 0>
-__device__ __forceinline__ void read_slice(i32x4 (&fa)[4], i32x4 (&fb)[4], const uint32_t (&pa)[4],
+__device__ __forceinline__ void read_slice(i32x4 (&fa)[FA], i32x4 (&fb)[FB], const uint32_t (&pa)[4],
                                            const uint32_t (&pb)[4], uint32_t sa, uint32_t sb) {
-  if constexpr (T < reads_per_slice<AO>() + reads_per_slice<BO>()) {
+  if constexpr (T < n_reads(AO, BO)) {
     next_read<AO, BO, KS, T>(fa, fb, pa, pb, sa, sb);
     read_slice<AO, BO, KS, T + 1>(fa, fb, pa, pb, sa, sb);
   }
@@ -246,30 +251,28 @@ struct StepCtx {
   int kremA, kremB, wave;
 };
 
-// The 16 MFMAs of slice S, each followed by at most one memory instruction:
-// the fragment reads of the next slice (for S = 3, slice 0 of the next step,
-// from its stages), in slice 1 the DMA loads of A two steps ahead and in
-// slice 3 those of B two steps ahead.
+// The 8 MFMAs of slice S.  After MFMA Q come the next slice's reads Q and
+// Q + 8 (for S = 3, slice 0 of the next step, from its stages) and, at odd Q,
+// one DMA load: in slice 1 of A two steps ahead, in slice 3 of B two steps
+// ahead.
 template <int AO, int BO, int S, int Q = 0>
-__device__ __forceinline__ void slice_body(f32x16 (&acc)[4][4], i32x4 (&ca)[4], i32x4 (&cb)[4],
-                                           i32x4 (&na)[4], i32x4 (&nb)[4], const uint32_t (&pa)[4],
+__device__ __forceinline__ void slice_body(f32x16 (&acc)[FA][FB], i32x4 (&ca)[FA], i32x4 (&cb)[FB],
+                                           i32x4 (&na)[FA], i32x4 (&nb)[FB], const uint32_t (&pa)[4],
                                            const uint32_t (&pb)[4], const LoadPlan& la, const LoadPlan& lb,
                                            const StepCtx& s) {
-  if constexpr (Q < 16) {
-    TPMLP_MFMA(acc[Q >> 2][Q & 3], cb[Q & 3], ca[Q >> 2]);
-    constexpr int NR = reads_per_slice<AO>() + reads_per_slice<BO>();
+  if constexpr (Q < 8) {
+    TPMLP_MFMA(acc[Q >> 1][Q & 1], cb[Q & 1], ca[Q >> 1]);
+    constexpr int NR = n_reads(AO, BO);
     if constexpr (S < 3 && Q < NR) next_read<AO, BO, S + 1, Q>(na, nb, pa, pb, s.sa, s.sb);
     if constexpr (S == 3 && Q < NR) next_read<AO, BO, 0, Q>(na, nb, pa, pb, s.nsa, s.nsb);
+    if constexpr (S < 3 && Q + 8 < NR) next_read<AO, BO, S + 1, Q + 8>(na, nb, pa, pb, s.sa, s.sb);
+    if constexpr (S == 3 && Q + 8 < NR) next_read<AO, BO, 0, Q + 8>(na, nb, pa, pb, s.nsa, s.nsb);
     if constexpr (S == 1 && (Q & 1)) dma<AO, (Q >> 1)>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
     if constexpr (S == 3 && (Q & 1)) dma<BO, (Q >> 1)>(s.rB, s.dB, lb, s.koB, s.kremB, s.wave);
     slice_body<AO, BO, S, Q + 1>(acc, ca, cb, na, nb, pa, pb, la, lb, s);
   }
 }
 
-// Tile order: the tiles one XCD works on form one contiguous range
-// (workgroups are dealt to the 8 XCDs round-robin and each XCD has its own
-// L2), and inside a range tiles go in groups of 4 tile rows so that the 32
-// tiles an XCD runs at once share 4 A panels and 8 B panels.
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
 // workgroup w runs on XCD w % 8.  Each XCD is given a contiguous range of the
 // logical tile order, and within a problem's batch the tiles go in groups of GM
@@ -302,10 +305,11 @@ __device__ __forceinline__ i32x2 pack4_bf16(float a, float b, float c, float d) 
   return __builtin_bit_cast(i32x2, v);
 }
 
-// Epilogue staging quadrant (per wave, 128 rows × 128 columns of bf16, 256 B
-// per row): chunk c (8 columns) of row r sits at slot c ^ (r & 15).
+// Epilogue staging region (per wave, 128 rows × 64 columns of bf16, 128 B per
+// row): chunk c (8 columns) of row r sits at slot c ^ (r & 7).
+constexpr int QROW = 128, QBYTES = 128 * QROW;
 __device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk, int half) {
-  return qbase + row * 256 + ((chunk ^ (row & 15)) << 4) + half * 8;
+  return qbase + row * QROW + ((chunk ^ (row & 7)) << 4) + half * 8;
 }
 
 template <int AO, int BO, int EPI>
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   tile_coords(second ? tile - g.tiles0 : tile, a, batch, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   const i32x4 rA = make_rsrc(a.A + batch * a.sA, a.a_bytes);
   const i32x4 rB = make_rsrc(a.B + batch * a.sB, a.b_bytes);
@@ -329,13 +333,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   const LoadPlan lb = make_plan<BO>(n0, a.N, a.ldb, wave, lane);
   uint32_t pa[4], pb[4];
   frag_addr<AO>(pa, wm * 128, lane);
-  frag_addr<BO>(pb, wn * 128, lane);
+  frag_addr<BO>(pb, wn * 64, lane);
 
-  f32x16 acc[4][4];
+  f32x16 acc[FA][FB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -348,14 +352,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   // the barrier both frees the step's stages and (after this wave's wait for
   // B(kt+1), A(kt+1)) publishes the next step's, whose slice 0 is read while
   // slice 3's MFMAs run.
-  i32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  i32x4 fa0[FA], fb0[FB], fa1[FA], fb1[FB];
   if (KT > 0) {
     // prologue: A(0), B(0), A(1), B(1); wait for the first two
     dma_all<AO>(rA, lds, la, 0, a.K, wave);
     dma_all<BO>(rB, lds + B_BASE, lb, 0, a.K, wave);
     dma_all<AO>(rA, lds + TILE_BYTES, la, la.kstep, a.K - BK, wave);
     dma_all<BO>(rB, lds + B_BASE + TILE_BYTES, lb, lb.kstep, a.K - BK, wave);
-    wait_vmcnt<16>();
+    wait_vmcnt<2 * NLOAD>();
     block_barrier();
     read_slice<AO, BO, 0>(fa0, fb0, pa, pb, lds_base, lds_base + B_BASE);
     wait_frags(fa0, fb0);
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
     wait_frags(fa1, fb1);
     // B(kt+1) and A(kt+1) have landed (this wave's share); A(kt+2) may still
     // be in flight.
-    wait_vmcnt<8>();
+    wait_vmcnt<NLOAD>();
     block_barrier();
     slice_body<AO, BO, 3>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
     // the next step's slice-0 fragments (unused after the last step) must
@@ -403,19 +407,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
 
   // ------------------------------------------------------------------ epilogue
   // Accumulator v of block (i, j) of lane L: row wm·128 + 32i + L%32,
-  // columns wn·128 + 32j + 8·(v/4) + 4·(L/32) + v%4.
+  // columns wn·64 + 32j + 8·(v/4) + 4·(L/32) + v%4.
   const int row_l = lane & 31, half = lane >> 5;
   if constexpr (EPI == EPI_STORE_F32) {
     float* C = static_cast<float*>(a.C) + static_cast<int64_t>(batch) * a.sC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FA; ++i) {
       const int row = m0 + wm * 128 + i * 32 + row_l;
       if (row >= a.M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < FB; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 128 + j * 32 + q * 8 + half * 4;
+          const int col = n0 + wn * 64 + j * 32 + q * 8 + half * 4;
           if (col < a.N) {
             f32x4 v;
             v[0] = acc[i][j][4 * q + 0];
@@ -429,37 +433,37 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
     }
   } else {
     block_barrier();  // every wave is done with the main-loop stages
-    const uint32_t qbase = lds_base + wave * 32768;
+    const uint32_t qbase = lds_base + wave * QBYTES;
     const int64_t cbase = static_cast<int64_t>(batch) * a.sC;
-    const int qm0 = m0 + wm * 128, qn0 = n0 + wn * 128;
+    const int qm0 = m0 + wm * 128, qn0 = n0 + wn * 64;
     constexpr int PASSES = EPI == EPI_GELU_ZY ? 2 : 1;
 
     if constexpr (EPI == EPI_GELU_GRAD) {
-      // Stage this quadrant's stored Z (same layout) with 16-B DMA loads:
-      // load j covers rows 4j..4j+3; lane: row 4j + L/16, slot L%16.
+      // Stage this region's stored Z (same layout) with 16-B DMA loads:
+      // load j covers rows 8j..8j+7; lane: row 8j + L/8, slot L%8.
       const i32x4 rZ = make_rsrc(a.Zin + cbase, a.c_bytes);
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int row = j * 4 + (lane >> 4);
-        const int c = (lane & 15) ^ (row & 15);
+      for (int j = 0; j < 16; ++j) {
+        const int row = j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (row & 7);
         const int gr = qm0 + row, gc = qn0 + c * 8;
         const uint32_t voff = (gr < a.M && gc < a.N)
                                   ? static_cast<uint32_t>((static_cast<int64_t>(gr) * a.ldc + gc) * 2)
                                   : OOB;
-        buffer_load_lds16(rZ, lds + wave * 32768 + j * 1024, voff);
+        buffer_load_lds16(rZ, lds + wave * QBYTES + j * 1024, voff);
       }
       wait_vmcnt<0>();
     }
 
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-      // accumulators -> bf16 -> staging quadrant, one 32×32 block at a time
+      // accumulators -> bf16 -> staging region, one 32×32 block at a time
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        i32x2 zr[4][4];
+      for (int i = 0; i < FA; ++i) {
+        i32x2 zr[FB][4];
         if constexpr (EPI == EPI_GELU_GRAD) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < FB; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               asm volatile("ds_read_b64 %0, %1"
@@ -468,12 +472,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
           // the Z registers are operands of the wait: no use moves above it
           asm volatile("s_waitcnt lgkmcnt(0)"
                        : "+v"(zr[0][0]), "+v"(zr[0][1]), "+v"(zr[0][2]), "+v"(zr[0][3]), "+v"(zr[1][0]),
-                         "+v"(zr[1][1]), "+v"(zr[1][2]), "+v"(zr[1][3]), "+v"(zr[2][0]), "+v"(zr[2][1]),
-                         "+v"(zr[2][2]), "+v"(zr[2][3]), "+v"(zr[3][0]), "+v"(zr[3][1]), "+v"(zr[3][2]),
-                         "+v"(zr[3][3])::"memory");
+                         "+v"(zr[1][1]), "+v"(zr[1][2]), "+v"(zr[1][3])::"memory");
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FB; ++j) {
           // The block's 16 accumulators are read in program order (volatile
           // asm keeps them behind the previous block's LDS writes), so only
           // one block is live in VGPRs and its 16 independent GeLU chains
@@ -504,15 +506,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // staging quadrant -> global: 4 rows × 256 B per wave-wide 16-B access
+      // staging region -> global: 8 rows × 128 B per wave-wide 16-B access
       bf16* C = static_cast<bf16*>(pass == 0 ? a.C : a.C2) + cbase;
 #pragma unroll
-      for (int it0 = 0; it0 < 32; it0 += 8) {
+      for (int it0 = 0; it0 < 16; it0 += 8) {
         i32x4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int row = (it0 + u) * 4 + (lane >> 4);
-          const uint32_t ad = qbase + row * 256 + (((lane & 15) ^ (row & 15)) << 4);
+          const int row = (it0 + u) * 8 + (lane >> 3);
+          const uint32_t ad = qbase + row * QROW + (((lane & 7) ^ (row & 7)) << 4);
           asm volatile("ds_read_b128 %0, %1" : "=v"(v[u]) : "v"(ad) : "memory");
         }
         asm volatile("s_waitcnt lgkmcnt(0)"
@@ -520,8 +522,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
                        "+v"(v[7])::"memory");
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int row = (it0 + u) * 4 + (lane >> 4);
-          const int gr = qm0 + row, gc = qn0 + (lane & 15) * 8;
+          const int row = (it0 + u) * 8 + (lane >> 3);
+          const int gr = qm0 + row, gc = qn0 + (lane & 7) * 8;
           if (gr < a.M && gc < a.N)
             *reinterpret_cast<i32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc) = v[u];
         }
