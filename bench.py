@@ -11,9 +11,16 @@ fp32 accumulation; all 8 shards resident on the one GPU and summed locally.
 FLOPs per step = 6 GEMMs × 2·n·d·m_i × t = 12·n·d·m_i·t (GeLU math and the
 reductions are not counted).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 
-Prints one JSON line.
+Prints one JSON line.  Besides the headline step it reports (unless
+--no-extra): the per-rank rate (one shard per launch, t_local = 1, as one TP
+rank runs it), the GPT-1T-shaped shard (n = 2048, d = 25600, m_i = 12800, one
+shard), and the sequence-parallel region's memory-bound kernels on the
+h = 4096 block (LN forward, reduce + dropout + residual, dropout backward,
+LN backward with the fused dU reduce) in GB/s against 8 TB/s, each timed
+after writing a 512 MiB scratch buffer so the 256 MiB last-level cache holds
+none of its inputs.
 """
 
 import argparse
@@ -34,9 +41,10 @@ WORKLOAD = "gpt8p3b_t8"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-rank, GPT-1T-shard and SP legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -76,6 +84,106 @@ def cpu_baseline(inp, t, budget_s):
             "sample": f"{shards} whole-shard passes (of {t} shards), full n={n}: fp64 NumPy forward + "
                       f"backward ({flops:.3e} FLOP in {el:.1f} s); host logical CPUs {os.cpu_count()}, "
                       f"affinity {len(os.sched_getaffinity(0))}"}
+
+
+def _stats(ms):
+    import numpy as np
+    return {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(np.min(ms)), 4),
+            "max_ms": round(float(np.max(ms)), 4)}
+
+
+def _time_events(fn, reps, before=None):
+    """Run fn() reps times on the current stream, each bracketed by events
+    (before() runs outside the bracket); returns the per-rep milliseconds."""
+    import torch
+    out = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def leg_mlp_shard(tp, n, d, mi, reps, seed):
+    """fwd + bwd GEMMs of one shard per launch (t_local = 1) on seeded device
+    data of the given shape: the rate one TP rank sees."""
+    import torch
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    bf = torch.bfloat16
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(bf)
+
+    X, G = rnd((n, d), 1.0), rnd((n, d), 0.01)
+    A, B = rnd((1, d, mi), 0.02), rnd((1, mi, d), 0.02)
+    Z = torch.empty((1, n, mi), dtype=bf, device=dev)
+    Y, D = torch.empty_like(Z), torch.empty_like(Z)
+    P, dXp = torch.empty((1, n, d), dtype=bf, device=dev), torch.empty((1, n, d), dtype=bf, device=dev)
+    dA = torch.empty((1, d, mi), dtype=torch.float32, device=dev)
+    dB = torch.empty((1, mi, d), dtype=torch.float32, device=dev)
+
+    def run():
+        tp.tpmlp_fwd(X, A, B, Z, Y, P)
+        tp.tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, None)
+
+    for _ in range(3):
+        run()
+    ms = _time_events(run, reps)
+    import numpy as np
+    med = float(np.median(ms))
+    flops = 12.0 * n * d * mi
+    return {"n": n, "d": d, "m_i": mi, "t_local": 1, "flop": flops,
+            "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2), **_stats(ms)}
+
+
+def leg_sp(tp, reps):
+    """The sequence-parallel region's memory-bound kernels on the h = 4096
+    block (s = 4096 tokens, t = 8 shards of 512 rows), each timed alone after
+    a cache flush; algorithmic bytes count each tensor read or written once."""
+    import numpy as np
+    import torch
+    from tpmlp_inputs import CONFIGS
+    cfg = CONFIGS["sp_block_t8"]
+    s, h, t, p = cfg["n"], cfg["d"], cfg["t"], cfg["p"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    bf = torch.bfloat16
+    x = torch.randn((s, h), generator=gen, device=dev).to(bf)
+    gamma = (1 + 0.1 * torch.randn((h,), generator=gen, device=dev)).to(bf)
+    beta = (0.1 * torch.randn((h,), generator=gen, device=dev)).to(bf)
+    parts = torch.randn((t, s, h), generator=gen, device=dev).to(bf)
+    g_out = (0.01 * torch.randn((s, h), generator=gen, device=dev)).to(bf)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def fl():
+        flush.zero_()
+
+    U, mean, rstd = tp.sp_ln_fwd(x, gamma, beta, t)
+    E = 2 * s * h  # bytes of one [s, h] bf16 tensor
+    legs = {
+        "ln_fwd": (lambda: tp.sp_ln_fwd(x, gamma, beta, t), 2 * E + 8 * s),
+        "reduce_dropout_residual_fwd": (lambda: tp.sp_dropres_fwd(parts, x, p, 0), (t + 2) * E),
+        "dropout_bwd": (lambda: tp.sp_dropres_bwd(g_out, t, p, 0), 2 * E),
+        "ln_bwd_with_reduce": (lambda: tp.sp_ln_bwd(parts, g_out, x, gamma, mean, rstd), (t + 3) * E + 8 * s),
+    }
+    out = {}
+    for name, (fn, nbytes) in legs.items():
+        fn()
+        torch.cuda.synchronize()
+        ms = _time_events(fn, reps, before=fl)
+        med = float(np.median(ms))
+        out[name] = {"bytes": nbytes, "gbs_median": round(nbytes / (med * 1e-3) / 1e9, 1),
+                     "frac_of_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), **_stats(ms)}
+    return {"workload": f"sequence-parallel region of the h={h} block: s={s}, t={t}, p={p}, bf16", **out}
 
 
 def recorded_traffic(kernel_file, summary):
@@ -226,6 +334,24 @@ def main():
         "wall_s_timed": round(wall, 3),
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
     }
+    rec["gemm_only"].update({"tflops_median": round(flops / (float(np.median(
+        np.array(fwd_ms) + np.array(bwd_ms))) * 1e-3) / 1e12, 2)})
+    rec["step_ms"] = _stats(step_ms)
+    # the reduce alone, inputs flushed from the last-level cache first
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    red_flushed = _time_events(lambda: tp.tpmlp_reduce_partials(P, O), 10, before=lambda: flush.zero_())
+    del flush
+    rec["roofline_reduce"]["cache_flushed"] = {
+        "gbs_median": round(red_bytes / (float(np.median(red_flushed)) * 1e-3) / 1e9, 1), **_stats(red_flushed)}
+    if not args.no_extra:
+        del Z, Y, P, D, dA, dB, dXp, O, dX
+        torch.cuda.empty_cache()
+        rec["per_rank"] = {"workload": "one shard of the 8.3B-shaped layer per launch (t_local=1)",
+                           **leg_mlp_shard(tp, n, d, mi, 20, seed=1)}
+        rec["gpt1t_shard"] = {"workload": "GPT-1T-shaped shard: h=25600, m_i=12800, n=2048 tokens, one shard",
+                              **leg_mlp_shard(tp, 2048, 25600, 12800, 10, seed=2)}
+        torch.cuda.empty_cache()
+        rec["sp_region"] = leg_sp(tp, 10)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, t, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
