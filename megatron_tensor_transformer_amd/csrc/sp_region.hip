@@ -7,11 +7,14 @@
 //   backward  dS = g_out ⊙ mask / (1-p)      (the MLP's upstream gradient)
 //             dx = g_out + LN'(Σ_i dU_i);  dγ = Σ_rows dU⊙x̂;  dβ = Σ_rows dU
 //
-// All kernels are HBM-bound and work on 8-element (16-B bf16) chunks.  The row
-// kernels give one wavefront per row (h ≤ 4096: a lane owns h/512 chunks held
-// in registers) and reduce with cross-lane shuffles; the dγ/dβ column sums are
-// deterministic: per-block partials in a fixed row order, then a fixed-order
-// sum over blocks.
+// All kernels are HBM-bound and work on 8-element (16-B bf16) chunks; sums of
+// the t partials load them in unconditional groups so the loads are in flight
+// together, and add them in shard order.  The LN kernels work row by row in
+// 512-thread blocks (h ≤ 4096: thread j owns chunk j of every row, held in
+// registers) and reduce with cross-lane shuffles plus a fixed-order sum over
+// the 8 waves.  In LN backward each block walks a strided set of rows,
+// so its dγ/dβ column partials stay in registers; the sums are deterministic:
+// per-block partials in a fixed row order, then a fixed-order sum over blocks.
 //
 // Dropout mask: Philox-4x32-10 (Salmon, Moraes, Dror & Shaw, SC'11), written
 // here from the paper's round function: counter (c0..c3) and key (k0,k1) go to
@@ -27,7 +30,9 @@ namespace {
 
 constexpr int WAVE = 64;
 constexpr int SP_THREADS = 256;   // 4 waves
-constexpr int LNB_ROWS = 32;      // rows per block in the LN backward
+constexpr int LNB_THREADS = 512;  // LN backward block: 8 waves
+constexpr int LNB_WAVES = LNB_THREADS / WAVE;
+constexpr int LNB_MAX_BLOCKS = 512;  // LN backward grid (two blocks per CU), rows strided over it
 
 // ------------------------------------------------------------------ Philox
 __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
@@ -40,8 +45,10 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
       k0 += W0;
       k1 += W1;
     }
-    const uint32_t hi0 = __umulhi(M0, c0), lo0 = M0 * c0;
-    const uint32_t hi1 = __umulhi(M1, c2), lo1 = M1 * c2;
+    // one 32×32→64-bit product each (v_mad_u64_u32) instead of separate hi/lo
+    const uint64_t p0 = static_cast<uint64_t>(M0) * c0, p1 = static_cast<uint64_t>(M1) * c2;
+    const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+    const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -72,18 +79,23 @@ __device__ __forceinline__ uint32_t keep8(uint64_t e0, uint64_t seed, uint32_t t
 }
 
 // ------------------------------------------------------------------ 8-element I/O
-template <typename T>
+// NT: a read-once streaming operand, loaded nontemporally so it does not
+// displace reused data in the caches.
+template <typename T, bool NT = true>
 __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
-    const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 u = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))
+                       : *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v[2 * q] = __uint_as_float(u[q] << 16);
       v[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
     }
   } else {
-    const f32x4 lo = reinterpret_cast<const f32x4*>(p)[0];
-    const f32x4 hi = reinterpret_cast<const f32x4*>(p)[1];
+    const f32x4 lo = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p))
+                        : reinterpret_cast<const f32x4*>(p)[0];
+    const f32x4 hi = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1)
+                        : reinterpret_cast<const f32x4*>(p)[1];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v[q] = lo[q];
@@ -92,12 +104,31 @@ __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void add8(const T* p, float (&v)[8]) {
-  float w[8];
-  load8(p, w);
+// v = Σ_{i<t} p[i·stride .. +7] in shard order.  Whole groups of 8, then 4,
+// then single partials: each group's loads are unconditional, so they are
+// issued back to back and waited for once.
+template <typename T, int G>
+__device__ __forceinline__ void add_group8(const T* p, int64_t stride, float (&v)[8]) {
+  float w[G][8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) v[q] += w[q];
+  for (int u = 0; u < G; ++u) load8(p + static_cast<int64_t>(u) * stride, w[u]);
+#pragma unroll
+  for (int u = 0; u < G; ++u)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] += w[u][k];
+}
+
+template <typename T>
+__device__ __forceinline__ void sum_partials8(const T* p, int64_t stride, int t, float (&v)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = 0.f;
+  int i = 0;
+  for (; i + 8 <= t; i += 8) add_group8<T, 8>(p + static_cast<int64_t>(i) * stride, stride, v);
+  if (i + 4 <= t) {
+    add_group8<T, 4>(p + static_cast<int64_t>(i) * stride, stride, v);
+    i += 4;
+  }
+  for (; i < t; ++i) add_group8<T, 1>(p + static_cast<int64_t>(i) * stride, stride, v);
 }
 
 template <typename T>
@@ -126,59 +157,79 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // ------------------------------------------------------------------ LN forward
-// One wave per row; lane owns chunks q·64 + lane (q < NQ) of the row.
-template <typename T, int NQ>
-__global__ __launch_bounds__(SP_THREADS) void ln_fwd_kernel(SpProblem p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * (SP_THREADS / WAVE) + (threadIdx.x >> 6);
-  if (row >= p.s) return;
-  const int nchunk = static_cast<int>(p.h / 8);
-  const T* x = static_cast<const T*>(p.x) + row * p.h;
-  float v[NQ][8];
-  float sum = 0.f;
+// A 512-thread block normalises rows 2b and 2b+1; thread j owns chunk j of
+// each (h ≤ 4096).  Two passes over the registers (mean, then the biased
+// variance of x - mean), each a wave sum combined over the 8 waves in a fixed
+// order through LDS.
+__device__ __forceinline__ void block_sum2(float (&v)[2], float (*red)[2], int lane, int wave) {
+  v[0] = wave_sum(v[0]);
+  v[1] = wave_sum(v[1]);
+  if (lane == 0) {
+    red[wave][0] = v[0];
+    red[wave][1] = v[1];
+  }
+  __syncthreads();
+  v[0] = v[1] = 0.f;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int c = q * WAVE + lane;
-    if (c < nchunk) {
-      load8(x + c * 8, v[q]);
+  for (int w = 0; w < LNB_WAVES; ++w) {
+    v[0] += red[w][0];
+    v[1] += red[w][1];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(LNB_THREADS) void ln_fwd_kernel(SpProblem p) {
+  __shared__ float red[2][LNB_WAVES][2];  // one buffer per reduction: no barrier between them
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = threadIdx.x;
+  const bool mine = c < p.h / 8;
+  const int64_t r0 = 2 * static_cast<int64_t>(blockIdx.x);
+  const bool two = r0 + 1 < p.s;
+  const T* x0 = static_cast<const T*>(p.x) + r0 * p.h + c * 8;
+  const T* x1 = two ? x0 + p.h : x0;  // a missing second row re-reads the first; dropped below
+  float v[2][8], g[8], b[8];
+  if (mine) {
+    load8(x0, v[0]);
+    load8(x1, v[1]);
+    load8<T, false>(static_cast<const T*>(p.gamma) + c * 8, g);
+    load8<T, false>(static_cast<const T*>(p.beta) + c * 8, b);
+  } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sum += v[q][k];
-    }
+    for (int k = 0; k < 8; ++k) v[0][k] = v[1][k] = 0.f;
   }
   const float inv_h = 1.0f / static_cast<float>(p.h);
-  const float mean = wave_sum(sum) * inv_h;
-  float ss = 0.f;
+  float s[2] = {0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int c = q * WAVE + lane;
-    if (c < nchunk) {
+  for (int k = 0; k < 8; ++k) {
+    s[0] += v[0][k];
+    s[1] += v[1][k];
+  }
+  block_sum2(s, red[0], lane, wave);
+  const float mean[2] = {s[0] * inv_h, s[1] * inv_h};
+  float q[2] = {0.f, 0.f};
+  if (mine) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float d = v[q][k] - mean;
-        ss += d * d;
-      }
+    for (int k = 0; k < 8; ++k) {
+      const float d0 = v[0][k] - mean[0], d1 = v[1][k] - mean[1];
+      q[0] += d0 * d0;
+      q[1] += d1 * d1;
     }
   }
-  const float var = wave_sum(ss) * inv_h;  // biased variance
-  const float rstd = 1.0f / sqrtf(var + p.eps);
-  const T* gam = static_cast<const T*>(p.gamma);
-  const T* bet = static_cast<const T*>(p.beta);
-  T* y = static_cast<T*>(p.ln_out) + row * p.h;
+  block_sum2(q, red[1], lane, wave);
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int c = q * WAVE + lane;
-    if (c < nchunk) {
-      float g[8], b[8], o[8];
-      load8(gam + c * 8, g);
-      load8(bet + c * 8, b);
+  for (int r = 0; r < 2; ++r) {
+    if (r == 1 && !two) break;
+    const float rstd = 1.0f / sqrtf(q[r] * inv_h + p.eps);
+    if (mine) {
+      float o[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = fmaf((v[q][k] - mean) * rstd, g[k], b[k]);
-      store8(y + c * 8, o);
+      for (int k = 0; k < 8; ++k) o[k] = fmaf((v[r][k] - mean[r]) * rstd, g[k], b[k]);
+      store8(static_cast<T*>(p.ln_out) + (r0 + r) * p.h + c * 8, o);
     }
-  }
-  if (lane == 0) {
-    p.mean[row] = mean;
-    p.rstd[row] = rstd;
+    if (threadIdx.x == 0) {
+      p.mean[r0 + r] = mean[r];
+      p.rstd[r0 + r] = rstd;
+    }
   }
 }
 
@@ -191,19 +242,18 @@ __global__ __launch_bounds__(SP_THREADS) void dropres_kernel(SpProblem p) {
   const int64_t step = static_cast<int64_t>(gridDim.x) * SP_THREADS;
   for (int64_t ch = static_cast<int64_t>(blockIdx.x) * SP_THREADS + threadIdx.x; ch < nchunk; ch += step) {
     const int64_t e = ch * 8;  // local element index; rows are contiguous
-    const uint32_t keep = keep8(static_cast<uint64_t>(p.row0 * p.h + e), p.seed, p.drop_threshold);
     float v[8];
     if constexpr (FWD) {
-      const T* part = static_cast<const T*>(p.partials);
-      load8(part + e, v);
-      for (int i = 1; i < p.t; ++i) add8(part + static_cast<int64_t>(i) * count + e, v);
       float xr[8];
-      load8(static_cast<const T*>(p.x) + e, xr);
+      load8(static_cast<const T*>(p.x) + e, xr);  // in flight with the partials
+      sum_partials8(static_cast<const T*>(p.partials) + e, count, p.t, v);
+      const uint32_t keep = keep8(static_cast<uint64_t>(p.row0 * p.h + e), p.seed, p.drop_threshold);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = xr[k] + (((keep >> k) & 1u) ? v[k] * p.keep_scale : 0.0f);
       store8(static_cast<T*>(p.out) + e, v);
     } else {
       load8(static_cast<const T*>(p.g_out) + e, v);
+      const uint32_t keep = keep8(static_cast<uint64_t>(p.row0 * p.h + e), p.seed, p.drop_threshold);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = ((keep >> k) & 1u) ? v[k] * p.keep_scale : 0.0f;
       store8(static_cast<T*>(p.dS) + e, v);
@@ -212,122 +262,126 @@ __global__ __launch_bounds__(SP_THREADS) void dropres_kernel(SpProblem p) {
 }
 
 // ------------------------------------------------------------------ LN backward
-// Block b handles rows [b·LNB_ROWS, ...): wave w takes rows b·LNB_ROWS + w + 4k.
-// Per row: dU = Σ_i dU_i, x̂ = (x-μ)·rstd, g̃ = dU⊙γ,
-// dx = g_out + rstd·(g̃ - mean(g̃) - x̂·mean(g̃⊙x̂)).  Column partials of dU⊙x̂
-// and dU accumulate in registers per lane, then the 4 waves are summed in
-// fixed order through LDS into ws[b][0|1][h].
-template <typename T, int NQ>
-__global__ __launch_bounds__(SP_THREADS) void ln_bwd_kernel(SpProblem p) {
-  extern __shared__ float colsum[];  // [2][h]
+// Block b handles rows b, b + nb, b + 2·nb, ... (nb = gridDim.x); thread j
+// owns chunk j of every row (h ≤ 4096).  Per row: dU = Σ_i dU_i,
+// x̂ = (x-μ)·rstd, g̃ = dU⊙γ, dx = g_out + rstd·(g̃ - mean(g̃) - x̂·mean(g̃⊙x̂));
+// the two row means are wave sums combined over the 8 waves in a fixed order
+// through LDS.  The thread's column partials of dU⊙x̂ and dU go to
+// ws[b][0|1][h] at the end.  Two blocks share a CU, so one's loads are in
+// flight while the other computes.
+template <typename T>
+__global__ __launch_bounds__(LNB_THREADS, 2) void ln_bwd_kernel(SpProblem p) {
+  __shared__ float red[2][LNB_WAVES][2];  // [row parity][wave][s1, s2]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nchunk = static_cast<int>(p.h / 8);
+  const int c = threadIdx.x;
+  const bool mine = c < p.h / 8;
   const int64_t count = p.s * p.h;
+  const int64_t nb = gridDim.x;
   const float inv_h = 1.0f / static_cast<float>(p.h);
-  const T* gam = static_cast<const T*>(p.gamma);
 
-  float gq[NQ][8];
+  float gq[8], dg[8], db[8];
+  if (mine) load8<T, false>(static_cast<const T*>(p.gamma) + c * 8, gq);
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int c = q * WAVE + lane;
-    if (c < nchunk) load8(gam + c * 8, gq[q]);
-  }
-  float dg[NQ][8], db[NQ][8];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) dg[q][k] = db[q][k] = 0.f;
+  for (int k = 0; k < 8; ++k) dg[k] = db[k] = 0.f;
 
-  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * LNB_ROWS;
-  for (int rr = wave; rr < LNB_ROWS; rr += SP_THREADS / WAVE) {
-    const int64_t row = r_begin + rr;
-    if (row >= p.s) break;
+  int par = 0;
+  for (int64_t row = blockIdx.x; row < p.s; row += nb, par ^= 1) {
+    const int64_t off = row * p.h + c * 8;
+    float du[8], xh[8], go[8];
+    float sm[2] = {0.f, 0.f};
     const float mu = p.mean[row], rs = p.rstd[row];
-    const T* dUp = static_cast<const T*>(p.dU_partials) + row * p.h;
-    const T* xr = static_cast<const T*>(p.x) + row * p.h;
-    float du[NQ][8], xh[NQ][8];
-    float s1 = 0.f, s2 = 0.f;
+    if (mine) {
+      load8(static_cast<const T*>(p.x) + off, xh);
+      load8(static_cast<const T*>(p.g_out) + off, go);
+      sum_partials8(static_cast<const T*>(p.dU_partials) + off, count, p.t, du);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int c = q * WAVE + lane;
-      if (c < nchunk) {
-        load8(dUp + c * 8, du[q]);
-        for (int i = 1; i < p.t; ++i) add8(dUp + static_cast<int64_t>(i) * count + c * 8, du[q]);
-        load8(xr + c * 8, xh[q]);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          xh[q][k] = (xh[q][k] - mu) * rs;
-          const float gt = du[q][k] * gq[q][k];
-          s1 += gt;
-          s2 += gt * xh[q][k];
-          dg[q][k] += du[q][k] * xh[q][k];
-          db[q][k] += du[q][k];
-        }
+      for (int k = 0; k < 8; ++k) {
+        xh[k] = (xh[k] - mu) * rs;
+        const float gt = du[k] * gq[k];
+        sm[0] += gt;
+        sm[1] += gt * xh[k];
+        dg[k] += du[k] * xh[k];
+        db[k] += du[k];
       }
     }
-    const float m1 = wave_sum(s1) * inv_h, m2 = wave_sum(s2) * inv_h;
-    const T* go = static_cast<const T*>(p.g_out) + row * p.h;
-    T* dx = static_cast<T*>(p.dx) + row * p.h;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int c = q * WAVE + lane;
-      if (c < nchunk) {
-        float o[8];
-        load8(go + c * 8, o);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float gt = du[q][k] * gq[q][k];
-          o[k] += rs * (gt - m1 - xh[q][k] * m2);
-        }
-        store8(dx + c * 8, o);
-      }
-    }
-  }
-  // Column partials of the 4 waves, summed through LDS in the fixed order
-  // ((w0 + w1) + w2) + w3, then written to this block's workspace slot.
-  const int h = static_cast<int>(p.h);
-  for (int w = 0; w < SP_THREADS / WAVE; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int c = q * WAVE + lane;
-        if (c < nchunk) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            float* g = &colsum[c * 8 + k];
-            float* b = &colsum[h + c * 8 + k];
-            *g = w ? *g + dg[q][k] : dg[q][k];
-            *b = w ? *b + db[q][k] : db[q][k];
-          }
-        }
-      }
+    sm[0] = wave_sum(sm[0]);
+    sm[1] = wave_sum(sm[1]);
+    if (lane == 0) {
+      red[par][wave][0] = sm[0];
+      red[par][wave][1] = sm[1];
     }
     __syncthreads();
+    float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < LNB_WAVES; ++w) {
+      m1 += red[par][w][0];
+      m2 += red[par][w][1];
+    }
+    // red[par] is rewritten two rows on, after the next barrier: no second
+    // barrier is needed here.
+    m1 *= inv_h;
+    m2 *= inv_h;
+    if (mine) {
+      float o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = go[k] + rs * (du[k] * gq[k] - m1 - xh[k] * m2);
+      store8(static_cast<T*>(p.dx) + off, o);
+    }
   }
-  float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * 2 * h;
-  for (int j = threadIdx.x; j < 2 * h; j += SP_THREADS) ws[j] = colsum[j];
+  const int64_t h = p.h;
+  if (mine) {
+    float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * 2 * h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ws[c * 8 + k] = dg[k];
+      ws[h + c * 8 + k] = db[k];
+    }
+  }
 }
 
-// dγ[j] = Σ_b ws[b][0][j], dβ[j] = Σ_b ws[b][1][j], b in increasing order.
+// dγ[j] = Σ_b ws[b][0][j], dβ[j] = Σ_b ws[b][1][j] over the nblk LN-backward
+// blocks.  A 256-thread block takes 32 of the 2h columns; thread (g, c) sums
+// block range g of 8 consecutive ranges in increasing b, then the 8 range sums
+// of each column are added in range order: a fixed order for any launch.
+constexpr int CS_COLS = 32, CS_GROUPS = SP_THREADS / CS_COLS;
 __global__ __launch_bounds__(SP_THREADS) void colsum_kernel(const float* __restrict__ ws, int64_t nblk,
                                                             int64_t h, float* __restrict__ dgamma,
                                                             float* __restrict__ dbeta) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * SP_THREADS + threadIdx.x;
-  if (j >= 2 * h) return;
+  __shared__ float part[CS_GROUPS][CS_COLS];
+  const int c = threadIdx.x % CS_COLS, g = threadIdx.x / CS_COLS;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * CS_COLS + c;
+  const int64_t per = (nblk + CS_GROUPS - 1) / CS_GROUPS;
+  const int64_t b0 = g * per, b1 = b0 + per < nblk ? b0 + per : nblk;
   float s = 0.f;
-  for (int64_t b = 0; b < nblk; ++b) s += ws[b * 2 * h + j];
-  if (j < h) dgamma[j] = s;
-  else dbeta[j - h] = s;
+  if (j < 2 * h) {
+    int64_t b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      float w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = ws[(b + u) * 2 * h + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += w[u];
+    }
+    for (; b < b1; ++b) s += ws[b * 2 * h + j];
+  }
+  part[g][c] = s;
+  __syncthreads();
+  if (g == 0 && j < 2 * h) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < CS_GROUPS; ++k) t += part[k][c];
+    if (j < h) dgamma[j] = t;
+    else dbeta[j - h] = t;
+  }
 }
 
-template <typename T, int NQ>
-hipError_t launch_nq(const SpProblem& p, hipStream_t stream) {
-  const int rows_per_block = SP_THREADS / WAVE;
+template <typename T>
+hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
   switch (p.phase) {
     case 0: {
-      const int64_t blocks = (p.s + rows_per_block - 1) / rows_per_block;
-      hipLaunchKernelGGL((ln_fwd_kernel<T, NQ>), dim3(static_cast<unsigned>(blocks)), dim3(SP_THREADS), 0,
-                         stream, p);
+      const int64_t blocks = (p.s + 1) / 2;
+      hipLaunchKernelGGL((ln_fwd_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(LNB_THREADS), 0, stream,
+                         p);
       return hipGetLastError();
     }
     case 1:
@@ -345,12 +399,12 @@ hipError_t launch_nq(const SpProblem& p, hipStream_t stream) {
     }
     default: {
       const int64_t nblk = sp_ln_bwd_row_blocks(p.s);
-      const size_t lds = 2 * static_cast<size_t>(p.h) * sizeof(float);
-      hipLaunchKernelGGL((ln_bwd_kernel<T, NQ>), dim3(static_cast<unsigned>(nblk)), dim3(SP_THREADS), lds,
+      // h ≤ 4096 (checked by the caller): one chunk of each row per thread
+      hipLaunchKernelGGL((ln_bwd_kernel<T>), dim3(static_cast<unsigned>(nblk)), dim3(LNB_THREADS), 0,
                          stream, p);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      const int64_t cb = (2 * p.h + SP_THREADS - 1) / SP_THREADS;
+      const int64_t cb = (2 * p.h + CS_COLS - 1) / CS_COLS;
       hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(cb)), dim3(SP_THREADS), 0, stream, p.ws,
                          nblk, p.h, p.dgamma, p.dbeta);
       return hipGetLastError();
@@ -358,18 +412,9 @@ hipError_t launch_nq(const SpProblem& p, hipStream_t stream) {
   }
 }
 
-template <typename T>
-hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
-  const int64_t nq = (p.h / 8 + WAVE - 1) / WAVE;
-  if (nq <= 1) return launch_nq<T, 1>(p, stream);
-  if (nq <= 2) return launch_nq<T, 2>(p, stream);
-  if (nq <= 4) return launch_nq<T, 4>(p, stream);
-  return launch_nq<T, 8>(p, stream);
-}
-
 }  // namespace
 
-int64_t sp_ln_bwd_row_blocks(int64_t s) { return (s + LNB_ROWS - 1) / LNB_ROWS; }
+int64_t sp_ln_bwd_row_blocks(int64_t s) { return s < LNB_MAX_BLOCKS ? s : LNB_MAX_BLOCKS; }
 
 hipError_t launch_sp(const SpProblem& p, hipStream_t stream) {
   if (p.s <= 0) return hipSuccess;

@@ -119,7 +119,9 @@ def test_sp_validation(L):
     assert call(_sp(s=0)) == 0
     assert call(_sp(phase=tp.SP_LN_BWD, dU_partials=0x1000, g_out=0x1000, dx=0x1000,
                     dgamma=0x1000, dbeta=0x1000, ws=0x1000, ws_bytes=16)) == tp.ERR_WORKSPACE
-    assert L.tpmlp_sp_workspace_bytes(4096, 4096) == (4096 // 32) * 2 * 4096 * 4
+    # one [2, h] fp32 slot per LN-backward block: min(s, 512) blocks
+    assert L.tpmlp_sp_workspace_bytes(4096, 4096) == 512 * 2 * 4096 * 4
+    assert L.tpmlp_sp_workspace_bytes(6, 64) == 6 * 2 * 64 * 4
 
 
 def test_sp_args_layout_matches_header(tmp_path):
