@@ -144,27 +144,23 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
     st = check_ptrs(dt, {X, A, B, Z, Y, G, D, dXp});
     if (st) return st;
   }
-  if (n > 0) {
-    // D_i = (G·B_iᵀ) ⊙ GeLU'(Z_i): A = G [n,d] (K-major), B(k,j) = B_i[j][k]
-    // (K-major, ld = d).
-    tpmlp::GemmProblem e{};
-    e.M = static_cast<int>(n);
-    e.N = static_cast<int>(m_i);
-    e.K = static_cast<int>(d);
-    e.batch = t_local;
-    e.A = G;
-    e.B = B;
-    e.C = D;
-    e.Zin = Z;
-    e.lda = d;
-    e.ldb = d;
-    e.ldc = m_i;
-    e.sA = 0;
-    e.sB = m_i * d;
-    e.sC = n * m_i;
-    st = hip_status(gemm(dt, e, tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_GELU_GRAD, stream));
-    if (st) return st;
-  }
+  // D_i = (G·B_iᵀ) ⊙ GeLU'(Z_i): A = G [n,d] (K-major), B(k,j) = B_i[j][k]
+  // (K-major, ld = d).  Empty (skipped) when n == 0.
+  tpmlp::GemmProblem e{};
+  e.M = static_cast<int>(n);
+  e.N = static_cast<int>(m_i);
+  e.K = static_cast<int>(d);
+  e.batch = t_local;
+  e.A = G;
+  e.B = B;
+  e.C = D;
+  e.Zin = Z;
+  e.lda = d;
+  e.ldb = d;
+  e.ldc = m_i;
+  e.sA = 0;
+  e.sB = m_i * d;
+  e.sC = n * m_i;
 
   // dB_i = Y_iᵀ·G: M = m_i, N = d, K = n; A(m,k) = Y_i[k][m] (M-major),
   // B(k,j) = G[k][j] (N-major).  With n == 0 this writes zeros.
@@ -182,6 +178,7 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
   wb.sA = n * m_i;
   wb.sB = 0;
   wb.sC = m_i * d;
+
   // dA_i = Xᵀ·D_i: M = d, N = m_i, K = n; A(m,k) = X[k][m], B(k,j) = D_i[k][j].
   tpmlp::GemmProblem wa{};
   wa.M = static_cast<int>(d);
@@ -197,37 +194,46 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
   wa.sA = 0;
   wa.sB = n * m_i;
   wa.sC = d * m_i;
-  // Both weight gradients in one launch: each alone leaves a partial last
-  // wave of tiles on the machine, together they fill it better.
+
+  // dX_i = D_i·A_iᵀ: M = n, N = d, K = m_i; A = D_i (K-major),
+  // B(k,j) = A_i[j][k] (K-major, ld = m_i).  Empty (skipped) when n == 0.
+  tpmlp::GemmProblem dx{};
+  dx.M = static_cast<int>(n);
+  dx.N = static_cast<int>(d);
+  dx.K = static_cast<int>(m_i);
+  dx.batch = t_local;
+  dx.A = D;
+  dx.B = A;
+  dx.C = dXp;
+  dx.lda = m_i;
+  dx.ldb = m_i;
+  dx.ldc = d;
+  dx.sA = n * m_i;
+  dx.sB = d * m_i;
+  dx.sC = n * d;
+
+  const tpmlp::GemmKind wgrad{tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32};
+  const tpmlp::GemmKind dgrad1{tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_GELU_GRAD};
+  const tpmlp::GemmKind dgrad2{tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE};
   if (dt == TPMLP_BF16) {
+    // Two launches: dgrad-1, then both weight gradients (K = n, the long
+    // ones) with dgrad-2 (which also needs D), whose tiles fill the machine
+    // around them.
+    st = hip_status(tpmlp::launch_gemm_bf16(e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, stream));
+    if (st) return st;
     const tpmlp::GemmProblem w[2] = {wb, wa};
-    st = hip_status(tpmlp::launch_gemm_bf16_group(w, 2, tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32, stream));
-    if (st) return st;
-  } else {
-    st = hip_status(gemm(dt, wb, tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32, stream));
-    if (st) return st;
-    st = hip_status(gemm(dt, wa, tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32, stream));
+    return hip_status(tpmlp::launch_gemm_bf16_group(w, 2, wgrad, &dx, dgrad2, stream));
+  }
+  if (n > 0) {
+    st = hip_status(gemm(dt, e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, stream));
     if (st) return st;
   }
-
+  st = hip_status(gemm(dt, wb, wgrad.a_order, wgrad.b_order, wgrad.epi, stream));
+  if (st) return st;
+  st = hip_status(gemm(dt, wa, wgrad.a_order, wgrad.b_order, wgrad.epi, stream));
+  if (st) return st;
   if (n > 0) {
-    // dX_i = D_i·A_iᵀ: M = n, N = d, K = m_i; A = D_i (K-major),
-    // B(k,j) = A_i[j][k] (K-major, ld = m_i).
-    tpmlp::GemmProblem dx{};
-    dx.M = static_cast<int>(n);
-    dx.N = static_cast<int>(d);
-    dx.K = static_cast<int>(m_i);
-    dx.batch = t_local;
-    dx.A = D;
-    dx.B = A;
-    dx.C = dXp;
-    dx.lda = m_i;
-    dx.ldb = m_i;
-    dx.ldc = d;
-    dx.sA = n * m_i;
-    dx.sB = d * m_i;
-    dx.sC = n * d;
-    st = hip_status(gemm(dt, dx, tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE, stream));
+    st = hip_status(gemm(dt, dx, dgrad2.a_order, dgrad2.b_order, dgrad2.epi, stream));
     if (st) return st;
   }
   return TPMLP_OK;

@@ -35,6 +35,7 @@
 // straight from the accumulators as 16-B stores.
 #include "common.h"
 #include "kernels.h"
+#include "tile_map.h"
 
 namespace tpmlp {
 namespace {
@@ -48,7 +49,7 @@ constexpr int B_BASE = A_STAGES * TILE_BYTES;
 constexpr int LDS_BYTES = (A_STAGES + B_STAGES) * TILE_BYTES;  // 160 KiB
 constexpr uint32_t OOB = 0x80000000u;  // past every descriptor's range (< 2^31)
 
-struct KArgs {
+struct alignas(64) KArgs {
   const bf16* A;
   const bf16* B;
   void* C;
@@ -61,11 +62,13 @@ struct KArgs {
   uint32_t a_bytes, b_bytes, c_bytes;
 };
 
-// One launch runs one or two problems of the same operand orders and
-// epilogue: tiles [0, tiles0) belong to p0, [tiles0, total) to p1.
+// One launch runs up to three problems: p[0] and p[1] (the long group, one
+// kind of operand orders and epilogue) and p[2] (another kind or the same);
+// t0..t2 are their tile counts (zero for an absent problem).
 struct KGroup {
-  KArgs p0, p1;
-  int tiles0, total;
+  KArgs p[3];
+  int t0, t1, t2;
+  XcdSplit split;  // the order of the tiles over the XCDs (tile_map.h)
 };
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -273,16 +276,9 @@ __device__ __forceinline__ void slice_body(f32x16 (&acc)[FA][FB], i32x4 (&ca)[FA
   }
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
-// workgroup w runs on XCD w % 8.  Each XCD is given a contiguous range of the
-// logical tile order, and within a problem's batch the tiles go in groups of GM
-// tile rows, so the workgroups resident on one XCD share operand panels in its L2.
-__device__ __forceinline__ int logical_tile(int wg, int total) {
-  const int q = total >> 3, r = total & 7;
-  const int xcd = wg & 7, local = wg >> 3;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
-
+// Within a problem's batch the tiles go in groups of GM tile rows, so the
+// workgroups resident on one XCD share operand panels in its L2 (the order of
+// tiles over the XCDs is in tile_map.h).
 __device__ __forceinline__ void tile_coords(int tile, const KArgs& a, int& batch, int& tm, int& tn) {
   const int per_batch = a.tiles_m * a.tiles_n;
   batch = tile / per_batch;
@@ -312,17 +308,12 @@ __device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk
   return qbase + row * QROW + ((chunk ^ (row & 7)) << 4) + half * 8;
 }
 
+// One 256×256 output tile of problem a.
 template <int AO, int BO, int EPI>
-__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-  TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
+__device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS char* lds) {
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-
-  const int tile = logical_tile(blockIdx.x, g.total);
-  const bool second = tile >= g.tiles0;
-  const KArgs& a = second ? g.p1 : g.p0;
   int batch, tm, tn;
-  tile_coords(second ? tile - g.tiles0 : tile, a, batch, tm, tn);
+  tile_coords(tile, a, batch, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -532,9 +523,30 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   }
 }
 
-template <int AO, int BO, int EPI>
+// The launch: problems 0 and 1 are of kind (AO0, BO0, EPI0), problem 2 of
+// kind (AO1, BO1, EPI1).
+template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1>
+__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
+  int prob, tile;
+  map_workgroup(g.split, g.t0, blockIdx.x, prob, tile);
+  if constexpr (AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1) {
+    const KArgs a = g.p[prob];  // one copy: wide scalar loads at the problem's offset
+    gemm_tile<AO0, BO0, EPI0>(a, tile, lds);
+  } else {
+    const KArgs a = g.p[prob];
+    if (prob == 2)
+      gemm_tile<AO1, BO1, EPI1>(a, tile, lds);
+    else
+      gemm_tile<AO0, BO0, EPI0>(a, tile, lds);
+  }
+}
+
+template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1>
 hipError_t launch_t(const KGroup& g, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<AO, BO, EPI>), dim3(g.total), dim3(NTHR), 0, stream, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<AO0, BO0, EPI0, AO1, BO1, EPI1>), dim3(g.t0 + g.t1 + g.t2), dim3(NTHR), 0,
+                     stream, g);
   return hipGetLastError();
 }
 
@@ -580,36 +592,53 @@ int64_t tiles_of(const GemmProblem& p) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16_group(const GemmProblem* probs, int count, int a_order, int b_order, int epi,
-                                  hipStream_t stream) {
-  if (probs == nullptr || count < 1 || count > 2) return hipErrorInvalidValue;
-  const GemmProblem* live[2];
-  int nlive = 0;
-  for (int i = 0; i < count; ++i)
-    if (!empty(probs[i])) live[nlive++] = &probs[i];
-  if (nlive == 0) return hipSuccess;
-  const int64_t t0 = tiles_of(*live[0]), t1 = nlive > 1 ? tiles_of(*live[1]) : 0;
-  if (t0 + t1 > 0x7fffffff) return hipErrorInvalidValue;
+hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
+                                  const GemmProblem* shortp, const GemmKind& short_kind, hipStream_t stream) {
+  if (nlong < 0 || nlong > 2 || (nlong > 0 && longp == nullptr)) return hipErrorInvalidValue;
+  const GemmProblem* lp[2];
+  int nl = 0;
+  for (int i = 0; i < nlong; ++i)
+    if (!empty(longp[i])) lp[nl++] = &longp[i];
+  const bool has_short = shortp != nullptr && !empty(*shortp);
+  const int64_t t0 = nl > 0 ? tiles_of(*lp[0]) : 0, t1 = nl > 1 ? tiles_of(*lp[1]) : 0;
+  const int64_t t2 = has_short ? tiles_of(*shortp) : 0;
+  if (t0 + t1 + t2 == 0) return hipSuccess;
+  if (t0 + t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
   KGroup g;
-  g.p0 = kargs(*live[0], a_order, b_order);
-  g.p1 = nlive > 1 ? kargs(*live[1], a_order, b_order) : g.p0;
-  g.tiles0 = static_cast<int>(t0);
-  g.total = static_cast<int>(t0 + t1);
-  if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_GELU_ZY)
-    return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
-  if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_STORE)
-    return launch_t<KMAJ, MNMAJ, EPI_STORE>(g, stream);
-  if (a_order == KMAJ && b_order == KMAJ && epi == EPI_GELU_GRAD)
-    return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
-  if (a_order == KMAJ && b_order == KMAJ && epi == EPI_STORE)
-    return launch_t<KMAJ, KMAJ, EPI_STORE>(g, stream);
-  if (a_order == MNMAJ && b_order == MNMAJ && epi == EPI_STORE_F32)
-    return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  g.p[0] = nl > 0 ? kargs(*lp[0], long_kind.a_order, long_kind.b_order) : KArgs{};
+  g.p[1] = nl > 1 ? kargs(*lp[1], long_kind.a_order, long_kind.b_order) : g.p[0];
+  g.p[2] = has_short ? kargs(*shortp, short_kind.a_order, short_kind.b_order) : g.p[0];
+  g.t0 = static_cast<int>(t0);
+  g.t1 = static_cast<int>(t1);
+  g.t2 = static_cast<int>(t2);
+  g.split = make_split(g.t0, g.t1, g.t2);
+  // with no long-group problem the launch is of the short kind alone, and
+  // vice versa
+  const GemmKind& k0 = nl > 0 ? long_kind : short_kind;
+  const GemmKind& k1 = has_short ? short_kind : long_kind;
+  auto is = [](const GemmKind& x, int ao, int bo, int epi) {
+    return x.a_order == ao && x.b_order == bo && x.epi == epi;
+  };
+  const bool same = is(k1, k0.a_order, k0.b_order, k0.epi);
+  if (same && is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
+    return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
+  if (same && is(k0, KMAJ, MNMAJ, EPI_STORE))
+    return launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE>(g, stream);
+  if (same && is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))
+    return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
+  if (same && is(k0, KMAJ, KMAJ, EPI_STORE))
+    return launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE>(g, stream);
+  if (same && is(k0, MNMAJ, MNMAJ, EPI_STORE_F32))
+    return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, MNMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  // the backward's last launch: both weight gradients, then dgrad-2
+  if (is(k0, MNMAJ, MNMAJ, EPI_STORE_F32) && is(k1, KMAJ, KMAJ, EPI_STORE))
+    return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, KMAJ, KMAJ, EPI_STORE>(g, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int epi, hipStream_t stream) {
-  return launch_gemm_bf16_group(&p, 1, a_order, b_order, epi, stream);
+  const GemmKind k{a_order, b_order, epi};
+  return launch_gemm_bf16_group(&p, 1, k, nullptr, k, stream);
 }
 
 }  // namespace tpmlp

@@ -36,11 +36,19 @@ struct GemmProblem {
 // bf16 inputs, fp32 accumulation (MFMA).  Returns a hipError_t.
 hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int epi,
                             hipStream_t stream);
-// Two problems with the same operand orders and epilogue in one launch (their
-// tiles share one grid, so the tail of one fills the machine with the other).
-// Empty problems are skipped; count is 1 or 2.
-hipError_t launch_gemm_bf16_group(const GemmProblem* probs, int count, int a_order, int b_order, int epi,
-                                  hipStream_t stream);
+// Operand orders and epilogue of one GEMM problem.
+struct GemmKind {
+  int a_order, b_order, epi;
+};
+
+// Up to three independent problems in one launch (their tiles share one
+// grid, so the machine stays full where each alone would leave part of it
+// idle): a long group of nlong (≤ 2) problems of one kind, put first, and an
+// optional short problem of another kind whose tiles fill in around them.
+// Empty problems are skipped.  Supported: equal kinds, and a long group of
+// (MNMAJ, MNMAJ, EPI_STORE_F32) with a short (KMAJ, KMAJ, EPI_STORE).
+hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
+                                  const GemmProblem* shortp, const GemmKind& short_kind, hipStream_t stream);
 // fp32 throughout.
 hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int epi,
                            hipStream_t stream);

@@ -1,0 +1,67 @@
+// Workgroup -> (problem, tile) order of the GEMM launches, host- and
+// device-callable so that the CPU tests can check it is a bijection.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2),
+// in increasing index: workgroup w runs on XCD w % 8 as its (w / 8)-th.  A
+// launch has a long group of tiles (problem 0's T0, then problem 1's T1; the
+// long-K problems) and a short one (problem 2's T2).  Its tiles form one
+// logical sequence in which the two groups are interleaved in proportion
+// (position j is preceded by floor(j·G/T) long-group tiles, G = T0 + T1,
+// T = G + T2).  XCD x takes a contiguous range of that sequence, exactly as
+// many positions as the round-robin deal gives it, and works first through
+// the long-group tiles of its range, then the short-group ones: every XCD gets
+// its proportional share of both, the long tiles first so the short ones fill
+// in behind them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+// Positions [begin, begin + count) of the logical sequence of `total` that the
+// round-robin deal gives XCD `xcd`.
+__host__ __device__ inline void xcd_range(int total, int xcd, int& begin, int& count) {
+  const int q = total >> 3, r = total & 7;
+  begin = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  count = xcd < r ? q + 1 : q;
+}
+
+// Per XCD: where its range starts in the short problem (short0), where it
+// starts in the long group (long0) and how many long-group tiles it has
+// (nlong).  Computed once per launch on the host (it needs 64-bit divisions).
+struct XcdSplit {
+  int long0[8], nlong[8], short0[8];
+};
+
+__host__ __device__ inline XcdSplit make_split(int t0, int t1, int t2) {
+  const int64_t glong = static_cast<int64_t>(t0) + t1, total = glong + t2;
+  XcdSplit s;
+  for (int x = 0; x < 8; ++x) {
+    int begin, count;
+    xcd_range(static_cast<int>(total), x, begin, count);
+    // long-group tiles before position j: floor(j·glong/total)
+    const int a = total > 0 ? static_cast<int>(begin * glong / total) : 0;
+    const int b = total > 0 ? static_cast<int>((static_cast<int64_t>(begin) + count) * glong / total) : 0;
+    s.long0[x] = a;
+    s.nlong[x] = b - a;
+    s.short0[x] = begin - a;
+  }
+  return s;
+}
+
+// prob: 0, 1 (the long group: problem 0's t0 tiles, then problem 1's) or 2
+// (the short problem); tile: index within that problem.
+__host__ __device__ inline void map_workgroup(const XcdSplit& s, int t0, int wg, int& prob, int& tile) {
+  const int xcd = wg & 7, local = wg >> 3;
+  if (local < s.nlong[xcd]) {
+    const int k = s.long0[xcd] + local;
+    prob = k < t0 ? 0 : 1;
+    tile = k < t0 ? k : k - t0;
+  } else {
+    prob = 2;
+    tile = s.short0[xcd] + (local - s.nlong[xcd]);
+  }
+}
+
+}  // namespace tpmlp
