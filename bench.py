@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the per-rank, GPT-1T-shard and SP legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing on the host")
+    ap.add_argument("--cpu-all-configs", action="store_true",
+                    help="also time the oracle once on every configuration (3x4 worked example, the "
+                         "single-shard layer, the 8.3B-shaped layer, the GPT-1T-shaped shard, the h=4096 "
+                         "sequence-parallel block); about a minute of host time")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 512 MiB (read 512 MiB, write 512 MiB), "
                          "the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -85,6 +89,60 @@ def cpu_baseline(inp, t, budget_s):
             "sample": f"{shards} whole-shard passes (of {t} shards), full n={n}: fp64 NumPy forward + "
                       f"backward ({flops:.3e} FLOP in {el:.1f} s); host logical CPUs {os.cpu_count()}, "
                       f"affinity {len(os.sched_getaffinity(0))}"}
+
+
+def cpu_all_configs():
+    """The fp64 oracle, forward + backward, once per configuration on the
+    host's cores (small ones: median of 5), with the BLAS it ran on."""
+    import threadpoolctl
+
+    from oracle import mlp as om
+    from oracle import sp_block as osp
+    from tpmlp_inputs import CONFIGS, config_inputs
+
+    info = threadpoolctl.threadpool_info()
+    blas = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+            for i in info if i.get("user_api") == "blas"]
+    out = {"host_logical_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "blas": blas}
+    for name in ("worked_example", "single_shard", "gpt8p3b_t8", "gpt1t_t8_shard0", "sp_block_t8"):
+        c = CONFIGS[name]
+        t0 = time.perf_counter()
+        inp = config_inputs(name, seed=0)
+        gen_s = time.perf_counter() - t0
+        n, d, m, t = c["n"], c["d"], c["m"], c["t"]
+        mi = m // t
+        if c["kind"] == "sp":
+            v = {k: inp[k].f64 for k in ("x", "A", "B", "G", "gamma", "beta")}
+
+            def run():
+                f = osp.sp_forward(v["x"], v["gamma"], v["beta"], c["eps"], v["A"], v["B"], t, c["p"],
+                                   c["mask_seed"])
+                osp.sp_backward(f, v["gamma"], v["A"], v["B"], v["G"], t, c["p"])
+            flops = 12.0 * n * d * mi * t
+        elif c.get("shards"):
+            X, A, B, G = (inp[k].f64 for k in "XABG")
+
+            def run():
+                Z, Y, P = om.shard_forward(X, A, B)
+                om.shard_backward(X, A, B, Z, Y, G)
+            flops = 12.0 * n * d * mi * len(c["shards"])
+        else:
+            X, A, B, G = (inp[k].f64 for k in "XABG")
+
+            def run():
+                f = om.tp_forward(X, A, B, t)
+                om.tp_backward(X, A, B, f, G)
+            flops = 12.0 * n * d * mi * t
+        reps = 5 if flops < 1e12 else 1
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            run()
+            times.append(time.perf_counter() - t0)
+        w = sorted(times)[len(times) // 2]
+        out[name] = {"flop": flops, "wall_s": round(w, 6), "gflops": round(flops / w / 1e9, 2),
+                     "reps": reps, "input_generation_s": round(gen_s, 2)}
+    return out
 
 
 def _stats(ms):
@@ -358,6 +416,8 @@ def main():
         rec["sp_region"] = leg_sp(tp, 10)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, t, args.cpu_seconds)
+    if args.cpu_all_configs:
+        rec["cpu_oracle_configs"] = cpu_all_configs()
     print(json.dumps(rec), flush=True)
 
 
