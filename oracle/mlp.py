@@ -15,6 +15,13 @@ gradient G = ∂ℓ/∂O
                                               ([TUT] §二 "前向少通信，反向为何仍要
                                                一次归约？")
 
+With the layers' biases ([TRAIN] ColumnParallelLinear: the bias is split like
+the output columns, b1_i; RowParallelLinear: one unsplit bias b2 added after
+the all-reduce) the shard computes Z_i = X·A_i + b1_i and the layer
+O = Σ_i P_i + b2; the bias gradients are the upstream gradients summed over
+the tokens ([TRAIN] custom autograd matmul rule, grad_bias = Σ over rows):
+db1_i = Σ_rows D_i, db2 = Σ_rows G.
+
 The sum over shards of P_i (forward) and of dX_i = D_i·A_iᵀ (backward) is what
 an all-reduce computes across GPUs ([TRAIN] RowParallelLinear / Column-
 ParallelLinear sections: forward all_reduce after the row-parallel matmul,
@@ -93,11 +100,14 @@ def split_rows(B, t):
 
 
 # ---------------------------------------------------------------- one shard
-def shard_forward(X, A_i, B_i, act="gelu"):
-    """Z_i = X·A_i, Y_i = φ(Z_i), P_i = Y_i·B_i  ([TUT] §二)."""
+def shard_forward(X, A_i, B_i, act="gelu", b1_i=None):
+    """Z_i = X·A_i (+ b1_i on every row), Y_i = φ(Z_i), P_i = Y_i·B_i
+    ([TUT] §二; the bias per [TRAIN] ColumnParallelLinear)."""
     f, _ = ACTIVATIONS[act]
     X = np.asarray(X, dtype=np.float64)
     Z = X @ np.asarray(A_i, dtype=np.float64)
+    if b1_i is not None:
+        Z = Z + np.asarray(b1_i, dtype=np.float64)[None, :]
     Y = f(Z)
     P = Y @ np.asarray(B_i, dtype=np.float64)
     return Z, Y, P
@@ -123,6 +133,26 @@ def shard_backward(X, A_i, B_i, Z, Y, G, act="gelu"):
     return D, dA, dB, dXi
 
 
+def bias_grad(g):
+    """Σ over the rows (tokens) of an upstream gradient: the gradient of a bias
+    broadcast over those rows ([TRAIN] custom autograd matmul rule)."""
+    g = np.asarray(g, dtype=np.float64)
+    out = np.zeros(g.shape[1])
+    for r in range(g.shape[0]):
+        out = out + g[r]
+    return out
+
+
+def split_bias(b1, t):
+    """b1 [m] -> t contiguous blocks of m/t, matching the column blocks of A."""
+    b1 = np.asarray(b1)
+    m = b1.shape[0]
+    if m % t:
+        raise ValueError(f"bias length {m} is not divisible by t={t}")
+    mi = m // t
+    return [b1[i * mi:(i + 1) * mi] for i in range(t)]
+
+
 def reduce_partials(partials):
     """Σ_i partial_i (the one-GPU stand-in for the all-reduce; a sum, not a
     mean, [TUT] §三)."""
@@ -133,14 +163,19 @@ def reduce_partials(partials):
 
 
 # ---------------------------------------------------------------- all shards
-def tp_forward(X, A, B, t, act="gelu"):
-    """Forward of all t shards from the full weights, plus O = Σ_i P_i."""
+def tp_forward(X, A, B, t, act="gelu", b1=None, b2=None):
+    """Forward of all t shards from the full weights, plus O = Σ_i P_i (+ b2
+    on every row, added once after the sum)."""
     A_s, B_s = split_columns(A, t), split_rows(B, t)
+    b1_s = split_bias(b1, t) if b1 is not None else [None] * t
     Z, Y, P = [], [], []
     for i in range(t):
-        z, y, p = shard_forward(X, A_s[i], B_s[i], act)
+        z, y, p = shard_forward(X, A_s[i], B_s[i], act, b1_s[i])
         Z.append(z), Y.append(y), P.append(p)
-    return {"Z": Z, "Y": Y, "P": P, "O": reduce_partials(P)}
+    O = reduce_partials(P)
+    if b2 is not None:
+        O = O + np.asarray(b2, dtype=np.float64)[None, :]
+    return {"Z": Z, "Y": Y, "P": P, "O": O, "biased": b1 is not None or b2 is not None}
 
 
 def tp_backward(X, A, B, fwd, G, act="gelu"):
@@ -151,30 +186,46 @@ def tp_backward(X, A, B, fwd, G, act="gelu"):
     for i in range(t):
         d_, da, db, dx = shard_backward(X, A_s[i], B_s[i], fwd["Z"][i], fwd["Y"][i], G, act)
         D.append(d_), dA.append(da), dB.append(db), dXp.append(dx)
-    return {"D": D, "dA": dA, "dB": dB, "dXp": dXp, "dX": reduce_partials(dXp)}
+    out = {"D": D, "dA": dA, "dB": dB, "dXp": dXp, "dX": reduce_partials(dXp)}
+    if fwd.get("biased"):
+        out["db1"] = [bias_grad(d_) for d_ in D]
+        out["db2"] = bias_grad(G)
+    return out
 
 
 # ---------------------------------------------------------------- unsharded
-def dense_forward(X, A, B, act="gelu"):
-    """The unsharded layer O = φ(X·A)·B ([TUT] §二, Y = f(XA)B)."""
+def dense_forward(X, A, B, act="gelu", b1=None, b2=None):
+    """The unsharded layer O = φ(X·A + b1)·B + b2 ([TUT] §二, Y = f(XA)B; the
+    biases broadcast over the rows)."""
     f, _ = ACTIVATIONS[act]
     X = np.asarray(X, dtype=np.float64)
-    return f(X @ np.asarray(A, dtype=np.float64)) @ np.asarray(B, dtype=np.float64)
+    H = X @ np.asarray(A, dtype=np.float64)
+    if b1 is not None:
+        H = H + np.asarray(b1, dtype=np.float64)[None, :]
+    O = f(H) @ np.asarray(B, dtype=np.float64)
+    if b2 is not None:
+        O = O + np.asarray(b2, dtype=np.float64)[None, :]
+    return O
 
 
-def dense_backward(X, A, B, G, act="gelu"):
+def dense_backward(X, A, B, G, act="gelu", b1=None):
     """Gradients of ℓ = Σ G⊙O for the unsharded layer by the chain rule:
-    H = X·A, ∂ℓ/∂H = (G·Bᵀ)⊙φ'(H), then the matmul rules grad_left = g·rightᵀ
-    and grad_right = leftᵀ·g ([TRAIN] custom autograd.Function C = A@B).
-    Returns (dX, dA, dB)."""
+    H = X·A (+ b1), ∂ℓ/∂H = (G·Bᵀ)⊙φ'(H), then the matmul rules
+    grad_left = g·rightᵀ and grad_right = leftᵀ·g ([TRAIN] custom
+    autograd.Function C = A@B).  Returns (dX, dA, dB); with b1 given also
+    (db1, db2) = (Σ_rows ∂ℓ/∂H, Σ_rows G)."""
     f, fp = ACTIVATIONS[act]
     X = np.asarray(X, dtype=np.float64)
     A = np.asarray(A, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
     G = np.asarray(G, dtype=np.float64)
     H = X @ A
+    if b1 is not None:
+        H = H + np.asarray(b1, dtype=np.float64)[None, :]
     dH = (G @ B.T) * fp(H)
-    return dH @ A.T, X.T @ dH, f(H).T @ G
+    if b1 is None:
+        return dH @ A.T, X.T @ dH, f(H).T @ G
+    return dH @ A.T, X.T @ dH, f(H).T @ G, bias_grad(dH), bias_grad(G)
 
 
 # ---------------------------------------------------------------- the wrong split

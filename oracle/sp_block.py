@@ -14,6 +14,10 @@ ReduceScatter is a sum over shards followed by a row split
 Block, pre-norm with the residual taken from the LayerNorm input ([TRAIN]
 Post-Norm 还是 Pre-Norm section; [SP] placement diagram):
     out = x + dropout_p( Σ_i φ(LN(x)·A_i)·B_i )
+With biases (optional): the column-parallel bias b1 inside φ and the
+row-parallel bias b2 added after the sum, before dropout — the
+bias + dropout + add of [EFF] §4.2:
+    out = x + dropout_p( Σ_i φ(LN(x)·A_i + b1_i)·B_i + b2 )
 The sequence-parallel degree equals the tensor-parallel degree t and must be
 at least 2 ([SP] 工程约束: sequence parallelism requires TP > 1).
 """
@@ -32,16 +36,17 @@ def _check(s, t):
         raise ValueError(f"sequence length {s} is not divisible by t={t}")
 
 
-def sp_forward(x, gamma, beta, eps, A, B, t, p, seed):
+def sp_forward(x, gamma, beta, eps, A, B, t, p, seed, b1=None, b2=None):
     """Sharded forward: per-shard LN on s/t rows, concat (AllGather), the t MLP
-    shards, sum then split (ReduceScatter), per-shard dropout + residual."""
+    shards, sum then split (ReduceScatter; the row bias is added to the sum),
+    per-shard dropout + residual."""
     x = np.asarray(x, dtype=np.float64)
     s, h = x.shape
     _check(s, t)
     sl = s // t
     parts = [ln_forward(x[r * sl:(r + 1) * sl], gamma, beta, eps) for r in range(t)]
     U = np.concatenate([q[0] for q in parts], axis=0)
-    fwd = _mlp.tp_forward(U, A, B, t)
+    fwd = _mlp.tp_forward(U, A, B, t, b1=b1, b2=b2)
     scale = 1.0 / (1.0 - p)
     outs, masks = [], []
     for r in range(t):
@@ -70,7 +75,7 @@ def sp_backward(fwd, gamma, A, B, G_out, t, p):
     scale = 1.0 / (1.0 - p)
     dS = np.concatenate([G_out[r * sl:(r + 1) * sl] * fwd["mask"][r * sl:(r + 1) * sl] * scale
                          for r in range(t)], axis=0)
-    bwd = _mlp.tp_backward(fwd["U"], A, B, fwd["mlp"], dS)
+    bwd = _mlp.tp_backward(fwd["U"], A, B, fwd["mlp"], dS)  # with biases also db1, db2 = Σ_rows dS
     dxs, dgs, dbs = [], [], []
     for r in range(t):
         rows = slice(r * sl, (r + 1) * sl)
@@ -87,20 +92,25 @@ def sp_backward(fwd, gamma, A, B, G_out, t, p):
     }
 
 
-def dense_forward(x, gamma, beta, eps, A, B, p, seed):
+def dense_forward(x, gamma, beta, eps, A, B, p, seed, b1=None, b2=None):
     """The same block with no sharding at all: LN on all rows, the unsharded
     MLP, one mask over the whole [s, h], residual."""
     x = np.asarray(x, dtype=np.float64)
     s, h = x.shape
     U, mean, rstd, xhat = ln_forward(x, gamma, beta, eps)
-    S = _mlp.dense_forward(U, A, B)
+    S = _mlp.dense_forward(U, A, B, b1=b1, b2=b2)
     M = keep_mask(0, s, h, p, seed)
     return {"U": U, "xhat": xhat, "rstd": rstd, "mask": M, "out": x + M * S / (1.0 - p)}
 
 
-def dense_backward(fwd, gamma, A, B, G_out, p):
+def dense_backward(fwd, gamma, A, B, G_out, p, b1=None):
     G_out = np.asarray(G_out, dtype=np.float64)
     dS = G_out * fwd["mask"] / (1.0 - p)
-    dU, dA, dB = _mlp.dense_backward(fwd["U"], A, B, dS)
+    out = {}
+    if b1 is None:
+        dU, dA, dB = _mlp.dense_backward(fwd["U"], A, B, dS)
+    else:
+        dU, dA, dB, out["db1"], out["db2"] = _mlp.dense_backward(fwd["U"], A, B, dS, b1=b1)
     dx_ln, dg, db = ln_backward(dU, fwd["xhat"], fwd["rstd"], gamma)
-    return {"dx": G_out + dx_ln, "dgamma": dg, "dbeta": db, "dA": dA, "dB": dB}
+    out.update({"dx": G_out + dx_ln, "dgamma": dg, "dbeta": db, "dA": dA, "dB": dB})
+    return out
