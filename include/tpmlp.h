@@ -16,7 +16,12 @@
  *           placement diagram and the RNG-domain table: LayerNorm, dropout and
  *           residual run on the rank's s/t rows; AllGather before fc1,
  *           ReduceScatter after fc2.
- *   [TRAIN] "Megatron 训练" (lovelonelytime), LayerNorm and Dropout sections.
+ *   [TRAIN] "Megatron 训练" (lovelonelytime), LayerNorm and Dropout sections;
+ *           ColumnParallelLinear / RowParallelLinear (where each layer's bias
+ *           lives) and the custom autograd matmul (its gradient).
+ *   [EFF]   notes on "Efficient Large-Scale Language Model Training on GPU
+ *           Clusters Using Megatron-LM" (unpurerationalist.github.io), §4.2:
+ *           bias + GeLU and bias + dropout + add fused into single kernels.
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers to row-major, contiguous tensors.  Shapes
@@ -47,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 1
+#define TPMLP_ABI_VERSION 2
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -82,6 +87,22 @@ enum {
  */
 int tpmlp_fwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
               const void* X, const void* A, const void* B, void* Z, void* Y, void* P);
+
+/*
+ * tpmlp_fwd_bias -- tpmlp_fwd with the first layer's bias.  The column-
+ * parallel layer's bias is split like its output columns, so shard i owns
+ * slice i and adds it before the activation ([TRAIN] ColumnParallelLinear);
+ * the add and the GeLU run in the GEMM's epilogue ([EFF] §4.2):
+ *
+ *   Z_i = X·A_i + 1·b1_iᵀ   (added to the fp32 accumulator, then rounded)
+ *   Y_i = GeLU(Z_i),  P_i = Y_i·B_i
+ *
+ *   b1 [t_local, m_i] of dt (row i = slice i of the full bias), not NULL.
+ *   Everything else, errors included, as for tpmlp_fwd.  The backward is
+ *   tpmlp_bwd unchanged (Z_i already holds the bias), plus tpmlp_bias_grad.
+ */
+int tpmlp_fwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+                   const void* X, const void* A, const void* B, const void* b1, void* Z, void* Y, void* P);
 
 /*
  * tpmlp_bwd -- backward of t_local MLP shards ([TUT] §二).
@@ -120,9 +141,47 @@ int tpmlp_reduce_partials(hipStream_t stream, int in_dt, int out_dt, int32_t t, 
                           int64_t cols, const void* partials, void* out);
 
 /*
+ * tpmlp_reduce_partials_bias -- out = Σ_i partials[i] + 1·biasᵀ.  The
+ * row-parallel layer's bias is not split: it is added once, after the
+ * all-reduce ([TRAIN] RowParallelLinear).  The fp32 shard-order sum is formed
+ * as in tpmlp_reduce_partials, then bias[c] is added in fp32 and the result
+ * rounded once to out_dt.
+ *
+ *   bias [cols] of out_dt, not NULL; other arguments as for
+ *   tpmlp_reduce_partials.
+ */
+int tpmlp_reduce_partials_bias(hipStream_t stream, int in_dt, int out_dt, int32_t t, int64_t rows,
+                               int64_t cols, const void* partials, const void* bias, void* out);
+
+/*
+ * tpmlp_bias_grad -- db[i] = Σ_r g[i][r]: the gradient of a bias broadcast
+ * over rows is the upstream gradient summed over the rows ([TRAIN] custom
+ * autograd matmul).  For the MLP: db1_i = Σ_rows D_i (g = D, t = t_local,
+ * cols = m_i) and db2 = Σ_rows G (g = G, t = 1, cols = d; under sequence
+ * parallelism g = dS).
+ *
+ *   dt    dtype of g (TPMLP_BF16 or TPMLP_F32)
+ *   g     [t, rows, cols]; db [t, cols] fp32
+ *   The sum is fp32 in a fixed order (column partials of 128-row chunks,
+ *   rows in increasing order within each of 8 row phases, then the chunks in
+ *   increasing order), so results are bit-reproducible.  rows == 0 sets db to
+ *   zero and needs no g or workspace.
+ *   ws / ws_bytes: at least tpmlp_bias_grad_workspace_bytes(t, rows, cols)
+ *   bytes, 4-byte aligned.
+ *   Limits: t <= 65535; ceil(cols/32)·ceil(rows/128) < 2^31.
+ */
+size_t tpmlp_bias_grad_workspace_bytes(int32_t t, int64_t rows, int64_t cols);
+int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,
+                    float* db, void* ws, size_t ws_bytes);
+
+/*
  * tpmlp_ln_sp -- the sequence-parallel region around one MLP block
  * ([SP] placement diagram; [TRAIN] LayerNorm and Dropout sections):
  *     out = x + dropout_p( Σ_i P_i ),   the MLP input being LN(x)
+ * With a bias (a->bias not NULL; [TRAIN] RowParallelLinear: the unsplit bias
+ * of the second layer is added after the reduction) the forward is
+ *     out = x + dropout_p( Σ_i P_i + b2 )
+ * with the bias add, dropout and residual add in one kernel ([EFF] §4.2).
  * The t sequence shards of s/t rows each are all resident (s rows in total);
  * the AllGather before fc1 is the row-block layout of ln_out itself, and the
  * ReduceScatter after fc2 is a sum over the t partials whose row blocks are
@@ -134,7 +193,8 @@ int tpmlp_reduce_partials(hipStream_t stream, int in_dt, int out_dt, int32_t t, 
  *
  * Phases (a->phase):
  *   TPMLP_SP_LN_FWD      x, gamma, beta -> ln_out [s,h] (dt), mean, rstd [s] (f32)
- *   TPMLP_SP_DROPRES_FWD partials [t,s,h] (the MLP's P_i), x -> out [s,h]
+ *   TPMLP_SP_DROPRES_FWD partials [t,s,h] (the MLP's P_i), x, bias [h] or
+ *                        NULL -> out [s,h]
  *   TPMLP_SP_DROPRES_BWD g_out [s,h] -> dS [s,h] = g_out⊙mask/(1-p)
  *                        (the MLP's upstream gradient G)
  *   TPMLP_SP_LN_BWD      dU_partials [t,s,h] (the MLP's dX_i), g_out, x,
@@ -181,6 +241,8 @@ typedef struct {
   float* dbeta;
   void* ws;
   size_t ws_bytes;
+  const void* bias;         /* DROPRES_FWD: [h] of dt, or NULL (no bias); ignored
+                               by the other phases                              */
 } tpmlp_sp_args;
 
 size_t tpmlp_sp_workspace_bytes(int64_t s, int64_t h);

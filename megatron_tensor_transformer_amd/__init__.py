@@ -45,7 +45,7 @@ class SpArgs(ctypes.Structure):
         ("rstd", ctypes.c_void_p), ("partials", ctypes.c_void_p), ("out", ctypes.c_void_p),
         ("g_out", ctypes.c_void_p), ("dS", ctypes.c_void_p), ("dU_partials", ctypes.c_void_p),
         ("dx", ctypes.c_void_p), ("dgamma", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
-        ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+        ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("bias", ctypes.c_void_p),
     ]
 
 
@@ -55,9 +55,13 @@ _lib = None
 _P, _I, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
     "tpmlp_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "tpmlp_fwd_bias": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]),
     "tpmlp_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I32]),
     "tpmlp_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
     "tpmlp_reduce_partials": (_I, [_P, _I, _I, _I32, _I64, _I64, _P, _P]),
+    "tpmlp_reduce_partials_bias": (_I, [_P, _I, _I, _I32, _I64, _I64, _P, _P, _P]),
+    "tpmlp_bias_grad_workspace_bytes": (_SZ, [_I32, _I64, _I64]),
+    "tpmlp_bias_grad": (_I, [_P, _I, _I32, _I64, _I64, _P, _P, _P, _SZ]),
     "tpmlp_sp_workspace_bytes": (_SZ, [_I64, _I64]),
     "tpmlp_ln_sp": (_I, [_P, ctypes.POINTER(SpArgs)]),
     "tpmlp_status_string": (ctypes.c_char_p, [_I]),
@@ -123,6 +127,14 @@ def tpmlp_fwd(X, A, B, Z, Y, P, stream=None):
                            _ptr(Z), _ptr(Y), _ptr(P)))
 
 
+def tpmlp_fwd_bias(X, A, B, b1, Z, Y, P, stream=None):
+    """tpmlp_fwd with the column bias b1 [t, m_i] (dtype of X)."""
+    t, d, mi = A.shape
+    n = X.shape[0]
+    _check(lib().tpmlp_fwd_bias(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B), _ptr(b1),
+                                _ptr(Z), _ptr(Y), _ptr(P)))
+
+
 def tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, ws=None, stream=None):
     """Gradients of t_local shards; dA [t,d,m_i] and dB [t,m_i,d] are fp32."""
     t, d, mi = A.shape
@@ -141,6 +153,23 @@ def tpmlp_reduce_partials(partials, out, stream=None):
                                        _ptr(partials), _ptr(out)))
 
 
+def tpmlp_reduce_partials_bias(partials, bias, out, stream=None):
+    """out [rows, cols] = Σ_i partials[i] + bias (bias [cols], dtype of out)."""
+    t = partials.shape[0]
+    rows = out.shape[0]
+    cols = out.numel() // rows if rows else (out.shape[1] if out.dim() > 1 else 1)
+    _check(lib().tpmlp_reduce_partials_bias(_stream(stream), _dt(partials), _dt(out), t, rows, cols,
+                                            _ptr(partials), _ptr(bias), _ptr(out)))
+
+
+def tpmlp_bias_grad(g, db, ws=None, stream=None):
+    """db [t, cols] (fp32) = Σ_rows g [t, rows, cols]."""
+    t, rows, cols = g.shape
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().tpmlp_bias_grad(_stream(stream), _dt(g), t, rows, cols, _ptr(g), _ptr(db), _ptr(ws),
+                                 ws_bytes))
+
+
 def tpmlp_ln_sp(args, stream=None):
     _check(lib().tpmlp_ln_sp(_stream(stream), ctypes.byref(args)))
 
@@ -153,6 +182,16 @@ def mlp_fwd(X, A, B, stream=None):
     Y = torch.empty_like(Z)
     P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
     tpmlp_fwd(X, A, B, Z, Y, P, stream)
+    return Z, Y, P
+
+
+def mlp_fwd_bias(X, A, B, b1, stream=None):
+    t, d, mi = A.shape
+    n = X.shape[0]
+    Z = torch.empty((t, n, mi), dtype=X.dtype, device=X.device)
+    Y = torch.empty_like(Z)
+    P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
+    tpmlp_fwd_bias(X, A, B, b1, Z, Y, P, stream)
     return Z, Y, P
 
 
@@ -180,6 +219,27 @@ def reduce_partials(partials, out_dtype=None, stream=None):
     return out
 
 
+def reduce_partials_bias(partials, bias, stream=None):
+    out = torch.empty(partials.shape[1:], dtype=bias.dtype, device=partials.device)
+    tpmlp_reduce_partials_bias(partials, bias, out, stream)
+    return out
+
+
+def bias_grad_workspace_bytes(t, rows, cols):
+    return lib().tpmlp_bias_grad_workspace_bytes(t, rows, cols)
+
+
+def bias_grad(g, stream=None):
+    """Column sums over the rows of g [t, rows, cols] or [rows, cols] -> fp32 [t, cols] or [cols]."""
+    g3 = g if g.dim() == 3 else g.unsqueeze(0)
+    t, rows, cols = g3.shape
+    db = torch.empty((t, cols), dtype=torch.float32, device=g.device)
+    nb = bias_grad_workspace_bytes(t, rows, cols)
+    ws = torch.empty(nb, dtype=torch.uint8, device=g.device) if nb else None
+    tpmlp_bias_grad(g3, db, ws, stream)
+    return db if g.dim() == 3 else db[0]
+
+
 def sp_ln_fwd(x, gamma, beta, t, eps=1e-5, stream=None):
     s, h = x.shape
     U = torch.empty_like(x)
@@ -191,12 +251,12 @@ def sp_ln_fwd(x, gamma, beta, t, eps=1e-5, stream=None):
     return U, mean, rstd
 
 
-def sp_dropres_fwd(partials, x, p, seed, row0=0, stream=None):
+def sp_dropres_fwd(partials, x, p, seed, row0=0, bias=None, stream=None):
     t = partials.shape[0]
     s, h = x.shape
     out = torch.empty_like(x)
     a = SpArgs(phase=SP_DROPRES_FWD, dt=_dt(x), t=t, s=s, h=h, row0=row0, eps=1.0, p_drop=p, seed=seed,
-               partials=_ptr(partials), x=_ptr(x), out=_ptr(out))
+               partials=_ptr(partials), x=_ptr(x), out=_ptr(out), bias=_ptr(bias))
     tpmlp_ln_sp(a, stream)
     return out
 

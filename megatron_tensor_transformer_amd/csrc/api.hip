@@ -58,6 +58,70 @@ hipError_t gemm(int dt, const tpmlp::GemmProblem& p, int ao, int bo, int epi, hi
                           : tpmlp::launch_gemm_f32(p, ao, bo, epi, s);
 }
 
+// The shard forward with an optional column bias b1 [t_local, m_i] (NULL: none).
+int fwd_impl(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local, const void* X,
+             const void* A, const void* B, const void* b1, void* Z, void* Y, void* P) {
+  int st = check_mlp_dims(dt, n, d, m_i, t_local);
+  if (st) return st;
+  if (n == 0) return TPMLP_OK;
+  st = check_ptrs(dt, {X, A, B, Z, Y, P});
+  if (st) return st;
+
+  // Z_i = X·A_i (+ b1_i) and Y_i = GeLU(Z_i): A = X [n,d] (K-major),
+  // B = A_i [d,m_i] (N-major), batched over shards with X shared.
+  tpmlp::GemmProblem g1{};
+  g1.M = static_cast<int>(n);
+  g1.N = static_cast<int>(m_i);
+  g1.K = static_cast<int>(d);
+  g1.batch = t_local;
+  g1.A = X;
+  g1.B = A;
+  g1.C = Z;
+  g1.C2 = Y;
+  g1.bias = b1;
+  g1.sBias = m_i;
+  g1.lda = d;
+  g1.ldb = m_i;
+  g1.ldc = m_i;
+  g1.sA = 0;
+  g1.sB = d * m_i;
+  g1.sC = n * m_i;
+  const int epi1 = b1 != nullptr ? tpmlp::EPI_BIAS_GELU_ZY : tpmlp::EPI_GELU_ZY;
+  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, epi1, stream));
+  if (st) return st;
+
+  // P_i = Y_i·B_i: A = Y_i [n,m_i] (K-major), B = B_i [m_i,d] (N-major).
+  tpmlp::GemmProblem g2{};
+  g2.M = static_cast<int>(n);
+  g2.N = static_cast<int>(d);
+  g2.K = static_cast<int>(m_i);
+  g2.batch = t_local;
+  g2.A = Y;
+  g2.B = B;
+  g2.C = P;
+  g2.lda = m_i;
+  g2.ldb = d;
+  g2.ldc = d;
+  g2.sA = n * m_i;
+  g2.sB = m_i * d;
+  g2.sC = n * d;
+  return hip_status(gemm(dt, g2, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+}
+
+int reduce_impl(hipStream_t stream, int in_dt, int out_dt, int32_t t, int64_t rows, int64_t cols,
+                const void* partials, const void* bias, void* out) {
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return TPMLP_ERR_DTYPE;
+  if (t < 1 || rows < 0 || cols < 1) return TPMLP_ERR_SHAPE;
+  if (rows > 0 && cols > (int64_t{1} << 62) / rows) return TPMLP_ERR_SHAPE;
+  const int64_t count = rows * cols;
+  if (count > (int64_t{1} << 62) / t) return TPMLP_ERR_SHAPE;
+  if (count == 0) return TPMLP_OK;
+  if (partials == nullptr || out == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(partials, elem_size(in_dt)) || !aligned(out, elem_size(out_dt))) return TPMLP_ERR_ALIGN;
+  if (bias != nullptr && !aligned(bias, elem_size(out_dt))) return TPMLP_ERR_ALIGN;
+  return hip_status(tpmlp::launch_reduce_partials(in_dt, out_dt, t, count, partials, out, bias, cols, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,48 +146,17 @@ const char* tpmlp_status_string(int status) {
 
 int tpmlp_fwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
               const void* X, const void* A, const void* B, void* Z, void* Y, void* P) {
+  return fwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, nullptr, Z, Y, P);
+}
+
+int tpmlp_fwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+                   const void* X, const void* A, const void* B, const void* b1, void* Z, void* Y, void* P) {
   int st = check_mlp_dims(dt, n, d, m_i, t_local);
   if (st) return st;
   if (n == 0) return TPMLP_OK;
-  st = check_ptrs(dt, {X, A, B, Z, Y, P});
+  st = check_ptrs(dt, {b1});
   if (st) return st;
-
-  // Z_i = X·A_i and Y_i = GeLU(Z_i): A = X [n,d] (K-major), B = A_i [d,m_i]
-  // (N-major), batched over shards with X shared.
-  tpmlp::GemmProblem g1{};
-  g1.M = static_cast<int>(n);
-  g1.N = static_cast<int>(m_i);
-  g1.K = static_cast<int>(d);
-  g1.batch = t_local;
-  g1.A = X;
-  g1.B = A;
-  g1.C = Z;
-  g1.C2 = Y;
-  g1.lda = d;
-  g1.ldb = m_i;
-  g1.ldc = m_i;
-  g1.sA = 0;
-  g1.sB = d * m_i;
-  g1.sC = n * m_i;
-  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_GELU_ZY, stream));
-  if (st) return st;
-
-  // P_i = Y_i·B_i: A = Y_i [n,m_i] (K-major), B = B_i [m_i,d] (N-major).
-  tpmlp::GemmProblem g2{};
-  g2.M = static_cast<int>(n);
-  g2.N = static_cast<int>(d);
-  g2.K = static_cast<int>(m_i);
-  g2.batch = t_local;
-  g2.A = Y;
-  g2.B = B;
-  g2.C = P;
-  g2.lda = m_i;
-  g2.ldb = d;
-  g2.ldc = d;
-  g2.sA = n * m_i;
-  g2.sB = m_i * d;
-  g2.sC = n * d;
-  return hip_status(gemm(dt, g2, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+  return fwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, b1, Z, Y, P);
 }
 
 size_t tpmlp_bwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
@@ -241,15 +274,39 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
 
 int tpmlp_reduce_partials(hipStream_t stream, int in_dt, int out_dt, int32_t t, int64_t rows,
                           int64_t cols, const void* partials, void* out) {
-  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return TPMLP_ERR_DTYPE;
-  if (t < 1 || rows < 0 || cols < 1) return TPMLP_ERR_SHAPE;
+  return reduce_impl(stream, in_dt, out_dt, t, rows, cols, partials, nullptr, out);
+}
+
+int tpmlp_reduce_partials_bias(hipStream_t stream, int in_dt, int out_dt, int32_t t, int64_t rows,
+                               int64_t cols, const void* partials, const void* bias, void* out) {
+  if (bias == nullptr) return TPMLP_ERR_NULLPTR;
+  return reduce_impl(stream, in_dt, out_dt, t, rows, cols, partials, bias, out);
+}
+
+size_t tpmlp_bias_grad_workspace_bytes(int32_t t, int64_t rows, int64_t cols) {
+  if (t < 1 || rows <= 0 || cols <= 0) return 0;
+  return static_cast<size_t>(t) * static_cast<size_t>(tpmlp::bias_grad_chunks(rows)) *
+         static_cast<size_t>(cols) * sizeof(float);
+}
+
+int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,
+                    float* db, void* ws, size_t ws_bytes) {
+  if (!valid_dt(dt)) return TPMLP_ERR_DTYPE;
+  if (t < 1 || rows < 0 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return TPMLP_ERR_SHAPE;
   if (rows > 0 && cols > (int64_t{1} << 62) / rows) return TPMLP_ERR_SHAPE;
-  const int64_t count = rows * cols;
-  if (count > (int64_t{1} << 62) / t) return TPMLP_ERR_SHAPE;
-  if (count == 0) return TPMLP_OK;
-  if (partials == nullptr || out == nullptr) return TPMLP_ERR_NULLPTR;
-  if (!aligned(partials, elem_size(in_dt)) || !aligned(out, elem_size(out_dt))) return TPMLP_ERR_ALIGN;
-  return hip_status(tpmlp::launch_reduce_partials(in_dt, out_dt, t, count, partials, out, stream));
+  if (rows * cols > (int64_t{1} << 62) / t) return TPMLP_ERR_SHAPE;
+  // launch grid limits: chunk × column-block blocks in x, shards in y
+  if (t > 65535 || ((cols + 31) / 32) * tpmlp::bias_grad_chunks(rows) > kMaxDim) return TPMLP_ERR_SHAPE;
+  if (db == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(db, 4)) return TPMLP_ERR_ALIGN;
+  if (rows > 0) {
+    if (g == nullptr) return TPMLP_ERR_NULLPTR;
+    if (!aligned(g, elem_size(dt))) return TPMLP_ERR_ALIGN;
+    const size_t need = tpmlp_bias_grad_workspace_bytes(t, rows, cols);
+    if (ws == nullptr || ws_bytes < need) return TPMLP_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return TPMLP_ERR_ALIGN;
+  }
+  return hip_status(tpmlp::launch_bias_grad(dt, t, rows, cols, g, db, static_cast<float*>(ws), stream));
 }
 
 size_t tpmlp_sp_workspace_bytes(int64_t s, int64_t h) {
@@ -297,6 +354,7 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
   p.dgamma = a->dgamma;
   p.dbeta = a->dbeta;
   p.ws = static_cast<float*>(a->ws);
+  p.bias = a->phase == TPMLP_SP_DROPRES_FWD ? a->bias : nullptr;
 
   const uintptr_t al = 16;
   auto ok = [&](std::initializer_list<const void*> ps) {
@@ -314,6 +372,7 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
       break;
     case TPMLP_SP_DROPRES_FWD:
       st = ok({a->partials, a->x, a->out});
+      if (!st && a->bias != nullptr && !aligned(a->bias, al)) st = TPMLP_ERR_ALIGN;
       break;
     case TPMLP_SP_DROPRES_BWD:
       st = ok({a->g_out, a->dS});

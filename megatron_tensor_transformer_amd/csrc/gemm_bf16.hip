@@ -55,6 +55,8 @@ struct alignas(64) KArgs {
   void* C;
   void* C2;
   const bf16* Zin;
+  const bf16* bias;
+  int64_t sBias;
   int M, N, K;
   int tiles_m, tiles_n, batch;
   int64_t lda, ldb, ldc;
@@ -304,6 +306,7 @@ __device__ __forceinline__ i32x2 pack4_bf16(float a, float b, float c, float d) 
 // Epilogue staging region (per wave, 128 rows × 64 columns of bf16, 128 B per
 // row): chunk c (8 columns) of row r sits at slot c ^ (r & 7).
 constexpr int QROW = 128, QBYTES = 128 * QROW;
+static_assert(NWAVE * (QBYTES + 128) <= LDS_BYTES, "epilogue staging and bias exceed the LDS");
 __device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk, int half) {
   return qbase + row * QROW + ((chunk ^ (row & 7)) << 4) + half * 8;
 }
@@ -427,7 +430,21 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
     const uint32_t qbase = lds_base + wave * QBYTES;
     const int64_t cbase = static_cast<int64_t>(batch) * a.sC;
     const int qm0 = m0 + wm * 128, qn0 = n0 + wn * 64;
-    constexpr int PASSES = EPI == EPI_GELU_ZY ? 2 : 1;
+    constexpr bool ZY = EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY;
+    constexpr int PASSES = ZY ? 2 : 1;
+    // column bias (EPI_BIAS_GELU_ZY): the wave's 64 bias values are staged
+    // in LDS past the eight staging regions and read back per row block, so
+    // they hold no registers across the passes (N is a multiple of 8, so a
+    // 4-column group is inside N whenever its first column is)
+    const uint32_t bbase = lds_base + NWAVE * QBYTES + wave * 128;
+    if constexpr (EPI == EPI_BIAS_GELU_ZY) {
+      if (lane < 16) {
+        const int col = qn0 + lane * 4;
+        const bf16* bias = a.bias + static_cast<int64_t>(batch) * a.sBias;
+        const i32x2 b = col < a.N ? *reinterpret_cast<const i32x2*>(bias + col) : i32x2{0, 0};
+        asm volatile("ds_write_b64 %0, %1" ::"v"(bbase + lane * 8), "v"(b) : "memory");
+      }
+    }
 
     if constexpr (EPI == EPI_GELU_GRAD) {
       // Stage this region's stored Z (same layout) with 16-B DMA loads:
@@ -452,6 +469,16 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 #pragma unroll
       for (int i = 0; i < FA; ++i) {
         i32x2 zr[FB][4];
+        if constexpr (EPI == EPI_BIAS_GELU_ZY) {
+#pragma unroll
+          for (int j = 0; j < FB; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              asm volatile("ds_read_b64 %0, %1" : "=v"(zr[j][q]) : "v"(bbase + (j * 32 + q * 8 + half * 4) * 2));
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(zr[0][0]), "+v"(zr[0][1]), "+v"(zr[0][2]), "+v"(zr[0][3]), "+v"(zr[1][0]),
+                         "+v"(zr[1][1]), "+v"(zr[1][2]), "+v"(zr[1][3])::"memory");
+        }
         if constexpr (EPI == EPI_GELU_GRAD) {
 #pragma unroll
           for (int j = 0; j < FB; ++j)
@@ -474,7 +501,15 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
           float v[16];
 #pragma unroll
           for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[i][j][e]));
-          if constexpr (EPI == EPI_GELU_ZY) {
+          if constexpr (EPI == EPI_BIAS_GELU_ZY) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bf16x4 bq = __builtin_bit_cast(bf16x4, zr[j][q]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[4 * q + e] += bf2f(bq[e]);
+            }
+          }
+          if constexpr (ZY) {
             if (pass == 1) {
 #pragma unroll
               for (int e = 0; e < 16; ++e) v[e] = gelu_fast(v[e]);
@@ -566,6 +601,8 @@ KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
   k.C = p.C;
   k.C2 = p.C2;
   k.Zin = static_cast<const bf16*>(p.Zin);
+  k.bias = static_cast<const bf16*>(p.bias);
+  k.sBias = p.sBias;
   k.M = p.M;
   k.N = p.N;
   k.K = p.K;
@@ -622,6 +659,8 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
   const bool same = is(k1, k0.a_order, k0.b_order, k0.epi);
   if (same && is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
     return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
+  if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
+    return launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY>(g, stream);
   if (same && is(k0, KMAJ, MNMAJ, EPI_STORE))
     return launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE>(g, stream);
   if (same && is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))

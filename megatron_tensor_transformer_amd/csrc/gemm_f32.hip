@@ -19,6 +19,8 @@ struct F32Args {
   float* C;
   float* C2;
   const float* Zin;
+  const float* bias;
+  int64_t sBias;
   int M, N, K;
   int tiles_m, tiles_n;
   int64_t lda, ldb, ldc;
@@ -87,10 +89,11 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(F32Args a) {
       const int col = n0 + tx * 4 + j;
       if (col >= a.N) continue;
       const int64_t off = cb + static_cast<int64_t>(row) * a.ldc + col;
-      const float x = acc[i][j];
+      float x = acc[i][j];
+      if constexpr (EPI == EPI_BIAS_GELU_ZY) x += a.bias[static_cast<int64_t>(batch) * a.sBias + col];
       if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_F32) {
         a.C[off] = x;
-      } else if constexpr (EPI == EPI_GELU_ZY) {
+      } else if constexpr (EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY) {
         a.C[off] = x;
         a.C2[off] = gelu_precise(x);
       } else {
@@ -118,6 +121,8 @@ hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int e
   k.C = static_cast<float*>(p.C);
   k.C2 = static_cast<float*>(p.C2);
   k.Zin = static_cast<const float*>(p.Zin);
+  k.bias = static_cast<const float*>(p.bias);
+  k.sBias = p.sBias;
   k.M = p.M;
   k.N = p.N;
   k.K = p.K;
@@ -131,6 +136,8 @@ hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int e
   k.sC = p.sC;
   if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_GELU_ZY)
     return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY>(k, p.batch, stream);
+  if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_BIAS_GELU_ZY)
+    return launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY>(k, p.batch, stream);
   if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_STORE)
     return launch_t<KMAJ, MNMAJ, EPI_STORE>(k, p.batch, stream);
   if (a_order == KMAJ && b_order == KMAJ && epi == EPI_GELU_GRAD)

@@ -18,7 +18,8 @@ enum Epilogue {
   EPI_STORE = 0,      // C = acc (dtype of the path)
   EPI_STORE_F32 = 1,  // C = acc as fp32 (weight gradients)
   EPI_GELU_ZY = 2,    // C = acc (Z), C2 = GeLU(acc) (Y)
-  EPI_GELU_GRAD = 3   // C = acc ⊙ GeLU'(Zin) (D)
+  EPI_GELU_GRAD = 3,  // C = acc ⊙ GeLU'(Zin) (D)
+  EPI_BIAS_GELU_ZY = 4  // z = acc + bias[col]: C = z (Z), C2 = GeLU(z) (Y)
 };
 
 struct GemmProblem {
@@ -29,6 +30,8 @@ struct GemmProblem {
   void* C;
   void* C2;          // EPI_GELU_ZY: Y
   const void* Zin;   // EPI_GELU_GRAD: stored Z, same layout as C
+  const void* bias;  // EPI_BIAS_GELU_ZY: [N] per batch entry, path dtype
+  int64_t sBias;     // its per-batch stride in elements
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;  // per-batch strides in elements (0 = shared operand)
 };
@@ -54,8 +57,14 @@ hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int e
                            hipStream_t stream);
 
 // out = Σ_i partials[i]; dtypes: 0 = f32, 1 = bf16.
+// out = Σ_i partials[i] (+ bias[col], bias NULL or [cols] of out_dt)
 hipError_t launch_reduce_partials(int in_dt, int out_dt, int t, int64_t count,
-                                  const void* partials, void* out, hipStream_t stream);
+                                  const void* partials, void* out, const void* bias, int64_t cols,
+                                  hipStream_t stream);
+// db[i][c] = Σ_r g[i][r][c] (fp32), via ws of t · bias_grad_chunks(rows) · cols floats
+int64_t bias_grad_chunks(int64_t rows);
+hipError_t launch_bias_grad(int dt, int t, int64_t rows, int64_t cols, const void* g, float* db, float* ws,
+                            hipStream_t stream);
 
 struct SpProblem {
   int phase, dt, t;
@@ -79,6 +88,7 @@ struct SpProblem {
   float* dgamma;
   float* dbeta;
   float* ws;
+  const void* bias;  // DROPRES_FWD: NULL or [h] of dt, added to Σ_i P_i before the dropout
 };
 
 int64_t sp_ln_bwd_row_blocks(int64_t s);

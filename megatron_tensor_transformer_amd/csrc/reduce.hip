@@ -1,12 +1,20 @@
-// out = Σ_{i<t} partials[i]: the one-GPU stand-in for the tensor-parallel
-// all-reduce after the row-parallel GEMM (forward) and of the column-parallel
-// input gradient (backward) -- [TRAIN] RowParallelLinear / ColumnParallelLinear
-// sections; a sum, never a mean ([TUT] §三).
+// out = Σ_{i<t} partials[i] (+ bias): the one-GPU stand-in for the
+// tensor-parallel all-reduce after the row-parallel GEMM (forward) and of the
+// column-parallel input gradient (backward) -- [TRAIN] RowParallelLinear /
+// ColumnParallelLinear sections; a sum, never a mean ([TUT] §三).  The
+// row-parallel layer's bias is not split: it is added once, after the sum
+// ([TRAIN] RowParallelLinear).
 //
 // HBM-bound streaming kernel: each thread owns 8 consecutive elements, issues
 // the 16-B loads of up to 8 partials back to back, then adds them in the fixed
-// order 0..t-1 in fp32 (bit-reproducible), and writes one 16-B (bf16) or
-// 2×16-B (fp32) store.  A scalar kernel covers the tail and unaligned inputs.
+// order 0..t-1 in fp32 (bit-reproducible), adds the bias, and writes one 16-B
+// (bf16) or 2×16-B (fp32) store.  A scalar kernel covers the tail and
+// unaligned inputs.  A thread's column advances by a fixed amount per
+// grid-stride step, so the bias index needs one division per thread.
+//
+// Bias gradient db[i] = Σ_rows g[i] ([TRAIN] custom autograd matmul: the bias
+// gradient is the upstream gradient summed over the tokens), in two fixed-order
+// stages: per 128-row chunk column partials, then a sum over the chunks.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,11 +73,38 @@ __device__ __forceinline__ void store8(float* p, const float (&acc)[8]) {
   reinterpret_cast<f32x4*>(p)[1] = hi;
 }
 
+// the 8 bias values at p (16-B aligned), widened; cached loads (reused)
+__device__ __forceinline__ void bias8(const bf16* p, float (&b)[8]) {
+  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    b[2 * q] = __uint_as_float(u[q] << 16);
+    b[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void bias8(const float* p, float (&b)[8]) {
+  const f32x4 lo = reinterpret_cast<const f32x4*>(p)[0], hi = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    b[q] = lo[q];
+    b[4 + q] = hi[q];
+  }
+}
+
+// bias: NULL or [cols] of Tout; with a bias, cols % 8 == 0 (each vector lies
+// in one row).  col tracks v·8 mod cols.
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(RT) void reduce_vec8_kernel(const Tin* __restrict__ p, Tout* __restrict__ out,
-                                                         int t, int64_t nvec, int64_t count) {
+                                                         int t, int64_t nvec, int64_t count,
+                                                         const Tout* __restrict__ bias, int64_t cols) {
   const int64_t step = static_cast<int64_t>(gridDim.x) * RT;
-  for (int64_t v = static_cast<int64_t>(blockIdx.x) * RT + threadIdx.x; v < nvec; v += step) {
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * RT + threadIdx.x;
+  int64_t col = 0, dcol = 0;
+  if (bias != nullptr) {
+    col = (v0 * 8) % cols;
+    dcol = (step * 8) % cols;
+  }
+  for (int64_t v = v0; v < nvec; v += step) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const Tin* src = p + v * 8;
     for (int i0 = 0; i0 < t; i0 += 8) {
@@ -81,6 +116,14 @@ __global__ __launch_bounds__(RT) void reduce_vec8_kernel(const Tin* __restrict__
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (i < n) in[i].add_to(acc);
+    }
+    if (bias != nullptr) {
+      float b[8];
+      bias8(bias + col, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += b[q];
+      col += dcol;
+      if (col >= cols) col -= cols;
     }
     store8(out + v * 8, acc);
   }
@@ -97,23 +140,160 @@ __device__ __forceinline__ void st1(T* p, float v) {
   else *p = v;
 }
 
+// 8 consecutive elements at p (16-B aligned), read once: nontemporal
+template <typename T>
+__device__ __forceinline__ void load8nt(const T* p, float (&w)[8]) {
+  Vec8<T> v;
+  v.load(p);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = 0.f;
+  v.add_to(w);
+}
+
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(RT) void reduce_scalar_kernel(const Tin* __restrict__ p, Tout* __restrict__ out,
-                                                           int t, int64_t begin, int64_t count) {
+                                                           int t, int64_t begin, int64_t count,
+                                                           const Tout* __restrict__ bias, int64_t cols) {
   const int64_t step = static_cast<int64_t>(gridDim.x) * RT;
-  for (int64_t e = begin + static_cast<int64_t>(blockIdx.x) * RT + threadIdx.x; e < count; e += step) {
+  const int64_t e0 = begin + static_cast<int64_t>(blockIdx.x) * RT + threadIdx.x;
+  int64_t col = 0, dcol = 0;
+  if (bias != nullptr) {
+    col = e0 % cols;
+    dcol = step % cols;
+  }
+  for (int64_t e = e0; e < count; e += step) {
     float acc = 0.f;
     for (int i = 0; i < t; ++i) acc += ld1(p + static_cast<int64_t>(i) * count + e);
+    if (bias != nullptr) {
+      acc += ld1(bias + col);
+      col += dcol;
+      if (col >= cols) col -= cols;
+    }
     st1(out + e, acc);
   }
 }
 
+// ---------------------------------------------------------------- bias gradient
+// Stage 1: block (x = chunk·ncb + column block, y = i) sums rows
+// [chunk·BG_RC, +BG_RC) of g[i] for BG_CG column groups of W columns; thread (phase r, group c) adds rows
+// r, r + BG_RP, ... in increasing order, then the BG_RP phase sums are added in
+// phase order through LDS.  ws[i][chunk][cols] receives the chunk's sums.
+constexpr int BG_RC = 128, BG_CG = 32, BG_RP = RT / BG_CG;
+
+template <typename T, int W>
+__global__ __launch_bounds__(RT) void bias_grad_partial_kernel(const T* __restrict__ g, float* __restrict__ ws,
+                                                               int64_t rows, int64_t cols, int64_t nchunk,
+                                                               int ncb) {
+  __shared__ float red[BG_RP][BG_CG][W];
+  const int c = threadIdx.x % BG_CG, r = threadIdx.x / BG_CG;
+  const int64_t chunk = blockIdx.x / ncb, i = blockIdx.y;
+  const int64_t col = (static_cast<int64_t>(blockIdx.x % ncb) * BG_CG + c) * W;
+  const int64_t r0 = chunk * BG_RC, r1 = r0 + BG_RC < rows ? r0 + BG_RC : rows;
+  const T* gi = g + i * rows * cols;
+  float s[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) s[k] = 0.f;
+  if (col < cols) {
+    int64_t row = r0 + r;
+    // groups of 4 rows: loads in flight together, added in row order
+    for (; row + 3 * BG_RP < r1; row += 4 * BG_RP) {
+      float w[4][W];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const T* q = gi + (row + u * BG_RP) * cols + col;
+        if constexpr (W == 8) load8nt(q, w[u]);
+        else w[u][0] = ld1(q);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < W; ++k) s[k] += w[u][k];
+    }
+    for (; row < r1; row += BG_RP) {
+      const T* q = gi + row * cols + col;
+      float w[W];
+      if constexpr (W == 8) load8nt(q, w);
+      else w[0] = ld1(q);
+#pragma unroll
+      for (int k = 0; k < W; ++k) s[k] += w[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < W; ++k) red[r][c][k] = s[k];
+  __syncthreads();
+  if (r == 0 && col < cols) {
+    float* o = ws + (i * nchunk + chunk) * cols + col;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      float a = 0.f;
+#pragma unroll
+      for (int q = 0; q < BG_RP; ++q) a += red[q][c][k];
+      o[k] = a;
+    }
+  }
+}
+
+// Stage 2: db[i][c] = Σ_chunk ws[i][chunk][c] in increasing chunk order.
+__global__ __launch_bounds__(RT) void bias_grad_final_kernel(const float* __restrict__ ws, float* __restrict__ db,
+                                                             int64_t t, int64_t cols, int64_t nchunk) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * RT + threadIdx.x;
+  if (e >= t * cols) return;
+  const int64_t i = e / cols, c = e - i * cols;
+  const float* w = ws + i * nchunk * cols + c;
+  float s = 0.f;
+  int64_t k = 0;
+  for (; k + 8 <= nchunk; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = w[(k + u) * cols];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; k < nchunk; ++k) s += w[k * cols];
+  db[e] = s;
+}
+
+__global__ __launch_bounds__(RT) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * RT + threadIdx.x;
+  if (e < n) p[e] = 0.f;
+}
+
+template <typename T>
+hipError_t run_bias_grad(int t, int64_t rows, int64_t cols, const void* g, float* db, float* ws,
+                         hipStream_t stream) {
+  if (rows == 0) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((t * cols + RT - 1) / RT)), dim3(RT), 0,
+                       stream, db, static_cast<int64_t>(t) * cols);
+    return hipGetLastError();
+  }
+  const int64_t nchunk = bias_grad_chunks(rows);
+  const T* gp = static_cast<const T*>(g);
+  const bool vec = cols % 8 == 0 && reinterpret_cast<uintptr_t>(g) % 16 == 0;
+  const int64_t w = vec ? 8 : 1;
+  const int ncb = static_cast<int>((cols / w + BG_CG - 1) / BG_CG);
+  const dim3 grid(static_cast<unsigned>(ncb * nchunk), static_cast<unsigned>(t));
+  if (vec)
+    hipLaunchKernelGGL((bias_grad_partial_kernel<T, 8>), grid, dim3(RT), 0, stream, gp, ws, rows, cols, nchunk,
+                       ncb);
+  else
+    hipLaunchKernelGGL((bias_grad_partial_kernel<T, 1>), grid, dim3(RT), 0, stream, gp, ws, rows, cols, nchunk,
+                       ncb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bias_grad_final_kernel, dim3(static_cast<unsigned>((t * cols + RT - 1) / RT)), dim3(RT), 0,
+                     stream, ws, db, static_cast<int64_t>(t), cols, nchunk);
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tout>
-hipError_t run(int t, int64_t count, const void* partials, void* out, hipStream_t stream) {
+hipError_t run(int t, int64_t count, const void* partials, void* out, const void* bias_v, int64_t cols,
+               hipStream_t stream) {
   const Tin* p = static_cast<const Tin*>(partials);
   Tout* o = static_cast<Tout*>(out);
+  const Tout* bias = static_cast<const Tout*>(bias_v);
   const bool aligned = (reinterpret_cast<uintptr_t>(p) % 16 == 0) &&
-                       (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (count % 8 == 0);
+                       (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (count % 8 == 0) &&
+                       (bias == nullptr || (cols % 8 == 0 && reinterpret_cast<uintptr_t>(bias) % 16 == 0));
   int64_t done = 0;
   if (aligned) {
     const int64_t nvec = count / 8;
@@ -121,7 +301,7 @@ hipError_t run(int t, int64_t count, const void* partials, void* out, hipStream_
     if (blocks > 8192) blocks = 8192;
     if (blocks > 0) {
       hipLaunchKernelGGL((reduce_vec8_kernel<Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(RT), 0,
-                         stream, p, o, t, nvec, count);
+                         stream, p, o, t, nvec, count, bias, cols);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -131,7 +311,7 @@ hipError_t run(int t, int64_t count, const void* partials, void* out, hipStream_
     int64_t blocks = (count - done + RT - 1) / RT;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL((reduce_scalar_kernel<Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(RT), 0,
-                       stream, p, o, t, done, count);
+                       stream, p, o, t, done, count, bias, cols);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -140,12 +320,21 @@ hipError_t run(int t, int64_t count, const void* partials, void* out, hipStream_
 }  // namespace
 
 hipError_t launch_reduce_partials(int in_dt, int out_dt, int t, int64_t count, const void* partials,
-                                  void* out, hipStream_t stream) {
+                                  void* out, const void* bias, int64_t cols, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
-  if (in_dt == 1 && out_dt == 1) return run<bf16, bf16>(t, count, partials, out, stream);
-  if (in_dt == 1 && out_dt == 0) return run<bf16, float>(t, count, partials, out, stream);
-  if (in_dt == 0 && out_dt == 1) return run<float, bf16>(t, count, partials, out, stream);
-  return run<float, float>(t, count, partials, out, stream);
+  if (in_dt == 1 && out_dt == 1) return run<bf16, bf16>(t, count, partials, out, bias, cols, stream);
+  if (in_dt == 1 && out_dt == 0) return run<bf16, float>(t, count, partials, out, bias, cols, stream);
+  if (in_dt == 0 && out_dt == 1) return run<float, bf16>(t, count, partials, out, bias, cols, stream);
+  return run<float, float>(t, count, partials, out, bias, cols, stream);
+}
+
+int64_t bias_grad_chunks(int64_t rows) { return rows <= 0 ? 0 : (rows + BG_RC - 1) / BG_RC; }
+
+hipError_t launch_bias_grad(int dt, int t, int64_t rows, int64_t cols, const void* g, float* db, float* ws,
+                            hipStream_t stream) {
+  if (t <= 0 || cols <= 0) return hipSuccess;
+  return dt == 1 ? run_bias_grad<bf16>(t, rows, cols, g, db, ws, stream)
+                 : run_bias_grad<float>(t, rows, cols, g, db, ws, stream);
 }
 
 }  // namespace tpmlp

@@ -2,8 +2,13 @@
 // f/g operator table; [EFF] §3.5.1 backward chain; [TRAIN] LayerNorm and
 // Dropout sections):
 //   forward   U = LN(x) (row blocks of all t sequence shards = the AllGather),
-//             out = x + dropout_p(Σ_i P_i)   (sum, then the row blocks are the
-//                                             ReduceScatter's shards)
+//             out = x + dropout_p(Σ_i P_i + b)  (sum, then the row blocks are
+//                                             the ReduceScatter's shards; the
+//                                             optional bias b of the
+//                                             row-parallel layer is added after
+//                                             the reduction and fused with the
+//                                             dropout and the residual add,
+//                                             [EFF] §4.2)
 //   backward  dS = g_out ⊙ mask / (1-p)      (the MLP's upstream gradient)
 //             dx = g_out + LN'(Σ_i dU_i);  dγ = Σ_rows dU⊙x̂;  dβ = Σ_rows dU
 //
@@ -234,19 +239,37 @@ __global__ __launch_bounds__(LNB_THREADS) void ln_fwd_kernel(SpProblem p) {
 }
 
 // ------------------------------------------------------------------ dropout + residual
-// phase 1: out = x + keep·scale·Σ_i P_i ;  phase 2: dS = g_out·keep·scale
+// phase 1: out = x + keep·scale·(Σ_i P_i + b) ;  phase 2: dS = g_out·keep·scale
+// With a bias, a thread's column chunk advances by a fixed amount per
+// grid-stride step (h % 8 == 0, so a chunk lies in one row).
 template <typename T, bool FWD>
 __global__ __launch_bounds__(SP_THREADS) void dropres_kernel(SpProblem p) {
   const int64_t nchunk = p.s * p.h / 8;
   const int64_t count = p.s * p.h;
   const int64_t step = static_cast<int64_t>(gridDim.x) * SP_THREADS;
-  for (int64_t ch = static_cast<int64_t>(blockIdx.x) * SP_THREADS + threadIdx.x; ch < nchunk; ch += step) {
+  const int64_t ch0 = static_cast<int64_t>(blockIdx.x) * SP_THREADS + threadIdx.x;
+  const T* bias = FWD ? static_cast<const T*>(p.bias) : nullptr;
+  const int64_t hc = p.h / 8;
+  int64_t cc = 0, dcc = 0;
+  if (bias != nullptr) {
+    cc = ch0 % hc;
+    dcc = step % hc;
+  }
+  for (int64_t ch = ch0; ch < nchunk; ch += step) {
     const int64_t e = ch * 8;  // local element index; rows are contiguous
     float v[8];
     if constexpr (FWD) {
       float xr[8];
       load8(static_cast<const T*>(p.x) + e, xr);  // in flight with the partials
       sum_partials8(static_cast<const T*>(p.partials) + e, count, p.t, v);
+      if (bias != nullptr) {
+        float b[8];
+        load8<T, false>(bias + cc * 8, b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] += b[k];
+        cc += dcc;
+        if (cc >= hc) cc -= hc;
+      }
       const uint32_t keep = keep8(static_cast<uint64_t>(p.row0 * p.h + e), p.seed, p.drop_threshold);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = xr[k] + (((keep >> k) & 1u) ? v[k] * p.keep_scale : 0.0f);

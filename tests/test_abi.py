@@ -30,7 +30,8 @@ def L():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("tpmlp_fwd", "tpmlp_bwd", "tpmlp_reduce_partials", "tpmlp_ln_sp"):
+    for n in ("tpmlp_fwd", "tpmlp_bwd", "tpmlp_reduce_partials", "tpmlp_ln_sp", "tpmlp_fwd_bias",
+              "tpmlp_reduce_partials_bias", "tpmlp_bias_grad", "tpmlp_bias_grad_workspace_bytes"):
         assert n in names
 
 
@@ -41,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 1
+    assert L.tpmlp_abi_version() == 2
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert L.tpmlp_status_string(s)
 
@@ -66,6 +67,47 @@ def test_fwd_validation(L):
     # fp32 accepts any row length and 4-byte alignment
     assert _fwd(L, dt=0, d=3, mi=5, ptr=0) == tp.ERR_NULLPTR
     assert _fwd(L, dt=0, d=3, mi=5, ptr=0x1002) == tp.ERR_ALIGN
+
+
+def test_fwd_bias_validation(L):
+    p = ctypes.c_void_p(0x1000)
+
+    def call(b1=p, dt=1, n=64, d=64, mi=64, t=2):
+        return L.tpmlp_fwd_bias(None, dt, n, d, mi, t, p, p, p, b1, p, p, p)
+    assert call(b1=None) == tp.ERR_NULLPTR
+    assert call(b1=ctypes.c_void_p(0x1008)) == tp.ERR_ALIGN
+    assert call(dt=0, b1=ctypes.c_void_p(0x1002)) == tp.ERR_ALIGN
+    assert call(mi=20) == tp.ERR_ALIGN
+    assert call(n=-1) == tp.ERR_SHAPE
+    assert call(n=0, b1=None) == 0  # empty input: nothing to do
+
+
+def test_reduce_bias_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    assert L.tpmlp_reduce_partials_bias(None, 1, 1, 8, 16, 16, p, None, p) == tp.ERR_NULLPTR
+    assert L.tpmlp_reduce_partials_bias(None, 1, 0, 8, 16, 16, p, ctypes.c_void_p(0x1002), p) == tp.ERR_ALIGN
+    assert L.tpmlp_reduce_partials_bias(None, 1, 1, 0, 16, 16, p, p, p) == tp.ERR_SHAPE
+    assert L.tpmlp_reduce_partials_bias(None, 1, 1, 8, 0, 16, None, p, None) == 0
+
+
+def test_bias_grad_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    # one fp32 [cols] partial per 128-row chunk and shard
+    assert L.tpmlp_bias_grad_workspace_bytes(8, 8192, 1536) == 8 * 64 * 1536 * 4
+    assert L.tpmlp_bias_grad_workspace_bytes(1, 129, 5) == 2 * 5 * 4
+    assert L.tpmlp_bias_grad_workspace_bytes(1, 0, 5) == 0
+    need = L.tpmlp_bias_grad_workspace_bytes(2, 300, 64)
+    assert L.tpmlp_bias_grad(None, 5, 2, 300, 64, p, p, p, need) == tp.ERR_DTYPE
+    assert L.tpmlp_bias_grad(None, 1, 0, 300, 64, p, p, p, need) == tp.ERR_SHAPE
+    assert L.tpmlp_bias_grad(None, 1, 2, -1, 64, p, p, p, need) == tp.ERR_SHAPE
+    assert L.tpmlp_bias_grad(None, 1, 2, 300, 0, p, p, p, need) == tp.ERR_SHAPE
+    assert L.tpmlp_bias_grad(None, 1, 70000, 300, 64, p, p, p, need) == tp.ERR_SHAPE
+    assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, None, p, need) == tp.ERR_NULLPTR
+    assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, None, p, p, need) == tp.ERR_NULLPTR
+    assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, p, p, need - 4) == tp.ERR_WORKSPACE
+    assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, p, None, need) == tp.ERR_WORKSPACE
+    assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, ctypes.c_void_p(0x1001), p, p, need) == tp.ERR_ALIGN
+    assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, ctypes.c_void_p(0x1002), p, need) == tp.ERR_ALIGN
 
 
 def test_bwd_validation(L):
@@ -117,6 +159,7 @@ def test_sp_validation(L):
     assert call(_sp(ln_out=0)) == tp.ERR_NULLPTR
     assert call(_sp(x=0x1004)) == tp.ERR_ALIGN
     assert call(_sp(s=0)) == 0
+    assert call(_sp(phase=tp.SP_DROPRES_FWD, partials=0x1000, out=0x1000, bias=0x1008)) == tp.ERR_ALIGN
     assert call(_sp(phase=tp.SP_LN_BWD, dU_partials=0x1000, g_out=0x1000, dx=0x1000,
                     dgamma=0x1000, dbeta=0x1000, ws=0x1000, ws_bytes=16)) == tp.ERR_WORKSPACE
     # one [2, h] fp32 slot per LN-backward block: min(s, 512) blocks

@@ -10,6 +10,8 @@ Recipe (the workloads of the tensor-parallel MLP shard, no dataset involved):
     B (full [m, d]), G, then for the sequence-parallel block γ and β.
   * The trillion-parameter-shaped case draws shard 0's A_0 [d, m/t] and
     B_0 [m/t, d] directly (the full A would not fit in host memory).
+  * Biases b1 [m], b2 [d] (bias_inputs) come from a stream of their own,
+    default_rng([seed, 1]), with std 0.5.
   * fp64 -> fp32 by round-to-nearest-even (numpy), fp32 -> bf16 by
     round-to-nearest-even on the bit pattern.  The oracle receives the rounded
     values upcast exactly to fp64.
@@ -119,6 +121,23 @@ def sp_inputs(s, h, m, t, dtype="bf16", seed=0, x_std=X_STD, w_std=W_STD,
     beta = f32_to_bf16_bits(b32) if dtype == "bf16" else b32
     return {"x": Tensor(x, dtype), "A": Tensor(A, dtype), "B": Tensor(B, dtype),
             "G": Tensor(G, dtype), "gamma": Tensor(gamma, dtype), "beta": Tensor(beta, dtype)}
+
+
+# Bias standard deviation: comparable to the pre-activation spread at the
+# workloads' widths (0.02·√3072 ≈ 1.1), so the bias moves GeLU's operating
+# point visibly.  (The layers initialise their biases to zero; a zero bias
+# would test nothing.)
+B_STD = 0.5
+
+
+def bias_inputs(m, d, dtype="bf16", seed=0, std=B_STD):
+    """b1 [m] (the column-parallel layer's bias) and b2 [d] (the row-parallel
+    layer's), from their own stream numpy.random.default_rng([seed, 1]) so the
+    other tensors' draws are unchanged."""
+    rng = np.random.default_rng([seed, 1])
+    b1 = _draw(rng, (m,), std, dtype)
+    b2 = _draw(rng, (d,), std, dtype)
+    return {"b1": Tensor(b1, dtype), "b2": Tensor(b2, dtype)}
 
 
 def config_inputs(name, seed=0):
