@@ -162,13 +162,16 @@ int tpmlp_reduce_partials_bias(hipStream_t stream, int in_dt, int out_dt, int32_
  *
  *   dt    dtype of g (TPMLP_BF16 or TPMLP_F32)
  *   g     [t, rows, cols]; db [t, cols] fp32
- *   The sum is fp32 in a fixed order (column partials of 128-row chunks,
- *   rows in increasing order within each of 8 row phases, then the chunks in
- *   increasing order), so results are bit-reproducible.  rows == 0 sets db to
+ *   The sum is fp32 in a fixed order, so results are bit-reproducible:
+ *   column partials of 128-row chunks (rows in increasing order within each
+ *   of 8 interleaved row phases, the phases added in order), then the chunk
+ *   partials in 8 consecutive ranges (each in increasing order, the ranges
+ *   added in order).  rows == 0 sets db to
  *   zero and needs no g or workspace.
  *   ws / ws_bytes: at least tpmlp_bias_grad_workspace_bytes(t, rows, cols)
  *   bytes, 4-byte aligned.
- *   Limits: t <= 65535; ceil(cols/32)·ceil(rows/128) < 2^31.
+ *   Limits: t <= 65535; ceil(cols/32)·ceil(rows/128) < 2^31;
+ *   ceil(t·cols/32) < 2^31.
  */
 size_t tpmlp_bias_grad_workspace_bytes(int32_t t, int64_t rows, int64_t cols);
 int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,

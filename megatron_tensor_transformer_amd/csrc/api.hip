@@ -296,7 +296,9 @@ int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t
   if (rows > 0 && cols > (int64_t{1} << 62) / rows) return TPMLP_ERR_SHAPE;
   if (rows * cols > (int64_t{1} << 62) / t) return TPMLP_ERR_SHAPE;
   // launch grid limits: chunk × column-block blocks in x, shards in y
-  if (t > 65535 || ((cols + 31) / 32) * tpmlp::bias_grad_chunks(rows) > kMaxDim) return TPMLP_ERR_SHAPE;
+  if (t > 65535 || ((cols + 31) / 32) * tpmlp::bias_grad_chunks(rows) > kMaxDim ||
+      (t * cols + 31) / 32 > kMaxDim)
+    return TPMLP_ERR_SHAPE;
   if (db == nullptr) return TPMLP_ERR_NULLPTR;
   if (!aligned(db, 4)) return TPMLP_ERR_ALIGN;
   if (rows > 0) {

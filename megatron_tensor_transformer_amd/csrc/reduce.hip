@@ -14,7 +14,9 @@
 //
 // Bias gradient db[i] = Σ_rows g[i] ([TRAIN] custom autograd matmul: the bias
 // gradient is the upstream gradient summed over the tokens), in two fixed-order
-// stages: per 128-row chunk column partials, then a sum over the chunks.
+// stages: per 128-row chunk column partials, then a sum over the chunks.  Both
+// stages split their sums into 8 interleaved or consecutive parts to have
+// enough loads in flight, and combine the parts in a fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -233,24 +235,39 @@ __global__ __launch_bounds__(RT) void bias_grad_partial_kernel(const T* __restri
   }
 }
 
-// Stage 2: db[i][c] = Σ_chunk ws[i][chunk][c] in increasing chunk order.
+// Stage 2: db[i][c] = Σ_chunk ws[i][chunk][c].  A block takes BG_CG of the
+// t·cols outputs; thread (range g, column c) sums chunk range g of BG_RP
+// consecutive ranges in increasing chunk order, then the range sums of each
+// output are added in range order: a fixed order for any launch.
 __global__ __launch_bounds__(RT) void bias_grad_final_kernel(const float* __restrict__ ws, float* __restrict__ db,
                                                              int64_t t, int64_t cols, int64_t nchunk) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * RT + threadIdx.x;
-  if (e >= t * cols) return;
-  const int64_t i = e / cols, c = e - i * cols;
-  const float* w = ws + i * nchunk * cols + c;
+  __shared__ float part[BG_RP][BG_CG];
+  const int c = threadIdx.x % BG_CG, g = threadIdx.x / BG_CG;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * BG_CG + c;
+  const int64_t per = (nchunk + BG_RP - 1) / BG_RP;
+  const int64_t k0 = g * per, k1 = k0 + per < nchunk ? k0 + per : nchunk;
   float s = 0.f;
-  int64_t k = 0;
-  for (; k + 8 <= nchunk; k += 8) {
-    float v[8];
+  if (e < t * cols) {
+    const int64_t i = e / cols, col = e - i * cols;
+    const float* w = ws + i * nchunk * cols + col;
+    int64_t k = k0;
+    for (; k + 4 <= k1; k += 4) {
+      float v[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = w[(k + u) * cols];
+      for (int u = 0; u < 4; ++u) v[u] = w[(k + u) * cols];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; k < k1; ++k) s += w[k * cols];
   }
-  for (; k < nchunk; ++k) s += w[k * cols];
-  db[e] = s;
+  part[g][c] = s;
+  __syncthreads();
+  if (g == 0 && e < t * cols) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < BG_RP; ++q) a += part[q][c];
+    db[e] = a;
+  }
 }
 
 __global__ __launch_bounds__(RT) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -280,8 +297,8 @@ hipError_t run_bias_grad(int t, int64_t rows, int64_t cols, const void* g, float
                        ncb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bias_grad_final_kernel, dim3(static_cast<unsigned>((t * cols + RT - 1) / RT)), dim3(RT), 0,
-                     stream, ws, db, static_cast<int64_t>(t), cols, nchunk);
+  hipLaunchKernelGGL(bias_grad_final_kernel, dim3(static_cast<unsigned>((t * cols + BG_CG - 1) / BG_CG)), dim3(RT),
+                     0, stream, ws, db, static_cast<int64_t>(t), cols, nchunk);
   return hipGetLastError();
 }
 
