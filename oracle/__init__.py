@@ -1,5 +1,6 @@
-"""Plain, slow fp64 CPU oracle for the tensor-parallel MLP shard and its
-sequence-parallel LayerNorm / dropout / residual region.
+"""Plain, slow fp64 CPU oracle for the tensor-parallel MLP shard, its
+sequence-parallel LayerNorm / dropout / residual region, and the
+tensor-parallel self-attention shard.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP library
@@ -29,7 +30,11 @@ Parity pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   * philox.*     -- Random123 published known-answer vectors.
   * sp_block.*   -- sharded == unsharded (AllReduce = AllGather∘ReduceScatter),
                     finite differences, torch fp64 autograd.
+  * attention.*  -- torch's fp64 scaled_dot_product_attention and autograd,
+                    finite differences, heads split over shards == unsplit,
+                    uniform attention when the queries are zero, shift
+                    invariance of the keys.
 No function here is "parity unpinned".
 """
 
-from . import mlp, layernorm, philox, sp_block  # noqa: F401
+from . import mlp, layernorm, philox, sp_block, attention  # noqa: F401

@@ -10,6 +10,9 @@ Recipe (the workloads of the tensor-parallel MLP shard, no dataset involved):
     B (full [m, d]), G, then for the sequence-parallel block γ and β.
   * The trillion-parameter-shaped case draws shard 0's A_0 [d, m/t] and
     B_0 [m/t, d] directly (the full A would not fit in host memory).
+  * The attention side (attn_inputs): X [s·b, d], W_qkv [d, 3d], W_proj
+    [d, d], G [s·b, d] drawn in that order with the same deviations; its
+    optional biases from default_rng([seed, 2]).
   * Biases b1 [m], b2 [d] (bias_inputs) come from a stream of their own,
     default_rng([seed, 1]), with std 0.5.
   * fp64 -> fp32 by round-to-nearest-even (numpy), fp32 -> bf16 by
@@ -36,6 +39,10 @@ CONFIGS = {
     # trillion-parameter-shaped layer: h=25600, m=4h, t=8, 2048 tokens, shard 0.
     "gpt1t_t8_shard0": dict(kind="mlp", n=2048, d=25600, m=102400, t=8, dtype="bf16",
                             x_std=X_STD, w_std=W_STD, g_std=G_STD, shards=(0,)),
+    # attention side of the GPT-8.3B-shaped layer: h=3072, 24 heads of 128,
+    # t=8 (3 heads per shard), b=8, s=1024 tokens per sequence, causal.
+    "gpt8p3b_attn_t8": dict(kind="attn", s=1024, b=8, d=3072, heads=24, t=8, dtype="bf16",
+                            causal=True, x_std=X_STD, w_std=W_STD, g_std=G_STD),
     # sequence-parallel block: s=4096, h=4096, m=4h, t=8, LN + dropout 0.1.
     "sp_block_t8": dict(kind="sp", n=4096, d=4096, m=16384, t=8, dtype="bf16",
                         x_std=X_STD, w_std=W_STD, g_std=G_STD,
@@ -140,8 +147,33 @@ def bias_inputs(m, d, dtype="bf16", seed=0, std=B_STD):
     return {"b1": Tensor(b1, dtype), "b2": Tensor(b2, dtype)}
 
 
+def attn_inputs(s, b, d, heads, dtype="bf16", seed=0, x_std=X_STD, w_std=W_STD, g_std=G_STD,
+                bias_std=None):
+    """X [s·b, d] (tokens in [s, b] order), W_qkv [d, 3d], W_proj [d, d],
+    G [s·b, d]; with bias_std also b_qkv [3d] and b_proj [d] from the stream
+    default_rng([seed, 2])."""
+    if d % heads:
+        raise ValueError("d must be divisible by the head count")
+    rng = np.random.default_rng(seed)
+    n = s * b
+    X = _draw(rng, (n, d), x_std, dtype)
+    Wqkv = _draw(rng, (d, 3 * d), w_std, dtype)
+    Wproj = _draw(rng, (d, d), w_std, dtype)
+    G = _draw(rng, (n, d), g_std, dtype)
+    out = {"X": Tensor(X, dtype), "Wqkv": Tensor(Wqkv, dtype), "Wproj": Tensor(Wproj, dtype),
+           "G": Tensor(G, dtype)}
+    if bias_std is not None:
+        rb = np.random.default_rng([seed, 2])
+        out["bqkv"] = Tensor(_draw(rb, (3 * d,), bias_std, dtype), dtype)
+        out["bproj"] = Tensor(_draw(rb, (d,), bias_std, dtype), dtype)
+    return out
+
+
 def config_inputs(name, seed=0):
     c = CONFIGS[name]
+    if c["kind"] == "attn":
+        return attn_inputs(c["s"], c["b"], c["d"], c["heads"], c["dtype"], seed, c["x_std"],
+                           c["w_std"], c["g_std"])
     if c["kind"] == "mlp":
         return mlp_inputs(c["n"], c["d"], c["m"], c["t"], c["dtype"], seed, c["x_std"],
                           c["w_std"], c["g_std"], c.get("shards"))
