@@ -21,7 +21,13 @@
  *           lives) and the custom autograd matmul (its gradient).
  *   [EFF]   notes on "Efficient Large-Scale Language Model Training on GPU
  *           Clusters Using Megatron-LM" (unpurerationalist.github.io), §4.2:
- *           bias + GeLU and bias + dropout + add fused into single kernels.
+ *           bias + GeLU and bias + dropout + add fused into single kernels;
+ *           the sequence-first [s, b, a, h] layout and the fused scale + mask
+ *           + softmax with an implicit causal mask.
+ * The attention entry points also follow [SENSE] §2.1.1 (the multi-head
+ * attention paragraph and module: heads split over shards, qkv
+ * column-parallel without gather, proj row-parallel with a split input) and
+ * [TRAIN] "Attention 层" (S = QKᵀ/√d, A = softmax(S), its gradient).
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers to row-major, contiguous tensors.  Shapes
@@ -52,7 +58,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 2
+#define TPMLP_ABI_VERSION 3
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -250,6 +256,65 @@ typedef struct {
 
 size_t tpmlp_sp_workspace_bytes(int64_t s, int64_t h);
 int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a);
+
+/*
+ * Self-attention shard ([SENSE] §2.1.1; [TRAIN] Attention 层; [EFF] §4.2).
+ * Shard i of the layer owns heads_local consecutive heads of width head_dim
+ * (w = heads_local·head_dim): the column block W_qkv,i [d, 3w] of the QKV
+ * weight, whose columns go head by head as (q | k | v, head_dim), and the
+ * row block W_proj,i [w, d] of the output projection.  Tokens are the rows of
+ * X [n, d], n = s·b, in sequence-first order: row s_idx·b + b_idx.
+ *
+ *   QKV_i = X·W_qkv,i                       [n, 3w]
+ *   per batch entry and head: S = q·kᵀ/√head_dim, with causal != 0 the
+ *   entries of key positions after the query position are −∞; A = softmax
+ *   of each row of S; o = A·v
+ *   O_i  = the heads' o side by side        [n, w]
+ *   P_i  = O_i·W_proj,i                     [n, d]  row-parallel partial;
+ *                                                   Σ_i P_i via
+ *                                                   tpmlp_reduce_partials
+ *   lse_i[b][h][s] = ln Σ_j exp(S_ij)       fp32, kept for the backward
+ * Backward, G = ∂ℓ/∂Σ_i P_i [n, d]:
+ *   dO_i = G·W_proj,iᵀ;  dW_proj,i = O_iᵀ·G (fp32)
+ *   per head: dv = Aᵀ·do;  dS = A ⊙ (do·vᵀ − δ), δ = rowsum(do ⊙ o);
+ *             dq = dS·k/√head_dim;  dk = dSᵀ·q/√head_dim  -> dQKV_i [n, 3w]
+ *   dW_qkv,i = Xᵀ·dQKV_i (fp32);  dX_i = dQKV_i·W_qkv,iᵀ   partial, summed by
+ *                                                   tpmlp_reduce_partials
+ * The attention dropout is not applied (the module on [SENSE] defaults it to
+ * 0).
+ *
+ *   dt          TPMLP_BF16 (flash-attention kernels on the matrix cores, fp32
+ *               softmax statistics) or TPMLP_F32 (fp32 throughout)
+ *   s, b        sequence length (>= 0; 0 enqueues nothing) and batch (>= 1)
+ *   heads_local heads per shard (>= 1); head_dim 64 or 128
+ *   t_local     shards processed by this call (>= 1), stacked on a leading
+ *               axis of every per-shard tensor
+ *   causal      0 (no mask) or 1 (causal)
+ * Layouts: X [n, d]; W_qkv [t_local, d, 3w]; W_proj [t_local, w, d];
+ *   QKV, dQKV [t_local, n, 3w]; O, dO [t_local, n, w]; lse [t_local, b,
+ *   heads_local, s] fp32; P, dXp [t_local, n, d]; dW_qkv [t_local, d, 3w]
+ *   and dW_proj [t_local, w, d] fp32.
+ * Limits: one shard's QKV smaller than 2^31 bytes; t_local·b·heads_local·s
+ *   < 2^31; bf16 needs d % 8 == 0 and 16-byte aligned bases.
+ * Workspace of the backward: tpmlp_attn_bwd_workspace_bytes(...) bytes (the
+ * δ rows), 4-byte aligned.
+ *
+ * tpmlp_attn_core_fwd / _bwd run the attention core alone on a given QKV
+ * (and O, lse, dO): QKV -> O, lse and (QKV, O, lse, dO) -> dQKV.
+ */
+int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
+                   const void* Wproj, void* QKV, void* O, float* lse, void* P);
+size_t tpmlp_attn_bwd_workspace_bytes(int32_t t_local, int64_t s, int64_t b, int32_t heads_local);
+int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
+                   const void* Wproj, const void* QKV, const void* O, const float* lse, const void* G, void* dO,
+                   void* dQKV, float* dWqkv, float* dWproj, void* dXp, void* ws, size_t ws_bytes);
+int tpmlp_attn_core_fwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
+                        int32_t head_dim, int causal, const void* qkv, void* o, float* lse);
+int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
+                        int32_t head_dim, int causal, const void* qkv, const void* o, const float* lse,
+                        const void* d_o, void* dqkv, void* ws, size_t ws_bytes);
 
 /* Status text for a return code; never NULL. */
 const char* tpmlp_status_string(int status);

@@ -63,6 +63,11 @@ SIGNATURES = {
     "tpmlp_bias_grad_workspace_bytes": (_SZ, [_I32, _I64, _I64]),
     "tpmlp_bias_grad": (_I, [_P, _I, _I32, _I64, _I64, _P, _P, _P, _SZ]),
     "tpmlp_sp_workspace_bytes": (_SZ, [_I64, _I64]),
+    "tpmlp_attn_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "tpmlp_attn_bwd_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I32]),
+    "tpmlp_attn_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I] + [_P] * 13 + [_SZ]),
+    "tpmlp_attn_core_fwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P]),
+    "tpmlp_attn_core_bwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _SZ]),
     "tpmlp_ln_sp": (_I, [_P, ctypes.POINTER(SpArgs)]),
     "tpmlp_status_string": (ctypes.c_char_p, [_I]),
     "tpmlp_last_hip_error": (_I, []),
@@ -168,6 +173,39 @@ def tpmlp_bias_grad(g, db, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_bias_grad(_stream(stream), _dt(g), t, rows, cols, _ptr(g), _ptr(db), _ptr(ws),
                                  ws_bytes))
+
+
+def tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, stream=None):
+    """X [s·b, d]; Wqkv [t, d, 3w]; Wproj [t, w, d]; QKV [t, s·b, 3w]; O [t, s·b, w];
+    lse [t, b, heads, s] fp32; P [t, s·b, d]; w = heads·head_dim."""
+    t, d, w3 = Wqkv.shape
+    heads = w3 // 3 // head_dim
+    _check(lib().tpmlp_attn_fwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), _ptr(X),
+                                _ptr(Wqkv), _ptr(Wproj), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(P)))
+
+
+def tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal,
+                   stream=None):
+    t, d, w3 = Wqkv.shape
+    heads = w3 // 3 // head_dim
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().tpmlp_attn_bwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), _ptr(X),
+                                _ptr(Wqkv), _ptr(Wproj), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(G), _ptr(dO),
+                                _ptr(dQKV), _ptr(dWqkv), _ptr(dWproj), _ptr(dXp), _ptr(ws), ws_bytes))
+
+
+def tpmlp_attn_core_fwd(qkv, o, lse, s, b, heads, head_dim, causal, stream=None):
+    """qkv [t, s·b, heads·3·head_dim] -> o [t, s·b, heads·head_dim], lse [t, b, heads, s]."""
+    t = qkv.shape[0]
+    _check(lib().tpmlp_attn_core_fwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), _ptr(qkv),
+                                     _ptr(o), _ptr(lse)))
+
+
+def tpmlp_attn_core_bwd(qkv, o, lse, d_o, dqkv, ws, s, b, heads, head_dim, causal, stream=None):
+    t = qkv.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().tpmlp_attn_core_bwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), _ptr(qkv),
+                                     _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dqkv), _ptr(ws), ws_bytes))
 
 
 def tpmlp_ln_sp(args, stream=None):
@@ -283,3 +321,36 @@ def sp_ln_bwd(dU_partials, g_out, x, gamma, mean, rstd, stream=None):
                dx=_ptr(dx), dgamma=_ptr(dgamma), dbeta=_ptr(dbeta), ws=_ptr(ws), ws_bytes=nb)
     tpmlp_ln_sp(a, stream)
     return dx, dgamma, dbeta
+
+
+def attn_bwd_workspace_bytes(t, s, b, heads):
+    return lib().tpmlp_attn_bwd_workspace_bytes(t, s, b, heads)
+
+
+def attn_fwd(X, Wqkv, Wproj, s, b, head_dim, causal=True, stream=None):
+    """Allocating wrapper: returns QKV, O, lse, P."""
+    t, d, w3 = Wqkv.shape
+    w = w3 // 3
+    n = X.shape[0]
+    QKV = torch.empty((t, n, w3), dtype=X.dtype, device=X.device)
+    O = torch.empty((t, n, w), dtype=X.dtype, device=X.device)
+    lse = torch.empty((t, b, w // head_dim, s), dtype=torch.float32, device=X.device)
+    P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
+    tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, stream)
+    return QKV, O, lse, P
+
+
+def attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, s, b, head_dim, causal=True, stream=None):
+    """Allocating wrapper: returns dO, dQKV, dWqkv, dWproj, dXp."""
+    t, d, w3 = Wqkv.shape
+    w = w3 // 3
+    n = X.shape[0]
+    dO = torch.empty((t, n, w), dtype=X.dtype, device=X.device)
+    dQKV = torch.empty((t, n, w3), dtype=X.dtype, device=X.device)
+    dWqkv = torch.empty((t, d, w3), dtype=torch.float32, device=X.device)
+    dWproj = torch.empty((t, w, d), dtype=torch.float32, device=X.device)
+    dXp = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
+    nb = attn_bwd_workspace_bytes(t, s, b, w // head_dim)
+    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=X.device)
+    tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal, stream)
+    return dO, dQKV, dWqkv, dWproj, dXp

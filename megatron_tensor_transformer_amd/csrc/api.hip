@@ -394,3 +394,251 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ attention
+namespace {
+
+// Shared checks of the attention entry points; fills the core problem.
+int attn_core_problem(int dt, int32_t t_local, int64_t s, int64_t b, int32_t nh, int32_t dh, int causal,
+                      tpmlp::AttnProblem& p) {
+  if (!valid_dt(dt)) return TPMLP_ERR_DTYPE;
+  if (t_local < 1 || s < 0 || b < 1 || nh < 1) return TPMLP_ERR_SHAPE;
+  if (dh != 64 && dh != 128) return TPMLP_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return TPMLP_ERR_ARG;
+  if (s > kMaxDim || b > kMaxDim) return TPMLP_ERR_SHAPE;
+  const int64_t n = s * b;
+  if (n > kMaxDim) return TPMLP_ERR_SHAPE;
+  const int es = elem_size(dt);
+  if (!fits(n, static_cast<int64_t>(nh) * 3 * dh, es)) return TPMLP_ERR_SHAPE;  // one shard's qkv
+  const int64_t wgs = static_cast<int64_t>(t_local) * b * nh * ((s + 127) / 128);
+  const int64_t rows = static_cast<int64_t>(t_local) * b * nh * s;
+  if (wgs > kMaxDim || rows > kMaxDim) return TPMLP_ERR_SHAPE;
+  p = tpmlp::AttnProblem{};
+  p.dt = dt;
+  p.T = t_local;
+  p.s = static_cast<int>(s);
+  p.b = static_cast<int>(b);
+  p.nh = nh;
+  p.dh = dh;
+  p.causal = causal != 0;
+  return TPMLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpmlp_attn_core_fwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
+                        int32_t head_dim, int causal, const void* qkv, void* o, float* lse) {
+  tpmlp::AttnProblem p;
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, p);
+  if (st) return st;
+  if (s == 0) return TPMLP_OK;
+  st = check_ptrs(dt, {qkv, o});
+  if (st) return st;
+  if (lse == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(lse, 4)) return TPMLP_ERR_ALIGN;
+  p.qkv = qkv;
+  p.o = o;
+  p.lse = lse;
+  return hip_status(tpmlp::launch_attn_fwd(p, stream));
+}
+
+size_t tpmlp_attn_bwd_workspace_bytes(int32_t t_local, int64_t s, int64_t b, int32_t heads_local) {
+  if (t_local < 1 || s <= 0 || b < 1 || heads_local < 1) return 0;
+  return static_cast<size_t>(t_local) * static_cast<size_t>(b) * static_cast<size_t>(heads_local) *
+         static_cast<size_t>(s) * sizeof(float);
+}
+
+int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
+                        int32_t head_dim, int causal, const void* qkv, const void* o, const float* lse,
+                        const void* d_o, void* dqkv, void* ws, size_t ws_bytes) {
+  tpmlp::AttnProblem p;
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, p);
+  if (st) return st;
+  if (s == 0) return TPMLP_OK;
+  st = check_ptrs(dt, {qkv, o, d_o, dqkv});
+  if (st) return st;
+  if (lse == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(lse, 4)) return TPMLP_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < tpmlp_attn_bwd_workspace_bytes(t_local, s, b, heads_local))
+    return TPMLP_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return TPMLP_ERR_ALIGN;
+  p.qkv = qkv;
+  p.o = const_cast<void*>(o);
+  p.lse = const_cast<float*>(lse);
+  p.dout = d_o;
+  p.dqkv = dqkv;
+  p.delta = static_cast<float*>(ws);
+  return hip_status(tpmlp::launch_attn_bwd(p, stream));
+}
+
+int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
+                   const void* Wproj, void* QKV, void* O, float* lse, void* P) {
+  tpmlp::AttnProblem ap;
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, ap);
+  if (st) return st;
+  const int64_t n = s * b, w = static_cast<int64_t>(heads_local) * head_dim;
+  st = check_mlp_dims(dt, n, d, 3 * w, t_local);  // X·W_qkv and O·W_proj sizes
+  if (st) return st;
+  if (s == 0) return TPMLP_OK;
+  st = check_ptrs(dt, {X, Wqkv, Wproj, QKV, O, P});
+  if (st) return st;
+  if (lse == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(lse, 4)) return TPMLP_ERR_ALIGN;
+  // QKV_i = X·W_qkv,i: A = X [n,d] (K-major), B = W_qkv,i [d,3w] (N-major)
+  tpmlp::GemmProblem g1{};
+  g1.M = static_cast<int>(n);
+  g1.N = static_cast<int>(3 * w);
+  g1.K = static_cast<int>(d);
+  g1.batch = t_local;
+  g1.A = X;
+  g1.B = Wqkv;
+  g1.C = QKV;
+  g1.lda = d;
+  g1.ldb = 3 * w;
+  g1.ldc = 3 * w;
+  g1.sA = 0;
+  g1.sB = d * 3 * w;
+  g1.sC = n * 3 * w;
+  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+  if (st) return st;
+  ap.qkv = QKV;
+  ap.o = O;
+  ap.lse = lse;
+  st = hip_status(tpmlp::launch_attn_fwd(ap, stream));
+  if (st) return st;
+  // P_i = O_i·W_proj,i: A = O_i [n,w] (K-major), B = W_proj,i [w,d] (N-major)
+  tpmlp::GemmProblem g2{};
+  g2.M = static_cast<int>(n);
+  g2.N = static_cast<int>(d);
+  g2.K = static_cast<int>(w);
+  g2.batch = t_local;
+  g2.A = O;
+  g2.B = Wproj;
+  g2.C = P;
+  g2.lda = w;
+  g2.ldb = d;
+  g2.ldc = d;
+  g2.sA = n * w;
+  g2.sB = w * d;
+  g2.sC = n * d;
+  return hip_status(gemm(dt, g2, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+}
+
+int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
+                   const void* Wproj, const void* QKV, const void* O, const float* lse, const void* G, void* dO,
+                   void* dQKV, float* dWqkv, float* dWproj, void* dXp, void* ws, size_t ws_bytes) {
+  tpmlp::AttnProblem ap;
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, ap);
+  if (st) return st;
+  const int64_t n = s * b, w = static_cast<int64_t>(heads_local) * head_dim;
+  st = check_mlp_dims(dt, n, d, 3 * w, t_local);
+  if (st) return st;
+  if (dWqkv == nullptr || dWproj == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(dWqkv, 4) || !aligned(dWproj, 4)) return TPMLP_ERR_ALIGN;
+  if (s > 0) {
+    st = check_ptrs(dt, {X, Wqkv, Wproj, QKV, O, G, dO, dQKV, dXp});
+    if (st) return st;
+    if (lse == nullptr) return TPMLP_ERR_NULLPTR;
+    if (!aligned(lse, 4)) return TPMLP_ERR_ALIGN;
+    if (ws == nullptr || ws_bytes < tpmlp_attn_bwd_workspace_bytes(t_local, s, b, heads_local))
+      return TPMLP_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return TPMLP_ERR_ALIGN;
+  }
+  // dO_i = G·W_proj,iᵀ: M = n, N = w, K = d; B(k,j) = W_proj,i[j][k] (K-major)
+  tpmlp::GemmProblem go{};
+  go.M = static_cast<int>(n);
+  go.N = static_cast<int>(w);
+  go.K = static_cast<int>(d);
+  go.batch = t_local;
+  go.A = G;
+  go.B = Wproj;
+  go.C = dO;
+  go.lda = d;
+  go.ldb = d;
+  go.ldc = w;
+  go.sA = 0;
+  go.sB = w * d;
+  go.sC = n * w;
+  // dW_proj,i = O_iᵀ·G: M = w, N = d, K = n (zeros when n == 0)
+  tpmlp::GemmProblem wp{};
+  wp.M = static_cast<int>(w);
+  wp.N = static_cast<int>(d);
+  wp.K = static_cast<int>(n);
+  wp.batch = t_local;
+  wp.A = O;
+  wp.B = G;
+  wp.C = dWproj;
+  wp.lda = w;
+  wp.ldb = d;
+  wp.ldc = d;
+  wp.sA = n * w;
+  wp.sB = 0;
+  wp.sC = w * d;
+  // dW_qkv,i = Xᵀ·dQKV_i: M = d, N = 3w, K = n
+  tpmlp::GemmProblem wq{};
+  wq.M = static_cast<int>(d);
+  wq.N = static_cast<int>(3 * w);
+  wq.K = static_cast<int>(n);
+  wq.batch = t_local;
+  wq.A = X;
+  wq.B = dQKV;
+  wq.C = dWqkv;
+  wq.lda = d;
+  wq.ldb = 3 * w;
+  wq.ldc = 3 * w;
+  wq.sA = 0;
+  wq.sB = n * 3 * w;
+  wq.sC = d * 3 * w;
+  // dX_i = dQKV_i·W_qkv,iᵀ: M = n, N = d, K = 3w; B(k,j) = W_qkv,i[j][k] (K-major)
+  tpmlp::GemmProblem dx{};
+  dx.M = static_cast<int>(n);
+  dx.N = static_cast<int>(d);
+  dx.K = static_cast<int>(3 * w);
+  dx.batch = t_local;
+  dx.A = dQKV;
+  dx.B = Wqkv;
+  dx.C = dXp;
+  dx.lda = 3 * w;
+  dx.ldb = 3 * w;
+  dx.ldc = d;
+  dx.sA = n * 3 * w;
+  dx.sB = d * 3 * w;
+  dx.sC = n * d;
+
+  const tpmlp::GemmKind wgrad{tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32};
+  const tpmlp::GemmKind dgrad{tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE};
+  ap.qkv = QKV;
+  ap.o = const_cast<void*>(O);
+  ap.lse = const_cast<float*>(lse);
+  ap.dout = dO;
+  ap.dqkv = dQKV;
+  ap.delta = static_cast<float*>(ws);
+  if (dt == TPMLP_BF16) {
+    // dW_proj (long) with dO (short), the core, then dW_qkv (long) with dX
+    st = hip_status(tpmlp::launch_gemm_bf16_group(&wp, 1, wgrad, &go, dgrad, stream));
+    if (st) return st;
+    if (s > 0) {
+      st = hip_status(tpmlp::launch_attn_bwd(ap, stream));
+      if (st) return st;
+    }
+    return hip_status(tpmlp::launch_gemm_bf16_group(&wq, 1, wgrad, &dx, dgrad, stream));
+  }
+  st = hip_status(gemm(dt, wp, wgrad.a_order, wgrad.b_order, wgrad.epi, stream));
+  if (st) return st;
+  if (s > 0) {
+    st = hip_status(gemm(dt, go, dgrad.a_order, dgrad.b_order, dgrad.epi, stream));
+    if (st) return st;
+    st = hip_status(tpmlp::launch_attn_bwd(ap, stream));
+    if (st) return st;
+  }
+  st = hip_status(gemm(dt, wq, wgrad.a_order, wgrad.b_order, wgrad.epi, stream));
+  if (st) return st;
+  if (s > 0) st = hip_status(gemm(dt, dx, dgrad.a_order, dgrad.b_order, dgrad.epi, stream));
+  return st;
+}
+
+}  // extern "C"

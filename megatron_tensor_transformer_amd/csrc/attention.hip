@@ -1,0 +1,804 @@
+// Core of the tensor-parallel self-attention shard: per (shard, batch entry,
+// head), S = q·kᵀ/√dh with an optional causal mask, A = softmax(S) row by row,
+// o = A·v ([TRAIN] Attention 层 section; the causal mask is the implicit one of
+// [EFF] §4.2's fused softmax), and its backward
+//   dv = Aᵀ·do,  dS = A ⊙ (do·vᵀ − δ),  δ_i = Σ_j A_ij (do_i·v_j) = do_i·o_i,
+//   dq = dS·k/√dh,  dk = dSᵀ·q/√dh.
+// The heads of a shard are the contiguous column groups of the column-parallel
+// QKV output ([SENSE] §2.1.1, multi-head attention module: per-head (q, k, v)
+// columns); tokens are rows in [s, b] order ([EFF] §4.2 layout).
+//
+// Layouts (T = resident shards, n = s·b, row r = s_idx·b + b_idx):
+//   qkv [T][n][nh·3·dh]: head h's q, k, v at columns h·3dh + {0, dh, 2dh}
+//   o   [T][n][nh·dh]:   head h at columns h·dh (the row-parallel input)
+//   lse [T][b][nh][s]:   natural log of Σ_j exp(S_ij) per query row (fp32)
+//
+// bf16 path: a flash-attention forward on the matrix cores.  A 256-thread
+// workgroup takes 128 query rows of one (shard, batch entry, head), 32 per
+// wave, with the wave's q fragments in registers; 64-row K and V tiles are
+// streamed into LDS with buffer→LDS DMA, double-buffered.  Per tile a wave
+// computes Sᵀ = K·Qᵀ so that each lane holds logits of its own query row
+// (lane L: row L%32), keeps the running row maximum and sum (online softmax,
+// base-2 exponentials with log2(e)/√dh folded into one fma), and accumulates
+// Oᵀ = Vᵀ·Pᵀ, again with row L%32 in lane L, so the rescaling by the running
+// maximum is lane-local.  The MFMA's k order for Pᵀ is a permutation of the
+// tile's keys (the one the S accumulators already hold); the V fragments are
+// read with the same permutation through the transposing LDS read, so no
+// register shuffle is needed.
+//
+// fp32 path (correctness reference, not tuned): one thread per query row
+// (forward, dq) or key row (dk, dv), online softmax in fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpmlp {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int AQ = 128;   // query rows per workgroup (4 waves × 32)
+constexpr int AKV = 64;   // key rows per step
+constexpr int ATHR = 256;
+constexpr uint32_t AOOB = 0x80000000u;
+
+// Byte offset of 16-B chunk `chunk` of row `row` in a [AKV][DH] bf16 tile.
+// The XOR swizzle keeps both the 16-row column reads (ds_read_b128, one chunk
+// of 16 consecutive rows) and the transposing reads (4 consecutive rows × 4
+// consecutive chunks) free of bank conflicts.
+template <int DH>
+__device__ __forceinline__ uint32_t kv_slot(int row, int chunk) {
+  int f;
+  if constexpr (DH == 128) f = ((row & 3) << 2) | ((row >> 2) & 3);
+  else f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return static_cast<uint32_t>(row * (DH * 2) + ((chunk ^ f) << 4));
+}
+
+struct AttnArgs {
+  const void* qkv;
+  void* o;
+  float* lse;
+  int s, b, nh, T;
+  int nqb;            // query blocks of AQ rows per (shard, batch entry, head)
+  float scale;        // 1/√dh
+  float scale_log2;   // log2(e)/√dh
+  uint32_t qkv_shard_bytes;
+};
+
+// Workgroup -> (shard, batch entry, head, query block); the longest causal
+// blocks (last in the sequence) are dealt first.
+__device__ __forceinline__ void attn_coords(const AttnArgs& a, int& T, int& bi, int& h, int& qb) {
+  const int x = blockIdx.x;
+  qb = a.nqb - 1 - (x % a.nqb);
+  int r = x / a.nqb;
+  h = r % a.nh;
+  r /= a.nh;
+  bi = r % a.b;
+  T = r / a.b;
+}
+
+// DMA of one [AKV][DH] tile: rows j·AKV .. +63 of a token-major tensor whose
+// row r (sequence position) of batch entry bi starts at element
+// (r·b + bi)·row_len, columns col .. col+DH-1.  Rows past s are zero-filled
+// (an offset past the descriptor's range).
+template <int DH>
+__device__ __forceinline__ void load_tile(i32x4 rsrc, TPMLP_LDS char* tile, int s, int b, int bi, int64_t row_len,
+                                          int64_t col, int j, int wave, int lane) {
+  constexpr int NI = AKV * DH * 2 / 1024 / 4;   // 1-KiB DMA loads per wave
+  constexpr int RPI = 1024 / (DH * 2);          // rows per load
+  constexpr int CPR = DH / 8;                   // chunks per row
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int I = wave * NI + q;
+    const int row = I * RPI + lane / CPR;
+    const int slot = lane % CPR;
+    int f;
+    if constexpr (DH == 128) f = ((row & 3) << 2) | ((row >> 2) & 3);
+    else f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    const int chunk = slot ^ f;
+    const int r = j * AKV + row;
+    const uint32_t voff =
+        r < s ? static_cast<uint32_t>(((static_cast<int64_t>(r) * b + bi) * row_len + col + chunk * 8) * 2) : AOOB;
+    buffer_load_lds16(rsrc, tile + I * 1024, voff);
+  }
+}
+
+// MFMA operand with rows = tile rows: lane L gets row `row`, elements
+// 8·chunk' .. +7 where chunk' = 2c + L/32 for k16 slice c.
+template <int DH>
+__device__ __forceinline__ bf16x8 frag_rows(const TPMLP_LDS char* tile, int row, int chunk) {
+  return *(const TPMLP_LDS bf16x8*)(tile + kv_slot<DH>(row, chunk));
+}
+
+// MFMA operand with rows = tile columns 32d .. 32d+31 and k = 16 tile rows of
+// block (u, c2) in the accumulators' order: lane L gets column 32d + L%32,
+// rows 32u + 16c2 + 4·(L/32) + {0..3} then the same + 8.
+template <int DH>
+__device__ __forceinline__ bf16x8 frag_tr(const TPMLP_LDS char* tile, int u, int c2, int d, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int r = 32 * u + 16 * c2 + 4 * (lane >> 5) + (i >> 2);
+  const int col = 32 * d + 16 * (g & 1) + 4 * (i & 3);
+  const s16x4 t0 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPMLP_LDS s16x4*)(tile + kv_slot<DH>(r, col >> 3) + (col & 7) * 2));
+  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (TPMLP_LDS s16x4*)(tile + kv_slot<DH>(r + 8, col >> 3) + (col & 7) * 2));
+  // whole-register moves (the element-wise form was miscompiled: only the
+  // first dword of each read was kept)
+  const i32x2 w0 = __builtin_bit_cast(i32x2, t0), w1 = __builtin_bit_cast(i32x2, t1);
+  i32x4 w;
+  w[0] = w0[0];
+  w[1] = w0[1];
+  w[2] = w1[0];
+  w[3] = w1[1];
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// values 8·c2 .. 8·c2+7 of an accumulator block as a bf16 MFMA operand
+__device__ __forceinline__ bf16x8 pack_acc(const f32x16& x, int c2) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = f2bf(x[8 * c2 + e]);
+  return f;
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int DH, bool CAUSAL>
+__global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int TILE = AKV * DH * 2;
+  constexpr int NC = DH / 16;   // k16 slices of the head dimension
+  constexpr int ND = DH / 32;   // 32-wide head-dimension blocks of o
+  constexpr int NI = TILE / 1024 / 4;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
+
+  int T, bi, h, qb;
+  attn_coords(a, T, bi, h, qb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int q0 = qb * AQ + wave * 32;
+  const int qrow = q0 + r32;
+  const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH;
+  const bf16* qkv = static_cast<const bf16*>(a.qkv) + static_cast<int64_t>(T) * a.s * a.b * row_len;
+  const i32x4 rsrc = make_rsrc(qkv, a.qkv_shard_bytes);
+
+  // key blocks this workgroup visits
+  const int kv_end = CAUSAL ? min(a.s, qb * AQ + AQ) : a.s;
+  const int nkv = (kv_end + AKV - 1) / AKV;
+
+  const int64_t kcol = static_cast<int64_t>(h) * 3 * DH + DH, vcol = kcol + DH;
+  // prologue: K and V of block 0 into stage 0
+  load_tile<DH>(rsrc, lds, a.s, a.b, bi, row_len, kcol, 0, wave, lane);
+  load_tile<DH>(rsrc, lds + TILE, a.s, a.b, bi, row_len, vcol, 0, wave, lane);
+
+  // this lane's q fragments: row qrow, dh = 16c + 8·hi + 0..7
+  bf16x8 qf[NC];
+  {
+    const bf16* qp = qkv + (static_cast<int64_t>(qrow) * a.b + bi) * row_len + h * 3 * DH + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (qrow < a.s) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
+      else qf[c] = bf16x8{};
+    }
+  }
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  for (int j = 0; j < nkv; ++j) {
+    const int st = j & 1;
+    if (j + 1 < nkv) {
+      TPMLP_LDS char* nxt = lds + (st ^ 1) * 2 * TILE;
+      load_tile<DH>(rsrc, nxt, a.s, a.b, bi, row_len, kcol, j + 1, wave, lane);
+      load_tile<DH>(rsrc, nxt + TILE, a.s, a.b, bi, row_len, vcol, j + 1, wave, lane);
+      wait_vmcnt<2 * NI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    const TPMLP_LDS char* kb = lds + st * 2 * TILE;
+    const TPMLP_LDS char* vb = kb + TILE;
+
+    // Sᵀ block: sacc[u][v] = S[qrow][kv], kv = 64j + 32u + 8(v/4) + 4·hi + v%4
+    f32x16 sacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[u][v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc[u] = mfma(frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi), qf[c], sacc[u]);
+    }
+
+    // mask, running maximum, exponentials, running sum
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kv = j * AKV + 32 * u + 8 * (v >> 2) + 4 * hi + (v & 3);
+        const bool keep = kv < a.s && (!CAUSAL || kv <= qrow);
+        sacc[u][v] = keep ? sacc[u][v] : -INFINITY;
+        mloc = fmaxf(mloc, sacc[u][v]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(m, mloc);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f((m - muse) * a.scale_log2);
+    const float off = -muse * a.scale_log2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][v], a.scale_log2, off));
+        sacc[u][v] = p;
+        lsum += p;
+      }
+    lsum += __shfl_xor(lsum, 32, 64);
+    l = l * alpha + lsum;
+    m = mnew;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
+
+    // Oᵀ += Vᵀ·Pᵀ over the tile's keys, 16 at a time.  P fragment (u, c2):
+    // this lane's values v = 8·c2 .. 8·c2+7 of sacc[u]; they are keys
+    // 32u + 16c2 + {0..3, 8..11} (hi = 0) or {4..7, 12..15} (hi = 1), and the
+    // V fragment rows are read in that same order.
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 pf = pack_acc(sacc[u], c2);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) oacc[d] = mfma(frag_tr<DH>(vb, u, c2, d, lane), pf, oacc[d]);
+      }
+    block_barrier();  // every wave is done with stage st before it is refilled
+  }
+
+  // o = oacc / l; lane holds row qrow, dh = 32d + 8(v/4) + 4·hi + v%4
+  if (qrow < a.s) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    bf16* op = static_cast<bf16*>(a.o) + static_cast<int64_t>(T) * a.s * a.b * a.nh * DH +
+               (static_cast<int64_t>(qrow) * a.b + bi) * a.nh * DH + h * DH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = f2bf(oacc[d][4 * q4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * d + 8 * q4 + 4 * hi) = w;
+      }
+    if (hi == 0) {
+      const float lse = l > 0.f ? m * a.scale + logf(l) : -INFINITY;
+      a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + qrow] = lse;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+// One thread per query row of one (shard, batch entry, head).
+template <int DH, bool CAUSAL>
+__global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.T) * a.b * a.nh * a.s;
+  if (idx >= total) return;
+  const int q = static_cast<int>(idx % a.s);
+  int64_t r = idx / a.s;
+  const int h = static_cast<int>(r % a.nh);
+  r /= a.nh;
+  const int bi = static_cast<int>(r % a.b);
+  const int T = static_cast<int>(r / a.b);
+  const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH;
+  const float* qkv = static_cast<const float*>(a.qkv) + static_cast<int64_t>(T) * a.s * a.b * row_len;
+  const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH;
+  float qv[DH], acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    qv[d] = qp[d];
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kend = CAUSAL ? q + 1 : a.s;
+  for (int kv = 0; kv < kend; ++kv) {
+    const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
+    float sdot = 0.f;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) sdot = fmaf(qv[d], kp[d], sdot);
+    const float sv = sdot * a.scale;
+    const float mn = fmaxf(m, sv);
+    const float alpha = expf(m - mn), p = expf(sv - mn);
+    l = l * alpha + p;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, kp[DH + d], acc[d] * alpha);
+    m = mn;
+  }
+  float* op = static_cast<float*>(a.o) + static_cast<int64_t>(T) * a.s * a.b * a.nh * DH +
+              (static_cast<int64_t>(q) * a.b + bi) * a.nh * DH + h * DH;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) op[d] = acc[d] / l;
+  a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + q] = m + logf(l);
+}
+
+// ------------------------------------------------------------------ backward
+struct AttnBwdArgs {
+  const void* qkv;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  void* dqkv;
+  int s, b, nh, T;
+  int nqb;            // blocks of AQ rows (dq workgroups, dk/dv workgroups)
+  float scale, scale_log2;
+  uint32_t qkv_shard_bytes, o_shard_bytes;
+};
+
+// δ[T][bi][h][q] = Σ_d do·o over the head's dh columns of row q (fp32): one
+// thread per (shard, token row, head).
+template <typename TT, int DH>
+__global__ __launch_bounds__(256) void attn_delta_kernel(AttnBwdArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(a.s) * a.b;
+  if (idx >= static_cast<int64_t>(a.T) * n * a.nh) return;
+  const int h = static_cast<int>(idx % a.nh);
+  const int64_t tr = idx / a.nh;  // T·n + token row
+  const int T = static_cast<int>(tr / n);
+  const int64_t r = tr % n;
+  const int q = static_cast<int>(r / a.b), bi = static_cast<int>(r % a.b);
+  const int64_t off = tr * a.nh * DH + static_cast<int64_t>(h) * DH;
+  const TT* op = static_cast<const TT*>(a.o) + off;
+  const TT* dp = static_cast<const TT*>(a.dout) + off;
+  float acc = 0.f;
+  if constexpr (sizeof(TT) == 2) {
+#pragma unroll
+    for (int c = 0; c < DH / 8; ++c) {
+      const bf16x8 x = reinterpret_cast<const bf16x8*>(op)[c];
+      const bf16x8 y = reinterpret_cast<const bf16x8*>(dp)[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(bf2f(x[e]), bf2f(y[e]), acc);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc = fmaf(op[d], dp[d], acc);
+  }
+  a.delta[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + q] = acc;
+}
+
+// dq: a workgroup takes 128 query rows of one (shard, batch entry, head), a
+// wave 32, with q and do fragments in registers; K and V tiles of 64 keys
+// stream through LDS.  Per tile: Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ (lane L holds row
+// L%32), P = exp2(S·log2(e)/√dh − lse·log2(e)), dS = P ⊙ (dP − δ), and
+// dQᵀ += Kᵀ·dSᵀ with the keys in the accumulators' order.
+template <int DH, bool CAUSAL>
+__global__ __launch_bounds__(ATHR, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int TILE = AKV * DH * 2;
+  constexpr int NC = DH / 16, ND = DH / 32;
+  constexpr int NI = TILE / 1024 / 4;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
+  const int x = blockIdx.x;
+  const int qb = a.nqb - 1 - (x % a.nqb);
+  int r = x / a.nqb;
+  const int h = r % a.nh;
+  r /= a.nh;
+  const int bi = r % a.b, T = r / a.b;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int qrow = qb * AQ + wave * 32 + r32;
+  const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
+  const int64_t n = static_cast<int64_t>(a.s) * a.b;
+  const bf16* qkv = static_cast<const bf16*>(a.qkv) + T * n * row_len;
+  const bf16* dout = static_cast<const bf16*>(a.dout) + T * n * orow;
+  const i32x4 rsrc = make_rsrc(qkv, a.qkv_shard_bytes);
+  const int64_t kcol = static_cast<int64_t>(h) * 3 * DH + DH, vcol = kcol + DH;
+  const int kv_end = CAUSAL ? min(a.s, qb * AQ + AQ) : a.s;
+  const int nkv = (kv_end + AKV - 1) / AKV;
+
+  load_tile<DH>(rsrc, lds, a.s, a.b, bi, row_len, kcol, 0, wave, lane);
+  load_tile<DH>(rsrc, lds + TILE, a.s, a.b, bi, row_len, vcol, 0, wave, lane);
+
+  bf16x8 qf[NC], df[NC];
+  const bool valid = qrow < a.s;
+  {
+    const bf16* qp = qkv + (static_cast<int64_t>(qrow) * a.b + bi) * row_len + h * 3 * DH + 8 * hi;
+    const bf16* dp = dout + (static_cast<int64_t>(qrow) * a.b + bi) * orow + h * DH + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[c] = valid ? *reinterpret_cast<const bf16x8*>(qp + 16 * c) : bf16x8{};
+      df[c] = valid ? *reinterpret_cast<const bf16x8*>(dp + 16 * c) : bf16x8{};
+    }
+  }
+  const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
+  const float lse2 = valid ? a.lse[srow + qrow] * 1.4426950408889634f : 0.f;
+  const float dlt = valid ? a.delta[srow + qrow] : 0.f;
+
+  f32x16 dq[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dq[d][v] = 0.f;
+
+  for (int j = 0; j < nkv; ++j) {
+    const int st = j & 1;
+    if (j + 1 < nkv) {
+      TPMLP_LDS char* nxt = lds + (st ^ 1) * 2 * TILE;
+      load_tile<DH>(rsrc, nxt, a.s, a.b, bi, row_len, kcol, j + 1, wave, lane);
+      load_tile<DH>(rsrc, nxt + TILE, a.s, a.b, bi, row_len, vcol, j + 1, wave, lane);
+      wait_vmcnt<2 * NI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    const TPMLP_LDS char* kb = lds + st * 2 * TILE;
+    const TPMLP_LDS char* vb = kb + TILE;
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[u][v] = pacc[u][v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        sacc[u] = mfma(frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi), qf[c], sacc[u]);
+        pacc[u] = mfma(frag_rows<DH>(vb, 32 * u + r32, 2 * c + hi), df[c], pacc[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kv = j * AKV + 32 * u + 8 * (v >> 2) + 4 * hi + (v & 3);
+        const bool keep = valid && kv < a.s && (!CAUSAL || kv <= qrow);
+        const float p = keep ? __builtin_amdgcn_exp2f(fmaf(sacc[u][v], a.scale_log2, -lse2)) : 0.f;
+        sacc[u][v] = p * (pacc[u][v] - dlt);  // dS
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 sf = pack_acc(sacc[u], c2);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dq[d] = mfma(frag_tr<DH>(kb, u, c2, d, lane), sf, dq[d]);
+      }
+    block_barrier();
+  }
+  if (valid) {
+    bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(qrow) * a.b + bi) * row_len +
+               h * 3 * DH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = f2bf(dq[d][4 * q4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(op + 32 * d + 8 * q4 + 4 * hi) = w;
+      }
+  }
+}
+
+// dk, dv: a workgroup takes 128 key rows, a wave 32, with k and v fragments in
+// registers; Q and dO tiles of 64 query rows (and their lse, δ) stream
+// through LDS.  Per tile: S'ᵀ = Q·Kᵀ and dP'ᵀ = dO·Vᵀ with lane L holding key
+// row L%32, P and dS as in dq, then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with the
+// query rows in the accumulators' order.
+template <int DH, bool CAUSAL>
+__global__ __launch_bounds__(ATHR, 1) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int TILE = AKV * DH * 2;
+  constexpr int NC = DH / 16, ND = DH / 32;
+  constexpr int NI = TILE / 1024 / 4;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  __shared__ float stat[2][2][AKV];  // [stage][lse·log2(e) | δ][row]
+  TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
+  const int x = blockIdx.x;
+  const int kb_idx = x % a.nqb;  // key block
+  int r = x / a.nqb;
+  const int h = r % a.nh;
+  r /= a.nh;
+  const int bi = r % a.b, T = r / a.b;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int krow = kb_idx * AQ + wave * 32 + r32;
+  const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
+  const int64_t n = static_cast<int64_t>(a.s) * a.b;
+  const bf16* qkv = static_cast<const bf16*>(a.qkv) + T * n * row_len;
+  const bf16* dout = static_cast<const bf16*>(a.dout) + T * n * orow;
+  const i32x4 rq = make_rsrc(qkv, a.qkv_shard_bytes);
+  const i32x4 rd = make_rsrc(dout, a.o_shard_bytes);
+  const int64_t qcol = static_cast<int64_t>(h) * 3 * DH, dcol = static_cast<int64_t>(h) * DH;
+  const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
+  const int j0 = CAUSAL ? (kb_idx * AQ) / AKV : 0;
+  const int nq = (a.s + AKV - 1) / AKV;
+
+  // statistics of query block j into stage st (threads 0..127: one value each)
+  auto load_stat = [&](int j, float& v) {
+    const int t = threadIdx.x & 63, qr = j * AKV + t;
+    if (threadIdx.x < 64) v = qr < a.s ? a.lse[srow + qr] * 1.4426950408889634f : 0.f;
+    else if (threadIdx.x < 128) v = qr < a.s ? a.delta[srow + qr] : 0.f;
+  };
+  auto store_stat = [&](int st, float v) {
+    if (threadIdx.x < 128) stat[st][threadIdx.x >> 6][threadIdx.x & 63] = v;
+  };
+
+  float sv = 0.f;
+  if (j0 < nq) {
+    load_stat(j0, sv);
+    load_tile<DH>(rq, lds, a.s, a.b, bi, row_len, qcol, j0, wave, lane);
+    load_tile<DH>(rd, lds + TILE, a.s, a.b, bi, orow, dcol, j0, wave, lane);
+  }
+
+  bf16x8 kf[NC], vf[NC];
+  const bool valid = krow < a.s;
+  {
+    const bf16* kp = qkv + (static_cast<int64_t>(krow) * a.b + bi) * row_len + h * 3 * DH + DH + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kf[c] = valid ? *reinterpret_cast<const bf16x8*>(kp + 16 * c) : bf16x8{};
+      vf[c] = valid ? *reinterpret_cast<const bf16x8*>(kp + DH + 16 * c) : bf16x8{};
+    }
+  }
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dk[d][v] = dv[d][v] = 0.f;
+  wait_vmcnt<0>();
+  store_stat(0, sv);
+
+  for (int j = j0; j < nq; ++j) {
+    const int st = (j - j0) & 1;
+    if (j + 1 < nq) {
+      load_stat(j + 1, sv);
+      TPMLP_LDS char* nxt = lds + (st ^ 1) * 2 * TILE;
+      load_tile<DH>(rq, nxt, a.s, a.b, bi, row_len, qcol, j + 1, wave, lane);
+      load_tile<DH>(rd, nxt + TILE, a.s, a.b, bi, orow, dcol, j + 1, wave, lane);
+      wait_vmcnt<2 * NI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wait_lgkmcnt0();  // this wave's stat writes of the previous step are done
+    block_barrier();
+    const TPMLP_LDS char* qt = lds + st * 2 * TILE;
+    const TPMLP_LDS char* dt = qt + TILE;
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[u][v] = pacc[u][v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        sacc[u] = mfma(frag_rows<DH>(qt, 32 * u + r32, 2 * c + hi), kf[c], sacc[u]);
+        pacc[u] = mfma(frag_rows<DH>(dt, 32 * u + r32, 2 * c + hi), vf[c], pacc[u]);
+      }
+    }
+    // lane: key krow, query rows 64j + 32u + 8(v/4) + 4·hi + v%4
+    f32x16 pv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g + e;
+          const int qi = 32 * u + 8 * g + 4 * hi + e;
+          const int qr = j * AKV + qi;
+          const bool keep = valid && qr < a.s && (!CAUSAL || qr >= krow);
+          const float p = keep ? __builtin_amdgcn_exp2f(fmaf(sacc[u][v], a.scale_log2, -stat[st][0][qi])) : 0.f;
+          pv[u][v] = p;
+          sacc[u][v] = p * (pacc[u][v] - stat[st][1][qi]);  // dS
+        }
+    // store the next block's statistics into the other stage (read after the
+    // next barrier)
+    if (j + 1 < nq) store_stat(st ^ 1, sv);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 pf = pack_acc(pv[u], c2);
+        const bf16x8 sf = pack_acc(sacc[u], c2);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          dv[d] = mfma(frag_tr<DH>(dt, u, c2, d, lane), pf, dv[d]);
+          dk[d] = mfma(frag_tr<DH>(qt, u, c2, d, lane), sf, dk[d]);
+        }
+      }
+    block_barrier();
+  }
+  if (valid) {
+    bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(krow) * a.b + bi) * row_len +
+               h * 3 * DH + DH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = f2bf(dk[d][4 * q4 + e] * a.scale);
+          wv[e] = f2bf(dv[d][4 * q4 + e]);
+        }
+        *reinterpret_cast<bf16x4*>(op + 32 * d + 8 * q4 + 4 * hi) = wk;
+        *reinterpret_cast<bf16x4*>(op + DH + 32 * d + 8 * q4 + 4 * hi) = wv;
+      }
+  }
+}
+
+// fp32 backward (correctness path): dq per query row, dk and dv per key row.
+template <int DH, bool CAUSAL>
+__global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(AttnBwdArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(a.T) * a.b * a.nh * a.s) return;
+  const int q = static_cast<int>(idx % a.s);
+  int64_t r = idx / a.s;
+  const int h = static_cast<int>(r % a.nh);
+  r /= a.nh;
+  const int bi = static_cast<int>(r % a.b), T = static_cast<int>(r / a.b);
+  const int64_t n = static_cast<int64_t>(a.s) * a.b;
+  const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
+  const float* qkv = static_cast<const float*>(a.qkv) + T * n * row_len;
+  const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH;
+  const float* dp = static_cast<const float*>(a.dout) + T * n * orow + (static_cast<int64_t>(q) * a.b + bi) * orow +
+                    h * DH;
+  const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
+  const float lse = a.lse[srow + q], dlt = a.delta[srow + q];
+  float qv[DH], dov[DH], acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    qv[d] = qp[d];
+    dov[d] = dp[d];
+    acc[d] = 0.f;
+  }
+  const int kend = CAUSAL ? q + 1 : a.s;
+  for (int kv = 0; kv < kend; ++kv) {
+    const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
+    float sdot = 0.f, pdot = 0.f;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) {
+      sdot = fmaf(qv[d], kp[d], sdot);
+      pdot = fmaf(dov[d], kp[DH + d], pdot);
+    }
+    const float p = expf(sdot * a.scale - lse);
+    const float ds = p * (pdot - dlt);
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[d] = fmaf(ds, kp[d], acc[d]);
+  }
+  float* op = static_cast<float*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(q) * a.b + bi) * row_len +
+              h * 3 * DH;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) op[d] = acc[d] * a.scale;
+}
+
+template <int DH, bool CAUSAL>
+__global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(AttnBwdArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(a.T) * a.b * a.nh * a.s) return;
+  const int kv = static_cast<int>(idx % a.s);
+  int64_t r = idx / a.s;
+  const int h = static_cast<int>(r % a.nh);
+  r /= a.nh;
+  const int bi = static_cast<int>(r % a.b), T = static_cast<int>(r / a.b);
+  const int64_t n = static_cast<int64_t>(a.s) * a.b;
+  const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
+  const float* qkv = static_cast<const float*>(a.qkv) + T * n * row_len;
+  const float* dout = static_cast<const float*>(a.dout) + T * n * orow;
+  const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
+  const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
+  float dk[DH], dv[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) dk[d] = dv[d] = 0.f;
+  for (int q = CAUSAL ? kv : 0; q < a.s; ++q) {
+    const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH;
+    const float* dp = dout + (static_cast<int64_t>(q) * a.b + bi) * orow + h * DH;
+    float sdot = 0.f, pdot = 0.f;
+    for (int d = 0; d < DH; ++d) {
+      sdot = fmaf(qp[d], kp[d], sdot);
+      pdot = fmaf(dp[d], kp[DH + d], pdot);
+    }
+    const float p = expf(sdot * a.scale - a.lse[srow + q]);
+    const float ds = p * (pdot - a.delta[srow + q]);
+#pragma unroll
+    for (int d = 0; d < DH; ++d) {
+      dv[d] = fmaf(p, dp[d], dv[d]);
+      dk[d] = fmaf(ds, qp[d], dk[d]);
+    }
+  }
+  float* op = static_cast<float*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(kv) * a.b + bi) * row_len +
+              h * 3 * DH + DH;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    op[d] = dk[d] * a.scale;
+    op[DH + d] = dv[d];
+  }
+}
+
+template <int DH, bool CAUSAL>
+hipError_t launch_bwd_t(const AttnBwdArgs& a, int dt, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(a.T) * a.b * a.nh * a.s;
+  const unsigned dblocks = static_cast<unsigned>((rows + 255) / 256);
+  if (dt == 1)
+    hipLaunchKernelGGL((attn_delta_kernel<bf16, DH>), dim3(dblocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_delta_kernel<float, DH>), dim3(dblocks), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dt == 1) {
+    const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.T) * a.b * a.nh * a.nqb);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
+  } else {
+    const unsigned blocks = static_cast<unsigned>((rows + 127) / 128);
+    hipLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<DH, CAUSAL>), dim3(blocks), dim3(128), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_f32_kernel<DH, CAUSAL>), dim3(blocks), dim3(128), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DH, bool CAUSAL>
+hipError_t launch_fwd_t(const AttnArgs& a, int dt, hipStream_t stream) {
+  if (dt == 1) {
+    const int64_t blocks = static_cast<int64_t>(a.T) * a.b * a.nh * a.nqb;
+    hipLaunchKernelGGL((attn_fwd_kernel<DH, CAUSAL>), dim3(static_cast<unsigned>(blocks)), dim3(ATHR), 0, stream,
+                       a);
+  } else {
+    const int64_t total = static_cast<int64_t>(a.T) * a.b * a.nh * a.s;
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<DH, CAUSAL>), dim3(static_cast<unsigned>((total + 127) / 128)),
+                       dim3(128), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnProblem& p, hipStream_t stream) {
+  AttnArgs a{};
+  a.qkv = p.qkv;
+  a.o = p.o;
+  a.lse = p.lse;
+  a.s = p.s;
+  a.b = p.b;
+  a.nh = p.nh;
+  a.T = p.T;
+  a.nqb = (p.s + AQ - 1) / AQ;
+  a.scale = 1.0f / sqrtf(static_cast<float>(p.dh));
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.qkv_shard_bytes = static_cast<uint32_t>(static_cast<int64_t>(p.s) * p.b * p.nh * 3 * p.dh * 2);
+  if (p.dh == 128)
+    return p.causal ? launch_fwd_t<128, true>(a, p.dt, stream) : launch_fwd_t<128, false>(a, p.dt, stream);
+  return p.causal ? launch_fwd_t<64, true>(a, p.dt, stream) : launch_fwd_t<64, false>(a, p.dt, stream);
+}
+
+hipError_t launch_attn_bwd(const AttnProblem& p, hipStream_t stream) {
+  AttnBwdArgs a{};
+  a.qkv = p.qkv;
+  a.o = p.o;
+  a.dout = p.dout;
+  a.lse = p.lse;
+  a.delta = p.delta;
+  a.dqkv = p.dqkv;
+  a.s = p.s;
+  a.b = p.b;
+  a.nh = p.nh;
+  a.T = p.T;
+  a.nqb = (p.s + AQ - 1) / AQ;
+  a.scale = 1.0f / sqrtf(static_cast<float>(p.dh));
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.qkv_shard_bytes = static_cast<uint32_t>(static_cast<int64_t>(p.s) * p.b * p.nh * 3 * p.dh * 2);
+  a.o_shard_bytes = static_cast<uint32_t>(static_cast<int64_t>(p.s) * p.b * p.nh * p.dh * 2);
+  if (p.dh == 128)
+    return p.causal ? launch_bwd_t<128, true>(a, p.dt, stream) : launch_bwd_t<128, false>(a, p.dt, stream);
+  return p.causal ? launch_bwd_t<64, true>(a, p.dt, stream) : launch_bwd_t<64, false>(a, p.dt, stream);
+}
+
+}  // namespace tpmlp

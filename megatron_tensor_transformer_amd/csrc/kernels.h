@@ -92,6 +92,20 @@ struct SpProblem {
 };
 
 int64_t sp_ln_bwd_row_blocks(int64_t s);
+
+// Attention core of T resident shards (layouts in attention.hip).
+struct AttnProblem {
+  int dt, T, s, b, nh, dh;
+  bool causal;
+  const void* qkv;   // [T][s·b][nh·3·dh]
+  void* o;           // [T][s·b][nh·dh]
+  float* lse;        // [T][b][nh][s]
+  const void* dout;  // backward: upstream gradient of o, layout of o
+  void* dqkv;        // backward: layout of qkv
+  float* delta;      // backward workspace [T][b][nh][s]
+};
+hipError_t launch_attn_fwd(const AttnProblem& p, hipStream_t stream);
+hipError_t launch_attn_bwd(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_sp(const SpProblem& p, hipStream_t stream);
 
 }  // namespace tpmlp

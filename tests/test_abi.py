@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 2
+    assert L.tpmlp_abi_version() == 3
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert L.tpmlp_status_string(s)
 
@@ -108,6 +108,36 @@ def test_bias_grad_validation(L):
     assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, p, None, need) == tp.ERR_WORKSPACE
     assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, ctypes.c_void_p(0x1001), p, p, need) == tp.ERR_ALIGN
     assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, ctypes.c_void_p(0x1002), p, need) == tp.ERR_ALIGN
+
+
+def test_attn_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    z = ctypes.c_void_p(0)
+
+    def core(dt=1, t=2, s=64, b=2, nh=2, dh=128, causal=1, qkv=p, o=p, lse=p):
+        return L.tpmlp_attn_core_fwd(None, dt, t, s, b, nh, dh, causal, qkv, o, lse)
+    assert core(dt=4) == tp.ERR_DTYPE
+    assert core(dh=96) == tp.ERR_SHAPE            # head_dim 64 or 128
+    assert core(b=0) == tp.ERR_SHAPE
+    assert core(nh=0) == tp.ERR_SHAPE
+    assert core(causal=2) == tp.ERR_ARG
+    assert core(qkv=z) == tp.ERR_NULLPTR
+    assert core(lse=z) == tp.ERR_NULLPTR
+    assert core(o=ctypes.c_void_p(0x1008)) == tp.ERR_ALIGN
+    assert core(s=0, qkv=z, o=z, lse=z) == 0     # empty sequence: nothing to do
+    assert core(s=1 << 20, b=1 << 10) == tp.ERR_SHAPE
+    # the backward's workspace is one fp32 δ per (shard, batch entry, head, row)
+    assert L.tpmlp_attn_bwd_workspace_bytes(8, 1024, 8, 3) == 8 * 8 * 3 * 1024 * 4
+    need = L.tpmlp_attn_bwd_workspace_bytes(2, 64, 2, 2)
+    assert L.tpmlp_attn_core_bwd(None, 1, 2, 64, 2, 2, 64, 1, p, p, p, p, p, p, need - 4) == tp.ERR_WORKSPACE
+    assert L.tpmlp_attn_core_bwd(None, 1, 2, 64, 2, 2, 64, 1, p, p, p, z, p, p, need) == tp.ERR_NULLPTR
+    # the layer: d % 8 for bf16, weight-gradient pointers required
+    assert L.tpmlp_attn_fwd(None, 1, 64, 2, 36, 2, 64, 2, 1, p, p, p, p, p, p, p) == tp.ERR_ALIGN
+    assert L.tpmlp_attn_fwd(None, 1, 64, 2, 256, 2, 64, 2, 1, p, p, p, p, p, z, p) == tp.ERR_NULLPTR
+    args = [p] * 10
+    # X, W_qkv, W_proj, QKV, O, lse, G | dO, dQKV, dW_qkv, dW_proj, dXp, ws, ws_bytes
+    assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, *args[:7], p, p, z, p, p, p, need) == tp.ERR_NULLPTR
+    assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, *args[:7], p, p, p, p, p, None, 0) == tp.ERR_WORKSPACE
 
 
 def test_bwd_validation(L):

@@ -1,0 +1,200 @@
+"""GPU parity of the self-attention shard (tpmlp_attn_core_fwd/_bwd and
+tpmlp_attn_fwd/_bwd) against the fp64 oracle (oracle/attention.py) on the
+same seeded inputs, through the C ABI.
+
+Bars (relative Frobenius error, fp64): fp32 path 1e-5, bf16 path 8e-3, for
+every output and gradient (o, lse, dq, dk, dv; QKV, O, P, the summed output,
+dO, dQKV, dW_qkv, dW_proj, dX).  lse is compared as exp(lse) (the row's
+softmax normaliser), whose relative error is lse's absolute error.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import megatron_tensor_transformer_amd as tp
+from oracle import attention as oa
+from tpmlp_inputs import CONFIGS, attn_inputs, config_inputs, qkv_inputs
+
+from gpu_util import dev, f64, relerr, say, shard_cols, shard_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 8e-3}
+
+
+def lse_err(gpu, ref):
+    """Relative Frobenius error of the softmax normalisers exp(lse)."""
+    return relerr(np.exp(f64(gpu)), np.exp(np.asarray(ref, np.float64)))
+
+
+# ------------------------------------------------------------------ the core
+def run_core(inp, T, s, b, nh, dh, causal):
+    qkv, do = dev(inp["qkv"]), dev(inp["do"])
+    o = torch.empty((T, s * b, nh * dh), dtype=qkv.dtype, device="cuda")
+    lse = torch.empty((T, b, nh, s), dtype=torch.float32, device="cuda")
+    tp.tpmlp_attn_core_fwd(qkv, o, lse, s, b, nh, dh, causal)
+    dqkv = torch.empty_like(qkv)
+    ws = torch.empty(max(tp.attn_bwd_workspace_bytes(T, s, b, nh), 4), dtype=torch.uint8, device="cuda")
+    tp.tpmlp_attn_core_bwd(qkv, o, lse, do, dqkv, ws, s, b, nh, dh, causal)
+    torch.cuda.synchronize()
+    return o, lse, dqkv
+
+
+def compare_core(T, s, b, nh, dh, causal, dtype, seed=0):
+    say(f"[gpu] attention core {dtype} T={T} s={s} b={b} nh={nh} dh={dh} causal={causal}")
+    inp = qkv_inputs(T, s, b, nh, dh, dtype=dtype, seed=seed)
+    o, lse, dqkv = run_core(inp, T, s, b, nh, dh, causal)
+    tol = TOL[dtype]
+    errs = {}
+    for i in range(T):
+        q, k, v = oa.split_heads(inp["qkv"].f64[i], s, b, nh, dh)
+        do = oa.unmerge_heads(inp["do"].f64[i], s, b, nh, dh)
+        ro, A, rlse = oa.core_forward(q, k, v, causal)
+        dq, dk, dv = oa.core_backward(q, k, v, A, do)
+        errs[f"o{i}"] = relerr(o[i], oa.merge_heads(ro))
+        errs[f"dqkv{i}"] = relerr(dqkv[i], oa.merge_qkv(dq, dk, dv))
+        gq, gk, gv = oa.split_heads(f64(dqkv[i]), s, b, nh, dh)
+        errs[f"dq{i}"], errs[f"dk{i}"], errs[f"dv{i}"] = relerr(gq, dq), relerr(gk, dk), relerr(gv, dv)
+        errs[f"lse{i}"] = lse_err(lse[i], rlse)
+    bad = {k: e for k, e in errs.items() if not (e <= tol)}
+    say(f"[gpu] attention core: worst {max(errs.values()):.3e}")
+    assert not bad, f"over {tol}: {bad}"
+
+
+@pytest.mark.parametrize("T,s,b,nh,dh,causal", [
+    (1, 1, 1, 1, 64, True),
+    (1, 5, 2, 2, 64, False),
+    (2, 70, 2, 1, 64, True),
+    (1, 33, 1, 2, 128, True),
+    (1, 130, 3, 1, 128, False),
+])
+def test_core_fp32(T, s, b, nh, dh, causal):
+    compare_core(T, s, b, nh, dh, causal, "f32")
+
+
+@pytest.mark.parametrize("T,s,b,nh,dh,causal", [
+    (1, 1, 1, 1, 64, True),      # one token: o = v
+    (1, 5, 2, 2, 64, False),     # one partial key tile
+    (2, 63, 1, 2, 64, True),
+    (1, 64, 2, 1, 128, True),    # exactly one key tile
+    (1, 65, 1, 1, 128, True),    # one row into the second tile
+    (2, 130, 3, 3, 128, False),  # two query blocks, ragged
+    (1, 300, 2, 2, 128, True),   # several query blocks and key tiles
+    (1, 257, 1, 2, 64, True),
+])
+def test_core_bf16(T, s, b, nh, dh, causal):
+    compare_core(T, s, b, nh, dh, causal, "bf16")
+
+
+def test_core_deterministic_bitwise():
+    inp = qkv_inputs(2, 200, 2, 2, 128, dtype="bf16", seed=4)
+    r1 = run_core(inp, 2, 200, 2, 2, 128, True)
+    r2 = run_core(inp, 2, 200, 2, 2, 128, True)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
+def test_core_uniform_when_queries_vanish():
+    """q = 0: the causal output row i is the mean of v_0..v_i (closed form)."""
+    T, s, b, nh, dh = 1, 150, 2, 1, 64
+    inp = qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=6)
+    qkv = dev(inp["qkv"])
+    qkv.view(T, s, b, nh, 3, dh)[:, :, :, :, 0, :] = 0
+    o = torch.empty((T, s * b, nh * dh), dtype=qkv.dtype, device="cuda")
+    lse = torch.empty((T, b, nh, s), dtype=torch.float32, device="cuda")
+    tp.tpmlp_attn_core_fwd(qkv, o, lse, s, b, nh, dh, True)
+    torch.cuda.synchronize()
+    v = f64(qkv).reshape(T, s, b, nh, 3, dh)[0, :, :, 0, 2, :]       # [s, b, dh]
+    ref = np.cumsum(v, axis=0) / np.arange(1, s + 1)[:, None, None]
+    assert relerr(f64(o).reshape(s, b, dh), ref) <= TOL["bf16"]
+    assert np.allclose(f64(lse)[0, :, 0, :], np.log(np.arange(1, s + 1))[None, :], rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------------------------ the layer
+def run_layer(inp, s, b, heads, t, causal):
+    X, Wq, Wp, G = (dev(inp[k]) for k in ("X", "Wqkv", "Wproj", "G"))
+    dh = X.shape[1] // heads
+    Wq_s, Wp_s = shard_cols(Wq, t), shard_rows(Wp, t)
+    QKV, O, lse, P = tp.attn_fwd(X, Wq_s, Wp_s, s, b, dh, causal)
+    Out = tp.reduce_partials(P)
+    dO, dQKV, dWqkv, dWproj, dXp = tp.attn_bwd(X, Wq_s, Wp_s, QKV, O, lse, G, s, b, dh, causal)
+    dX = tp.reduce_partials(dXp)
+    torch.cuda.synchronize()
+    return dict(QKV=QKV, O=O, lse=lse, P=P, Out=Out, dO=dO, dQKV=dQKV, dWqkv=dWqkv, dWproj=dWproj, dXp=dXp, dX=dX)
+
+
+def compare_layer(s, b, d, heads, t, causal, dtype, seed=0):
+    # weights of std 1.2/√d give logits of std ≈ 1.4 (w²·d), as the 0.02
+    # initialisation does at d = 3072; larger ones make the softmax one-hot
+    # and the fp32 logits' rounding dominate the comparison
+    say(f"[gpu] attention layer {dtype} s={s} b={b} d={d} heads={heads} t={t} causal={causal}")
+    inp = attn_inputs(s, b, d, heads, dtype=dtype, seed=seed, x_std=1.0, w_std=1.2 / np.sqrt(d), g_std=1.0)
+    r = run_layer(inp, s, b, heads, t, causal)
+    L = {k: v.f64 for k, v in inp.items()}
+    f = oa.tp_forward(L["X"], L["Wqkv"], L["Wproj"], t, s, b, heads, causal)
+    g = oa.tp_backward(L["X"], L["Wqkv"], L["Wproj"], f, L["G"])
+    tol = TOL[dtype]
+    errs = {"Out": relerr(r["Out"], f["Out"]), "dX": relerr(r["dX"], g["dX"])}
+    for i in range(t):
+        fs, gs = f["shards"][i], g["shards"][i]
+        for k, ref in (("QKV", fs["QKV"]), ("O", fs["O"]), ("P", fs["P"]), ("dO", gs["dO"]),
+                       ("dQKV", gs["dQKV"]), ("dWqkv", gs["dWqkv"]), ("dWproj", gs["dWproj"]),
+                       ("dXp", gs["dXp"])):
+            errs[f"{k}{i}"] = relerr(r[k][i], ref)
+        errs[f"lse{i}"] = lse_err(r["lse"][i], fs["lse"])
+    bad = {k: e for k, e in errs.items() if not (e <= tol)}
+    say(f"[gpu] attention layer: worst {max(errs.values()):.3e}")
+    assert not bad, f"over {tol}: {bad}"
+
+
+@pytest.mark.parametrize("s,b,d,heads,t,causal", [
+    (5, 2, 128, 2, 2, True),
+    (40, 1, 256, 2, 1, False),
+])
+def test_layer_fp32(s, b, d, heads, t, causal):
+    compare_layer(s, b, d, heads, t, causal, "f32")
+
+
+@pytest.mark.parametrize("s,b,d,heads,t,causal", [
+    (5, 2, 128, 2, 2, True),
+    (70, 3, 256, 4, 2, True),      # dh = 64
+    (130, 2, 512, 4, 2, False),    # dh = 128
+    (200, 2, 768, 6, 3, True),
+])
+def test_layer_bf16(s, b, d, heads, t, causal):
+    compare_layer(s, b, d, heads, t, causal, "bf16")
+
+
+def test_gpt8p3b_attention_shard0_full():
+    """h = 3072, 24 heads of 128, t = 8 (3 heads per shard), b = 8, s = 1024,
+    causal: all 8 shards on the GPU; shard 0 compared in full with the oracle
+    computing that shard from scratch (its QKV, attention, projection and
+    every gradient), plus sampled rows of the summed output's input
+    gradient partial of shard 7."""
+    c = CONFIGS["gpt8p3b_attn_t8"]
+    s, b, d, heads, t, causal = c["s"], c["b"], c["d"], c["heads"], c["t"], c["causal"]
+    inp = config_inputs("gpt8p3b_attn_t8", seed=0)
+    say(f"[gpu] 8.3B-shaped attention: s={s} b={b} d={d} heads={heads} t={t}")
+    r = run_layer(inp, s, b, heads, t, causal)
+    nh = heads // t
+    Xf, Gf = inp["X"].f32, inp["G"].f32
+    Wq, Wp = inp["Wqkv"].f32, inp["Wproj"].f32
+    w = d // t
+    errs = {}
+    for i in (0, 7):
+        Wq_i, Wp_i = Wq[:, 3 * w * i:3 * w * (i + 1)], Wp[w * i:w * (i + 1), :]
+        fs = oa.shard_forward(Xf, Wq_i, Wp_i, s, b, nh, causal)
+        gs = oa.shard_backward(Xf, Wq_i, Wp_i, fs, Gf, s, b, nh)
+        for k, ref in (("QKV", fs["QKV"]), ("O", fs["O"]), ("P", fs["P"]), ("dO", gs["dO"]),
+                       ("dQKV", gs["dQKV"]), ("dWqkv", gs["dWqkv"]), ("dWproj", gs["dWproj"]),
+                       ("dXp", gs["dXp"])):
+            errs[f"{k}{i}"] = relerr(r[k][i], ref)
+        errs[f"lse{i}"] = lse_err(r["lse"][i], fs["lse"])
+        del fs, gs
+    bad = {k: e for k, e in errs.items() if not (e <= TOL["bf16"])}
+    say(f"[gpu] 8.3B-shaped attention: worst {max(errs.values()):.3e}")
+    assert not bad, f"over {TOL['bf16']}: {bad}"
+    del r
+    torch.cuda.empty_cache()

@@ -169,6 +169,15 @@ def attn_inputs(s, b, d, heads, dtype="bf16", seed=0, x_std=X_STD, w_std=W_STD, 
     return out
 
 
+def qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=0, std=1.0):
+    """The attention core's inputs alone: qkv [T, s·b, nh·3·dh] and an upstream
+    gradient do [T, s·b, nh·dh], both N(0, std²)."""
+    rng = np.random.default_rng(seed)
+    qkv = _draw(rng, (T, s * b, nh * 3 * dh), std, dtype)
+    do = _draw(rng, (T, s * b, nh * dh), std, dtype)
+    return {"qkv": Tensor(qkv, dtype), "do": Tensor(do, dtype)}
+
+
 def config_inputs(name, seed=0):
     c = CONFIGS[name]
     if c["kind"] == "attn":
