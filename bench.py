@@ -307,6 +307,76 @@ def leg_biased(tp, X, A_s, B_s, G, bufs, reps, flops):
                               **_stats(g2_ms)}}
 
 
+def leg_attention(tp, reps):
+    """The attention side of the 8.3B-shaped layer: h = 3072, 24 heads of 128,
+    t = 8 shards resident, b = 8, s = 1024, causal, bf16.  Forward = QKV GEMM,
+    flash-attention core, projection GEMM; backward = dW_proj with dO, the
+    core's backward, dW_qkv with dX.  FLOP counts: GEMMs 2·m·n·k each; the
+    core 4·b·s²·h forward and 8·b·s²·h backward in the pages' formula (no
+    causal discount, [EFF] FLOPs appendix), and also the causal half."""
+    import numpy as np
+    import torch
+    from tpmlp_inputs import CONFIGS
+    c = CONFIGS["gpt8p3b_attn_t8"]
+    s, b, d, heads, t = c["s"], c["b"], c["d"], c["heads"], c["t"]
+    dh = d // heads
+    w = d // t
+    n = s * b
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    bf = torch.bfloat16
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(bf)
+    X, G = rnd((n, d), 1.0), rnd((n, d), 0.01)
+    Wq, Wp = rnd((t, d, 3 * w), 0.02), rnd((t, w, d), 0.02)
+    QKV = torch.empty((t, n, 3 * w), dtype=bf, device=dev)
+    O = torch.empty((t, n, w), dtype=bf, device=dev)
+    lse = torch.empty((t, b, heads // t, s), dtype=torch.float32, device=dev)
+    P = torch.empty((t, n, d), dtype=bf, device=dev)
+    dO, dQKV = torch.empty_like(O), torch.empty_like(QKV)
+    dWq = torch.empty((t, d, 3 * w), dtype=torch.float32, device=dev)
+    dWp = torch.empty((t, w, d), dtype=torch.float32, device=dev)
+    dXp = torch.empty_like(P)
+    ws = torch.empty(tp.attn_bwd_workspace_bytes(t, s, b, heads // t), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        tp.tpmlp_attn_fwd(X, Wq, Wp, QKV, O, lse, P, s, b, dh, True, stream)
+
+    def core_f():
+        tp.tpmlp_attn_core_fwd(QKV, O, lse, s, b, heads // t, dh, True, stream)
+
+    def core_b():
+        tp.tpmlp_attn_core_bwd(QKV, O, lse, dO, dQKV, ws, s, b, heads // t, dh, True, stream)
+
+    def bwd():
+        tp.tpmlp_attn_bwd(X, Wq, Wp, QKV, O, lse, G, dO, dQKV, dWq, dWp, dXp, ws, s, b, dh, True, stream)
+
+    for _ in range(3):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    out = {"workload": f"attention side of the 8.3B-shaped layer: h={d}, {heads} heads of {dh}, t={t} "
+                       f"resident, b={b}, s={s}, causal, bf16"}
+    gemm_f = 2.0 * n * d * 3 * w * t + 2.0 * n * w * d * t
+    core_f_flop = 4.0 * b * s * s * d            # QK^T and A·V over all heads, pages' formula
+    for name, fn, fl in (("fwd", fwd, gemm_f + core_f_flop), ("bwd", bwd, 2 * gemm_f + 2 * core_f_flop),
+                         ("core_fwd", core_f, core_f_flop), ("core_bwd", core_b, 2 * core_f_flop)):
+        ms = _time_events(fn, reps)
+        med = float(np.median(ms))
+        out[name] = {"flop_pages_formula": fl, "tflops_median": round(fl / (med * 1e-3) / 1e12, 2),
+                     **_stats(ms)}
+        if name.startswith("core"):
+            out[name]["tflops_causal_half"] = round(fl / 2 / (med * 1e-3) / 1e12, 2)
+    step = out["fwd"]["median_ms"] + out["bwd"]["median_ms"]
+    tot = 3 * gemm_f + 3 * core_f_flop
+    out["step"] = {"median_ms": round(step, 4), "tflops": round(tot / (step * 1e-3) / 1e12, 2),
+                   "pct_of_peak": round(100.0 * tot / (step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    return out
+
+
 def recorded_traffic(kernel_file, summary):
     """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     in a profiles/ summary, or None when the summary is missing or the kernel
@@ -477,6 +547,8 @@ def main():
                               **leg_mlp_shard(tp, 2048, 25600, 12800, 10, seed=2)}
         torch.cuda.empty_cache()
         rec["sp_region"] = leg_sp(tp, 10)
+        torch.cuda.empty_cache()
+        rec["attention"] = leg_attention(tp, 10)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, t, args.cpu_seconds)
     if args.cpu_all_configs:

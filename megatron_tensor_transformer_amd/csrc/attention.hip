@@ -110,28 +110,45 @@ __device__ __forceinline__ bf16x8 frag_rows(const TPMLP_LDS char* tile, int row,
   return *(const TPMLP_LDS bf16x8*)(tile + kv_slot<DH>(row, chunk));
 }
 
-// MFMA operand with rows = tile columns 32d .. 32d+31 and k = 16 tile rows of
-// block (u, c2) in the accumulators' order: lane L gets column 32d + L%32,
-// rows 32u + 16c2 + 4·(L/32) + {0..3} then the same + 8.
-template <int DH>
-__device__ __forceinline__ bf16x8 frag_tr(const TPMLP_LDS char* tile, int u, int c2, int d, int lane) {
+// MFMA operands with rows = tile columns 32d .. 32d+31 (d < ND) and k = 16
+// tile rows of block (u, c2) in the accumulators' order: lane L gets column
+// 32d + L%32, rows 32u + 16c2 + 4·(L/32) + {0..3} then the same + 8.  The
+// transposing reads are inline asm (the builtin form made the compiler wait
+// for every outstanding buffer→LDS load first, and its element-wise
+// assembly into bf16x8 was miscompiled), followed by one explicit LDS wait;
+// the results are operands of the wait so no use can move above it.
+template <int DH, int ND>
+__device__ __forceinline__ void frag_tr(const TPMLP_LDS char* tile, int u, int c2, int lane, bf16x8 (&out)[ND]) {
   const int g = lane >> 4, i = lane & 15;
   const int r = 32 * u + 16 * c2 + 4 * (lane >> 5) + (i >> 2);
-  const int col = 32 * d + 16 * (g & 1) + 4 * (i & 3);
-  const s16x4 t0 =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPMLP_LDS s16x4*)(tile + kv_slot<DH>(r, col >> 3) + (col & 7) * 2));
-  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (TPMLP_LDS s16x4*)(tile + kv_slot<DH>(r + 8, col >> 3) + (col & 7) * 2));
-  // whole-register moves (the element-wise form was miscompiled: only the
-  // first dword of each read was kept)
-  const i32x2 w0 = __builtin_bit_cast(i32x2, t0), w1 = __builtin_bit_cast(i32x2, t1);
-  i32x4 w;
-  w[0] = w0[0];
-  w[1] = w0[1];
-  w[2] = w1[0];
-  w[3] = w1[1];
-  return __builtin_bit_cast(bf16x8, w);
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tile));
+  i32x2 t[2 * ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const int col = 32 * d + 16 * (g & 1) + 4 * (i & 3);
+    const uint32_t a0 = base + kv_slot<DH>(r, col >> 3) + (col & 7) * 2;
+    const uint32_t a1 = base + kv_slot<DH>(r + 8, col >> 3) + (col & 7) * 2;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(t[2 * d]) : "v"(a0) : "memory");
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(t[2 * d + 1]) : "v"(a1) : "memory");
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0])::"memory");
+#pragma unroll
+  for (int k = 1; k < 2 * ND; ++k) asm volatile("" : "+v"(t[k]));
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    i32x4 w;
+    w[0] = t[2 * d][0];
+    w[1] = t[2 * d][1];
+    w[2] = t[2 * d + 1][0];
+    w[3] = t[2 * d + 1][1];
+    out[d] = __builtin_bit_cast(bf16x8, w);
+  }
 }
+
+// Workgroup barrier that is also a compiler barrier for memory accesses (LDS
+// reads must not move above it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // values 8·c2 .. 8·c2+7 of an accumulator block as a bf16 MFMA operand
 __device__ __forceinline__ bf16x8 pack_acc(const f32x16& x, int c2) {
@@ -139,6 +156,40 @@ __device__ __forceinline__ bf16x8 pack_acc(const f32x16& x, int c2) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = f2bf(x[8 * c2 + e]);
   return f;
+}
+
+// max / sum of a value over lanes L and L^32 (the two halves of a row):
+// v_permlane32_swap gives each lane both halves' values, in a VALU op.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Keep entries (u, v) of a tile's accumulator pair whose index
+// 32u + 8(v/4) + 4·hi + v%4 (relative to the tile) lies in [lo, hi_): the
+// rest become `fill`.  lo and hi_ are per-lane bounds already relative to the
+// tile and to this lane's 4·hi offset.
+__device__ __forceinline__ void mask_range(f32x16 (&x)[2], int lo, int hi_, float fill) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int k = 32 * u + 8 * (v >> 2) + (v & 3);
+      x[u][v] = (k >= lo && k < hi_) ? x[u][v] : fill;
+    }
+}
+
+// the same for one accumulator block u
+__device__ __forceinline__ void mask_range1(f32x16& x, int u, int lo, int hi_, float fill) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int k = 32 * u + 8 * (v >> 2) + (v & 3);
+    x[v] = (k >= lo && k < hi_) ? x[v] : fill;
+  }
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -201,7 +252,7 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
     } else {
       wait_vmcnt<0>();
     }
-    block_barrier();
+    lds_barrier();
     const TPMLP_LDS char* kb = lds + st * 2 * TILE;
     const TPMLP_LDS char* vb = kb + TILE;
 
@@ -209,27 +260,31 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
     f32x16 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      // all of the half's K fragments first, so the reads overlap
+      bf16x8 kf[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[c] = frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi);
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[u][v] = 0.f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sacc[u] = mfma(frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi), qf[c], sacc[u]);
+      for (int c = 0; c < NC; ++c) sacc[u] = mfma(kf[c], qf[c], sacc[u]);
     }
 
-    // mask, running maximum, exponentials, running sum
+    // mask (only tiles that reach past s or, causal, past the wave's first
+    // query row), running maximum, exponentials, running sum
+    const int t0 = j * AKV;
+    if (t0 + AKV > a.s || (CAUSAL && t0 + AKV - 1 > q0)) {
+      const int lim = CAUSAL ? min(qrow + 1, a.s) : a.s;
+      mask_range(sacc, -1 << 30, lim - t0 - 4 * hi, -INFINITY);
+    }
     float mloc = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kv = j * AKV + 32 * u + 8 * (v >> 2) + 4 * hi + (v & 3);
-        const bool keep = kv < a.s && (!CAUSAL || kv <= qrow);
-        sacc[u][v] = keep ? sacc[u][v] : -INFINITY;
-        mloc = fmaxf(mloc, sacc[u][v]);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[u][v]);
+    mloc = pair_max(mloc);
     const float mnew = fmaxf(m, mloc);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f((m - muse) * a.scale_log2);
     const float off = -muse * a.scale_log2;
     float lsum = 0.f;
 #pragma unroll
@@ -240,13 +295,18 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
         sacc[u][v] = p;
         lsum += p;
       }
-    lsum += __shfl_xor(lsum, 32, 64);
-    l = l * alpha + lsum;
+    lsum = pair_sum(lsum);
+    // rescale the running sum and output only when some row's maximum grew
+    if (__any(mnew != m)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - muse) * a.scale_log2);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
+    }
+    l += lsum;
     m = mnew;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
 
     // Oᵀ += Vᵀ·Pᵀ over the tile's keys, 16 at a time.  P fragment (u, c2):
     // this lane's values v = 8·c2 .. 8·c2+7 of sacc[u]; they are keys
@@ -257,10 +317,12 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const bf16x8 pf = pack_acc(sacc[u], c2);
+        bf16x8 vf[ND];
+        frag_tr<DH, ND>(vb, u, c2, lane, vf);
 #pragma unroll
-        for (int d = 0; d < ND; ++d) oacc[d] = mfma(frag_tr<DH>(vb, u, c2, d, lane), pf, oacc[d]);
+        for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pf, oacc[d]);
       }
-    block_barrier();  // every wave is done with stage st before it is refilled
+    lds_barrier();  // every wave is done with stage st before it is refilled
   }
 
   // o = oacc / l; lane holds row qrow, dh = 32d + 8(v/4) + 4·hi + v%4
@@ -374,12 +436,14 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnBwdArgs a) {
 }
 
 // dq: a workgroup takes 128 query rows of one (shard, batch entry, head), a
-// wave 32, with q and do fragments in registers; K and V tiles of 64 keys
-// stream through LDS.  Per tile: Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ (lane L holds row
+// wave 32, with q, do and o fragments in registers; K and V tiles of 64 keys
+// stream through LDS.  δ = rowsum(do ⊙ o) is formed here from the registers
+// and written to the workspace for the dk/dv kernel, which runs after.  Per
+// 32-key half of a tile: Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ (lane L holds query row
 // L%32), P = exp2(S·log2(e)/√dh − lse·log2(e)), dS = P ⊙ (dP − δ), and
 // dQᵀ += Kᵀ·dSᵀ with the keys in the accumulators' order.
 template <int DH, bool CAUSAL>
-__global__ __launch_bounds__(ATHR, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int TILE = AKV * DH * 2;
   constexpr int NC = DH / 16, ND = DH / 32;
   constexpr int NI = TILE / 1024 / 4;
@@ -393,11 +457,10 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   const int bi = r % a.b, T = r / a.b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
-  const int qrow = qb * AQ + wave * 32 + r32;
+  const int q0 = qb * AQ + wave * 32, qrow = q0 + r32;
   const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
   const int64_t n = static_cast<int64_t>(a.s) * a.b;
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + T * n * row_len;
-  const bf16* dout = static_cast<const bf16*>(a.dout) + T * n * orow;
   const i32x4 rsrc = make_rsrc(qkv, a.qkv_shard_bytes);
   const int64_t kcol = static_cast<int64_t>(h) * 3 * DH + DH, vcol = kcol + DH;
   const int kv_end = CAUSAL ? min(a.s, qb * AQ + AQ) : a.s;
@@ -408,18 +471,26 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 
   bf16x8 qf[NC], df[NC];
   const bool valid = qrow < a.s;
+  const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
+  float dlt = 0.f;
   {
-    const bf16* qp = qkv + (static_cast<int64_t>(qrow) * a.b + bi) * row_len + h * 3 * DH + 8 * hi;
-    const bf16* dp = dout + (static_cast<int64_t>(qrow) * a.b + bi) * orow + h * DH + 8 * hi;
+    const int64_t tok = static_cast<int64_t>(qrow) * a.b + bi;
+    const bf16* qp = qkv + tok * row_len + h * 3 * DH + 8 * hi;
+    const int64_t oo = T * n * orow + tok * orow + h * DH + 8 * hi;
+    const bf16* dp = static_cast<const bf16*>(a.dout) + oo;
+    const bf16* op = static_cast<const bf16*>(a.o) + oo;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       qf[c] = valid ? *reinterpret_cast<const bf16x8*>(qp + 16 * c) : bf16x8{};
       df[c] = valid ? *reinterpret_cast<const bf16x8*>(dp + 16 * c) : bf16x8{};
+      const bf16x8 of = valid ? *reinterpret_cast<const bf16x8*>(op + 16 * c) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = fmaf(bf2f(df[c][e]), bf2f(of[e]), dlt);
     }
   }
-  const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
+  dlt += __shfl_xor(dlt, 32, 64);
+  if (valid && hi == 0) a.delta[srow + qrow] = dlt;
   const float lse2 = valid ? a.lse[srow + qrow] * 1.4426950408889634f : 0.f;
-  const float dlt = valid ? a.delta[srow + qrow] : 0.f;
 
   f32x16 dq[ND];
 #pragma unroll
@@ -437,38 +508,45 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     } else {
       wait_vmcnt<0>();
     }
-    block_barrier();
+    lds_barrier();
     const TPMLP_LDS char* kb = lds + st * 2 * TILE;
     const TPMLP_LDS char* vb = kb + TILE;
-    f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      f32x16 sacc, pacc;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[u][v] = pacc[u][v] = 0.f;
+      for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+      bf16x8 kr[NC], vr[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc[u] = mfma(frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi), qf[c], sacc[u]);
-        pacc[u] = mfma(frag_rows<DH>(vb, 32 * u + r32, 2 * c + hi), df[c], pacc[u]);
+        kr[c] = frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi);
+        vr[c] = frag_rows<DH>(vb, 32 * u + r32, 2 * c + hi);
       }
-    }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int c = 0; c < NC; ++c) {
+        sacc = mfma(kr[c], qf[c], sacc);
+        pacc = mfma(vr[c], df[c], pacc);
+      }
+      const int t0 = j * AKV;
+      if (t0 + AKV > a.s || q0 + 31 >= a.s || (CAUSAL && t0 + AKV - 1 > q0)) {
+        const int lim = valid ? (CAUSAL ? min(qrow + 1, a.s) : a.s) : 0;
+        mask_range1(sacc, u, -1 << 30, lim - t0 - 4 * hi, -INFINITY);
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int kv = j * AKV + 32 * u + 8 * (v >> 2) + 4 * hi + (v & 3);
-        const bool keep = valid && kv < a.s && (!CAUSAL || kv <= qrow);
-        const float p = keep ? __builtin_amdgcn_exp2f(fmaf(sacc[u][v], a.scale_log2, -lse2)) : 0.f;
-        sacc[u][v] = p * (pacc[u][v] - dlt);  // dS
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], a.scale_log2, -lse2));
+        sacc[v] = p * (pacc[v] - dlt);  // dS
       }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 sf = pack_acc(sacc[u], c2);
+        const bf16x8 sf = pack_acc(sacc, c2);
+        bf16x8 kt[ND];
+        frag_tr<DH, ND>(kb, u, c2, lane, kt);
 #pragma unroll
-        for (int d = 0; d < ND; ++d) dq[d] = mfma(frag_tr<DH>(kb, u, c2, d, lane), sf, dq[d]);
+        for (int d = 0; d < ND; ++d) dq[d] = mfma(kt[d], sf, dq[d]);
       }
-    block_barrier();
+    }
+    lds_barrier();
   }
   if (valid) {
     bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(qrow) * a.b + bi) * row_len +
@@ -487,16 +565,16 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 
 // dk, dv: a workgroup takes 128 key rows, a wave 32, with k and v fragments in
 // registers; Q and dO tiles of 64 query rows (and their lse, δ) stream
-// through LDS.  Per tile: S'ᵀ = Q·Kᵀ and dP'ᵀ = dO·Vᵀ with lane L holding key
-// row L%32, P and dS as in dq, then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with the
-// query rows in the accumulators' order.
+// through LDS.  Per 32-query half of a tile: S'ᵀ = Q·Kᵀ and dP'ᵀ = dO·Vᵀ
+// with lane L holding key row L%32, P and dS as in dq, then dVᵀ += dOᵀ·P and
+// dKᵀ += Qᵀ·dS with the query rows in the accumulators' order.
 template <int DH, bool CAUSAL>
-__global__ __launch_bounds__(ATHR, 1) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   constexpr int TILE = AKV * DH * 2;
   constexpr int NC = DH / 16, ND = DH / 32;
   constexpr int NI = TILE / 1024 / 4;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
-  __shared__ float stat[2][2][AKV];  // [stage][lse·log2(e) | δ][row]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][AKV];  // [stage][lse·log2(e) | δ][row]
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
   const int x = blockIdx.x;
   const int kb_idx = x % a.nqb;  // key block
@@ -506,7 +584,7 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   const int bi = r % a.b, T = r / a.b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
-  const int krow = kb_idx * AQ + wave * 32 + r32;
+  const int k0 = kb_idx * AQ + wave * 32, krow = k0 + r32;
   const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
   const int64_t n = static_cast<int64_t>(a.s) * a.b;
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + T * n * row_len;
@@ -518,7 +596,7 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   const int j0 = CAUSAL ? (kb_idx * AQ) / AKV : 0;
   const int nq = (a.s + AKV - 1) / AKV;
 
-  // statistics of query block j into stage st (threads 0..127: one value each)
+  // statistics of query block j (threads 0..127: one value each)
   auto load_stat = [&](int j, float& v) {
     const int t = threadIdx.x & 63, qr = j * AKV + t;
     if (threadIdx.x < 64) v = qr < a.s ? a.lse[srow + qr] * 1.4426950408889634f : 0.f;
@@ -529,11 +607,9 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   };
 
   float sv = 0.f;
-  if (j0 < nq) {
-    load_stat(j0, sv);
-    load_tile<DH>(rq, lds, a.s, a.b, bi, row_len, qcol, j0, wave, lane);
-    load_tile<DH>(rd, lds + TILE, a.s, a.b, bi, orow, dcol, j0, wave, lane);
-  }
+  load_stat(j0, sv);
+  load_tile<DH>(rq, lds, a.s, a.b, bi, row_len, qcol, j0, wave, lane);
+  load_tile<DH>(rd, lds + TILE, a.s, a.b, bi, orow, dcol, j0, wave, lane);
 
   bf16x8 kf[NC], vf[NC];
   const bool valid = krow < a.s;
@@ -564,53 +640,68 @@ __global__ __launch_bounds__(ATHR, 1) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     } else {
       wait_vmcnt<0>();
     }
-    wait_lgkmcnt0();  // this wave's stat writes of the previous step are done
-    block_barrier();
+    lds_wait();  // this wave's statistics writes of the previous step are done
+    lds_barrier();
     const TPMLP_LDS char* qt = lds + st * 2 * TILE;
     const TPMLP_LDS char* dt = qt + TILE;
-    f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      f32x16 sacc, pacc;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[u][v] = pacc[u][v] = 0.f;
+      for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+      bf16x8 qr_[NC], dr[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc[u] = mfma(frag_rows<DH>(qt, 32 * u + r32, 2 * c + hi), kf[c], sacc[u]);
-        pacc[u] = mfma(frag_rows<DH>(dt, 32 * u + r32, 2 * c + hi), vf[c], pacc[u]);
+        qr_[c] = frag_rows<DH>(qt, 32 * u + r32, 2 * c + hi);
+        dr[c] = frag_rows<DH>(dt, 32 * u + r32, 2 * c + hi);
       }
-    }
-    // lane: key krow, query rows 64j + 32u + 8(v/4) + 4·hi + v%4
-    f32x16 pv[2];
+      // the statistics of this lane's 16 query rows, 4 consecutive per read
+      f32x4 ls[4], ds[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int g = 0; g < 4; ++g) {
+        ls[g] = *reinterpret_cast<const f32x4*>(&stat[st][0][32 * u + 8 * g + 4 * hi]);
+        ds[g] = *reinterpret_cast<const f32x4*>(&stat[st][1][32 * u + 8 * g + 4 * hi]);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        sacc = mfma(qr_[c], kf[c], sacc);
+        pacc = mfma(dr[c], vf[c], pacc);
+      }
+      // lane: key krow, query rows 64j + 32u + 8(v/4) + 4·hi + v%4; the
+      // mask runs only on tiles that reach past s, past this wave's keys'
+      // diagonal, or hold key rows past s
+      const int t0 = j * AKV;
+      if (t0 + AKV > a.s || k0 + 31 >= a.s || (CAUSAL && t0 < k0 + 31)) {
+        const int lo = CAUSAL ? krow - t0 - 4 * hi : -1 << 30;
+        const int hi_ = valid ? a.s - t0 - 4 * hi : lo;
+        mask_range1(sacc, u, lo, hi_, -INFINITY);
+      }
+      f32x16 pv;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * g + e;
-          const int qi = 32 * u + 8 * g + 4 * hi + e;
-          const int qr = j * AKV + qi;
-          const bool keep = valid && qr < a.s && (!CAUSAL || qr >= krow);
-          const float p = keep ? __builtin_amdgcn_exp2f(fmaf(sacc[u][v], a.scale_log2, -stat[st][0][qi])) : 0.f;
-          pv[u][v] = p;
-          sacc[u][v] = p * (pacc[u][v] - stat[st][1][qi]);  // dS
+          pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[v], a.scale_log2, -ls[g][e]));
+          sacc[v] = pv[v] * (pacc[v] - ds[g][e]);  // dS
         }
-    // store the next block's statistics into the other stage (read after the
-    // next barrier)
-    if (j + 1 < nq) store_stat(st ^ 1, sv);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 pf = pack_acc(pv[u], c2);
-        const bf16x8 sf = pack_acc(sacc[u], c2);
+        const bf16x8 pf = pack_acc(pv, c2);
+        const bf16x8 sf = pack_acc(sacc, c2);
+        bf16x8 ft[ND];
+        frag_tr<DH, ND>(dt, u, c2, lane, ft);
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          dv[d] = mfma(frag_tr<DH>(dt, u, c2, d, lane), pf, dv[d]);
-          dk[d] = mfma(frag_tr<DH>(qt, u, c2, d, lane), sf, dk[d]);
-        }
+        for (int d = 0; d < ND; ++d) dv[d] = mfma(ft[d], pf, dv[d]);
+        frag_tr<DH, ND>(qt, u, c2, lane, ft);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dk[d] = mfma(ft[d], sf, dk[d]);
       }
-    block_barrier();
+    }
+    // the next block's statistics go into the other stage (read after the
+    // next barrier)
+    if (j + 1 < nq) store_stat(st ^ 1, sv);
+    lds_barrier();
   }
   if (valid) {
     bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(krow) * a.b + bi) * row_len +
@@ -722,20 +813,19 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(AttnBwdArgs a) {
 template <int DH, bool CAUSAL>
 hipError_t launch_bwd_t(const AttnBwdArgs& a, int dt, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.T) * a.b * a.nh * a.s;
-  const unsigned dblocks = static_cast<unsigned>((rows + 255) / 256);
-  if (dt == 1)
-    hipLaunchKernelGGL((attn_delta_kernel<bf16, DH>), dim3(dblocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_delta_kernel<float, DH>), dim3(dblocks), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   if (dt == 1) {
+    // dq also forms δ (into the workspace) for the dk/dv kernel after it
     const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.T) * a.b * a.nh * a.nqb);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
   } else {
+    const unsigned dblocks = static_cast<unsigned>((rows + 255) / 256);
+    hipLaunchKernelGGL((attn_delta_kernel<float, DH>), dim3(dblocks), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const unsigned blocks = static_cast<unsigned>((rows + 127) / 128);
     hipLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<DH, CAUSAL>), dim3(blocks), dim3(128), 0, stream, a);
     e = hipGetLastError();
