@@ -28,8 +28,11 @@
 //
 // fp32 path (correctness reference, not tuned): one thread per query row
 // (forward, dq) or key row (dk, dv), online softmax in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
+#include "tile_map.h"
 
 namespace tpmlp {
 namespace {
@@ -37,7 +40,7 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int AQ = 128;   // query rows per workgroup (4 waves × 32)
+constexpr int AQ = 128;   // query (key) rows per workgroup (4 waves × 32)
 constexpr int AKV = 64;   // key rows per step
 constexpr int ATHR = 256;
 constexpr uint32_t AOOB = 0x80000000u;
@@ -65,10 +68,20 @@ struct AttnArgs {
   uint32_t qkv_shard_bytes;
 };
 
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.  The
+// logical order (shard, batch entry, head, block) is mapped so that each XCD
+// runs a contiguous range of it: the blocks of one head, which read the same
+// K/V (or Q/dO) panel, share an L2.
+__device__ __forceinline__ int xcd_logical(int total) {
+  int begin, count;
+  xcd_range(total, static_cast<int>(blockIdx.x & 7), begin, count);
+  return begin + static_cast<int>(blockIdx.x >> 3);
+}
+
 // Workgroup -> (shard, batch entry, head, query block); the longest causal
-// blocks (last in the sequence) are dealt first.
+// blocks (last in the sequence) come first within a head.
 __device__ __forceinline__ void attn_coords(const AttnArgs& a, int& T, int& bi, int& h, int& qb) {
-  const int x = blockIdx.x;
+  const int x = xcd_logical(static_cast<int>(gridDim.x));
   qb = a.nqb - 1 - (x % a.nqb);
   int r = x / a.nqb;
   h = r % a.nh;
@@ -196,14 +209,99 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Per-lane DMA plan of a [AKV][DH] tile: the byte offset of this lane's 16-B
+// chunk for key block 0 and its row; block j adds j·AKV rows.
+template <int DH, int NW = 4>
+struct TilePlan {
+  static constexpr int NI = AKV * DH * 2 / 1024 / NW;
+  uint32_t voff[NI];
+  int row[NI];
+};
+
+template <int DH, int NW = 4>
+__device__ __forceinline__ TilePlan<DH, NW> tile_plan(int b, int bi, int64_t row_len, int64_t col, int wave,
+                                                      int lane) {
+  constexpr int RPI = 1024 / (DH * 2), CPR = DH / 8;
+  TilePlan<DH, NW> p;
+#pragma unroll
+  for (int q = 0; q < TilePlan<DH, NW>::NI; ++q) {
+    const int I = wave * TilePlan<DH, NW>::NI + q;
+    const int row = I * RPI + lane / CPR;
+    int f;
+    if constexpr (DH == 128) f = ((row & 3) << 2) | ((row >> 2) & 3);
+    else f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    const int chunk = (lane % CPR) ^ f;
+    p.row[q] = row;
+    p.voff[q] = static_cast<uint32_t>(((static_cast<int64_t>(row) * b + bi) * row_len + col + chunk * 8) * 2);
+  }
+  return p;
+}
+
+// DMA of key/query block j by plan p into `tile` (stride = bytes per AKV rows
+// of the tensor, rows past s zero-filled).
+template <int DH, int NW = 4>
+__device__ __forceinline__ void issue_tile(i32x4 rsrc, TPMLP_LDS char* tile, const TilePlan<DH, NW>& p, int j,
+                                           uint32_t stride, int s, int wave) {
+#pragma unroll
+  for (int q = 0; q < TilePlan<DH, NW>::NI; ++q) {
+    const uint32_t voff = j * AKV + p.row[q] < s ? p.voff[q] + static_cast<uint32_t>(j) * stride : AOOB;
+    buffer_load_lds16(rsrc, tile + (wave * TilePlan<DH, NW>::NI + q) * 1024, voff);
+  }
+}
+
+// Per-lane LDS addresses of the transposing reads of a tile at its base
+// (blocks (u, c2) add (32u + 16c2) rows, a constant: the swizzle depends on
+// the row modulo 16 only).  Entry 2d + k: column block d, second read k.
+template <int DH, int ND>
+__device__ __forceinline__ void tr_addrs(uint32_t base, int lane, uint32_t (&o)[2 * ND]) {
+  const int g = lane >> 4, i = lane & 15;
+  const int r = 4 * (lane >> 5) + (i >> 2);
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const int col = 32 * d + 16 * (g & 1) + 4 * (i & 3);
+    o[2 * d] = base + kv_slot<DH>(r, col >> 3) + (col & 7) * 2;
+    o[2 * d + 1] = base + kv_slot<DH>(r + 8, col >> 3) + (col & 7) * 2;
+  }
+}
+
+// The ND transposed fragments of block (u, c2) at byte offset IMM (stage,
+// tile and block) from the precomputed addresses; one explicit LDS wait.
+template <int DH, int ND, int IMM>
+__device__ __forceinline__ void frag_tr_at(const uint32_t (&ad)[2 * ND], bf16x8 (&out)[ND]) {
+  // the instruction's offset field has 16 bits: a larger IMM moves its high
+  // part into the address
+  constexpr uint32_t HI = (static_cast<uint32_t>(IMM) >> 16) << 16, LO = IMM - HI;
+  i32x2 t[2 * ND];
+#pragma unroll
+  for (int k = 0; k < 2 * ND; ++k)
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(t[k]) : "v"(ad[k] + HI), "i"(LO) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0])::"memory");
+#pragma unroll
+  for (int k = 1; k < 2 * ND; ++k) asm volatile("" : "+v"(t[k]));
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    i32x4 w;
+    w[0] = t[2 * d][0];
+    w[1] = t[2 * d][1];
+    w[2] = t[2 * d + 1][0];
+    w[3] = t[2 * d + 1][1];
+    out[d] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 template <int DH, bool CAUSAL>
 __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int TILE = AKV * DH * 2;
+  constexpr int TILE = AKV * DH * 2, RB = DH * 2;
   constexpr int NC = DH / 16;   // k16 slices of the head dimension
   constexpr int ND = DH / 32;   // 32-wide head-dimension blocks of o
-  constexpr int NI = TILE / 1024 / 4;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  constexpr int NW = ATHR / 64;
+  constexpr int NI = TilePlan<DH, NW>::NI;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
   int T, bi, h, qb;
   attn_coords(a, T, bi, h, qb);
@@ -214,15 +312,18 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH;
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + static_cast<int64_t>(T) * a.s * a.b * row_len;
   const i32x4 rsrc = make_rsrc(qkv, a.qkv_shard_bytes);
+  const uint32_t stride = static_cast<uint32_t>(static_cast<int64_t>(AKV) * a.b * row_len * 2);
 
   // key blocks this workgroup visits
   const int kv_end = CAUSAL ? min(a.s, qb * AQ + AQ) : a.s;
   const int nkv = (kv_end + AKV - 1) / AKV;
 
-  const int64_t kcol = static_cast<int64_t>(h) * 3 * DH + DH, vcol = kcol + DH;
+  const int64_t kcol = static_cast<int64_t>(h) * 3 * DH + DH;
+  const TilePlan<DH, NW> kp = tile_plan<DH, NW>(a.b, bi, row_len, kcol, wave, lane);
+  const TilePlan<DH, NW> vp = tile_plan<DH, NW>(a.b, bi, row_len, kcol + DH, wave, lane);
   // prologue: K and V of block 0 into stage 0
-  load_tile<DH>(rsrc, lds, a.s, a.b, bi, row_len, kcol, 0, wave, lane);
-  load_tile<DH>(rsrc, lds + TILE, a.s, a.b, bi, row_len, vcol, 0, wave, lane);
+  issue_tile<DH, NW>(rsrc, lds, kp, 0, stride, a.s, wave);
+  issue_tile<DH, NW>(rsrc, lds + TILE, vp, 0, stride, a.s, wave);
 
   // this lane's q fragments: row qrow, dh = 16c + 8·hi + 0..7
   bf16x8 qf[NC];
@@ -234,6 +335,12 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
       else qf[c] = bf16x8{};
     }
   }
+  // row-fragment offsets (row r32, chunk 2c + hi) and transposed-read addresses
+  uint32_t ko[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ko[c] = kv_slot<DH>(r32, 2 * c + hi);
+  uint32_t va[2 * ND];
+  tr_addrs<DH, ND>(lds_base, lane, va);
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -242,28 +349,28 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  for (int j = 0; j < nkv; ++j) {
-    const int st = j & 1;
+  // one key tile in stage ST (compile-time, so every LDS offset is an
+  // immediate); the DMA of the next tile runs during it
+  auto step = [&](auto stc, int j) {
+    constexpr int ST = decltype(stc)::value;
     if (j + 1 < nkv) {
-      TPMLP_LDS char* nxt = lds + (st ^ 1) * 2 * TILE;
-      load_tile<DH>(rsrc, nxt, a.s, a.b, bi, row_len, kcol, j + 1, wave, lane);
-      load_tile<DH>(rsrc, nxt + TILE, a.s, a.b, bi, row_len, vcol, j + 1, wave, lane);
+      TPMLP_LDS char* nxt = lds + (ST ^ 1) * 2 * TILE;
+      issue_tile<DH, NW>(rsrc, nxt, kp, j + 1, stride, a.s, wave);
+      issue_tile<DH, NW>(rsrc, nxt + TILE, vp, j + 1, stride, a.s, wave);
       wait_vmcnt<2 * NI>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();
-    const TPMLP_LDS char* kb = lds + st * 2 * TILE;
-    const TPMLP_LDS char* vb = kb + TILE;
+    const TPMLP_LDS char* kb = lds + ST * 2 * TILE;
 
     // Sᵀ block: sacc[u][v] = S[qrow][kv], kv = 64j + 32u + 8(v/4) + 4·hi + v%4
     f32x16 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      // all of the half's K fragments first, so the reads overlap
       bf16x8 kf[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kf[c] = frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi);
+      for (int c = 0; c < NC; ++c) kf[c] = *(const TPMLP_LDS bf16x8*)(kb + u * 32 * RB + ko[c]);
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[u][v] = 0.f;
 #pragma unroll
@@ -312,18 +419,28 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
     // this lane's values v = 8·c2 .. 8·c2+7 of sacc[u]; they are keys
     // 32u + 16c2 + {0..3, 8..11} (hi = 0) or {4..7, 12..15} (hi = 1), and the
     // V fragment rows are read in that same order.
+    constexpr int VB = ST * 2 * TILE + TILE;
+    bf16x8 vf[ND];
+    frag_tr_at<DH, ND, VB>(va, vf);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[0], 0), oacc[d]);
+    frag_tr_at<DH, ND, VB + 16 * RB>(va, vf);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 pf = pack_acc(sacc[u], c2);
-        bf16x8 vf[ND];
-        frag_tr<DH, ND>(vb, u, c2, lane, vf);
+    for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[0], 1), oacc[d]);
+    frag_tr_at<DH, ND, VB + 32 * RB>(va, vf);
 #pragma unroll
-        for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pf, oacc[d]);
-      }
-    lds_barrier();  // every wave is done with stage st before it is refilled
+    for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[1], 0), oacc[d]);
+    frag_tr_at<DH, ND, VB + 48 * RB>(va, vf);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[1], 1), oacc[d]);
+    lds_barrier();  // every wave is done with stage ST before it is refilled
+  };
+  int j = 0;
+  for (; j + 1 < nkv; j += 2) {
+    step(ic<0>{}, j);
+    step(ic<1>{}, j + 1);
   }
+  if (j < nkv) step(ic<0>{}, j);
 
   // o = oacc / l; lane holds row qrow, dh = 32d + 8(v/4) + 4·hi + v%4
   if (qrow < a.s) {
@@ -449,7 +566,7 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int NI = TILE / 1024 / 4;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
-  const int x = blockIdx.x;
+  const int x = xcd_logical(static_cast<int>(gridDim.x));
   const int qb = a.nqb - 1 - (x % a.nqb);
   int r = x / a.nqb;
   const int h = r % a.nh;
@@ -576,8 +693,8 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][AKV];  // [stage][lse·log2(e) | δ][row]
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
-  const int x = blockIdx.x;
-  const int kb_idx = x % a.nqb;  // key block
+  const int x = xcd_logical(static_cast<int>(gridDim.x));
+  const int kb_idx = x % a.nqb;  // key block (the first ones have the most query blocks)
   int r = x / a.nqb;
   const int h = r % a.nh;
   r /= a.nh;
