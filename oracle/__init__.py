@@ -1,6 +1,6 @@
 """Plain, slow fp64 CPU oracle for the tensor-parallel MLP shard, its
-sequence-parallel LayerNorm / dropout / residual region, and the
-tensor-parallel self-attention shard.
+sequence-parallel LayerNorm / dropout / residual region, the tensor-parallel
+self-attention shard and the vocabulary-parallel cross-entropy head.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP library
@@ -30,6 +30,9 @@ Parity pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   * philox.*     -- Random123 published known-answer vectors.
   * sp_block.*   -- sharded == unsharded (AllReduce = AllGather∘ReduceScatter),
                     finite differences, torch fp64 autograd.
+  * vocab_ce.*   -- torch's fp64 cross_entropy and autograd, split == unsplit
+                    for every divisor of V, finite differences, the closed
+                    form of zero logits.
   * attention.*  -- torch's fp64 scaled_dot_product_attention and autograd,
                     finite differences, heads split over shards == unsplit,
                     uniform attention when the queries are zero, shift
@@ -37,4 +40,4 @@ Parity pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
 No function here is "parity unpinned".
 """
 
-from . import mlp, layernorm, philox, sp_block, attention  # noqa: F401
+from . import mlp, layernorm, philox, sp_block, attention, vocab_ce  # noqa: F401

@@ -13,6 +13,9 @@ Recipe (the workloads of the tensor-parallel MLP shard, no dataset involved):
   * The attention side (attn_inputs): X [s·b, d], W_qkv [d, 3d], W_proj
     [d, d], G [s·b, d] drawn in that order with the same deviations; its
     optional biases from default_rng([seed, 2]).
+  * The logit layer (vocab_inputs): X [n, h], W [V, h], targets uniform in
+    [0, V), g [n] (the upstream gradient of each token's loss; the mean loss
+    over n tokens has g = 1/n), drawn in that order.
   * Biases b1 [m], b2 [d] (bias_inputs) come from a stream of their own,
     default_rng([seed, 1]), with std 0.5.
   * fp64 -> fp32 by round-to-nearest-even (numpy), fp32 -> bf16 by
@@ -43,6 +46,11 @@ CONFIGS = {
     # t=8 (3 heads per shard), b=8, s=1024 tokens per sequence, causal.
     "gpt8p3b_attn_t8": dict(kind="attn", s=1024, b=8, d=3072, heads=24, t=8, dtype="bf16",
                             causal=True, x_std=X_STD, w_std=W_STD, g_std=G_STD),
+    # logit layer + cross-entropy of the 8.3B-shaped model: h=3072, a padded
+    # GPT-2 vocabulary V=51200 (50257 rounded up to a multiple of 1024), t=8
+    # (6400 entries per shard), n=b·s=8·1024 tokens.
+    "gpt8p3b_vocab_t8": dict(kind="vocab", n=8192, d=3072, V=51200, t=8, dtype="bf16",
+                             x_std=X_STD, w_std=W_STD, g_std=1.0 / 8192),
     # sequence-parallel block: s=4096, h=4096, m=4h, t=8, LN + dropout 0.1.
     "sp_block_t8": dict(kind="sp", n=4096, d=4096, m=16384, t=8, dtype="bf16",
                         x_std=X_STD, w_std=W_STD, g_std=G_STD,
@@ -169,6 +177,18 @@ def attn_inputs(s, b, d, heads, dtype="bf16", seed=0, x_std=X_STD, w_std=W_STD, 
     return out
 
 
+def vocab_inputs(n, h, V, dtype="bf16", seed=0, x_std=X_STD, w_std=W_STD, g_std=1.0):
+    """The logit layer: X [n, h], the embedding table W [V, h], integer targets
+    [n] uniform in [0, V) (int32), and an upstream gradient per token's loss
+    g [n], drawn in that order."""
+    rng = np.random.default_rng(seed)
+    X = _draw(rng, (n, h), x_std, dtype)
+    W = _draw(rng, (V, h), w_std, dtype)
+    targets = rng.integers(0, V, size=n).astype(np.int32)
+    g = _draw(rng, (n,), g_std, "f32")
+    return {"X": Tensor(X, dtype), "W": Tensor(W, dtype), "targets": targets, "g": Tensor(g, "f32")}
+
+
 def qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=0, std=1.0):
     """The attention core's inputs alone: qkv [T, s·b, nh·3·dh] and an upstream
     gradient do [T, s·b, nh·dh], both N(0, std²)."""
@@ -180,6 +200,8 @@ def qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=0, std=1.0):
 
 def config_inputs(name, seed=0):
     c = CONFIGS[name]
+    if c["kind"] == "vocab":
+        return vocab_inputs(c["n"], c["d"], c["V"], c["dtype"], seed, c["x_std"], c["w_std"], c["g_std"])
     if c["kind"] == "attn":
         return attn_inputs(c["s"], c["b"], c["d"], c["heads"], c["dtype"], seed, c["x_std"],
                            c["w_std"], c["g_std"])
