@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 3
+#define TPMLP_ABI_VERSION 4
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -315,6 +315,41 @@ int tpmlp_attn_core_fwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, 
 int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
                         int32_t head_dim, int causal, const void* qkv, const void* o, const float* lse,
                         const void* d_o, void* dqkv, void* ws, size_t ws_bytes);
+
+/*
+ * Vocabulary-parallel logit layer and cross-entropy ([SENSE] §2.2.2, Eq. (3)
+ * and (4); the logit layer's FLOPs per [EFF]'s appendix).  Shard i owns
+ * vocabulary entries [vocab_start + i·v_i, vocab_start + (i+1)·v_i): rows
+ * W_i [v_i, h] of the embedding table.
+ *
+ * tpmlp_vocab_ce_fwd:
+ *   logits_i = X·W_iᵀ                              [n, v_i]  dt
+ *   per shard and token: m_i = max, s_i = Σ exp(x − m_i), τ_i = target logit
+ *   if the target is the shard's entry, else 0; combined by a max and two
+ *   sums in shard order (the three small all-reduces of the page):
+ *   row_max = max_i m_i, row_sum = Σ_i s_i·exp(m_i − row_max),
+ *   loss = ln(row_sum) + row_max − Σ_i τ_i          [n] fp32 each
+ * tpmlp_vocab_ce_bwd, g [n] fp32 = ∂ℓ/∂loss (1/n for the mean loss):
+ *   dlogits_i = g·(exp(logits_i − row_max)/row_sum − onehot(target))   dt
+ *   dW_i = dlogits_iᵀ·X  [v_i, h] fp32;  dX_i = dlogits_i·W_i [n, h] dt
+ *   (partial: dX = Σ_i dX_i by tpmlp_reduce_partials)
+ *
+ *   X [n, h]; W [t_local, v_i, h]; targets [n] int32 global vocabulary ids;
+ *   logits, dlogits [t_local, n, v_i]; dW [t_local, v_i, h]; dXp [t_local,
+ *   n, h].  Exponentials and sums in fp32.  A target outside the resident
+ *   shards contributes no target logit (its owner is another rank).
+ *   bf16 needs h % 8 == 0 and v_i % 8 == 0 (as d and m_i of tpmlp_fwd).
+ *   Workspace of the forward: tpmlp_vocab_ce_workspace_bytes(t_local, n)
+ *   bytes (the shards' statistics), 4-byte aligned.
+ */
+size_t tpmlp_vocab_ce_workspace_bytes(int32_t t_local, int64_t n);
+int tpmlp_vocab_ce_fwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t v_i, int32_t t_local,
+                       int64_t vocab_start, const void* X, const void* W, const int32_t* targets, void* logits,
+                       float* loss, float* row_max, float* row_sum, void* ws, size_t ws_bytes);
+int tpmlp_vocab_ce_bwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t v_i, int32_t t_local,
+                       int64_t vocab_start, const void* X, const void* W, const int32_t* targets,
+                       const void* logits, const float* row_max, const float* row_sum, const float* g,
+                       void* dlogits, float* dW, void* dXp);
 
 /* Status text for a return code; never NULL. */
 const char* tpmlp_status_string(int status);

@@ -69,6 +69,9 @@ SIGNATURES = {
     "tpmlp_attn_core_fwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P]),
     "tpmlp_attn_core_bwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _SZ]),
     "tpmlp_ln_sp": (_I, [_P, ctypes.POINTER(SpArgs)]),
+    "tpmlp_vocab_ce_workspace_bytes": (_SZ, [_I32, _I64]),
+    "tpmlp_vocab_ce_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I64] + [_P] * 8 + [_SZ]),
+    "tpmlp_vocab_ce_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I64] + [_P] * 10),
     "tpmlp_status_string": (ctypes.c_char_p, [_I]),
     "tpmlp_last_hip_error": (_I, []),
     "tpmlp_abi_version": (_I, []),
@@ -354,3 +357,46 @@ def attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, s, b, head_dim, causal=True, stream
     ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=X.device)
     tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal, stream)
     return dO, dQKV, dWqkv, dWproj, dXp
+
+
+# ---------------------------------------------------------------- vocabulary-parallel cross-entropy
+def tpmlp_vocab_ce_fwd(X, W, targets, logits, loss, row_max, row_sum, ws, vocab_start=0, stream=None):
+    """X [n,h]; W [t,v_i,h]; targets [n] int32; logits [t,n,v_i]; loss, row_max, row_sum [n] fp32."""
+    t, vi, h = W.shape
+    n = X.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().tpmlp_vocab_ce_fwd(_stream(stream), _dt(X), n, h, vi, t, vocab_start, _ptr(X), _ptr(W),
+                                    _ptr(targets), _ptr(logits), _ptr(loss), _ptr(row_max), _ptr(row_sum),
+                                    _ptr(ws), ws_bytes))
+
+
+def tpmlp_vocab_ce_bwd(X, W, targets, logits, row_max, row_sum, g, dlogits, dW, dXp, vocab_start=0, stream=None):
+    t, vi, h = W.shape
+    n = X.shape[0]
+    _check(lib().tpmlp_vocab_ce_bwd(_stream(stream), _dt(X), n, h, vi, t, vocab_start, _ptr(X), _ptr(W),
+                                    _ptr(targets), _ptr(logits), _ptr(row_max), _ptr(row_sum), _ptr(g),
+                                    _ptr(dlogits), _ptr(dW), _ptr(dXp)))
+
+
+def vocab_ce_fwd(X, W, targets, vocab_start=0, stream=None):
+    """Allocating wrapper: returns logits, loss, row_max, row_sum."""
+    t, vi, h = W.shape
+    n = X.shape[0]
+    logits = torch.empty((t, n, vi), dtype=X.dtype, device=X.device)
+    loss = torch.empty(n, dtype=torch.float32, device=X.device)
+    rmax, rsum = torch.empty_like(loss), torch.empty_like(loss)
+    nb = lib().tpmlp_vocab_ce_workspace_bytes(t, n)
+    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=X.device)
+    tpmlp_vocab_ce_fwd(X, W, targets, logits, loss, rmax, rsum, ws, vocab_start, stream)
+    return logits, loss, rmax, rsum
+
+
+def vocab_ce_bwd(X, W, targets, logits, row_max, row_sum, g, vocab_start=0, stream=None):
+    """Allocating wrapper: returns dlogits, dW (fp32), dXp."""
+    t, vi, h = W.shape
+    n = X.shape[0]
+    dlogits = torch.empty_like(logits)
+    dW = torch.empty((t, vi, h), dtype=torch.float32, device=X.device)
+    dXp = torch.empty((t, n, h), dtype=X.dtype, device=X.device)
+    tpmlp_vocab_ce_bwd(X, W, targets, logits, row_max, row_sum, g, dlogits, dW, dXp, vocab_start, stream)
+    return dlogits, dW, dXp

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpmlp.so")
-SOURCES = ["api.hip", "gemm_bf16.hip", "gemm_f32.hip", "reduce.hip", "sp_region.hip", "attention.hip"]
+SOURCES = ["api.hip", "gemm_bf16.hip", "gemm_f32.hip", "reduce.hip", "sp_region.hip", "attention.hip", "vocab_ce.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

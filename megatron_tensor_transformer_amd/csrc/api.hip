@@ -641,4 +641,120 @@ int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, 
   return st;
 }
 
+size_t tpmlp_vocab_ce_workspace_bytes(int32_t t_local, int64_t n) {
+  if (t_local < 1 || n <= 0) return 0;
+  return 3 * static_cast<size_t>(t_local) * static_cast<size_t>(n) * sizeof(float);
+}
+
+int tpmlp_vocab_ce_fwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t v_i, int32_t t_local,
+                       int64_t vocab_start, const void* X, const void* W, const int32_t* targets, void* logits,
+                       float* loss, float* row_max, float* row_sum, void* ws, size_t ws_bytes) {
+  int st = check_mlp_dims(dt, n, h, v_i, t_local);  // X·W_iᵀ has the first GEMM's sizes
+  if (st) return st;
+  if (vocab_start < 0) return TPMLP_ERR_ARG;
+  if (n == 0) return TPMLP_OK;
+  st = check_ptrs(dt, {X, W, logits});
+  if (st) return st;
+  if (targets == nullptr || loss == nullptr || row_max == nullptr || row_sum == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(targets, 4) || !aligned(loss, 4) || !aligned(row_max, 4) || !aligned(row_sum, 4))
+    return TPMLP_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < tpmlp_vocab_ce_workspace_bytes(t_local, n)) return TPMLP_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return TPMLP_ERR_ALIGN;
+  // logits_i = X·W_iᵀ: A = X [n,h] (K-major), B(k,j) = W_i[j][k] (K-major)
+  tpmlp::GemmProblem g{};
+  g.M = static_cast<int>(n);
+  g.N = static_cast<int>(v_i);
+  g.K = static_cast<int>(h);
+  g.batch = t_local;
+  g.A = X;
+  g.B = W;
+  g.C = logits;
+  g.lda = h;
+  g.ldb = h;
+  g.ldc = v_i;
+  g.sA = 0;
+  g.sB = v_i * h;
+  g.sC = n * v_i;
+  st = hip_status(gemm(dt, g, tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE, stream));
+  if (st) return st;
+  tpmlp::VocabProblem p{};
+  p.dt = dt;
+  p.T = t_local;
+  p.n = n;
+  p.vi = v_i;
+  p.start0 = vocab_start;
+  p.logits = logits;
+  p.target = targets;
+  p.stats = static_cast<float*>(ws);
+  p.loss = loss;
+  p.rmax = row_max;
+  p.rsum = row_sum;
+  return hip_status(tpmlp::launch_vocab_ce_fwd(p, stream));
+}
+
+int tpmlp_vocab_ce_bwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t v_i, int32_t t_local,
+                       int64_t vocab_start, const void* X, const void* W, const int32_t* targets,
+                       const void* logits, const float* row_max, const float* row_sum, const float* g,
+                       void* dlogits, float* dW, void* dXp) {
+  int st = check_mlp_dims(dt, n, h, v_i, t_local);
+  if (st) return st;
+  if (vocab_start < 0) return TPMLP_ERR_ARG;
+  if (dW == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(dW, 4)) return TPMLP_ERR_ALIGN;
+  if (n > 0) {
+    st = check_ptrs(dt, {X, W, logits, dlogits, dXp});
+    if (st) return st;
+    if (targets == nullptr || row_max == nullptr || row_sum == nullptr || g == nullptr) return TPMLP_ERR_NULLPTR;
+    if (!aligned(targets, 4) || !aligned(row_max, 4) || !aligned(row_sum, 4) || !aligned(g, 4))
+      return TPMLP_ERR_ALIGN;
+    tpmlp::VocabProblem p{};
+    p.dt = dt;
+    p.T = t_local;
+    p.n = n;
+    p.vi = v_i;
+    p.start0 = vocab_start;
+    p.logits = logits;
+    p.target = targets;
+    p.rmax = const_cast<float*>(row_max);
+    p.rsum = const_cast<float*>(row_sum);
+    p.g = g;
+    p.dlogits = dlogits;
+    st = hip_status(tpmlp::launch_vocab_ce_bwd(p, stream));
+    if (st) return st;
+  }
+  // dW_i = dlogits_iᵀ·X: M = v_i, N = h, K = n (zeros when n == 0)
+  tpmlp::GemmProblem gw{};
+  gw.M = static_cast<int>(v_i);
+  gw.N = static_cast<int>(h);
+  gw.K = static_cast<int>(n);
+  gw.batch = t_local;
+  gw.A = dlogits;
+  gw.B = X;
+  gw.C = dW;
+  gw.lda = v_i;
+  gw.ldb = h;
+  gw.ldc = h;
+  gw.sA = n * v_i;
+  gw.sB = 0;
+  gw.sC = v_i * h;
+  st = hip_status(gemm(dt, gw, tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32, stream));
+  if (st || n == 0) return st;
+  // dX_i = dlogits_i·W_i: M = n, N = h, K = v_i; B(k,j) = W_i[k][j] (N-major)
+  tpmlp::GemmProblem gx{};
+  gx.M = static_cast<int>(n);
+  gx.N = static_cast<int>(h);
+  gx.K = static_cast<int>(v_i);
+  gx.batch = t_local;
+  gx.A = dlogits;
+  gx.B = W;
+  gx.C = dXp;
+  gx.lda = v_i;
+  gx.ldb = h;
+  gx.ldc = h;
+  gx.sA = n * v_i;
+  gx.sB = v_i * h;
+  gx.sC = n * h;
+  return hip_status(gemm(dt, gx, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+}
+
 }  // extern "C"

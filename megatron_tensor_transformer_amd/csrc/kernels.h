@@ -105,6 +105,22 @@ struct AttnProblem {
   float* delta;      // backward workspace [T][b][nh][s]
 };
 hipError_t launch_attn_fwd(const AttnProblem& p, hipStream_t stream);
+
+// Vocabulary-parallel cross-entropy of T resident shards (vocab_ce.hip).
+struct VocabProblem {
+  int dt, T;
+  int64_t n, vi, start0;  // tokens, vocabulary entries per shard, first entry of shard 0
+  const void* logits;     // [T][n][vi]
+  const int* target;      // [n], global vocabulary ids
+  float* stats;           // workspace [3][T][n]: per-shard max, sum, target logit
+  float* loss;            // [n]
+  float* rmax;            // [n] row max over all shards
+  float* rsum;            // [n] Σ exp(x − rmax) over all shards
+  const float* g;         // backward: [n] upstream gradient of each loss
+  void* dlogits;          // backward: [T][n][vi]
+};
+hipError_t launch_vocab_ce_fwd(const VocabProblem& p, hipStream_t stream);
+hipError_t launch_vocab_ce_bwd(const VocabProblem& p, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_sp(const SpProblem& p, hipStream_t stream);
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 3
+    assert L.tpmlp_abi_version() == 4
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert L.tpmlp_status_string(s)
 
@@ -138,6 +138,29 @@ def test_attn_validation(L):
     # X, W_qkv, W_proj, QKV, O, lse, G | dO, dQKV, dW_qkv, dW_proj, dXp, ws, ws_bytes
     assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, *args[:7], p, p, z, p, p, p, need) == tp.ERR_NULLPTR
     assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, *args[:7], p, p, p, p, p, None, 0) == tp.ERR_WORKSPACE
+
+
+def test_vocab_ce_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    z = ctypes.c_void_p(0)
+    # one fp32 max, sum and target logit per (shard, token)
+    assert L.tpmlp_vocab_ce_workspace_bytes(8, 8192) == 3 * 8 * 8192 * 4
+    need = L.tpmlp_vocab_ce_workspace_bytes(2, 64)
+
+    def fwd(dt=1, n=64, h=64, vi=64, t=2, start=0, X=p, tg=p, ws=p, nb=need):
+        return L.tpmlp_vocab_ce_fwd(None, dt, n, h, vi, t, start, X, p, tg, p, p, p, p, ws, nb)
+    assert fwd(dt=3) == tp.ERR_DTYPE
+    assert fwd(vi=0) == tp.ERR_SHAPE
+    assert fwd(vi=12) == tp.ERR_ALIGN
+    assert fwd(start=-1) == tp.ERR_ARG
+    assert fwd(X=z) == tp.ERR_NULLPTR
+    assert fwd(tg=z) == tp.ERR_NULLPTR
+    assert fwd(nb=need - 4) == tp.ERR_WORKSPACE
+    assert fwd(ws=z) == tp.ERR_WORKSPACE
+    assert fwd(n=0, X=z, tg=z, ws=z, nb=0) == 0
+    # backward: dW required; g required when n > 0
+    assert L.tpmlp_vocab_ce_bwd(None, 1, 64, 64, 64, 2, 0, p, p, p, p, p, p, p, p, z, p) == tp.ERR_NULLPTR
+    assert L.tpmlp_vocab_ce_bwd(None, 1, 64, 64, 64, 2, 0, p, p, p, p, p, p, z, p, p, p) == tp.ERR_NULLPTR
 
 
 def test_bwd_validation(L):
