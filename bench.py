@@ -377,6 +377,66 @@ def leg_attention(tp, reps):
     return out
 
 
+def leg_vocab(tp, reps):
+    """The logit layer and vocabulary-parallel cross-entropy of the 8.3B-shaped
+    model: n = 8192 tokens, h = 3072, V = 51200 in t = 8 shards of 6400, bf16,
+    g = 1/n.  TFLOP/s over the GEMMs (2·n·h·V forward, twice that backward,
+    [EFF] FLOPs appendix); the cross-entropy kernels in GB/s against their
+    compulsory bytes (statistics: the logits read once; backward: logits read
+    and dlogits written once)."""
+    import numpy as np
+    import torch
+    from tpmlp_inputs import CONFIGS
+    c = CONFIGS["gpt8p3b_vocab_t8"]
+    n, h, V, t = c["n"], c["d"], c["V"], c["t"]
+    vi = V // t
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    bf = torch.bfloat16
+    X = torch.randn((n, h), generator=gen, device=dev).to(bf)
+    W = (0.02 * torch.randn((t, vi, h), generator=gen, device=dev)).to(bf)
+    tg = torch.randint(0, V, (n,), generator=gen, device=dev, dtype=torch.int32)
+    g = torch.full((n,), 1.0 / n, dtype=torch.float32, device=dev)
+    logits = torch.empty((t, n, vi), dtype=bf, device=dev)
+    loss, rmax, rsum = (torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(tp.lib().tpmlp_vocab_ce_workspace_bytes(t, n), dtype=torch.uint8, device=dev)
+    dlogits = torch.empty_like(logits)
+    dW = torch.empty((t, vi, h), dtype=torch.float32, device=dev)
+    dXp = torch.empty((t, n, h), dtype=bf, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        tp.tpmlp_vocab_ce_fwd(X, W, tg, logits, loss, rmax, rsum, ws, 0, stream)
+
+    def bwd():
+        tp.tpmlp_vocab_ce_bwd(X, W, tg, logits, rmax, rsum, g, dlogits, dW, dXp, 0, stream)
+
+    for _ in range(3):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for k in range(reps):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        bwd()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    b_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    fl = 2.0 * n * h * V
+    step = float(np.median(f_ms)) + float(np.median(b_ms))
+    return {"workload": f"logit layer + vocabulary-parallel cross-entropy: n={n}, h={h}, V={V}, t={t} "
+                        f"resident ({vi} per shard), bf16, mean loss",
+            "fwd": {"tflops_median": round(fl / (float(np.median(f_ms)) * 1e-3) / 1e12, 2), **_stats(f_ms)},
+            "bwd": {"tflops_median": round(2 * fl / (float(np.median(b_ms)) * 1e-3) / 1e12, 2), **_stats(b_ms)},
+            "step": {"median_ms": round(step, 4), "tflops": round(3 * fl / (step * 1e-3) / 1e12, 2),
+                     "pct_of_peak": round(100.0 * 3 * fl / (step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+            "logits_bytes": t * n * vi * 2}
+
+
 def recorded_traffic(kernel_file, summary):
     """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     in a profiles/ summary, or None when the summary is missing or the kernel
@@ -549,6 +609,8 @@ def main():
         rec["sp_region"] = leg_sp(tp, 10)
         torch.cuda.empty_cache()
         rec["attention"] = leg_attention(tp, 10)
+        torch.cuda.empty_cache()
+        rec["vocab_ce"] = leg_vocab(tp, 10)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, t, args.cpu_seconds)
     if args.cpu_all_configs:
