@@ -40,6 +40,7 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
+constexpr float RESCALE = 8.f;  // exp2 units the running maximum may pass before o is rescaled
 constexpr int AQ = 128;   // query (key) rows per workgroup (4 waves × 32)
 constexpr int AKV = 64;   // key rows per step
 constexpr int ATHR = 256;
@@ -242,10 +243,17 @@ __device__ __forceinline__ TilePlan<DH, NW> tile_plan(int b, int bi, int64_t row
 template <int DH, int NW = 4>
 __device__ __forceinline__ void issue_tile(i32x4 rsrc, TPMLP_LDS char* tile, const TilePlan<DH, NW>& p, int j,
                                            uint32_t stride, int s, int wave) {
+  const uint32_t jo = static_cast<uint32_t>(j) * stride;
+  if (j * AKV + AKV <= s) {  // the whole block is in range: no per-row check
 #pragma unroll
-  for (int q = 0; q < TilePlan<DH, NW>::NI; ++q) {
-    const uint32_t voff = j * AKV + p.row[q] < s ? p.voff[q] + static_cast<uint32_t>(j) * stride : AOOB;
-    buffer_load_lds16(rsrc, tile + (wave * TilePlan<DH, NW>::NI + q) * 1024, voff);
+    for (int q = 0; q < TilePlan<DH, NW>::NI; ++q)
+      buffer_load_lds16(rsrc, tile + (wave * TilePlan<DH, NW>::NI + q) * 1024, p.voff[q] + jo);
+  } else {
+#pragma unroll
+    for (int q = 0; q < TilePlan<DH, NW>::NI; ++q) {
+      const uint32_t voff = j * AKV + p.row[q] < s ? p.voff[q] + jo : AOOB;
+      buffer_load_lds16(rsrc, tile + (wave * TilePlan<DH, NW>::NI + q) * 1024, voff);
+    }
   }
 }
 
@@ -289,8 +297,72 @@ __device__ __forceinline__ void frag_tr_at(const uint32_t (&ad)[2 * ND], bf16x8 
   }
 }
 
+// Split form of frag_tr_at for software pipelining: issue the 2·ND reads of a
+// block into t (no wait), then tr_wait<N> once at most N newer LDS reads may
+// still be in flight, then tr_frags.  Only LDS reads issued here are in flight
+// in the code that uses these (the compiler's own LDS loads of the step have
+// been waited for before), so the count is exact.
+template <int DH, int ND, int IMM>
+__device__ __forceinline__ void tr_issue(const uint32_t (&ad)[2 * ND], i32x2 (&t)[2 * ND]) {
+  constexpr uint32_t HI = (static_cast<uint32_t>(IMM) >> 16) << 16, LO = IMM - HI;
+#pragma unroll
+  for (int k = 0; k < 2 * ND; ++k)
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(t[k]) : "v"(ad[k] + HI), "i"(LO) : "memory");
+}
+
+template <int N, int ND>
+__device__ __forceinline__ void tr_wait(i32x2 (&t)[2 * ND]) {
+  static_assert(N == 0 || N == 4 || N == 8, "lgkmcnt");
+  if constexpr (N == 8) asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(t[0])::"memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(t[0])::"memory");
+  else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0])::"memory");
+#pragma unroll
+  for (int k = 1; k < 2 * ND; ++k) asm volatile("" : "+v"(t[k]));
+}
+
+template <int ND>
+__device__ __forceinline__ void tr_frags(const i32x2 (&t)[2 * ND], bf16x8 (&out)[ND]) {
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    i32x4 w;
+    w[0] = t[2 * d][0];
+    w[1] = t[2 * d][1];
+    w[2] = t[2 * d + 1][0];
+    w[3] = t[2 * d + 1][1];
+    out[d] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
 template <int V>
 using ic = std::integral_constant<int, V>;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// ds_read_b128 at addr + IMM, issued now; the result may be used only after
+// an lgkm_wait that covers it.
+template <int IMM>
+__device__ __forceinline__ i32x4 lds_rd128(uint32_t addr) {
+  static_assert(IMM >= 0 && IMM < 65536, "ds offset");
+  i32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(IMM) : "memory");
+  return r;
+}
+
+// Wait until at most N LDS reads are in flight, and publish x and y (two
+// results of reads issued before those N) to the compiler.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(i32x4& x, i32x4& y) {
+  static_assert(N == 0 || N == 2 || N == 4, "lgkmcnt");
+  if constexpr (N == 4) asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(x), "+v"(y)::"memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(x), "+v"(y)::"memory");
+  else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y)::"memory");
+}
 
 template <int DH, bool CAUSAL>
 __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
@@ -338,7 +410,7 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   // row-fragment offsets (row r32, chunk 2c + hi) and transposed-read addresses
   uint32_t ko[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) ko[c] = kv_slot<DH>(r32, 2 * c + hi);
+  for (int c = 0; c < NC; ++c) ko[c] = lds_base + kv_slot<DH>(r32, 2 * c + hi);
   uint32_t va[2 * ND];
   tr_addrs<DH, ND>(lds_base, lane, va);
 
@@ -350,36 +422,51 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
 
   // one key tile in stage ST (compile-time, so every LDS offset is an
-  // immediate); the DMA of the next tile runs during it
+  // immediate).  One barrier per tile: after it every wave has finished the
+  // previous tile, so the other stage is free and the next tile's DMA is
+  // issued into it, running during this tile.
   auto step = [&](auto stc, int j) {
     constexpr int ST = decltype(stc)::value;
+    wait_vmcnt<0>();  // this wave's share of tile j (the only DMA in flight)
+    lds_barrier();
     if (j + 1 < nkv) {
       TPMLP_LDS char* nxt = lds + (ST ^ 1) * 2 * TILE;
       issue_tile<DH, NW>(rsrc, nxt, kp, j + 1, stride, a.s, wave);
       issue_tile<DH, NW>(rsrc, nxt + TILE, vp, j + 1, stride, a.s, wave);
-      wait_vmcnt<2 * NI>();
-    } else {
-      wait_vmcnt<0>();
     }
-    lds_barrier();
-    const TPMLP_LDS char* kb = lds + ST * 2 * TILE;
+    // A causal tile whose first key is past the wave's last query row (or a
+    // wave wholly past s) contributes nothing: skip its work.
+    const int t0 = j * AKV;
+    if (q0 >= a.s || (CAUSAL && t0 > q0 + 31)) return;
 
-    // Sᵀ block: sacc[u][v] = S[qrow][kv], kv = 64j + 32u + 8(v/4) + 4·hi + v%4
+    // Sᵀ block: sacc[u][v] = S[qrow][kv], kv = 64j + 32u + 8(v/4) + 4·hi + v%4.
+    // The two 32-key halves alternate (independent accumulators), and the K
+    // fragments of slice c + 3 are read while slice c's MFMAs run (four
+    // register pairs in a ring).
+    constexpr int KB = ST * 2 * TILE;
     f32x16 sacc[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x8 kf[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kf[c] = *(const TPMLP_LDS bf16x8*)(kb + u * 32 * RB + ko[c]);
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[u][v] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) sacc[u] = mfma(kf[c], qf[c], sacc[u]);
-    }
+    i32x4 kr[4][2];
+    auto kread = [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      kr[c % 4][0] = lds_rd128<KB>(ko[c]);
+      kr[c % 4][1] = lds_rd128<KB + 32 * RB>(ko[c]);
+    };
+    static_for<0, (NC < 3 ? NC : 3)>(kread);
+    static_for<0, NC>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int later = 2 * (NC - 1 - c < 2 ? NC - 1 - c : 2);  // reads issued after slice c's
+      lgkm_wait<later>(kr[c % 4][0], kr[c % 4][1]);
+      sacc[0] = mfma(__builtin_bit_cast(bf16x8, kr[c % 4][0]), qf[c], sacc[0]);
+      sacc[1] = mfma(__builtin_bit_cast(bf16x8, kr[c % 4][1]), qf[c], sacc[1]);
+      if constexpr (c + 3 < NC) kread(ic<c + 3>{});
+    });
 
     // mask (only tiles that reach past s or, causal, past the wave's first
     // query row), running maximum, exponentials, running sum
-    const int t0 = j * AKV;
     if (t0 + AKV > a.s || (CAUSAL && t0 + AKV - 1 > q0)) {
       const int lim = CAUSAL ? min(qrow + 1, a.s) : a.s;
       mask_range(sacc, -1 << 30, lim - t0 - 4 * hi, -INFINITY);
@@ -390,9 +477,22 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[u][v]);
     mloc = pair_max(mloc);
+    // The exponent reference m moves only when some row's maximum passes it
+    // by more than RESCALE in exp2 units (always on the first tile, where m is
+    // −∞).  Otherwise P = 2^((S−m)·log2(e)/√dh) stays ≤ 2^RESCALE, and
+    // o = Σ P·v / Σ P and lse = m/√dh + ln Σ P hold for any reference, so the
+    // rescaling of the running sum and of o is skipped.
     const float mnew = fmaxf(m, mloc);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float off = -muse * a.scale_log2;
+    if (__any((mnew - m) * a.scale_log2 > RESCALE)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - (mnew == -INFINITY ? 0.f : mnew)) * a.scale_log2);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
+      m = mnew;
+    }
+    const float off = -(m == -INFINITY ? 0.f : m) * a.scale_log2;
     float lsum = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -402,38 +502,41 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
         sacc[u][v] = p;
         lsum += p;
       }
-    lsum = pair_sum(lsum);
-    // rescale the running sum and output only when some row's maximum grew
-    if (__any(mnew != m)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - muse) * a.scale_log2);
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < ND; ++d)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[d][v] *= alpha;
-    }
-    l += lsum;
-    m = mnew;
+    l += pair_sum(lsum);
 
     // Oᵀ += Vᵀ·Pᵀ over the tile's keys, 16 at a time.  P fragment (u, c2):
     // this lane's values v = 8·c2 .. 8·c2+7 of sacc[u]; they are keys
     // 32u + 16c2 + {0..3, 8..11} (hi = 0) or {4..7, 12..15} (hi = 1), and the
     // V fragment rows are read in that same order.
+    // The reads of block g+1 are in flight while block g's MFMAs run (two
+    // register sets; a set is refilled only after the MFMAs that read it
+    // were issued).
     constexpr int VB = ST * 2 * TILE + TILE;
+    constexpr int NR = 2 * ND;
+    i32x2 ta[NR], tb[NR];
     bf16x8 vf[ND];
-    frag_tr_at<DH, ND, VB>(va, vf);
+    tr_issue<DH, ND, VB>(va, ta);
+    tr_issue<DH, ND, VB + 16 * RB>(va, tb);
+    tr_wait<NR, ND>(ta);
+    tr_frags<ND>(ta, vf);
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[0], 0), oacc[d]);
-    frag_tr_at<DH, ND, VB + 16 * RB>(va, vf);
+    asm volatile("s_nop 1" ::: "memory");
+    tr_issue<DH, ND, VB + 32 * RB>(va, ta);
+    tr_wait<NR, ND>(tb);
+    tr_frags<ND>(tb, vf);
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[0], 1), oacc[d]);
-    frag_tr_at<DH, ND, VB + 32 * RB>(va, vf);
+    asm volatile("s_nop 1" ::: "memory");
+    tr_issue<DH, ND, VB + 48 * RB>(va, tb);
+    tr_wait<NR, ND>(ta);
+    tr_frags<ND>(ta, vf);
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[1], 0), oacc[d]);
-    frag_tr_at<DH, ND, VB + 48 * RB>(va, vf);
+    tr_wait<0, ND>(tb);
+    tr_frags<ND>(tb, vf);
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[d] = mfma(vf[d], pack_acc(sacc[1], 1), oacc[d]);
-    lds_barrier();  // every wave is done with stage ST before it is refilled
   };
   int j = 0;
   for (; j + 1 < nkv; j += 2) {

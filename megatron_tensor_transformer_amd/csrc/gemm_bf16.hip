@@ -550,8 +550,10 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
         for (int u = 0; u < 8; ++u) {
           const int row = (it0 + u) * 8 + (lane >> 3);
           const int gr = qm0 + row, gc = qn0 + (lane & 7) * 8;
+          // whole 128-B lines, not re-read by this launch: streamed past the L2
+          // (leaves it to the A and B panels)
           if (gr < a.M && gc < a.N)
-            *reinterpret_cast<i32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc) = v[u];
+            __builtin_nontemporal_store(v[u], reinterpret_cast<i32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc));
         }
       }
     }

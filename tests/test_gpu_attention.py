@@ -14,7 +14,7 @@ import torch
 
 import megatron_tensor_transformer_amd as tp
 from oracle import attention as oa
-from tpmlp_inputs import CONFIGS, attn_inputs, config_inputs, qkv_inputs
+from tpmlp_inputs import CONFIGS, Tensor, attn_inputs, config_inputs, f32_to_bf16_bits, qkv_inputs
 
 from gpu_util import dev, f64, relerr, say, shard_cols, shard_rows
 
@@ -41,9 +41,10 @@ def run_core(inp, T, s, b, nh, dh, causal):
     return o, lse, dqkv
 
 
-def compare_core(T, s, b, nh, dh, causal, dtype, seed=0):
+def compare_core(T, s, b, nh, dh, causal, dtype, seed=0, inp=None):
     say(f"[gpu] attention core {dtype} T={T} s={s} b={b} nh={nh} dh={dh} causal={causal}")
-    inp = qkv_inputs(T, s, b, nh, dh, dtype=dtype, seed=seed)
+    if inp is None:
+        inp = qkv_inputs(T, s, b, nh, dh, dtype=dtype, seed=seed)
     o, lse, dqkv = run_core(inp, T, s, b, nh, dh, causal)
     tol = TOL[dtype]
     errs = {}
@@ -85,6 +86,21 @@ def test_core_fp32(T, s, b, nh, dh, causal):
 ])
 def test_core_bf16(T, s, b, nh, dh, causal):
     compare_core(T, s, b, nh, dh, causal, "bf16")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_core_bf16_growing_logits(causal):
+    """Keys scaled by 2^⌊j/64⌋ (exact in bf16): every key tile doubles the
+    logits' spread, so the row maxima grow by less than the forward's rescale
+    threshold on the early tiles (P well above 1 against a stale reference)
+    and by more on the later ones (the reference moves mid-row)."""
+    T, s, b, nh, dh = 1, 320, 2, 2, 128
+    inp = qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=8)
+    x = inp["qkv"].f32.reshape(T, s, b, nh, 3, dh).copy()
+    x[:, :, :, :, 1, :] *= (2.0 ** (np.arange(s) // 64)).astype(np.float32)[None, :, None, None, None]
+    inp["qkv"] = Tensor(f32_to_bf16_bits(x.reshape(T, s * b, nh * 3 * dh)), "bf16")
+    assert np.array_equal(inp["qkv"].f32.reshape(x.shape), x)  # the scaling is exact
+    compare_core(T, s, b, nh, dh, causal, "bf16", inp=inp)
 
 
 def test_core_deterministic_bitwise():
