@@ -718,56 +718,92 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) dq[d][v] = 0.f;
 
-  for (int j = 0; j < nkv; ++j) {
-    const int st = j & 1;
+  // row-fragment and transposed-read addresses (block offsets are immediates)
+  constexpr int RB = DH * 2, NR = 2 * ND;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  uint32_t ro[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ro[c] = lds_base + kv_slot<DH>(r32, 2 * c + hi);
+  uint32_t va[NR];
+  tr_addrs<DH, ND>(lds_base, lane, va);
+
+  // One key block in stage ST (compile-time: every LDS offset is an
+  // immediate).  One barrier per block: after it every wave has finished the
+  // previous block, so the other stage is free and the next block's DMA is
+  // issued into it, running during this block.
+  auto step = [&](auto stc, int j) {
+    constexpr int ST = decltype(stc)::value;
+    wait_vmcnt<0>();  // this wave's share of block j
+    lds_barrier();
     if (j + 1 < nkv) {
-      TPMLP_LDS char* nxt = lds + (st ^ 1) * 2 * TILE;
+      TPMLP_LDS char* nxt = lds + (ST ^ 1) * 2 * TILE;
       load_tile<DH>(rsrc, nxt, a.s, a.b, bi, row_len, kcol, j + 1, wave, lane);
       load_tile<DH>(rsrc, nxt + TILE, a.s, a.b, bi, row_len, vcol, j + 1, wave, lane);
-      wait_vmcnt<2 * NI>();
-    } else {
-      wait_vmcnt<0>();
     }
-    lds_barrier();
-    const TPMLP_LDS char* kb = lds + st * 2 * TILE;
-    const TPMLP_LDS char* vb = kb + TILE;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    // a causal block whose first key is past the wave's last query row (or a
+    // wave wholly past s) contributes nothing
+    const int t0 = j * AKV;
+    if (q0 >= a.s || (CAUSAL && t0 > q0 + 31)) return;
+    const bool masked = t0 + AKV > a.s || q0 + 31 >= a.s || (CAUSAL && t0 + AKV - 1 > q0);
+    static_for<0, 2>([&](auto uc) {
+      constexpr int U = decltype(uc)::value;
+      constexpr int KB = ST * 2 * TILE + U * 32 * RB, VB = KB + TILE;  // key rows 32U.. of K and V
+      // Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ for the lane's query row: slices read
+      // three ahead
       f32x16 sacc, pacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
-      bf16x8 kr[NC], vr[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kr[c] = frag_rows<DH>(kb, 32 * u + r32, 2 * c + hi);
-        vr[c] = frag_rows<DH>(vb, 32 * u + r32, 2 * c + hi);
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        sacc = mfma(kr[c], qf[c], sacc);
-        pacc = mfma(vr[c], df[c], pacc);
-      }
-      const int t0 = j * AKV;
-      if (t0 + AKV > a.s || q0 + 31 >= a.s || (CAUSAL && t0 + AKV - 1 > q0)) {
+      i32x4 kr[4], vr[4];
+      auto rd2 = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        kr[c % 4] = lds_rd128<KB>(ro[c]);
+        vr[c % 4] = lds_rd128<VB>(ro[c]);
+      };
+      static_for<0, (NC < 3 ? NC : 3)>(rd2);
+      static_for<0, NC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        constexpr int later = 2 * (NC - 1 - c < 2 ? NC - 1 - c : 2);
+        lgkm_wait<later>(kr[c % 4], vr[c % 4]);
+        sacc = mfma(__builtin_bit_cast(bf16x8, kr[c % 4]), qf[c], sacc);
+        pacc = mfma(__builtin_bit_cast(bf16x8, vr[c % 4]), df[c], pacc);
+        if constexpr (c + 3 < NC) rd2(ic<c + 3>{});
+      });
+      // both transposed K blocks are read while dS is formed
+      i32x2 ta[NR], tb[NR];
+      tr_issue<DH, ND, KB>(va, ta);
+      tr_issue<DH, ND, KB + 16 * RB>(va, tb);
+      if (masked) {
         const int lim = valid ? (CAUSAL ? min(qrow + 1, a.s) : a.s) : 0;
-        mask_range1(sacc, u, -1 << 30, lim - t0 - 4 * hi, -INFINITY);
+        mask_range1(sacc, U, -1 << 30, lim - t0 - 4 * hi, -INFINITY);
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], a.scale_log2, -lse2));
         sacc[v] = p * (pacc[v] - dlt);  // dS
       }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 sf = pack_acc(sacc, c2);
-        bf16x8 kt[ND];
-        frag_tr<DH, ND>(kb, u, c2, lane, kt);
+      bf16x8 kt[ND];
+      tr_wait<NR, ND>(ta);
+      tr_frags<ND>(ta, kt);
+      {
+        const bf16x8 sf = pack_acc(sacc, 0);
 #pragma unroll
         for (int d = 0; d < ND; ++d) dq[d] = mfma(kt[d], sf, dq[d]);
       }
-    }
-    lds_barrier();
+      tr_wait<0, ND>(tb);
+      tr_frags<ND>(tb, kt);
+      {
+        const bf16x8 sf = pack_acc(sacc, 1);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dq[d] = mfma(kt[d], sf, dq[d]);
+      }
+    });
+  };
+  int j = 0;
+  for (; j + 1 < nkv; j += 2) {
+    step(ic<0>{}, j);
+    step(ic<1>{}, j + 1);
   }
+  if (j < nkv) step(ic<0>{}, j);
   if (valid) {
     bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(qrow) * a.b + bi) * row_len +
                h * 3 * DH;
@@ -849,52 +885,86 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   wait_vmcnt<0>();
   store_stat(0, sv);
 
-  for (int j = j0; j < nq; ++j) {
-    const int st = (j - j0) & 1;
+  // row-fragment and transposed-read addresses (block offsets are immediates)
+  constexpr int RB = DH * 2, NR = 2 * ND;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  uint32_t ro[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ro[c] = lds_base + kv_slot<DH>(r32, 2 * c + hi);
+  uint32_t va[NR];
+  tr_addrs<DH, ND>(lds_base, lane, va);
+  // this lane's statistics: 4 consecutive query rows per 16-B read
+  const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&stat[0][0][0])) + 16 * hi;
+
+  // One query block in stage ST (compile-time: every LDS offset is an
+  // immediate).  One barrier per block: after it every wave has finished the
+  // previous block, so the other stage (tiles and statistics) is free; the
+  // next block's DMA and statistics loads are issued into it and run during
+  // this block.
+  auto step = [&](auto stc, int j) {
+    constexpr int ST = decltype(stc)::value;
+    wait_vmcnt<0>();  // this wave's share of block j and its statistic
+    lds_wait();       // its statistics write of the previous step
+    lds_barrier();
     if (j + 1 < nq) {
       load_stat(j + 1, sv);
-      TPMLP_LDS char* nxt = lds + (st ^ 1) * 2 * TILE;
+      TPMLP_LDS char* nxt = lds + (ST ^ 1) * 2 * TILE;
       load_tile<DH>(rq, nxt, a.s, a.b, bi, row_len, qcol, j + 1, wave, lane);
       load_tile<DH>(rd, nxt + TILE, a.s, a.b, bi, orow, dcol, j + 1, wave, lane);
-      wait_vmcnt<2 * NI>();
-    } else {
-      wait_vmcnt<0>();
     }
-    lds_wait();  // this wave's statistics writes of the previous step are done
-    lds_barrier();
-    const TPMLP_LDS char* qt = lds + st * 2 * TILE;
-    const TPMLP_LDS char* dt = qt + TILE;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    const int t0 = j * AKV;
+    const bool masked = t0 + AKV > a.s || k0 + 31 >= a.s || (CAUSAL && t0 < k0 + 31);
+    // a causal block whose last query row is before the wave's first key (or
+    // a wave wholly past s) contributes nothing
+    const bool dead = k0 >= a.s || (CAUSAL && t0 + AKV - 1 < k0);
+    if (!dead) static_for<0, 2>([&](auto uc) {
+      constexpr int U = decltype(uc)::value;
+      constexpr int QB = ST * 2 * TILE + U * 32 * RB, DB = QB + TILE;  // rows 32U.. of Q and dO
+      // statistics of the lane's 16 query rows (lse·log2(e), δ), read ahead
+      f32x4 ls[4], ds[4];
+      i32x4 sr[8];
+      static_for<0, 4>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        sr[g] = lds_rd128<((2 * ST + 0) * AKV + 32 * U + 8 * g) * 4>(sbase);
+        sr[4 + g] = lds_rd128<((2 * ST + 1) * AKV + 32 * U + 8 * g) * 4>(sbase);
+      });
+      // S = Q·Kᵀ and dP = dO·Vᵀ for the lane's key: slices read three ahead
       f32x16 sacc, pacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
-      bf16x8 qr_[NC], dr[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qr_[c] = frag_rows<DH>(qt, 32 * u + r32, 2 * c + hi);
-        dr[c] = frag_rows<DH>(dt, 32 * u + r32, 2 * c + hi);
-      }
-      // the statistics of this lane's 16 query rows, 4 consecutive per read
-      f32x4 ls[4], ds[4];
+      i32x4 qr[4], dr[4];
+      auto rd2 = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        qr[c % 4] = lds_rd128<QB>(ro[c]);
+        dr[c % 4] = lds_rd128<DB>(ro[c]);
+      };
+      static_for<0, (NC < 3 ? NC : 3)>(rd2);
+      static_for<0, NC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        constexpr int later = 2 * (NC - 1 - c < 2 ? NC - 1 - c : 2);
+        lgkm_wait<later>(qr[c % 4], dr[c % 4]);
+        sacc = mfma(__builtin_bit_cast(bf16x8, qr[c % 4]), kf[c], sacc);
+        pacc = mfma(__builtin_bit_cast(bf16x8, dr[c % 4]), vf[c], pacc);
+        if constexpr (c + 3 < NC) rd2(ic<c + 3>{});
+      });
+      // every LDS read above is complete (the last wait was for zero)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        ls[g] = *reinterpret_cast<const f32x4*>(&stat[st][0][32 * u + 8 * g + 4 * hi]);
-        ds[g] = *reinterpret_cast<const f32x4*>(&stat[st][1][32 * u + 8 * g + 4 * hi]);
+        asm volatile("" : "+v"(sr[g]), "+v"(sr[4 + g]));
+        ls[g] = __builtin_bit_cast(f32x4, sr[g]);
+        ds[g] = __builtin_bit_cast(f32x4, sr[4 + g]);
       }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        sacc = mfma(qr_[c], kf[c], sacc);
-        pacc = mfma(dr[c], vf[c], pacc);
-      }
-      // lane: key krow, query rows 64j + 32u + 8(v/4) + 4·hi + v%4; the
+      // the first two transposed blocks are read while P and dS are formed
+      i32x2 ta[NR], tb[NR];
+      tr_issue<DH, ND, DB>(va, ta);
+      tr_issue<DH, ND, QB>(va, tb);
+      // lane: key krow, query rows 64j + 32U + 8(v/4) + 4·hi + v%4; the
       // mask runs only on tiles that reach past s, past this wave's keys'
       // diagonal, or hold key rows past s
-      const int t0 = j * AKV;
-      if (t0 + AKV > a.s || k0 + 31 >= a.s || (CAUSAL && t0 < k0 + 31)) {
+      if (masked) {
         const int lo = CAUSAL ? krow - t0 - 4 * hi : -1 << 30;
         const int hi_ = valid ? a.s - t0 - 4 * hi : lo;
-        mask_range1(sacc, u, lo, hi_, -INFINITY);
+        mask_range1(sacc, U, lo, hi_, -INFINITY);
       }
       f32x16 pv;
 #pragma unroll
@@ -905,24 +975,50 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
           pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[v], a.scale_log2, -ls[g][e]));
           sacc[v] = pv[v] * (pacc[v] - ds[g][e]);  // dS
         }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 pf = pack_acc(pv, c2);
-        const bf16x8 sf = pack_acc(sacc, c2);
-        bf16x8 ft[ND];
-        frag_tr<DH, ND>(dt, u, c2, lane, ft);
+      // dv += Pᵀ·dO and dk += dSᵀ·Q over the block's 32 query rows, 16 at a
+      // time; block g + 1's reads are in flight during block g's MFMAs
+      bf16x8 ft[ND];
+      tr_wait<NR, ND>(ta);
+      tr_frags<ND>(ta, ft);
+      {
+        const bf16x8 pf = pack_acc(pv, 0);
 #pragma unroll
         for (int d = 0; d < ND; ++d) dv[d] = mfma(ft[d], pf, dv[d]);
-        frag_tr<DH, ND>(qt, u, c2, lane, ft);
+      }
+      tr_issue<DH, ND, DB + 16 * RB>(va, ta);
+      tr_wait<NR, ND>(tb);
+      tr_frags<ND>(tb, ft);
+      {
+        const bf16x8 sf = pack_acc(sacc, 0);
 #pragma unroll
         for (int d = 0; d < ND; ++d) dk[d] = mfma(ft[d], sf, dk[d]);
       }
-    }
+      tr_issue<DH, ND, QB + 16 * RB>(va, tb);
+      tr_wait<NR, ND>(ta);
+      tr_frags<ND>(ta, ft);
+      {
+        const bf16x8 pf = pack_acc(pv, 1);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dv[d] = mfma(ft[d], pf, dv[d]);
+      }
+      tr_wait<0, ND>(tb);
+      tr_frags<ND>(tb, ft);
+      {
+        const bf16x8 sf = pack_acc(sacc, 1);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dk[d] = mfma(ft[d], sf, dk[d]);
+      }
+    });
     // the next block's statistics go into the other stage (read after the
     // next barrier)
-    if (j + 1 < nq) store_stat(st ^ 1, sv);
-    lds_barrier();
+    if (j + 1 < nq) store_stat(ST ^ 1, sv);
+  };
+  int j = j0;
+  for (; j + 1 < nq; j += 2) {
+    step(ic<0>{}, j);
+    step(ic<1>{}, j + 1);
   }
+  if (j < nq) step(ic<0>{}, j);
   if (valid) {
     bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(krow) * a.b + bi) * row_len +
                h * 3 * DH + DH;
