@@ -10,6 +10,14 @@ the sequence-first layout of [EFF] §4.2), a heads of width dh = d / a.
         S = q·kᵀ / √dh       ([TRAIN] Attention 层 section)
         S[i][j] = −∞ for j > i when the mask is causal (GPT; [EFF] §4.2: the
                                  implicit causal mask of the fused softmax)
+        S[i][j] = −∞ where a general mask hides key j from query i (the
+                                 fused softmax's other kernel in [EFF] §4.2,
+                                 for masks like BERT's; [TRAIN]'s BERT layer
+                                 uses the padding mask type); mask[β] is one
+                                 [s, s] boolean array shared by all heads and
+                                 shards, combined with the causal one
+        a row whose keys are all hidden has o = 0, no softmax (A = 0) and
+                                 lse = −∞, so it passes no gradient
         A = softmax(S) over each row ([TRAIN] Attention 层 section)
         o = A·v
     Ocat = the heads' o side by side, [n, d] in (head, dh) column order
@@ -82,25 +90,29 @@ def unmerge_heads(Ocat, s, b, nh, dh):
 
 
 # ---------------------------------------------------------------- the core
-def core_forward(q, k, v, causal):
-    """Per (batch entry, head): S = q·kᵀ/√dh, causal mask, row softmax, o = A·v.
-    Returns o [b, nh, s, dh], A [b, nh, s, s], lse [b, nh, s]."""
+def core_forward(q, k, v, causal, mask=None):
+    """Per (batch entry, head): S = q·kᵀ/√dh, causal and/or general mask
+    (mask [b, s, s], True hides key j from query i), row softmax, o = A·v.
+    Returns o [b, nh, s, dh], A [b, nh, s, s], lse [b, nh, s]; rows with every
+    key hidden get o = 0, A = 0, lse = −∞."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     b, nh, s, dh = q.shape
     scale = 1.0 / np.sqrt(dh)
     o = np.zeros_like(q)
     A = np.zeros((b, nh, s, s))
     lse = np.zeros((b, nh, s))
-    keep = np.tril(np.ones((s, s), dtype=bool)) if causal else np.ones((s, s), dtype=bool)
+    base = np.tril(np.ones((s, s), dtype=bool)) if causal else np.ones((s, s), dtype=bool)
     for bi in range(b):
+        keep = base if mask is None else base & ~np.asarray(mask[bi], dtype=bool)
+        seen = keep.any(axis=1)
         for h in range(nh):
             S = (q[bi, h] @ k[bi, h].T) * scale
             S = np.where(keep, S, -np.inf)
-            mx = S.max(axis=1, keepdims=True)
+            mx = np.where(seen, S.max(axis=1), 0.0)[:, None]
             E = np.exp(S - mx)
             z = E.sum(axis=1, keepdims=True)
-            A[bi, h] = E / z
-            lse[bi, h] = (mx + np.log(z))[:, 0]
+            A[bi, h] = np.where(seen[:, None], E / np.where(seen[:, None], z, 1.0), 0.0)
+            lse[bi, h] = np.where(seen, mx[:, 0] + np.log(np.where(seen, z[:, 0], 1.0)), -np.inf)
             o[bi, h] = A[bi, h] @ v[bi, h]
     return o, A, lse
 
@@ -123,7 +135,7 @@ def core_backward(q, k, v, A, do):
 
 
 # ---------------------------------------------------------------- one shard
-def shard_forward(X, Wqkv_i, Wproj_i, s, b, nh, causal, bqkv_i=None):
+def shard_forward(X, Wqkv_i, Wproj_i, s, b, nh, causal, bqkv_i=None, mask=None):
     """QKV_i = X·W_qkv,i (+ bqkv_i), the core on the shard's nh heads,
     P_i = Ocat_i·W_proj,i."""
     X = _f64(X)
@@ -132,7 +144,7 @@ def shard_forward(X, Wqkv_i, Wproj_i, s, b, nh, causal, bqkv_i=None):
     if bqkv_i is not None:
         QKV = QKV + _f64(bqkv_i)[None, :]
     q, k, v = split_heads(QKV, s, b, nh, dh)
-    o, A, lse = core_forward(q, k, v, causal)
+    o, A, lse = core_forward(q, k, v, causal, mask)
     Ocat = merge_heads(o)
     P = Ocat @ _f64(Wproj_i)
     return {"QKV": QKV, "A": A, "lse": lse, "O": Ocat, "P": P}
@@ -156,7 +168,7 @@ def shard_backward(X, Wqkv_i, Wproj_i, fwd, G, s, b, nh):
 
 
 # ---------------------------------------------------------------- all shards
-def tp_forward(X, Wqkv, Wproj, t, s, b, heads, causal, bqkv=None, bproj=None):
+def tp_forward(X, Wqkv, Wproj, t, s, b, heads, causal, bqkv=None, bproj=None, mask=None):
     """All t shards from the full weights (heads/t heads each) and
     Out = Σ_i P_i (+ bproj once after the sum)."""
     if heads % t:
@@ -165,7 +177,7 @@ def tp_forward(X, Wqkv, Wproj, t, s, b, heads, causal, bqkv=None, bproj=None):
     Wq_s = _mlp.split_columns(Wqkv, t)
     Wp_s = _mlp.split_rows(Wproj, t)
     bq_s = _mlp.split_bias(bqkv, t) if bqkv is not None else [None] * t
-    shards = [shard_forward(X, Wq_s[i], Wp_s[i], s, b, nh, causal, bq_s[i]) for i in range(t)]
+    shards = [shard_forward(X, Wq_s[i], Wp_s[i], s, b, nh, causal, bq_s[i], mask) for i in range(t)]
     Out = _mlp.reduce_partials([sh["P"] for sh in shards])
     if bproj is not None:
         Out = Out + _f64(bproj)[None, :]

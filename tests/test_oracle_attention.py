@@ -4,7 +4,10 @@ its own formulas: torch's fp64 scaled_dot_product_attention and its autograd
 through the whole shard, the heads split over shards against the unsplit
 layer, the closed form of uniform attention when the queries vanish, and the
 shift invariance of the keys (a softmax row is unchanged when all its logits
-move together).  Plausible mistakes planted in the oracle must fail one of
+move together).  The general mask: torch's boolean attn_mask, key padding
+against the same attention on the truncated keys, the causal pattern given as
+a general mask, rows with every key hidden, and finite differences through a
+masked layer.  Plausible mistakes planted in the oracle must fail one of
 them."""
 
 import numpy as np
@@ -173,9 +176,135 @@ def check_key_shift_invariance():
     return bool(relerr(o1, o0) < 1e-13 and np.abs(dk.sum(axis=2)).max() < 1e-12)
 
 
+def _mask(b, s, seed, p=0.4, keep_diag=True):
+    """Random boolean mask [b, s, s] (True hides the key); with keep_diag every
+    query sees at least its own position."""
+    m = np.random.default_rng(seed).random((b, s, s)) < p
+    if keep_diag:
+        m[:, np.arange(s), np.arange(s)] = False
+    return m
+
+
+def check_mask_vs_torch_sdpa():
+    """A random general mask, alone and with the causal one, against torch's
+    fp64 SDPA with the boolean attn_mask (True there = may attend) and its
+    autograd; every row keeps at least one key."""
+    q, k, v = _qkv(s=7, seed=11)
+    b, nh, s, dh = q.shape
+    do = np.random.default_rng(12).standard_normal(q.shape)
+    m = _mask(b, s, 13)
+    ok = True
+    for causal in (False, True):
+        o, A, lse = oa.core_forward(q, k, v, causal, m)
+        dq, dk, dv = oa.core_backward(q, k, v, A, do)
+        allow = ~m & (np.tril(np.ones((s, s), bool)) if causal else True)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(allow)[:, None])
+        (to * torch.tensor(do)).sum().backward()
+        ok &= relerr(o, to.detach().numpy()) < 1e-13 and relerr(dq, tq.grad.numpy()) < 1e-12
+        ok &= relerr(dk, tk.grad.numpy()) < 1e-12 and relerr(dv, tv.grad.numpy()) < 1e-12
+    return bool(ok)
+
+
+def check_key_padding_is_truncation():
+    """Hiding keys j >= L_β (a padding mask) equals attention over the first
+    L_β keys only; the hidden keys get zero dk, dv."""
+    q, k, v = _qkv(s=8, b=3, seed=14)
+    b, nh, s, dh = q.shape
+    do = np.random.default_rng(15).standard_normal(q.shape)
+    L = [8, 5, 3]
+    m = np.zeros((b, s, s), bool)
+    for bi, n in enumerate(L):
+        m[bi, :, n:] = True
+    ok = True
+    for causal in (False, True):
+        o, A, lse = oa.core_forward(q, k, v, causal, m)
+        dq, dk, dv = oa.core_backward(q, k, v, A, do)
+        for bi, n in enumerate(L):
+            sl = (slice(bi, bi + 1), slice(None))
+            q1, k1, v1 = q[sl], k[sl][:, :, :n], v[sl][:, :, :n]
+            # truncated keys, all queries: the causal pattern of a query i >= n
+            # sees every kept key, which tril on an [s, n] block expresses
+            keep = np.tril(np.ones((s, n), bool)) if causal else np.ones((s, n), bool)
+            S = np.einsum("bhid,bhjd->bhij", q1, k1) / np.sqrt(dh)
+            S = np.where(keep, S, -np.inf)
+            At = np.exp(S - S.max(-1, keepdims=True))
+            At /= At.sum(-1, keepdims=True)
+            ok &= relerr(o[sl], At @ v1) < 1e-13
+            ok &= np.allclose(lse[sl], logsumexp(S, axis=-1), rtol=0, atol=1e-13)
+            ok &= np.all(dk[sl][:, :, n:] == 0) and np.all(dv[sl][:, :, n:] == 0)
+            dP = do[sl] @ np.swapaxes(v1, -1, -2)
+            dS = At * (dP - (dP * At).sum(-1, keepdims=True))
+            ok &= relerr(dq[sl], dS @ k1 / np.sqrt(dh)) < 1e-12
+            ok &= relerr(dk[sl][:, :, :n], np.swapaxes(dS, -1, -2) @ q1 / np.sqrt(dh)) < 1e-12
+    return bool(ok)
+
+
+def check_causal_pattern_as_general_mask():
+    q, k, v = _qkv(s=6, seed=16)
+    b, s = q.shape[0], q.shape[2]
+    m = np.broadcast_to(np.triu(np.ones((s, s), bool), 1), (b, s, s))
+    o1, A1, l1 = oa.core_forward(q, k, v, True)
+    o2, A2, l2 = oa.core_forward(q, k, v, False, m)
+    return bool(np.array_equal(o1, o2) and np.array_equal(A1, A2) and np.array_equal(l1, l2))
+
+
+def check_rows_with_every_key_hidden():
+    """A query that may see no key: o = 0, lse = −∞, dq = 0; the other rows are
+    those of the same mask with that row opened to a single key."""
+    q, k, v = _qkv(s=6, seed=17)
+    b, nh, s, dh = q.shape
+    do = np.random.default_rng(18).standard_normal(q.shape)
+    m = _mask(b, s, 19)
+    m[0, 2, :] = True
+    m[1, 0, :] = True
+    o, A, lse = oa.core_forward(q, k, v, False, m)
+    dq, dk, dv = oa.core_backward(q, k, v, A, do)
+    ok = np.all(o[0, :, 2] == 0) and np.all(o[1, :, 0] == 0)
+    ok &= np.all(np.isneginf(lse[0, :, 2])) and np.all(np.isneginf(lse[1, :, 0]))
+    ok &= np.all(dq[0, :, 2] == 0) and np.all(dq[1, :, 0] == 0) and np.all(np.isfinite(dk))
+    m2 = m.copy()
+    m2[0, 2, 0] = False
+    m2[1, 0, 0] = False
+    o2, _, _ = oa.core_forward(q, k, v, False, m2)
+    rows = np.ones((b, s), bool)
+    rows[0, 2] = rows[1, 0] = False
+    ok &= np.array_equal(o.transpose(0, 2, 1, 3)[rows], o2.transpose(0, 2, 1, 3)[rows])
+    return bool(ok)
+
+
+def check_masked_finite_differences(step=1e-6):
+    """Central differences of ℓ = Σ G⊙Out on every entry of X, W_qkv, W_proj
+    through a layer with a general mask (one query row fully hidden), causal."""
+    s, b, d, heads, t = 4, 2, 4, 2, 2
+    L = _layer(s, b, d, heads, seed=21)
+    m = _mask(b, s, 22, p=0.5, keep_diag=False)
+    m[1, 3, :] = True
+
+    def fwd(X, Wq, Wp):
+        return oa.tp_forward(X, Wq, Wp, t, s, b, heads, True, mask=m)
+    f = fwd(L["X"], L["Wqkv"], L["Wproj"])
+    g = oa.tp_backward(L["X"], L["Wqkv"], L["Wproj"], f, L["G"])
+    grads = {"X": g["dX"], "Wqkv": np.concatenate([sh["dWqkv"] for sh in g["shards"]], 1),
+             "Wproj": np.concatenate([sh["dWproj"] for sh in g["shards"]], 0)}
+    worst = 0.0
+    for name in ("X", "Wqkv", "Wproj"):
+        for idx in np.ndindex(L[name].shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                args = {kk: L[kk].copy() for kk in ("X", "Wqkv", "Wproj")}
+                args[name][idx] += sgn * step
+                vals.append(float((fwd(args["X"], args["Wqkv"], args["Wproj"])["Out"] * L["G"]).sum()))
+            fd = (vals[0] - vals[1]) / (2 * step)
+            worst = max(worst, abs(fd - grads[name][idx]) / max(1.0, abs(grads[name][idx])))
+    return worst <= 1e-7
+
+
 PINS = [check_core_causal, check_core_full, check_layer_vs_torch, check_finite_differences,
         check_sharded_equals_unsharded, check_uniform_attention_closed_form,
-        check_causal_first_row_and_lse, check_key_shift_invariance]
+        check_causal_first_row_and_lse, check_key_shift_invariance, check_mask_vs_torch_sdpa,
+        check_key_padding_is_truncation, check_causal_pattern_as_general_mask,
+        check_rows_with_every_key_hidden, check_masked_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -193,25 +322,33 @@ def _some_pin_fails():
     return False
 
 
-def _mutant_core(monkeypatch, transform_S=None, transform_keep=None, dS_rule=None, dk_rule=None):
+def _mutant_core(monkeypatch, transform_S=None, transform_keep=None, dS_rule=None, dk_rule=None,
+                 transform_mask=None):
     """Re-plant core_forward / core_backward with one step changed."""
-    def fwd(q, k, v, causal):
+    def fwd(q, k, v, causal, mask=None):
         q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
         b, nh, s, dh = q.shape
         o, A, lse = np.zeros_like(q), np.zeros((b, nh, s, s)), np.zeros((b, nh, s))
-        keep = np.tril(np.ones((s, s), bool)) if causal else np.ones((s, s), bool)
+        base = np.tril(np.ones((s, s), bool)) if causal else np.ones((s, s), bool)
         if transform_keep:
-            keep = transform_keep(keep, causal)
+            base = transform_keep(base, causal)
         for bi in range(b):
+            keep = base
+            if mask is not None:
+                mb = np.asarray(mask[bi], bool)
+                keep = base & ~(transform_mask(mb) if transform_mask else mb)
+            seen = keep.any(axis=1)
             for h in range(nh):
                 S = q[bi, h] @ k[bi, h].T / np.sqrt(dh)
                 if transform_S:
                     S = transform_S(S, dh)
                 S = np.where(keep, S, -np.inf)
-                mx = S.max(axis=1, keepdims=True)
+                mx = np.where(seen, S.max(axis=1), 0.0)[:, None]
                 E = np.exp(S - mx)
-                z = E.sum(axis=1, keepdims=True)
-                A[bi, h], lse[bi, h], o[bi, h] = E / z, (mx + np.log(z))[:, 0], (E / z) @ v[bi, h]
+                z = np.where(seen[:, None], E.sum(axis=1, keepdims=True), 1.0)
+                A[bi, h] = E / z
+                lse[bi, h] = np.where(seen, mx[:, 0] + np.log(z[:, 0]), -np.inf)
+                o[bi, h] = A[bi, h] @ v[bi, h]
         return o, A, lse
 
     def bwd(q, k, v, A, do):
@@ -268,4 +405,21 @@ def test_mutant_head_column_order(monkeypatch):
         return np.stack([dq, dk, dv], axis=2).transpose(3, 0, 2, 1, 4).reshape(s * b, 3 * nh * dh)
     monkeypatch.setattr(oa, "split_heads", split)
     monkeypatch.setattr(oa, "merge_qkv", merge)
+    assert _some_pin_fails()
+
+
+def test_mutant_general_mask_transposed(monkeypatch):
+    """mask[β][j][i] read for query i, key j."""
+    _mutant_core(monkeypatch, transform_mask=lambda mb: mb.T)
+    assert _some_pin_fails()
+
+
+def test_mutant_general_mask_ignored(monkeypatch):
+    _mutant_core(monkeypatch, transform_mask=lambda mb: np.zeros_like(mb))
+    assert _some_pin_fails()
+
+
+def test_mutant_general_mask_off_by_one(monkeypatch):
+    """The mask read one key to the right (key j uses the bit of key j + 1)."""
+    _mutant_core(monkeypatch, transform_mask=lambda mb: np.concatenate([mb[:, 1:], mb[:, :1]], axis=1))
     assert _some_pin_fails()

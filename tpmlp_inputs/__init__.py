@@ -198,6 +198,26 @@ def qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=0, std=1.0):
     return {"qkv": Tensor(qkv, dtype), "do": Tensor(do, dtype)}
 
 
+def attn_mask(b, s, kind="padding", seed=0, p=0.3):
+    """A general attention mask [b, s, s] as uint8 (1 hides key j from query
+    i), shared by all heads and shards.
+      "padding": BERT-style: entry β has a valid length L_β drawn uniformly
+                 from [⌈s/2⌉, s]; a position is hidden when the query or the
+                 key is at or past L_β (padded query rows see no key)
+      "random":  each entry hidden with probability p (rows may end up with
+                 no visible key)"""
+    rng = np.random.default_rng([seed, 3])
+    if kind == "padding":
+        L = rng.integers((s + 1) // 2, s + 1, size=b)
+        pos = np.arange(s)
+        m = (pos[None, :, None] >= L[:, None, None]) | (pos[None, None, :] >= L[:, None, None])
+    elif kind == "random":
+        m = rng.random((b, s, s)) < p
+    else:
+        raise ValueError(kind)
+    return m.astype(np.uint8)
+
+
 def config_inputs(name, seed=0):
     c = CONFIGS[name]
     if c["kind"] == "vocab":
