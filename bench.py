@@ -343,16 +343,16 @@ def leg_attention(tp, reps):
     stream = torch.cuda.current_stream()
 
     def fwd():
-        tp.tpmlp_attn_fwd(X, Wq, Wp, QKV, O, lse, P, s, b, dh, True, stream)
+        tp.tpmlp_attn_fwd(X, Wq, Wp, QKV, O, lse, P, s, b, dh, True, stream=stream)
 
     def core_f():
-        tp.tpmlp_attn_core_fwd(QKV, O, lse, s, b, heads // t, dh, True, stream)
+        tp.tpmlp_attn_core_fwd(QKV, O, lse, s, b, heads // t, dh, True, stream=stream)
 
     def core_b():
-        tp.tpmlp_attn_core_bwd(QKV, O, lse, dO, dQKV, ws, s, b, heads // t, dh, True, stream)
+        tp.tpmlp_attn_core_bwd(QKV, O, lse, dO, dQKV, ws, s, b, heads // t, dh, True, stream=stream)
 
     def bwd():
-        tp.tpmlp_attn_bwd(X, Wq, Wp, QKV, O, lse, G, dO, dQKV, dWq, dWp, dXp, ws, s, b, dh, True, stream)
+        tp.tpmlp_attn_bwd(X, Wq, Wp, QKV, O, lse, G, dO, dQKV, dWq, dWp, dXp, ws, s, b, dh, True, stream=stream)
 
     for _ in range(3):
         fwd()
@@ -374,6 +374,29 @@ def leg_attention(tp, reps):
     tot = 3 * gemm_f + 3 * core_f_flop
     out["step"] = {"median_ms": round(step, 4), "tflops": round(tot / (step * 1e-3) / 1e12, 2),
                    "pct_of_peak": round(100.0 * tot / (step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    # the core with a general mask instead: BERT-style padding (lengths drawn
+    # from [s/2, s], padded query rows see no key), not causal; the flop count
+    # is the pages' unmasked one, so the rate is what the mask leaves of it
+    from tpmlp_inputs import attn_mask
+    mbytes = torch.from_numpy(attn_mask(b, s, "padding", seed=7)).to(dev)
+    visible = float(mbytes.numel() - int(mbytes.sum().item())) / mbytes.numel()
+    mask = tp.attn_pack_mask(mbytes)  # once per batch; every layer and pass reads the packed form
+
+    def core_mf():
+        tp.tpmlp_attn_core_fwd(QKV, O, lse, s, b, heads // t, dh, False, mask=mask, stream=stream)
+
+    def core_mb():
+        tp.tpmlp_attn_core_bwd(QKV, O, lse, dO, dQKV, ws, s, b, heads // t, dh, False, mask=mask, stream=stream)
+    core_mf()
+    core_mb()
+    torch.cuda.synchronize()
+    pad = {"mask": "padding (BERT-style), not causal", "visible_fraction": round(visible, 4)}
+    for name, fn, fl in (("core_fwd", core_mf, core_f_flop), ("core_bwd", core_mb, 2 * core_f_flop)):
+        ms = _time_events(fn, reps)
+        med = float(np.median(ms))
+        pad[name] = {"tflops_pages_formula": round(fl / (med * 1e-3) / 1e12, 2),
+                     "tflops_visible_entries": round(fl * visible / (med * 1e-3) / 1e12, 2), **_stats(ms)}
+    out["padding_mask"] = pad
     return out
 
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 4
+#define TPMLP_ABI_VERSION 5
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -267,8 +267,10 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a);
  *
  *   QKV_i = X·W_qkv,i                       [n, 3w]
  *   per batch entry and head: S = q·kᵀ/√head_dim, with causal != 0 the
- *   entries of key positions after the query position are −∞; A = softmax
- *   of each row of S; o = A·v
+ *   entries of key positions after the query position are −∞, and with a
+ *   general mask the entries it hides are −∞ as well; A = softmax of each
+ *   row of S; o = A·v (a row that sees no key: o = 0, lse = −∞, and it
+ *   passes no gradient)
  *   O_i  = the heads' o side by side        [n, w]
  *   P_i  = O_i·W_proj,i                     [n, d]  row-parallel partial;
  *                                                   Σ_i P_i via
@@ -290,31 +292,50 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a);
  *   t_local     shards processed by this call (>= 1), stacked on a leading
  *               axis of every per-shard tensor
  *   causal      0 (no mask) or 1 (causal)
+ *   mask        null (none) or a general mask packed by tpmlp_attn_pack_mask
+ *               (4-byte aligned): it hides key position j from query
+ *               position i of batch entry β for every head and shard — the
+ *               general mask of [EFF] §4.2's fused softmax (BERT's padding
+ *               mask is one); combined with causal when both are given.
  * Layouts: X [n, d]; W_qkv [t_local, d, 3w]; W_proj [t_local, w, d];
  *   QKV, dQKV [t_local, n, 3w]; O, dO [t_local, n, w]; lse [t_local, b,
  *   heads_local, s] fp32; P, dXp [t_local, n, d]; dW_qkv [t_local, d, 3w]
  *   and dW_proj [t_local, w, d] fp32.
  * Limits: one shard's QKV smaller than 2^31 bytes; t_local·b·heads_local·s
- *   < 2^31; bf16 needs d % 8 == 0 and 16-byte aligned bases.
+ *   < 2^31; with a mask, 4·s·⌈s/32⌉ < 2^31; bf16 needs d % 8 == 0 and
+ *   16-byte aligned bases.
  * Workspace of the backward: tpmlp_attn_bwd_workspace_bytes(...) bytes (the
  * δ rows), 4-byte aligned.
  *
  * tpmlp_attn_core_fwd / _bwd run the attention core alone on a given QKV
  * (and O, lse, dO): QKV -> O, lse and (QKV, O, lse, dO) -> dQKV.
+ *
+ * General mask, packed once per batch and read by every layer and both
+ * passes: tpmlp_attn_pack_mask turns a byte mask [b][s][s] (mask[β][i][j] !=
+ * 0 hides key j from query i; caller-owned device memory, any alignment) into
+ * tpmlp_attn_mask_words(b, s) 32-bit words (W = ⌈s/32⌉; part 0 [b][s][W] by
+ * query row: bit j of word w = key 32w + j hidden; part 1 [b][s][W] by key
+ * column: bit i of word w = query 32w + i hidden; positions past s set).
+ * tpmlp_attn_mask_words returns 0 for b < 1 or s < 1.  Errors: SHAPE (b < 1,
+ * s < 0, 4·s·W >= 2^31), NULLPTR, ALIGN (packed not 4-byte aligned); s = 0
+ * enqueues nothing.
  */
+size_t tpmlp_attn_mask_words(int64_t b, int64_t s);
+int tpmlp_attn_pack_mask(hipStream_t stream, int64_t b, int64_t s, const uint8_t* mask, uint32_t* packed);
 int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
-                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
-                   const void* Wproj, void* QKV, void* O, float* lse, void* P);
+                   int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                   const void* Wqkv, const void* Wproj, void* QKV, void* O, float* lse, void* P);
 size_t tpmlp_attn_bwd_workspace_bytes(int32_t t_local, int64_t s, int64_t b, int32_t heads_local);
 int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
-                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
-                   const void* Wproj, const void* QKV, const void* O, const float* lse, const void* G, void* dO,
-                   void* dQKV, float* dWqkv, float* dWproj, void* dXp, void* ws, size_t ws_bytes);
+                   int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                   const void* Wqkv, const void* Wproj, const void* QKV, const void* O, const float* lse,
+                   const void* G, void* dO, void* dQKV, float* dWqkv, float* dWproj, void* dXp, void* ws,
+                   size_t ws_bytes);
 int tpmlp_attn_core_fwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
-                        int32_t head_dim, int causal, const void* qkv, void* o, float* lse);
+                        int32_t head_dim, int causal, const uint32_t* mask, const void* qkv, void* o, float* lse);
 int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
-                        int32_t head_dim, int causal, const void* qkv, const void* o, const float* lse,
-                        const void* d_o, void* dqkv, void* ws, size_t ws_bytes);
+                        int32_t head_dim, int causal, const uint32_t* mask, const void* qkv, const void* o,
+                        const float* lse, const void* d_o, void* dqkv, void* ws, size_t ws_bytes);
 
 /*
  * Vocabulary-parallel logit layer and cross-entropy ([SENSE] §2.2.2, Eq. (3)

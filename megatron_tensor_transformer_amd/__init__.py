@@ -63,11 +63,13 @@ SIGNATURES = {
     "tpmlp_bias_grad_workspace_bytes": (_SZ, [_I32, _I64, _I64]),
     "tpmlp_bias_grad": (_I, [_P, _I, _I32, _I64, _I64, _P, _P, _P, _SZ]),
     "tpmlp_sp_workspace_bytes": (_SZ, [_I64, _I64]),
-    "tpmlp_attn_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "tpmlp_attn_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tpmlp_attn_bwd_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I32]),
-    "tpmlp_attn_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I] + [_P] * 13 + [_SZ]),
-    "tpmlp_attn_core_fwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P]),
-    "tpmlp_attn_core_bwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _SZ]),
+    "tpmlp_attn_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I] + [_P] * 14 + [_SZ]),
+    "tpmlp_attn_core_fwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P, _P]),
+    "tpmlp_attn_core_bwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _P, _SZ]),
+    "tpmlp_attn_mask_words": (_SZ, [_I64, _I64]),
+    "tpmlp_attn_pack_mask": (_I, [_P, _I64, _I64, _P, _P]),
     "tpmlp_ln_sp": (_I, [_P, ctypes.POINTER(SpArgs)]),
     "tpmlp_vocab_ce_workspace_bytes": (_SZ, [_I32, _I64]),
     "tpmlp_vocab_ce_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I64] + [_P] * 8 + [_SZ]),
@@ -178,37 +180,76 @@ def tpmlp_bias_grad(g, db, ws=None, stream=None):
                                  ws_bytes))
 
 
-def tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, stream=None):
+def tpmlp_attn_pack_mask(mask, packed, stream=None):
+    """mask [b, s, s] uint8/bool (nonzero hides key j from query i) -> packed
+    int32 [2, b, s, ⌈s/32⌉] (the form the attention entry points take)."""
+    if mask.dtype not in (torch.uint8, torch.bool) or mask.dim() != 3 or mask.shape[1] != mask.shape[2]:
+        raise TpmlpValueError(ERR_ARG, "mask must be uint8 or bool of shape (b, s, s)")
+    b, s, _ = mask.shape
+    _check(lib().tpmlp_attn_pack_mask(_stream(stream), b, s, _ptr(mask), _ptr(packed)))
+
+
+def attn_pack_mask(mask, stream=None):
+    """Allocating wrapper: the packed form of a [b, s, s] mask, int32 [2, b, s, ⌈s/32⌉]."""
+    b, s = mask.shape[0], mask.shape[1]
+    packed = torch.empty((2, b, s, (s + 31) // 32), dtype=torch.int32, device=mask.device)
+    tpmlp_attn_pack_mask(mask, packed, stream)
+    return packed
+
+
+def _mask_ptr(mask, s, b, stream):
+    """The general attention mask for an entry point: None, a packed int32
+    tensor [2, b, s, ⌈s/32⌉] (attn_pack_mask), or a uint8 / bool tensor
+    [b, s, s], which is packed here on the call's stream."""
+    if mask is None:
+        return None, None
+    if mask.dtype in (torch.uint8, torch.bool):
+        if tuple(mask.shape) != (b, s, s):
+            raise TpmlpValueError(ERR_ARG, f"mask must have shape {(b, s, s)}")
+        mask = attn_pack_mask(mask, stream)
+        if stream is not None:
+            mask.record_stream(stream)  # freed only after the call's work on that stream
+    if mask.dtype != torch.int32 or tuple(mask.shape) != (2, b, s, (s + 31) // 32):
+        raise TpmlpValueError(ERR_ARG, f"packed mask must be int32 of shape {(2, b, s, (s + 31) // 32)}")
+    return _ptr(mask), mask
+
+
+def tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, mask=None, stream=None):
     """X [s·b, d]; Wqkv [t, d, 3w]; Wproj [t, w, d]; QKV [t, s·b, 3w]; O [t, s·b, w];
-    lse [t, b, heads, s] fp32; P [t, s·b, d]; w = heads·head_dim."""
+    lse [t, b, heads, s] fp32; P [t, s·b, d]; w = heads·head_dim; mask None, a
+    packed mask (attn_pack_mask) or a [b, s, s] uint8/bool mask."""
     t, d, w3 = Wqkv.shape
     heads = w3 // 3 // head_dim
-    _check(lib().tpmlp_attn_fwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), _ptr(X),
+    mp, _keep = _mask_ptr(mask, s, b, stream)
+    _check(lib().tpmlp_attn_fwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), mp, _ptr(X),
                                 _ptr(Wqkv), _ptr(Wproj), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(P)))
 
 
 def tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal,
-                   stream=None):
+                   mask=None, stream=None):
     t, d, w3 = Wqkv.shape
     heads = w3 // 3 // head_dim
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().tpmlp_attn_bwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), _ptr(X),
+    mp, _keep = _mask_ptr(mask, s, b, stream)
+    _check(lib().tpmlp_attn_bwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), mp, _ptr(X),
                                 _ptr(Wqkv), _ptr(Wproj), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(G), _ptr(dO),
                                 _ptr(dQKV), _ptr(dWqkv), _ptr(dWproj), _ptr(dXp), _ptr(ws), ws_bytes))
 
 
-def tpmlp_attn_core_fwd(qkv, o, lse, s, b, heads, head_dim, causal, stream=None):
+def tpmlp_attn_core_fwd(qkv, o, lse, s, b, heads, head_dim, causal, mask=None, stream=None):
     """qkv [t, s·b, heads·3·head_dim] -> o [t, s·b, heads·head_dim], lse [t, b, heads, s]."""
     t = qkv.shape[0]
-    _check(lib().tpmlp_attn_core_fwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), _ptr(qkv),
-                                     _ptr(o), _ptr(lse)))
+    mp, _keep = _mask_ptr(mask, s, b, stream)
+    _check(lib().tpmlp_attn_core_fwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), mp,
+                                     _ptr(qkv), _ptr(o), _ptr(lse)))
 
 
-def tpmlp_attn_core_bwd(qkv, o, lse, d_o, dqkv, ws, s, b, heads, head_dim, causal, stream=None):
+def tpmlp_attn_core_bwd(qkv, o, lse, d_o, dqkv, ws, s, b, heads, head_dim, causal, mask=None, stream=None):
     t = qkv.shape[0]
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().tpmlp_attn_core_bwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), _ptr(qkv),
-                                     _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dqkv), _ptr(ws), ws_bytes))
+    mp, _keep = _mask_ptr(mask, s, b, stream)
+    _check(lib().tpmlp_attn_core_bwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), mp,
+                                     _ptr(qkv), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dqkv), _ptr(ws), ws_bytes))
 
 
 def tpmlp_ln_sp(args, stream=None):
@@ -330,7 +371,7 @@ def attn_bwd_workspace_bytes(t, s, b, heads):
     return lib().tpmlp_attn_bwd_workspace_bytes(t, s, b, heads)
 
 
-def attn_fwd(X, Wqkv, Wproj, s, b, head_dim, causal=True, stream=None):
+def attn_fwd(X, Wqkv, Wproj, s, b, head_dim, causal=True, mask=None, stream=None):
     """Allocating wrapper: returns QKV, O, lse, P."""
     t, d, w3 = Wqkv.shape
     w = w3 // 3
@@ -339,11 +380,11 @@ def attn_fwd(X, Wqkv, Wproj, s, b, head_dim, causal=True, stream=None):
     O = torch.empty((t, n, w), dtype=X.dtype, device=X.device)
     lse = torch.empty((t, b, w // head_dim, s), dtype=torch.float32, device=X.device)
     P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
-    tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, stream)
+    tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, mask, stream)
     return QKV, O, lse, P
 
 
-def attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, s, b, head_dim, causal=True, stream=None):
+def attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, s, b, head_dim, causal=True, mask=None, stream=None):
     """Allocating wrapper: returns dO, dQKV, dWqkv, dWproj, dXp."""
     t, d, w3 = Wqkv.shape
     w = w3 // 3
@@ -355,7 +396,8 @@ def attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, s, b, head_dim, causal=True, stream
     dXp = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
     nb = attn_bwd_workspace_bytes(t, s, b, w // head_dim)
     ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=X.device)
-    tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal, stream)
+    tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal, mask,
+                   stream)
     return dO, dQKV, dWqkv, dWproj, dXp
 
 

@@ -400,7 +400,7 @@ namespace {
 
 // Shared checks of the attention entry points; fills the core problem.
 int attn_core_problem(int dt, int32_t t_local, int64_t s, int64_t b, int32_t nh, int32_t dh, int causal,
-                      tpmlp::AttnProblem& p) {
+                      const uint32_t* mask, tpmlp::AttnProblem& p) {
   if (!valid_dt(dt)) return TPMLP_ERR_DTYPE;
   if (t_local < 1 || s < 0 || b < 1 || nh < 1) return TPMLP_ERR_SHAPE;
   if (dh != 64 && dh != 128) return TPMLP_ERR_SHAPE;
@@ -413,6 +413,10 @@ int attn_core_problem(int dt, int32_t t_local, int64_t s, int64_t b, int32_t nh,
   const int64_t wgs = static_cast<int64_t>(t_local) * b * nh * ((s + 127) / 128);
   const int64_t rows = static_cast<int64_t>(t_local) * b * nh * s;
   if (wgs > kMaxDim || rows > kMaxDim) return TPMLP_ERR_SHAPE;
+  if (mask != nullptr) {  // one batch entry's part of the packed mask: s·⌈s/32⌉ words
+    if (s * ((s + 31) / 32) * 4 > kMaxDim) return TPMLP_ERR_SHAPE;
+    if (!aligned(mask, 4)) return TPMLP_ERR_ALIGN;
+  }
   p = tpmlp::AttnProblem{};
   p.dt = dt;
   p.T = t_local;
@@ -421,6 +425,7 @@ int attn_core_problem(int dt, int32_t t_local, int64_t s, int64_t b, int32_t nh,
   p.nh = nh;
   p.dh = dh;
   p.causal = causal != 0;
+  p.mask = mask;
   return TPMLP_OK;
 }
 
@@ -429,9 +434,9 @@ int attn_core_problem(int dt, int32_t t_local, int64_t s, int64_t b, int32_t nh,
 extern "C" {
 
 int tpmlp_attn_core_fwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
-                        int32_t head_dim, int causal, const void* qkv, void* o, float* lse) {
+                        int32_t head_dim, int causal, const uint32_t* mask, const void* qkv, void* o, float* lse) {
   tpmlp::AttnProblem p;
-  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, p);
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, mask, p);
   if (st) return st;
   if (s == 0) return TPMLP_OK;
   st = check_ptrs(dt, {qkv, o});
@@ -444,6 +449,20 @@ int tpmlp_attn_core_fwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, 
   return hip_status(tpmlp::launch_attn_fwd(p, stream));
 }
 
+size_t tpmlp_attn_mask_words(int64_t b, int64_t s) {
+  if (b < 1 || s < 1 || s > kMaxDim || b > kMaxDim) return 0;
+  return 2 * static_cast<size_t>(b) * static_cast<size_t>(s) * static_cast<size_t>((s + 31) / 32);
+}
+
+int tpmlp_attn_pack_mask(hipStream_t stream, int64_t b, int64_t s, const uint8_t* mask, uint32_t* packed) {
+  if (b < 1 || s < 0) return TPMLP_ERR_SHAPE;
+  if (s == 0) return TPMLP_OK;
+  if (s * ((s + 31) / 32) * 4 > kMaxDim || b * s > kMaxDim) return TPMLP_ERR_SHAPE;
+  if (mask == nullptr || packed == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(packed, 4)) return TPMLP_ERR_ALIGN;
+  return hip_status(tpmlp::launch_attn_pack_mask(static_cast<int>(b), static_cast<int>(s), mask, packed, stream));
+}
+
 size_t tpmlp_attn_bwd_workspace_bytes(int32_t t_local, int64_t s, int64_t b, int32_t heads_local) {
   if (t_local < 1 || s <= 0 || b < 1 || heads_local < 1) return 0;
   return static_cast<size_t>(t_local) * static_cast<size_t>(b) * static_cast<size_t>(heads_local) *
@@ -451,10 +470,10 @@ size_t tpmlp_attn_bwd_workspace_bytes(int32_t t_local, int64_t s, int64_t b, int
 }
 
 int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, int64_t b, int32_t heads_local,
-                        int32_t head_dim, int causal, const void* qkv, const void* o, const float* lse,
-                        const void* d_o, void* dqkv, void* ws, size_t ws_bytes) {
+                        int32_t head_dim, int causal, const uint32_t* mask, const void* qkv, const void* o,
+                        const float* lse, const void* d_o, void* dqkv, void* ws, size_t ws_bytes) {
   tpmlp::AttnProblem p;
-  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, p);
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, mask, p);
   if (st) return st;
   if (s == 0) return TPMLP_OK;
   st = check_ptrs(dt, {qkv, o, d_o, dqkv});
@@ -474,10 +493,10 @@ int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, 
 }
 
 int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
-                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
-                   const void* Wproj, void* QKV, void* O, float* lse, void* P) {
+                   int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                   const void* Wqkv, const void* Wproj, void* QKV, void* O, float* lse, void* P) {
   tpmlp::AttnProblem ap;
-  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, ap);
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, mask, ap);
   if (st) return st;
   const int64_t n = s * b, w = static_cast<int64_t>(heads_local) * head_dim;
   st = check_mlp_dims(dt, n, d, 3 * w, t_local);  // X·W_qkv and O·W_proj sizes
@@ -528,11 +547,12 @@ int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, 
 }
 
 int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
-                   int32_t head_dim, int32_t t_local, int causal, const void* X, const void* Wqkv,
-                   const void* Wproj, const void* QKV, const void* O, const float* lse, const void* G, void* dO,
-                   void* dQKV, float* dWqkv, float* dWproj, void* dXp, void* ws, size_t ws_bytes) {
+                   int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                   const void* Wqkv, const void* Wproj, const void* QKV, const void* O, const float* lse,
+                   const void* G, void* dO, void* dQKV, float* dWqkv, float* dWproj, void* dXp, void* ws,
+                   size_t ws_bytes) {
   tpmlp::AttnProblem ap;
-  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, ap);
+  int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, mask, ap);
   if (st) return st;
   const int64_t n = s * b, w = static_cast<int64_t>(heads_local) * head_dim;
   st = check_mlp_dims(dt, n, d, 3 * w, t_local);

@@ -58,6 +58,28 @@ __device__ __forceinline__ uint32_t kv_slot(int row, int chunk) {
   return static_cast<uint32_t>(row * (DH * 2) + ((chunk ^ f) << 4));
 }
 
+// The general mask arrives bit-packed (tpmlp_attn_pack_mask): W = ⌈s/32⌉
+// 32-bit words per position, part 0 by query row (bit j of word w of row q:
+// key 32w + j hidden from q), part 1 by key column (bit i of word w of column
+// k: k hidden from query 32w + i); positions past s are set.  A lane reads one
+// word per 32-wide half tile through a buffer resource.
+__device__ uint32_t tpmlp_llvm_buffer_load_u32(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.i32");
+
+// The 16 bits of a 32-position mask word that belong to this lane's
+// accumulator entries: entry v = 4g + e is position 8g + 4·hi + e.
+__device__ __forceinline__ uint32_t lane_bits16(uint32_t word, int hi) {
+  const uint32_t x = (word >> (4 * hi)) & 0x0F0F0F0Fu;
+  return (x & 0xFu) | ((x >> 4) & 0xF0u) | ((x >> 8) & 0xF00u) | ((x >> 12) & 0xF000u);
+}
+
+// −∞ where bit v of bits is set (the general mask hides accumulator entry v).
+__device__ __forceinline__ void apply_mask16(f32x16& x, uint32_t bits) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if ((bits >> v) & 1u) x[v] = -INFINITY;
+}
+
 struct AttnArgs {
   const void* qkv;
   void* o;
@@ -67,6 +89,8 @@ struct AttnArgs {
   float scale;        // 1/√dh
   float scale_log2;   // log2(e)/√dh
   uint32_t qkv_shard_bytes;
+  const uint32_t* mask;  // packed general mask (2 parts of [b][s][mw] words), or null
+  int mw;                // words per position, ⌈s/32⌉
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.  The
@@ -364,7 +388,7 @@ __device__ __forceinline__ void lgkm_wait(i32x4& x, i32x4& y) {
   else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y)::"memory");
 }
 
-template <int DH, bool CAUSAL>
+template <int DH, bool CAUSAL, bool GMASK>
 __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = AKV * DH * 2, RB = DH * 2;
   constexpr int NC = DH / 16;   // k16 slices of the head dimension
@@ -381,6 +405,10 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   const int r32 = lane & 31, hi = lane >> 5;
   const int q0 = qb * AQ + wave * 32;
   const int qrow = q0 + r32;
+  // this batch entry's general mask (read only when GMASK)
+  const i32x4 mrs = GMASK ? make_rsrc(a.mask + static_cast<int64_t>(bi) * a.s * a.mw,
+                                        static_cast<uint32_t>(static_cast<int64_t>(a.s) * a.mw * 4))
+                             : i32x4{0, 0, 0, 0};
   const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH;
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + static_cast<int64_t>(T) * a.s * a.b * row_len;
   const i32x4 rsrc = make_rsrc(qkv, a.qkv_shard_bytes);
@@ -421,6 +449,17 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.f;
   float m = -INFINITY, l = 0.f;
 
+  // general-mask words of key tile jj for this lane's row (one per 32 keys)
+  uint32_t mwn[2] = {~0u, ~0u};
+  auto mask_words = [&](int jj) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pos = jj * AKV + 32 * u;
+      mwn[u] = qrow < a.s && pos < a.s ? tpmlp_llvm_buffer_load_u32(mrs, (qrow * a.mw + pos / 32) * 4, 0, 0) : ~0u;
+    }
+  };
+  if constexpr (GMASK) mask_words(0);
+
   // one key tile in stage ST (compile-time, so every LDS offset is an
   // immediate).  One barrier per tile: after it every wave has finished the
   // previous tile, so the other stage is free and the next tile's DMA is
@@ -429,15 +468,27 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
     constexpr int ST = decltype(stc)::value;
     wait_vmcnt<0>();  // this wave's share of tile j (the only DMA in flight)
     lds_barrier();
+    // A causal tile whose first key is past the wave's last query row (or a
+    // wave wholly past s) contributes nothing: its work is skipped.
+    const int t0 = j * AKV;
+    const bool dead = q0 >= a.s || (CAUSAL && t0 > q0 + 31);
+    // general mask of the tile's keys for this lane's row (bit v of mk[u]:
+    // accumulator entry v of half u), from the words loaded one tile ahead;
+    // the next tile's words are loaded before its DMA
+    uint32_t mk[2] = {0u, 0u};
+    bool hidden = false;
+    if constexpr (GMASK) {
+      mk[0] = lane_bits16(mwn[0], hi);
+      mk[1] = lane_bits16(mwn[1], hi);
+      if (j + 1 < nkv) mask_words(j + 1);
+      hidden = __all((mk[0] & mk[1]) == 0xFFFFu);  // the wave sees no key of the tile
+    }
     if (j + 1 < nkv) {
       TPMLP_LDS char* nxt = lds + (ST ^ 1) * 2 * TILE;
       issue_tile<DH, NW>(rsrc, nxt, kp, j + 1, stride, a.s, wave);
       issue_tile<DH, NW>(rsrc, nxt + TILE, vp, j + 1, stride, a.s, wave);
     }
-    // A causal tile whose first key is past the wave's last query row (or a
-    // wave wholly past s) contributes nothing: skip its work.
-    const int t0 = j * AKV;
-    if (q0 >= a.s || (CAUSAL && t0 > q0 + 31)) return;
+    if (dead || hidden) return;
 
     // Sᵀ block: sacc[u][v] = S[qrow][kv], kv = 64j + 32u + 8(v/4) + 4·hi + v%4.
     // The two 32-key halves alternate (independent accumulators), and the K
@@ -470,6 +521,10 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
     if (t0 + AKV > a.s || (CAUSAL && t0 + AKV - 1 > q0)) {
       const int lim = CAUSAL ? min(qrow + 1, a.s) : a.s;
       mask_range(sacc, -1 << 30, lim - t0 - 4 * hi, -INFINITY);
+    }
+    if constexpr (GMASK) {
+      apply_mask16(sacc[0], mk[0]);
+      apply_mask16(sacc[1], mk[1]);
     }
     float mloc = -INFINITY;
 #pragma unroll
@@ -590,7 +645,9 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   const int kend = CAUSAL ? q + 1 : a.s;
+  const uint32_t* mrow = a.mask ? a.mask + (static_cast<int64_t>(bi) * a.s + q) * a.mw : nullptr;
   for (int kv = 0; kv < kend; ++kv) {
+    if (mrow && ((mrow[kv >> 5] >> (kv & 31)) & 1u)) continue;
     const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
     float sdot = 0.f;
 #pragma unroll
@@ -605,9 +662,10 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   }
   float* op = static_cast<float*>(a.o) + static_cast<int64_t>(T) * a.s * a.b * a.nh * DH +
               (static_cast<int64_t>(q) * a.b + bi) * a.nh * DH + h * DH;
+  // a row that sees no key: o = 0, lse = −∞
 #pragma unroll
-  for (int d = 0; d < DH; ++d) op[d] = acc[d] / l;
-  a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + q] = m + logf(l);
+  for (int d = 0; d < DH; ++d) op[d] = l > 0.f ? acc[d] / l : 0.f;
+  a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + q] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ backward
@@ -622,6 +680,8 @@ struct AttnBwdArgs {
   int nqb;            // blocks of AQ rows (dq workgroups, dk/dv workgroups)
   float scale, scale_log2;
   uint32_t qkv_shard_bytes, o_shard_bytes;
+  const uint32_t* mask;  // packed general mask (2 parts of [b][s][mw] words), or null
+  int mw;                // words per position, ⌈s/32⌉
 };
 
 // δ[T][bi][h][q] = Σ_d do·o over the head's dh columns of row q (fp32): one
@@ -662,7 +722,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnBwdArgs a) {
 // 32-key half of a tile: Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ (lane L holds query row
 // L%32), P = exp2(S·log2(e)/√dh − lse·log2(e)), dS = P ⊙ (dP − δ), and
 // dQᵀ += Kᵀ·dSᵀ with the keys in the accumulators' order.
-template <int DH, bool CAUSAL>
+template <int DH, bool CAUSAL, bool GMASK>
 __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int TILE = AKV * DH * 2;
   constexpr int NC = DH / 16, ND = DH / 32;
@@ -710,7 +770,16 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   }
   dlt += __shfl_xor(dlt, 32, 64);
   if (valid && hi == 0) a.delta[srow + qrow] = dlt;
-  const float lse2 = valid ? a.lse[srow + qrow] * 1.4426950408889634f : 0.f;
+  // lse = −∞ (a row that sees no key, every entry hidden): +∞ here makes
+  // P = 2^(−∞ − ∞) = 0 instead of NaN
+  float lse2 = 0.f;
+  if (valid) {
+    const float l = a.lse[srow + qrow];
+    lse2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
+  }
+  const i32x4 mrs = GMASK ? make_rsrc(a.mask + static_cast<int64_t>(bi) * a.s * a.mw,
+                                        static_cast<uint32_t>(static_cast<int64_t>(a.s) * a.mw * 4))
+                             : i32x4{0, 0, 0, 0};
 
   f32x16 dq[ND];
 #pragma unroll
@@ -727,6 +796,17 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   uint32_t va[NR];
   tr_addrs<DH, ND>(lds_base, lane, va);
 
+  // general-mask words of key block jj for this lane's row (one per 32 keys)
+  uint32_t mwn[2] = {~0u, ~0u};
+  auto mask_words = [&](int jj) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pos = jj * AKV + 32 * u;
+      mwn[u] = valid && pos < a.s ? tpmlp_llvm_buffer_load_u32(mrs, (qrow * a.mw + pos / 32) * 4, 0, 0) : ~0u;
+    }
+  };
+  if constexpr (GMASK) mask_words(0);
+
   // One key block in stage ST (compile-time: every LDS offset is an
   // immediate).  One barrier per block: after it every wave has finished the
   // previous block, so the other stage is free and the next block's DMA is
@@ -735,15 +815,27 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     constexpr int ST = decltype(stc)::value;
     wait_vmcnt<0>();  // this wave's share of block j
     lds_barrier();
+    // a causal block whose first key is past the wave's last query row (or a
+    // wave wholly past s) contributes nothing
+    const int t0 = j * AKV;
+    const bool dead = q0 >= a.s || (CAUSAL && t0 > q0 + 31);
+    // general mask of the block's keys for this lane's row (bit v of mk[u]:
+    // accumulator entry v of half u), from the words loaded one block ahead;
+    // the next block's words are loaded before its DMA
+    uint32_t mk[2] = {0u, 0u};
+    bool hidden = false;
+    if constexpr (GMASK) {
+      mk[0] = lane_bits16(mwn[0], hi);
+      mk[1] = lane_bits16(mwn[1], hi);
+      if (j + 1 < nkv) mask_words(j + 1);
+      hidden = __all((mk[0] & mk[1]) == 0xFFFFu);  // the wave sees no key of the block
+    }
     if (j + 1 < nkv) {
       TPMLP_LDS char* nxt = lds + (ST ^ 1) * 2 * TILE;
       load_tile<DH>(rsrc, nxt, a.s, a.b, bi, row_len, kcol, j + 1, wave, lane);
       load_tile<DH>(rsrc, nxt + TILE, a.s, a.b, bi, row_len, vcol, j + 1, wave, lane);
     }
-    // a causal block whose first key is past the wave's last query row (or a
-    // wave wholly past s) contributes nothing
-    const int t0 = j * AKV;
-    if (q0 >= a.s || (CAUSAL && t0 > q0 + 31)) return;
+    if (dead || hidden) return;
     const bool masked = t0 + AKV > a.s || q0 + 31 >= a.s || (CAUSAL && t0 + AKV - 1 > q0);
     static_for<0, 2>([&](auto uc) {
       constexpr int U = decltype(uc)::value;
@@ -776,6 +868,7 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
         const int lim = valid ? (CAUSAL ? min(qrow + 1, a.s) : a.s) : 0;
         mask_range1(sacc, U, -1 << 30, lim - t0 - 4 * hi, -INFINITY);
       }
+      if constexpr (GMASK) apply_mask16(sacc, mk[U]);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], a.scale_log2, -lse2));
@@ -824,7 +917,7 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 // through LDS.  Per 32-query half of a tile: S'ᵀ = Q·Kᵀ and dP'ᵀ = dO·Vᵀ
 // with lane L holding key row L%32, P and dS as in dq, then dVᵀ += dOᵀ·P and
 // dKᵀ += Qᵀ·dS with the query rows in the accumulators' order.
-template <int DH, bool CAUSAL>
+template <int DH, bool CAUSAL, bool GMASK>
 __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   constexpr int TILE = AKV * DH * 2;
   constexpr int NC = DH / 16, ND = DH / 32;
@@ -855,7 +948,11 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   // statistics of query block j (threads 0..127: one value each)
   auto load_stat = [&](int j, float& v) {
     const int t = threadIdx.x & 63, qr = j * AKV + t;
-    if (threadIdx.x < 64) v = qr < a.s ? a.lse[srow + qr] * 1.4426950408889634f : 0.f;
+    if (threadIdx.x < 64) {
+      // lse = −∞ (a row that sees no key): +∞ makes its P = 0 instead of NaN
+      const float l = qr < a.s ? a.lse[srow + qr] : 0.f;
+      v = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
+    }
     else if (threadIdx.x < 128) v = qr < a.s ? a.delta[srow + qr] : 0.f;
   };
   auto store_stat = [&](int st, float v) {
@@ -869,6 +966,10 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
 
   bf16x8 kf[NC], vf[NC];
   const bool valid = krow < a.s;
+  // this batch entry's general mask (read only when GMASK and krow < s)
+  const i32x4 mrs = GMASK ? make_rsrc(a.mask + (static_cast<int64_t>(a.b) + bi) * a.s * a.mw,
+                                        static_cast<uint32_t>(static_cast<int64_t>(a.s) * a.mw * 4))
+                             : i32x4{0, 0, 0, 0};
   {
     const bf16* kp = qkv + (static_cast<int64_t>(krow) * a.b + bi) * row_len + h * 3 * DH + DH + 8 * hi;
 #pragma unroll
@@ -896,6 +997,18 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   // this lane's statistics: 4 consecutive query rows per 16-B read
   const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&stat[0][0][0])) + 16 * hi;
 
+  // general-mask words of query block jj for this lane's key (column part,
+  // one per 32 query rows)
+  uint32_t mwn[2] = {~0u, ~0u};
+  auto mask_words = [&](int jj) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pos = jj * AKV + 32 * u;
+      mwn[u] = valid && pos < a.s ? tpmlp_llvm_buffer_load_u32(mrs, (krow * a.mw + pos / 32) * 4, 0, 0) : ~0u;
+    }
+  };
+  if constexpr (GMASK) mask_words(j0);
+
   // One query block in stage ST (compile-time: every LDS offset is an
   // immediate).  One barrier per block: after it every wave has finished the
   // previous block, so the other stage (tiles and statistics) is free; the
@@ -906,18 +1019,30 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
     wait_vmcnt<0>();  // this wave's share of block j and its statistic
     lds_wait();       // its statistics write of the previous step
     lds_barrier();
+    const int t0 = j * AKV;
+    const bool masked = t0 + AKV > a.s || k0 + 31 >= a.s || (CAUSAL && t0 < k0 + 31);
+    // a causal block whose last query row is before the wave's first key (or
+    // a wave wholly past s) contributes nothing
+    const bool dead = k0 >= a.s || (CAUSAL && t0 + AKV - 1 < k0);
+    // general mask of (query row, this lane's key), from the packed mask's
+    // column part: bit v of mk[U] for accumulator entry v, query row t0 + 32U +
+    // 8(v/4) + 4·hi + v%4; from the words loaded one block ahead, the next
+    // block's words loaded before its DMA
+    uint32_t mk[2] = {0u, 0u};
+    bool hidden = false;
+    if constexpr (GMASK) {
+      mk[0] = lane_bits16(mwn[0], hi);
+      mk[1] = lane_bits16(mwn[1], hi);
+      if (j + 1 < nq) mask_words(j + 1);
+      hidden = __all((mk[0] & mk[1]) == 0xFFFFu);  // no query of the block sees the wave's keys
+    }
     if (j + 1 < nq) {
       load_stat(j + 1, sv);
       TPMLP_LDS char* nxt = lds + (ST ^ 1) * 2 * TILE;
       load_tile<DH>(rq, nxt, a.s, a.b, bi, row_len, qcol, j + 1, wave, lane);
       load_tile<DH>(rd, nxt + TILE, a.s, a.b, bi, orow, dcol, j + 1, wave, lane);
     }
-    const int t0 = j * AKV;
-    const bool masked = t0 + AKV > a.s || k0 + 31 >= a.s || (CAUSAL && t0 < k0 + 31);
-    // a causal block whose last query row is before the wave's first key (or
-    // a wave wholly past s) contributes nothing
-    const bool dead = k0 >= a.s || (CAUSAL && t0 + AKV - 1 < k0);
-    if (!dead) static_for<0, 2>([&](auto uc) {
+    if (!dead && !hidden) static_for<0, 2>([&](auto uc) {
       constexpr int U = decltype(uc)::value;
       constexpr int QB = ST * 2 * TILE + U * 32 * RB, DB = QB + TILE;  // rows 32U.. of Q and dO
       // statistics of the lane's 16 query rows (lse·log2(e), δ), read ahead
@@ -966,6 +1091,7 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
         const int hi_ = valid ? a.s - t0 - 4 * hi : lo;
         mask_range1(sacc, U, lo, hi_, -INFINITY);
       }
+      if constexpr (GMASK) apply_mask16(sacc, mk[U]);
       f32x16 pv;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
@@ -1064,7 +1190,9 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(AttnBwdArgs a) {
     acc[d] = 0.f;
   }
   const int kend = CAUSAL ? q + 1 : a.s;
+  const uint32_t* mrow = a.mask ? a.mask + (static_cast<int64_t>(bi) * a.s + q) * a.mw : nullptr;
   for (int kv = 0; kv < kend; ++kv) {
+    if (mrow && ((mrow[kv >> 5] >> (kv & 31)) & 1u)) continue;  // hidden (all of them when lse = −∞)
     const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
     float sdot = 0.f, pdot = 0.f;
 #pragma unroll
@@ -1101,7 +1229,9 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(AttnBwdArgs a) {
   float dk[DH], dv[DH];
 #pragma unroll
   for (int d = 0; d < DH; ++d) dk[d] = dv[d] = 0.f;
+  const uint32_t* mcol = a.mask ? a.mask + ((static_cast<int64_t>(a.b) + bi) * a.s + kv) * a.mw : nullptr;
   for (int q = CAUSAL ? kv : 0; q < a.s; ++q) {
+    if (mcol && ((mcol[q >> 5] >> (q & 31)) & 1u)) continue;
     const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH;
     const float* dp = dout + (static_cast<int64_t>(q) * a.b + bi) * orow + h * DH;
     float sdot = 0.f, pdot = 0.f;
@@ -1133,10 +1263,17 @@ hipError_t launch_bwd_t(const AttnBwdArgs& a, int dt, hipStream_t stream) {
   if (dt == 1) {
     // dq also forms δ (into the workspace) for the dk/dv kernel after it
     const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.T) * a.b * a.nh * a.nqb);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL>), dim3(blocks), dim3(ATHR), 0, stream, a);
+    if (a.mask) {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, CAUSAL, true>), dim3(blocks), dim3(ATHR), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL, true>), dim3(blocks), dim3(ATHR), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, CAUSAL, false>), dim3(blocks), dim3(ATHR), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL, false>), dim3(blocks), dim3(ATHR), 0, stream, a);
+    }
   } else {
     const unsigned dblocks = static_cast<unsigned>((rows + 255) / 256);
     hipLaunchKernelGGL((attn_delta_kernel<float, DH>), dim3(dblocks), dim3(256), 0, stream, a);
@@ -1155,8 +1292,12 @@ template <int DH, bool CAUSAL>
 hipError_t launch_fwd_t(const AttnArgs& a, int dt, hipStream_t stream) {
   if (dt == 1) {
     const int64_t blocks = static_cast<int64_t>(a.T) * a.b * a.nh * a.nqb;
-    hipLaunchKernelGGL((attn_fwd_kernel<DH, CAUSAL>), dim3(static_cast<unsigned>(blocks)), dim3(ATHR), 0, stream,
-                       a);
+    if (a.mask)
+      hipLaunchKernelGGL((attn_fwd_kernel<DH, CAUSAL, true>), dim3(static_cast<unsigned>(blocks)), dim3(ATHR), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<DH, CAUSAL, false>), dim3(static_cast<unsigned>(blocks)), dim3(ATHR), 0,
+                         stream, a);
   } else {
     const int64_t total = static_cast<int64_t>(a.T) * a.b * a.nh * a.s;
     hipLaunchKernelGGL((attn_fwd_f32_kernel<DH, CAUSAL>), dim3(static_cast<unsigned>((total + 127) / 128)),
@@ -1165,7 +1306,41 @@ hipError_t launch_fwd_t(const AttnArgs& a, int dt, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Bit-packing of a byte mask [b][s][s] (nonzero hides key j from query i):
+// one thread per output word; part 0 (rows) reads 32 consecutive bytes of a
+// row, part 1 (columns) 32 bytes of a column (adjacent threads take adjacent
+// columns, so each of those reads is coalesced).  Positions past s are set.
+__global__ __launch_bounds__(256) void attn_pack_mask_kernel(const uint8_t* __restrict__ mask,
+                                                             uint32_t* __restrict__ out, int b, int s, int mw) {
+  const int64_t per_part = static_cast<int64_t>(b) * s * mw;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= 2 * per_part) return;
+  const int part = static_cast<int>(idx / per_part);
+  int64_t r = idx - part * per_part;
+  const int w = static_cast<int>(r % mw);
+  r /= mw;
+  const int pos = static_cast<int>(r % s), bi = static_cast<int>(r / s);
+  const uint8_t* m = mask + static_cast<int64_t>(bi) * s * s;
+  uint32_t word = 0;
+  for (int j = 0; j < 32; ++j) {
+    const int x = 32 * w + j;
+    bool hid = true;
+    if (x < s) hid = (part == 0 ? m[static_cast<int64_t>(pos) * s + x] : m[static_cast<int64_t>(x) * s + pos]) != 0;
+    word |= static_cast<uint32_t>(hid) << j;
+  }
+  out[idx] = word;
+}
+
 }  // namespace
+
+hipError_t launch_attn_pack_mask(int b, int s, const uint8_t* mask, uint32_t* packed, hipStream_t stream) {
+  const int mw = (s + 31) / 32;
+  const int64_t words = 2 * static_cast<int64_t>(b) * s * mw;
+  if (words == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_pack_mask_kernel, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, stream,
+                     mask, packed, b, s, mw);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_fwd(const AttnProblem& p, hipStream_t stream) {
   AttnArgs a{};
@@ -1180,6 +1355,8 @@ hipError_t launch_attn_fwd(const AttnProblem& p, hipStream_t stream) {
   a.scale = 1.0f / sqrtf(static_cast<float>(p.dh));
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.qkv_shard_bytes = static_cast<uint32_t>(static_cast<int64_t>(p.s) * p.b * p.nh * 3 * p.dh * 2);
+  a.mask = p.mask;
+  a.mw = (p.s + 31) / 32;
   if (p.dh == 128)
     return p.causal ? launch_fwd_t<128, true>(a, p.dt, stream) : launch_fwd_t<128, false>(a, p.dt, stream);
   return p.causal ? launch_fwd_t<64, true>(a, p.dt, stream) : launch_fwd_t<64, false>(a, p.dt, stream);
@@ -1202,6 +1379,8 @@ hipError_t launch_attn_bwd(const AttnProblem& p, hipStream_t stream) {
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.qkv_shard_bytes = static_cast<uint32_t>(static_cast<int64_t>(p.s) * p.b * p.nh * 3 * p.dh * 2);
   a.o_shard_bytes = static_cast<uint32_t>(static_cast<int64_t>(p.s) * p.b * p.nh * p.dh * 2);
+  a.mask = p.mask;
+  a.mw = (p.s + 31) / 32;
   if (p.dh == 128)
     return p.causal ? launch_bwd_t<128, true>(a, p.dt, stream) : launch_bwd_t<128, false>(a, p.dt, stream);
   return p.causal ? launch_bwd_t<64, true>(a, p.dt, stream) : launch_bwd_t<64, false>(a, p.dt, stream);

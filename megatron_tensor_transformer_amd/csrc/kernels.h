@@ -97,6 +97,7 @@ int64_t sp_ln_bwd_row_blocks(int64_t s);
 struct AttnProblem {
   int dt, T, s, b, nh, dh;
   bool causal;
+  const uint32_t* mask;  // packed general mask (launch_attn_pack_mask), or null
   const void* qkv;   // [T][s·b][nh·3·dh]
   void* o;           // [T][s·b][nh·dh]
   float* lse;        // [T][b][nh][s]
@@ -105,6 +106,9 @@ struct AttnProblem {
   float* delta;      // backward workspace [T][b][nh][s]
 };
 hipError_t launch_attn_fwd(const AttnProblem& p, hipStream_t stream);
+// Byte mask [b][s][s] -> the packed form the attention kernels read:
+// 2·b·s·⌈s/32⌉ words (rows part, then columns part).
+hipError_t launch_attn_pack_mask(int b, int s, const uint8_t* mask, uint32_t* packed, hipStream_t stream);
 
 // Vocabulary-parallel cross-entropy of T resident shards (vocab_ce.hip).
 struct VocabProblem {

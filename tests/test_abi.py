@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 4
+    assert L.tpmlp_abi_version() == 5
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert L.tpmlp_status_string(s)
 
@@ -114,8 +114,8 @@ def test_attn_validation(L):
     p = ctypes.c_void_p(0x1000)
     z = ctypes.c_void_p(0)
 
-    def core(dt=1, t=2, s=64, b=2, nh=2, dh=128, causal=1, qkv=p, o=p, lse=p):
-        return L.tpmlp_attn_core_fwd(None, dt, t, s, b, nh, dh, causal, qkv, o, lse)
+    def core(dt=1, t=2, s=64, b=2, nh=2, dh=128, causal=1, qkv=p, o=p, lse=p, mask=None):
+        return L.tpmlp_attn_core_fwd(None, dt, t, s, b, nh, dh, causal, mask, qkv, o, lse)
     assert core(dt=4) == tp.ERR_DTYPE
     assert core(dh=96) == tp.ERR_SHAPE            # head_dim 64 or 128
     assert core(b=0) == tp.ERR_SHAPE
@@ -126,18 +126,33 @@ def test_attn_validation(L):
     assert core(o=ctypes.c_void_p(0x1008)) == tp.ERR_ALIGN
     assert core(s=0, qkv=z, o=z, lse=z) == 0     # empty sequence: nothing to do
     assert core(s=1 << 20, b=1 << 10) == tp.ERR_SHAPE
+    # a packed general mask: 4-byte aligned, one batch entry's part (s·⌈s/32⌉
+    # words) below 2^31 bytes
+    assert core(mask=ctypes.c_void_p(0x1002)) == tp.ERR_ALIGN
+    assert core(mask=p, s=1 << 17, b=1, nh=1, t=1) == tp.ERR_SHAPE
+    assert L.tpmlp_attn_mask_words(8, 1024) == 2 * 8 * 1024 * 32
+    assert L.tpmlp_attn_mask_words(3, 33) == 2 * 3 * 33 * 2
+    assert L.tpmlp_attn_mask_words(0, 33) == 0
+    assert L.tpmlp_attn_pack_mask(None, 0, 64, p, p) == tp.ERR_SHAPE
+    assert L.tpmlp_attn_pack_mask(None, 2, -1, p, p) == tp.ERR_SHAPE
+    assert L.tpmlp_attn_pack_mask(None, 2, 64, z, p) == tp.ERR_NULLPTR
+    assert L.tpmlp_attn_pack_mask(None, 2, 64, p, z) == tp.ERR_NULLPTR
+    assert L.tpmlp_attn_pack_mask(None, 2, 64, ctypes.c_void_p(0x1001), ctypes.c_void_p(0x1002)) == tp.ERR_ALIGN
+    assert L.tpmlp_attn_pack_mask(None, 2, 0, z, z) == 0
     # the backward's workspace is one fp32 δ per (shard, batch entry, head, row)
     assert L.tpmlp_attn_bwd_workspace_bytes(8, 1024, 8, 3) == 8 * 8 * 3 * 1024 * 4
     need = L.tpmlp_attn_bwd_workspace_bytes(2, 64, 2, 2)
-    assert L.tpmlp_attn_core_bwd(None, 1, 2, 64, 2, 2, 64, 1, p, p, p, p, p, p, need - 4) == tp.ERR_WORKSPACE
-    assert L.tpmlp_attn_core_bwd(None, 1, 2, 64, 2, 2, 64, 1, p, p, p, z, p, p, need) == tp.ERR_NULLPTR
+    assert L.tpmlp_attn_core_bwd(None, 1, 2, 64, 2, 2, 64, 1, None, p, p, p, p, p, p, need - 4) == tp.ERR_WORKSPACE
+    assert L.tpmlp_attn_core_bwd(None, 1, 2, 64, 2, 2, 64, 1, None, p, p, z, p, p, p, need) == tp.ERR_NULLPTR
     # the layer: d % 8 for bf16, weight-gradient pointers required
-    assert L.tpmlp_attn_fwd(None, 1, 64, 2, 36, 2, 64, 2, 1, p, p, p, p, p, p, p) == tp.ERR_ALIGN
-    assert L.tpmlp_attn_fwd(None, 1, 64, 2, 256, 2, 64, 2, 1, p, p, p, p, p, z, p) == tp.ERR_NULLPTR
+    assert L.tpmlp_attn_fwd(None, 1, 64, 2, 36, 2, 64, 2, 1, None, p, p, p, p, p, p, p) == tp.ERR_ALIGN
+    assert L.tpmlp_attn_fwd(None, 1, 64, 2, 256, 2, 64, 2, 1, None, p, p, p, p, p, z, p) == tp.ERR_NULLPTR
     args = [p] * 10
     # X, W_qkv, W_proj, QKV, O, lse, G | dO, dQKV, dW_qkv, dW_proj, dXp, ws, ws_bytes
-    assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, *args[:7], p, p, z, p, p, p, need) == tp.ERR_NULLPTR
-    assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, *args[:7], p, p, p, p, p, None, 0) == tp.ERR_WORKSPACE
+    assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, None, *args[:7], p, p, z, p, p, p,
+                            need) == tp.ERR_NULLPTR
+    assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, None, *args[:7], p, p, p, p, p, None,
+                            0) == tp.ERR_WORKSPACE
 
 
 def test_vocab_ce_validation(L):

@@ -14,7 +14,7 @@ import torch
 
 import megatron_tensor_transformer_amd as tp
 from oracle import attention as oa
-from tpmlp_inputs import CONFIGS, Tensor, attn_inputs, config_inputs, f32_to_bf16_bits, qkv_inputs
+from tpmlp_inputs import CONFIGS, Tensor, attn_inputs, attn_mask, config_inputs, f32_to_bf16_bits, qkv_inputs
 
 from gpu_util import dev, f64, relerr, say, shard_cols, shard_rows
 
@@ -29,29 +29,31 @@ def lse_err(gpu, ref):
 
 
 # ------------------------------------------------------------------ the core
-def run_core(inp, T, s, b, nh, dh, causal):
+def run_core(inp, T, s, b, nh, dh, causal, mask=None):
     qkv, do = dev(inp["qkv"]), dev(inp["do"])
+    m = None if mask is None else torch.from_numpy(mask).cuda()
     o = torch.empty((T, s * b, nh * dh), dtype=qkv.dtype, device="cuda")
     lse = torch.empty((T, b, nh, s), dtype=torch.float32, device="cuda")
-    tp.tpmlp_attn_core_fwd(qkv, o, lse, s, b, nh, dh, causal)
+    tp.tpmlp_attn_core_fwd(qkv, o, lse, s, b, nh, dh, causal, mask=m)
     dqkv = torch.empty_like(qkv)
     ws = torch.empty(max(tp.attn_bwd_workspace_bytes(T, s, b, nh), 4), dtype=torch.uint8, device="cuda")
-    tp.tpmlp_attn_core_bwd(qkv, o, lse, do, dqkv, ws, s, b, nh, dh, causal)
+    tp.tpmlp_attn_core_bwd(qkv, o, lse, do, dqkv, ws, s, b, nh, dh, causal, mask=m)
     torch.cuda.synchronize()
     return o, lse, dqkv
 
 
-def compare_core(T, s, b, nh, dh, causal, dtype, seed=0, inp=None):
-    say(f"[gpu] attention core {dtype} T={T} s={s} b={b} nh={nh} dh={dh} causal={causal}")
+def compare_core(T, s, b, nh, dh, causal, dtype, seed=0, inp=None, mask=None):
+    say(f"[gpu] attention core {dtype} T={T} s={s} b={b} nh={nh} dh={dh} causal={causal} "
+        f"mask={'none' if mask is None else 'general'}")
     if inp is None:
         inp = qkv_inputs(T, s, b, nh, dh, dtype=dtype, seed=seed)
-    o, lse, dqkv = run_core(inp, T, s, b, nh, dh, causal)
+    o, lse, dqkv = run_core(inp, T, s, b, nh, dh, causal, mask)
     tol = TOL[dtype]
     errs = {}
     for i in range(T):
         q, k, v = oa.split_heads(inp["qkv"].f64[i], s, b, nh, dh)
         do = oa.unmerge_heads(inp["do"].f64[i], s, b, nh, dh)
-        ro, A, rlse = oa.core_forward(q, k, v, causal)
+        ro, A, rlse = oa.core_forward(q, k, v, causal, None if mask is None else mask.astype(bool))
         dq, dk, dv = oa.core_backward(q, k, v, A, do)
         errs[f"o{i}"] = relerr(o[i], oa.merge_heads(ro))
         errs[f"dqkv{i}"] = relerr(dqkv[i], oa.merge_qkv(dq, dk, dv))
@@ -103,6 +105,57 @@ def test_core_bf16_growing_logits(causal):
     compare_core(T, s, b, nh, dh, causal, "bf16", inp=inp)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,s,b,nh,dh,causal,kind", [
+    (1, 5, 2, 2, 64, False, "random"),
+    (1, 70, 2, 1, 64, True, "padding"),     # padded query rows see no key
+    (2, 130, 3, 1, 128, False, "padding"),
+    (1, 130, 2, 2, 128, True, "random"),
+    (1, 257, 2, 1, 128, False, "random"),   # s % 4 != 0: byte-wise mask reads
+    (1, 256, 2, 2, 64, False, "random"),    # s % 4 == 0: word-wise mask reads
+])
+def test_core_general_mask(T, s, b, nh, dh, causal, kind, dtype):
+    """The general mask (BERT-style padding, or random entries), alone or with
+    the causal one, against the oracle's masked core; rows that see no key
+    must come out as o = 0, lse = −∞, no gradient."""
+    mask = attn_mask(b, s, kind, seed=s)
+    compare_core(T, s, b, nh, dh, causal, dtype, seed=1, mask=mask)
+
+
+@pytest.mark.parametrize("b,s", [(1, 1), (2, 33), (3, 64), (2, 100)])
+def test_pack_mask_bits(b, s):
+    """The packed mask against NumPy's bit packing of the same bytes: part 0
+    by query row, part 1 by key column (the transpose), positions past s set."""
+    m = attn_mask(b, s, "random", seed=b * 100 + s, p=0.4)
+    packed = tp.attn_pack_mask(torch.from_numpy(m).cuda())
+    torch.cuda.synchronize()
+    W = (s + 31) // 32
+    pad = np.ones((b, s, 32 * W), np.uint8)
+    rows, cols = pad.copy(), pad.copy()
+    rows[:, :, :s] = m != 0
+    cols[:, :, :s] = np.swapaxes(m, 1, 2) != 0
+    ref = np.stack([np.packbits(x, axis=-1, bitorder="little").view(np.uint32).reshape(b, s, W)
+                    for x in (rows, cols)])
+    assert np.array_equal(packed.cpu().numpy().view(np.uint32), ref)
+
+
+def test_core_rows_with_no_visible_key():
+    """Rows whose every key is hidden: exactly zero output and dq, lse = −∞."""
+    T, s, b, nh, dh = 1, 100, 2, 2, 128
+    mask = attn_mask(b, s, "random", seed=5, p=0.2)
+    mask[0, 7, :] = 1
+    mask[1, 64:70, :] = 1
+    inp = qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=2)
+    o, lse, dqkv = run_core(inp, T, s, b, nh, dh, False, mask)
+    o4 = f64(o).reshape(s, b, nh, dh)
+    dq4 = f64(dqkv).reshape(s, b, nh, 3, dh)[:, :, :, 0, :]
+    l4 = f64(lse)[0]
+    for bi, rows in ((0, [7]), (1, list(range(64, 70)))):
+        assert np.all(o4[rows, bi] == 0) and np.all(dq4[rows, bi] == 0)
+        assert np.all(np.isneginf(l4[bi][:, rows]))
+    assert np.all(np.isfinite(f64(dqkv)))
+
+
 def test_core_deterministic_bitwise():
     inp = qkv_inputs(2, 200, 2, 2, 128, dtype="bf16", seed=4)
     r1 = run_core(inp, 2, 200, 2, 2, 128, True)
@@ -129,27 +182,29 @@ def test_core_uniform_when_queries_vanish():
 
 
 # ------------------------------------------------------------------ the layer
-def run_layer(inp, s, b, heads, t, causal):
+def run_layer(inp, s, b, heads, t, causal, mask=None):
     X, Wq, Wp, G = (dev(inp[k]) for k in ("X", "Wqkv", "Wproj", "G"))
     dh = X.shape[1] // heads
+    m = None if mask is None else torch.from_numpy(mask).cuda()
     Wq_s, Wp_s = shard_cols(Wq, t), shard_rows(Wp, t)
-    QKV, O, lse, P = tp.attn_fwd(X, Wq_s, Wp_s, s, b, dh, causal)
+    QKV, O, lse, P = tp.attn_fwd(X, Wq_s, Wp_s, s, b, dh, causal, mask=m)
     Out = tp.reduce_partials(P)
-    dO, dQKV, dWqkv, dWproj, dXp = tp.attn_bwd(X, Wq_s, Wp_s, QKV, O, lse, G, s, b, dh, causal)
+    dO, dQKV, dWqkv, dWproj, dXp = tp.attn_bwd(X, Wq_s, Wp_s, QKV, O, lse, G, s, b, dh, causal, mask=m)
     dX = tp.reduce_partials(dXp)
     torch.cuda.synchronize()
     return dict(QKV=QKV, O=O, lse=lse, P=P, Out=Out, dO=dO, dQKV=dQKV, dWqkv=dWqkv, dWproj=dWproj, dXp=dXp, dX=dX)
 
 
-def compare_layer(s, b, d, heads, t, causal, dtype, seed=0):
+def compare_layer(s, b, d, heads, t, causal, dtype, seed=0, mask=None):
     # weights of std 1.2/√d give logits of std ≈ 1.4 (w²·d), as the 0.02
     # initialisation does at d = 3072; larger ones make the softmax one-hot
     # and the fp32 logits' rounding dominate the comparison
     say(f"[gpu] attention layer {dtype} s={s} b={b} d={d} heads={heads} t={t} causal={causal}")
     inp = attn_inputs(s, b, d, heads, dtype=dtype, seed=seed, x_std=1.0, w_std=1.2 / np.sqrt(d), g_std=1.0)
-    r = run_layer(inp, s, b, heads, t, causal)
+    r = run_layer(inp, s, b, heads, t, causal, mask)
     L = {k: v.f64 for k, v in inp.items()}
-    f = oa.tp_forward(L["X"], L["Wqkv"], L["Wproj"], t, s, b, heads, causal)
+    f = oa.tp_forward(L["X"], L["Wqkv"], L["Wproj"], t, s, b, heads, causal,
+                      mask=None if mask is None else mask.astype(bool))
     g = oa.tp_backward(L["X"], L["Wqkv"], L["Wproj"], f, L["G"])
     tol = TOL[dtype]
     errs = {"Out": relerr(r["Out"], f["Out"]), "dX": relerr(r["dX"], g["dX"])}
@@ -214,3 +269,10 @@ def test_gpt8p3b_attention_shard0_full():
     assert not bad, f"over {TOL['bf16']}: {bad}"
     del r
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_padding_mask(dtype):
+    """The layer with a BERT-style padding mask (non-causal), heads over 2 shards."""
+    s, b = 90, 3
+    compare_layer(s, b, 256, 4, 2, False, dtype, seed=3, mask=attn_mask(b, s, "padding", seed=9))
