@@ -285,6 +285,14 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a);
  * The attention dropout is not applied (the module on [SENSE] defaults it to
  * 0).
  *
+ * Biases ([TRAIN] ColumnParallelLinear / RowParallelLinear, as for the MLP):
+ * tpmlp_attn_fwd_bias adds the QKV column bias bqkv [t_local, 3w] (shard i's
+ * slice of b_qkv, path dtype, same alignment as the weights; NULL is NULLPTR)
+ * in the QKV GEMM's epilogue: QKV_i = X·W_qkv,i + bqkv_i.  The projection's
+ * bias is added once after the sum (tpmlp_reduce_partials_bias).  Their
+ * gradients are column sums (tpmlp_bias_grad): db_qkv,i = Σ_rows dQKV_i,
+ * db_proj = Σ_rows G.  The backward is unchanged.
+ *
  *   dt          TPMLP_BF16 (flash-attention kernels on the matrix cores, fp32
  *               softmax statistics) or TPMLP_F32 (fp32 throughout)
  *   s, b        sequence length (>= 0; 0 enqueues nothing) and batch (>= 1)
@@ -325,6 +333,10 @@ int tpmlp_attn_pack_mask(hipStream_t stream, int64_t b, int64_t s, const uint8_t
 int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
                    int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
                    const void* Wqkv, const void* Wproj, void* QKV, void* O, float* lse, void* P);
+int tpmlp_attn_fwd_bias(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                        int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                        const void* Wqkv, const void* Wproj, const void* bqkv, void* QKV, void* O, float* lse,
+                        void* P);
 size_t tpmlp_attn_bwd_workspace_bytes(int32_t t_local, int64_t s, int64_t b, int32_t heads_local);
 int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
                    int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,

@@ -64,6 +64,7 @@ SIGNATURES = {
     "tpmlp_bias_grad": (_I, [_P, _I, _I32, _I64, _I64, _P, _P, _P, _SZ]),
     "tpmlp_sp_workspace_bytes": (_SZ, [_I64, _I64]),
     "tpmlp_attn_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "tpmlp_attn_fwd_bias": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I] + [_P] * 9),
     "tpmlp_attn_bwd_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I32]),
     "tpmlp_attn_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I] + [_P] * 14 + [_SZ]),
     "tpmlp_attn_core_fwd": (_I, [_P, _I, _I32, _I64, _I64, _I32, _I32, _I, _P, _P, _P, _P]),
@@ -225,6 +226,16 @@ def tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, mask=
                                 _ptr(Wqkv), _ptr(Wproj), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(P)))
 
 
+def tpmlp_attn_fwd_bias(X, Wqkv, Wproj, bqkv, QKV, O, lse, P, s, b, head_dim, causal, mask=None, stream=None):
+    """tpmlp_attn_fwd with the QKV column bias bqkv [t, 3w] added in the QKV GEMM."""
+    t, d, w3 = Wqkv.shape
+    heads = w3 // 3 // head_dim
+    mp, _keep = _mask_ptr(mask, s, b, stream)
+    _check(lib().tpmlp_attn_fwd_bias(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), mp,
+                                     _ptr(X), _ptr(Wqkv), _ptr(Wproj), _ptr(bqkv), _ptr(QKV), _ptr(O), _ptr(lse),
+                                     _ptr(P)))
+
+
 def tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal,
                    mask=None, stream=None):
     t, d, w3 = Wqkv.shape
@@ -371,8 +382,8 @@ def attn_bwd_workspace_bytes(t, s, b, heads):
     return lib().tpmlp_attn_bwd_workspace_bytes(t, s, b, heads)
 
 
-def attn_fwd(X, Wqkv, Wproj, s, b, head_dim, causal=True, mask=None, stream=None):
-    """Allocating wrapper: returns QKV, O, lse, P."""
+def attn_fwd(X, Wqkv, Wproj, s, b, head_dim, causal=True, mask=None, stream=None, bqkv=None):
+    """Allocating wrapper: returns QKV, O, lse, P (bqkv [t, 3w]: the QKV bias)."""
     t, d, w3 = Wqkv.shape
     w = w3 // 3
     n = X.shape[0]
@@ -380,7 +391,10 @@ def attn_fwd(X, Wqkv, Wproj, s, b, head_dim, causal=True, mask=None, stream=None
     O = torch.empty((t, n, w), dtype=X.dtype, device=X.device)
     lse = torch.empty((t, b, w // head_dim, s), dtype=torch.float32, device=X.device)
     P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
-    tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, mask, stream)
+    if bqkv is None:
+        tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, mask, stream)
+    else:
+        tpmlp_attn_fwd_bias(X, Wqkv, Wproj, bqkv, QKV, O, lse, P, s, b, head_dim, causal, mask, stream)
     return QKV, O, lse, P
 
 

@@ -492,9 +492,14 @@ int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, 
   return hip_status(tpmlp::launch_attn_bwd(p, stream));
 }
 
-int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
-                   int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
-                   const void* Wqkv, const void* Wproj, void* QKV, void* O, float* lse, void* P) {
+}  // extern "C"
+
+namespace {
+
+// The shard forward with an optional QKV column bias bqkv [t_local, 3w] (NULL: none).
+int attn_fwd_impl(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                  int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                  const void* Wqkv, const void* Wproj, const void* bqkv, void* QKV, void* O, float* lse, void* P) {
   tpmlp::AttnProblem ap;
   int st = attn_core_problem(dt, t_local, s, b, heads_local, head_dim, causal, mask, ap);
   if (st) return st;
@@ -521,7 +526,10 @@ int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, 
   g1.sA = 0;
   g1.sB = d * 3 * w;
   g1.sC = n * 3 * w;
-  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+  g1.bias = bqkv;
+  g1.sBias = 3 * w;
+  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, bqkv != nullptr ? tpmlp::EPI_BIAS_STORE : tpmlp::EPI_STORE,
+                       stream));
   if (st) return st;
   ap.qkv = QKV;
   ap.o = O;
@@ -544,6 +552,27 @@ int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, 
   g2.sB = w * d;
   g2.sC = n * d;
   return hip_status(gemm(dt, g2, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpmlp_attn_fwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                   int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                   const void* Wqkv, const void* Wproj, void* QKV, void* O, float* lse, void* P) {
+  return attn_fwd_impl(stream, dt, s, b, d, heads_local, head_dim, t_local, causal, mask, X, Wqkv, Wproj, nullptr,
+                       QKV, O, lse, P);
+}
+
+int tpmlp_attn_fwd_bias(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,
+                        int32_t head_dim, int32_t t_local, int causal, const uint32_t* mask, const void* X,
+                        const void* Wqkv, const void* Wproj, const void* bqkv, void* QKV, void* O, float* lse,
+                        void* P) {
+  if (bqkv == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(bqkv, dt == TPMLP_BF16 ? 16 : 4)) return TPMLP_ERR_ALIGN;
+  return attn_fwd_impl(stream, dt, s, b, d, heads_local, head_dim, t_local, causal, mask, X, Wqkv, Wproj, bqkv,
+                       QKV, O, lse, P);
 }
 
 int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, int32_t heads_local,

@@ -431,13 +431,14 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
     const int64_t cbase = static_cast<int64_t>(batch) * a.sC;
     const int qm0 = m0 + wm * 128, qn0 = n0 + wn * 64;
     constexpr bool ZY = EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY;
+    constexpr bool BIAS = EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE;
     constexpr int PASSES = ZY ? 2 : 1;
-    // column bias (EPI_BIAS_GELU_ZY): the wave's 64 bias values are staged
+    // column bias (EPI_BIAS_GELU_ZY, EPI_BIAS_STORE): the wave's 64 bias values are staged
     // in LDS past the eight staging regions and read back per row block, so
     // they hold no registers across the passes (N is a multiple of 8, so a
     // 4-column group is inside N whenever its first column is)
     const uint32_t bbase = lds_base + NWAVE * QBYTES + wave * 128;
-    if constexpr (EPI == EPI_BIAS_GELU_ZY) {
+    if constexpr (BIAS) {
       if (lane < 16) {
         const int col = qn0 + lane * 4;
         const bf16* bias = a.bias + static_cast<int64_t>(batch) * a.sBias;
@@ -469,7 +470,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 #pragma unroll
       for (int i = 0; i < FA; ++i) {
         i32x2 zr[FB][4];
-        if constexpr (EPI == EPI_BIAS_GELU_ZY) {
+        if constexpr (BIAS) {
 #pragma unroll
           for (int j = 0; j < FB; ++j)
 #pragma unroll
@@ -501,7 +502,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
           float v[16];
 #pragma unroll
           for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[i][j][e]));
-          if constexpr (EPI == EPI_BIAS_GELU_ZY) {
+          if constexpr (BIAS) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const bf16x4 bq = __builtin_bit_cast(bf16x4, zr[j][q]);
@@ -665,6 +666,8 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
     return launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY>(g, stream);
   if (same && is(k0, KMAJ, MNMAJ, EPI_STORE))
     return launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE>(g, stream);
+  if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_STORE))
+    return launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_BIAS_STORE>(g, stream);
   if (same && is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))
     return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
   if (same && is(k0, KMAJ, KMAJ, EPI_STORE))

@@ -90,8 +90,9 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(F32Args a) {
       if (col >= a.N) continue;
       const int64_t off = cb + static_cast<int64_t>(row) * a.ldc + col;
       float x = acc[i][j];
-      if constexpr (EPI == EPI_BIAS_GELU_ZY) x += a.bias[static_cast<int64_t>(batch) * a.sBias + col];
-      if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_F32) {
+      if constexpr (EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE)
+        x += a.bias[static_cast<int64_t>(batch) * a.sBias + col];
+      if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_F32 || EPI == EPI_BIAS_STORE) {
         a.C[off] = x;
       } else if constexpr (EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY) {
         a.C[off] = x;
@@ -140,6 +141,8 @@ hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int e
     return launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY>(k, p.batch, stream);
   if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_STORE)
     return launch_t<KMAJ, MNMAJ, EPI_STORE>(k, p.batch, stream);
+  if (a_order == KMAJ && b_order == MNMAJ && epi == EPI_BIAS_STORE)
+    return launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE>(k, p.batch, stream);
   if (a_order == KMAJ && b_order == KMAJ && epi == EPI_GELU_GRAD)
     return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD>(k, p.batch, stream);
   if (a_order == KMAJ && b_order == KMAJ && epi == EPI_STORE)

@@ -19,7 +19,8 @@ enum Epilogue {
   EPI_STORE_F32 = 1,  // C = acc as fp32 (weight gradients)
   EPI_GELU_ZY = 2,    // C = acc (Z), C2 = GeLU(acc) (Y)
   EPI_GELU_GRAD = 3,  // C = acc ⊙ GeLU'(Zin) (D)
-  EPI_BIAS_GELU_ZY = 4  // z = acc + bias[col]: C = z (Z), C2 = GeLU(z) (Y)
+  EPI_BIAS_GELU_ZY = 4,  // z = acc + bias[col]: C = z (Z), C2 = GeLU(z) (Y)
+  EPI_BIAS_STORE = 5     // C = acc + bias[col] (dtype of the path)
 };
 
 struct GemmProblem {
@@ -30,7 +31,7 @@ struct GemmProblem {
   void* C;
   void* C2;          // EPI_GELU_ZY: Y
   const void* Zin;   // EPI_GELU_GRAD: stored Z, same layout as C
-  const void* bias;  // EPI_BIAS_GELU_ZY: [N] per batch entry, path dtype
+  const void* bias;  // EPI_BIAS_GELU_ZY / EPI_BIAS_STORE: [N] per batch entry, path dtype
   int64_t sBias;     // its per-batch stride in elements
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;  // per-batch strides in elements (0 = shared operand)

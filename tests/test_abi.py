@@ -147,6 +147,10 @@ def test_attn_validation(L):
     # the layer: d % 8 for bf16, weight-gradient pointers required
     assert L.tpmlp_attn_fwd(None, 1, 64, 2, 36, 2, 64, 2, 1, None, p, p, p, p, p, p, p) == tp.ERR_ALIGN
     assert L.tpmlp_attn_fwd(None, 1, 64, 2, 256, 2, 64, 2, 1, None, p, p, p, p, p, z, p) == tp.ERR_NULLPTR
+    # the biased forward: the QKV bias is required and aligned like the weights
+    assert L.tpmlp_attn_fwd_bias(None, 1, 64, 2, 256, 2, 64, 2, 1, None, p, p, p, z, p, p, p, p) == tp.ERR_NULLPTR
+    assert L.tpmlp_attn_fwd_bias(None, 1, 64, 2, 256, 2, 64, 2, 1, None, p, p, p, ctypes.c_void_p(0x1008), p, p, p,
+                                 p) == tp.ERR_ALIGN
     args = [p] * 10
     # X, W_qkv, W_proj, QKV, O, lse, G | dO, dQKV, dW_qkv, dW_proj, dXp, ws, ws_bytes
     assert L.tpmlp_attn_bwd(None, 1, 64, 2, 256, 2, 64, 2, 1, None, *args[:7], p, p, z, p, p, p,

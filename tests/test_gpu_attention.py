@@ -276,3 +276,40 @@ def test_layer_padding_mask(dtype):
     """The layer with a BERT-style padding mask (non-causal), heads over 2 shards."""
     s, b = 90, 3
     compare_layer(s, b, 256, 4, 2, False, dtype, seed=3, mask=attn_mask(b, s, "padding", seed=9))
+
+
+@pytest.mark.parametrize("dtype,causal", [("f32", True), ("bf16", True), ("bf16", False)])
+def test_layer_with_biases(dtype, causal):
+    """QKV bias in the QKV GEMM's epilogue (tpmlp_attn_fwd_bias), the
+    projection bias after the sum (tpmlp_reduce_partials_bias), and both bias
+    gradients as column sums (tpmlp_bias_grad), against the oracle's biased
+    layer."""
+    s, b, d, heads, t = 70, 2, 256, 4, 2
+    say(f"[gpu] attention layer with biases {dtype} causal={causal}")
+    inp = attn_inputs(s, b, d, heads, dtype=dtype, seed=4, x_std=1.0, w_std=1.2 / np.sqrt(d), g_std=1.0,
+                      bias_std=0.5)
+    X, Wq, Wp, G = (dev(inp[k]) for k in ("X", "Wqkv", "Wproj", "G"))
+    bq, bp = dev(inp["bqkv"]), dev(inp["bproj"])
+    dh = d // heads
+    Wq_s, Wp_s = shard_cols(Wq, t), shard_rows(Wp, t)
+    bq_s = bq.reshape(t, 3 * d // t).contiguous()
+    QKV, O, lse, P = tp.attn_fwd(X, Wq_s, Wp_s, s, b, dh, causal, bqkv=bq_s)
+    Out = tp.reduce_partials_bias(P, bp)
+    dO, dQKV, dWqkv, dWproj, dXp = tp.attn_bwd(X, Wq_s, Wp_s, QKV, O, lse, G, s, b, dh, causal)
+    dX = tp.reduce_partials(dXp)
+    dbq = tp.bias_grad(dQKV)
+    dbp = tp.bias_grad(G)
+    torch.cuda.synchronize()
+    L = {k: v.f64 for k, v in inp.items()}
+    f = oa.tp_forward(L["X"], L["Wqkv"], L["Wproj"], t, s, b, heads, causal, bqkv=L["bqkv"], bproj=L["bproj"])
+    g = oa.tp_backward(L["X"], L["Wqkv"], L["Wproj"], f, L["G"])
+    errs = {"Out": relerr(Out, f["Out"]), "dX": relerr(dX, g["dX"]), "dbproj": relerr(dbp, g["dbproj"])}
+    for i in range(t):
+        errs[f"QKV{i}"] = relerr(QKV[i], f["shards"][i]["QKV"])
+        errs[f"dQKV{i}"] = relerr(dQKV[i], g["shards"][i]["dQKV"])
+        errs[f"dbqkv{i}"] = relerr(dbq[i], g["shards"][i]["dbqkv"])
+        errs[f"dWqkv{i}"] = relerr(dWqkv[i], g["shards"][i]["dWqkv"])
+    tol = TOL[dtype]
+    bad = {k: e for k, e in errs.items() if not (e <= tol)}
+    say(f"[gpu] attention layer with biases: worst {max(errs.values()):.3e}")
+    assert not bad, f"over {tol}: {bad}"
