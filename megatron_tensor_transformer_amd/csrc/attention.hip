@@ -1,7 +1,8 @@
 // Core of the tensor-parallel self-attention shard: per (shard, batch entry,
-// head), S = q·kᵀ/√dh with an optional causal mask, A = softmax(S) row by row,
-// o = A·v ([TRAIN] Attention 层 section; the causal mask is the implicit one of
-// [EFF] §4.2's fused softmax), and its backward
+// head), S = q·kᵀ/√dh with an optional causal mask and an optional general
+// mask, A = softmax(S) row by row, o = A·v ([TRAIN] Attention 层 section; the
+// causal mask is the implicit one of [EFF] §4.2's fused softmax, the general
+// one that section's other kernel, e.g. BERT's padding mask), and its backward
 //   dv = Aᵀ·do,  dS = A ⊙ (do·vᵀ − δ),  δ_i = Σ_j A_ij (do_i·v_j) = do_i·o_i,
 //   dq = dS·k/√dh,  dk = dSᵀ·q/√dh.
 // The heads of a shard are the contiguous column groups of the column-parallel
@@ -25,6 +26,12 @@
 // tile's keys (the one the S accumulators already hold); the V fragments are
 // read with the same permutation through the transposing LDS read, so no
 // register shuffle is needed.
+//
+// LDS fragment reads are explicit inline asm, issued ahead of their MFMAs and
+// waited for with counted waits; one barrier per key (or query) tile.  A
+// general mask arrives bit-packed once per batch (by query row for the
+// forward and dq, by key column for dk/dv); a lane reads one word per 32
+// positions a tile ahead, and a wave skips tiles it cannot see at all.
 //
 // fp32 path (correctness reference, not tuned): one thread per query row
 // (forward, dq) or key row (dk, dv), online softmax in fp32.
@@ -141,48 +148,6 @@ __device__ __forceinline__ void load_tile(i32x4 rsrc, TPMLP_LDS char* tile, int 
   }
 }
 
-// MFMA operand with rows = tile rows: lane L gets row `row`, elements
-// 8·chunk' .. +7 where chunk' = 2c + L/32 for k16 slice c.
-template <int DH>
-__device__ __forceinline__ bf16x8 frag_rows(const TPMLP_LDS char* tile, int row, int chunk) {
-  return *(const TPMLP_LDS bf16x8*)(tile + kv_slot<DH>(row, chunk));
-}
-
-// MFMA operands with rows = tile columns 32d .. 32d+31 (d < ND) and k = 16
-// tile rows of block (u, c2) in the accumulators' order: lane L gets column
-// 32d + L%32, rows 32u + 16c2 + 4·(L/32) + {0..3} then the same + 8.  The
-// transposing reads are inline asm (the builtin form made the compiler wait
-// for every outstanding buffer→LDS load first, and its element-wise
-// assembly into bf16x8 was miscompiled), followed by one explicit LDS wait;
-// the results are operands of the wait so no use can move above it.
-template <int DH, int ND>
-__device__ __forceinline__ void frag_tr(const TPMLP_LDS char* tile, int u, int c2, int lane, bf16x8 (&out)[ND]) {
-  const int g = lane >> 4, i = lane & 15;
-  const int r = 32 * u + 16 * c2 + 4 * (lane >> 5) + (i >> 2);
-  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tile));
-  i32x2 t[2 * ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const int col = 32 * d + 16 * (g & 1) + 4 * (i & 3);
-    const uint32_t a0 = base + kv_slot<DH>(r, col >> 3) + (col & 7) * 2;
-    const uint32_t a1 = base + kv_slot<DH>(r + 8, col >> 3) + (col & 7) * 2;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(t[2 * d]) : "v"(a0) : "memory");
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(t[2 * d + 1]) : "v"(a1) : "memory");
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0])::"memory");
-#pragma unroll
-  for (int k = 1; k < 2 * ND; ++k) asm volatile("" : "+v"(t[k]));
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    i32x4 w;
-    w[0] = t[2 * d][0];
-    w[1] = t[2 * d][1];
-    w[2] = t[2 * d + 1][0];
-    w[3] = t[2 * d + 1][1];
-    out[d] = __builtin_bit_cast(bf16x8, w);
-  }
-}
-
 // Workgroup barrier that is also a compiler barrier for memory accesses (LDS
 // reads must not move above it).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -296,36 +261,18 @@ __device__ __forceinline__ void tr_addrs(uint32_t base, int lane, uint32_t (&o)[
   }
 }
 
-// The ND transposed fragments of block (u, c2) at byte offset IMM (stage,
-// tile and block) from the precomputed addresses; one explicit LDS wait.
-template <int DH, int ND, int IMM>
-__device__ __forceinline__ void frag_tr_at(const uint32_t (&ad)[2 * ND], bf16x8 (&out)[ND]) {
-  // the instruction's offset field has 16 bits: a larger IMM moves its high
-  // part into the address
-  constexpr uint32_t HI = (static_cast<uint32_t>(IMM) >> 16) << 16, LO = IMM - HI;
-  i32x2 t[2 * ND];
-#pragma unroll
-  for (int k = 0; k < 2 * ND; ++k)
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(t[k]) : "v"(ad[k] + HI), "i"(LO) : "memory");
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0])::"memory");
-#pragma unroll
-  for (int k = 1; k < 2 * ND; ++k) asm volatile("" : "+v"(t[k]));
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    i32x4 w;
-    w[0] = t[2 * d][0];
-    w[1] = t[2 * d][1];
-    w[2] = t[2 * d + 1][0];
-    w[3] = t[2 * d + 1][1];
-    out[d] = __builtin_bit_cast(bf16x8, w);
-  }
-}
-
-// Split form of frag_tr_at for software pipelining: issue the 2·ND reads of a
-// block into t (no wait), then tr_wait<N> once at most N newer LDS reads may
-// still be in flight, then tr_frags.  Only LDS reads issued here are in flight
-// in the code that uses these (the compiler's own LDS loads of the step have
-// been waited for before), so the count is exact.
+// Transposed MFMA operands of one 16-row block at byte offset IMM (stage,
+// tile and block) from the per-lane addresses of tr_addrs: lane L gets
+// columns 32d + L%32 (d < ND), rows 4·(L/32) + {0..3} then the same + 8, the
+// accumulators' key order.  Software-pipelined in three parts: tr_issue
+// sends the 2·ND reads of a block (no wait), tr_wait<N> waits until at most N
+// newer LDS operations are in flight (LDS completes in order, so every read
+// issued before those N is done; other LDS operations only make the wait more
+// conservative), and tr_frags assembles the operands.  The reads are inline
+// asm: the transposing-read builtin made the compiler wait for every
+// outstanding buffer→LDS load before it, and its element-wise assembly into
+// bf16x8 was miscompiled (only the first dword survived).  The offset field
+// has 16 bits: a larger IMM moves its high part into the address.
 template <int DH, int ND, int IMM>
 __device__ __forceinline__ void tr_issue(const uint32_t (&ad)[2 * ND], i32x2 (&t)[2 * ND]) {
   constexpr uint32_t HI = (static_cast<uint32_t>(IMM) >> 16) << 16, LO = IMM - HI;
