@@ -135,7 +135,7 @@ def test_nan_propagates_to_its_row_only():
 
 
 # ------------------------------------------------------------------ full-size, sampled
-def _sampled_check(inp, t, shards, rng_seed, n_rows, n_cols, label):
+def _sampled_check(inp, t, shards, rng_seed, n_rows, n_cols, label, last_rows=0):
     """Full-size GPU run; the oracle computes sampled rows (tokens) and sampled
     hidden columns one by one: rows of O, Z_i, Y_i, P_i, D_i, dX_i, dX depend
     only on the same rows of X and G; columns H of A_i give D_i[:, H],
@@ -151,6 +151,8 @@ def _sampled_check(inp, t, shards, rng_seed, n_rows, n_cols, label):
     mi = A_s.shape[2]
     rng = np.random.default_rng(rng_seed)
     rows = np.sort(rng.choice(n, size=min(n_rows, n), replace=False))
+    if last_rows:
+        rows = np.union1d(rows, np.arange(n - last_rows, n))
     Xf, Gf = inp["X"].f32, inp["G"].f32
     Af = inp["A"].f32
     Bf = inp["B"].f32
@@ -190,3 +192,16 @@ def test_gpt8p3b_shard_config_sampled():
 def test_gpt1t_shard_config_sampled():
     """h = 25600, m = 4h, t = 8 -> one shard A_0 25600×12800, B_0 12800×25600, n = 2048."""
     _sampled_check(config_inputs("gpt1t_t8_shard0", seed=0), 8, 1, 1, 12, 24, "1T-shaped, shard 0")
+
+
+def test_largest_operand_sampled():
+    """Operands at the size limit: X, G, P, dX_i of n = 262136 rows × d = 4096
+    bf16 are 2^31 − 65536 bytes, just under the 2^31-byte bound of the 32-bit
+    buffer offsets (m_i = 64, one shard, so the GEMMs stay small).  Sampled
+    rows and hidden columns as for the full-size configurations; the last
+    rows are always among the samples (the offsets nearest the bound)."""
+    n, d, m = 262136, 4096, 64
+    assert n * d * 2 == (1 << 31) - 65536
+    say(f"[gpu] largest operands: drawing n={n} d={d} m={m}")
+    inp = mlp_inputs(n, d, m, 1, dtype="bf16", seed=11)
+    _sampled_check(inp, 1, 1, 5, 40, 4, "largest operands", last_rows=4)
