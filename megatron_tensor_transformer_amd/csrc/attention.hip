@@ -100,26 +100,37 @@ struct AttnArgs {
   int mw;                // words per position, ⌈s/32⌉
 };
 
-// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.  The
-// logical order (shard, batch entry, head, block) is mapped so that each XCD
-// runs a contiguous range of it: the blocks of one head, which read the same
-// K/V (or Q/dO) panel, share an L2.
-__device__ __forceinline__ int xcd_logical(int total) {
-  int begin, count;
-  xcd_range(total, static_cast<int>(blockIdx.x & 7), begin, count);
-  return begin + static_cast<int>(blockIdx.x >> 3);
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+// Workgroup -> (shard, batch entry, head) and block position p (0 = the most
+// work): each XCD keeps the blocks of a contiguous run of heads (shared K/V or
+// Q/dO panels in its L2).  Causal blocks differ in length, so heavy_first_block
+// starts all the run's longest blocks first and the short ones fill in behind
+// them; without the causal mask they are alike and go head by head (a head's
+// blocks run together and share its panel while it is in the L2).
+template <bool CAUSAL>
+__device__ __forceinline__ void attn_block(int nh, int b, int nblk, int& T, int& bi, int& h, int& p) {
+  int flat;
+  if constexpr (CAUSAL) {
+    heavy_first_block(static_cast<int>(gridDim.x) / nblk, nblk, static_cast<int>(blockIdx.x), flat, p);
+  } else {
+    int begin, count;
+    xcd_range(static_cast<int>(gridDim.x), static_cast<int>(blockIdx.x & 7), begin, count);
+    const int x = begin + static_cast<int>(blockIdx.x >> 3);
+    flat = x / nblk;
+    p = x - flat * nblk;
+  }
+  h = flat % nh;
+  flat /= nh;
+  bi = flat % b;
+  T = flat / b;
 }
 
-// Workgroup -> (shard, batch entry, head, query block); the longest causal
-// blocks (last in the sequence) come first within a head.
+// Forward: the longest causal query blocks are the last in the sequence.
+template <bool CAUSAL>
 __device__ __forceinline__ void attn_coords(const AttnArgs& a, int& T, int& bi, int& h, int& qb) {
-  const int x = xcd_logical(static_cast<int>(gridDim.x));
-  qb = a.nqb - 1 - (x % a.nqb);
-  int r = x / a.nqb;
-  h = r % a.nh;
-  r /= a.nh;
-  bi = r % a.b;
-  T = r / a.b;
+  int p;
+  attn_block<CAUSAL>(a.nh, a.b, a.nqb, T, bi, h, p);
+  qb = a.nqb - 1 - p;
 }
 
 // DMA of one [AKV][DH] tile: rows j·AKV .. +63 of a token-major tensor whose
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
   int T, bi, h, qb;
-  attn_coords(a, T, bi, h, qb);
+  attn_coords<CAUSAL>(a, T, bi, h, qb);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
   const int q0 = qb * AQ + wave * 32;
@@ -676,12 +687,9 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int NI = TILE / 1024 / 4;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
-  const int x = xcd_logical(static_cast<int>(gridDim.x));
-  const int qb = a.nqb - 1 - (x % a.nqb);
-  int r = x / a.nqb;
-  const int h = r % a.nh;
-  r /= a.nh;
-  const int bi = r % a.b, T = r / a.b;
+  int T, bi, h, p;
+  attn_block<CAUSAL>(a.nh, a.b, a.nqb, T, bi, h, p);
+  const int qb = a.nqb - 1 - p;  // the last query blocks see the most keys
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
   const int q0 = qb * AQ + wave * 32, qrow = q0 + r32;
@@ -872,12 +880,8 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][AKV];  // [stage][lse·log2(e) | δ][row]
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
-  const int x = xcd_logical(static_cast<int>(gridDim.x));
-  const int kb_idx = x % a.nqb;  // key block (the first ones have the most query blocks)
-  int r = x / a.nqb;
-  const int h = r % a.nh;
-  r /= a.nh;
-  const int bi = r % a.b, T = r / a.b;
+  int T, bi, h, kb_idx;
+  attn_block<CAUSAL>(a.nh, a.b, a.nqb, T, bi, h, kb_idx);  // the first key blocks see the most query blocks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
   const int k0 = kb_idx * AQ + wave * 32, krow = k0 + r32;

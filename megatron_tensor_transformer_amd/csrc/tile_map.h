@@ -64,4 +64,36 @@ __host__ __device__ inline void map_workgroup(const XcdSplit& s, int t0, int wg,
   }
 }
 
+// Attention launches: `heads` independent sequences of `nblk` blocks each, in
+// the logical order head by head; block position p (0 = the most work, e.g.
+// the last causal query block) of head h is logical index h·nblk + p.  XCD x
+// keeps its contiguous range of that order (a head's blocks read the same
+// K/V or Q/dO panel, so they share its L2), but runs it position-major: all
+// its heads' position-0 blocks first, then position 1, ...  so the longest
+// blocks start first and the short ones fill in behind them.  wg -> (head, p).
+__host__ __device__ inline void heavy_first_block(int heads, int nblk, int wg, int& head, int& p) {
+  const int total = heads * nblk;
+  int begin, count;
+  xcd_range(total, wg & 7, begin, count);
+  const int local = wg >> 3;
+  const int last = begin + count - 1;
+  const int h_first = begin / nblk, p_first = begin - h_first * nblk;
+  const int h_last = last / nblk, p_last = last - h_last * nblk;
+  const int H = h_last - h_first + 1;
+  // Blocks at positions < P in the range: every head of the run has one at
+  // each position, except the first head before p_first and the last head
+  // after p_last.  Monotone in P: the position of `local` by bisection.
+  auto before = [&](int P) {
+    return P * H - (P < p_first ? P : p_first) - (P - p_last - 1 > 0 ? P - p_last - 1 : 0);
+  };
+  int lo = 0, hi = nblk - 1;  // largest P with before(P) <= local
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (before(mid) <= local) lo = mid;
+    else hi = mid - 1;
+  }
+  p = lo;
+  head = (p >= p_first ? h_first : h_first + 1) + (local - before(p));
+}
+
 }  // namespace tpmlp

@@ -75,3 +75,52 @@ def test_map_is_a_bijection(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout[-2000:]
     assert "bad 0" in run.stdout
+
+
+HEAVY_FIRST = r"""
+#include "tile_map.h"
+#include <cstdio>
+#include <vector>
+int main() {
+  int bad = 0, cases = 0;
+  for (int heads : {1, 2, 3, 7, 8, 9, 24, 100, 192, 193})
+    for (int nblk : {1, 2, 3, 5, 8, 9, 16}) {
+      const int total = heads * nblk;
+      ++cases;
+      std::vector<int> seen(total, 0);
+      std::vector<int> prev_p(8, -1);
+      for (int wg = 0; wg < total; ++wg) {
+        int h, p;
+        tpmlp::heavy_first_block(heads, nblk, wg, h, p);
+        if (h < 0 || h >= heads || p < 0 || p >= nblk) { ++bad; continue; }
+        const int logical = h * nblk + p;
+        ++seen[logical];
+        // the block lies in the XCD's own contiguous range ...
+        int begin, count;
+        tpmlp::xcd_range(total, wg & 7, begin, count);
+        if (logical < begin || logical >= begin + count) ++bad;
+        // ... and each XCD sees its positions in non-decreasing order
+        if (p < prev_p[wg & 7]) ++bad;
+        prev_p[wg & 7] = p;
+      }
+      for (int v : seen) bad += v != 1;
+    }
+  std::printf("%d %d\n", cases, bad);
+  return 0;
+}
+"""
+
+
+def test_heavy_first_block_order(tmp_path):
+    """Attention block order: a bijection onto (head, position); every block
+    stays in its XCD's contiguous range of the head-major order; within an XCD
+    the positions (0 = most work) come in non-decreasing order."""
+    src = tmp_path / "hf.cpp"
+    src.write_text(HEAVY_FIRST)
+    exe = tmp_path / "hf"
+    r = subprocess.run(["hipcc", "--offload-arch=gfx950", "-O2", "-std=c++17", f"-I{CSRC}", str(src), "-o",
+                        str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True, timeout=60).stdout.split()
+    cases, bad = int(out[0]), int(out[1])
+    assert cases == 70 and bad == 0
