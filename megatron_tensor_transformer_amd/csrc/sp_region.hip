@@ -14,10 +14,11 @@
 //
 // All kernels are HBM-bound and work on 8-element (16-B bf16) chunks; sums of
 // the t partials load them in unconditional groups so the loads are in flight
-// together, and add them in shard order.  The LN kernels work row by row in
-// 512-thread blocks (h ≤ 4096: thread j owns chunk j of every row, held in
-// registers) and reduce with cross-lane shuffles plus a fixed-order sum over
-// the 8 waves.  In LN backward each block walks a strided set of rows,
+// together, and add them in shard order.  LN forward gives each row one wave
+// (h ≤ 4096: at most 8 chunks per lane, in registers) and reduces with
+// cross-lane shuffles.  LN backward works in 512-thread blocks (thread j owns
+// chunk j of every row) with shuffles plus a fixed-order sum over the 8
+// waves; each block walks a strided set of rows,
 // so its dγ/dβ column partials stay in registers; the sums are deterministic:
 // per-block partials in a fixed row order, then a fixed-order sum over blocks.
 //
@@ -182,59 +183,67 @@ __device__ __forceinline__ void block_sum2(float (&v)[2], float (*red)[2], int l
   }
 }
 
+// LN forward: one wave per row (h ≤ 4096: at most 8 16-B chunks per lane, all
+// loaded before the first use, so a wave keeps 8 KB in flight); mean and
+// variance are wave sums in a fixed lane order (butterfly), no LDS or barrier.
 template <typename T>
-__global__ __launch_bounds__(LNB_THREADS) void ln_fwd_kernel(SpProblem p) {
-  __shared__ float red[2][LNB_WAVES][2];  // one buffer per reduction: no barrier between them
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = threadIdx.x;
-  const bool mine = c < p.h / 8;
-  const int64_t r0 = 2 * static_cast<int64_t>(blockIdx.x);
-  const bool two = r0 + 1 < p.s;
-  const T* x0 = static_cast<const T*>(p.x) + r0 * p.h + c * 8;
-  const T* x1 = two ? x0 + p.h : x0;  // a missing second row re-reads the first; dropped below
-  float v[2][8], g[8], b[8];
-  if (mine) {
-    load8(x0, v[0]);
-    load8(x1, v[1]);
-    load8<T, false>(static_cast<const T*>(p.gamma) + c * 8, g);
-    load8<T, false>(static_cast<const T*>(p.beta) + c * 8, b);
-  } else {
+__global__ __launch_bounds__(SP_THREADS) void ln_fwd_kernel(SpProblem p) {
+  constexpr int MAXC = 8;  // chunks per lane for h ≤ 4096
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (SP_THREADS / WAVE) + (threadIdx.x >> 6);
+  if (row >= p.s) return;
+  const int hc = p.h / 8;
+  const T* xr = static_cast<const T*>(p.x) + row * p.h;
+  float v[MAXC][8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[0][k] = v[1][k] = 0.f;
+  for (int k = 0; k < MAXC; ++k) {
+    const int c = lane + WAVE * k;
+    if (c < hc) {
+      load8(xr + c * 8, v[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
+    }
   }
   const float inv_h = 1.0f / static_cast<float>(p.h);
-  float s[2] = {0.f, 0.f};
+  float sum = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    s[0] += v[0][k];
-    s[1] += v[1][k];
-  }
-  block_sum2(s, red[0], lane, wave);
-  const float mean[2] = {s[0] * inv_h, s[1] * inv_h};
-  float q[2] = {0.f, 0.f};
-  if (mine) {
+  for (int k = 0; k < MAXC; ++k)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float d0 = v[0][k] - mean[0], d1 = v[1][k] - mean[1];
-      q[0] += d0 * d0;
-      q[1] += d1 * d1;
+    for (int e = 0; e < 8; ++e) sum += v[k][e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, WAVE);
+  const float mean = sum * inv_h;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXC; ++k) {
+    if (lane + WAVE * k < hc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[k][e] - mean;
+        q += d * d;
+      }
     }
   }
-  block_sum2(q, red[1], lane, wave);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    if (r == 1 && !two) break;
-    const float rstd = 1.0f / sqrtf(q[r] * inv_h + p.eps);
-    if (mine) {
-      float o[8];
+  for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o, WAVE);
+  const float rstd = 1.0f / sqrtf(q * inv_h + p.eps);
+  T* yr = static_cast<T*>(p.ln_out) + row * p.h;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = fmaf((v[r][k] - mean[r]) * rstd, g[k], b[k]);
-      store8(static_cast<T*>(p.ln_out) + (r0 + r) * p.h + c * 8, o);
+  for (int k = 0; k < MAXC; ++k) {
+    const int c = lane + WAVE * k;
+    if (c < hc) {
+      float g[8], b[8], o[8];
+      load8<T, false>(static_cast<const T*>(p.gamma) + c * 8, g);
+      load8<T, false>(static_cast<const T*>(p.beta) + c * 8, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf((v[k][e] - mean) * rstd, g[e], b[e]);
+      store8(yr + c * 8, o);
     }
-    if (threadIdx.x == 0) {
-      p.mean[r0 + r] = mean[r];
-      p.rstd[r0 + r] = rstd;
-    }
+  }
+  if (lane == 0) {
+    p.mean[row] = mean;
+    p.rstd[row] = rstd;
   }
 }
 
@@ -402,8 +411,8 @@ template <typename T>
 hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
   switch (p.phase) {
     case 0: {
-      const int64_t blocks = (p.s + 1) / 2;
-      hipLaunchKernelGGL((ln_fwd_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(LNB_THREADS), 0, stream,
+      const int64_t blocks = (p.s + SP_THREADS / WAVE - 1) / (SP_THREADS / WAVE);  // one wave per row
+      hipLaunchKernelGGL((ln_fwd_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(SP_THREADS), 0, stream,
                          p);
       return hipGetLastError();
     }
