@@ -307,8 +307,14 @@ __device__ __forceinline__ i32x2 pack4_bf16(float a, float b, float c, float d) 
 // row): chunk c (8 columns) of row r sits at slot c ^ (r & 7).
 constexpr int QROW = 128, QBYTES = 128 * QROW;
 static_assert(NWAVE * (QBYTES + 128) <= LDS_BYTES, "epilogue staging and bias exceed the LDS");
+// 16-B chunk slot of a staging row.  A row is 128 B, half of the LDS's 256-B
+// bank width, so rows of one parity share a bank half; XOR-ing with row/2
+// gives the 16 rows of a parity that one accumulator write covers 8 distinct
+// slots (2 rows per bank: the minimum for 512 B), and a 1-KB read of 8 whole
+// rows touches each bank 4 times (also the minimum).
+__device__ __forceinline__ int quad_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk, int half) {
-  return qbase + row * QROW + ((chunk ^ (row & 7)) << 4) + half * 8;
+  return qbase + row * QROW + (quad_slot(row, chunk) << 4) + half * 8;
 }
 
 // One 256×256 output tile of problem a.
@@ -454,7 +460,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int row = j * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (row & 7);
+        const int c = quad_slot(row, lane & 7);
         const int gr = qm0 + row, gc = qn0 + c * 8;
         const uint32_t voff = (gr < a.M && gc < a.N)
                                   ? static_cast<uint32_t>((static_cast<int64_t>(gr) * a.ldc + gc) * 2)
@@ -541,7 +547,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int row = (it0 + u) * 8 + (lane >> 3);
-          const uint32_t ad = qbase + row * QROW + (((lane & 7) ^ (row & 7)) << 4);
+          const uint32_t ad = qbase + row * QROW + (quad_slot(row, lane & 7) << 4);
           asm volatile("ds_read_b128 %0, %1" : "=v"(v[u]) : "v"(ad) : "memory");
         }
         asm volatile("s_waitcnt lgkmcnt(0)"
