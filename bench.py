@@ -404,9 +404,10 @@ def leg_vocab(tp, reps):
     """The logit layer and vocabulary-parallel cross-entropy of the 8.3B-shaped
     model: n = 8192 tokens, h = 3072, V = 51200 in t = 8 shards of 6400, bf16,
     g = 1/n.  TFLOP/s over the GEMMs (2·n·h·V forward, twice that backward,
-    [EFF] FLOPs appendix); the cross-entropy kernels in GB/s against their
-    compulsory bytes (statistics: the logits read once; backward: logits read
-    and dlogits written once)."""
+    [EFF] FLOPs appendix), the cross-entropy kernels included in the time: the
+    row statistics come from the logit GEMM's epilogue, then a combine over the
+    shards; backward: dlogits (logits read and dlogits written once), then the
+    two GEMMs."""
     import numpy as np
     import torch
     from tpmlp_inputs import CONFIGS
@@ -423,7 +424,7 @@ def leg_vocab(tp, reps):
     g = torch.full((n,), 1.0 / n, dtype=torch.float32, device=dev)
     logits = torch.empty((t, n, vi), dtype=bf, device=dev)
     loss, rmax, rsum = (torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
-    ws = torch.empty(tp.lib().tpmlp_vocab_ce_workspace_bytes(t, n), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tp.lib().tpmlp_vocab_ce_workspace_bytes(t, n, vi), dtype=torch.uint8, device=dev)
     dlogits = torch.empty_like(logits)
     dW = torch.empty((t, vi, h), dtype=torch.float32, device=dev)
     dXp = torch.empty((t, n, h), dtype=bf, device=dev)

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 5
+#define TPMLP_ABI_VERSION 6
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -359,9 +359,12 @@ int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, 
  *   logits_i = X·W_iᵀ                              [n, v_i]  dt
  *   per shard and token: m_i = max, s_i = Σ exp(x − m_i), τ_i = target logit
  *   if the target is the shard's entry, else 0; combined by a max and two
- *   sums in shard order (the three small all-reduces of the page):
+ *   sums (the three small all-reduces of the page):
  *   row_max = max_i m_i, row_sum = Σ_i s_i·exp(m_i − row_max),
  *   loss = ln(row_sum) + row_max − Σ_i τ_i          [n] fp32 each
+ *   The statistics are those of the logits as stored; they are taken per 64
+ *   columns (on the bf16 path in the logit GEMM's epilogue) and combined in a
+ *   fixed order.
  * tpmlp_vocab_ce_bwd, g [n] fp32 = ∂ℓ/∂loss (1/n for the mean loss):
  *   dlogits_i = g·(exp(logits_i − row_max)/row_sum − onehot(target))   dt
  *   dW_i = dlogits_iᵀ·X  [v_i, h] fp32;  dX_i = dlogits_i·W_i [n, h] dt
@@ -372,10 +375,11 @@ int tpmlp_attn_core_bwd(hipStream_t stream, int dt, int32_t t_local, int64_t s, 
  *   n, h].  Exponentials and sums in fp32.  A target outside the resident
  *   shards contributes no target logit (its owner is another rank).
  *   bf16 needs h % 8 == 0 and v_i % 8 == 0 (as d and m_i of tpmlp_fwd).
- *   Workspace of the forward: tpmlp_vocab_ce_workspace_bytes(t_local, n)
- *   bytes (the shards' statistics), 4-byte aligned.
+ *   Workspace of the forward: tpmlp_vocab_ce_workspace_bytes(t_local, n,
+ *   v_i) bytes (a pair of floats per shard, token and 64 columns), 8-byte
+ *   aligned.
  */
-size_t tpmlp_vocab_ce_workspace_bytes(int32_t t_local, int64_t n);
+size_t tpmlp_vocab_ce_workspace_bytes(int32_t t_local, int64_t n, int64_t v_i);
 int tpmlp_vocab_ce_fwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t v_i, int32_t t_local,
                        int64_t vocab_start, const void* X, const void* W, const int32_t* targets, void* logits,
                        float* loss, float* row_max, float* row_sum, void* ws, size_t ws_bytes);

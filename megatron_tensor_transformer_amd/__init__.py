@@ -72,7 +72,7 @@ SIGNATURES = {
     "tpmlp_attn_mask_words": (_SZ, [_I64, _I64]),
     "tpmlp_attn_pack_mask": (_I, [_P, _I64, _I64, _P, _P]),
     "tpmlp_ln_sp": (_I, [_P, ctypes.POINTER(SpArgs)]),
-    "tpmlp_vocab_ce_workspace_bytes": (_SZ, [_I32, _I64]),
+    "tpmlp_vocab_ce_workspace_bytes": (_SZ, [_I32, _I64, _I64]),
     "tpmlp_vocab_ce_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I64] + [_P] * 8 + [_SZ]),
     "tpmlp_vocab_ce_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I64] + [_P] * 10),
     "tpmlp_status_string": (ctypes.c_char_p, [_I]),
@@ -441,8 +441,8 @@ def vocab_ce_fwd(X, W, targets, vocab_start=0, stream=None):
     logits = torch.empty((t, n, vi), dtype=X.dtype, device=X.device)
     loss = torch.empty(n, dtype=torch.float32, device=X.device)
     rmax, rsum = torch.empty_like(loss), torch.empty_like(loss)
-    nb = lib().tpmlp_vocab_ce_workspace_bytes(t, n)
-    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=X.device)
+    nb = lib().tpmlp_vocab_ce_workspace_bytes(t, n, vi)
+    ws = torch.empty(max(nb, 8), dtype=torch.uint8, device=X.device)
     tpmlp_vocab_ce_fwd(X, W, targets, logits, loss, rmax, rsum, ws, vocab_start, stream)
     return logits, loss, rmax, rsum
 

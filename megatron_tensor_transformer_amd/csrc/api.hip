@@ -690,9 +690,11 @@ int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, 
   return st;
 }
 
-size_t tpmlp_vocab_ce_workspace_bytes(int32_t t_local, int64_t n) {
-  if (t_local < 1 || n <= 0) return 0;
-  return 3 * static_cast<size_t>(t_local) * static_cast<size_t>(n) * sizeof(float);
+size_t tpmlp_vocab_ce_workspace_bytes(int32_t t_local, int64_t n, int64_t v_i) {
+  if (t_local < 1 || n <= 0 || v_i <= 0) return 0;
+  // a (max, sum) pair of floats per shard, token and 64-column group
+  return 2 * static_cast<size_t>(t_local) * static_cast<size_t>(n) * static_cast<size_t>((v_i + 63) / 64) *
+         sizeof(float);
 }
 
 int tpmlp_vocab_ce_fwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t v_i, int32_t t_local,
@@ -707,9 +709,10 @@ int tpmlp_vocab_ce_fwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t
   if (targets == nullptr || loss == nullptr || row_max == nullptr || row_sum == nullptr) return TPMLP_ERR_NULLPTR;
   if (!aligned(targets, 4) || !aligned(loss, 4) || !aligned(row_max, 4) || !aligned(row_sum, 4))
     return TPMLP_ERR_ALIGN;
-  if (ws == nullptr || ws_bytes < tpmlp_vocab_ce_workspace_bytes(t_local, n)) return TPMLP_ERR_WORKSPACE;
-  if (!aligned(ws, 4)) return TPMLP_ERR_ALIGN;
-  // logits_i = X·W_iᵀ: A = X [n,h] (K-major), B(k,j) = W_i[j][k] (K-major)
+  if (ws == nullptr || ws_bytes < tpmlp_vocab_ce_workspace_bytes(t_local, n, v_i)) return TPMLP_ERR_WORKSPACE;
+  if (!aligned(ws, 8)) return TPMLP_ERR_ALIGN;
+  // logits_i = X·W_iᵀ: A = X [n,h] (K-major), B(k,j) = W_i[j][k] (K-major);
+  // on the bf16 path its epilogue also takes the row statistics per 64-column group
   tpmlp::GemmProblem g{};
   g.M = static_cast<int>(n);
   g.N = static_cast<int>(v_i);
@@ -724,9 +727,12 @@ int tpmlp_vocab_ce_fwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t
   g.sA = 0;
   g.sB = v_i * h;
   g.sC = n * v_i;
-  st = hip_status(gemm(dt, g, tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE, stream));
+  const bool fused = dt == TPMLP_BF16;
+  g.rstats = static_cast<float*>(ws);
+  st = hip_status(gemm(dt, g, tpmlp::KMAJ, tpmlp::KMAJ, fused ? tpmlp::EPI_STORE_ROWSTATS : tpmlp::EPI_STORE, stream));
   if (st) return st;
   tpmlp::VocabProblem p{};
+  p.stats_done = fused;
   p.dt = dt;
   p.T = t_local;
   p.n = n;

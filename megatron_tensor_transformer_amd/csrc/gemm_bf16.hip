@@ -57,6 +57,7 @@ struct alignas(64) KArgs {
   const bf16* Zin;
   const bf16* bias;
   int64_t sBias;
+  float* rstats;
   int M, N, K;
   int tiles_m, tiles_n, batch;
   int64_t lda, ldb, ldc;
@@ -476,6 +477,9 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 #pragma unroll
       for (int i = 0; i < FA; ++i) {
         i32x2 zr[FB][4];
+        // EPI_STORE_ROWSTATS: this lane's row statistics over its 32 of the
+        // wave's 64 columns, of the values as stored (bf16-rounded)
+        float rmx = -INFINITY, rsm = 0.f;
         if constexpr (BIAS) {
 #pragma unroll
           for (int j = 0; j < FB; ++j)
@@ -529,12 +533,53 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
               for (int e = 0; e < 4; ++e) v[4 * q + e] *= gelu_grad_fast(bf2f(z[e]));
             }
           }
+          i32x2 pk[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const i32x2 pk = pack4_bf16(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          for (int q = 0; q < 4; ++q) pk[q] = pack4_bf16(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          if constexpr (EPI == EPI_STORE_ROWSTATS) {
+            // value 4q + e is column qn0 + 32j + 8q + 4·half + e; columns past N
+            // take no part
+            float x[16];
+            float bm = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t w = static_cast<uint32_t>(pk[q][e >> 1]);
+                const float y = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                x[4 * q + e] = qn0 + 32 * j + 8 * q + 4 * half + e < a.N ? y : -INFINITY;
+                bm = fmaxf(bm, x[4 * q + e]);
+              }
+            if (bm > rmx) {
+              rsm *= __expf(rmx - bm);
+              rmx = bm;
+            }
+            if (rmx != -INFINITY) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) rsm += __expf(x[e] - rmx);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
             asm volatile("ds_write_b64 %0, %1" ::"v"(quad_addr(qbase, i * 32 + row_l, j * 4 + q, half)),
-                         "v"(pk)
+                         "v"(pk[q])
                          : "memory");
+        }
+        if constexpr (EPI == EPI_STORE_ROWSTATS) {
+          // the row's two halves sit in lanes L and L+32: merge, and one of
+          // them writes the pair of the wave's 64-column group
+          const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmx), __float_as_uint(rmx), false, false);
+          const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(rsm), __float_as_uint(rsm), false, false);
+          const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
+          const float s0 = __uint_as_float(ps[0]), s1 = __uint_as_float(ps[1]);
+          const float mm = fmaxf(m0, m1);
+          const float ss = mm == -INFINITY ? 0.f : s0 * __expf(m0 - mm) + s1 * __expf(m1 - mm);
+          const int row = qm0 + i * 32 + row_l;
+          const int ng = (a.N + 63) >> 6;
+          if (half == 0 && row < a.M && qn0 < a.N) {
+            float* r = a.rstats + (static_cast<int64_t>(batch) * a.M + row) * ng * 2 + (qn0 >> 6) * 2;
+            r[0] = mm;
+            r[1] = ss;
           }
         }
       }
@@ -612,6 +657,7 @@ KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
   k.Zin = static_cast<const bf16*>(p.Zin);
   k.bias = static_cast<const bf16*>(p.bias);
   k.sBias = p.sBias;
+  k.rstats = p.rstats;
   k.M = p.M;
   k.N = p.N;
   k.K = p.K;
@@ -678,6 +724,8 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
     return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
   if (same && is(k0, KMAJ, KMAJ, EPI_STORE))
     return launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE>(g, stream);
+  if (same && is(k0, KMAJ, KMAJ, EPI_STORE_ROWSTATS))
+    return launch_t<KMAJ, KMAJ, EPI_STORE_ROWSTATS, KMAJ, KMAJ, EPI_STORE_ROWSTATS>(g, stream);
   if (same && is(k0, MNMAJ, MNMAJ, EPI_STORE_F32))
     return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, MNMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
   // the backward's last launch: both weight gradients, then dgrad-2

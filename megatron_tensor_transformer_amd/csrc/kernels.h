@@ -20,7 +20,9 @@ enum Epilogue {
   EPI_GELU_ZY = 2,    // C = acc (Z), C2 = GeLU(acc) (Y)
   EPI_GELU_GRAD = 3,  // C = acc ⊙ GeLU'(Zin) (D)
   EPI_BIAS_GELU_ZY = 4,  // z = acc + bias[col]: C = z (Z), C2 = GeLU(z) (Y)
-  EPI_BIAS_STORE = 5     // C = acc + bias[col] (dtype of the path)
+  EPI_BIAS_STORE = 5,    // C = acc + bias[col] (dtype of the path)
+  EPI_STORE_ROWSTATS = 6  // C = acc (bf16), and per row and 64-column group of C as stored:
+                          // (max, Σ exp(c − max)) into rstats (the cross-entropy's statistics)
 };
 
 struct GemmProblem {
@@ -33,6 +35,7 @@ struct GemmProblem {
   const void* Zin;   // EPI_GELU_GRAD: stored Z, same layout as C
   const void* bias;  // EPI_BIAS_GELU_ZY / EPI_BIAS_STORE: [N] per batch entry, path dtype
   int64_t sBias;     // its per-batch stride in elements
+  float* rstats;     // EPI_STORE_ROWSTATS: [batch][M][⌈N/64⌉] pairs (max, sum) of floats
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;  // per-batch strides in elements (0 = shared operand)
 };
@@ -117,7 +120,8 @@ struct VocabProblem {
   int64_t n, vi, start0;  // tokens, vocabulary entries per shard, first entry of shard 0
   const void* logits;     // [T][n][vi]
   const int* target;      // [n], global vocabulary ids
-  float* stats;           // workspace [3][T][n]: per-shard max, sum, target logit
+  float* stats;           // workspace [T][n][⌈vi/64⌉] pairs (max, Σ exp(x − max)) per 64-column group
+  bool stats_done;        // the logit GEMM's epilogue has written stats (bf16 path)
   float* loss;            // [n]
   float* rmax;            // [n] row max over all shards
   float* rsum;            // [n] Σ exp(x − rmax) over all shards

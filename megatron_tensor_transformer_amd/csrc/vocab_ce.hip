@@ -7,11 +7,15 @@
 //             loss = ln S + m − τ
 // Backward: dx_k = g·(exp(x_k − m)/S − [k = target]).
 //
-// All three kernels are HBM-bound.  Statistics: one wave per (shard, token)
-// row, 16-B loads, a per-lane online max/sum (rescaled only when a lane's
-// maximum grows), then a fixed-order wave reduction of the (max, sum) pairs.
-// Combine: one thread per token, shards in order.  Backward: 8 elements per
-// thread, the row's (m, S, g, target) read once per row segment.
+// The statistics are taken per row and 64-column group of a shard's logits:
+// on the bf16 path by the logit GEMM's epilogue from its accumulators as they
+// are stored (the logits are then never re-read for them), on the fp32 path
+// by a separate kernel.  The combine takes all groups of all shards (the
+// shards' max and sums are the same max and sums over more terms, [SENSE]
+// Eq. (3)/(4)): one wave per token, a per-lane online max/sum over the groups
+// in a fixed order, then a fixed-order butterfly; lane 0 adds the target logit
+// of the shard that owns it.  Backward: 8 elements per thread, the row's
+// (m, S, g, target) read once per row segment.  All are HBM-bound.
 #include "common.h"
 #include "kernels.h"
 
@@ -54,76 +58,64 @@ __device__ __forceinline__ void merge(float& m, float& s, float m2, float s2) {
   m = mm;
 }
 
-// Statistics of row (shard i, token r): m_i, s_i, τ_i into stats[3][T][n].
-// VEC: the row is 16-B aligned with V_i % 8 == 0 (else element by element).
-template <typename T, bool VEC>
-__global__ __launch_bounds__(CT) void ce_stats_kernel(const T* __restrict__ x, const int* __restrict__ target,
-                                                      float* __restrict__ stats, int Tn, int64_t n, int64_t vi,
-                                                      int64_t start0) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * (CT / 64) + (threadIdx.x >> 6);
-  if (row >= static_cast<int64_t>(Tn) * n) return;
-  const int64_t i = row / n, r = row - i * n;
+// Statistics of row (shard i, token r) over column group g (columns 64g ..
+// 64g+63 of the shard): (max, Σ exp(x − max)) into stats[i][r][g].  One thread
+// per group; the fp32 path's counterpart of the bf16 GEMM epilogue.
+template <typename T>
+__global__ __launch_bounds__(CT) void ce_group_stats_kernel(const T* __restrict__ x, float* __restrict__ stats,
+                                                            int Tn, int64_t n, int64_t vi, int64_t ng) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * CT + threadIdx.x;
+  if (idx >= static_cast<int64_t>(Tn) * n * ng) return;
+  const int64_t row = idx / ng, g = idx - row * ng;
   const T* xr = x + row * vi;
+  const int64_t c0 = 64 * g, c1 = c0 + 64 < vi ? c0 + 64 : vi;
   float m = -INFINITY, s = 0.f;
-  if constexpr (VEC) {
-    for (int64_t c = static_cast<int64_t>(lane) * 8; c < vi; c += 64 * 8) {
-      float v[8];
-      load8v(xr + c, v);
-      float cm = v[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) cm = fmaxf(cm, v[k]);
-      if (cm > m) {
-        s *= __expf(m - cm);
-        m = cm;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) s += __expf(v[k] - m);
+  for (int64_t c = c0; c < c1; ++c) {
+    const float v = ld1v(xr + c);
+    if (v > m) {
+      s *= __expf(m - v);
+      m = v;
     }
-  } else {
-    for (int64_t c = lane; c < vi; c += 64) {
-      const float v = ld1v(xr + c);
-      if (v > m) {
-        s *= __expf(m - v);
-        m = v;
-      }
-      s += __expf(v - m);
-    }
+    s += __expf(v - m);
   }
-  // fixed-order butterfly over the wave
+  stats[2 * idx] = m;
+  stats[2 * idx + 1] = s;
+}
+
+// Token r: combine the (max, sum) pairs of every group of every shard, in
+// order, add the target logit of the shard that owns the target; loss, and
+// the row's max and sum for the backward.  One wave per token.
+template <typename T>
+__global__ __launch_bounds__(CT) void ce_combine_kernel(const float* __restrict__ stats, const T* __restrict__ x,
+                                                        const int* __restrict__ target, float* __restrict__ loss,
+                                                        float* __restrict__ rmax, float* __restrict__ rsum, int Tn,
+                                                        int64_t n, int64_t vi, int64_t ng, int64_t start0) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * (CT / 64) + (threadIdx.x >> 6);
+  if (r >= n) return;
+  float m = -INFINITY, s = 0.f;
+  const int64_t per = Tn * ng;  // pairs of token r: shard i's groups at (i·n + r)·ng
+  for (int64_t k = lane; k < per; k += 64) {
+    const int64_t i = k / ng, g = k - i * ng;
+    const float* p = stats + ((i * n + r) * ng + g) * 2;
+    merge(m, s, p[0], p[1]);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
     merge(m, s, m2, s2);
   }
   if (lane == 0) {
-    const int64_t k = static_cast<int64_t>(target[r]) - (start0 + i * vi);
-    const float tau = (k >= 0 && k < vi) ? ld1v(xr + k) : 0.f;
-    const int64_t tn = static_cast<int64_t>(Tn) * n;
-    stats[row] = m;
-    stats[tn + row] = s;
-    stats[2 * tn + row] = tau;
+    const int64_t gt = static_cast<int64_t>(target[r]) - start0;  // column in the resident shards' vocabulary
+    float tau = 0.f;
+    if (gt >= 0 && gt < static_cast<int64_t>(Tn) * vi) {
+      const int64_t i = gt / vi, k = gt - i * vi;
+      tau = ld1v(x + (i * n + r) * vi + k);
+    }
+    loss[r] = logf(s) + m - tau;
+    rmax[r] = m;
+    rsum[r] = s;
   }
-}
-
-// Combine the shards' statistics of token r in shard order; loss, and the
-// row's max and sum for the backward.
-__global__ __launch_bounds__(CT) void ce_combine_kernel(const float* __restrict__ stats, float* __restrict__ loss,
-                                                        float* __restrict__ rmax, float* __restrict__ rsum, int Tn,
-                                                        int64_t n) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * CT + threadIdx.x;
-  if (r >= n) return;
-  const int64_t tn = static_cast<int64_t>(Tn) * n;
-  float m = -INFINITY;
-  for (int i = 0; i < Tn; ++i) m = fmaxf(m, stats[i * n + r]);
-  float S = 0.f, tau = 0.f;
-  for (int i = 0; i < Tn; ++i) {
-    S += stats[tn + i * n + r] * __expf(stats[i * n + r] - m);
-    tau += stats[2 * tn + i * n + r];
-  }
-  loss[r] = logf(S) + m - tau;
-  rmax[r] = m;
-  rsum[r] = S;
 }
 
 // dx[i][r][k] = g_r·(exp(x − m_r)/S_r − [k = target_r − start_i]); 8 elements
@@ -175,19 +167,16 @@ __global__ __launch_bounds__(CT) void ce_bwd_kernel(const T* __restrict__ x, con
 template <typename T>
 hipError_t run_fwd(const VocabProblem& p, hipStream_t stream) {
   const T* x = static_cast<const T*>(p.logits);
-  const int64_t rows = static_cast<int64_t>(p.T) * p.n;
-  const bool vec = p.vi % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
-  const unsigned blocks = static_cast<unsigned>((rows + CT / 64 - 1) / (CT / 64));
-  if (vec)
-    hipLaunchKernelGGL((ce_stats_kernel<T, true>), dim3(blocks), dim3(CT), 0, stream, x, p.target, p.stats, p.T, p.n,
-                       p.vi, p.start0);
-  else
-    hipLaunchKernelGGL((ce_stats_kernel<T, false>), dim3(blocks), dim3(CT), 0, stream, x, p.target, p.stats, p.T,
-                       p.n, p.vi, p.start0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ce_combine_kernel, dim3(static_cast<unsigned>((p.n + CT - 1) / CT)), dim3(CT), 0, stream,
-                     p.stats, p.loss, p.rmax, p.rsum, p.T, p.n);
+  const int64_t ng = (p.vi + 63) / 64;
+  if (!p.stats_done) {
+    const int64_t groups = static_cast<int64_t>(p.T) * p.n * ng;
+    hipLaunchKernelGGL((ce_group_stats_kernel<T>), dim3(static_cast<unsigned>((groups + CT - 1) / CT)), dim3(CT), 0,
+                       stream, x, p.stats, p.T, p.n, p.vi, ng);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((ce_combine_kernel<T>), dim3(static_cast<unsigned>((p.n + CT / 64 - 1) / (CT / 64))), dim3(CT),
+                     0, stream, p.stats, x, p.target, p.loss, p.rmax, p.rsum, p.T, p.n, p.vi, ng, p.start0);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 5
+    assert L.tpmlp_abi_version() == 6
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert L.tpmlp_status_string(s)
 
@@ -162,9 +162,11 @@ def test_attn_validation(L):
 def test_vocab_ce_validation(L):
     p = ctypes.c_void_p(0x1000)
     z = ctypes.c_void_p(0)
-    # one fp32 max, sum and target logit per (shard, token)
-    assert L.tpmlp_vocab_ce_workspace_bytes(8, 8192) == 3 * 8 * 8192 * 4
-    need = L.tpmlp_vocab_ce_workspace_bytes(2, 64)
+    # a pair of fp32 (max, sum) per shard, token and 64 vocabulary columns
+    assert L.tpmlp_vocab_ce_workspace_bytes(8, 8192, 6400) == 2 * 8 * 8192 * 100 * 4
+    assert L.tpmlp_vocab_ce_workspace_bytes(3, 5, 65) == 2 * 3 * 5 * 2 * 4
+    assert L.tpmlp_vocab_ce_workspace_bytes(3, 5, 0) == 0
+    need = L.tpmlp_vocab_ce_workspace_bytes(2, 64, 64)
 
     def fwd(dt=1, n=64, h=64, vi=64, t=2, start=0, X=p, tg=p, ws=p, nb=need):
         return L.tpmlp_vocab_ce_fwd(None, dt, n, h, vi, t, start, X, p, tg, p, p, p, p, ws, nb)
@@ -176,6 +178,7 @@ def test_vocab_ce_validation(L):
     assert fwd(tg=z) == tp.ERR_NULLPTR
     assert fwd(nb=need - 4) == tp.ERR_WORKSPACE
     assert fwd(ws=z) == tp.ERR_WORKSPACE
+    assert fwd(ws=ctypes.c_void_p(0x1004)) == tp.ERR_ALIGN  # pairs of floats: 8-byte aligned
     assert fwd(n=0, X=z, tg=z, ws=z, nb=0) == 0
     # backward: dW required; g required when n > 0
     assert L.tpmlp_vocab_ce_bwd(None, 1, 64, 64, 64, 2, 0, p, p, p, p, p, p, p, p, z, p) == tp.ERR_NULLPTR
