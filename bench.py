@@ -487,7 +487,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(every box here has one GPU; the path would shard one TP rank per GPU).",
+              "(a multi-GPU run would place one TP rank per GPU and replace the local "
+              "reduction by an all-reduce).",
               file=sys.stderr)
         sys.exit(2)
 

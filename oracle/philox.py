@@ -4,8 +4,8 @@
 The pages draw the dropout mask from a Bernoulli distribution ([TRAIN] Dropout
 section) and require that sequence-parallel ranks draw different masks ([SP]
 "Dropout 的 RNG 为什么要分域管理？" and its RNG-domain table).  Neither page
-names a generator.  This build fixes one published counter-based generator so
-that the kernel and this oracle can each implement it from its definition:
+names a generator.  The library fixes one published counter-based generator
+so that the kernel and this oracle can each implement it from its definition:
 
   Philox-4x32 with 10 rounds, from J. K. Salmon, M. A. Moraes, R. O. Dror,
   D. E. Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11 (§4):
@@ -14,8 +14,8 @@ that the kernel and this oracle can each implement it from its definition:
     with M0 = 0xD2511F53, M1 = 0xCD9E8D57; the key is bumped by the Weyl
     constants (0x9E3779B9, 0xBB67AE85) between rounds.
 
-Mask rule (this build's reading; the same rule is written independently in the
-HIP source): for element e of the row-major [s, h] activation (e = row·h + col,
+Mask rule (the reading taken where the pages are silent; the same rule is
+written independently in the HIP source): for element e of the row-major [s, h] activation (e = row·h + col,
 over the whole sequence, so each sequence shard sees its own block of
 counters), q = e // 4 and w = e % 4; u = word w of Philox(counter=(q mod 2³²,
 q div 2³², 0, 0), key=(seed mod 2³², seed div 2³²)).  The element is dropped

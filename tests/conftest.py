@@ -15,8 +15,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped only where there is no GPU at all; on a GPU machine a
-    # missing or broken library makes them fail, never fall back.
+    # GPU tests are skipped only where there is no GPU at all; on a machine
+    # with a GPU a missing or broken library makes them fail, never fall back.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
