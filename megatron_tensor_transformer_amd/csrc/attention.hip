@@ -915,7 +915,10 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   load_tile<DH>(rq, lds, a.s, a.b, bi, row_len, qcol, j0, wave, lane);
   load_tile<DH>(rd, lds + TILE, a.s, a.b, bi, orow, dcol, j0, wave, lane);
 
-  bf16x8 kf[NC], vf[NC];
+  // k and v fragments of the lane's key, kept in AGPRs (an MFMA operand may
+  // come from either register file; the VGPRs go to the S and dP
+  // accumulators, which the VALU reads)
+  i32x4 kf[NC], vf[NC];
   const bool valid = krow < a.s;
   // this batch entry's general mask (read only when GMASK and krow < s)
   const i32x4 mrs = GMASK ? make_rsrc(a.mask + (static_cast<int64_t>(a.b) + bi) * a.s * a.mw,
@@ -925,8 +928,9 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
     const bf16* kp = qkv + (static_cast<int64_t>(krow) * a.b + bi) * row_len + h * 3 * DH + DH + 8 * hi;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      kf[c] = valid ? *reinterpret_cast<const bf16x8*>(kp + 16 * c) : bf16x8{};
-      vf[c] = valid ? *reinterpret_cast<const bf16x8*>(kp + DH + 16 * c) : bf16x8{};
+      kf[c] = valid ? *reinterpret_cast<const i32x4*>(kp + 16 * c) : i32x4{0, 0, 0, 0};
+      vf[c] = valid ? *reinterpret_cast<const i32x4*>(kp + DH + 16 * c) : i32x4{0, 0, 0, 0};
+      asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
     }
   }
   f32x16 dk[ND], dv[ND];
@@ -1004,10 +1008,12 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
         sr[g] = lds_rd128<((2 * ST + 0) * AKV + 32 * U + 8 * g) * 4>(sbase);
         sr[4 + g] = lds_rd128<((2 * ST + 1) * AKV + 32 * U + 8 * g) * 4>(sbase);
       });
-      // S = Q·Kᵀ and dP = dO·Vᵀ for the lane's key: slices read three ahead
+      // S = Q·Kᵀ and dP = dO·Vᵀ for the lane's key: slices read three ahead.
+      // The products are inline asm with VGPR accumulators (the compiler's
+      // form for this one-wave-per-SIMD kernel keeps them in AGPRs, and every
+      // VALU use below would first copy them out); the first slice starts
+      // from zero.
       f32x16 sacc, pacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
       i32x4 qr[4], dr[4];
       auto rd2 = [&](auto cc) {
         constexpr int c = decltype(cc)::value;
@@ -1019,10 +1025,18 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
         constexpr int c = decltype(cc)::value;
         constexpr int later = 2 * (NC - 1 - c < 2 ? NC - 1 - c : 2);
         lgkm_wait<later>(qr[c % 4], dr[c % 4]);
-        sacc = mfma(__builtin_bit_cast(bf16x8, qr[c % 4]), kf[c], sacc);
-        pacc = mfma(__builtin_bit_cast(bf16x8, dr[c % 4]), vf[c], pacc);
+        if constexpr (c == 0) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(qr[0]), "a"(kf[0]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(pacc) : "v"(dr[0]), "a"(vf[0]));
+        } else {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qr[c % 4]), "a"(kf[c]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pacc) : "v"(dr[c % 4]), "a"(vf[c]));
+        }
         if constexpr (c + 3 < NC) rd2(ic<c + 3>{});
       });
+      // the VALU reads the results only after the MFMA pipeline has written
+      // them (the wait states the compiler inserts for its own MFMAs)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(sacc), "+v"(pacc));
       // every LDS read above is complete (the last wait was for zero)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
