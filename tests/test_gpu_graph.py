@@ -1,5 +1,6 @@
-"""One MLP shard step (tpmlp_fwd, tpmlp_reduce_partials, tpmlp_bwd, tpmlp_reduce_partials)
-captured into a HIP graph and replayed.
+"""Whole steps captured into a HIP graph and replayed: the MLP shard step (tpmlp_fwd,
+tpmlp_reduce_partials, tpmlp_bwd, tpmlp_reduce_partials), the attention side of the
+layer (causal, or with a packed padding mask) and the vocabulary-parallel cross-entropy.
 
 The library only enqueues kernels on the caller's stream: it allocates, clears and
 synchronises nothing, so the whole step can be captured once and replayed.  Every replay
@@ -9,11 +10,12 @@ the replays, and the inputs change between them, so a replay that reused stale r
 skipped a node would show.
 """
 
+import numpy as np
 import pytest
 import torch
 
 import megatron_tensor_transformer_amd as tp
-from tpmlp_inputs import mlp_inputs
+from tpmlp_inputs import attn_inputs, attn_mask, mlp_inputs, vocab_inputs
 
 from gpu_util import dev, say, shard_cols, shard_rows
 
@@ -94,3 +96,78 @@ def test_step_graph_replays_match_eager(dtype, n, d, m, t):
         assert torch.isfinite(scratch)
         for name in OUTS:
             assert torch.equal(out[name], ref[k][name]), f"replay {rep} (input set {k}): {name} differs"
+
+
+def _graph_check(step, sets, order=(1, 2, 0, 1)):
+    """Capture step(*static inputs) (it returns a dict of output tensors, allocated in
+    the graph's pool) and replay it on each input set of `order`, comparing bit for bit
+    with step(*set) run eagerly."""
+    ref = []
+    for args in sets:
+        out = step(*args)
+        torch.cuda.synchronize()
+        ref.append({k: v.clone() for k, v in out.items()})
+    static = [a.clone() for a in sets[0]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(*static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step(*static)
+    torch.cuda.synchronize()
+    for rep, k in enumerate(order):
+        for dst, src in zip(static, sets[k]):
+            dst.copy_(src)
+        for v in out.values():
+            v.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, v in out.items():
+            assert torch.equal(v, ref[k][name]), f"replay {rep} (input set {k}): {name} differs"
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_attention_layer_graph(masked):
+    s, b, d, heads, t = 130, 2, 256, 2, 2
+    dh = d // heads
+    say(f"[gpu] graph capture attention s={s} b={b} d={d} heads={heads} t={t} masked={masked}")
+    sets = []
+    for seed in (31, 32, 33):
+        inp = attn_inputs(s, b, d, heads, dtype="bf16", seed=seed, x_std=1.0, w_std=1.2 / np.sqrt(d), g_std=1.0)
+        X, Wq, Wp, G = (dev(inp[k]) for k in ("X", "Wqkv", "Wproj", "G"))
+        m = torch.from_numpy(attn_mask(b, s, "padding", seed=seed)).cuda() if masked else None
+        args = [X, shard_cols(Wq, t), shard_rows(Wp, t), G] + ([m] if masked else [])
+        sets.append(args)
+
+    def step(X, Wq, Wp, G, m=None):
+        QKV, O, lse, P = tp.attn_fwd(X, Wq, Wp, s, b, dh, not masked, mask=m)
+        Out = tp.reduce_partials(P)
+        dO, dQKV, dWqkv, dWproj, dXp = tp.attn_bwd(X, Wq, Wp, QKV, O, lse, G, s, b, dh, not masked, mask=m)
+        dX = tp.reduce_partials(dXp)
+        return dict(QKV=QKV, O=O, lse=lse, Out=Out, dQKV=dQKV, dWqkv=dWqkv, dWproj=dWproj, dX=dX)
+
+    _graph_check(step, sets)
+
+
+def test_vocab_ce_graph():
+    n, h, V, t = 300, 264, 2064, 2
+    say(f"[gpu] graph capture vocab CE n={n} h={h} V={V} t={t}")
+    sets = []
+    for seed in (41, 42, 43):
+        inp = vocab_inputs(n, h, V, dtype="bf16", seed=seed, x_std=1.0, w_std=1.2 / np.sqrt(h), g_std=1.0)
+        X, W = dev(inp["X"]), dev(inp["W"])
+        tg = torch.from_numpy(inp["targets"]).cuda()
+        g = torch.from_numpy(inp["g"].f32.copy()).cuda()
+        sets.append([X, W.reshape(t, V // t, h).contiguous(), tg, g])
+
+    def step(X, W, tg, g):
+        logits, loss, rmax, rsum = tp.vocab_ce_fwd(X, W, tg)
+        dlogits, dW, dXp = tp.vocab_ce_bwd(X, W, tg, logits, rmax, rsum, g)
+        dX = tp.reduce_partials(dXp)
+        return dict(logits=logits, loss=loss, rmax=rmax, rsum=rsum, dlogits=dlogits, dW=dW, dX=dX)
+
+    _graph_check(step, sets)
