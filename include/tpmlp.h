@@ -41,6 +41,10 @@
  *     (earlier kernels of the same call may have been enqueued).
  *   - The caller owns every buffer and keeps it alive until the stream work
  *     completes.  Inputs and outputs must not overlap.
+ *   - A call issues no allocation, memset, copy or synchronisation, only
+ *     kernel launches, so a sequence of calls may be captured into a HIP
+ *     graph on the caller's stream and replayed (replays read the buffers'
+ *     contents at replay time).
  *   - bf16 operands need 16-byte aligned base pointers and row lengths that
  *     are multiples of 8 elements (d % 8 == 0, m_i % 8 == 0); f32 operands
  *     need 4-byte alignment only.  Each per-shard operand must be smaller
