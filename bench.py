@@ -13,14 +13,17 @@ reductions are not counted).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 
-Prints one JSON line.  Besides the headline step it reports (unless
+Prints one JSON line.  The engine clock is sampled from the host during the
+timed steps (`sclk_mhz`).  Besides the headline step it reports (unless
 --no-extra): the per-rank rate (one shard per launch, t_local = 1, as one TP
-rank runs it), the GPT-1T-shaped shard (n = 2048, d = 25600, m_i = 12800, one
-shard), and the sequence-parallel region's memory-bound kernels on the
-h = 4096 block (LN forward, reduce + dropout + residual, dropout backward,
-LN backward with the fused dU reduce) in GB/s against 8 TB/s, each timed
-after writing a 512 MiB scratch buffer so the 256 MiB last-level cache holds
-none of its inputs.
+rank runs it), the single-shard layer (n = 2048, d = 1024, m = 4096, t = 1),
+the GPT-1T-shaped shard (n = 2048, d = 25600, m_i = 12800, one shard), the
+sequence-parallel region's memory-bound kernels on the h = 4096 block (LN
+forward, reduce + dropout + residual, dropout backward, LN backward with the
+fused dU reduce) in GB/s against 8 TB/s, each timed after writing a 512 MiB
+scratch buffer so the 256 MiB last-level cache holds none of its inputs, the
+whole sequence-parallel block step on that block, the biased layer, the
+attention side and the vocabulary-parallel cross-entropy.
 """
 
 import argparse
@@ -145,6 +148,101 @@ def cpu_all_configs():
     return out
 
 
+class ClockSampler:
+    """Samples the GPU's engine clock (and socket power) from the host every
+    `period` seconds while the timed loop runs, through the AMD SMI library's
+    GPU metrics table (per-XCD current gfx clocks), so the result can be read
+    against the clock the peak assumes.  Host-side only: it never touches the
+    GPU's command queues."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period = period
+        self.samples = []   # (mean over XCDs of the current gfx clock in MHz, socket power W or None)
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._smi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._smi = amdsmi
+            self._handle = self._pick(amdsmi, handles)
+        except Exception as e:  # no SMI library or no access: report why
+            self.error = f"{type(e).__name__}: {e}"
+
+    @staticmethod
+    def _pick(amdsmi, handles):
+        """The handle of cuda:0, matched by PCI bus id when torch exposes it."""
+        import torch
+        if len(handles) == 1:
+            return handles[0]
+        try:
+            pr = torch.cuda.get_device_properties(0)
+            bus = (int(pr.pci_domain_id), int(pr.pci_bus_id), int(pr.pci_device_id))
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, b, df = bdf.split(":")
+                if (int(dom, 16), int(b, 16), int(df.split(".")[0], 16)) == bus:
+                    return h
+        except Exception:
+            pass
+        return handles[0]
+
+    def read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = m.get("current_gfxclks")
+        vals = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000] if isinstance(clks, list) else []
+        if not vals:
+            c = m.get("current_gfxclk")
+            vals = [c] if isinstance(c, (int, float)) and 0 < c < 10000 else []
+        pw = m.get("current_socket_power")
+        if not isinstance(pw, (int, float)) or not 0 < pw < 5000:
+            pw = m.get("average_socket_power")
+        pw = pw if isinstance(pw, (int, float)) and 0 < pw < 5000 else None
+        return (sum(vals) / len(vals) if vals else None), pw
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read())
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._handle is None:
+            return
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        import numpy as np
+        clk = [c for c, _ in self.samples if c is not None]
+        pw = [p for _, p in self.samples if p is not None]
+        out = {"source": "AMD SMI GPU metrics, mean over XCDs of current_gfxclks, sampled every "
+                         f"{int(self.period * 1000)} ms during the timed steps",
+               "samples": len(clk)}
+        if clk:
+            out.update({"median_mhz": round(float(np.median(clk)), 1), "min_mhz": round(float(np.min(clk)), 1),
+                        "max_mhz": round(float(np.max(clk)), 1),
+                        "frac_of_2400": round(float(np.median(clk)) / 2400.0, 4)})
+        if pw:
+            out["socket_power_w_median"] = round(float(np.median(pw)), 1)
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
 def _stats(ms):
     import numpy as np
     return {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(np.min(ms)), 4),
@@ -168,7 +266,24 @@ def _time_events(fn, reps, before=None):
     return out
 
 
-def leg_mlp_shard(tp, n, d, mi, reps, seed):
+def _time_batched(fn, reps, inner):
+    """Like _time_events, but each bracket holds `inner` back-to-back calls
+    (for steps short enough that the host's launch latency would otherwise
+    show); returns the per-call milliseconds of each bracket."""
+    import torch
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(inner):
+            fn()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) / inner)
+    return out
+
+
+def leg_mlp_shard(tp, n, d, mi, reps, seed, inner=1):
     """fwd + bwd GEMMs of one shard per launch (t_local = 1) on seeded device
     data of the given shape: the rate one TP rank sees."""
     import torch
@@ -194,11 +309,11 @@ def leg_mlp_shard(tp, n, d, mi, reps, seed):
 
     for _ in range(3):
         run()
-    ms = _time_events(run, reps)
+    ms = _time_events(run, reps) if inner == 1 else _time_batched(run, reps, inner)
     import numpy as np
     med = float(np.median(ms))
     flops = 12.0 * n * d * mi
-    return {"n": n, "d": d, "m_i": mi, "t_local": 1, "flop": flops,
+    return {"n": n, "d": d, "m_i": mi, "t_local": 1, "flop": flops, "steps_per_timing": inner,
             "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2), **_stats(ms)}
 
@@ -243,6 +358,95 @@ def leg_sp(tp, reps):
         out[name] = {"bytes": nbytes, "gbs_median": round(nbytes / (med * 1e-3) / 1e9, 1),
                      "frac_of_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), **_stats(ms)}
     return {"workload": f"sequence-parallel region of the h={h} block: s={s}, t={t}, p={p}, bf16", **out}
+
+
+def leg_c5_block(tp, reps):
+    """The whole sequence-parallel block step on the h = 4096 configuration
+    (s = 4096 tokens, h = 4096, m = 4h, t = 8 sequence and tensor shards,
+    p = 0.1, bf16): LN forward on every sequence shard (the AllGather is the
+    row-block layout of its output), the 8 MLP shards' forward, the sum of the
+    partials fused with dropout and the residual add (the ReduceScatter),
+    dropout backward, the MLP shards' backward, LN backward with the sum of the
+    input-gradient partials and dγ/dβ.  TFLOP/s over the MLP GEMMs,
+    12·n·d·m_i per shard ([EFF] FLOPs appendix); the SP kernels' time is
+    included."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from tpmlp_inputs import CONFIGS
+    cfg = CONFIGS["sp_block_t8"]
+    s, h, m, t, p = cfg["n"], cfg["d"], cfg["m"], cfg["t"], cfg["p"]
+    mi = m // t
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    bf = torch.bfloat16
+
+    def rnd(shape, std, mean=0.0):
+        return (mean + torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(bf)
+
+    x, g_out = rnd((s, h), 1.0), rnd((s, h), 0.01)
+    gamma, beta = rnd((h,), 0.1, 1.0), rnd((h,), 0.1)
+    A, B = rnd((t, h, mi), 0.02), rnd((t, mi, h), 0.02)
+    U, out, dS, dx = (torch.empty((s, h), dtype=bf, device=dev) for _ in range(4))
+    mean, rstd = (torch.empty(s, dtype=torch.float32, device=dev) for _ in range(2))
+    Z, Y, D = (torch.empty((t, s, mi), dtype=bf, device=dev) for _ in range(3))
+    P, dXp = (torch.empty((t, s, h), dtype=bf, device=dev) for _ in range(2))
+    dA = torch.empty((t, h, mi), dtype=torch.float32, device=dev)
+    dB = torch.empty((t, mi, h), dtype=torch.float32, device=dev)
+    dgamma, dbeta = (torch.empty(h, dtype=torch.float32, device=dev) for _ in range(2))
+    nb = tp.lib().tpmlp_sp_workspace_bytes(s, h)
+    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=dev)
+    P_ = tp._ptr
+    common = dict(dt=tp.BF16, t=t, s=s, h=h, eps=cfg["eps"], p_drop=p, seed=cfg["mask_seed"])
+    a_ln = tp.SpArgs(phase=tp.SP_LN_FWD, x=P_(x), gamma=P_(gamma), beta=P_(beta), ln_out=P_(U), mean=P_(mean),
+                     rstd=P_(rstd), **common)
+    a_dr = tp.SpArgs(phase=tp.SP_DROPRES_FWD, partials=P_(P), x=P_(x), out=P_(out), **common)
+    a_db = tp.SpArgs(phase=tp.SP_DROPRES_BWD, g_out=P_(g_out), dS=P_(dS), **common)
+    a_lb = tp.SpArgs(phase=tp.SP_LN_BWD, dU_partials=P_(dXp), g_out=P_(g_out), x=P_(x), gamma=P_(gamma),
+                     mean=P_(mean), rstd=P_(rstd), dx=P_(dx), dgamma=P_(dgamma), dbeta=P_(dbeta), ws=P_(ws),
+                     ws_bytes=nb, **common)
+    stream = torch.cuda.current_stream()
+    names = ("ln_fwd", "mlp_fwd", "reduce_dropout_residual", "dropout_bwd", "mlp_bwd", "ln_bwd_with_reduce")
+
+    def step(ev=None):
+        rec = (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None)
+        rec(0)
+        tp.tpmlp_ln_sp(a_ln, stream)
+        rec(1)
+        tp.tpmlp_fwd(U, A, B, Z, Y, P, stream)
+        rec(2)
+        tp.tpmlp_ln_sp(a_dr, stream)
+        rec(3)
+        tp.tpmlp_ln_sp(a_db, stream)
+        rec(4)
+        tp.tpmlp_bwd(U, A, B, Z, Y, dS, D, dA, dB, dXp, None, stream)
+        rec(5)
+        tp.tpmlp_ln_sp(a_lb, stream)
+        rec(6)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(reps)]
+    for k in range(reps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    step_ms = [e[0].elapsed_time(e[6]) for e in evs]
+    med = float(np.median(step_ms))
+    flops = 12.0 * s * h * mi * t
+    parts = {nm: round(float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])), 4)
+             for i, nm in enumerate(names)}
+    gemm_ms = parts["mlp_fwd"] + parts["mlp_bwd"]
+    _ = ctypes  # the SpArgs structures hold the raw pointers for the calls above
+    return {"workload": f"sequence-parallel block step: s={s}, h={h}, m={m}, t={t} sequence and tensor shards "
+                        f"resident, p={p}, bf16 (LN -> MLP fwd -> reduce+dropout+residual -> dropout bwd -> "
+                        f"MLP bwd -> LN bwd with the dU reduce)",
+            "flop": flops, "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "gemm_only_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
+            "median_ms_by_part": parts, **_stats(step_ms)}
 
 
 def leg_biased(tp, X, A_s, B_s, G, bufs, reps, flops):
@@ -362,18 +566,28 @@ def leg_attention(tp, reps):
                        f"resident, b={b}, s={s}, causal, bf16"}
     gemm_f = 2.0 * n * d * 3 * w * t + 2.0 * n * w * d * t
     core_f_flop = 4.0 * b * s * s * d            # QK^T and A·V over all heads, pages' formula
-    for name, fn, fl in (("fwd", fwd, gemm_f + core_f_flop), ("bwd", bwd, 2 * gemm_f + 2 * core_f_flop),
-                         ("core_fwd", core_f, core_f_flop), ("core_bwd", core_b, 2 * core_f_flop)):
+    # executed work of the causal core: only the s(s+1)/2 visible (query, key)
+    # pairs of each sequence and head are computed
+    core_f_exec = core_f_flop * (s + 1) / (2.0 * s)
+    for name, fn, fl, fx in (("fwd", fwd, gemm_f + core_f_flop, gemm_f + core_f_exec),
+                             ("bwd", bwd, 2 * gemm_f + 2 * core_f_flop, 2 * gemm_f + 2 * core_f_exec),
+                             ("core_fwd", core_f, core_f_flop, core_f_exec),
+                             ("core_bwd", core_b, 2 * core_f_flop, 2 * core_f_exec)):
         ms = _time_events(fn, reps)
         med = float(np.median(ms))
-        out[name] = {"flop_pages_formula": fl, "tflops_median": round(fl / (med * 1e-3) / 1e12, 2),
+        out[name] = {"flop_executed": fx, "tflops_median": round(fx / (med * 1e-3) / 1e12, 2),
+                     "pct_of_peak": round(100.0 * fx / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "flop_pages_formula": fl, "tflops_pages_formula": round(fl / (med * 1e-3) / 1e12, 2),
                      **_stats(ms)}
-        if name.startswith("core"):
-            out[name]["tflops_causal_half"] = round(fl / 2 / (med * 1e-3) / 1e12, 2)
     step = out["fwd"]["median_ms"] + out["bwd"]["median_ms"]
-    tot = 3 * gemm_f + 3 * core_f_flop
-    out["step"] = {"median_ms": round(step, 4), "tflops": round(tot / (step * 1e-3) / 1e12, 2),
-                   "pct_of_peak": round(100.0 * tot / (step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    tot_x = 3 * gemm_f + 3 * core_f_exec
+    tot_p = 3 * gemm_f + 3 * core_f_flop
+    out["step"] = {"median_ms": round(step, 4), "flop_executed": tot_x,
+                   "tflops": round(tot_x / (step * 1e-3) / 1e12, 2),
+                   "pct_of_peak": round(100.0 * tot_x / (step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                   "tflops_pages_formula": round(tot_p / (step * 1e-3) / 1e12, 2),
+                   "note": "tflops counts executed work (the causal core's visible pairs); "
+                           "tflops_pages_formula counts 4·b·s²·h for the core regardless of the mask"}
     # the core with a general mask instead: BERT-style padding (lengths drawn
     # from [s/2, s], padded query rows see no key), not causal; the flop count
     # is the pages' unmasked one, so the rate is what the mask leaves of it
@@ -554,11 +768,15 @@ def main():
 
     # timed region: K whole steps, events around each entry point
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    clocks = ClockSampler()
+    idle_clk = clocks.read()[0] if clocks.error is None else None
+    clocks.start()
     t_wall0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    clocks.stop()
 
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     r1_ms = [e[1].elapsed_time(e[2]) for e in evs]
@@ -610,6 +828,7 @@ def main():
                             "frac": round(red_gbs / PEAK_HBM_GBS, 4),
                             "traffic": recorded_traffic("reduce.hip", "reduce_gpt8p3b_t8_traffic.md"),
                             "bytes_per_launch": red_bytes, "avg_launch_ms": round(red_ms, 4)},
+        "sclk_mhz": {**clocks.summary(), "before_timed_mhz": idle_clk},
         "wall_s_timed": round(wall, 3),
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
     }
@@ -628,10 +847,15 @@ def main():
         torch.cuda.empty_cache()
         rec["per_rank"] = {"workload": "one shard of the 8.3B-shaped layer per launch (t_local=1)",
                            **leg_mlp_shard(tp, n, d, mi, 20, seed=1)}
+        rec["c2"] = {"workload": "single-shard layer: n=b*s=4*512=2048, d=1024, m=4096, t=1 (fwd+bwd, no "
+                                 "reduction: with one shard the sum is the partial itself)",
+                     **leg_mlp_shard(tp, 2048, 1024, 4096, 20, seed=4, inner=20)}
         rec["gpt1t_shard"] = {"workload": "GPT-1T-shaped shard: h=25600, m_i=12800, n=2048 tokens, one shard",
                               **leg_mlp_shard(tp, 2048, 25600, 12800, 10, seed=2)}
         torch.cuda.empty_cache()
         rec["sp_region"] = leg_sp(tp, 10)
+        torch.cuda.empty_cache()
+        rec["c5_block"] = leg_c5_block(tp, 10)
         torch.cuda.empty_cache()
         rec["attention"] = leg_attention(tp, 10)
         torch.cuda.empty_cache()

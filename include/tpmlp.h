@@ -1,8 +1,9 @@
 /*
  * tpmlp.h -- C ABI of the tensor-parallel MLP shard library for AMD MI355X
  * (gfx950).  Every entry point enqueues HIP kernels on the caller's stream and
- * returns; nothing here allocates, keeps a pointer after returning, or holds
- * global mutable state.  The library is thread-safe.
+ * returns; nothing here allocates or keeps a pointer after returning.  The
+ * only host state is the per-thread code of the last failed launch
+ * (tpmlp_last_hip_error).  The library is thread-safe.
  *
  * Sources (page title, section):
  *   [TUT]   "024｜Megatron-LM：按矩阵结构切分 Transformer，减少模型并行通信",
@@ -46,9 +47,12 @@
  *     graph on the caller's stream and replayed (replays read the buffers'
  *     contents at replay time).
  *   - bf16 operands need 16-byte aligned base pointers and row lengths that
- *     are multiples of 8 elements (d % 8 == 0, m_i % 8 == 0); f32 operands
- *     need 4-byte alignment only.  Each per-shard operand must be smaller
- *     than 2^31 bytes.
+ *     are multiples of 8 elements (d % 8 == 0, m_i % 8 == 0); so do the fp32
+ *     weight gradients the bf16 path writes (dA, dB, dW_qkv, dW_proj, dW:
+ *     16-byte aligned, written with 16-byte stores).  On the f32 path the
+ *     GEMM operands and outputs need 4-byte alignment only; tpmlp_ln_sp has
+ *     its own rules (below).  Each per-shard operand must be smaller than
+ *     2^31 bytes.
  */
 #ifndef TPMLP_H
 #define TPMLP_H
@@ -81,8 +85,14 @@ enum {
  * tpmlp_fwd -- forward of t_local MLP shards ([TUT] §二; [SENSE] Eq.(1)/(2)).
  *
  *   Z_i = X·A_i          [n, m_i]   (stored: the backward needs it)
- *   Y_i = GeLU(Z_i)      [n, m_i]   exact erf GeLU, evaluated on the fp32
- *                                   accumulator before Z_i is rounded
+ *   Y_i = GeLU(Z_i)      [n, m_i]   the erf GeLU z·Φ(z), evaluated on the
+ *                                   fp32 accumulator before Z_i is rounded.
+ *                                   f32 path: erff from the device library.
+ *                                   bf16 path: a clamped odd polynomial of
+ *                                   degree 9 in z² for Φ on |z| <= 4.5 (Φ
+ *                                   exactly 0 / 1 beyond), |GeLU error| <=
+ *                                   7e-5 over all z, far below bf16's 2^-9
+ *                                   relative resolution
  *   P_i = Y_i·B_i        [n, d]     row-parallel partial output; O = Σ_i P_i
  *                                   is formed by tpmlp_reduce_partials
  *
@@ -117,8 +127,12 @@ int tpmlp_fwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i
 /*
  * tpmlp_bwd -- backward of t_local MLP shards ([TUT] §二).
  *
- *   D_i   = (G·B_iᵀ) ⊙ GeLU'(Z_i)   [n, m_i]  dt; GeLU' is evaluated on the
- *                                            stored Z_i
+ *   D_i   = (G·B_iᵀ) ⊙ GeLU'(Z_i)   [n, m_i]  dt; GeLU' = Φ(z) + z·ϕ(z) is
+ *                                            evaluated on the stored Z_i
+ *                                            (f32 path: erff / expf; bf16
+ *                                            path: the same kind of clamped
+ *                                            polynomial as the forward,
+ *                                            |GeLU' error| <= 1.5e-4)
  *   dA_i  = Xᵀ·D_i                  [d, m_i]  fp32
  *   dB_i  = Y_iᵀ·G                  [m_i, d]  fp32
  *   dX_i  = D_i·A_iᵀ                [n, d]    dt, partial input gradient;
@@ -127,6 +141,7 @@ int tpmlp_fwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i
  *
  *   Inputs X, A, B as for tpmlp_fwd; Z, Y from tpmlp_fwd; G [n, d] the
  *   upstream gradient ∂ℓ/∂O.  With n == 0, dA and dB are set to zero.
+ *   dA and dB: 16-byte aligned on the bf16 path, 4-byte on the f32 path.
  *   ws / ws_bytes: workspace, at least tpmlp_bwd_workspace_bytes(...) bytes
  *   (may be NULL when that is 0).
  */

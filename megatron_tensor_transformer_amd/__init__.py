@@ -114,6 +114,44 @@ def _dt(t):
     raise TpmlpValueError(ERR_DTYPE, f"unsupported dtype {t.dtype}")
 
 
+def _expect(ref, *specs, final=True):
+    """Check every tensor an entry point reads or writes before the library is
+    called: the C side receives bare pointers and cannot check extents, so a
+    tensor of the wrong shape, dtype or device would be read or written past
+    its allocation.  ref is the tensor that fixes the device; each spec is
+    (name, tensor, shape, dtype), where a None tensor is skipped (an optional
+    argument) and a shape entry of None matches any size.  final: this is the
+    entry point's last check, so the common device must also be a GPU."""
+    for name, t, shape, dtype in specs:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TpmlpValueError(ERR_ARG, f"{name} is not a tensor")
+        if t.device != ref.device:
+            raise TpmlpValueError(ERR_ARG, f"{name} is on {t.device}, expected {ref.device}")
+        if dtype is not None and t.dtype != dtype:
+            raise TpmlpValueError(ERR_DTYPE, f"{name} has dtype {t.dtype}, expected {dtype}")
+        if shape is not None:
+            if t.dim() != len(shape) or any(e is not None and int(a) != int(e) for a, e in zip(t.shape, shape)):
+                want = tuple("*" if e is None else int(e) for e in shape)
+                raise TpmlpValueError(ERR_SHAPE, f"{name} has shape {tuple(t.shape)}, expected {want}")
+    if final and not ref.is_cuda:
+        raise TpmlpValueError(ERR_ARG, "tensor is not on a GPU")
+
+
+def _path_dtype(X):
+    """The path dtype of an entry point, from its first activation operand."""
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TpmlpValueError(ERR_DTYPE, f"unsupported dtype {X.dtype}")
+    return X.dtype
+
+
+def _dims(name, t, nd):
+    if not isinstance(t, torch.Tensor) or t.dim() != nd:
+        raise TpmlpValueError(ERR_SHAPE, f"{name} must be a {nd}-d tensor")
+    return tuple(int(x) for x in t.shape)
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -130,33 +168,56 @@ def _stream(stream):
 
 
 # ---------------------------------------------------------------- raw entry points
+def _mlp_fwd_check(X, A, B, Z, Y, P, b1=None):
+    t, d, mi = _dims("A", A, 3)
+    n = _dims("X", X, 2)[0]
+    dt = _path_dtype(X)
+    _expect(X, ("X", X, (n, d), dt), ("A", A, (t, d, mi), dt), ("B", B, (t, mi, d), dt),
+            ("b1", b1, (t, mi), dt), ("Z", Z, (t, n, mi), dt), ("Y", Y, (t, n, mi), dt), ("P", P, (t, n, d), dt))
+    return t, d, mi, n
+
+
 def tpmlp_fwd(X, A, B, Z, Y, P, stream=None):
     """X [n,d]; A [t,d,m_i]; B [t,m_i,d]; Z, Y [t,n,m_i]; P [t,n,d] (all one dtype)."""
-    t, d, mi = A.shape
-    n = X.shape[0]
+    t, d, mi, n = _mlp_fwd_check(X, A, B, Z, Y, P)
     _check(lib().tpmlp_fwd(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B),
                            _ptr(Z), _ptr(Y), _ptr(P)))
 
 
 def tpmlp_fwd_bias(X, A, B, b1, Z, Y, P, stream=None):
     """tpmlp_fwd with the column bias b1 [t, m_i] (dtype of X)."""
-    t, d, mi = A.shape
-    n = X.shape[0]
+    if b1 is None:
+        raise TpmlpValueError(ERR_NULLPTR, "b1 is required")
+    t, d, mi, n = _mlp_fwd_check(X, A, B, Z, Y, P, b1)
     _check(lib().tpmlp_fwd_bias(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B), _ptr(b1),
                                 _ptr(Z), _ptr(Y), _ptr(P)))
 
 
 def tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, ws=None, stream=None):
     """Gradients of t_local shards; dA [t,d,m_i] and dB [t,m_i,d] are fp32."""
-    t, d, mi = A.shape
-    n = X.shape[0]
+    t, d, mi = _dims("A", A, 3)
+    n = _dims("X", X, 2)[0]
+    dt, f32 = _path_dtype(X), torch.float32
+    _expect(X, ("X", X, (n, d), dt), ("A", A, (t, d, mi), dt), ("B", B, (t, mi, d), dt),
+            ("Z", Z, (t, n, mi), dt), ("Y", Y, (t, n, mi), dt), ("G", G, (n, d), dt), ("D", D, (t, n, mi), dt),
+            ("dA", dA, (t, d, mi), f32), ("dB", dB, (t, mi, d), f32), ("dXp", dXp, (t, n, d), dt),
+            ("ws", ws, None, None))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_bwd(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B), _ptr(Z),
                            _ptr(Y), _ptr(G), _ptr(D), _ptr(dA), _ptr(dB), _ptr(dXp), _ptr(ws), ws_bytes))
 
 
+def _reduce_check(partials, out, final=True):
+    if not isinstance(partials, torch.Tensor) or not isinstance(out, torch.Tensor) or partials.dim() < 2:
+        raise TpmlpValueError(ERR_SHAPE, "partials must be [t, rows, ...] and out [rows, ...]")
+    _path_dtype(partials)
+    _path_dtype(out)
+    _expect(partials, ("out", out, tuple(partials.shape[1:]), out.dtype), final=final)
+
+
 def tpmlp_reduce_partials(partials, out, stream=None):
     """out [rows, cols] = Σ_i partials[i]."""
+    _reduce_check(partials, out)
     t = partials.shape[0]
     rows = out.shape[0]
     cols = out.numel() // rows if rows else (out.shape[1] if out.dim() > 1 else 1)
@@ -166,16 +227,22 @@ def tpmlp_reduce_partials(partials, out, stream=None):
 
 def tpmlp_reduce_partials_bias(partials, bias, out, stream=None):
     """out [rows, cols] = Σ_i partials[i] + bias (bias [cols], dtype of out)."""
+    if bias is None:
+        raise TpmlpValueError(ERR_NULLPTR, "bias is required")
+    _reduce_check(partials, out, final=False)
     t = partials.shape[0]
     rows = out.shape[0]
     cols = out.numel() // rows if rows else (out.shape[1] if out.dim() > 1 else 1)
+    _expect(out, ("bias", bias, (cols,), out.dtype))
     _check(lib().tpmlp_reduce_partials_bias(_stream(stream), _dt(partials), _dt(out), t, rows, cols,
                                             _ptr(partials), _ptr(bias), _ptr(out)))
 
 
 def tpmlp_bias_grad(g, db, ws=None, stream=None):
     """db [t, cols] (fp32) = Σ_rows g [t, rows, cols]."""
-    t, rows, cols = g.shape
+    t, rows, cols = _dims("g", g, 3)
+    _expect(g, ("g", g, (t, rows, cols), _path_dtype(g)), ("db", db, (t, cols), torch.float32),
+            ("ws", ws, None, None))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_bias_grad(_stream(stream), _dt(g), t, rows, cols, _ptr(g), _ptr(db), _ptr(ws),
                                  ws_bytes))
@@ -187,6 +254,7 @@ def tpmlp_attn_pack_mask(mask, packed, stream=None):
     if mask.dtype not in (torch.uint8, torch.bool) or mask.dim() != 3 or mask.shape[1] != mask.shape[2]:
         raise TpmlpValueError(ERR_ARG, "mask must be uint8 or bool of shape (b, s, s)")
     b, s, _ = mask.shape
+    _expect(mask, ("packed", packed, (2, b, s, (s + 31) // 32), torch.int32))
     _check(lib().tpmlp_attn_pack_mask(_stream(stream), b, s, _ptr(mask), _ptr(packed)))
 
 
@@ -215,12 +283,34 @@ def _mask_ptr(mask, s, b, stream):
     return _ptr(mask), mask
 
 
+def _attn_fwd_check(X, Wqkv, Wproj, bqkv, QKV, O, lse, P, s, b, head_dim, final=True):
+    t, d, w3 = _dims("Wqkv", Wqkv, 3)
+    if head_dim <= 0 or w3 % (3 * head_dim):
+        raise TpmlpValueError(ERR_SHAPE, f"Wqkv's {w3} columns are not heads of 3·{head_dim}")
+    heads = w3 // 3 // head_dim
+    n, w = s * b, w3 // 3
+    dt = _path_dtype(X)
+    _expect(X, ("X", X, (n, d), dt), ("Wqkv", Wqkv, (t, d, w3), dt), ("Wproj", Wproj, (t, w, d), dt),
+            ("bqkv", bqkv, (t, w3), dt), ("QKV", QKV, (t, n, w3), dt), ("O", O, (t, n, w), dt),
+            ("lse", lse, (t, b, heads, s), torch.float32), ("P", P, (t, n, d), dt), final=final)
+    return t, d, heads
+
+
+def _attn_core_check(qkv, o, lse, d_o, dqkv, s, b, heads, head_dim, final=True):
+    t = _dims("qkv", qkv, 3)[0]
+    n, w = s * b, heads * head_dim
+    dt = _path_dtype(qkv)
+    _expect(qkv, ("qkv", qkv, (t, n, 3 * w), dt), ("o", o, (t, n, w), dt),
+            ("lse", lse, (t, b, heads, s), torch.float32), ("d_o", d_o, (t, n, w), dt),
+            ("dqkv", dqkv, (t, n, 3 * w), dt), final=final)
+    return t
+
+
 def tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, mask=None, stream=None):
     """X [s·b, d]; Wqkv [t, d, 3w]; Wproj [t, w, d]; QKV [t, s·b, 3w]; O [t, s·b, w];
     lse [t, b, heads, s] fp32; P [t, s·b, d]; w = heads·head_dim; mask None, a
     packed mask (attn_pack_mask) or a [b, s, s] uint8/bool mask."""
-    t, d, w3 = Wqkv.shape
-    heads = w3 // 3 // head_dim
+    t, d, heads = _attn_fwd_check(X, Wqkv, Wproj, None, QKV, O, lse, P, s, b, head_dim)
     mp, _keep = _mask_ptr(mask, s, b, stream)
     _check(lib().tpmlp_attn_fwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), mp, _ptr(X),
                                 _ptr(Wqkv), _ptr(Wproj), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(P)))
@@ -228,8 +318,9 @@ def tpmlp_attn_fwd(X, Wqkv, Wproj, QKV, O, lse, P, s, b, head_dim, causal, mask=
 
 def tpmlp_attn_fwd_bias(X, Wqkv, Wproj, bqkv, QKV, O, lse, P, s, b, head_dim, causal, mask=None, stream=None):
     """tpmlp_attn_fwd with the QKV column bias bqkv [t, 3w] added in the QKV GEMM."""
-    t, d, w3 = Wqkv.shape
-    heads = w3 // 3 // head_dim
+    if bqkv is None:
+        raise TpmlpValueError(ERR_NULLPTR, "bqkv is required")
+    t, d, heads = _attn_fwd_check(X, Wqkv, Wproj, bqkv, QKV, O, lse, P, s, b, head_dim)
     mp, _keep = _mask_ptr(mask, s, b, stream)
     _check(lib().tpmlp_attn_fwd_bias(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), mp,
                                      _ptr(X), _ptr(Wqkv), _ptr(Wproj), _ptr(bqkv), _ptr(QKV), _ptr(O), _ptr(lse),
@@ -238,8 +329,12 @@ def tpmlp_attn_fwd_bias(X, Wqkv, Wproj, bqkv, QKV, O, lse, P, s, b, head_dim, ca
 
 def tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp, ws, s, b, head_dim, causal,
                    mask=None, stream=None):
-    t, d, w3 = Wqkv.shape
-    heads = w3 // 3 // head_dim
+    t, d, heads = _attn_fwd_check(X, Wqkv, Wproj, None, QKV, O, lse, None, s, b, head_dim, final=False)
+    n, w = s * b, heads * head_dim
+    dt, f32 = X.dtype, torch.float32
+    _expect(X, ("G", G, (n, d), dt), ("dO", dO, (t, n, w), dt), ("dQKV", dQKV, (t, n, 3 * w), dt),
+            ("dWqkv", dWqkv, (t, d, 3 * w), f32), ("dWproj", dWproj, (t, w, d), f32), ("dXp", dXp, (t, n, d), dt),
+            ("ws", ws, None, None))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     mp, _keep = _mask_ptr(mask, s, b, stream)
     _check(lib().tpmlp_attn_bwd(_stream(stream), _dt(X), s, b, d, heads, head_dim, t, int(causal), mp, _ptr(X),
@@ -249,14 +344,15 @@ def tpmlp_attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, dO, dQKV, dWqkv, dWproj, dXp,
 
 def tpmlp_attn_core_fwd(qkv, o, lse, s, b, heads, head_dim, causal, mask=None, stream=None):
     """qkv [t, s·b, heads·3·head_dim] -> o [t, s·b, heads·head_dim], lse [t, b, heads, s]."""
-    t = qkv.shape[0]
+    t = _attn_core_check(qkv, o, lse, None, None, s, b, heads, head_dim)
     mp, _keep = _mask_ptr(mask, s, b, stream)
     _check(lib().tpmlp_attn_core_fwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), mp,
                                      _ptr(qkv), _ptr(o), _ptr(lse)))
 
 
 def tpmlp_attn_core_bwd(qkv, o, lse, d_o, dqkv, ws, s, b, heads, head_dim, causal, mask=None, stream=None):
-    t = qkv.shape[0]
+    t = _attn_core_check(qkv, o, lse, d_o, dqkv, s, b, heads, head_dim, final=False)
+    _expect(qkv, ("ws", ws, None, None))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     mp, _keep = _mask_ptr(mask, s, b, stream)
     _check(lib().tpmlp_attn_core_bwd(_stream(stream), _dt(qkv), t, s, b, heads, head_dim, int(causal), mp,
@@ -334,7 +430,8 @@ def bias_grad(g, stream=None):
 
 
 def sp_ln_fwd(x, gamma, beta, t, eps=1e-5, stream=None):
-    s, h = x.shape
+    s, h = _dims("x", x, 2)
+    _expect(x, ("gamma", gamma, (h,), _path_dtype(x)), ("beta", beta, (h,), x.dtype))
     U = torch.empty_like(x)
     mean = torch.empty(s, dtype=torch.float32, device=x.device)
     rstd = torch.empty_like(mean)
@@ -345,8 +442,9 @@ def sp_ln_fwd(x, gamma, beta, t, eps=1e-5, stream=None):
 
 
 def sp_dropres_fwd(partials, x, p, seed, row0=0, bias=None, stream=None):
-    t = partials.shape[0]
-    s, h = x.shape
+    t = _dims("partials", partials, 3)[0]
+    s, h = _dims("x", x, 2)
+    _expect(x, ("partials", partials, (t, s, h), _path_dtype(x)), ("bias", bias, (h,), x.dtype))
     out = torch.empty_like(x)
     a = SpArgs(phase=SP_DROPRES_FWD, dt=_dt(x), t=t, s=s, h=h, row0=row0, eps=1.0, p_drop=p, seed=seed,
                partials=_ptr(partials), x=_ptr(x), out=_ptr(out), bias=_ptr(bias))
@@ -355,7 +453,8 @@ def sp_dropres_fwd(partials, x, p, seed, row0=0, bias=None, stream=None):
 
 
 def sp_dropres_bwd(g_out, t, p, seed, row0=0, stream=None):
-    s, h = g_out.shape
+    s, h = _dims("g_out", g_out, 2)
+    _path_dtype(g_out)
     dS = torch.empty_like(g_out)
     a = SpArgs(phase=SP_DROPRES_BWD, dt=_dt(g_out), t=t, s=s, h=h, row0=row0, eps=1.0, p_drop=p,
                seed=seed, g_out=_ptr(g_out), dS=_ptr(dS))
@@ -364,8 +463,11 @@ def sp_dropres_bwd(g_out, t, p, seed, row0=0, stream=None):
 
 
 def sp_ln_bwd(dU_partials, g_out, x, gamma, mean, rstd, stream=None):
-    t = dU_partials.shape[0]
-    s, h = x.shape
+    t = _dims("dU_partials", dU_partials, 3)[0]
+    s, h = _dims("x", x, 2)
+    dt = _path_dtype(x)
+    _expect(x, ("dU_partials", dU_partials, (t, s, h), dt), ("g_out", g_out, (s, h), dt),
+            ("gamma", gamma, (h,), dt), ("mean", mean, (s,), torch.float32), ("rstd", rstd, (s,), torch.float32))
     dx = torch.empty_like(x)
     dgamma = torch.empty(h, dtype=torch.float32, device=x.device)
     dbeta = torch.empty_like(dgamma)
@@ -416,10 +518,20 @@ def attn_bwd(X, Wqkv, Wproj, QKV, O, lse, G, s, b, head_dim, causal=True, mask=N
 
 
 # ---------------------------------------------------------------- vocabulary-parallel cross-entropy
+def _vocab_check(X, W, targets, logits, row_max, row_sum, final=True):
+    t, vi, h = _dims("W", W, 3)
+    n = _dims("X", X, 2)[0]
+    dt, f32 = _path_dtype(X), torch.float32
+    _expect(X, ("X", X, (n, h), dt), ("W", W, (t, vi, h), dt), ("targets", targets, (n,), torch.int32),
+            ("logits", logits, (t, n, vi), dt), ("row_max", row_max, (n,), f32), ("row_sum", row_sum, (n,), f32),
+            final=final)
+    return t, vi, h, n
+
+
 def tpmlp_vocab_ce_fwd(X, W, targets, logits, loss, row_max, row_sum, ws, vocab_start=0, stream=None):
     """X [n,h]; W [t,v_i,h]; targets [n] int32; logits [t,n,v_i]; loss, row_max, row_sum [n] fp32."""
-    t, vi, h = W.shape
-    n = X.shape[0]
+    t, vi, h, n = _vocab_check(X, W, targets, logits, row_max, row_sum, final=False)
+    _expect(X, ("loss", loss, (n,), torch.float32), ("ws", ws, None, None))
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_vocab_ce_fwd(_stream(stream), _dt(X), n, h, vi, t, vocab_start, _ptr(X), _ptr(W),
                                     _ptr(targets), _ptr(logits), _ptr(loss), _ptr(row_max), _ptr(row_sum),
@@ -427,8 +539,9 @@ def tpmlp_vocab_ce_fwd(X, W, targets, logits, loss, row_max, row_sum, ws, vocab_
 
 
 def tpmlp_vocab_ce_bwd(X, W, targets, logits, row_max, row_sum, g, dlogits, dW, dXp, vocab_start=0, stream=None):
-    t, vi, h = W.shape
-    n = X.shape[0]
+    t, vi, h, n = _vocab_check(X, W, targets, logits, row_max, row_sum, final=False)
+    _expect(X, ("g", g, (n,), torch.float32), ("dlogits", dlogits, (t, n, vi), X.dtype),
+            ("dW", dW, (t, vi, h), torch.float32), ("dXp", dXp, (t, n, h), X.dtype))
     _check(lib().tpmlp_vocab_ce_bwd(_stream(stream), _dt(X), n, h, vi, t, vocab_start, _ptr(X), _ptr(W),
                                     _ptr(targets), _ptr(logits), _ptr(row_max), _ptr(row_sum), _ptr(g),
                                     _ptr(dlogits), _ptr(dW), _ptr(dXp)))

@@ -44,6 +44,10 @@ int check_mlp_dims(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
   return TPMLP_OK;
 }
 
+// fp32 weight gradients: the bf16 path's GEMM epilogue writes them with 16-B
+// vector stores (4 consecutive columns; rows are multiples of 8 columns)
+uintptr_t wgrad_align(int dt) { return dt == TPMLP_BF16 ? 16 : 4; }
+
 int check_ptrs(int dt, std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if (p == nullptr) return TPMLP_ERR_NULLPTR;
@@ -172,7 +176,7 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
   if (ws_bytes < tpmlp_bwd_workspace_bytes(dt, n, d, m_i, t_local)) return TPMLP_ERR_WORKSPACE;
   (void)ws;
   if (dA == nullptr || dB == nullptr) return TPMLP_ERR_NULLPTR;
-  if (!aligned(dA, 4) || !aligned(dB, 4)) return TPMLP_ERR_ALIGN;
+  if (!aligned(dA, wgrad_align(dt)) || !aligned(dB, wgrad_align(dt))) return TPMLP_ERR_ALIGN;
   if (n > 0) {
     st = check_ptrs(dt, {X, A, B, Z, Y, G, D, dXp});
     if (st) return st;
@@ -587,7 +591,7 @@ int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, 
   st = check_mlp_dims(dt, n, d, 3 * w, t_local);
   if (st) return st;
   if (dWqkv == nullptr || dWproj == nullptr) return TPMLP_ERR_NULLPTR;
-  if (!aligned(dWqkv, 4) || !aligned(dWproj, 4)) return TPMLP_ERR_ALIGN;
+  if (!aligned(dWqkv, wgrad_align(dt)) || !aligned(dWproj, wgrad_align(dt))) return TPMLP_ERR_ALIGN;
   if (s > 0) {
     st = check_ptrs(dt, {X, Wqkv, Wproj, QKV, O, G, dO, dQKV, dXp});
     if (st) return st;
@@ -755,7 +759,7 @@ int tpmlp_vocab_ce_bwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t
   if (st) return st;
   if (vocab_start < 0) return TPMLP_ERR_ARG;
   if (dW == nullptr) return TPMLP_ERR_NULLPTR;
-  if (!aligned(dW, 4)) return TPMLP_ERR_ALIGN;
+  if (!aligned(dW, wgrad_align(dt))) return TPMLP_ERR_ALIGN;
   if (n > 0) {
     st = check_ptrs(dt, {X, W, logits, dlogits, dXp});
     if (st) return st;

@@ -199,6 +199,13 @@ def test_bwd_validation(L):
     a[6] = z  # D missing
     assert L.tpmlp_bwd(None, 1, 64, 64, 64, 2, *a, None, 0) == tp.ERR_NULLPTR
     assert L.tpmlp_bwd_workspace_bytes(1, 8192, 3072, 1536, 8) == 0
+    # the bf16 path writes the fp32 weight gradients with 16-byte stores
+    for k in (7, 8):  # dA, dB
+        a = [p] * 10
+        a[k] = ctypes.c_void_p(0x1008)
+        assert L.tpmlp_bwd(None, 1, 64, 64, 64, 2, *a, None, 0) == tp.ERR_ALIGN
+        a[6] = z  # f32 path: 4-byte alignment suffices, so the next check (D) fails
+        assert L.tpmlp_bwd(None, 0, 64, 64, 64, 2, *a, None, 0) == tp.ERR_NULLPTR
 
 
 def test_reduce_validation(L):
