@@ -3,7 +3,9 @@
  * (gfx950).  Every entry point enqueues HIP kernels on the caller's stream and
  * returns; nothing here allocates or keeps a pointer after returning.  The
  * only host state is the per-thread code of the last failed launch
- * (tpmlp_last_hip_error).  The library is thread-safe.
+ * (tpmlp_last_hip_error) and, once tpmlp_bias_grad_noalloc has run on a
+ * device, that device's address of the library's fixed scratch array (looked
+ * up once, under a lock).  The library is thread-safe.
  *
  * Sources (page title, section):
  *   [TUT]   "024｜Megatron-LM：按矩阵结构切分 Transformer，减少模型并行通信",
@@ -66,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 6
+#define TPMLP_ABI_VERSION 7
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -78,7 +80,9 @@ enum {
   TPMLP_ERR_ALIGN = -4,     /* bf16 base pointer not 16-B aligned or row length % 8 */
   TPMLP_ERR_HIP = -5,       /* a kernel launch failed (tpmlp_last_hip_error)     */
   TPMLP_ERR_WORKSPACE = -6, /* workspace missing or smaller than required        */
-  TPMLP_ERR_ARG = -7        /* other invalid argument (phase, probability, eps)  */
+  TPMLP_ERR_ARG = -7,       /* other invalid argument (phase, probability, eps)  */
+  TPMLP_ERR_SCRATCH = -8    /* more scratch needed than an allocation-free entry
+                               point's fixed array holds                         */
 };
 
 /*
@@ -201,6 +205,29 @@ int tpmlp_reduce_partials_bias(hipStream_t stream, int in_dt, int out_dt, int32_
 size_t tpmlp_bias_grad_workspace_bytes(int32_t t, int64_t rows, int64_t cols);
 int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,
                     float* db, void* ws, size_t ws_bytes);
+
+/*
+ * tpmlp_bias_grad_noalloc -- tpmlp_bias_grad without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments (minus ws / ws_bytes), kernels, fixed
+ * summation order and results, bit for bit, as tpmlp_bias_grad.
+ *
+ * The chunk partials go to a fixed device array of the library,
+ * TPMLP_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, which each GPU the library
+ * runs on holds until the process ends; its address is looked up on the
+ * first call on a device.  A call whose tpmlp_bias_grad_workspace_bytes(t,
+ * rows, cols) exceeds it returns TPMLP_ERR_SCRATCH with nothing enqueued
+ * (the 8.3B-shaped layer's db1, t = 8, rows = 8192, cols = 1536, needs
+ * 3 MiB).  The array is shared by every call on that GPU and keeps the last
+ * call's contents (nothing in it needs clearing: each call writes every
+ * partial it reads); calls that overlap on one GPU (other streams, other
+ * threads) race on it and must be serialised by the caller.  A failed
+ * address lookup returns TPMLP_ERR_HIP.
+ */
+#define TPMLP_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int tpmlp_bias_grad_noalloc(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,
+                            float* db);
 
 /*
  * tpmlp_ln_sp -- the sequence-parallel region around one MLP block

@@ -20,6 +20,8 @@ F32, BF16 = 0, 1
 SP_LN_FWD, SP_DROPRES_FWD, SP_DROPRES_BWD, SP_LN_BWD = 0, 1, 2, 3
 
 ERR_NULLPTR, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_HIP, ERR_WORKSPACE, ERR_ARG = -1, -2, -3, -4, -5, -6, -7
+ERR_SCRATCH = -8
+NOALLOC_SCRATCH_BYTES = 16 << 20  # TPMLP_NOALLOC_SCRATCH_BYTES
 
 
 class TpmlpError(RuntimeError):
@@ -62,6 +64,7 @@ SIGNATURES = {
     "tpmlp_reduce_partials_bias": (_I, [_P, _I, _I, _I32, _I64, _I64, _P, _P, _P]),
     "tpmlp_bias_grad_workspace_bytes": (_SZ, [_I32, _I64, _I64]),
     "tpmlp_bias_grad": (_I, [_P, _I, _I32, _I64, _I64, _P, _P, _P, _SZ]),
+    "tpmlp_bias_grad_noalloc": (_I, [_P, _I, _I32, _I64, _I64, _P, _P]),
     "tpmlp_sp_workspace_bytes": (_SZ, [_I64, _I64]),
     "tpmlp_attn_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tpmlp_attn_fwd_bias": (_I, [_P, _I, _I64, _I64, _I64, _I32, _I32, _I32, _I] + [_P] * 9),
@@ -246,6 +249,14 @@ def tpmlp_bias_grad(g, db, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_bias_grad(_stream(stream), _dt(g), t, rows, cols, _ptr(g), _ptr(db), _ptr(ws),
                                  ws_bytes))
+
+
+def tpmlp_bias_grad_noalloc(g, db, stream=None):
+    """tpmlp_bias_grad with the library's fixed scratch array instead of a
+    workspace: allocates nothing (calls on one GPU must not overlap)."""
+    t, rows, cols = _dims("g", g, 3)
+    _expect(g, ("g", g, (t, rows, cols), _path_dtype(g)), ("db", db, (t, cols), torch.float32))
+    _check(lib().tpmlp_bias_grad_noalloc(_stream(stream), _dt(g), t, rows, cols, _ptr(g), _ptr(db)))
 
 
 def tpmlp_attn_pack_mask(mask, packed, stream=None):

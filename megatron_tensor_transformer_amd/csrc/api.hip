@@ -3,6 +3,7 @@
 // every error status is returned with nothing enqueued.
 #include <math.h>
 #include <initializer_list>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/tpmlp.h"
@@ -144,6 +145,8 @@ const char* tpmlp_status_string(int status) {
     case TPMLP_ERR_HIP: return "a HIP kernel launch failed";
     case TPMLP_ERR_WORKSPACE: return "workspace missing or too small";
     case TPMLP_ERR_ARG: return "invalid argument";
+    case TPMLP_ERR_SCRATCH:
+      return "the call needs more scratch than the allocation-free entry point's fixed array holds";
     default: return "unknown status";
   }
 }
@@ -293,8 +296,12 @@ size_t tpmlp_bias_grad_workspace_bytes(int32_t t, int64_t rows, int64_t cols) {
          static_cast<size_t>(cols) * sizeof(float);
 }
 
-int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,
-                    float* db, void* ws, size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+// The checks of tpmlp_bias_grad other than its workspace's.
+int bias_grad_check(int dt, int32_t t, int64_t rows, int64_t cols, const void* g, const float* db) {
   if (!valid_dt(dt)) return TPMLP_ERR_DTYPE;
   if (t < 1 || rows < 0 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return TPMLP_ERR_SHAPE;
   if (rows > 0 && cols > (int64_t{1} << 62) / rows) return TPMLP_ERR_SHAPE;
@@ -308,10 +315,87 @@ int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t
   if (rows > 0) {
     if (g == nullptr) return TPMLP_ERR_NULLPTR;
     if (!aligned(g, elem_size(dt))) return TPMLP_ERR_ALIGN;
+  }
+  return TPMLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpmlp_bias_grad(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,
+                    float* db, void* ws, size_t ws_bytes) {
+  const int st = bias_grad_check(dt, t, rows, cols, g, db);
+  if (st) return st;
+  if (rows > 0) {
     const size_t need = tpmlp_bias_grad_workspace_bytes(t, rows, cols);
     if (ws == nullptr || ws_bytes < need) return TPMLP_ERR_WORKSPACE;
     if (!aligned(ws, 4)) return TPMLP_ERR_ALIGN;
   }
+  return hip_status(tpmlp::launch_bias_grad(dt, t, rows, cols, g, db, static_cast<float*>(ws), stream));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- allocation-free bias gradient
+// tpmlp_bias_grad_noalloc keeps the bias gradient's chunk partials in a fixed
+// device array of the library instead of a caller's workspace.  Each device
+// holds its own copy of the array at its own address: the host-side name
+// `scratch` is only a stand-in, so its device address is looked up once per
+// device (with that device current) and kept; kernels are only ever given the
+// looked-up address.
+namespace {
+
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[TPMLP_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // the address of `scratch` on each device, or null before the lookup
+
+// The scratch address on the device that runs `stream` (the current device
+// for the null stream).  HIP status on failure.
+hipError_t scratch_for(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpmlp_bias_grad_noalloc(hipStream_t stream, int dt, int32_t t, int64_t rows, int64_t cols, const void* g,
+                            float* db) {
+  const int st = bias_grad_check(dt, t, rows, cols, g, db);
+  if (st) return st;
+  if (tpmlp_bias_grad_workspace_bytes(t, rows, cols) > TPMLP_NOALLOC_SCRATCH_BYTES) return TPMLP_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (rows > 0) {  // rows == 0 only zeroes db and needs no scratch
+    const int hs = hip_status(scratch_for(stream, &ws));
+    if (hs) return hs;
+  }
+  // stage 1 writes every chunk partial that stage 2 reads: nothing needs clearing
   return hip_status(tpmlp::launch_bias_grad(dt, t, rows, cols, g, db, static_cast<float*>(ws), stream));
 }
 

@@ -42,8 +42,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 6
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+    assert L.tpmlp_abi_version() == 7
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         assert L.tpmlp_status_string(s)
 
 
@@ -108,6 +108,22 @@ def test_bias_grad_validation(L):
     assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, p, None, need) == tp.ERR_WORKSPACE
     assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, ctypes.c_void_p(0x1001), p, p, need) == tp.ERR_ALIGN
     assert L.tpmlp_bias_grad(None, 1, 2, 300, 64, p, ctypes.c_void_p(0x1002), p, need) == tp.ERR_ALIGN
+
+
+def test_bias_grad_noalloc_validation(L):
+    """Same checks as tpmlp_bias_grad, and inputs whose partials would not fit
+    the fixed 16 MiB scratch array are refused before anything runs."""
+    p = ctypes.c_void_p(0x1000)
+    assert L.tpmlp_bias_grad_noalloc(None, 5, 2, 300, 64, p, p) == tp.ERR_DTYPE
+    assert L.tpmlp_bias_grad_noalloc(None, 1, 0, 300, 64, p, p) == tp.ERR_SHAPE
+    assert L.tpmlp_bias_grad_noalloc(None, 1, 2, 300, 64, p, None) == tp.ERR_NULLPTR
+    assert L.tpmlp_bias_grad_noalloc(None, 1, 2, 300, 64, None, p) == tp.ERR_NULLPTR
+    assert L.tpmlp_bias_grad_noalloc(None, 1, 2, 300, 64, ctypes.c_void_p(0x1001), p) == tp.ERR_ALIGN
+    # 8 shards, 64 chunks of 128 rows, 8200 columns: 16.8 MB of partials > 16 MiB
+    assert L.tpmlp_bias_grad_workspace_bytes(8, 8192, 8200) > tp.NOALLOC_SCRATCH_BYTES
+    assert L.tpmlp_bias_grad_noalloc(None, 1, 8, 8192, 8200, p, p) == tp.ERR_SCRATCH
+    assert L.tpmlp_bias_grad_workspace_bytes(8, 8192, 8192) == tp.NOALLOC_SCRATCH_BYTES
+    assert b"scratch" in L.tpmlp_status_string(tp.ERR_SCRATCH)
 
 
 def test_attn_validation(L):
