@@ -257,9 +257,20 @@ int tpmlp_bias_grad_noalloc(hipStream_t stream, int dt, int32_t t, int64_t rows,
  *                        dgamma, dbeta [h] (f32, summed over all s rows in a
  *                        fixed order; needs ws)
  * LayerNorm: biased variance over h, eps inside the square root, statistics
- * in fp32.  Requirements: t >= 2 (sequence parallelism needs tensor
- * parallelism, [SP] 工程约束), s % t == 0, 0 <= p < 1, eps > 0, bf16 needs
- * h % 8 == 0.
+ * in fp32.  Requirements (checked; SHAPE, ALIGN or ARG otherwise):
+ *   - t >= 2 (sequence parallelism needs tensor parallelism, [SP] 工程约束),
+ *     s >= 0, s % t == 0, row0 >= 0;
+ *   - h >= 8 and h % 8 == 0 for both dtypes (the kernels move 8-element
+ *     chunks); any such width: rows wider than 4096 take a slower
+ *     multi-pass path (the row is re-read from the cache per pass, and LN
+ *     backward forms its two row means in a pass of their own);
+ *   - every tensor pointer 16-byte aligned for both dtypes (f32 included);
+ *     mean, rstd, dgamma, dbeta 4-byte aligned;
+ *   - s·h and t·s·h elements of dt each smaller than 2^31 bytes;
+ *   - 0 <= p < 1, eps > 0.
+ * s == 0 enqueues nothing.  LN_BWD's workspace: tpmlp_sp_workspace_bytes(s,
+ * h) bytes, 4-byte aligned (per-block column partials of dγ/dβ, plus two row
+ * means per row when h > 4096).
  */
 typedef enum {
   TPMLP_SP_LN_FWD = 0,

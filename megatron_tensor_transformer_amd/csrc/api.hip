@@ -401,7 +401,7 @@ int tpmlp_bias_grad_noalloc(hipStream_t stream, int dt, int32_t t, int64_t rows,
 
 size_t tpmlp_sp_workspace_bytes(int64_t s, int64_t h) {
   if (s <= 0 || h <= 0) return 0;
-  return static_cast<size_t>(tpmlp::sp_ln_bwd_row_blocks(s)) * 2 * static_cast<size_t>(h) * sizeof(float);
+  return static_cast<size_t>(tpmlp::sp_workspace_floats(s, h)) * sizeof(float);
 }
 
 int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
@@ -409,7 +409,7 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
   if (!valid_dt(a->dt)) return TPMLP_ERR_DTYPE;
   if (a->phase < TPMLP_SP_LN_FWD || a->phase > TPMLP_SP_LN_BWD) return TPMLP_ERR_ARG;
   if (a->t < 2) return TPMLP_ERR_SHAPE;  // sequence parallelism needs TP > 1
-  if (a->s < 0 || a->h < 8 || a->h > 4096 || a->row0 < 0) return TPMLP_ERR_SHAPE;
+  if (a->s < 0 || a->h < 8 || a->row0 < 0) return TPMLP_ERR_SHAPE;
   if (a->s % a->t != 0) return TPMLP_ERR_SHAPE;
   if (a->h % 8 != 0) return TPMLP_ERR_ALIGN;
   if (!(a->p_drop >= 0.0f && a->p_drop < 1.0f)) return TPMLP_ERR_ARG;
@@ -459,6 +459,7 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
     case TPMLP_SP_LN_FWD:
       st = ok({a->x, a->gamma, a->beta, a->ln_out});
       if (!st && (a->mean == nullptr || a->rstd == nullptr)) st = TPMLP_ERR_NULLPTR;
+      if (!st && (!aligned(a->mean, 4) || !aligned(a->rstd, 4))) st = TPMLP_ERR_ALIGN;
       break;
     case TPMLP_SP_DROPRES_FWD:
       st = ok({a->partials, a->x, a->out});
@@ -472,6 +473,9 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a) {
       if (!st && (a->mean == nullptr || a->rstd == nullptr || a->dgamma == nullptr ||
                   a->dbeta == nullptr))
         st = TPMLP_ERR_NULLPTR;
+      if (!st && (!aligned(a->mean, 4) || !aligned(a->rstd, 4) || !aligned(a->dgamma, 4) ||
+                  !aligned(a->dbeta, 4)))
+        st = TPMLP_ERR_ALIGN;
       if (!st && (a->ws == nullptr || a->ws_bytes < tpmlp_sp_workspace_bytes(a->s, a->h)))
         st = TPMLP_ERR_WORKSPACE;
       if (!st && !aligned(a->ws, 4)) st = TPMLP_ERR_ALIGN;

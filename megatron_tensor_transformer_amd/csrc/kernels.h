@@ -95,7 +95,11 @@ struct SpProblem {
   const void* bias;  // DROPRES_FWD: NULL or [h] of dt, added to Σ_i P_i before the dropout
 };
 
-int64_t sp_ln_bwd_row_blocks(int64_t s);
+// LN backward's per-block column partials: row blocks of the grid, and the
+// floats of the SP workspace (the partials, plus two row means per row when
+// h > 4096)
+int64_t sp_ln_bwd_row_blocks(int64_t s, int64_t h);
+int64_t sp_workspace_floats(int64_t s, int64_t h);
 
 // Attention core of T resident shards (layouts in attention.hip).
 struct AttnProblem {

@@ -14,12 +14,14 @@
 //
 // All kernels are HBM-bound and work on 8-element (16-B bf16) chunks; sums of
 // the t partials load them in unconditional groups so the loads are in flight
-// together, and add them in shard order.  LN forward gives each row one wave
-// (h ≤ 4096: at most 8 chunks per lane, in registers) and reduces with
-// cross-lane shuffles.  LN backward works in 512-thread blocks (thread j owns
-// chunk j of every row) with shuffles plus a fixed-order sum over the 8
-// waves; each block walks a strided set of rows,
-// so its dγ/dβ column partials stay in registers; the sums are deterministic:
+// together, and add them in shard order.  For h ≤ 4096, LN forward gives each
+// row one wave (at most 8 chunks per lane, in registers) and reduces with
+// cross-lane shuffles, and LN backward works in 512-thread blocks (thread j
+// owns chunk j of every row) with shuffles plus a fixed-order sum over the 8
+// waves; each block walks a strided set of rows, so its dγ/dβ column partials
+// stay in registers.  Wider rows loop over 4096-element pieces of the row (a
+// block per row; LN backward first forms the two row means, then dx and the
+// column partials per 4096-column slab).  The sums are deterministic:
 // per-block partials in a fixed row order, then a fixed-order sum over blocks.
 //
 // Dropout mask: Philox-4x32-10 (Salmon, Moraes, Dror & Shaw, SC'11), written
@@ -247,6 +249,146 @@ __global__ __launch_bounds__(SP_THREADS) void ln_fwd_kernel(SpProblem p) {
   }
 }
 
+// ------------------------------------------------------------------ wide rows (h > 4096)
+// Rows wider than 8 chunks per lane of a wave (h > 4096) take a 512-thread
+// block per row, which loops over the row in 4096-element pieces (thread j
+// owns chunks j, j + 512, ...), re-reading the row from the cache in each
+// pass instead of holding it in registers.
+constexpr int LNW_THREADS = 512, LNW_WAVES = LNW_THREADS / WAVE;
+constexpr int64_t LN_FAST_MAX_H = 4096;
+
+// Sum over the block in a fixed order: each wave's butterfly, then the waves'
+// sums in wave order.  Every thread gets the result; `red` may be reused
+// right after (the trailing barrier).
+__device__ __forceinline__ float block_sum_fixed(float v, float* red, int lane, int wave) {
+  v = wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < LNW_WAVES; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(LNW_THREADS) void ln_fwd_wide_kernel(SpProblem p) {
+  __shared__ float red[LNW_WAVES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t hc = p.h / 8;
+  const float inv_h = 1.0f / static_cast<float>(p.h);
+  const T* xr = static_cast<const T*>(p.x) + row * p.h;
+  float sum = 0.f;
+  for (int64_t c = threadIdx.x; c < hc; c += LNW_THREADS) {
+    float v[8];
+    load8<T, false>(xr + c * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += v[e];
+  }
+  const float mean = block_sum_fixed(sum, red, lane, wave) * inv_h;
+  float q = 0.f;
+  for (int64_t c = threadIdx.x; c < hc; c += LNW_THREADS) {
+    float v[8];
+    load8<T, false>(xr + c * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[e] - mean;
+      q += d * d;
+    }
+  }
+  const float rstd = 1.0f / sqrtf(block_sum_fixed(q, red, lane, wave) * inv_h + p.eps);
+  T* yr = static_cast<T*>(p.ln_out) + row * p.h;
+  for (int64_t c = threadIdx.x; c < hc; c += LNW_THREADS) {
+    float v[8], g[8], b[8], o[8];
+    load8<T, false>(xr + c * 8, v);
+    load8<T, false>(static_cast<const T*>(p.gamma) + c * 8, g);
+    load8<T, false>(static_cast<const T*>(p.beta) + c * 8, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = fmaf((v[e] - mean) * rstd, g[e], b[e]);
+    store8(yr + c * 8, o);
+  }
+  if (threadIdx.x == 0) {
+    p.mean[row] = mean;
+    p.rstd[row] = rstd;
+  }
+}
+
+// LN backward, wide rows, pass 1: the two row means of the input gradient,
+// m1 = mean(dU⊙γ) and m2 = mean(dU⊙γ⊙x̂) with dU = Σ_i dU_i (shard order),
+// to rowstats[row][0..1].
+template <typename T>
+__global__ __launch_bounds__(LNW_THREADS) void ln_bwd_rowstats_kernel(SpProblem p, float* __restrict__ rowstats) {
+  __shared__ float red[LNW_WAVES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t hc = p.h / 8, count = p.s * p.h;
+  const float mu = p.mean[row], rs = p.rstd[row];
+  float s1 = 0.f, s2 = 0.f;
+  for (int64_t c = threadIdx.x; c < hc; c += LNW_THREADS) {
+    const int64_t off = row * p.h + c * 8;
+    float du[8], xh[8], gq[8];
+    load8<T, false>(static_cast<const T*>(p.x) + off, xh);
+    load8<T, false>(static_cast<const T*>(p.gamma) + c * 8, gq);
+    sum_partials8(static_cast<const T*>(p.dU_partials) + off, count, p.t, du);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float gt = du[k] * gq[k];
+      s1 += gt;
+      s2 += gt * ((xh[k] - mu) * rs);
+    }
+  }
+  const float inv_h = 1.0f / static_cast<float>(p.h);
+  s1 = block_sum_fixed(s1, red, lane, wave);
+  s2 = block_sum_fixed(s2, red, lane, wave);
+  if (threadIdx.x == 0) {
+    rowstats[2 * row] = s1 * inv_h;
+    rowstats[2 * row + 1] = s2 * inv_h;
+  }
+}
+
+// LN backward, wide rows, pass 2: block (b, slab) owns columns
+// [4096·slab, 4096·slab + 4096) (thread j chunk 4096·slab/8 + j) of rows b,
+// b + nb, ...; dx = g_out + rstd·(dU⊙γ − m1 − x̂·m2) with dU summed again in
+// the same order as pass 1, and the thread's column partials of dU⊙x̂ and dU
+// go to ws[b][0|1][h].
+template <typename T>
+__global__ __launch_bounds__(LNW_THREADS) void ln_bwd_wide_kernel(SpProblem p, const float* __restrict__ rowstats) {
+  const int64_t c = static_cast<int64_t>(blockIdx.y) * LNW_THREADS + threadIdx.x;
+  const bool mine = c < p.h / 8;
+  const int64_t count = p.s * p.h;
+  const int64_t nb = gridDim.x;
+  float gq[8], dg[8], db[8];
+  if (mine) load8<T, false>(static_cast<const T*>(p.gamma) + c * 8, gq);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dg[k] = db[k] = 0.f;
+  if (mine) {
+    for (int64_t row = blockIdx.x; row < p.s; row += nb) {
+      const int64_t off = row * p.h + c * 8;
+      const float mu = p.mean[row], rs = p.rstd[row];
+      const float m1 = rowstats[2 * row], m2 = rowstats[2 * row + 1];
+      float du[8], xh[8], go[8], o[8];
+      load8(static_cast<const T*>(p.x) + off, xh);
+      load8(static_cast<const T*>(p.g_out) + off, go);
+      sum_partials8(static_cast<const T*>(p.dU_partials) + off, count, p.t, du);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        xh[k] = (xh[k] - mu) * rs;
+        o[k] = go[k] + rs * (du[k] * gq[k] - m1 - xh[k] * m2);
+        dg[k] += du[k] * xh[k];
+        db[k] += du[k];
+      }
+      store8(static_cast<T*>(p.dx) + off, o);
+    }
+    float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * 2 * p.h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ws[c * 8 + k] = dg[k];
+      ws[p.h + c * 8 + k] = db[k];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dropout + residual
 // phase 1: out = x + keep·scale·(Σ_i P_i + b) ;  phase 2: dS = g_out·keep·scale
 // With a bias, a thread's column chunk advances by a fixed amount per
@@ -409,8 +551,14 @@ __global__ __launch_bounds__(SP_THREADS) void colsum_kernel(const float* __restr
 
 template <typename T>
 hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
+  const bool wide = p.h > LN_FAST_MAX_H;
   switch (p.phase) {
     case 0: {
+      if (wide) {
+        hipLaunchKernelGGL((ln_fwd_wide_kernel<T>), dim3(static_cast<unsigned>(p.s)), dim3(LNW_THREADS), 0,
+                           stream, p);
+        return hipGetLastError();
+      }
       const int64_t blocks = (p.s + SP_THREADS / WAVE - 1) / (SP_THREADS / WAVE);  // one wave per row
       hipLaunchKernelGGL((ln_fwd_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(SP_THREADS), 0, stream,
                          p);
@@ -430,11 +578,25 @@ hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
       return hipGetLastError();
     }
     default: {
-      const int64_t nblk = sp_ln_bwd_row_blocks(p.s);
-      // h ≤ 4096 (checked by the caller): one chunk of each row per thread
-      hipLaunchKernelGGL((ln_bwd_kernel<T>), dim3(static_cast<unsigned>(nblk)), dim3(LNB_THREADS), 0,
-                         stream, p);
-      hipError_t e = hipGetLastError();
+      const int64_t nblk = sp_ln_bwd_row_blocks(p.s, p.h);
+      hipError_t e;
+      if (wide) {
+        // the row means first (rowstats after the per-block partials in ws),
+        // then dx and the column partials in 4096-column slabs
+        float* rowstats = p.ws + nblk * 2 * p.h;
+        hipLaunchKernelGGL((ln_bwd_rowstats_kernel<T>), dim3(static_cast<unsigned>(p.s)), dim3(LNW_THREADS), 0,
+                           stream, p, rowstats);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t slabs = (p.h / 8 + LNW_THREADS - 1) / LNW_THREADS;
+        hipLaunchKernelGGL((ln_bwd_wide_kernel<T>), dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(slabs)),
+                           dim3(LNW_THREADS), 0, stream, p, static_cast<const float*>(rowstats));
+      } else {
+        // one chunk of each row per thread
+        hipLaunchKernelGGL((ln_bwd_kernel<T>), dim3(static_cast<unsigned>(nblk)), dim3(LNB_THREADS), 0,
+                           stream, p);
+      }
+      e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t cb = (2 * p.h + CS_COLS - 1) / CS_COLS;
       hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(cb)), dim3(SP_THREADS), 0, stream, p.ws,
@@ -446,7 +608,18 @@ hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
 
 }  // namespace
 
-int64_t sp_ln_bwd_row_blocks(int64_t s) { return s < LNB_MAX_BLOCKS ? s : LNB_MAX_BLOCKS; }
+int64_t sp_ln_bwd_row_blocks(int64_t s, int64_t h) {
+  // wide rows: the 4096-column slabs share the grid of about LNB_MAX_BLOCKS
+  const int64_t slabs = h > LN_FAST_MAX_H ? (h / 8 + LNW_THREADS - 1) / LNW_THREADS : 1;
+  const int64_t cap = (LNB_MAX_BLOCKS + slabs - 1) / slabs;
+  return s < cap ? s : cap;
+}
+
+int64_t sp_workspace_floats(int64_t s, int64_t h) {
+  // per row block: the column partials of dU⊙x̂ and dU; wide rows also keep
+  // the two row means of every row
+  return sp_ln_bwd_row_blocks(s, h) * 2 * h + (h > LN_FAST_MAX_H ? 2 * s : 0);
+}
 
 hipError_t launch_sp(const SpProblem& p, hipStream_t stream) {
   if (p.s <= 0) return hipSuccess;

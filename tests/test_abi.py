@@ -247,8 +247,16 @@ def test_sp_validation(L):
     assert L.tpmlp_ln_sp(None, None) == tp.ERR_NULLPTR
     assert call(_sp(t=1)) == tp.ERR_SHAPE          # SP requires TP > 1
     assert call(_sp(s=60)) == tp.ERR_SHAPE         # s % t
-    assert call(_sp(h=8200)) == tp.ERR_SHAPE       # h limit
-    assert call(_sp(h=36)) == tp.ERR_ALIGN
+    assert call(_sp(h=4)) == tp.ERR_SHAPE          # h >= 8
+    assert call(_sp(h=36)) == tp.ERR_ALIGN         # h % 8 == 0, both dtypes
+    assert call(_sp(h=36, dt=0)) == tp.ERR_ALIGN
+    # any width that is a multiple of 8 passes the shape checks (the next
+    # check, a NULL output, fails instead)
+    for h in (4104, 6144, 25600, 40000):
+        assert call(_sp(h=h, ln_out=0)) == tp.ERR_NULLPTR
+    assert call(_sp(s=1 << 16, h=1 << 15)) == tp.ERR_SHAPE  # 2^32 bytes: over the operand limit
+    assert call(_sp(dt=0, x=0x1004)) == tp.ERR_ALIGN       # f32 too needs 16-byte bases
+    assert call(_sp(mean=0x1002)) == tp.ERR_ALIGN
     assert call(_sp(phase=9)) == tp.ERR_ARG
     assert call(_sp(p_drop=1.0)) == tp.ERR_ARG
     assert call(_sp(p_drop=-0.1)) == tp.ERR_ARG
@@ -263,6 +271,10 @@ def test_sp_validation(L):
     # one [2, h] fp32 slot per LN-backward block: min(s, 512) blocks
     assert L.tpmlp_sp_workspace_bytes(4096, 4096) == 512 * 2 * 4096 * 4
     assert L.tpmlp_sp_workspace_bytes(6, 64) == 6 * 2 * 64 * 4
+    # rows wider than 4096: 4096-column slabs share a grid of about 512
+    # blocks (h = 25600: 7 slabs, 74 row blocks), plus two row means per row
+    assert L.tpmlp_sp_workspace_bytes(4096, 25600) == (74 * 2 * 25600 + 2 * 4096) * 4
+    assert L.tpmlp_sp_workspace_bytes(32, 6144) == (32 * 2 * 6144 + 2 * 32) * 4
 
 
 def test_sp_args_layout_matches_header(tmp_path):

@@ -60,6 +60,12 @@ def check_block(inp, t, p, seed, eps, dtype, label):
     (48, 24, 48, 4, "f32"),
     (96, 520, 1056, 4, "bf16"),
     (512, 4096, 2048, 8, "bf16"),
+    # rows wider than 4096 (the GPT-1T-shaped layer's h = 25600): the LN
+    # kernels loop over 4096-element pieces of a row
+    (64, 6144, 512, 2, "bf16"),
+    (32, 25600, 256, 2, "bf16"),
+    (16, 4104, 64, 2, "f32"),
+    (24, 6144, 96, 4, "f32"),
 ])
 def test_sp_block_small(s, h, m, t, dtype):
     inp = sp_inputs(s, h, m, t, dtype=dtype, seed=3)
