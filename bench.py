@@ -40,6 +40,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_LAUNCHES = 4           # GEMM core launches per step
 METRIC = "TP-MLP shard fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
 WORKLOAD = "gpt8p3b_t8"
+LEGS = ("biased_step", "per_rank", "c2", "gpt1t_shard", "sp_region", "c5_block", "attention", "vocab_ce")
 
 
 def parse():
@@ -48,7 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the per-rank, GPT-1T-shard and SP legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip every leg besides the headline step")
+    ap.add_argument("--legs", default=None,
+                    help="comma-separated subset of the extra legs to run (default: all): " + ",".join(LEGS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--cpu-all-configs", action="store_true",
@@ -227,11 +230,17 @@ class ClockSampler:
 
     def summary(self):
         import numpy as np
-        clk = [c for c, _ in self.samples if c is not None]
-        pw = [p for _, p in self.samples if p is not None]
+        # the metrics table refreshes on its own schedule: samples before its
+        # first refresh repeat the reading taken before the load and are left
+        # out (all of them, when it never refreshed)
+        first = self.samples[0][0] if self.samples else None
+        k = next((i for i, (c, _) in enumerate(self.samples) if c != first), None)
+        live = self.samples[k:] if k is not None else []
+        clk = [c for c, _ in live if c is not None]
+        pw = [p for _, p in live if p is not None]
         out = {"source": "AMD SMI GPU metrics, mean over XCDs of current_gfxclks, sampled every "
-                         f"{int(self.period * 1000)} ms during the timed steps",
-               "samples": len(clk)}
+                         f"{int(self.period * 1000)} ms",
+               "samples": len(self.samples), "samples_after_first_refresh": len(clk)}
         if clk:
             out.update({"median_mhz": round(float(np.median(clk)), 1), "min_mhz": round(float(np.min(clk)), 1),
                         "max_mhz": round(float(np.max(clk)), 1),
@@ -835,32 +844,30 @@ def main():
     rec["gemm_only"].update({"tflops_median": round(flops / (float(np.median(
         np.array(fwd_ms) + np.array(bwd_ms))) * 1e-3) / 1e12, 2)})
     rec["step_ms"] = _stats(step_ms)
-    # the clock under sustained load: about a second more of the same step,
+    # the clock under sustained load: about two seconds more of the same step,
     # untimed, sampled the same way (the timed steps alone may be too short
     # for the clock to settle)
     soak = ClockSampler()
     soak.start()
     t_soak = time.perf_counter()
-    while time.perf_counter() - t_soak < 1.0:
+    while time.perf_counter() - t_soak < 2.0:
         for _ in range(10):
             step()
         torch.cuda.synchronize()
     soak.stop()
     sus = soak.summary()
-    tw = rec["sclk_mhz"]["timed_window"]
     # the SMI metrics table refreshes more slowly than a short timed window:
-    # when every sample there equals the reading taken before it, the window
-    # saw no refresh and only the soak's figure describes the loaded clock
-    tw["refreshed"] = not (tw.get("min_mhz") is not None and tw.get("min_mhz") == tw.get("max_mhz")
-                           and idle_clk is not None and abs(tw["min_mhz"] - idle_clk) < 0.5)
+    # when it did not refresh there (no samples after its first refresh),
+    # only the soak's figure describes the loaded clock
     rec["sclk_mhz"].update({
         "median_mhz": sus.get("median_mhz"), "max_mhz": sus.get("max_mhz"),
         "frac_of_2400": sus.get("frac_of_2400"), "socket_power_w_median": sus.get("socket_power_w_median"),
         "clock_adjusted_peak_tflops": (round(PEAK_BF16_TFLOPS * sus["median_mhz"] / 2400.0, 1)
                                        if sus.get("median_mhz") else None),
-        "sustained_1s": {k: v for k, v in sus.items() if k != "source"},
+        "sustained_2s": {k: v for k, v in sus.items() if k != "source"},
         "source": "AMD SMI GPU metrics (mean over XCDs of current_gfxclks, socket power), sampled every 5 ms "
-                  "over about 1 s of the same step run right after the timed steps"})
+                  "over about 2 s of the same step run right after the timed steps, from the table's first "
+                  "refresh on"})
     if rec["sclk_mhz"]["clock_adjusted_peak_tflops"]:
         rec["pct_of_clock_adjusted_peak"] = round(100.0 * value / rec["sclk_mhz"]["clock_adjusted_peak_tflops"], 2)
     # the reduce alone, inputs flushed from the last-level cache first
@@ -869,25 +876,30 @@ def main():
     del flush
     rec["roofline_reduce"]["cache_flushed"] = {
         "gbs_median": round(red_bytes / (float(np.median(red_flushed)) * 1e-3) / 1e9, 1), **_stats(red_flushed)}
-    if not args.no_extra:
+    legs = set() if args.no_extra else set(LEGS if args.legs is None else args.legs.split(","))
+    unknown = legs - set(LEGS)
+    if unknown:
+        print(f"unknown legs: {sorted(unknown)}; known: {LEGS}", file=sys.stderr)
+        sys.exit(2)
+    if "biased_step" in legs:
         rec["biased_step"] = leg_biased(tp, X, A_s, B_s, G, (Z, Y, P, O, D, dA, dB, dXp, dX), 10, flops)
-        del Z, Y, P, D, dA, dB, dXp, O, dX
-        torch.cuda.empty_cache()
+    del Z, Y, P, D, dA, dB, dXp, O, dX
+    torch.cuda.empty_cache()
+    if "per_rank" in legs:
         rec["per_rank"] = {"workload": "one shard of the 8.3B-shaped layer per launch (t_local=1)",
                            **leg_mlp_shard(tp, n, d, mi, 20, seed=1)}
+    if "c2" in legs:
         rec["c2"] = {"workload": "single-shard layer: n=b*s=4*512=2048, d=1024, m=4096, t=1 (fwd+bwd, no "
                                  "reduction: with one shard the sum is the partial itself)",
                      **leg_mlp_shard(tp, 2048, 1024, 4096, 20, seed=4, inner=20)}
+    if "gpt1t_shard" in legs:
         rec["gpt1t_shard"] = {"workload": "GPT-1T-shaped shard: h=25600, m_i=12800, n=2048 tokens, one shard",
                               **leg_mlp_shard(tp, 2048, 25600, 12800, 10, seed=2)}
-        torch.cuda.empty_cache()
-        rec["sp_region"] = leg_sp(tp, 10)
-        torch.cuda.empty_cache()
-        rec["c5_block"] = leg_c5_block(tp, 10)
-        torch.cuda.empty_cache()
-        rec["attention"] = leg_attention(tp, 10)
-        torch.cuda.empty_cache()
-        rec["vocab_ce"] = leg_vocab(tp, 10)
+    for name, fn in (("sp_region", lambda: leg_sp(tp, 10)), ("c5_block", lambda: leg_c5_block(tp, 10)),
+                     ("attention", lambda: leg_attention(tp, 10)), ("vocab_ce", lambda: leg_vocab(tp, 10))):
+        if name in legs:
+            torch.cuda.empty_cache()
+            rec[name] = fn()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, t, args.cpu_seconds)
     if args.cpu_all_configs:
