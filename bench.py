@@ -312,9 +312,12 @@ def leg_mlp_shard(tp, n, d, mi, reps, seed, inner=1):
     dA = torch.empty((1, d, mi), dtype=torch.float32, device=dev)
     dB = torch.empty((1, mi, d), dtype=torch.float32, device=dev)
 
+    wsf = tp.workspace(tp.fwd_workspace_bytes(X, A), dev)
+    wsb = tp.workspace(tp.bwd_workspace_bytes(X, A), dev)
+
     def run():
-        tp.tpmlp_fwd(X, A, B, Z, Y, P)
-        tp.tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, None)
+        tp.tpmlp_fwd(X, A, B, Z, Y, P, wsf)
+        tp.tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, wsb)
 
     for _ in range(3):
         run()
@@ -407,6 +410,8 @@ def leg_c5_block(tp, reps):
     dgamma, dbeta = (torch.empty(h, dtype=torch.float32, device=dev) for _ in range(2))
     nb = tp.lib().tpmlp_sp_workspace_bytes(s, h)
     ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=dev)
+    wsf = tp.workspace(tp.fwd_workspace_bytes(U, A), dev)
+    wsb = tp.workspace(tp.bwd_workspace_bytes(U, A), dev)
     P_ = tp._ptr
     common = dict(dt=tp.BF16, t=t, s=s, h=h, eps=cfg["eps"], p_drop=p, seed=cfg["mask_seed"])
     a_ln = tp.SpArgs(phase=tp.SP_LN_FWD, x=P_(x), gamma=P_(gamma), beta=P_(beta), ln_out=P_(U), mean=P_(mean),
@@ -424,13 +429,13 @@ def leg_c5_block(tp, reps):
         rec(0)
         tp.tpmlp_ln_sp(a_ln, stream)
         rec(1)
-        tp.tpmlp_fwd(U, A, B, Z, Y, P, stream)
+        tp.tpmlp_fwd(U, A, B, Z, Y, P, wsf, stream)
         rec(2)
         tp.tpmlp_ln_sp(a_dr, stream)
         rec(3)
         tp.tpmlp_ln_sp(a_db, stream)
         rec(4)
-        tp.tpmlp_bwd(U, A, B, Z, Y, dS, D, dA, dB, dXp, None, stream)
+        tp.tpmlp_bwd(U, A, B, Z, Y, dS, D, dA, dB, dXp, wsb, stream)
         rec(5)
         tp.tpmlp_ln_sp(a_lb, stream)
         rec(6)
@@ -478,14 +483,16 @@ def leg_biased(tp, X, A_s, B_s, G, bufs, reps, flops):
     ws1 = torch.empty(tp.bias_grad_workspace_bytes(t, n, mi), dtype=torch.uint8, device=dev)
     ws2 = torch.empty(tp.bias_grad_workspace_bytes(1, n, d), dtype=torch.uint8, device=dev)
     G3 = G.reshape(1, n, d)
+    wsf = tp.workspace(tp.fwd_workspace_bytes(X, A_s, bias=True), dev)
+    wsb = tp.workspace(tp.bwd_workspace_bytes(X, A_s), dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         rec = (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None)
         rec(0)
-        tp.tpmlp_fwd_bias(X, A_s, B_s, b1, Z, Y, P, stream)
+        tp.tpmlp_fwd_bias(X, A_s, B_s, b1, Z, Y, P, wsf, stream)
         tp.tpmlp_reduce_partials_bias(P, b2, O, stream)
-        tp.tpmlp_bwd(X, A_s, B_s, Z, Y, G, D, dA, dB, dXp, None, stream)
+        tp.tpmlp_bwd(X, A_s, B_s, Z, Y, G, D, dA, dB, dXp, wsb, stream)
         rec(1)
         tp.tpmlp_bias_grad(D, db1, ws1, stream)
         rec(2)
@@ -745,14 +752,14 @@ def main():
     dB = torch.empty((t, mi, d), dtype=torch.float32, device=dev)
     dXp = torch.empty_like(P)
     dX = torch.empty_like(O)
-    nb = tp.bwd_workspace_bytes(X, A_s)
-    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    wsf = tp.workspace(tp.fwd_workspace_bytes(X, A_s), dev)
+    ws = tp.workspace(tp.bwd_workspace_bytes(X, A_s), dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        tp.tpmlp_fwd(X, A_s, B_s, Z, Y, P, stream)
+        tp.tpmlp_fwd(X, A_s, B_s, Z, Y, P, wsf, stream)
         if ev is not None:
             ev[1].record(stream)
         tp.tpmlp_reduce_partials(P, O, stream)

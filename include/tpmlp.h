@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 7
+#define TPMLP_ABI_VERSION 8
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -108,9 +108,19 @@ enum {
  *   X [n, d]; A [t_local, d, m_i] (shard i = column block i of the full
  *   first weight); B [t_local, m_i, d] (shard i = row block i of the full
  *   second weight); Z, Y [t_local, n, m_i]; P [t_local, n, d]; all of dt.
+ *   ws / ws_bytes: workspace of at least tpmlp_fwd_workspace_bytes(dt, n, d,
+ *   m_i, t_local) bytes, 16-byte aligned (may be NULL when that is 0; less
+ *   is TPMLP_ERR_WORKSPACE).  It is non-zero only for bf16 shapes whose
+ *   products have too few 256×256 output tiles to fill the GPU: those run
+ *   K-split (each K slice's fp32 partial tile in ws, then a fix-up kernel
+ *   adds the slices in a fixed order and applies the GeLU or plain
+ *   epilogue).  The split depends only on the sizes, so results are
+ *   bit-reproducible; they differ from an unsplit product only by the fp32
+ *   summation order.
  */
+size_t tpmlp_fwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local);
 int tpmlp_fwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
-              const void* X, const void* A, const void* B, void* Z, void* Y, void* P);
+              const void* X, const void* A, const void* B, void* Z, void* Y, void* P, void* ws, size_t ws_bytes);
 
 /*
  * tpmlp_fwd_bias -- tpmlp_fwd with the first layer's bias.  The column-
@@ -122,11 +132,14 @@ int tpmlp_fwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
  *   Y_i = GeLU(Z_i),  P_i = Y_i·B_i
  *
  *   b1 [t_local, m_i] of dt (row i = slice i of the full bias), not NULL.
- *   Everything else, errors included, as for tpmlp_fwd.  The backward is
- *   tpmlp_bwd unchanged (Z_i already holds the bias), plus tpmlp_bias_grad.
+ *   Everything else, errors included, as for tpmlp_fwd; the workspace is
+ *   tpmlp_fwd_bias_workspace_bytes(...) bytes.  The backward is tpmlp_bwd
+ *   unchanged (Z_i already holds the bias), plus tpmlp_bias_grad.
  */
+size_t tpmlp_fwd_bias_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local);
 int tpmlp_fwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
-                   const void* X, const void* A, const void* B, const void* b1, void* Z, void* Y, void* P);
+                   const void* X, const void* A, const void* B, const void* b1, void* Z, void* Y, void* P, void* ws,
+                   size_t ws_bytes);
 
 /*
  * tpmlp_bwd -- backward of t_local MLP shards ([TUT] §二).
@@ -146,8 +159,10 @@ int tpmlp_fwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i
  *   Inputs X, A, B as for tpmlp_fwd; Z, Y from tpmlp_fwd; G [n, d] the
  *   upstream gradient ∂ℓ/∂O.  With n == 0, dA and dB are set to zero.
  *   dA and dB: 16-byte aligned on the bf16 path, 4-byte on the f32 path.
- *   ws / ws_bytes: workspace, at least tpmlp_bwd_workspace_bytes(...) bytes
- *   (may be NULL when that is 0).
+ *   ws / ws_bytes: workspace, at least tpmlp_bwd_workspace_bytes(...) bytes,
+ *   16-byte aligned (may be NULL when that is 0; less is
+ *   TPMLP_ERR_WORKSPACE): as for tpmlp_fwd, products that would leave the
+ *   GPU idle (few output tiles, long K) run K-split there.
  */
 size_t tpmlp_bwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local);
 int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,

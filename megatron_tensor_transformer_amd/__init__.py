@@ -56,8 +56,10 @@ _lib = None
 # exported C symbols and their ctypes signatures
 _P, _I, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
-    "tpmlp_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]),
-    "tpmlp_fwd_bias": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "tpmlp_fwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I32]),
+    "tpmlp_fwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ]),
+    "tpmlp_fwd_bias_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I32]),
+    "tpmlp_fwd_bias": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
     "tpmlp_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I32]),
     "tpmlp_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
     "tpmlp_reduce_partials": (_I, [_P, _I, _I, _I32, _I64, _I64, _P, _P]),
@@ -180,20 +182,25 @@ def _mlp_fwd_check(X, A, B, Z, Y, P, b1=None):
     return t, d, mi, n
 
 
-def tpmlp_fwd(X, A, B, Z, Y, P, stream=None):
-    """X [n,d]; A [t,d,m_i]; B [t,m_i,d]; Z, Y [t,n,m_i]; P [t,n,d] (all one dtype)."""
+def tpmlp_fwd(X, A, B, Z, Y, P, ws=None, stream=None):
+    """X [n,d]; A [t,d,m_i]; B [t,m_i,d]; Z, Y [t,n,m_i]; P [t,n,d] (all one dtype);
+    ws: a device buffer of at least fwd_workspace_bytes(X, A) bytes (None when that is 0)."""
     t, d, mi, n = _mlp_fwd_check(X, A, B, Z, Y, P)
+    _expect(X, ("ws", ws, None, None))
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_fwd(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B),
-                           _ptr(Z), _ptr(Y), _ptr(P)))
+                           _ptr(Z), _ptr(Y), _ptr(P), _ptr(ws), ws_bytes))
 
 
-def tpmlp_fwd_bias(X, A, B, b1, Z, Y, P, stream=None):
+def tpmlp_fwd_bias(X, A, B, b1, Z, Y, P, ws=None, stream=None):
     """tpmlp_fwd with the column bias b1 [t, m_i] (dtype of X)."""
     if b1 is None:
         raise TpmlpValueError(ERR_NULLPTR, "b1 is required")
     t, d, mi, n = _mlp_fwd_check(X, A, B, Z, Y, P, b1)
+    _expect(X, ("ws", ws, None, None))
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_fwd_bias(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B), _ptr(b1),
-                                _ptr(Z), _ptr(Y), _ptr(P)))
+                                _ptr(Z), _ptr(Y), _ptr(P), _ptr(ws), ws_bytes))
 
 
 def tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, ws=None, stream=None):
@@ -375,13 +382,24 @@ def tpmlp_ln_sp(args, stream=None):
 
 
 # ---------------------------------------------------------------- allocating wrappers
+def fwd_workspace_bytes(X, A, bias=False):
+    t, d, mi = A.shape
+    f = lib().tpmlp_fwd_bias_workspace_bytes if bias else lib().tpmlp_fwd_workspace_bytes
+    return f(_dt(X), X.shape[0], d, mi, t)
+
+
+def workspace(nbytes, device):
+    """A device workspace of nbytes (None when 0), as the entry points take it."""
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
 def mlp_fwd(X, A, B, stream=None):
     t, d, mi = A.shape
     n = X.shape[0]
     Z = torch.empty((t, n, mi), dtype=X.dtype, device=X.device)
     Y = torch.empty_like(Z)
     P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
-    tpmlp_fwd(X, A, B, Z, Y, P, stream)
+    tpmlp_fwd(X, A, B, Z, Y, P, workspace(fwd_workspace_bytes(X, A), X.device), stream)
     return Z, Y, P
 
 
@@ -391,7 +409,7 @@ def mlp_fwd_bias(X, A, B, b1, stream=None):
     Z = torch.empty((t, n, mi), dtype=X.dtype, device=X.device)
     Y = torch.empty_like(Z)
     P = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
-    tpmlp_fwd_bias(X, A, B, b1, Z, Y, P, stream)
+    tpmlp_fwd_bias(X, A, B, b1, Z, Y, P, workspace(fwd_workspace_bytes(X, A, bias=True), X.device), stream)
     return Z, Y, P
 
 

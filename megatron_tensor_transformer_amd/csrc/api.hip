@@ -63,18 +63,12 @@ hipError_t gemm(int dt, const tpmlp::GemmProblem& p, int ao, int bo, int epi, hi
                           : tpmlp::launch_gemm_f32(p, ao, bo, epi, s);
 }
 
-// The shard forward with an optional column bias b1 [t_local, m_i] (NULL: none).
-int fwd_impl(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local, const void* X,
-             const void* A, const void* B, const void* b1, void* Z, void* Y, void* P) {
-  int st = check_mlp_dims(dt, n, d, m_i, t_local);
-  if (st) return st;
-  if (n == 0) return TPMLP_OK;
-  st = check_ptrs(dt, {X, A, B, Z, Y, P});
-  if (st) return st;
-
+// The forward's two products (pointers may be null for a size query).
+void fwd_problems(int64_t n, int64_t d, int64_t m_i, int32_t t_local, const void* X, const void* A, const void* B,
+                  const void* b1, void* Z, void* Y, void* P, tpmlp::GemmProblem& g1, tpmlp::GemmProblem& g2) {
   // Z_i = X·A_i (+ b1_i) and Y_i = GeLU(Z_i): A = X [n,d] (K-major),
   // B = A_i [d,m_i] (N-major), batched over shards with X shared.
-  tpmlp::GemmProblem g1{};
+  g1 = tpmlp::GemmProblem{};
   g1.M = static_cast<int>(n);
   g1.N = static_cast<int>(m_i);
   g1.K = static_cast<int>(d);
@@ -91,12 +85,9 @@ int fwd_impl(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int3
   g1.sA = 0;
   g1.sB = d * m_i;
   g1.sC = n * m_i;
-  const int epi1 = b1 != nullptr ? tpmlp::EPI_BIAS_GELU_ZY : tpmlp::EPI_GELU_ZY;
-  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, epi1, stream));
-  if (st) return st;
 
   // P_i = Y_i·B_i: A = Y_i [n,m_i] (K-major), B = B_i [m_i,d] (N-major).
-  tpmlp::GemmProblem g2{};
+  g2 = tpmlp::GemmProblem{};
   g2.M = static_cast<int>(n);
   g2.N = static_cast<int>(d);
   g2.K = static_cast<int>(m_i);
@@ -110,6 +101,41 @@ int fwd_impl(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int3
   g2.sA = n * m_i;
   g2.sB = m_i * d;
   g2.sC = n * d;
+}
+
+size_t fwd_ws_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local, bool bias) {
+  if (dt != TPMLP_BF16 || check_mlp_dims(dt, n, d, m_i, t_local) != TPMLP_OK || n == 0) return 0;
+  tpmlp::GemmProblem g1, g2;
+  fwd_problems(n, d, m_i, t_local, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, g1, g2);
+  const tpmlp::GemmKind k1{tpmlp::KMAJ, tpmlp::MNMAJ, bias ? tpmlp::EPI_BIAS_GELU_ZY : tpmlp::EPI_GELU_ZY};
+  const tpmlp::GemmKind k2{tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE};
+  const size_t a = tpmlp::gemm_bf16_split_bytes(&g1, 1, k1, nullptr, k1);
+  const size_t b = tpmlp::gemm_bf16_split_bytes(&g2, 1, k2, nullptr, k2);
+  return a > b ? a : b;
+}
+
+// The shard forward with an optional column bias b1 [t_local, m_i] (NULL: none).
+int fwd_impl(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local, const void* X,
+             const void* A, const void* B, const void* b1, void* Z, void* Y, void* P, void* ws, size_t ws_bytes) {
+  int st = check_mlp_dims(dt, n, d, m_i, t_local);
+  if (st) return st;
+  if (n == 0) return TPMLP_OK;
+  st = check_ptrs(dt, {X, A, B, Z, Y, P});
+  if (st) return st;
+  const size_t need = fwd_ws_bytes(dt, n, d, m_i, t_local, b1 != nullptr);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return TPMLP_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 16)) return TPMLP_ERR_ALIGN;
+  tpmlp::GemmProblem g1, g2;
+  fwd_problems(n, d, m_i, t_local, X, A, B, b1, Z, Y, P, g1, g2);
+  const int epi1 = b1 != nullptr ? tpmlp::EPI_BIAS_GELU_ZY : tpmlp::EPI_GELU_ZY;
+  if (dt == TPMLP_BF16) {
+    st = hip_status(tpmlp::launch_gemm_bf16_ws(g1, tpmlp::KMAJ, tpmlp::MNMAJ, epi1, ws, ws_bytes, stream));
+    if (st) return st;
+    return hip_status(
+        tpmlp::launch_gemm_bf16_ws(g2, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, ws, ws_bytes, stream));
+  }
+  st = hip_status(gemm(dt, g1, tpmlp::KMAJ, tpmlp::MNMAJ, epi1, stream));
+  if (st) return st;
   return hip_status(gemm(dt, g2, tpmlp::KMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE, stream));
 }
 
@@ -151,42 +177,42 @@ const char* tpmlp_status_string(int status) {
   }
 }
 
+size_t tpmlp_fwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  return fwd_ws_bytes(dt, n, d, m_i, t_local, false);
+}
+
+size_t tpmlp_fwd_bias_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  return fwd_ws_bytes(dt, n, d, m_i, t_local, true);
+}
+
 int tpmlp_fwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
-              const void* X, const void* A, const void* B, void* Z, void* Y, void* P) {
-  return fwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, nullptr, Z, Y, P);
+              const void* X, const void* A, const void* B, void* Z, void* Y, void* P, void* ws, size_t ws_bytes) {
+  return fwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, nullptr, Z, Y, P, ws, ws_bytes);
 }
 
 int tpmlp_fwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
-                   const void* X, const void* A, const void* B, const void* b1, void* Z, void* Y, void* P) {
+                   const void* X, const void* A, const void* B, const void* b1, void* Z, void* Y, void* P, void* ws,
+                   size_t ws_bytes) {
   int st = check_mlp_dims(dt, n, d, m_i, t_local);
   if (st) return st;
   if (n == 0) return TPMLP_OK;
   st = check_ptrs(dt, {b1});
   if (st) return st;
-  return fwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, b1, Z, Y, P);
+  return fwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, b1, Z, Y, P, ws, ws_bytes);
 }
 
-size_t tpmlp_bwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
-  (void)dt, (void)n, (void)d, (void)m_i, (void)t_local;
-  return 0;
-}
+}  // extern "C"
 
-int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
-              const void* X, const void* A, const void* B, const void* Z, const void* Y,
-              const void* G, void* D, float* dA, float* dB, void* dXp, void* ws, size_t ws_bytes) {
-  int st = check_mlp_dims(dt, n, d, m_i, t_local);
-  if (st) return st;
-  if (ws_bytes < tpmlp_bwd_workspace_bytes(dt, n, d, m_i, t_local)) return TPMLP_ERR_WORKSPACE;
-  (void)ws;
-  if (dA == nullptr || dB == nullptr) return TPMLP_ERR_NULLPTR;
-  if (!aligned(dA, wgrad_align(dt)) || !aligned(dB, wgrad_align(dt))) return TPMLP_ERR_ALIGN;
-  if (n > 0) {
-    st = check_ptrs(dt, {X, A, B, Z, Y, G, D, dXp});
-    if (st) return st;
-  }
+namespace {
+
+// The backward's four products (pointers may be null for a size query).
+void bwd_problems(int64_t n, int64_t d, int64_t m_i, int32_t t_local, const void* X, const void* A,
+                  const void* B, const void* Z, const void* Y, const void* G, void* D, float* dA, float* dB,
+                  void* dXp, tpmlp::GemmProblem& e, tpmlp::GemmProblem& wb, tpmlp::GemmProblem& wa,
+                  tpmlp::GemmProblem& dx) {
   // D_i = (G·B_iᵀ) ⊙ GeLU'(Z_i): A = G [n,d] (K-major), B(k,j) = B_i[j][k]
   // (K-major, ld = d).  Empty (skipped) when n == 0.
-  tpmlp::GemmProblem e{};
+  e = tpmlp::GemmProblem{};
   e.M = static_cast<int>(n);
   e.N = static_cast<int>(m_i);
   e.K = static_cast<int>(d);
@@ -204,7 +230,7 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
 
   // dB_i = Y_iᵀ·G: M = m_i, N = d, K = n; A(m,k) = Y_i[k][m] (M-major),
   // B(k,j) = G[k][j] (N-major).  With n == 0 this writes zeros.
-  tpmlp::GemmProblem wb{};
+  wb = tpmlp::GemmProblem{};
   wb.M = static_cast<int>(m_i);
   wb.N = static_cast<int>(d);
   wb.K = static_cast<int>(n);
@@ -220,7 +246,7 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
   wb.sC = m_i * d;
 
   // dA_i = Xᵀ·D_i: M = d, N = m_i, K = n; A(m,k) = X[k][m], B(k,j) = D_i[k][j].
-  tpmlp::GemmProblem wa{};
+  wa = tpmlp::GemmProblem{};
   wa.M = static_cast<int>(d);
   wa.N = static_cast<int>(m_i);
   wa.K = static_cast<int>(n);
@@ -237,7 +263,7 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
 
   // dX_i = D_i·A_iᵀ: M = n, N = d, K = m_i; A = D_i (K-major),
   // B(k,j) = A_i[j][k] (K-major, ld = m_i).  Empty (skipped) when n == 0.
-  tpmlp::GemmProblem dx{};
+  dx = tpmlp::GemmProblem{};
   dx.M = static_cast<int>(n);
   dx.N = static_cast<int>(d);
   dx.K = static_cast<int>(m_i);
@@ -251,18 +277,59 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
   dx.sA = n * m_i;
   dx.sB = d * m_i;
   dx.sC = n * d;
+}
 
-  const tpmlp::GemmKind wgrad{tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32};
-  const tpmlp::GemmKind dgrad1{tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_GELU_GRAD};
-  const tpmlp::GemmKind dgrad2{tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE};
+const tpmlp::GemmKind kWgrad{tpmlp::MNMAJ, tpmlp::MNMAJ, tpmlp::EPI_STORE_F32};
+const tpmlp::GemmKind kDgrad1{tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_GELU_GRAD};
+const tpmlp::GemmKind kDgrad2{tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_STORE};
+
+size_t bwd_ws_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  if (dt != TPMLP_BF16 || check_mlp_dims(dt, n, d, m_i, t_local) != TPMLP_OK) return 0;
+  tpmlp::GemmProblem e, wb, wa, dx;
+  bwd_problems(n, d, m_i, t_local, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+               nullptr, e, wb, wa, dx);
+  const tpmlp::GemmProblem w[2] = {wb, wa};
+  const size_t a = tpmlp::gemm_bf16_split_bytes(&e, 1, kDgrad1, nullptr, kDgrad1);
+  const size_t b = tpmlp::gemm_bf16_split_bytes(w, 2, kWgrad, &dx, kDgrad2);
+  return a > b ? a : b;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tpmlp_bwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  return bwd_ws_bytes(dt, n, d, m_i, t_local);
+}
+
+int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+              const void* X, const void* A, const void* B, const void* Z, const void* Y,
+              const void* G, void* D, float* dA, float* dB, void* dXp, void* ws, size_t ws_bytes) {
+  int st = check_mlp_dims(dt, n, d, m_i, t_local);
+  if (st) return st;
+  const size_t need = tpmlp_bwd_workspace_bytes(dt, n, d, m_i, t_local);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return TPMLP_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 16)) return TPMLP_ERR_ALIGN;
+  if (dA == nullptr || dB == nullptr) return TPMLP_ERR_NULLPTR;
+  if (!aligned(dA, wgrad_align(dt)) || !aligned(dB, wgrad_align(dt))) return TPMLP_ERR_ALIGN;
+  if (n > 0) {
+    st = check_ptrs(dt, {X, A, B, Z, Y, G, D, dXp});
+    if (st) return st;
+  }
+  tpmlp::GemmProblem e, wb, wa, dx;
+  bwd_problems(n, d, m_i, t_local, X, A, B, Z, Y, G, D, dA, dB, dXp, e, wb, wa, dx);
+  const tpmlp::GemmKind& wgrad = kWgrad;
+  const tpmlp::GemmKind& dgrad1 = kDgrad1;
+  const tpmlp::GemmKind& dgrad2 = kDgrad2;
   if (dt == TPMLP_BF16) {
     // Two launches: dgrad-1, then both weight gradients (K = n, the long
     // ones) with dgrad-2 (which also needs D), whose tiles fill the machine
-    // around them.
-    st = hip_status(tpmlp::launch_gemm_bf16(e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, stream));
+    // around them.  Products that would leave the machine idle run K-split
+    // in the workspace.
+    st = hip_status(tpmlp::launch_gemm_bf16_ws(e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, ws, ws_bytes, stream));
     if (st) return st;
     const tpmlp::GemmProblem w[2] = {wb, wa};
-    return hip_status(tpmlp::launch_gemm_bf16_group(w, 2, wgrad, &dx, dgrad2, stream));
+    return hip_status(tpmlp::launch_gemm_bf16_group(w, 2, wgrad, &dx, dgrad2, ws, ws_bytes, stream));
   }
   if (n > 0) {
     st = hip_status(gemm(dt, e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, stream));
@@ -760,13 +827,13 @@ int tpmlp_attn_bwd(hipStream_t stream, int dt, int64_t s, int64_t b, int64_t d, 
   ap.delta = static_cast<float*>(ws);
   if (dt == TPMLP_BF16) {
     // dW_proj (long) with dO (short), the core, then dW_qkv (long) with dX
-    st = hip_status(tpmlp::launch_gemm_bf16_group(&wp, 1, wgrad, &go, dgrad, stream));
+    st = hip_status(tpmlp::launch_gemm_bf16_group(&wp, 1, wgrad, &go, dgrad, nullptr, 0, stream));
     if (st) return st;
     if (s > 0) {
       st = hip_status(tpmlp::launch_attn_bwd(ap, stream));
       if (st) return st;
     }
-    return hip_status(tpmlp::launch_gemm_bf16_group(&wq, 1, wgrad, &dx, dgrad, stream));
+    return hip_status(tpmlp::launch_gemm_bf16_group(&wq, 1, wgrad, &dx, dgrad, nullptr, 0, stream));
   }
   st = hip_status(gemm(dt, wp, wgrad.a_order, wgrad.b_order, wgrad.epi, stream));
   if (st) return st;

@@ -63,6 +63,10 @@ struct alignas(64) KArgs {
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;
   uint32_t a_bytes, b_bytes, c_bytes;
+  // split K: ksplit slices of kchunk (a multiple of BK) each; slice s writes
+  // its fp32 partial tile at C + s·sSlice (ksplit = 1: no split)
+  int ksplit, kchunk;
+  int64_t sSlice;
 };
 
 // One launch runs up to three problems: p[0] and p[1] (the long group, one
@@ -614,6 +618,29 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 
 // The launch: problems 0 and 1 are of kind (AO0, BO0, EPI0), problem 2 of
 // kind (AO1, BO1, EPI1).
+// A tile of a K-split problem: its slice s (the slowest index of the tile
+// order, so one slice's tiles run together) becomes a problem of its own over
+// k in [s·kchunk, min(K, (s+1)·kchunk)): the operands' base pointers and
+// buffer ranges move to the slice's first k (the K-edge test zero-fills the
+// rest) and the fp32 partial goes to the slice's plane.
+template <int AO, int BO>
+__device__ __forceinline__ void select_slice(KArgs& a, int& tile) {
+  if (a.ksplit <= 1) return;
+  const int per_slice = a.tiles_m * a.tiles_n * a.batch;
+  const int slice = tile / per_slice;
+  tile -= slice * per_slice;
+  const int k0 = slice * a.kchunk;
+  const int rest = a.K - k0;
+  a.K = rest < a.kchunk ? (rest > 0 ? rest : 0) : a.kchunk;
+  const int64_t offA = AO == KMAJ ? k0 : static_cast<int64_t>(k0) * a.lda;
+  const int64_t offB = BO == KMAJ ? k0 : static_cast<int64_t>(k0) * a.ldb;
+  a.A += offA;
+  a.B += offB;
+  a.a_bytes = a.a_bytes > offA * 2 ? a.a_bytes - static_cast<uint32_t>(offA * 2) : 0u;
+  a.b_bytes = a.b_bytes > offB * 2 ? a.b_bytes - static_cast<uint32_t>(offB * 2) : 0u;
+  a.C = static_cast<float*>(a.C) + slice * a.sSlice;
+}
+
 template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -621,14 +648,104 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   int prob, tile;
   map_workgroup(g.split, g.t0, blockIdx.x, prob, tile);
   if constexpr (AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1) {
-    const KArgs a = g.p[prob];  // one copy: wide scalar loads at the problem's offset
+    KArgs a = g.p[prob];  // one copy: wide scalar loads at the problem's offset
+    if constexpr (EPI0 == EPI_STORE_F32) select_slice<AO0, BO0>(a, tile);
     gemm_tile<AO0, BO0, EPI0>(a, tile, lds);
   } else {
-    const KArgs a = g.p[prob];
-    if (prob == 2)
+    KArgs a = g.p[prob];
+    if (prob == 2) {
+      if constexpr (EPI1 == EPI_STORE_F32) select_slice<AO1, BO1>(a, tile);
       gemm_tile<AO1, BO1, EPI1>(a, tile, lds);
-    else
+    } else {
+      if constexpr (EPI0 == EPI_STORE_F32) select_slice<AO0, BO0>(a, tile);
       gemm_tile<AO0, BO0, EPI0>(a, tile, lds);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ split-K fix-up
+// out = epilogue(Σ_{s<S} part[s]) for one problem that ran K-split: the
+// slices' fp32 partial tiles are added in slice order (a fixed order, so the
+// result is bit-reproducible) and the problem's own epilogue is applied with
+// the same fp32 arithmetic as the unsplit kernel's.  A thread owns 8
+// consecutive columns of one row (N % 8 == 0).
+struct FixArgs {
+  const float* part;  // [S][batch][M][N]
+  int S, batch, M, N;
+  int64_t sSlice;     // batch·M·N
+  void* C;
+  void* C2;
+  const bf16* Zin;
+  const bf16* bias;
+  int64_t sBias, ldc, sC;
+};
+
+constexpr int FIX_THREADS = 256;
+
+template <int EPI>
+__global__ __launch_bounds__(FIX_THREADS) void splitk_fixup_kernel(FixArgs f) {
+  const int64_t nvec = static_cast<int64_t>(f.batch) * f.M * (f.N / 8);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * FIX_THREADS;
+  const int64_t per_b = static_cast<int64_t>(f.M) * (f.N / 8);
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * FIX_THREADS + threadIdx.x; v < nvec; v += step) {
+    const int64_t b = v / per_b;
+    const int64_t rem = v - b * per_b;
+    const int64_t row = rem / (f.N / 8);
+    const int64_t col = (rem - row * (f.N / 8)) * 8;
+    const float* src = f.part + (b * f.M + row) * f.N + col;
+    float x[8];
+    {
+      const f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+      const f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[q] = lo[q];
+        x[4 + q] = hi[q];
+      }
+    }
+    for (int sl = 1; sl < f.S; ++sl) {
+      const f32x4* q4 = reinterpret_cast<const f32x4*>(src + sl * f.sSlice);
+      const f32x4 lo = __builtin_nontemporal_load(q4), hi = __builtin_nontemporal_load(q4 + 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[q] += lo[q];
+        x[4 + q] += hi[q];
+      }
+    }
+    const int64_t o = b * f.sC + row * f.ldc + col;
+    if constexpr (EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE) {
+      const bf16x8 bb = *reinterpret_cast<const bf16x8*>(f.bias + b * f.sBias + col);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] += bf2f(bb[e]);
+    }
+    if constexpr (EPI == EPI_STORE_F32) {
+      f32x4 lo, hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo[q] = x[q];
+        hi[q] = x[4 + q];
+      }
+      float* c = static_cast<float*>(f.C) + o;
+      reinterpret_cast<f32x4*>(c)[0] = lo;
+      reinterpret_cast<f32x4*>(c)[1] = hi;
+    } else {
+      bf16x8 r;
+      if constexpr (EPI == EPI_GELU_GRAD) {
+        const bf16x8 z = *reinterpret_cast<const bf16x8*>(f.Zin + o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e] * gelu_grad_fast(bf2f(z[e])));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e]);
+      }
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(f.C) + o) = r;
+      if constexpr (EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY) {
+        bf16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = f2bf(gelu_fast(x[e]));
+        *reinterpret_cast<bf16x8*>(static_cast<bf16*>(f.C2) + o) = y;
+      }
+    }
   }
 }
 
@@ -673,6 +790,9 @@ KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
   k.a_bytes = extent_bytes(a_order, p.M, p.K, p.lda);
   k.b_bytes = extent_bytes(b_order, p.N, p.K, p.ldb);
   k.c_bytes = static_cast<uint32_t>(((static_cast<int64_t>(p.M) - 1) * p.ldc + p.N) * 2);
+  k.ksplit = 1;
+  k.kchunk = p.K;
+  k.sSlice = 0;
   return k;
 }
 
@@ -682,61 +802,245 @@ int64_t tiles_of(const GemmProblem& p) {
   return empty(p) ? 0 : static_cast<int64_t>((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
 }
 
+// ---------------------------------------------------------------- split-K plan
+// A launch whose tiles cannot fill the 256 CUs, or whose longest tiles leave
+// most of the machine idle at the end, runs some problems K-split: slice s of
+// S computes its fp32 partial tile over a contiguous range of K, and a fix-up
+// kernel adds the S partials in slice order and applies the problem's
+// epilogue.  The choice minimises a cost model in units of one K step (64) of
+// a tile on a loaded machine: the launch takes about max(longest tile,
+// total tile work / 256 CUs), each tile also pays a fixed prologue/epilogue,
+// and a split pays its fix-up's fp32 traffic and launch.  The choice depends
+// only on the shapes, so a call is bit-reproducible.
+constexpr double kTileFixedSteps = 4.0;  // a tile's prologue + epilogue (≈ 6.7 µs at ≈ 1.6 µs per step)
+constexpr double kFixBytesPerStep = 6.4e6;  // fix-up traffic per step time (≈ 4 TB/s × 1.6 µs)
+constexpr double kFixLaunchSteps = 2.0;
+constexpr int kCUs = 256;
+constexpr int kMinStepsPerSlice = 8;
+
+struct SplitPlan {
+  int s[3];
+  size_t off[3];  // byte offset of each split problem's partial planes in the workspace
+  size_t bytes;
+};
+
+bool splittable(const GemmKind& k) { return k.epi != EPI_STORE_ROWSTATS; }
+
+// problems: up to three (null = absent); kinds: theirs
+SplitPlan plan_split(const GemmProblem* const (&pr)[3], const GemmKind* const (&kd)[3]) {
+  SplitPlan best{{1, 1, 1}, {0, 0, 0}, 0};
+  double T[3], KS[3], MN[3];
+  bool can[3];
+  for (int i = 0; i < 3; ++i) {
+    const bool live = pr[i] != nullptr && !empty(*pr[i]);
+    T[i] = live ? static_cast<double>(tiles_of(*pr[i])) : 0.0;
+    KS[i] = live ? static_cast<double>((pr[i]->K + BK - 1) / BK) : 0.0;
+    MN[i] = live ? static_cast<double>(pr[i]->batch) * pr[i]->M * pr[i]->N : 0.0;
+    can[i] = live && splittable(*kd[i]) && pr[i]->N % 8 == 0;
+  }
+  auto cost = [&](const int (&s)[3]) {
+    double longest = 0.0, work = 0.0, fix = 0.0;
+    for (int i = 0; i < 3; ++i) {
+      if (T[i] == 0.0) continue;
+      const double c = static_cast<double>((static_cast<int64_t>(KS[i]) + s[i] - 1) / s[i]) + kTileFixedSteps;
+      longest = c > longest ? c : longest;
+      work += T[i] * s[i] * c;
+      if (s[i] > 1) fix += 2.0 * s[i] * MN[i] * 4.0 / kFixBytesPerStep + kFixLaunchSteps;
+    }
+    const double spread = work / kCUs;
+    return (longest > spread ? longest : spread) + fix;
+  };
+  int s[3] = {1, 1, 1};
+  double bc = cost(s);
+  static const int kS[5] = {1, 2, 4, 8, 16};
+  for (int a = 0; a < 5; ++a)
+    for (int b = 0; b < 5; ++b)
+      for (int c = 0; c < 5; ++c) {
+        const int cand[3] = {kS[a], kS[b], kS[c]};
+        bool ok = true;
+        for (int i = 0; i < 3; ++i)
+          if (cand[i] > 1 && (!can[i] || KS[i] < kMinStepsPerSlice * cand[i])) ok = false;
+        // the two long problems share one kind: split alike unless that kind
+        // already is the fp32 store a split runs as
+        if (T[0] > 0.0 && T[1] > 0.0 && kd[0]->epi != EPI_STORE_F32 && cand[0] != cand[1]) ok = false;
+        if (!ok) continue;
+        const double cc = cost(cand);
+        if (cc < bc * 0.97) {  // a split must win clearly
+          bc = cc;
+          for (int i = 0; i < 3; ++i) s[i] = cand[i];
+        }
+      }
+  size_t off = 0;
+  for (int i = 0; i < 3; ++i) {
+    best.s[i] = s[i];
+    best.off[i] = off;
+    if (s[i] > 1) off += (static_cast<size_t>(s[i]) * static_cast<size_t>(MN[i]) * 4 + 255) / 256 * 256;
+  }
+  best.bytes = off;
+  return best;
+}
+
+hipError_t fixup(const GemmProblem& p, int epi, const float* part, int S, hipStream_t stream) {
+  FixArgs f;
+  f.part = part;
+  f.S = S;
+  f.batch = p.batch;
+  f.M = p.M;
+  f.N = p.N;
+  f.sSlice = static_cast<int64_t>(p.batch) * p.M * p.N;
+  f.C = p.C;
+  f.C2 = p.C2;
+  f.Zin = static_cast<const bf16*>(p.Zin);
+  f.bias = static_cast<const bf16*>(p.bias);
+  f.sBias = p.sBias;
+  f.ldc = p.ldc;
+  f.sC = p.sC;
+  const int64_t nvec = static_cast<int64_t>(p.batch) * p.M * (p.N / 8);
+  int64_t blocks = (nvec + FIX_THREADS - 1) / FIX_THREADS;
+  if (blocks > 8192) blocks = 8192;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(FIX_THREADS);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(splitk_fixup_kernel<EPI_STORE>, grid, block, 0, stream, f); break;
+    case EPI_STORE_F32: hipLaunchKernelGGL(splitk_fixup_kernel<EPI_STORE_F32>, grid, block, 0, stream, f); break;
+    case EPI_GELU_ZY: hipLaunchKernelGGL(splitk_fixup_kernel<EPI_GELU_ZY>, grid, block, 0, stream, f); break;
+    case EPI_GELU_GRAD: hipLaunchKernelGGL(splitk_fixup_kernel<EPI_GELU_GRAD>, grid, block, 0, stream, f); break;
+    case EPI_BIAS_GELU_ZY:
+      hipLaunchKernelGGL(splitk_fixup_kernel<EPI_BIAS_GELU_ZY>, grid, block, 0, stream, f);
+      break;
+    case EPI_BIAS_STORE: hipLaunchKernelGGL(splitk_fixup_kernel<EPI_BIAS_STORE>, grid, block, 0, stream, f); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
+size_t gemm_bf16_split_bytes(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
+                             const GemmProblem* shortp, const GemmKind& short_kind) {
+  const GemmProblem* pr[3] = {nlong > 0 ? &longp[0] : nullptr, nlong > 1 ? &longp[1] : nullptr, shortp};
+  const GemmKind* kd[3] = {&long_kind, &long_kind, &short_kind};
+  return plan_split(pr, kd).bytes;
+}
+
 hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
-                                  const GemmProblem* shortp, const GemmKind& short_kind, hipStream_t stream) {
+                                  const GemmProblem* shortp, const GemmKind& short_kind, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
   if (nlong < 0 || nlong > 2 || (nlong > 0 && longp == nullptr)) return hipErrorInvalidValue;
+  // the split plan over the three problem slots (long 0, long 1, short)
+  const GemmProblem* slot[3] = {nlong > 0 ? &longp[0] : nullptr, nlong > 1 ? &longp[1] : nullptr, shortp};
+  const GemmKind* kslot[3] = {&long_kind, &long_kind, &short_kind};
+  SplitPlan plan = plan_split(slot, kslot);
+  if (ws == nullptr || ws_bytes < plan.bytes) plan = SplitPlan{{1, 1, 1}, {0, 0, 0}, 0};
+  char* wsb = static_cast<char*>(ws);
+
+  // a K-split problem runs as an fp32 store of its slices' partials
+  GemmProblem sp[3];
+  GemmKind sk[3];
+  for (int i = 0; i < 3; ++i) {
+    if (slot[i] == nullptr) continue;
+    sp[i] = *slot[i];
+    sk[i] = *kslot[i];
+    if (plan.s[i] > 1) {
+      sp[i].C = wsb + plan.off[i];
+      sp[i].C2 = nullptr;
+      sp[i].ldc = sp[i].N;
+      sp[i].sC = static_cast<int64_t>(sp[i].M) * sp[i].N;
+      sk[i].epi = EPI_STORE_F32;
+    }
+  }
+  // the long group has one kind: split or not, its problems must agree
+  if (nlong == 2 && plan.s[0] > 1 && plan.s[1] > 1 && sk[0].epi != sk[1].epi) return hipErrorInvalidValue;
+  if (nlong == 2 && (plan.s[0] > 1) != (plan.s[1] > 1) && long_kind.epi != EPI_STORE_F32)
+    return hipErrorInvalidValue;
+
   const GemmProblem* lp[2];
+  int li[2];
   int nl = 0;
   for (int i = 0; i < nlong; ++i)
-    if (!empty(longp[i])) lp[nl++] = &longp[i];
-  const bool has_short = shortp != nullptr && !empty(*shortp);
-  const int64_t t0 = nl > 0 ? tiles_of(*lp[0]) : 0, t1 = nl > 1 ? tiles_of(*lp[1]) : 0;
-  const int64_t t2 = has_short ? tiles_of(*shortp) : 0;
+    if (!empty(sp[i])) {
+      lp[nl] = &sp[i];
+      li[nl++] = i;
+    }
+  const bool has_short = shortp != nullptr && !empty(sp[2]);
+  const int64_t t0 = nl > 0 ? tiles_of(*lp[0]) * plan.s[li[0]] : 0;
+  const int64_t t1 = nl > 1 ? tiles_of(*lp[1]) * plan.s[li[1]] : 0;
+  const int64_t t2 = has_short ? tiles_of(sp[2]) * plan.s[2] : 0;
   if (t0 + t1 + t2 == 0) return hipSuccess;
   if (t0 + t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
+  const GemmKind lk = nl > 0 ? sk[li[0]] : long_kind;
+  const GemmKind shk = has_short ? sk[2] : short_kind;
   KGroup g;
-  g.p[0] = nl > 0 ? kargs(*lp[0], long_kind.a_order, long_kind.b_order) : KArgs{};
-  g.p[1] = nl > 1 ? kargs(*lp[1], long_kind.a_order, long_kind.b_order) : g.p[0];
-  g.p[2] = has_short ? kargs(*shortp, short_kind.a_order, short_kind.b_order) : g.p[0];
+  auto mk = [&](const GemmProblem& q, int i, const GemmKind& k) {
+    KArgs a = kargs(q, k.a_order, k.b_order);
+    if (plan.s[i] > 1) {
+      const int ks = (q.K + BK - 1) / BK;
+      a.ksplit = plan.s[i];
+      a.kchunk = (ks + plan.s[i] - 1) / plan.s[i] * BK;
+      a.sSlice = static_cast<int64_t>(q.batch) * q.M * q.N;
+    }
+    return a;
+  };
+  g.p[0] = nl > 0 ? mk(*lp[0], li[0], lk) : KArgs{};
+  g.p[1] = nl > 1 ? mk(*lp[1], li[1], lk) : g.p[0];
+  g.p[2] = has_short ? mk(sp[2], 2, shk) : g.p[0];
   g.t0 = static_cast<int>(t0);
   g.t1 = static_cast<int>(t1);
   g.t2 = static_cast<int>(t2);
   g.split = make_split(g.t0, g.t1, g.t2);
   // with no long-group problem the launch is of the short kind alone, and
   // vice versa
-  const GemmKind& k0 = nl > 0 ? long_kind : short_kind;
-  const GemmKind& k1 = has_short ? short_kind : long_kind;
+  const GemmKind& k0 = nl > 0 ? lk : shk;
+  const GemmKind& k1 = has_short ? shk : lk;
   auto is = [](const GemmKind& x, int ao, int bo, int epi) {
     return x.a_order == ao && x.b_order == bo && x.epi == epi;
   };
   const bool same = is(k1, k0.a_order, k0.b_order, k0.epi);
+  hipError_t e = hipErrorInvalidValue;
   if (same && is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
-    return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
-  if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
-    return launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY>(g, stream);
-  if (same && is(k0, KMAJ, MNMAJ, EPI_STORE))
-    return launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE>(g, stream);
-  if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_STORE))
-    return launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_BIAS_STORE>(g, stream);
-  if (same && is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))
-    return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
-  if (same && is(k0, KMAJ, KMAJ, EPI_STORE))
-    return launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE>(g, stream);
-  if (same && is(k0, KMAJ, KMAJ, EPI_STORE_ROWSTATS))
-    return launch_t<KMAJ, KMAJ, EPI_STORE_ROWSTATS, KMAJ, KMAJ, EPI_STORE_ROWSTATS>(g, stream);
-  if (same && is(k0, MNMAJ, MNMAJ, EPI_STORE_F32))
-    return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, MNMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
-  // the backward's last launch: both weight gradients, then dgrad-2
-  if (is(k0, MNMAJ, MNMAJ, EPI_STORE_F32) && is(k1, KMAJ, KMAJ, EPI_STORE))
-    return launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, KMAJ, KMAJ, EPI_STORE>(g, stream);
-  return hipErrorInvalidValue;
+    e = launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
+  else if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
+    e = launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY>(g, stream);
+  else if (same && is(k0, KMAJ, MNMAJ, EPI_STORE))
+    e = launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE>(g, stream);
+  else if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_STORE))
+    e = launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_BIAS_STORE>(g, stream);
+  else if (same && is(k0, KMAJ, MNMAJ, EPI_STORE_F32))
+    e = launch_t<KMAJ, MNMAJ, EPI_STORE_F32, KMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  else if (same && is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))
+    e = launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
+  else if (same && is(k0, KMAJ, KMAJ, EPI_STORE))
+    e = launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE>(g, stream);
+  else if (same && is(k0, KMAJ, KMAJ, EPI_STORE_ROWSTATS))
+    e = launch_t<KMAJ, KMAJ, EPI_STORE_ROWSTATS, KMAJ, KMAJ, EPI_STORE_ROWSTATS>(g, stream);
+  else if (same && is(k0, KMAJ, KMAJ, EPI_STORE_F32))
+    e = launch_t<KMAJ, KMAJ, EPI_STORE_F32, KMAJ, KMAJ, EPI_STORE_F32>(g, stream);
+  else if (same && is(k0, MNMAJ, MNMAJ, EPI_STORE_F32))
+    e = launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, MNMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  // the backward's last launch: both weight gradients, then dgrad-2 (as
+  // itself, or as its K-split fp32 partials)
+  else if (is(k0, MNMAJ, MNMAJ, EPI_STORE_F32) && is(k1, KMAJ, KMAJ, EPI_STORE))
+    e = launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, KMAJ, KMAJ, EPI_STORE>(g, stream);
+  else if (is(k0, MNMAJ, MNMAJ, EPI_STORE_F32) && is(k1, KMAJ, KMAJ, EPI_STORE_F32))
+    e = launch_t<MNMAJ, MNMAJ, EPI_STORE_F32, KMAJ, KMAJ, EPI_STORE_F32>(g, stream);
+  if (e != hipSuccess) return e;
+  // the fix-ups, in slot order
+  for (int i = 0; i < 3; ++i) {
+    if (slot[i] == nullptr || plan.s[i] <= 1 || empty(sp[i])) continue;
+    e = fixup(*slot[i], kslot[i]->epi, reinterpret_cast<const float*>(wsb + plan.off[i]), plan.s[i], stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_bf16(const GemmProblem& p, int a_order, int b_order, int epi, hipStream_t stream) {
   const GemmKind k{a_order, b_order, epi};
-  return launch_gemm_bf16_group(&p, 1, k, nullptr, k, stream);
+  return launch_gemm_bf16_group(&p, 1, k, nullptr, k, nullptr, 0, stream);
+}
+
+hipError_t launch_gemm_bf16_ws(const GemmProblem& p, int a_order, int b_order, int epi, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  const GemmKind k{a_order, b_order, epi};
+  return launch_gemm_bf16_group(&p, 1, k, nullptr, k, ws, ws_bytes, stream);
 }
 
 }  // namespace tpmlp

@@ -54,8 +54,16 @@ struct GemmKind {
 // optional short problem of another kind whose tiles fill in around them.
 // Empty problems are skipped.  Supported: equal kinds, and a long group of
 // (MNMAJ, MNMAJ, EPI_STORE_F32) with a short (KMAJ, KMAJ, EPI_STORE).
+// With a workspace of at least gemm_bf16_split_bytes(...) bytes, problems
+// that would leave the machine idle run K-split (fp32 partials in ws, then a
+// fix-up kernel per split problem); with less (or none), nothing is split.
+size_t gemm_bf16_split_bytes(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
+                             const GemmProblem* shortp, const GemmKind& short_kind);
 hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
-                                  const GemmProblem* shortp, const GemmKind& short_kind, hipStream_t stream);
+                                  const GemmProblem* shortp, const GemmKind& short_kind, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+hipError_t launch_gemm_bf16_ws(const GemmProblem& p, int a_order, int b_order, int epi, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
 // fp32 throughout.
 hipError_t launch_gemm_f32(const GemmProblem& p, int a_order, int b_order, int epi,
                            hipStream_t stream);

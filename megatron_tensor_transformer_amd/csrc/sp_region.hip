@@ -164,7 +164,112 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ------------------------------------------------------------------ raw 16-B loads
+// Buffer loads whose offset may be past the buffer's range (then they read
+// zeros and touch no memory), so every wave issues the same number of loads
+// whether or not a row exists: the compiler's counted waits then let the next
+// row's loads stay in flight while the current row is computed.
+extern "C" __device__ i32x4 tpmlp_llvm_buffer_load_v4(i32x4 rsrc, int voffset, int soffset,
+                                                      int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+constexpr uint32_t SP_OOB = 0x80000000u;  // past every range (operands are < 2^31 bytes)
+constexpr int AUX_NT = 2;                 // nontemporal: read once
+
+__device__ __forceinline__ i32x4 raw_load(i32x4 rsrc, uint32_t off) {
+  return tpmlp_llvm_buffer_load_v4(rsrc, static_cast<int>(off), 0, AUX_NT);
+}
+
+// 8 bf16 values held as one 16-B word -> fp32
+__device__ __forceinline__ void raw_to_f(i32x4 r, float (&v)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t u = static_cast<uint32_t>(r[q]);
+    v[2 * q] = __uint_as_float(u << 16);
+    v[2 * q + 1] = __uint_as_float(u & 0xFFFF0000u);
+  }
+}
+
 // ------------------------------------------------------------------ LN forward
+// bf16, h ≤ 4096: a wave walks rows r, r + W, ... (W waves in the grid); the
+// next row's loads are issued before the current row is reduced and written,
+// so each wave keeps a row in flight while it computes.  The γ and β chunks of
+// the output are loaded before the next row's prefetch, so waiting for them
+// leaves the prefetch in flight.
+__global__ __launch_bounds__(SP_THREADS) void ln_fwd_pipe_kernel(SpProblem p) {
+  constexpr int MAXC = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * (SP_THREADS / WAVE);
+  int64_t row = static_cast<int64_t>(blockIdx.x) * (SP_THREADS / WAVE) + (threadIdx.x >> 6);
+  if (row >= p.s) return;
+  const int hc = static_cast<int>(p.h / 8);
+  const float inv_h = 1.0f / static_cast<float>(p.h);
+  const i32x4 rx = make_rsrc(p.x, static_cast<uint32_t>(p.s * p.h * 2));
+  const i32x4 rg = make_rsrc(p.gamma, static_cast<uint32_t>(p.h * 2));
+  const i32x4 rb = make_rsrc(p.beta, static_cast<uint32_t>(p.h * 2));
+  i32x4 nxt[MAXC];
+  auto issue = [&](int64_t r) {
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      const int c = lane + WAVE * k;
+      nxt[k] = raw_load(rx, r < p.s && c < hc ? static_cast<uint32_t>((r * p.h + c * 8) * 2) : SP_OOB);
+    }
+  };
+  issue(row);
+  for (;;) {
+    float v[MAXC][8];
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) raw_to_f(nxt[k], v[k]);  // chunks past h read as zeros
+    i32x4 g[MAXC], b[MAXC];
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      const int c = lane + WAVE * k;
+      const uint32_t off = c < hc ? static_cast<uint32_t>(c * 16) : SP_OOB;
+      g[k] = tpmlp_llvm_buffer_load_v4(rg, static_cast<int>(off), 0, 0);
+      b[k] = tpmlp_llvm_buffer_load_v4(rb, static_cast<int>(off), 0, 0);
+    }
+    issue(row + nw);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += v[k][e];
+    sum = wave_sum(sum);
+    const float mean = sum * inv_h;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      if (lane + WAVE * k < hc) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = v[k][e] - mean;
+          q += d * d;
+        }
+      }
+    }
+    q = wave_sum(q);
+    const float rstd = 1.0f / sqrtf(q * inv_h + p.eps);
+    bf16* yr = static_cast<bf16*>(p.ln_out) + row * p.h;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      const int c = lane + WAVE * k;
+      if (c < hc) {
+        float gf[8], bf[8], o[8];
+        raw_to_f(g[k], gf);
+        raw_to_f(b[k], bf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf((v[k][e] - mean) * rstd, gf[e], bf[e]);
+        store8(yr + c * 8, o);
+      }
+    }
+    if (lane == 0) {
+      p.mean[row] = mean;
+      p.rstd[row] = rstd;
+    }
+    row += nw;
+    if (row >= p.s) break;
+  }
+  wait_vmcnt<0>();  // the last (empty) prefetch
+}
+
 // A 512-thread block normalises rows 2b and 2b+1; thread j owns chunk j of
 // each (h ≤ 4096).  Two passes over the registers (mean, then the biased
 // variance of x - mean), each a wave sum combined over the 8 waves in a fixed
@@ -435,7 +540,162 @@ __global__ __launch_bounds__(SP_THREADS) void dropres_kernel(SpProblem p) {
   }
 }
 
+// Forward, bf16, t = 8 partials: the loads of x and the partials are issued
+// first and the chunk's Philox blocks computed while they are in flight; the
+// sum of the partials is then formed in shard order as in dropres_kernel, so
+// the results are the same bit for bit.
+__global__ __launch_bounds__(SP_THREADS) void dropres_fwd8_kernel(SpProblem p) {
+  constexpr int T8 = 8;
+  const int64_t nchunk = p.s * p.h / 8;
+  const int64_t count = p.s * p.h;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * SP_THREADS;
+  const int64_t ch0 = static_cast<int64_t>(blockIdx.x) * SP_THREADS + threadIdx.x;
+  const bf16* bias = static_cast<const bf16*>(p.bias);
+  const int64_t hc = p.h / 8;
+  int64_t cc = 0, dcc = 0;
+  if (bias != nullptr) {
+    cc = ch0 % hc;
+    dcc = step % hc;
+  }
+  const i32x4 rx = make_rsrc(p.x, static_cast<uint32_t>(count * 2));
+  const i32x4 rp = make_rsrc(p.partials, static_cast<uint32_t>(T8 * count * 2));
+  for (int64_t ch = ch0; ch < nchunk; ch += step) {
+    const int64_t e = ch * 8;
+    const uint32_t off = static_cast<uint32_t>(e * 2);
+    const i32x4 xin = raw_load(rx, off);
+    i32x4 pr[T8];
+#pragma unroll
+    for (int i = 0; i < T8; ++i) pr[i] = raw_load(rp, off + static_cast<uint32_t>(i * count * 2));
+    // keep the loads ahead of the Philox arithmetic and the arithmetic ahead
+    // of the first wait for their data (the scheduler would otherwise start
+    // the sum first and leave the arithmetic for after the loads)
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t keep = keep8(static_cast<uint64_t>(p.row0 * p.h + e), p.seed, p.drop_threshold);
+    asm volatile("" : "+v"(keep));  // materialised here, not sunk to its later use
+    __builtin_amdgcn_sched_barrier(0);
+    float v[8], xr[8];
+    raw_to_f(xin, xr);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < T8; ++i) {
+      float w[8];
+      raw_to_f(pr[i], w);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += w[k];
+    }
+    if (bias != nullptr) {
+      float b[8];
+      load8<bf16, false>(bias + cc * 8, b);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += b[k];
+      cc += dcc;
+      if (cc >= hc) cc -= hc;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xr[k] + (((keep >> k) & 1u) ? v[k] * p.keep_scale : 0.0f);
+    store8(static_cast<bf16*>(p.out) + e, v);
+  }
+}
+
 // ------------------------------------------------------------------ LN backward
+// bf16, t = 8 partials, h ≤ 4096: ln_bwd_kernel with the next row's loads (x,
+// g_out and the 8 partials) issued before the current row is reduced across
+// the block and written, so a block keeps a row in flight while it computes.
+// Same arithmetic in the same order as ln_bwd_kernel.
+__global__ __launch_bounds__(LNB_THREADS, 2) void ln_bwd_pipe_kernel(SpProblem p) {
+  constexpr int T8 = 8;
+  __shared__ float red[2][LNB_WAVES][2];  // [row parity][wave][s1, s2]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = threadIdx.x;
+  const bool mine = c < p.h / 8;
+  const int64_t count = p.s * p.h;
+  const int64_t nb = gridDim.x;
+  const float inv_h = 1.0f / static_cast<float>(p.h);
+  const i32x4 rx = make_rsrc(p.x, static_cast<uint32_t>(count * 2));
+  const i32x4 rg = make_rsrc(p.g_out, static_cast<uint32_t>(count * 2));
+  const i32x4 rp = make_rsrc(p.dU_partials, static_cast<uint32_t>(T8 * count * 2));
+
+  float gq[8], dg[8], db[8];
+  if (mine) load8<bf16, false>(static_cast<const bf16*>(p.gamma) + c * 8, gq);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dg[k] = db[k] = 0.f;
+
+  i32x4 nx, ng, np[T8];
+  auto issue = [&](int64_t r) {
+    const uint32_t off = r < p.s && mine ? static_cast<uint32_t>((r * p.h + c * 8) * 2) : SP_OOB;
+    nx = raw_load(rx, off);
+    ng = raw_load(rg, off);
+#pragma unroll
+    for (int i = 0; i < T8; ++i)
+      np[i] = raw_load(rp, off == SP_OOB ? SP_OOB : off + static_cast<uint32_t>(i * count * 2));
+  };
+  int64_t row = blockIdx.x;
+  issue(row);
+  for (int par = 0;; par ^= 1) {
+    float du[8], xh[8], go[8];
+    raw_to_f(nx, xh);
+    raw_to_f(ng, go);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) du[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < T8; ++i) {
+      float w[8];
+      raw_to_f(np[i], w);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) du[k] += w[k];
+    }
+    const float mu = p.mean[row], rs = p.rstd[row];
+    issue(row + nb);
+    float sm[2] = {0.f, 0.f};
+    if (mine) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        xh[k] = (xh[k] - mu) * rs;
+        const float gt = du[k] * gq[k];
+        sm[0] += gt;
+        sm[1] += gt * xh[k];
+        dg[k] += du[k] * xh[k];
+        db[k] += du[k];
+      }
+    }
+    sm[0] = wave_sum(sm[0]);
+    sm[1] = wave_sum(sm[1]);
+    if (lane == 0) {
+      red[par][wave][0] = sm[0];
+      red[par][wave][1] = sm[1];
+    }
+    __syncthreads();
+    float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < LNB_WAVES; ++w) {
+      m1 += red[par][w][0];
+      m2 += red[par][w][1];
+    }
+    // red[par] is rewritten two rows on, after the next barrier
+    m1 *= inv_h;
+    m2 *= inv_h;
+    if (mine) {
+      float o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = go[k] + rs * (du[k] * gq[k] - m1 - xh[k] * m2);
+      store8(static_cast<bf16*>(p.dx) + row * p.h + c * 8, o);
+    }
+    row += nb;
+    if (row >= p.s) break;
+  }
+  wait_vmcnt<0>();  // the last (empty) prefetch
+  const int64_t h = p.h;
+  if (mine) {
+    float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * 2 * h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ws[c * 8 + k] = dg[k];
+      ws[h + c * 8 + k] = db[k];
+    }
+  }
+}
+
 // Block b handles rows b, b + nb, b + 2·nb, ... (nb = gridDim.x); thread j
 // owns chunk j of every row (h ≤ 4096).  Per row: dU = Σ_i dU_i,
 // x̂ = (x-μ)·rstd, g̃ = dU⊙γ, dx = g_out + rstd·(g̃ - mean(g̃) - x̂·mean(g̃⊙x̂));
@@ -559,6 +819,13 @@ hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
                            stream, p);
         return hipGetLastError();
       }
+      if constexpr (sizeof(T) == 2) {
+        // about two rows per wave, at most 2048 waves (8 per CU)
+        const int64_t waves = (p.s + 1) / 2 < 2048 ? (p.s + 1) / 2 : 2048;
+        const int64_t blocks = (waves + SP_THREADS / WAVE - 1) / (SP_THREADS / WAVE);
+        hipLaunchKernelGGL(ln_fwd_pipe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(SP_THREADS), 0, stream, p);
+        return hipGetLastError();
+      }
       const int64_t blocks = (p.s + SP_THREADS / WAVE - 1) / (SP_THREADS / WAVE);  // one wave per row
       hipLaunchKernelGGL((ln_fwd_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(SP_THREADS), 0, stream,
                          p);
@@ -569,7 +836,12 @@ hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
       const int64_t nchunk = p.s * p.h / 8;
       int64_t blocks = (nchunk + SP_THREADS - 1) / SP_THREADS;
       if (blocks > 16384) blocks = 16384;
-      if (p.phase == 1)
+      if (sizeof(T) == 2 && p.phase == 1 && p.t == 8) {
+        // (the backward's dropout kernel is bound by the Philox arithmetic:
+        // issuing its one load ahead of it gained nothing, so it keeps the
+        // plain form)
+        hipLaunchKernelGGL(dropres_fwd8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(SP_THREADS), 0, stream, p);
+      } else if (p.phase == 1)
         hipLaunchKernelGGL((dropres_kernel<T, true>), dim3(static_cast<unsigned>(blocks)), dim3(SP_THREADS), 0,
                            stream, p);
       else
@@ -591,6 +863,8 @@ hipError_t launch_dt(const SpProblem& p, hipStream_t stream) {
         const int64_t slabs = (p.h / 8 + LNW_THREADS - 1) / LNW_THREADS;
         hipLaunchKernelGGL((ln_bwd_wide_kernel<T>), dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(slabs)),
                            dim3(LNW_THREADS), 0, stream, p, static_cast<const float*>(rowstats));
+      } else if (sizeof(T) == 2 && p.t == 8) {
+        hipLaunchKernelGGL(ln_bwd_pipe_kernel, dim3(static_cast<unsigned>(nblk)), dim3(LNB_THREADS), 0, stream, p);
       } else {
         // one chunk of each row per thread
         hipLaunchKernelGGL((ln_bwd_kernel<T>), dim3(static_cast<unsigned>(nblk)), dim3(LNB_THREADS), 0,

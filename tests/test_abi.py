@@ -42,14 +42,14 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 7
+    assert L.tpmlp_abi_version() == 8
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         assert L.tpmlp_status_string(s)
 
 
-def _fwd(L, dt=1, n=64, d=64, mi=64, t=2, ptr=0x1000):
+def _fwd(L, dt=1, n=64, d=64, mi=64, t=2, ptr=0x1000, ws=None, ws_bytes=0):
     p = ctypes.c_void_p(ptr)
-    return L.tpmlp_fwd(None, dt, n, d, mi, t, p, p, p, p, p, p)
+    return L.tpmlp_fwd(None, dt, n, d, mi, t, p, p, p, p, p, p, ws, ws_bytes)
 
 
 def test_fwd_validation(L):
@@ -69,11 +69,33 @@ def test_fwd_validation(L):
     assert _fwd(L, dt=0, d=3, mi=5, ptr=0x1002) == tp.ERR_ALIGN
 
 
+def test_split_k_workspace(L):
+    """Shapes whose products leave the GPU idle (few 256×256 tiles, long K)
+    need a workspace for their K-split partials; the 8.3B-shaped layer and
+    the fp32 path need none.  A missing or short workspace is refused before
+    anything is enqueued."""
+    fw, bw = L.tpmlp_fwd_workspace_bytes, L.tpmlp_bwd_workspace_bytes
+    assert fw(1, 8192, 3072, 1536, 8) == 0 and bw(1, 8192, 3072, 1536, 8) == 0
+    assert fw(0, 2048, 1024, 4096, 1) == 0 and bw(0, 2048, 1024, 4096, 1) == 0
+    # single-shard layer: P = Y·B has 8×4 tiles over K = 4096 (split in 4),
+    # dX likewise (split in 2): S fp32 planes of n×d each
+    assert fw(1, 2048, 1024, 4096, 1) == 4 * 2048 * 1024 * 4
+    assert bw(1, 2048, 1024, 4096, 1) == 2 * 2048 * 1024 * 4
+    assert L.tpmlp_fwd_bias_workspace_bytes(1, 2048, 1024, 4096, 1) == fw(1, 2048, 1024, 4096, 1)
+    need = fw(1, 2048, 1024, 4096, 1)
+    assert _fwd(L, n=2048, d=1024, mi=4096, t=1) == tp.ERR_WORKSPACE
+    assert _fwd(L, n=2048, d=1024, mi=4096, t=1, ws=ctypes.c_void_p(0x1000), ws_bytes=need - 1) == tp.ERR_WORKSPACE
+    assert _fwd(L, n=2048, d=1024, mi=4096, t=1, ws=ctypes.c_void_p(0x1008), ws_bytes=need) == tp.ERR_ALIGN
+    p = ctypes.c_void_p(0x1000)
+    a = [p] * 10
+    assert L.tpmlp_bwd(None, 1, 2048, 1024, 4096, 1, *a, None, 0) == tp.ERR_WORKSPACE
+
+
 def test_fwd_bias_validation(L):
     p = ctypes.c_void_p(0x1000)
 
     def call(b1=p, dt=1, n=64, d=64, mi=64, t=2):
-        return L.tpmlp_fwd_bias(None, dt, n, d, mi, t, p, p, p, b1, p, p, p)
+        return L.tpmlp_fwd_bias(None, dt, n, d, mi, t, p, p, p, b1, p, p, p, None, 0)
     assert call(b1=None) == tp.ERR_NULLPTR
     assert call(b1=ctypes.c_void_p(0x1008)) == tp.ERR_ALIGN
     assert call(dt=0, b1=ctypes.c_void_p(0x1002)) == tp.ERR_ALIGN

@@ -39,17 +39,20 @@ def _buffers(X, A, B):
         dXp=torch.empty((t, n, d), dtype=X.dtype, **e),
         dX=torch.empty((n, d), dtype=X.dtype, **e),
         ws=torch.empty(max(tp.bwd_workspace_bytes(X, A), 16), dtype=torch.uint8, **e),
+        wsf=torch.empty(max(tp.fwd_workspace_bytes(X, A), 16), dtype=torch.uint8, **e),
     )
 
 
 def _step(X, A, B, G, o):
-    tp.tpmlp_fwd(X, A, B, o["Z"], o["Y"], o["P"])
+    tp.tpmlp_fwd(X, A, B, o["Z"], o["Y"], o["P"], o["wsf"])
     tp.tpmlp_reduce_partials(o["P"], o["O"])
     tp.tpmlp_bwd(X, A, B, o["Z"], o["Y"], G, o["D"], o["dA"], o["dB"], o["dXp"], o["ws"])
     tp.tpmlp_reduce_partials(o["dXp"], o["dX"])
 
 
-@pytest.mark.parametrize("dtype,n,d,m,t", [("bf16", 520, 264, 512, 4), ("f32", 130, 72, 96, 3)])
+@pytest.mark.parametrize("dtype,n,d,m,t", [("bf16", 520, 264, 512, 4), ("f32", 130, 72, 96, 3),
+                                           # K-split products (the fix-up kernels are captured too)
+                                           ("bf16", 256, 2048, 512, 1)])
 def test_step_graph_replays_match_eager(dtype, n, d, m, t):
     say(f"[gpu] graph capture {dtype} n={n} d={d} m={m} t={t}")
     sets = []

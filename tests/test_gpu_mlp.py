@@ -75,6 +75,49 @@ def test_bf16_ragged(n, d, m, t):
     compare_full(inp, t, "bf16")
 
 
+# Shapes whose products have too few output tiles for the GPU and a long K:
+# the library runs them K-split (fp32 slice partials in the workspace, then a
+# fix-up kernel per product).  Which products split is a function of the
+# sizes; the workspace queries show that each of these shapes splits.
+SPLIT_SHAPES = [
+    (256, 2048, 512, 1),    # GEMM1 (GeLU fix-up) and dgrad-1 (GeLU' fix-up) split
+    (300, 4096, 512, 2),    # the same with two shards, ragged M
+    (16384, 512, 256, 1),   # both weight gradients split (fp32 fix-up), K = n = 16384
+    (2048, 1024, 4096, 1),  # the single-shard config: GEMM2 and dgrad-2 split
+]
+
+
+@pytest.mark.parametrize("n,d,m,t", SPLIT_SHAPES)
+def test_bf16_split_k(n, d, m, t):
+    inp = mlp_inputs(n, d, m, t, dtype="bf16", seed=13)
+    X, A = dev(inp["X"]), shard_cols(dev(inp["A"]), t)
+    assert tp.fwd_workspace_bytes(X, A) + tp.bwd_workspace_bytes(X, A) > 0, "shape does not split"
+    compare_full(inp, t, "bf16", "K-split")
+
+
+def test_bf16_split_k_bias_and_determinism():
+    """The column bias in the split GEMM1's fix-up (bias + GeLU), and two runs
+    of a split step agree bit for bit."""
+    from tpmlp_inputs import bias_inputs
+    n, d, m, t = 256, 2048, 1024, 2
+    inp = mlp_inputs(n, d, m, t, dtype="bf16", seed=14)
+    b = bias_inputs(m, d, dtype="bf16", seed=14)
+    X, A, B, G = (dev(inp[k]) for k in "XABG")
+    A_s, B_s = shard_cols(A, t), shard_rows(B, t)
+    b1 = dev(b["b1"]).reshape(t, m // t).contiguous()
+    assert tp.fwd_workspace_bytes(X, A_s, bias=True) > 0
+    Z, Y, P = tp.mlp_fwd_bias(X, A_s, B_s, b1)
+    Z2, Y2, P2 = tp.mlp_fwd_bias(X, A_s, B_s, b1)
+    torch.cuda.synchronize()
+    for u, v in ((Z, Z2), (Y, Y2), (P, P2)):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+    fwd = om.tp_forward(inp["X"].f64, inp["A"].f64, inp["B"].f64, t, b1=b["b1"].f64)
+    for i in range(t):
+        assert relerr(Z[i], fwd["Z"][i]) <= TOL["bf16"]
+        assert relerr(Y[i], fwd["Y"][i]) <= TOL["bf16"]
+        assert relerr(P[i], fwd["P"][i]) <= TOL["bf16"]
+
+
 def test_single_shard_config():
     """t = 1, n = 4·512, d = 1024, m = 4096, bf16: full comparison."""
     compare_full(config_inputs("single_shard", seed=0), 1, "bf16", "single-shard config")
