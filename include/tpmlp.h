@@ -170,6 +170,34 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
               const void* G, void* D, float* dA, float* dB, void* dXp, void* ws, size_t ws_bytes);
 
 /*
+ * tpmlp_bwd_bias -- tpmlp_bwd of the biased layer (tpmlp_fwd_bias), with the
+ * two bias gradients ([TRAIN] custom autograd matmul: a bias broadcast over
+ * the rows gets the upstream gradient summed over the rows):
+ *
+ *   db1_i = Σ_rows D_i   [t_local, m_i] fp32 (the column-parallel bias,
+ *                        split like A's columns)
+ *   db2   = Σ_rows G     [d] fp32 (the row-parallel bias, added once)
+ *
+ * On the bf16 path the column sums of D are taken in the dgrad-1 GEMM's
+ * epilogue, of the values as stored (bf16), per 128-row chunk ([EFF] §4.2:
+ * the bias work fused into the GEMM instead of a pass over D); the chunk
+ * sums are then added in chunk order.  db2 is a two-stage column sum of G
+ * as in tpmlp_bias_grad.  Both orders are fixed, so results are
+ * bit-reproducible; db1 differs from tpmlp_bias_grad's over the stored D only
+ * by the fp32 summation order.
+ *
+ *   Everything else as for tpmlp_bwd; db1, db2 not NULL, 4-byte aligned;
+ *   t_local <= 65535.  With n == 0, dA, dB, db1 and db2 are set to zero.
+ *   ws / ws_bytes: at least tpmlp_bwd_bias_workspace_bytes(...) bytes,
+ *   16-byte aligned (the chunk sums of D and G, plus tpmlp_bwd's split
+ *   partials of the weight-gradient launch; dgrad-1 is never split here).
+ */
+size_t tpmlp_bwd_bias_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local);
+int tpmlp_bwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+                   const void* X, const void* A, const void* B, const void* Z, const void* Y, const void* G, void* D,
+                   float* dA, float* dB, void* dXp, float* db1, float* db2, void* ws, size_t ws_bytes);
+
+/*
  * tpmlp_reduce_partials -- out = Σ_{i=0}^{t-1} partials[i]  (the one-GPU
  * stand-in for the all-reduce after the row-parallel GEMM and for the
  * all-reduce of the column-parallel input gradient: [TRAIN] RowParallelLinear

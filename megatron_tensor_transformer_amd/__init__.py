@@ -62,6 +62,8 @@ SIGNATURES = {
     "tpmlp_fwd_bias": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
     "tpmlp_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I32]),
     "tpmlp_bwd": (_I, [_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
+    "tpmlp_bwd_bias_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I32]),
+    "tpmlp_bwd_bias": (_I, [_P, _I, _I64, _I64, _I64, _I32] + [_P] * 13 + [_SZ]),
     "tpmlp_reduce_partials": (_I, [_P, _I, _I, _I32, _I64, _I64, _P, _P]),
     "tpmlp_reduce_partials_bias": (_I, [_P, _I, _I, _I32, _I64, _I64, _P, _P, _P]),
     "tpmlp_bias_grad_workspace_bytes": (_SZ, [_I32, _I64, _I64]),
@@ -215,6 +217,23 @@ def tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().tpmlp_bwd(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B), _ptr(Z),
                            _ptr(Y), _ptr(G), _ptr(D), _ptr(dA), _ptr(dB), _ptr(dXp), _ptr(ws), ws_bytes))
+
+
+def tpmlp_bwd_bias(X, A, B, Z, Y, G, D, dA, dB, dXp, db1, db2, ws=None, stream=None):
+    """tpmlp_bwd plus the bias gradients db1 [t, m_i] = Σ_rows D_i and db2 [d] = Σ_rows G (fp32)."""
+    t, d, mi = _dims("A", A, 3)
+    n = _dims("X", X, 2)[0]
+    dt, f32 = _path_dtype(X), torch.float32
+    if db1 is None or db2 is None:
+        raise TpmlpValueError(ERR_NULLPTR, "db1 and db2 are required")
+    _expect(X, ("X", X, (n, d), dt), ("A", A, (t, d, mi), dt), ("B", B, (t, mi, d), dt),
+            ("Z", Z, (t, n, mi), dt), ("Y", Y, (t, n, mi), dt), ("G", G, (n, d), dt), ("D", D, (t, n, mi), dt),
+            ("dA", dA, (t, d, mi), f32), ("dB", dB, (t, mi, d), f32), ("dXp", dXp, (t, n, d), dt),
+            ("db1", db1, (t, mi), f32), ("db2", db2, (d,), f32), ("ws", ws, None, None))
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().tpmlp_bwd_bias(_stream(stream), _dt(X), n, d, mi, t, _ptr(X), _ptr(A), _ptr(B), _ptr(Z),
+                                _ptr(Y), _ptr(G), _ptr(D), _ptr(dA), _ptr(dB), _ptr(dXp), _ptr(db1), _ptr(db2),
+                                _ptr(ws), ws_bytes))
 
 
 def _reduce_check(partials, out, final=True):
@@ -429,6 +448,26 @@ def mlp_bwd(X, A, B, Z, Y, G, stream=None):
     ws = torch.empty(nb, dtype=torch.uint8, device=X.device) if nb else None
     tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp, ws, stream)
     return D, dA, dB, dXp
+
+
+def bwd_bias_workspace_bytes(X, A):
+    t, d, mi = A.shape
+    return lib().tpmlp_bwd_bias_workspace_bytes(_dt(X), X.shape[0], d, mi, t)
+
+
+def mlp_bwd_bias(X, A, B, Z, Y, G, stream=None):
+    """Allocating wrapper: returns D, dA, dB, dXp, db1 [t, m_i], db2 [d] (fp32 gradients)."""
+    t, d, mi = A.shape
+    n = X.shape[0]
+    D = torch.empty((t, n, mi), dtype=X.dtype, device=X.device)
+    dA = torch.empty((t, d, mi), dtype=torch.float32, device=X.device)
+    dB = torch.empty((t, mi, d), dtype=torch.float32, device=X.device)
+    dXp = torch.empty((t, n, d), dtype=X.dtype, device=X.device)
+    db1 = torch.empty((t, mi), dtype=torch.float32, device=X.device)
+    db2 = torch.empty((d,), dtype=torch.float32, device=X.device)
+    tpmlp_bwd_bias(X, A, B, Z, Y, G, D, dA, dB, dXp, db1, db2, workspace(bwd_bias_workspace_bytes(X, A), X.device),
+                   stream)
+    return D, dA, dB, dXp, db1, db2
 
 
 def reduce_partials(partials, out_dtype=None, stream=None):

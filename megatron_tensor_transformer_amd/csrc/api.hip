@@ -302,16 +302,50 @@ size_t tpmlp_bwd_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int3
   return bwd_ws_bytes(dt, n, d, m_i, t_local);
 }
 
-int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
-              const void* X, const void* A, const void* B, const void* Z, const void* Y,
-              const void* G, void* D, float* dA, float* dB, void* dXp, void* ws, size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the biased backward: the weight-gradient launch's split
+// partials (dgrad-1 with the fused column sums is never split), then the
+// 128-row chunk column sums of D (db1) and of G (db2).
+struct BwdBiasWs {
+  size_t split, db1, db2, total;
+};
+
+BwdBiasWs bwd_bias_ws(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  BwdBiasWs w{0, 0, 0, 0};
+  if (check_mlp_dims(dt, n, d, m_i, t_local) != TPMLP_OK) return w;
+  if (dt == TPMLP_BF16) {
+    tpmlp::GemmProblem e, wb, wa, dx;
+    bwd_problems(n, d, m_i, t_local, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                 nullptr, e, wb, wa, dx);
+    const tpmlp::GemmProblem wp[2] = {wb, wa};
+    w.split = align256(tpmlp::gemm_bf16_split_bytes(wp, 2, kWgrad, &dx, kDgrad2));
+  }
+  const int64_t nc = tpmlp::bias_grad_chunks(n);
+  w.db1 = align256(static_cast<size_t>(t_local) * static_cast<size_t>(nc) * static_cast<size_t>(m_i) * 4);
+  w.db2 = align256(static_cast<size_t>(nc) * static_cast<size_t>(d) * 4);
+  w.total = w.split + w.db1 + w.db2;
+  return w;
+}
+
+// The shard backward; with db1 and db2 (both non-null) also the bias
+// gradients db1_i = Σ_rows D_i and db2 = Σ_rows G.
+int bwd_impl(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local, const void* X,
+             const void* A, const void* B, const void* Z, const void* Y, const void* G, void* D, float* dA, float* dB,
+             void* dXp, float* db1, float* db2, void* ws, size_t ws_bytes) {
   int st = check_mlp_dims(dt, n, d, m_i, t_local);
   if (st) return st;
-  const size_t need = tpmlp_bwd_workspace_bytes(dt, n, d, m_i, t_local);
+  const bool bias = db1 != nullptr;
+  const size_t need = bias ? bwd_bias_ws(dt, n, d, m_i, t_local).total : tpmlp_bwd_workspace_bytes(dt, n, d, m_i, t_local);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return TPMLP_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return TPMLP_ERR_ALIGN;
   if (dA == nullptr || dB == nullptr) return TPMLP_ERR_NULLPTR;
   if (!aligned(dA, wgrad_align(dt)) || !aligned(dB, wgrad_align(dt))) return TPMLP_ERR_ALIGN;
+  if (bias && (!aligned(db1, 4) || !aligned(db2, 4))) return TPMLP_ERR_ALIGN;
   if (n > 0) {
     st = check_ptrs(dt, {X, A, B, Z, Y, G, D, dXp});
     if (st) return st;
@@ -321,18 +355,49 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
   const tpmlp::GemmKind& wgrad = kWgrad;
   const tpmlp::GemmKind& dgrad1 = kDgrad1;
   const tpmlp::GemmKind& dgrad2 = kDgrad2;
+  // the biased backward's workspace regions
+  BwdBiasWs bw{0, 0, 0, 0};
+  float* ws_db1 = nullptr;
+  float* ws_db2 = nullptr;
+  void* ws_split = ws;
+  size_t split_bytes = ws_bytes;
+  if (bias) {
+    bw = bwd_bias_ws(dt, n, d, m_i, t_local);
+    ws_db1 = reinterpret_cast<float*>(static_cast<char*>(ws) + bw.split);
+    ws_db2 = reinterpret_cast<float*>(static_cast<char*>(ws) + bw.split + bw.db1);
+    split_bytes = bw.split;
+  }
   if (dt == TPMLP_BF16) {
     // Two launches: dgrad-1, then both weight gradients (K = n, the long
     // ones) with dgrad-2 (which also needs D), whose tiles fill the machine
     // around them.  Products that would leave the machine idle run K-split
-    // in the workspace.
-    st = hip_status(tpmlp::launch_gemm_bf16_ws(e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, ws, ws_bytes, stream));
+    // in the workspace.  With the bias gradients, dgrad-1's epilogue also
+    // writes the column sums of each 128-row chunk of D ([EFF] §4.2: the
+    // bias work fused into the GEMM), summed over the chunks after it.
+    if (bias) {
+      e.colsum = ws_db1;
+      st = hip_status(tpmlp::launch_gemm_bf16_ws(e, tpmlp::KMAJ, tpmlp::KMAJ, tpmlp::EPI_GELU_GRAD_DB, nullptr, 0,
+                                                 stream));
+      if (st) return st;
+      st = hip_status(tpmlp::launch_bias_grad_final(t_local, n, m_i, db1, ws_db1, stream));
+    } else {
+      st = hip_status(
+          tpmlp::launch_gemm_bf16_ws(e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, ws, ws_bytes, stream));
+    }
     if (st) return st;
     const tpmlp::GemmProblem w[2] = {wb, wa};
-    return hip_status(tpmlp::launch_gemm_bf16_group(w, 2, wgrad, &dx, dgrad2, ws, ws_bytes, stream));
+    st = hip_status(tpmlp::launch_gemm_bf16_group(w, 2, wgrad, &dx, dgrad2, ws_split, split_bytes, stream));
+    if (st || !bias) return st;
+    return hip_status(tpmlp::launch_bias_grad(dt, 1, n, d, G, db2, ws_db2, stream));
   }
   if (n > 0) {
     st = hip_status(gemm(dt, e, dgrad1.a_order, dgrad1.b_order, dgrad1.epi, stream));
+    if (st) return st;
+  }
+  if (bias) {
+    st = hip_status(tpmlp::launch_bias_grad(dt, t_local, n, m_i, D, db1, ws_db1, stream));
+    if (st) return st;
+    st = hip_status(tpmlp::launch_bias_grad(dt, 1, n, d, G, db2, ws_db2, stream));
     if (st) return st;
   }
   st = hip_status(gemm(dt, wb, wgrad.a_order, wgrad.b_order, wgrad.epi, stream));
@@ -344,6 +409,28 @@ int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int
     if (st) return st;
   }
   return TPMLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpmlp_bwd(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+              const void* X, const void* A, const void* B, const void* Z, const void* Y,
+              const void* G, void* D, float* dA, float* dB, void* dXp, void* ws, size_t ws_bytes) {
+  return bwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, Z, Y, G, D, dA, dB, dXp, nullptr, nullptr, ws, ws_bytes);
+}
+
+size_t tpmlp_bwd_bias_workspace_bytes(int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local) {
+  return bwd_bias_ws(dt, n, d, m_i, t_local).total;
+}
+
+int tpmlp_bwd_bias(hipStream_t stream, int dt, int64_t n, int64_t d, int64_t m_i, int32_t t_local,
+                   const void* X, const void* A, const void* B, const void* Z, const void* Y, const void* G, void* D,
+                   float* dA, float* dB, void* dXp, float* db1, float* db2, void* ws, size_t ws_bytes) {
+  if (db1 == nullptr || db2 == nullptr) return TPMLP_ERR_NULLPTR;
+  if (t_local > 65535) return TPMLP_ERR_SHAPE;  // the chunk sums' grid
+  return bwd_impl(stream, dt, n, d, m_i, t_local, X, A, B, Z, Y, G, D, dA, dB, dXp, db1, db2, ws, ws_bytes);
 }
 
 int tpmlp_reduce_partials(hipStream_t stream, int in_dt, int out_dt, int32_t t, int64_t rows,

@@ -58,6 +58,7 @@ struct alignas(64) KArgs {
   const bf16* bias;
   int64_t sBias;
   float* rstats;
+  float* colsum;
   int M, N, K;
   int tiles_m, tiles_n, batch;
   int64_t lda, ldb, ldc;
@@ -458,7 +459,8 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
       }
     }
 
-    if constexpr (EPI == EPI_GELU_GRAD) {
+    constexpr bool GG = EPI == EPI_GELU_GRAD || EPI == EPI_GELU_GRAD_DB;
+    if constexpr (GG) {
       // Stage this region's stored Z (same layout) with 16-B DMA loads:
       // load j covers rows 8j..8j+7; lane: row 8j + L/8, slot L%8.
       const i32x4 rZ = make_rsrc(a.Zin + cbase, a.c_bytes);
@@ -475,6 +477,16 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
       wait_vmcnt<0>();
     }
 
+    // EPI_GELU_GRAD_DB: this lane's column sums, over the wave's 128 rows,
+    // of the values as stored (bf16-rounded); entry 4q + e of cs[j] is
+    // column qn0 + 32j + 8q + 4·half + e
+    float cs[FB][16];
+    if constexpr (EPI == EPI_GELU_GRAD_DB) {
+#pragma unroll
+      for (int j = 0; j < FB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cs[j][e] = 0.f;
+    }
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
       // accumulators -> bf16 -> staging region, one 32×32 block at a time
@@ -494,7 +506,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
                        : "+v"(zr[0][0]), "+v"(zr[0][1]), "+v"(zr[0][2]), "+v"(zr[0][3]), "+v"(zr[1][0]),
                          "+v"(zr[1][1]), "+v"(zr[1][2]), "+v"(zr[1][3])::"memory");
         }
-        if constexpr (EPI == EPI_GELU_GRAD) {
+        if constexpr (GG) {
 #pragma unroll
           for (int j = 0; j < FB; ++j)
 #pragma unroll
@@ -529,7 +541,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 #pragma unroll
               for (int e = 0; e < 16; ++e) v[e] = gelu_fast(v[e]);
             }
-          } else if constexpr (EPI == EPI_GELU_GRAD) {
+          } else if constexpr (GG) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const bf16x4 z = __builtin_bit_cast(bf16x4, zr[j][q]);
@@ -540,6 +552,16 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
           i32x2 pk[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) pk[q] = pack4_bf16(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          if constexpr (EPI == EPI_GELU_GRAD_DB) {
+            // rows past M and columns past N hold zeros (zero-filled operands)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t w = static_cast<uint32_t>(pk[q][e >> 1]);
+                cs[j][4 * q + e] += __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+              }
+          }
           if constexpr (EPI == EPI_STORE_ROWSTATS) {
             // value 4q + e is column qn0 + 32j + 8q + 4·half + e; columns past N
             // take no part
@@ -611,6 +633,37 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
           if (gr < a.M && gc < a.N)
             __builtin_nontemporal_store(v[u], reinterpret_cast<i32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc));
         }
+      }
+    }
+    if constexpr (EPI == EPI_GELU_GRAD_DB) {
+      // sum over the 32 rows of each half (lanes of one half hold one row
+      // each), in a fixed butterfly order; lane 0 / 32 then holds the wave's
+      // 128-row column sums of its half's columns
+#pragma unroll
+      for (int j = 0; j < FB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float x = cs[j][e];
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, 64);
+          cs[j][e] = x;
+        }
+      const int64_t nchunk = (a.M + 127) / 128;
+      const int64_t chunk = qm0 / 128;
+      if (row_l == 0 && chunk < nchunk) {
+        float* out = a.colsum + (static_cast<int64_t>(batch) * nchunk + chunk) * a.N;
+#pragma unroll
+        for (int j = 0; j < FB; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = qn0 + 32 * j + 8 * q + 4 * half;
+            if (col < a.N) {
+              f32x4 w;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) w[e] = cs[j][4 * q + e];
+              *reinterpret_cast<f32x4*>(out + col) = w;
+            }
+          }
       }
     }
   }
@@ -775,6 +828,7 @@ KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
   k.bias = static_cast<const bf16*>(p.bias);
   k.sBias = p.sBias;
   k.rstats = p.rstats;
+  k.colsum = p.colsum;
   k.M = p.M;
   k.N = p.N;
   k.K = p.K;
@@ -810,11 +864,15 @@ int64_t tiles_of(const GemmProblem& p) {
 // epilogue.  The choice minimises a cost model in units of one K step (64) of
 // a tile on a loaded machine: the launch takes about max(longest tile,
 // total tile work / 256 CUs), each tile also pays a fixed prologue/epilogue,
-// and a split pays its fix-up's fp32 traffic and launch.  The choice depends
-// only on the shapes, so a call is bit-reproducible.
-constexpr double kTileFixedSteps = 4.0;  // a tile's prologue + epilogue (≈ 6.7 µs at ≈ 1.6 µs per step)
-constexpr double kFixBytesPerStep = 6.4e6;  // fix-up traffic per step time (≈ 4 TB/s × 1.6 µs)
-constexpr double kFixLaunchSteps = 2.0;
+// and a split pays its fix-up kernel, which reads the S fp32 partial planes
+// (the GEMM writes them in its epilogue, in place of the output).  The
+// choice depends only on the shapes, so a call is bit-reproducible.
+// Measured on the single-shard layer (n = 2048, d = 1024, m = 4096): a
+// 16-step tile takes 31 µs alone on the GPU, about 1.5 µs per step plus
+// ≈ 6 µs; the fix-up reads its planes at ≈ 5.4 TB/s.
+constexpr double kTileFixedSteps = 4.0;     // a tile's prologue + epilogue
+constexpr double kFixBytesPerStep = 8.0e6;  // fix-up reads per step time (≈ 5.4 TB/s × 1.5 µs)
+constexpr double kFixLaunchSteps = 1.2;
 constexpr int kCUs = 256;
 constexpr int kMinStepsPerSlice = 8;
 
@@ -824,7 +882,7 @@ struct SplitPlan {
   size_t bytes;
 };
 
-bool splittable(const GemmKind& k) { return k.epi != EPI_STORE_ROWSTATS; }
+bool splittable(const GemmKind& k) { return k.epi != EPI_STORE_ROWSTATS && k.epi != EPI_GELU_GRAD_DB; }
 
 // problems: up to three (null = absent); kinds: theirs
 SplitPlan plan_split(const GemmProblem* const (&pr)[3], const GemmKind* const (&kd)[3]) {
@@ -845,7 +903,7 @@ SplitPlan plan_split(const GemmProblem* const (&pr)[3], const GemmKind* const (&
       const double c = static_cast<double>((static_cast<int64_t>(KS[i]) + s[i] - 1) / s[i]) + kTileFixedSteps;
       longest = c > longest ? c : longest;
       work += T[i] * s[i] * c;
-      if (s[i] > 1) fix += 2.0 * s[i] * MN[i] * 4.0 / kFixBytesPerStep + kFixLaunchSteps;
+      if (s[i] > 1) fix += s[i] * MN[i] * 4.0 / kFixBytesPerStep + kFixLaunchSteps;
     }
     const double spread = work / kCUs;
     return (longest > spread ? longest : spread) + fix;
@@ -1008,6 +1066,8 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
     e = launch_t<KMAJ, MNMAJ, EPI_STORE_F32, KMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
   else if (same && is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))
     e = launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD>(g, stream);
+  else if (same && is(k0, KMAJ, KMAJ, EPI_GELU_GRAD_DB))
+    e = launch_t<KMAJ, KMAJ, EPI_GELU_GRAD_DB, KMAJ, KMAJ, EPI_GELU_GRAD_DB>(g, stream);
   else if (same && is(k0, KMAJ, KMAJ, EPI_STORE))
     e = launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE>(g, stream);
   else if (same && is(k0, KMAJ, KMAJ, EPI_STORE_ROWSTATS))

@@ -21,8 +21,11 @@ enum Epilogue {
   EPI_GELU_GRAD = 3,  // C = acc ⊙ GeLU'(Zin) (D)
   EPI_BIAS_GELU_ZY = 4,  // z = acc + bias[col]: C = z (Z), C2 = GeLU(z) (Y)
   EPI_BIAS_STORE = 5,    // C = acc + bias[col] (dtype of the path)
-  EPI_STORE_ROWSTATS = 6  // C = acc (bf16), and per row and 64-column group of C as stored:
-                          // (max, Σ exp(c − max)) into rstats (the cross-entropy's statistics)
+  EPI_STORE_ROWSTATS = 6,  // C = acc (bf16), and per row and 64-column group of C as stored:
+                           // (max, Σ exp(c − max)) into rstats (the cross-entropy's statistics)
+  EPI_GELU_GRAD_DB = 7     // EPI_GELU_GRAD, and the column sums of C as stored over each
+                           // 128-row chunk into colsum [batch][⌈M/128⌉][N] (the bias gradient's
+                           // first stage)
 };
 
 struct GemmProblem {
@@ -36,6 +39,7 @@ struct GemmProblem {
   const void* bias;  // EPI_BIAS_GELU_ZY / EPI_BIAS_STORE: [N] per batch entry, path dtype
   int64_t sBias;     // its per-batch stride in elements
   float* rstats;     // EPI_STORE_ROWSTATS: [batch][M][⌈N/64⌉] pairs (max, sum) of floats
+  float* colsum;     // EPI_GELU_GRAD_DB: [batch][⌈M/128⌉][N] column sums of 128-row chunks
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;  // per-batch strides in elements (0 = shared operand)
 };
@@ -77,6 +81,9 @@ hipError_t launch_reduce_partials(int in_dt, int out_dt, int t, int64_t count,
 int64_t bias_grad_chunks(int64_t rows);
 hipError_t launch_bias_grad(int dt, int t, int64_t rows, int64_t cols, const void* g, float* db, float* ws,
                             hipStream_t stream);
+// the second stage alone: db[i][c] = Σ_chunk ws[i][chunk][c] in the fixed order
+hipError_t launch_bias_grad_final(int t, int64_t rows, int64_t cols, float* db, const float* ws,
+                                  hipStream_t stream);
 
 struct SpProblem {
   int phase, dt, t;

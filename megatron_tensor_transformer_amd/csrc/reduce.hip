@@ -347,6 +347,19 @@ hipError_t launch_reduce_partials(int in_dt, int out_dt, int t, int64_t count, c
 
 int64_t bias_grad_chunks(int64_t rows) { return rows <= 0 ? 0 : (rows + BG_RC - 1) / BG_RC; }
 
+hipError_t launch_bias_grad_final(int t, int64_t rows, int64_t cols, float* db, const float* ws,
+                                  hipStream_t stream) {
+  if (t <= 0 || cols <= 0) return hipSuccess;
+  if (rows <= 0) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((t * cols + RT - 1) / RT)), dim3(RT), 0, stream,
+                       db, static_cast<int64_t>(t) * cols);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(bias_grad_final_kernel, dim3(static_cast<unsigned>((t * cols + BG_CG - 1) / BG_CG)), dim3(RT), 0,
+                     stream, ws, db, static_cast<int64_t>(t), cols, bias_grad_chunks(rows));
+  return hipGetLastError();
+}
+
 hipError_t launch_bias_grad(int dt, int t, int64_t rows, int64_t cols, const void* g, float* db, float* ws,
                             hipStream_t stream) {
   if (t <= 0 || cols <= 0) return hipSuccess;

@@ -77,9 +77,9 @@ def test_split_k_workspace(L):
     fw, bw = L.tpmlp_fwd_workspace_bytes, L.tpmlp_bwd_workspace_bytes
     assert fw(1, 8192, 3072, 1536, 8) == 0 and bw(1, 8192, 3072, 1536, 8) == 0
     assert fw(0, 2048, 1024, 4096, 1) == 0 and bw(0, 2048, 1024, 4096, 1) == 0
-    # single-shard layer: P = Y·B has 8×4 tiles over K = 4096 (split in 4),
-    # dX likewise (split in 2): S fp32 planes of n×d each
-    assert fw(1, 2048, 1024, 4096, 1) == 4 * 2048 * 1024 * 4
+    # single-shard layer: P = Y·B has 8×4 tiles over K = 4096 (split in 8),
+    # dX in the weight-gradient launch (split in 2): S fp32 planes of n×d each
+    assert fw(1, 2048, 1024, 4096, 1) == 8 * 2048 * 1024 * 4
     assert bw(1, 2048, 1024, 4096, 1) == 2 * 2048 * 1024 * 4
     assert L.tpmlp_fwd_bias_workspace_bytes(1, 2048, 1024, 4096, 1) == fw(1, 2048, 1024, 4096, 1)
     need = fw(1, 2048, 1024, 4096, 1)
@@ -244,6 +244,23 @@ def test_bwd_validation(L):
         assert L.tpmlp_bwd(None, 1, 64, 64, 64, 2, *a, None, 0) == tp.ERR_ALIGN
         a[6] = z  # f32 path: 4-byte alignment suffices, so the next check (D) fails
         assert L.tpmlp_bwd(None, 0, 64, 64, 64, 2, *a, None, 0) == tp.ERR_NULLPTR
+
+
+def test_bwd_bias_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    z = ctypes.c_void_p(0)
+    a = [p] * 10
+    need = L.tpmlp_bwd_bias_workspace_bytes(1, 64, 64, 64, 2)
+    # the chunk sums of D (2 shards × 1 chunk × 64) and of G (1 chunk × 64), 256-byte aligned regions
+    assert need == 512 + 256
+    assert L.tpmlp_bwd_bias(None, 1, 64, 64, 64, 2, *a, z, p, p, need) == tp.ERR_NULLPTR
+    assert L.tpmlp_bwd_bias(None, 1, 64, 64, 64, 2, *a, p, z, p, need) == tp.ERR_NULLPTR
+    assert L.tpmlp_bwd_bias(None, 1, 64, 64, 64, 2, *a, p, p, p, need - 1) == tp.ERR_WORKSPACE
+    assert L.tpmlp_bwd_bias(None, 1, 64, 64, 64, 2, *a, p, p, z, 0) == tp.ERR_WORKSPACE
+    assert L.tpmlp_bwd_bias(None, 1, 64, 64, 64, 2, *a, ctypes.c_void_p(0x1002), p, p, need) == tp.ERR_ALIGN
+    assert L.tpmlp_bwd_bias(None, 3, 64, 64, 64, 2, *a, p, p, p, need) == tp.ERR_DTYPE
+    a[6] = z  # D missing
+    assert L.tpmlp_bwd_bias(None, 1, 64, 64, 64, 2, *a, p, p, p, need) == tp.ERR_NULLPTR
 
 
 def test_reduce_validation(L):

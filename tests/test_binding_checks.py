@@ -58,6 +58,8 @@ CASES = {
     "tpmlp_fwd": (tp.tpmlp_fwd, mlp_fwd_args, {}),
     "tpmlp_fwd_bias": (tp.tpmlp_fwd_bias, lambda: {**mlp_fwd_args(), "b1": e((2, 8))}, {}),
     "tpmlp_bwd": (tp.tpmlp_bwd, mlp_bwd_args, {}),
+    "tpmlp_bwd_bias": (tp.tpmlp_bwd_bias, lambda: {**mlp_bwd_args(), "db1": e((2, 8), f32), "db2": e((24,), f32)},
+                       {}),
     "tpmlp_reduce_partials": (tp.tpmlp_reduce_partials, lambda: dict(partials=e((3, 16, 24)), out=e((16, 24), f32)),
                               {}),
     "tpmlp_reduce_partials_bias": (tp.tpmlp_reduce_partials_bias,

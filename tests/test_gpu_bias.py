@@ -26,24 +26,29 @@ TOL = {"f32": 1e-5, "bf16": 8e-3}
 SUM_TOL = 1e-5
 
 
-def run_biased_step(X, A_s, B_s, b1_s, b2, G):
+def run_biased_step(X, A_s, B_s, b1_s, b2, G, fused=False):
+    """fused: tpmlp_bwd_bias (db1 from the dgrad-1 epilogue, db2 inside the
+    call); else tpmlp_bwd and two tpmlp_bias_grad calls."""
     Z, Y, P = tp.mlp_fwd_bias(X, A_s, B_s, b1_s)
     O = tp.reduce_partials_bias(P, b2)
-    D, dA, dB, dXp = tp.mlp_bwd(X, A_s, B_s, Z, Y, G)
+    if fused:
+        D, dA, dB, dXp, db1, db2 = tp.mlp_bwd_bias(X, A_s, B_s, Z, Y, G)
+    else:
+        D, dA, dB, dXp = tp.mlp_bwd(X, A_s, B_s, Z, Y, G)
+        db1 = tp.bias_grad(D)
+        db2 = tp.bias_grad(G)
     dX = tp.reduce_partials(dXp)
-    db1 = tp.bias_grad(D)
-    db2 = tp.bias_grad(G)
     torch.cuda.synchronize()
     return dict(Z=Z, Y=Y, P=P, O=O, D=D, dA=dA, dB=dB, dXp=dXp, dX=dX, db1=db1, db2=db2)
 
 
-def compare_biased(inp, bias, t, dtype):
+def compare_biased(inp, bias, t, dtype, fused=False):
     X, A, B, G = (dev(inp[k]) for k in "XABG")
     b1, b2 = dev(bias["b1"]), dev(bias["b2"])
     n, d = X.shape
     m = A.shape[1]
-    say(f"[gpu] biased step {dtype} n={n} d={d} m={m} t={t}")
-    r = run_biased_step(X, shard_cols(A, t), shard_rows(B, t), b1.reshape(t, m // t).contiguous(), b2, G)
+    say(f"[gpu] biased step {dtype} n={n} d={d} m={m} t={t} fused={fused}")
+    r = run_biased_step(X, shard_cols(A, t), shard_rows(B, t), b1.reshape(t, m // t).contiguous(), b2, G, fused)
     Xo, Ao, Bo, Go = (inp[k].f64 for k in "XABG")
     b1o, b2o = bias["b1"].f64, bias["b2"].f64
     fwd = om.tp_forward(Xo, Ao, Bo, t, b1=b1o, b2=b2o)
@@ -66,10 +71,42 @@ def compare_biased(inp, bias, t, dtype):
     return errs
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("n,d,m,t", [(1, 4, 8, 2), (17, 36, 40, 2), (130, 72, 400, 2), (65, 100, 300, 3)])
-def test_fp32_biased_ragged(n, d, m, t):
+def test_fp32_biased_ragged(n, d, m, t, fused):
     inp = mlp_inputs(n, d, m, t, dtype="f32", seed=21, x_std=1.0, w_std=0.2, g_std=1.0)
-    compare_biased(inp, bias_inputs(m, d, "f32", seed=21), t, "f32")
+    compare_biased(inp, bias_inputs(m, d, "f32", seed=21), t, "f32", fused)
+
+
+@pytest.mark.parametrize("n,d,m,t", [
+    (1, 8, 16, 2),          # one token: one partial 128-row chunk
+    (129, 264, 272, 2),     # a second chunk of one row; ragged N and K tails
+    (1000, 264, 272, 2),    # ragged M inside a 256-row tile (chunk 7 of 8 is partial)
+    (520, 520, 1584, 3),
+    (300, 4096, 512, 2),    # a shape whose unbiased backward splits dgrad-1 (the fused one does not)
+])
+def test_bf16_fused_bias_grad(n, d, m, t):
+    """tpmlp_bwd_bias against the oracle, and its D, dA, dB, dX_i against
+    tpmlp_bwd's (the same products; bit for bit where tpmlp_bwd does not split
+    dgrad-1), and its db1 against the column sums of its own stored D."""
+    inp = mlp_inputs(n, d, m, t, dtype="bf16", seed=22)
+    bias = bias_inputs(m, d, "bf16", seed=22)
+    compare_biased(inp, bias, t, "bf16", fused=True)
+    X, A, B, G = (dev(inp[k]) for k in "XABG")
+    A_s, B_s = shard_cols(A, t), shard_rows(B, t)
+    b1 = dev(bias["b1"]).reshape(t, m // t).contiguous()
+    Z, Y, P = tp.mlp_fwd_bias(X, A_s, B_s, b1)
+    f = tp.mlp_bwd_bias(X, A_s, B_s, Z, Y, G)
+    u = tp.mlp_bwd(X, A_s, B_s, Z, Y, G)
+    f2 = tp.mlp_bwd_bias(X, A_s, B_s, Z, Y, G)
+    torch.cuda.synchronize()
+    for a, b in zip(f, f2):  # repeatable bit for bit
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    if tp.bwd_workspace_bytes(X, A_s) == 0:
+        for a, b in zip(f[:4], u):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
 
 
 @pytest.mark.parametrize("n,d,m,t", [
