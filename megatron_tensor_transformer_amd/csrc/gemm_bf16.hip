@@ -864,15 +864,16 @@ int64_t tiles_of(const GemmProblem& p) {
 // epilogue.  The choice minimises a cost model in units of one K step (64) of
 // a tile on a loaded machine: the launch takes about max(longest tile,
 // total tile work / 256 CUs), each tile also pays a fixed prologue/epilogue,
-// and a split pays its fix-up kernel, which reads the S fp32 partial planes
-// (the GEMM writes them in its epilogue, in place of the output).  The
+// and a split pays the S fp32 partial planes twice (the GEMM's epilogue
+// writes them, the fix-up kernel reads them) and the fix-up's launch.  The
 // choice depends only on the shapes, so a call is bit-reproducible.
 // Measured on the single-shard layer (n = 2048, d = 1024, m = 4096): a
 // 16-step tile takes 31 µs alone on the GPU, about 1.5 µs per step plus
-// ≈ 6 µs; the fix-up reads its planes at ≈ 5.4 TB/s.
+// ≈ 6 µs; P = Y·B split in 4 takes 32 + 7 µs (fix-up), split in 8 36 + 13 µs
+// (256 tiles writing 64 MB of fp32 partials at once), unsplit ≈ 100 µs.
 constexpr double kTileFixedSteps = 4.0;     // a tile's prologue + epilogue
-constexpr double kFixBytesPerStep = 8.0e6;  // fix-up reads per step time (≈ 5.4 TB/s × 1.5 µs)
-constexpr double kFixLaunchSteps = 1.2;
+constexpr double kFixBytesPerStep = 6.4e6;  // partial-plane traffic per step time (≈ 4 TB/s × 1.6 µs)
+constexpr double kFixLaunchSteps = 2.0;
 constexpr int kCUs = 256;
 constexpr int kMinStepsPerSlice = 8;
 
@@ -903,7 +904,7 @@ SplitPlan plan_split(const GemmProblem* const (&pr)[3], const GemmKind* const (&
       const double c = static_cast<double>((static_cast<int64_t>(KS[i]) + s[i] - 1) / s[i]) + kTileFixedSteps;
       longest = c > longest ? c : longest;
       work += T[i] * s[i] * c;
-      if (s[i] > 1) fix += s[i] * MN[i] * 4.0 / kFixBytesPerStep + kFixLaunchSteps;
+      if (s[i] > 1) fix += 2.0 * s[i] * MN[i] * 4.0 / kFixBytesPerStep + kFixLaunchSteps;
     }
     const double spread = work / kCUs;
     return (longest > spread ? longest : spread) + fix;

@@ -77,9 +77,9 @@ def test_split_k_workspace(L):
     fw, bw = L.tpmlp_fwd_workspace_bytes, L.tpmlp_bwd_workspace_bytes
     assert fw(1, 8192, 3072, 1536, 8) == 0 and bw(1, 8192, 3072, 1536, 8) == 0
     assert fw(0, 2048, 1024, 4096, 1) == 0 and bw(0, 2048, 1024, 4096, 1) == 0
-    # single-shard layer: P = Y·B has 8×4 tiles over K = 4096 (split in 8),
+    # single-shard layer: P = Y·B has 8×4 tiles over K = 4096 (split in 4),
     # dX in the weight-gradient launch (split in 2): S fp32 planes of n×d each
-    assert fw(1, 2048, 1024, 4096, 1) == 8 * 2048 * 1024 * 4
+    assert fw(1, 2048, 1024, 4096, 1) == 4 * 2048 * 1024 * 4
     assert bw(1, 2048, 1024, 4096, 1) == 2 * 2048 * 1024 * 4
     assert L.tpmlp_fwd_bias_workspace_bytes(1, 2048, 1024, 4096, 1) == fw(1, 2048, 1024, 4096, 1)
     need = fw(1, 2048, 1024, 4096, 1)
