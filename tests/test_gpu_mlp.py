@@ -40,6 +40,7 @@ def compare_full(inp, t, dtype, extra=""):
         errs[f"D{i}"] = relerr(r["D"][i], bwd["D"][i])
         errs[f"dXp{i}"] = relerr(r["dXp"][i], bwd["dXp"][i])
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    say(f"[gpu] step {dtype} {extra}: worst {max(errs.values()):.3e} ({max(errs, key=errs.get)})")
     assert not bad, f"over {tol}: {bad}"
     return errs
 
