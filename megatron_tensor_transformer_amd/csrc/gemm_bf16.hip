@@ -313,6 +313,9 @@ __device__ __forceinline__ i32x2 pack4_bf16(float a, float b, float c, float d) 
 // row): chunk c (8 columns) of row r sits at slot c ^ (r & 7).
 constexpr int QROW = 128, QBYTES = 128 * QROW;
 static_assert(NWAVE * (QBYTES + 128) <= LDS_BYTES, "epilogue staging and bias exceed the LDS");
+// fp32 staging (half a wave's region at a time): 64 rows × 64 floats
+constexpr int FQROW = 256, FQBYTES = 64 * FQROW;
+static_assert(NWAVE * FQBYTES <= LDS_BYTES, "fp32 epilogue staging exceeds the LDS");
 // 16-B chunk slot of a staging row.  A row is 128 B, half of the LDS's 256-B
 // bank width, so rows of one parity share a bank half; XOR-ing with row/2
 // gives the 16 rows of a parity that one accumulator write covers 8 distinct
@@ -416,24 +419,58 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
   // columns wn·64 + 32j + 8·(v/4) + 4·(L/32) + v%4.
   const int row_l = lane & 31, half = lane >> 5;
   if constexpr (EPI == EPI_STORE_F32) {
+    // fp32 results go through LDS as well: each wave stages half of its
+    // 128×64 region at a time (64 rows × 256 B = 16 KiB; 8 waves use 128 KiB
+    // of the main loop's stages), so that every store instruction writes 4
+    // whole rows of 256 B, two full 128-B lines each, instead of 32 rows of
+    // 32 B that fill their lines only in groups of four.  Chunk c (4 floats)
+    // of staging row r sits at slot c ^ (r & 15): the 16 lanes that one LDS
+    // cycle serves then hit 16 distinct slots, writing (16 rows, one chunk)
+    // and reading (one row, 16 chunks) alike.
+    block_barrier();  // every wave is done with the main-loop stages
     float* C = static_cast<float*>(a.C) + static_cast<int64_t>(batch) * a.sC;
+    const uint32_t fbase = lds_base + wave * FQBYTES;
+    const int qm0 = m0 + wm * 128, qn0 = n0 + wn * 64;
 #pragma unroll
-    for (int i = 0; i < FA; ++i) {
-      const int row = m0 + wm * 128 + i * 32 + row_l;
-      if (row >= a.M) continue;
+    for (int hp = 0; hp < 2; ++hp) {
 #pragma unroll
-      for (int j = 0; j < FB; ++j) {
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * hp + ii;
+        const int r = ii * 32 + row_l;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 64 + j * 32 + q * 8 + half * 4;
-          if (col < a.N) {
-            f32x4 v;
-            v[0] = acc[i][j][4 * q + 0];
-            v[1] = acc[i][j][4 * q + 1];
-            v[2] = acc[i][j][4 * q + 2];
-            v[3] = acc[i][j][4 * q + 3];
-            *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row) * a.ldc + col) = v;
+        for (int j = 0; j < FB; ++j) {
+          float v[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[i][j][e]));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = j * 8 + q * 2 + half;
+            f32x4 w;
+            w[0] = v[4 * q];
+            w[1] = v[4 * q + 1];
+            w[2] = v[4 * q + 2];
+            w[3] = v[4 * q + 3];
+            asm volatile("ds_write_b128 %0, %1" ::"v"(fbase + r * FQROW + ((c ^ (r & 15)) << 4)), "v"(w)
+                         : "memory");
           }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it0 = 0; it0 < 16; it0 += 8) {
+        f32x4 w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = (it0 + u) * 4 + (lane >> 4), c = lane & 15;
+          asm volatile("ds_read_b128 %0, %1" : "=v"(w[u]) : "v"(fbase + r * FQROW + ((c ^ (r & 15)) << 4)) : "memory");
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]),
+                       "+v"(w[7])::"memory");
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int gr = qm0 + 64 * hp + (it0 + u) * 4 + (lane >> 4), gc = qn0 + (lane & 15) * 4;
+          if (gr < a.M && gc < a.N) *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc) = w[u];
         }
       }
     }
