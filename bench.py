@@ -37,10 +37,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU × 2.4 GHz × 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix cores; the vector units' figure is the same)
 GEMM_LAUNCHES = 4           # GEMM core launches per step
 METRIC = "TP-MLP shard fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
 WORKLOAD = "gpt8p3b_t8"
-LEGS = ("biased_step", "per_rank", "c2", "gpt1t_shard", "sp_region", "c5_block", "attention", "vocab_ce")
+LEGS = ("biased_step", "per_rank", "c2", "gpt1t_shard", "sp_region", "c5_block", "attention", "vocab_ce",
+        "fp32_path")
 
 
 def parse():
@@ -328,6 +330,48 @@ def leg_mlp_shard(tp, n, d, mi, reps, seed, inner=1):
     return {"n": n, "d": d, "m_i": mi, "t_local": 1, "flop": flops, "steps_per_timing": inner,
             "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2), **_stats(ms)}
+
+
+def leg_fp32(tp, reps):
+    """The fp32 path (the single-card numeric-alignment path) on the 8.3B-shaped
+    layer: the same step as the headline (8 shards' forward, the partial sum,
+    their backward, the partial sum) with fp32 tensors throughout; its GEMMs
+    run v_mfma_f32_32x32x2_f32.  TFLOP/s against the fp32 dense peak."""
+    import numpy as np
+    import torch
+    from tpmlp_inputs import CONFIGS
+    cfg = CONFIGS["gpt8p3b_t8"]
+    n, d, m, t = cfg["n"], cfg["d"], cfg["m"], cfg["t"]
+    mi = m // t
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    f32 = torch.float32
+
+    def rnd(shape, std):
+        return torch.randn(shape, generator=gen, device=dev, dtype=f32) * std
+
+    X, G = rnd((n, d), 1.0), rnd((n, d), 0.01)
+    A, B = rnd((t, d, mi), 0.02), rnd((t, mi, d), 0.02)
+    Z, Y, D = (torch.empty((t, n, mi), dtype=f32, device=dev) for _ in range(3))
+    P, dXp = (torch.empty((t, n, d), dtype=f32, device=dev) for _ in range(2))
+    dA, dB = torch.empty((t, d, mi), dtype=f32, device=dev), torch.empty((t, mi, d), dtype=f32, device=dev)
+    O, dX = torch.empty((n, d), dtype=f32, device=dev), torch.empty((n, d), dtype=f32, device=dev)
+
+    def run():
+        tp.tpmlp_fwd(X, A, B, Z, Y, P)
+        tp.tpmlp_reduce_partials(P, O)
+        tp.tpmlp_bwd(X, A, B, Z, Y, G, D, dA, dB, dXp)
+        tp.tpmlp_reduce_partials(dXp, dX)
+
+    run()
+    torch.cuda.synchronize()
+    ms = _time_events(run, reps)
+    med = float(np.median(ms))
+    flops = 12.0 * n * d * mi * t
+    return {"workload": f"fp32 path of the 8.3B-shaped layer: n={n}, d={d}, m_i={mi}, t={t}, fp32 tensors",
+            "flop": flops, "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
+            "pct_of_fp32_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2), **_stats(ms)}
 
 
 def leg_sp(tp, reps):
@@ -889,7 +933,8 @@ def main():
         rec["gpt1t_shard"] = {"workload": "GPT-1T-shaped shard: h=25600, m_i=12800, n=2048 tokens, one shard",
                               **leg_mlp_shard(tp, 2048, 25600, 12800, 10, seed=2)}
     for name, fn in (("sp_region", lambda: leg_sp(tp, 10)), ("c5_block", lambda: leg_c5_block(tp, 10)),
-                     ("attention", lambda: leg_attention(tp, 10)), ("vocab_ce", lambda: leg_vocab(tp, 10))):
+                     ("attention", lambda: leg_attention(tp, 10)), ("vocab_ce", lambda: leg_vocab(tp, 10)),
+                     ("fp32_path", lambda: leg_fp32(tp, 5))):
         if name in legs:
             torch.cuda.empty_cache()
             rec[name] = fn()

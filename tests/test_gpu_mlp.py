@@ -57,7 +57,10 @@ def test_worked_example_fp32():
     assert max(errs.values()) <= 1e-5
 
 
-@pytest.mark.parametrize("n,d,m,t", [(1, 4, 8, 2), (17, 36, 40, 2), (130, 72, 400, 2), (65, 100, 300, 3)])
+# the fp32 GEMM works in 128×128 tiles, K steps of 16: the last two cases
+# span several tiles in every dimension with ragged tails (wgrad K = n)
+@pytest.mark.parametrize("n,d,m,t", [(1, 4, 8, 2), (17, 36, 40, 2), (130, 72, 400, 2), (65, 100, 300, 3),
+                                     (257, 300, 1042, 2), (600, 129, 774, 3)])
 def test_fp32_ragged(n, d, m, t):
     inp = mlp_inputs(n, d, m, t, dtype="f32", seed=11, x_std=1.0, w_std=0.2, g_std=1.0)
     compare_full(inp, t, "f32")
