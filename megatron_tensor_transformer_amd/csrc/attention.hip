@@ -33,8 +33,9 @@
 // forward and dq, by key column for dk/dv); a lane reads one word per 32
 // positions a tile ahead, and a wave skips tiles it cannot see at all.
 //
-// fp32 path (correctness reference, not tuned): one thread per query row
-// (forward, dq) or key row (dk, dv), online softmax in fp32.
+// fp32 path (the numeric-alignment path, not tuned): two lanes per query row
+// (forward, dq) or key row (dk, dv), each holding half of the row's columns;
+// online softmax in fp32.
 #include <type_traits>
 
 #include "common.h"
@@ -580,12 +581,21 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ fp32 path
-// One thread per query row of one (shard, batch entry, head).
+// Two lanes per query row of one (shard, batch entry, head): lane half j of a
+// pair holds columns j·dh/2 .. of the row (q, the o accumulator), and the dot
+// products are the two halves' partial sums added across the pair.
+template <int DH>
+__device__ __forceinline__ float pair_dot_sum(float x) {
+  return x + __shfl_xor(x, 1);
+}
+
 template <int DH, bool CAUSAL>
 __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x;
+  constexpr int H = DH / 2;
+  const int64_t idx = (static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x) >> 1;
+  const int j = threadIdx.x & 1;
   const int64_t total = static_cast<int64_t>(a.T) * a.b * a.nh * a.s;
-  if (idx >= total) return;
+  if (idx >= total) return;  // both lanes of a pair leave together
   const int q = static_cast<int>(idx % a.s);
   int64_t r = idx / a.s;
   const int h = static_cast<int>(r % a.nh);
@@ -594,10 +604,10 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   const int T = static_cast<int>(r / a.b);
   const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH;
   const float* qkv = static_cast<const float*>(a.qkv) + static_cast<int64_t>(T) * a.s * a.b * row_len;
-  const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH;
-  float qv[DH], acc[DH];
+  const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH + j * H;
+  float qv[H], acc[H];
 #pragma unroll
-  for (int d = 0; d < DH; ++d) {
+  for (int d = 0; d < H; ++d) {
     qv[d] = qp[d];
     acc[d] = 0.f;
   }
@@ -605,25 +615,26 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   const int kend = CAUSAL ? q + 1 : a.s;
   const uint32_t* mrow = a.mask ? a.mask + (static_cast<int64_t>(bi) * a.s + q) * a.mw : nullptr;
   for (int kv = 0; kv < kend; ++kv) {
-    if (mrow && ((mrow[kv >> 5] >> (kv & 31)) & 1u)) continue;
-    const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
+    if (mrow && ((mrow[kv >> 5] >> (kv & 31)) & 1u)) continue;  // the same for both lanes
+    const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH + j * H;
     float sdot = 0.f;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) sdot = fmaf(qv[d], kp[d], sdot);
-    const float sv = sdot * a.scale;
+    for (int d = 0; d < H; ++d) sdot = fmaf(qv[d], kp[d], sdot);
+    const float sv = pair_dot_sum<DH>(sdot) * a.scale;
     const float mn = fmaxf(m, sv);
     const float alpha = expf(m - mn), p = expf(sv - mn);
     l = l * alpha + p;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, kp[DH + d], acc[d] * alpha);
+    for (int d = 0; d < H; ++d) acc[d] = fmaf(p, kp[DH + d], acc[d] * alpha);
     m = mn;
   }
   float* op = static_cast<float*>(a.o) + static_cast<int64_t>(T) * a.s * a.b * a.nh * DH +
-              (static_cast<int64_t>(q) * a.b + bi) * a.nh * DH + h * DH;
+              (static_cast<int64_t>(q) * a.b + bi) * a.nh * DH + h * DH + j * H;
   // a row that sees no key: o = 0, lse = −∞
 #pragma unroll
-  for (int d = 0; d < DH; ++d) op[d] = l > 0.f ? acc[d] / l : 0.f;
-  a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + q] = l > 0.f ? m + logf(l) : -INFINITY;
+  for (int d = 0; d < H; ++d) op[d] = l > 0.f ? acc[d] / l : 0.f;
+  if (j == 0)
+    a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + q] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ backward
@@ -1129,11 +1140,14 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   }
 }
 
-// fp32 backward (correctness path): dq per query row, dk and dv per key row.
+// fp32 backward: dq per query row, dk and dv per key row, two lanes per row
+// as in the forward (lane half j holds columns j·dh/2 ..).
 template <int DH, bool CAUSAL>
 __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(AttnBwdArgs a) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(a.T) * a.b * a.nh * a.s) return;
+  constexpr int H = DH / 2;
+  const int64_t idx = (static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x) >> 1;
+  const int j = threadIdx.x & 1;
+  if (idx >= static_cast<int64_t>(a.T) * a.b * a.nh * a.s) return;  // both lanes of a pair
   const int q = static_cast<int>(idx % a.s);
   int64_t r = idx / a.s;
   const int h = static_cast<int>(r % a.nh);
@@ -1142,14 +1156,14 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(AttnBwdArgs a) {
   const int64_t n = static_cast<int64_t>(a.s) * a.b;
   const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
   const float* qkv = static_cast<const float*>(a.qkv) + T * n * row_len;
-  const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH;
+  const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH + j * H;
   const float* dp = static_cast<const float*>(a.dout) + T * n * orow + (static_cast<int64_t>(q) * a.b + bi) * orow +
-                    h * DH;
+                    h * DH + j * H;
   const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
   const float lse = a.lse[srow + q], dlt = a.delta[srow + q];
-  float qv[DH], dov[DH], acc[DH];
+  float qv[H], dov[H], acc[H];
 #pragma unroll
-  for (int d = 0; d < DH; ++d) {
+  for (int d = 0; d < H; ++d) {
     qv[d] = qp[d];
     dov[d] = dp[d];
     acc[d] = 0.f;
@@ -1158,28 +1172,30 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(AttnBwdArgs a) {
   const uint32_t* mrow = a.mask ? a.mask + (static_cast<int64_t>(bi) * a.s + q) * a.mw : nullptr;
   for (int kv = 0; kv < kend; ++kv) {
     if (mrow && ((mrow[kv >> 5] >> (kv & 31)) & 1u)) continue;  // hidden (all of them when lse = −∞)
-    const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
+    const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH + j * H;
     float sdot = 0.f, pdot = 0.f;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) {
+    for (int d = 0; d < H; ++d) {
       sdot = fmaf(qv[d], kp[d], sdot);
       pdot = fmaf(dov[d], kp[DH + d], pdot);
     }
-    const float p = expf(sdot * a.scale - lse);
-    const float ds = p * (pdot - dlt);
+    const float p = expf(pair_dot_sum<DH>(sdot) * a.scale - lse);
+    const float ds = p * (pair_dot_sum<DH>(pdot) - dlt);
 #pragma unroll
-    for (int d = 0; d < DH; ++d) acc[d] = fmaf(ds, kp[d], acc[d]);
+    for (int d = 0; d < H; ++d) acc[d] = fmaf(ds, kp[d], acc[d]);
   }
   float* op = static_cast<float*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(q) * a.b + bi) * row_len +
-              h * 3 * DH;
+              h * 3 * DH + j * H;
 #pragma unroll
-  for (int d = 0; d < DH; ++d) op[d] = acc[d] * a.scale;
+  for (int d = 0; d < H; ++d) op[d] = acc[d] * a.scale;
 }
 
 template <int DH, bool CAUSAL>
 __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(AttnBwdArgs a) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(a.T) * a.b * a.nh * a.s) return;
+  constexpr int H = DH / 2;
+  const int64_t idx = (static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x) >> 1;
+  const int j = threadIdx.x & 1;
+  if (idx >= static_cast<int64_t>(a.T) * a.b * a.nh * a.s) return;  // both lanes of a pair
   const int kv = static_cast<int>(idx % a.s);
   int64_t r = idx / a.s;
   const int h = static_cast<int>(r % a.nh);
@@ -1189,33 +1205,38 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(AttnBwdArgs a) {
   const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
   const float* qkv = static_cast<const float*>(a.qkv) + T * n * row_len;
   const float* dout = static_cast<const float*>(a.dout) + T * n * orow;
-  const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH;
+  const float* kp = qkv + (static_cast<int64_t>(kv) * a.b + bi) * row_len + h * 3 * DH + DH + j * H;
   const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
-  float dk[DH], dv[DH];
+  float kr[H], vr[H], dk[H], dv[H];
 #pragma unroll
-  for (int d = 0; d < DH; ++d) dk[d] = dv[d] = 0.f;
+  for (int d = 0; d < H; ++d) {
+    kr[d] = kp[d];
+    vr[d] = kp[DH + d];
+    dk[d] = dv[d] = 0.f;
+  }
   const uint32_t* mcol = a.mask ? a.mask + ((static_cast<int64_t>(a.b) + bi) * a.s + kv) * a.mw : nullptr;
   for (int q = CAUSAL ? kv : 0; q < a.s; ++q) {
-    if (mcol && ((mcol[q >> 5] >> (q & 31)) & 1u)) continue;
-    const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH;
-    const float* dp = dout + (static_cast<int64_t>(q) * a.b + bi) * orow + h * DH;
+    if (mcol && ((mcol[q >> 5] >> (q & 31)) & 1u)) continue;  // the same for both lanes
+    const float* qp = qkv + (static_cast<int64_t>(q) * a.b + bi) * row_len + h * 3 * DH + j * H;
+    const float* dp = dout + (static_cast<int64_t>(q) * a.b + bi) * orow + h * DH + j * H;
     float sdot = 0.f, pdot = 0.f;
-    for (int d = 0; d < DH; ++d) {
-      sdot = fmaf(qp[d], kp[d], sdot);
-      pdot = fmaf(dp[d], kp[DH + d], pdot);
-    }
-    const float p = expf(sdot * a.scale - a.lse[srow + q]);
-    const float ds = p * (pdot - a.delta[srow + q]);
 #pragma unroll
-    for (int d = 0; d < DH; ++d) {
+    for (int d = 0; d < H; ++d) {
+      sdot = fmaf(qp[d], kr[d], sdot);
+      pdot = fmaf(dp[d], vr[d], pdot);
+    }
+    const float p = expf(pair_dot_sum<DH>(sdot) * a.scale - a.lse[srow + q]);
+    const float ds = p * (pair_dot_sum<DH>(pdot) - a.delta[srow + q]);
+#pragma unroll
+    for (int d = 0; d < H; ++d) {
       dv[d] = fmaf(p, dp[d], dv[d]);
       dk[d] = fmaf(ds, qp[d], dk[d]);
     }
   }
   float* op = static_cast<float*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(kv) * a.b + bi) * row_len +
-              h * 3 * DH + DH;
+              h * 3 * DH + DH + j * H;
 #pragma unroll
-  for (int d = 0; d < DH; ++d) {
+  for (int d = 0; d < H; ++d) {
     op[d] = dk[d] * a.scale;
     op[DH + d] = dv[d];
   }
@@ -1244,7 +1265,7 @@ hipError_t launch_bwd_t(const AttnBwdArgs& a, int dt, hipStream_t stream) {
     hipLaunchKernelGGL((attn_delta_kernel<float, DH>), dim3(dblocks), dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned blocks = static_cast<unsigned>((rows + 127) / 128);
+    const unsigned blocks = static_cast<unsigned>((2 * rows + 127) / 128);  // two lanes per row
     hipLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<DH, CAUSAL>), dim3(blocks), dim3(128), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1265,7 +1286,7 @@ hipError_t launch_fwd_t(const AttnArgs& a, int dt, hipStream_t stream) {
                          stream, a);
   } else {
     const int64_t total = static_cast<int64_t>(a.T) * a.b * a.nh * a.s;
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<DH, CAUSAL>), dim3(static_cast<unsigned>((total + 127) / 128)),
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<DH, CAUSAL>), dim3(static_cast<unsigned>((2 * total + 127) / 128)),
                        dim3(128), 0, stream, a);
   }
   return hipGetLastError();
