@@ -3,9 +3,11 @@
  * (gfx950).  Every entry point enqueues HIP kernels on the caller's stream and
  * returns; nothing here allocates or keeps a pointer after returning.  The
  * only host state is the per-thread code of the last failed launch
- * (tpmlp_last_hip_error) and, once tpmlp_bias_grad_noalloc has run on a
- * device, that device's address of the library's fixed scratch array (looked
- * up once, under a lock).  The library is thread-safe.
+ * (tpmlp_last_hip_error), the process-wide GEMM tile policy
+ * (tpmlp_set_gemm_tile_policy, an atomic integer) and, once
+ * tpmlp_bias_grad_noalloc has run on a device, that device's address of the
+ * library's fixed scratch array (looked up once, under a lock).  The library
+ * is thread-safe.
  *
  * Sources (page title, section):
  *   [TUT]   "024｜Megatron-LM：按矩阵结构切分 Transformer，减少模型并行通信",
@@ -68,7 +70,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 8
+#define TPMLP_ABI_VERSION 9
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
 
@@ -487,6 +489,25 @@ int tpmlp_vocab_ce_bwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t
                        int64_t vocab_start, const void* X, const void* W, const int32_t* targets,
                        const void* logits, const float* row_max, const float* row_sum, const float* g,
                        void* dlogits, float* dW, void* dXp);
+
+/*
+ * Tile width of the bf16 GEMMs, a tuning and testing knob.  Results do not
+ * depend on it: both widths accumulate each output element's K sum in the
+ * same order, 16-wide K slices in turn.  The default, TPMLP_GEMM_TILE_AUTO, gives a
+ * launch 256×192 output tiles instead of 256×256 where that fills the GPU's
+ * 256 compute units in fewer rounds of tiles (one-kind launches with the
+ * plain, GeLU, GeLU' or bias epilogue that run without a K split; e.g. one
+ * shard of the 8.3B-shaped layer, n = 8192, m_i = 1536: 256 tiles instead
+ * of 192).  TPMLP_GEMM_TILE_256 keeps 256×256 everywhere; TPMLP_GEMM_TILE_192
+ * takes 256×192 wherever it is available.  Process-wide; calls already
+ * enqueued are not affected.  Returns TPMLP_OK, or TPMLP_ERR_ARG for another
+ * value.
+ */
+#define TPMLP_GEMM_TILE_AUTO 0
+#define TPMLP_GEMM_TILE_256 1
+#define TPMLP_GEMM_TILE_192 2
+int tpmlp_set_gemm_tile_policy(int policy);
+int tpmlp_gemm_tile_policy(void);
 
 /* Status text for a return code; never NULL. */
 const char* tpmlp_status_string(int status);

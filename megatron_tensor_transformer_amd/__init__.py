@@ -85,6 +85,8 @@ SIGNATURES = {
     "tpmlp_status_string": (ctypes.c_char_p, [_I]),
     "tpmlp_last_hip_error": (_I, []),
     "tpmlp_abi_version": (_I, []),
+    "tpmlp_set_gemm_tile_policy": (_I, [_I]),
+    "tpmlp_gemm_tile_policy": (_I, []),
 }
 
 
@@ -398,6 +400,19 @@ def tpmlp_attn_core_bwd(qkv, o, lse, d_o, dqkv, ws, s, b, heads, head_dim, causa
 
 def tpmlp_ln_sp(args, stream=None):
     _check(lib().tpmlp_ln_sp(_stream(stream), ctypes.byref(args)))
+
+
+# bf16 GEMM tile width policy (process-wide): automatic, 256x256 only, or
+# 256x192 wherever available; results do not depend on it
+GEMM_TILE_AUTO, GEMM_TILE_256, GEMM_TILE_192 = 0, 1, 2
+
+
+def set_gemm_tile_policy(policy):
+    _check(lib().tpmlp_set_gemm_tile_policy(policy))
+
+
+def gemm_tile_policy():
+    return lib().tpmlp_gemm_tile_policy()
 
 
 # ---------------------------------------------------------------- allocating wrappers

@@ -159,6 +159,19 @@ extern "C" {
 
 int tpmlp_abi_version(void) { return TPMLP_ABI_VERSION; }
 
+static_assert(TPMLP_GEMM_TILE_AUTO == tpmlp::TILE_AUTO && TPMLP_GEMM_TILE_256 == tpmlp::TILE_256 &&
+                  TPMLP_GEMM_TILE_192 == tpmlp::TILE_192,
+              "tile policy values");
+
+int tpmlp_set_gemm_tile_policy(int policy) {
+  if (policy != TPMLP_GEMM_TILE_AUTO && policy != TPMLP_GEMM_TILE_256 && policy != TPMLP_GEMM_TILE_192)
+    return TPMLP_ERR_ARG;
+  tpmlp::set_gemm_tile_policy(policy);
+  return TPMLP_OK;
+}
+
+int tpmlp_gemm_tile_policy(void) { return tpmlp::gemm_tile_policy(); }
+
 int tpmlp_last_hip_error(void) { return g_last_hip_error; }
 
 const char* tpmlp_status_string(int status) {

@@ -33,6 +33,8 @@
 // Epilogue: bf16 outputs are staged through LDS (each wave its own 128×64
 // region) and written with coalesced 16-B stores; fp32 outputs are written
 // straight from the accumulators as 16-B stores.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "tile_map.h"
@@ -98,35 +100,48 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // stage.  base[j] is the byte offset of the lane's 16-B chunk at k0 = 0 (OOB
 // when the row lies past the matrix edge); the k part is added per step.
 // kq / kq_odd are the lane's k offset inside the step, for the K-edge test.
+template <int NL = NLOAD>
 struct LoadPlan {
-  uint32_t base[NLOAD];
+  uint32_t base[NL];
   uint32_t kstep;  // bytes to add per K step (64 k)
   int kq;
   int kq_odd;
+  int kseg;        // NL odd, M/N-major: 16·((NL·wave) % 4), the k-rows of load 0
 };
 
-template <int ORDER>
-__device__ __forceinline__ LoadPlan make_plan(int r0, int R, int64_t ld, int wave, int lane) {
-  LoadPlan p;
+// NL loads per wave and stage: 4 for a 256-row operand stage, 3 for a
+// 192-row one (the B stage of the 256×192 tile).
+template <int ORDER, int NL = NLOAD>
+__device__ __forceinline__ LoadPlan<NL> make_plan(int r0, int R, int64_t ld, int wave, int lane) {
+  LoadPlan<NL> p;
+  p.kseg = 0;
   if constexpr (ORDER == KMAJ) {
-    // load j: rows (NLOAD·wave + j)·8 .. +7; lane: row + lane/8, slot lane%8
+    // load j: rows (NL·wave + j)·8 .. +7; lane: row + lane/8, slot lane%8
 #pragma unroll
-    for (int j = 0; j < NLOAD; ++j) {
-      const int row = (wave * NLOAD + j) * 8 + (lane >> 3);
+    for (int j = 0; j < NL; ++j) {
+      const int row = (wave * NL + j) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((row >> 1) & 7);
       const int gr = r0 + row;
       p.base[j] = gr < R ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + c * 8) * 2) : OOB;
     }
     p.kstep = BK * 2;
-    // (row >> 1) & 7 = (4·(NLOAD·wave + j) + lane/16) & 7 only depends on
-    // the parity of j (NLOAD is even)
+    // (row >> 1) & 7 = (4·(NL·wave + j) + lane/16) & 7 only depends on the
+    // parity of NL·wave + j: of j when NL is even; for odd NL the two values
+    // trade places on odd waves, so that the parity of j still picks
     p.kq = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
     p.kq_odd = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
+    if constexpr (NL & 1) {
+      if (wave & 1) {
+        const int t = p.kq;
+        p.kq = p.kq_odd;
+        p.kq_odd = t;
+      }
+    }
   } else {
-    // load j: column block seg/4, k-rows 16·(seg%4) + lane/4, seg = NLOAD·wave + j
+    // load j: column block seg/4, k-rows 16·(seg%4) + lane/4, seg = NL·wave + j
 #pragma unroll
-    for (int j = 0; j < NLOAD; ++j) {
-      const int seg = wave * NLOAD + j;
+    for (int j = 0; j < NL; ++j) {
+      const int seg = wave * NL + j;
       const int blk = seg >> 2;
       const int kr = (seg & 3) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ (((kr >> 1) & 1) << 1);
@@ -136,31 +151,34 @@ __device__ __forceinline__ LoadPlan make_plan(int r0, int R, int64_t ld, int wav
     p.kstep = static_cast<uint32_t>(BK * ld * 2);
     p.kq = lane >> 2;
     p.kq_odd = 0;
+    if constexpr (NL & 3) p.kseg = ((NL * wave) & 3) * 16;
   }
   return p;
 }
 
 // DMA load J of one operand for the K step at byte offset koff (krem = K minus
 // the step's first k) into stage `tile`.
-template <int ORDER, int J>
-__device__ __forceinline__ void dma(i32x4 rsrc, TPMLP_LDS char* tile, const LoadPlan& p, uint32_t koff,
+template <int ORDER, int J, int NL = NLOAD>
+__device__ __forceinline__ void dma(i32x4 rsrc, TPMLP_LDS char* tile, const LoadPlan<NL>& p, uint32_t koff,
                                     int krem, int wave) {
   bool ok;
   if constexpr (ORDER == KMAJ)
     ok = ((J & 1) ? p.kq_odd : p.kq) < krem;
-  else
+  else if constexpr ((NL & 3) == 0)
     ok = (J & 3) * 16 + p.kq < krem;
+  else
+    ok = ((p.kseg + J * 16) & 63) + p.kq < krem;
   const uint32_t voff = ok ? p.base[J] + koff : OOB;
-  // both layouts: load (NLOAD·wave + J) fills the tile's 1-KiB segment of that index
-  buffer_load_lds16(rsrc, tile + (wave * NLOAD + J) * 1024, voff);
+  // both layouts: load (NL·wave + J) fills the tile's 1-KiB segment of that index
+  buffer_load_lds16(rsrc, tile + (wave * NL + J) * 1024, voff);
 }
 
-template <int ORDER, int J = 0>
-__device__ __forceinline__ void dma_all(i32x4 rsrc, TPMLP_LDS char* tile, const LoadPlan& p, uint32_t koff,
+template <int ORDER, int NL = NLOAD, int J = 0>
+__device__ __forceinline__ void dma_all(i32x4 rsrc, TPMLP_LDS char* tile, const LoadPlan<NL>& p, uint32_t koff,
                                         int krem, int wave) {
-  if constexpr (J < NLOAD) {
-    dma<ORDER, J>(rsrc, tile, p, koff, krem, wave);
-    dma_all<ORDER, J + 1>(rsrc, tile, p, koff, krem, wave);
+  if constexpr (J < NL) {
+    dma<ORDER, J, NL>(rsrc, tile, p, koff, krem, wave);
+    dma_all<ORDER, NL, J + 1>(rsrc, tile, p, koff, krem, wave);
   }
 }
 
@@ -224,31 +242,36 @@ __device__ __forceinline__ void read_op(i32x4 (&fr)[NF], const uint32_t (&f)[4],
 __device__ __forceinline__ void wait_frags(i32x4 (&a)[FA], i32x4 (&b)[FB]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
 }
+// the same for the 256×192 tile's fragments (2 of A, 3 of B)
+__device__ __forceinline__ void wait_frags(i32x4 (&a)[2], i32x4 (&b)[3]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]));
+}
 
 #define TPMLP_MFMA(ACC, BF, AF) \
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(ACC) : "v"(BF), "v"(AF))
 
+template <int FA_ = FA, int FB_ = FB>
 constexpr int n_reads(int ao, int bo) {
-  return (ao == KMAJ ? FA : 2 * FA) + (bo == KMAJ ? FB : 2 * FB);
+  return (ao == KMAJ ? FA_ : 2 * FA_) + (bo == KMAJ ? FB_ : 2 * FB_);
 }
 
 // One read op for the next slice, from the merged A-then-B op list.
-template <int AO, int BO, int KS, int T>
-__device__ __forceinline__ void next_read(i32x4 (&fa)[FA], i32x4 (&fb)[FB], const uint32_t (&pa)[4],
+template <int AO, int BO, int KS, int T, int FA_ = FA, int FB_ = FB>
+__device__ __forceinline__ void next_read(i32x4 (&fa)[FA_], i32x4 (&fb)[FB_], const uint32_t (&pa)[4],
                                           const uint32_t (&pb)[4], uint32_t sa, uint32_t sb) {
-  constexpr int NA = reads_per_slice<AO, FA>();
+  constexpr int NA = reads_per_slice<AO, FA_>();
   if constexpr (T < NA)
     read_op<AO, KS, T>(fa, pa, sa);
   else
     read_op<BO, KS, T - NA>(fb, pb, sb);
 }
 
-template <int AO, int BO, int KS, int T = 0>
-__device__ __forceinline__ void read_slice(i32x4 (&fa)[FA], i32x4 (&fb)[FB], const uint32_t (&pa)[4],
+template <int AO, int BO, int KS, int FA_ = FA, int FB_ = FB, int T = 0>
+__device__ __forceinline__ void read_slice(i32x4 (&fa)[FA_], i32x4 (&fb)[FB_], const uint32_t (&pa)[4],
                                            const uint32_t (&pb)[4], uint32_t sa, uint32_t sb) {
-  if constexpr (T < n_reads(AO, BO)) {
-    next_read<AO, BO, KS, T>(fa, fb, pa, pb, sa, sb);
-    read_slice<AO, BO, KS, T + 1>(fa, fb, pa, pb, sa, sb);
+  if constexpr (T < n_reads<FA_, FB_>(AO, BO)) {
+    next_read<AO, BO, KS, T, FA_, FB_>(fa, fb, pa, pb, sa, sb);
+    read_slice<AO, BO, KS, FA_, FB_, T + 1>(fa, fb, pa, pb, sa, sb);
   }
 }
 
@@ -262,25 +285,31 @@ struct StepCtx {
   int kremA, kremB, wave;
 };
 
-// The 8 MFMAs of slice S.  After MFMA Q come the next slice's reads Q and
-// Q + 8 (for S = 3, slice 0 of the next step, from its stages) and, at odd Q,
-// one DMA load: in slice 1 of A two steps ahead, in slice 3 of B two steps
-// ahead.
-template <int AO, int BO, int S, int Q = 0>
-__device__ __forceinline__ void slice_body(f32x16 (&acc)[FA][FB], i32x4 (&ca)[FA], i32x4 (&cb)[FB],
-                                           i32x4 (&na)[FA], i32x4 (&nb)[FB], const uint32_t (&pa)[4],
-                                           const uint32_t (&pb)[4], const LoadPlan& la, const LoadPlan& lb,
-                                           const StepCtx& s) {
-  if constexpr (Q < 8) {
-    TPMLP_MFMA(acc[Q >> 1][Q & 1], cb[Q & 1], ca[Q >> 1]);
-    constexpr int NR = n_reads(AO, BO);
-    if constexpr (S < 3 && Q < NR) next_read<AO, BO, S + 1, Q>(na, nb, pa, pb, s.sa, s.sb);
-    if constexpr (S == 3 && Q < NR) next_read<AO, BO, 0, Q>(na, nb, pa, pb, s.nsa, s.nsb);
-    if constexpr (S < 3 && Q + 8 < NR) next_read<AO, BO, S + 1, Q + 8>(na, nb, pa, pb, s.sa, s.sb);
-    if constexpr (S == 3 && Q + 8 < NR) next_read<AO, BO, 0, Q + 8>(na, nb, pa, pb, s.nsa, s.nsb);
-    if constexpr (S == 1 && (Q & 1)) dma<AO, (Q >> 1)>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
-    if constexpr (S == 3 && (Q & 1)) dma<BO, (Q >> 1)>(s.rB, s.dB, lb, s.koB, s.kremB, s.wave);
-    slice_body<AO, BO, S, Q + 1>(acc, ca, cb, na, nb, pa, pb, la, lb, s);
+// The FA·FB MFMAs of slice S (8 for the 256×256 tile, 6 for 256×192).  After
+// MFMA Q come the next slice's reads Q and Q + FA·FB (for S = 3, slice 0 of
+// the next step, from its stages) and, at odd Q, one DMA load: in slice 1 of
+// A two steps ahead (a fourth A load of the 256×192 tile after MFMA 1 of
+// slice 2), in slice 3 of B two steps ahead.
+template <int AO, int BO, int S, int FA_ = FA, int FB_ = FB, int NLB = NLOAD, int Q = 0>
+__device__ __forceinline__ void slice_body(f32x16 (&acc)[FA_][FB_], i32x4 (&ca)[FA_], i32x4 (&cb)[FB_],
+                                           i32x4 (&na)[FA_], i32x4 (&nb)[FB_], const uint32_t (&pa)[4],
+                                           const uint32_t (&pb)[4], const LoadPlan<NLOAD>& la,
+                                           const LoadPlan<NLB>& lb, const StepCtx& s) {
+  constexpr int NQ = FA_ * FB_;
+  if constexpr (Q < NQ) {
+    TPMLP_MFMA(acc[Q / FB_][Q % FB_], cb[Q % FB_], ca[Q / FB_]);
+    constexpr int NR = n_reads<FA_, FB_>(AO, BO);
+    if constexpr (S < 3 && Q < NR) next_read<AO, BO, S + 1, Q, FA_, FB_>(na, nb, pa, pb, s.sa, s.sb);
+    if constexpr (S == 3 && Q < NR) next_read<AO, BO, 0, Q, FA_, FB_>(na, nb, pa, pb, s.nsa, s.nsb);
+    if constexpr (S < 3 && Q + NQ < NR) next_read<AO, BO, S + 1, Q + NQ, FA_, FB_>(na, nb, pa, pb, s.sa, s.sb);
+    if constexpr (S == 3 && Q + NQ < NR) next_read<AO, BO, 0, Q + NQ, FA_, FB_>(na, nb, pa, pb, s.nsa, s.nsb);
+    if constexpr (S == 1 && (Q & 1) && (Q >> 1) < NLOAD)
+      dma<AO, (Q >> 1)>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
+    if constexpr (S == 2 && NQ / 2 < NLOAD && Q == 1)
+      dma<AO, NQ / 2>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
+    if constexpr (S == 3 && (Q & 1) && (Q >> 1) < NLB)
+      dma<BO, (Q >> 1), NLB>(s.rB, s.dB, lb, s.koB, s.kremB, s.wave);
+    slice_body<AO, BO, S, FA_, FB_, NLB, Q + 1>(acc, ca, cb, na, nb, pa, pb, la, lb, s);
   }
 }
 
@@ -326,29 +355,39 @@ __device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk
   return qbase + row * QROW + (quad_slot(row, chunk) << 4) + half * 8;
 }
 
-// One 256×256 output tile of problem a.
-template <int AO, int BO, int EPI>
+// The 256×192 tile's epilogue (defined below).
+template <int EPI>
+__device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, int m0, int n0, TPMLP_LDS char* lds);
+
+// One output tile of problem a: 256×TN, TN = 256 (8 waves as 2×4, each 128×64:
+// 4×2 blocks) or TN = 192 (8 waves as 4×2, each 64×96: 2×3 blocks; its B
+// stage holds 192 rows and takes 3 DMA loads per wave).
+template <int AO, int BO, int EPI, int TN = BN>
 __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS char* lds) {
+  static_assert(TN == 256 || TN == 192, "tile width");
+  constexpr int FA_ = TN == 256 ? FA : 2, FB_ = TN == 256 ? FB : 3;
+  constexpr int WN = TN / (32 * FB_);   // waves across N: 4 or 2
+  constexpr int NLB = TN / 64;          // B loads per wave and stage: 4 or 3
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   int batch, tm, tn;
   tile_coords(tile, a, batch, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * TN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WN, wn = wave % WN;
 
   const i32x4 rA = make_rsrc(a.A + batch * a.sA, a.a_bytes);
   const i32x4 rB = make_rsrc(a.B + batch * a.sB, a.b_bytes);
-  const LoadPlan la = make_plan<AO>(m0, a.M, a.lda, wave, lane);
-  const LoadPlan lb = make_plan<BO>(n0, a.N, a.ldb, wave, lane);
+  const LoadPlan<NLOAD> la = make_plan<AO>(m0, a.M, a.lda, wave, lane);
+  const LoadPlan<NLB> lb = make_plan<BO, NLB>(n0, a.N, a.ldb, wave, lane);
   uint32_t pa[4], pb[4];
-  frag_addr<AO>(pa, wm * 128, lane);
-  frag_addr<BO>(pb, wn * 64, lane);
+  frag_addr<AO>(pa, wm * 32 * FA_, lane);
+  frag_addr<BO>(pb, wn * 32 * FB_, lane);
 
-  f32x16 acc[FA][FB];
+  f32x16 acc[FA_][FB_];
 #pragma unroll
-  for (int i = 0; i < FA; ++i)
+  for (int i = 0; i < FA_; ++i)
 #pragma unroll
-    for (int j = 0; j < FB; ++j)
+    for (int j = 0; j < FB_; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -361,16 +400,16 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
   // the barrier both frees the step's stages and (after this wave's wait for
   // B(kt+1), A(kt+1)) publishes the next step's, whose slice 0 is read while
   // slice 3's MFMAs run.
-  i32x4 fa0[FA], fb0[FB], fa1[FA], fb1[FB];
+  i32x4 fa0[FA_], fb0[FB_], fa1[FA_], fb1[FB_];
   if (KT > 0) {
     // prologue: A(0), B(0), A(1), B(1); wait for the first two
     dma_all<AO>(rA, lds, la, 0, a.K, wave);
-    dma_all<BO>(rB, lds + B_BASE, lb, 0, a.K, wave);
+    dma_all<BO, NLB>(rB, lds + B_BASE, lb, 0, a.K, wave);
     dma_all<AO>(rA, lds + TILE_BYTES, la, la.kstep, a.K - BK, wave);
-    dma_all<BO>(rB, lds + B_BASE + TILE_BYTES, lb, lb.kstep, a.K - BK, wave);
-    wait_vmcnt<2 * NLOAD>();
+    dma_all<BO, NLB>(rB, lds + B_BASE + TILE_BYTES, lb, lb.kstep, a.K - BK, wave);
+    wait_vmcnt<NLOAD + NLB>();
     block_barrier();
-    read_slice<AO, BO, 0>(fa0, fb0, pa, pb, lds_base, lds_base + B_BASE);
+    read_slice<AO, BO, 0, FA_, FB_>(fa0, fb0, pa, pb, lds_base, lds_base + B_BASE);
     wait_frags(fa0, fb0);
   }
 
@@ -393,17 +432,17 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
     s.kremB = a.K - (kt + 2) * BK;
     s.wave = wave;
 
-    slice_body<AO, BO, 0>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
+    slice_body<AO, BO, 0, FA_, FB_, NLB>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
     wait_frags(fa1, fb1);
-    slice_body<AO, BO, 1>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
+    slice_body<AO, BO, 1, FA_, FB_, NLB>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
     wait_frags(fa0, fb0);
-    slice_body<AO, BO, 2>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
+    slice_body<AO, BO, 2, FA_, FB_, NLB>(acc, fa0, fb0, fa1, fb1, pa, pb, la, lb, s);
     wait_frags(fa1, fb1);
     // B(kt+1) and A(kt+1) have landed (this wave's share); A(kt+2) may still
     // be in flight.
     wait_vmcnt<NLOAD>();
     block_barrier();
-    slice_body<AO, BO, 3>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
+    slice_body<AO, BO, 3, FA_, FB_, NLB>(acc, fa1, fb1, fa0, fb0, pa, pb, la, lb, s);
     // the next step's slice-0 fragments (unused after the last step) must
     // have landed before their registers are touched again
     wait_frags(fa0, fb0);
@@ -415,6 +454,10 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // ------------------------------------------------------------------ epilogue
+  if constexpr (TN == 192) {
+    epilogue_n192<EPI>(a, acc, batch, m0, n0, lds);
+    return;
+  } else {
   // Accumulator v of block (i, j) of lane L: row wm·128 + 32i + L%32,
   // columns wn·64 + 32j + 8·(v/4) + 4·(L/32) + v%4.
   const int row_l = lane & 31, half = lane >> 5;
@@ -704,6 +747,152 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
       }
     }
   }
+  }  // TN == 256
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue of the 256×192 tile.  Each wave stages its 64×96 bf16 region in
+// LDS (rows of 256 B: chunk c of 8 columns of row r at 16-B slot c ^ (r % 16);
+// 16 KiB per wave), then all 8 waves store the whole 256×192 tile together:
+// a tile row is 384 B, three 128-B lines, and each wave-wide 16-B store
+// writes 8 whole lines.  Z and Y (the GeLU epilogues) take one pass each,
+// with a workgroup barrier before each pass's stores and after them.
+// Accumulator v of block (i, j) of lane L: row wm·64 + 32i + L%32, columns
+// wn·96 + 32j + 8·(v/4) + 4·(L/32) + v%4 (wm = wave / 2, wn = wave % 2).
+constexpr int N192_QROW = 256, N192_QBYTES = 64 * N192_QROW;
+static_assert(NWAVE * N192_QBYTES + NWAVE * 256 <= LDS_BYTES, "256x192 epilogue staging exceeds the LDS");
+
+__device__ __forceinline__ uint32_t n192_addr(uint32_t qbase, int row, int chunk) {
+  return qbase + row * N192_QROW + ((chunk ^ (row & 15)) << 4);
+}
+
+template <int EPI>
+__device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, int m0, int n0, TPMLP_LDS char* lds) {
+  static_assert(EPI == EPI_STORE || EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE ||
+                    EPI == EPI_GELU_GRAD,
+                "epilogue not available for the 256x192 tile");
+  constexpr bool ZY = EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY;
+  constexpr bool BIAS = EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE;
+  constexpr bool GG = EPI == EPI_GELU_GRAD;
+  constexpr int PASSES = ZY ? 2 : 1;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int row_l = lane & 31, half = lane >> 5;
+  const uint32_t qbase = lds_base + wave * N192_QBYTES;
+  const int64_t cbase = static_cast<int64_t>(batch) * a.sC;
+  const int qm0 = m0 + wm * 64, qn0 = n0 + wn * 96;
+  block_barrier();  // every wave is done with the main-loop stages
+
+  // column bias: the wave's 96 values, staged past the staging regions
+  const uint32_t bbase = lds_base + NWAVE * N192_QBYTES + wave * 256;
+  if constexpr (BIAS) {
+    if (lane < 24) {
+      const int col = qn0 + lane * 4;
+      const bf16* bias = a.bias + static_cast<int64_t>(batch) * a.sBias;
+      const i32x2 b = col < a.N ? *reinterpret_cast<const i32x2*>(bias + col) : i32x2{0, 0};
+      asm volatile("ds_write_b64 %0, %1" ::"v"(bbase + lane * 8), "v"(b) : "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  if constexpr (GG) {
+    // the region's stored Z in the staging layout: load j fills rows
+    // 4j..4j+3 (1 KiB); lane: row 4j + L/16, slot L%16, chunk slot ^ (row % 16)
+    const i32x4 rZ = make_rsrc(a.Zin + cbase, a.c_bytes);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = j * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      const int gr = qm0 + row, gc = qn0 + c * 8;
+      const uint32_t voff = (c < 12 && gr < a.M && gc < a.N)
+                                ? static_cast<uint32_t>((static_cast<int64_t>(gr) * a.ldc + gc) * 2)
+                                : OOB;
+      buffer_load_lds16(rZ, lds + wave * N192_QBYTES + j * 1024, voff);
+    }
+    wait_vmcnt<0>();
+  }
+
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = i * 32 + row_l;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        i32x2 zr[4];
+        if constexpr (BIAS) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            asm volatile("ds_read_b64 %0, %1" : "=v"(zr[q]) : "v"(bbase + (j * 32 + q * 8 + half * 4) * 2));
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(zr[0]), "+v"(zr[1]), "+v"(zr[2]), "+v"(zr[3])::"memory");
+        }
+        if constexpr (GG) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            asm volatile("ds_read_b64 %0, %1" : "=v"(zr[q]) : "v"(n192_addr(qbase, row, j * 4 + q) + half * 8));
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(zr[0]), "+v"(zr[1]), "+v"(zr[2]), "+v"(zr[3])::"memory");
+        }
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[i][j][e]));
+        if constexpr (BIAS) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x4 bq = __builtin_bit_cast(bf16x4, zr[q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] += bf2f(bq[e]);
+          }
+        }
+        if constexpr (ZY) {
+          if (pass == 1) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = gelu_fast(v[e]);
+          }
+        } else if constexpr (GG) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x4 z = __builtin_bit_cast(bf16x4, zr[q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] *= gelu_grad_fast(bf2f(z[e]));
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 pk = pack4_bf16(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          asm volatile("ds_write_b64 %0, %1" ::"v"(n192_addr(qbase, row, j * 4 + q) + half * 8), "v"(pk)
+                       : "memory");
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();  // every region of this pass is staged
+    // the tile: 256 rows × 24 chunks, 12 per thread; thread t, round it:
+    // chunk it·512 + t in row-major order
+    bf16* C = static_cast<bf16*>(pass == 0 ? a.C : a.C2) + cbase;
+#pragma unroll
+    for (int it0 = 0; it0 < 12; it0 += 6) {
+      i32x4 w[6];
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        const int flat = (it0 + u) * NTHR + static_cast<int>(threadIdx.x);
+        const int R = flat / 24, c = flat - R * 24;
+        const int rw = (R >> 6) * 2 + (c >= 12 ? 1 : 0), rr = R & 63, cc = c >= 12 ? c - 12 : c;
+        const uint32_t ad = n192_addr(lds_base + rw * N192_QBYTES, rr, cc);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(w[u]) : "v"(ad) : "memory");
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5])::"memory");
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        const int flat = (it0 + u) * NTHR + static_cast<int>(threadIdx.x);
+        const int R = flat / 24, c = flat - R * 24;
+        const int gr = m0 + R, gc = n0 + c * 8;
+        if (gr < a.M && gc < a.N)
+          __builtin_nontemporal_store(w[u], reinterpret_cast<i32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc));
+      }
+    }
+    if (pass + 1 < PASSES) block_barrier();  // the staging regions are read before the next pass writes them
+  }
 }
 
 // The launch: problems 0 and 1 are of kind (AO0, BO0, EPI0), problem 2 of
@@ -731,13 +920,18 @@ __device__ __forceinline__ void select_slice(KArgs& a, int& tile) {
   a.C = static_cast<float*>(a.C) + slice * a.sSlice;
 }
 
-template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1>
+template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1, int TN = BN>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
   int prob, tile;
   map_workgroup(g.split, g.t0, blockIdx.x, prob, tile);
-  if constexpr (AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1) {
+  if constexpr (TN != BN) {
+    // the 256×192 tile: launches of one kind, never K-split
+    static_assert(AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1, "one kind per 256x192 launch");
+    KArgs a = g.p[prob];
+    gemm_tile<AO0, BO0, EPI0, TN>(a, tile, lds);
+  } else if constexpr (AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1) {
     KArgs a = g.p[prob];  // one copy: wide scalar loads at the problem's offset
     if constexpr (EPI0 == EPI_STORE_F32) select_slice<AO0, BO0>(a, tile);
     gemm_tile<AO0, BO0, EPI0>(a, tile, lds);
@@ -839,9 +1033,9 @@ __global__ __launch_bounds__(FIX_THREADS) void splitk_fixup_kernel(FixArgs f) {
   }
 }
 
-template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1>
+template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1, int TN = BN>
 hipError_t launch_t(const KGroup& g, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<AO0, BO0, EPI0, AO1, BO1, EPI1>), dim3(g.t0 + g.t1 + g.t2), dim3(NTHR), 0,
+  hipLaunchKernelGGL((gemm_bf16_kernel<AO0, BO0, EPI0, AO1, BO1, EPI1, TN>), dim3(g.t0 + g.t1 + g.t2), dim3(NTHR), 0,
                      stream, g);
   return hipGetLastError();
 }
@@ -855,7 +1049,7 @@ uint32_t extent_bytes(int order, int rows, int K, int64_t ld) {
 }
 
 
-KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
+KArgs kargs(const GemmProblem& p, int a_order, int b_order, int tn = BN) {
   KArgs k;
   k.A = static_cast<const bf16*>(p.A);
   k.B = static_cast<const bf16*>(p.B);
@@ -870,7 +1064,7 @@ KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
   k.N = p.N;
   k.K = p.K;
   k.tiles_m = (p.M + BM - 1) / BM;
-  k.tiles_n = (p.N + BN - 1) / BN;
+  k.tiles_n = (p.N + tn - 1) / tn;
   k.batch = p.batch;
   k.lda = p.lda;
   k.ldb = p.ldb;
@@ -889,8 +1083,8 @@ KArgs kargs(const GemmProblem& p, int a_order, int b_order) {
 
 bool empty(const GemmProblem& p) { return p.M <= 0 || p.N <= 0 || p.batch <= 0; }
 
-int64_t tiles_of(const GemmProblem& p) {
-  return empty(p) ? 0 : static_cast<int64_t>((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+int64_t tiles_of(const GemmProblem& p, int tn = BN) {
+  return empty(p) ? 0 : static_cast<int64_t>((p.M + BM - 1) / BM) * ((p.N + tn - 1) / tn) * p.batch;
 }
 
 // ---------------------------------------------------------------- split-K plan
@@ -1009,7 +1203,32 @@ hipError_t fixup(const GemmProblem& p, int epi, const float* part, int S, hipStr
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- tile width
+// A launch of one kind that runs unsplit may take the 256×192 tile instead of
+// 256×256 when that fills the 256 CUs in fewer rounds of tiles: 8192×1536 is
+// 192 tiles of 256×256 (three quarters of the CUs for one round) or 256 of
+// 256×192 (all of them); 8192×3072 is 384 (two rounds, the second half empty)
+// or 512 (two full ones).  Cost of a round, in K steps of a 256×256 tile: the
+// steps plus the fixed prologue/epilogue.  A 256×192 step does 3/4 of the
+// MFMA work but moves 7/8 of the operand bytes, and the K loop is bound by
+// that stream: measured on one shard of the 8.3B-shaped layer, 72.8 against
+// 81.0 µs (Z = X·A_i, 48 steps, one round each) and 72.3 against 80.7 µs
+// (P = Y·B_i, 24 steps, two rounds each), i.e. 0.9 of a step per step.  Only
+// shapes decide, so a call is reproducible.
+constexpr double k192StepFrac = 0.9, k192FixedSteps = 3.5;
+std::atomic<int> g_tile_policy{TILE_AUTO};
+
+bool n192_kind(const GemmKind& k) {
+  if (k.a_order != KMAJ) return false;
+  if (k.b_order == MNMAJ)
+    return k.epi == EPI_STORE || k.epi == EPI_GELU_ZY || k.epi == EPI_BIAS_GELU_ZY || k.epi == EPI_BIAS_STORE;
+  return k.epi == EPI_STORE || k.epi == EPI_GELU_GRAD;
+}
+
 }  // namespace
+
+void set_gemm_tile_policy(int policy) { g_tile_policy.store(policy, std::memory_order_relaxed); }
+int gemm_tile_policy() { return g_tile_policy.load(std::memory_order_relaxed); }
 
 size_t gemm_bf16_split_bytes(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
                              const GemmProblem* shortp, const GemmKind& short_kind) {
@@ -1058,16 +1277,41 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
       li[nl++] = i;
     }
   const bool has_short = shortp != nullptr && !empty(sp[2]);
-  const int64_t t0 = nl > 0 ? tiles_of(*lp[0]) * plan.s[li[0]] : 0;
-  const int64_t t1 = nl > 1 ? tiles_of(*lp[1]) * plan.s[li[1]] : 0;
-  const int64_t t2 = has_short ? tiles_of(sp[2]) * plan.s[2] : 0;
-  if (t0 + t1 + t2 == 0) return hipSuccess;
-  if (t0 + t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
   const GemmKind lk = nl > 0 ? sk[li[0]] : long_kind;
   const GemmKind shk = has_short ? sk[2] : short_kind;
+  // with no long-group problem the launch is of the short kind alone, and
+  // vice versa
+  const GemmKind& k0 = nl > 0 ? lk : shk;
+  const GemmKind& k1 = has_short ? shk : lk;
+  auto is = [](const GemmKind& x, int ao, int bo, int epi) {
+    return x.a_order == ao && x.b_order == bo && x.epi == epi;
+  };
+  const bool same = is(k1, k0.a_order, k0.b_order, k0.epi);
+  int tn = BN;
+  const int policy = g_tile_policy.load(std::memory_order_relaxed);
+  if (policy != TILE_256 && same && n192_kind(k0) && plan.s[0] <= 1 && plan.s[1] <= 1 &&
+      plan.s[2] <= 1) {
+    int64_t T256 = 0, T192 = 0;
+    int ks = 0;
+    for (int i = 0; i < 3; ++i) {
+      if (slot[i] == nullptr || empty(sp[i]) || (i == 2 && !has_short) || (i < 2 && i >= nlong)) continue;
+      T256 += tiles_of(sp[i]);
+      T192 += tiles_of(sp[i], 192);
+      const int k = (sp[i].K + BK - 1) / BK;
+      ks = k > ks ? k : ks;
+    }
+    const double r256 = static_cast<double>((T256 + kCUs - 1) / kCUs), r192 = static_cast<double>((T192 + kCUs - 1) / kCUs);
+    const double c256 = r256 * (ks + kTileFixedSteps), c192 = r192 * (k192StepFrac * ks + k192FixedSteps);
+    if (policy == TILE_192 || c192 < 0.95 * c256) tn = 192;
+  }
+  const int64_t t0 = nl > 0 ? tiles_of(*lp[0], tn) * plan.s[li[0]] : 0;
+  const int64_t t1 = nl > 1 ? tiles_of(*lp[1], tn) * plan.s[li[1]] : 0;
+  const int64_t t2 = has_short ? tiles_of(sp[2], tn) * plan.s[2] : 0;
+  if (t0 + t1 + t2 == 0) return hipSuccess;
+  if (t0 + t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
   KGroup g;
   auto mk = [&](const GemmProblem& q, int i, const GemmKind& k) {
-    KArgs a = kargs(q, k.a_order, k.b_order);
+    KArgs a = kargs(q, k.a_order, k.b_order, tn);
     if (plan.s[i] > 1) {
       const int ks = (q.K + BK - 1) / BK;
       a.ksplit = plan.s[i];
@@ -1083,15 +1327,22 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
   g.t1 = static_cast<int>(t1);
   g.t2 = static_cast<int>(t2);
   g.split = make_split(g.t0, g.t1, g.t2);
-  // with no long-group problem the launch is of the short kind alone, and
-  // vice versa
-  const GemmKind& k0 = nl > 0 ? lk : shk;
-  const GemmKind& k1 = has_short ? shk : lk;
-  auto is = [](const GemmKind& x, int ao, int bo, int epi) {
-    return x.a_order == ao && x.b_order == bo && x.epi == epi;
-  };
-  const bool same = is(k1, k0.a_order, k0.b_order, k0.epi);
   hipError_t e = hipErrorInvalidValue;
+  if (tn == 192) {
+    if (is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
+      e = launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY, 192>(g, stream);
+    else if (is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
+      e = launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, 192>(g, stream);
+    else if (is(k0, KMAJ, MNMAJ, EPI_STORE))
+      e = launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE, 192>(g, stream);
+    else if (is(k0, KMAJ, MNMAJ, EPI_BIAS_STORE))
+      e = launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_BIAS_STORE, 192>(g, stream);
+    else if (is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))
+      e = launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD, 192>(g, stream);
+    else if (is(k0, KMAJ, KMAJ, EPI_STORE))
+      e = launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE, 192>(g, stream);
+    return e;  // never K-split: no fix-up
+  }
   if (same && is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
     e = launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
   else if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))

@@ -61,6 +61,14 @@ struct GemmKind {
 // With a workspace of at least gemm_bf16_split_bytes(...) bytes, problems
 // that would leave the machine idle run K-split (fp32 partials in ws, then a
 // fix-up kernel per split problem); with less (or none), nothing is split.
+// The bf16 GEMM's tile width policy (process-wide): TILE_AUTO picks 256×192
+// tiles where a cost model of CU rounds favours them, TILE_256 never does,
+// TILE_192 does wherever they are available (launches of one kind with the
+// plain, GeLU, bias or GeLU' epilogue that run unsplit).
+enum TilePolicy { TILE_AUTO = 0, TILE_256 = 1, TILE_192 = 2 };
+void set_gemm_tile_policy(int policy);
+int gemm_tile_policy();
+
 size_t gemm_bf16_split_bytes(const GemmProblem* longp, int nlong, const GemmKind& long_kind,
                              const GemmProblem* shortp, const GemmKind& short_kind);
 hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const GemmKind& long_kind,

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.tpmlp_abi_version() == 8
+    assert L.tpmlp_abi_version() == 9
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         assert L.tpmlp_status_string(s)
 
@@ -333,3 +333,14 @@ def test_sp_args_layout_matches_header(tmp_path):
     assert out[0] == ctypes.sizeof(tp.SpArgs)
     for f, off in zip(fields, out[1:]):
         assert getattr(tp.SpArgs, f).offset == off, f
+
+
+def test_gemm_tile_policy_knob(L):
+    # host-only state: set, read back, reject other values, restore
+    assert tp.gemm_tile_policy() == tp.GEMM_TILE_AUTO
+    for p in (tp.GEMM_TILE_256, tp.GEMM_TILE_192, tp.GEMM_TILE_AUTO):
+        tp.set_gemm_tile_policy(p)
+        assert tp.gemm_tile_policy() == p
+    for bad in (-1, 3, 192):
+        assert L.tpmlp_set_gemm_tile_policy(bad) == tp.ERR_ARG
+    assert tp.gemm_tile_policy() == tp.GEMM_TILE_AUTO
