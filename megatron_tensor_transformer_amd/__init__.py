@@ -402,9 +402,9 @@ def tpmlp_ln_sp(args, stream=None):
     _check(lib().tpmlp_ln_sp(_stream(stream), ctypes.byref(args)))
 
 
-# bf16 GEMM tile width policy (process-wide): automatic, 256x256 only, or
-# 256x192 wherever available; results do not depend on it
-GEMM_TILE_AUTO, GEMM_TILE_256, GEMM_TILE_192 = 0, 1, 2
+# bf16 GEMM tile and schedule policy (process-wide): automatic, 256x256 only,
+# 256x192 wherever available, or a K-split tail wherever available
+GEMM_TILE_AUTO, GEMM_TILE_256, GEMM_TILE_192, GEMM_STREAMK = 0, 1, 2, 3
 
 
 def set_gemm_tile_policy(policy):

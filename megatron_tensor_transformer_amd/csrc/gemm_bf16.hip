@@ -70,6 +70,15 @@ struct alignas(64) KArgs {
   // its fp32 partial tile at C + s·sSlice (ksplit = 1: no split)
   int ksplit, kchunk;
   int64_t sSlice;
+  // K-split tail (sk_L > 0: this problem's work items are tail pieces): the
+  // sk_T tiles from tile index sk_first on (sk_KS K steps each) each split
+  // into sk_q pieces of sk_L steps; item c = j·sk_T + u takes steps
+  // [j·sk_L, min((j+1)·sk_L, sk_KS)) of tail tile u and writes its fp32
+  // partial into slot c of sk_ws (256×256 floats per slot).  Items with the
+  // same j cover the same K range, so neighbouring tiles' items share their
+  // operand slices in the L2.
+  int sk_L, sk_T, sk_first, sk_KS, sk_q;
+  float* sk_ws;
 };
 
 // One launch runs up to three problems: p[0] and p[1] (the long group, one
@@ -920,6 +929,43 @@ __device__ __forceinline__ void select_slice(KArgs& a, int& tile) {
   a.C = static_cast<float*>(a.C) + slice * a.sSlice;
 }
 
+// Restrict problem a to k in [k0, k0 + len): the operands' base pointers and
+// buffer ranges move to k0 (the K-edge test zero-fills past the new K).
+template <int AO, int BO>
+__device__ __forceinline__ void shift_k(KArgs& a, int k0, int len) {
+  const int64_t offA = AO == KMAJ ? k0 : static_cast<int64_t>(k0) * a.lda;
+  const int64_t offB = BO == KMAJ ? k0 : static_cast<int64_t>(k0) * a.ldb;
+  a.A += offA;
+  a.B += offB;
+  a.a_bytes = a.a_bytes > offA * 2 ? a.a_bytes - static_cast<uint32_t>(offA * 2) : 0u;
+  a.b_bytes = a.b_bytes > offB * 2 ? a.b_bytes - static_cast<uint32_t>(offB * 2) : 0u;
+  a.K = len;
+}
+
+// Tail item c of problem a (a.sk_L > 0): piece j of tail tile u, an fp32
+// partial tile in slot c.
+template <int AO, int BO>
+__device__ __forceinline__ void sk_item(const KArgs& a, int c, TPMLP_LDS char* lds) {
+  const int j = c / a.sk_T, u = c - j * a.sk_T;
+  const int kb = j * a.sk_L;
+  if (j >= a.sk_q || kb >= a.sk_KS) return;  // the whole workgroup: c is uniform
+  const int ke = kb + a.sk_L < a.sk_KS ? kb + a.sk_L : a.sk_KS;
+  int batch, tm, tn;
+  tile_coords(u + a.sk_first, a, batch, tm, tn);
+  KArgs b = a;
+  const int k0 = kb * BK;
+  const int rest = a.K - k0;
+  const int len = (ke - kb) * BK < rest ? (ke - kb) * BK : rest;
+  shift_k<AO, BO>(b, k0, len);
+  // the slot holds the tile at row stride 256; the epilogue adds
+  // (batch·sC + row·ldc + col) to C, so C is moved back by the tile origin
+  float* slot = a.sk_ws + static_cast<int64_t>(c) * (BM * BN);
+  b.C = slot - (static_cast<int64_t>(tm) * BM * BN + static_cast<int64_t>(tn) * BN);
+  b.ldc = BN;
+  b.sC = 0;
+  gemm_tile<AO, BO, EPI_STORE_F32>(b, u + a.sk_first, lds);
+}
+
 template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1, int TN = BN>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -938,7 +984,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   } else {
     KArgs a = g.p[prob];
     if (prob == 2) {
-      if constexpr (EPI1 == EPI_STORE_F32) select_slice<AO1, BO1>(a, tile);
+      if constexpr (EPI1 == EPI_STORE_F32) {
+        if (a.sk_L > 0) {
+          sk_item<AO1, BO1>(a, tile, lds);
+          return;
+        }
+        select_slice<AO1, BO1>(a, tile);
+      }
       gemm_tile<AO1, BO1, EPI1>(a, tile, lds);
     } else {
       if constexpr (EPI0 == EPI_STORE_F32) select_slice<AO0, BO0>(a, tile);
@@ -965,6 +1017,47 @@ struct FixArgs {
 };
 
 constexpr int FIX_THREADS = 256;
+
+// The epilogue of a fixed-up sum x of 8 consecutive columns at element offset
+// o of the output (bias offset ob): the same fp32 arithmetic as the GEMM's own
+// epilogue.
+template <int EPI>
+__device__ __forceinline__ void fix_store(float (&x)[8], int64_t o, int64_t ob, void* C, void* C2, const bf16* Zin,
+                                          const bf16* bias) {
+  if constexpr (EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE) {
+    const bf16x8 bb = *reinterpret_cast<const bf16x8*>(bias + ob);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += bf2f(bb[e]);
+  }
+  if constexpr (EPI == EPI_STORE_F32) {
+    f32x4 lo, hi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lo[q] = x[q];
+      hi[q] = x[4 + q];
+    }
+    float* c = static_cast<float*>(C) + o;
+    reinterpret_cast<f32x4*>(c)[0] = lo;
+    reinterpret_cast<f32x4*>(c)[1] = hi;
+  } else {
+    bf16x8 r;
+    if constexpr (EPI == EPI_GELU_GRAD) {
+      const bf16x8 z = *reinterpret_cast<const bf16x8*>(Zin + o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e] * gelu_grad_fast(bf2f(z[e])));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e]);
+    }
+    *reinterpret_cast<bf16x8*>(static_cast<bf16*>(C) + o) = r;
+    if constexpr (EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY) {
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = f2bf(gelu_fast(x[e]));
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(C2) + o) = y;
+    }
+  }
+}
 
 template <int EPI>
 __global__ __launch_bounds__(FIX_THREADS) void splitk_fixup_kernel(FixArgs f) {
@@ -996,41 +1089,37 @@ __global__ __launch_bounds__(FIX_THREADS) void splitk_fixup_kernel(FixArgs f) {
         x[4 + q] += hi[q];
       }
     }
-    const int64_t o = b * f.sC + row * f.ldc + col;
-    if constexpr (EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE) {
-      const bf16x8 bb = *reinterpret_cast<const bf16x8*>(f.bias + b * f.sBias + col);
+    fix_store<EPI>(x, b * f.sC + row * f.ldc + col, b * f.sBias + col, f.C, f.C2, f.Zin, f.bias);
+  }
+}
+
+// Tail fix-up: out = epilogue(Σ_j piece j) for the tail tiles of problem a,
+// the pieces added in K order, so the result is bit-reproducible.  32 blocks
+// per tile; a thread owns 8 consecutive columns of one row.
+template <int EPI>
+__global__ __launch_bounds__(FIX_THREADS) void sk_fixup_kernel(KArgs a) {
+  const int u = static_cast<int>(blockIdx.x >> 5);
+  const int v = static_cast<int>(blockIdx.x & 31) * FIX_THREADS + static_cast<int>(threadIdx.x);
+  const int r = v >> 5, cc = (v & 31) * 8;
+  int batch, tm, tn;
+  tile_coords(u + a.sk_first, a, batch, tm, tn);
+  const int64_t row = static_cast<int64_t>(tm) * BM + r, col = static_cast<int64_t>(tn) * BN + cc;
+  if (row >= a.M || col >= a.N) return;
+  float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] += bf2f(bb[e]);
-    }
-    if constexpr (EPI == EPI_STORE_F32) {
-      f32x4 lo, hi;
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  for (int j = 0; j < a.sk_q; ++j) {
+    const int64_t slot = static_cast<int64_t>(j) * a.sk_T + u;
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(a.sk_ws + slot * (BM * BN) + r * BN + cc);
+    const f32x4 lo = __builtin_nontemporal_load(q4), hi = __builtin_nontemporal_load(q4 + 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        lo[q] = x[q];
-        hi[q] = x[4 + q];
-      }
-      float* c = static_cast<float*>(f.C) + o;
-      reinterpret_cast<f32x4*>(c)[0] = lo;
-      reinterpret_cast<f32x4*>(c)[1] = hi;
-    } else {
-      bf16x8 r;
-      if constexpr (EPI == EPI_GELU_GRAD) {
-        const bf16x8 z = *reinterpret_cast<const bf16x8*>(f.Zin + o);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e] * gelu_grad_fast(bf2f(z[e])));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e]);
-      }
-      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(f.C) + o) = r;
-      if constexpr (EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY) {
-        bf16x8 y;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = f2bf(gelu_fast(x[e]));
-        *reinterpret_cast<bf16x8*>(static_cast<bf16*>(f.C2) + o) = y;
-      }
+    for (int q = 0; q < 4; ++q) {
+      x[q] += lo[q];
+      x[4 + q] += hi[q];
     }
   }
+  fix_store<EPI>(x, static_cast<int64_t>(batch) * a.sC + row * a.ldc + col,
+                 static_cast<int64_t>(batch) * a.sBias + col, a.C, a.C2, a.Zin, a.bias);
 }
 
 template <int AO0, int BO0, int EPI0, int AO1, int BO1, int EPI1, int TN = BN>
@@ -1050,7 +1139,7 @@ uint32_t extent_bytes(int order, int rows, int K, int64_t ld) {
 
 
 KArgs kargs(const GemmProblem& p, int a_order, int b_order, int tn = BN) {
-  KArgs k;
+  KArgs k{};  // every field zero unless set below (no K split, no stream-K items)
   k.A = static_cast<const bf16*>(p.A);
   k.B = static_cast<const bf16*>(p.B);
   k.C = p.C;
@@ -1112,13 +1201,80 @@ struct SplitPlan {
   int s[3];
   size_t off[3];  // byte offset of each split problem's partial planes in the workspace
   size_t bytes;
+  // K-split tail (sk_slot >= 0): that problem's first sk_first tiles run as
+  // whole tiles, the sk_T after them as sk_q pieces of sk_L K steps each
+  int sk_slot, sk_L, sk_T, sk_first, sk_KS, sk_q;
+  size_t sk_off;
 };
 
 bool splittable(const GemmKind& k) { return k.epi != EPI_STORE_ROWSTATS && k.epi != EPI_GELU_GRAD_DB; }
 
+std::atomic<int> g_tile_policy{TILE_AUTO};
+
+// Output bytes per element of a kind's epilogue (the fix-up's writes and reads
+// beyond the partials).
+double out_bytes(const GemmKind& k) {
+  switch (k.epi) {
+    case EPI_GELU_ZY:
+    case EPI_BIAS_GELU_ZY:
+    case EPI_GELU_GRAD: return 4.0;
+    case EPI_STORE_F32: return 4.0;
+    default: return 2.0;
+  }
+}
+
+// K-split tail for a launch of one problem whose tiles fill r ≥ 1 whole
+// rounds of the kCUs CUs and then at most half of one more: the last Tt =
+// T − r·kCUs tiles are each split into q = min(⌊kCUs/Tt⌋, KS) pieces of L =
+// ⌈KS/q⌉ K steps, all Tt·q ≤ kCUs pieces running as one extra round, and a
+// fix-up adds each tile's pieces in order and applies the epilogue.  The
+// pieces of one index j cover the same K range in every tail tile, so tiles
+// that share an operand panel read it together (a stream-K split into equal
+// ranges of the tail's whole step sequence cut tiles at different K and
+// made the panels of a launch with a large B operand, the GPT-1T-shaped
+// shard's Z = X·A_i, be read once per tile: slower than no split).  Cost, in
+// K steps of a tile: r whole rounds, one piece round, and the partial planes
+// written and read plus the outputs at kFixBytesPerStep.
+void plan_stream_k(SplitPlan& pl, const GemmProblem* const (&pr)[3], const GemmKind* const (&kd)[3], int policy) {
+  pl.sk_slot = -1;
+  if (policy == TILE_256 || policy == TILE_192) return;
+  int live = -1, nlive = 0;
+  for (int i = 0; i < 3; ++i)
+    if (pr[i] != nullptr && !empty(*pr[i])) {
+      live = i;
+      ++nlive;
+    }
+  if (nlive != 1 || pl.s[live] > 1) return;
+  const GemmProblem& p = *pr[live];
+  const GemmKind& k = *kd[live];
+  if (!splittable(k) || k.epi == EPI_STORE_F32 || p.N % 8 != 0) return;
+  const int64_t T = tiles_of(p);
+  const int KS = (p.K + BK - 1) / BK;
+  const int64_t r = T / kCUs, Tt = T - r * kCUs;
+  if (r < 1 || Tt == 0 || KS < 2) return;
+  int64_t q = kCUs / Tt;
+  if (q > KS) q = KS;
+  if (q < 2) return;
+  const int64_t L = (KS + q - 1) / q;
+  q = (KS + L - 1) / L;  // pieces that are not empty
+  const double now = static_cast<double>(r + 1) * (KS + kTileFixedSteps);
+  const double bytes = static_cast<double>(Tt) * q * BM * BN * 4.0 * 2.0 + static_cast<double>(Tt) * BM * BN * out_bytes(k);
+  const double sk = static_cast<double>(r) * (KS + kTileFixedSteps) + L + kTileFixedSteps +
+                    bytes / kFixBytesPerStep + kFixLaunchSteps;
+  if (policy != TILE_STREAMK && !(sk < 0.95 * now)) return;
+  pl.sk_slot = live;
+  pl.sk_L = static_cast<int>(L);
+  pl.sk_T = static_cast<int>(Tt);
+  pl.sk_q = static_cast<int>(q);
+  pl.sk_first = static_cast<int>(r * kCUs);
+  pl.sk_KS = KS;
+  pl.sk_off = pl.bytes;
+  pl.bytes += static_cast<size_t>(Tt * q) * BM * BN * 4;
+}
+
 // problems: up to three (null = absent); kinds: theirs
 SplitPlan plan_split(const GemmProblem* const (&pr)[3], const GemmKind* const (&kd)[3]) {
-  SplitPlan best{{1, 1, 1}, {0, 0, 0}, 0};
+  SplitPlan best{{1, 1, 1}, {0, 0, 0}, 0, -1, 0, 0, 0, 0, 0, 0};
   double T[3], KS[3], MN[3];
   bool can[3];
   for (int i = 0; i < 3; ++i) {
@@ -1167,6 +1323,7 @@ SplitPlan plan_split(const GemmProblem* const (&pr)[3], const GemmKind* const (&
     if (s[i] > 1) off += (static_cast<size_t>(s[i]) * static_cast<size_t>(MN[i]) * 4 + 255) / 256 * 256;
   }
   best.bytes = off;
+  plan_stream_k(best, pr, kd, g_tile_policy.load(std::memory_order_relaxed));
   return best;
 }
 
@@ -1216,13 +1373,60 @@ hipError_t fixup(const GemmProblem& p, int epi, const float* part, int S, hipStr
 // (P = Y·B_i, 24 steps, two rounds each), i.e. 0.9 of a step per step.  Only
 // shapes decide, so a call is reproducible.
 constexpr double k192StepFrac = 0.9, k192FixedSteps = 3.5;
-std::atomic<int> g_tile_policy{TILE_AUTO};
 
 bool n192_kind(const GemmKind& k) {
   if (k.a_order != KMAJ) return false;
   if (k.b_order == MNMAJ)
     return k.epi == EPI_STORE || k.epi == EPI_GELU_ZY || k.epi == EPI_BIAS_GELU_ZY || k.epi == EPI_BIAS_STORE;
   return k.epi == EPI_STORE || k.epi == EPI_GELU_GRAD;
+}
+
+// A launch planned with a K-split tail: the first sk_first tiles as whole
+// tiles (problem 0, the problem's own epilogue), the sk_T·sk_q tail pieces as
+// problem 2 (fp32 partials), then the fix-up over the sk_T tail tiles.
+hipError_t launch_stream_k(const GemmProblem& p, const GemmKind& k, const SplitPlan& pl, char* wsb,
+                           hipStream_t stream) {
+  KGroup g;
+  const KArgs a = kargs(p, k.a_order, k.b_order);
+  KArgs b = a;
+  b.sk_L = pl.sk_L;
+  b.sk_T = pl.sk_T;
+  b.sk_first = pl.sk_first;
+  b.sk_KS = pl.sk_KS;
+  b.sk_q = pl.sk_q;
+  b.sk_ws = reinterpret_cast<float*>(wsb + pl.sk_off);
+  g.p[0] = a;
+  g.p[1] = a;
+  g.p[2] = b;
+  g.t0 = pl.sk_first;
+  g.t1 = 0;
+  g.t2 = pl.sk_T * pl.sk_q;
+  g.split = make_split(g.t0, g.t1, g.t2);
+  auto is = [&](int ao, int bo, int epi) { return k.a_order == ao && k.b_order == bo && k.epi == epi; };
+  hipError_t e = hipErrorInvalidValue;
+  if (is(KMAJ, MNMAJ, EPI_GELU_ZY))
+    e = launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  else if (is(KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
+    e = launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  else if (is(KMAJ, MNMAJ, EPI_STORE))
+    e = launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  else if (is(KMAJ, MNMAJ, EPI_BIAS_STORE))
+    e = launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_STORE_F32>(g, stream);
+  else if (is(KMAJ, KMAJ, EPI_GELU_GRAD))
+    e = launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_STORE_F32>(g, stream);
+  else if (is(KMAJ, KMAJ, EPI_STORE))
+    e = launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE_F32>(g, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(pl.sk_T) * 32), block(FIX_THREADS);
+  switch (k.epi) {
+    case EPI_STORE: hipLaunchKernelGGL(sk_fixup_kernel<EPI_STORE>, grid, block, 0, stream, b); break;
+    case EPI_GELU_ZY: hipLaunchKernelGGL(sk_fixup_kernel<EPI_GELU_ZY>, grid, block, 0, stream, b); break;
+    case EPI_GELU_GRAD: hipLaunchKernelGGL(sk_fixup_kernel<EPI_GELU_GRAD>, grid, block, 0, stream, b); break;
+    case EPI_BIAS_GELU_ZY: hipLaunchKernelGGL(sk_fixup_kernel<EPI_BIAS_GELU_ZY>, grid, block, 0, stream, b); break;
+    case EPI_BIAS_STORE: hipLaunchKernelGGL(sk_fixup_kernel<EPI_BIAS_STORE>, grid, block, 0, stream, b); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1245,8 +1449,9 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
   const GemmProblem* slot[3] = {nlong > 0 ? &longp[0] : nullptr, nlong > 1 ? &longp[1] : nullptr, shortp};
   const GemmKind* kslot[3] = {&long_kind, &long_kind, &short_kind};
   SplitPlan plan = plan_split(slot, kslot);
-  if (ws == nullptr || ws_bytes < plan.bytes) plan = SplitPlan{{1, 1, 1}, {0, 0, 0}, 0};
+  if (ws == nullptr || ws_bytes < plan.bytes) plan = SplitPlan{{1, 1, 1}, {0, 0, 0}, 0, -1, 0, 0, 0, 0, 0, 0};
   char* wsb = static_cast<char*>(ws);
+  if (plan.sk_slot >= 0) return launch_stream_k(*slot[plan.sk_slot], *kslot[plan.sk_slot], plan, wsb, stream);
 
   // a K-split problem runs as an fp32 store of its slices' partials
   GemmProblem sp[3];
@@ -1326,7 +1531,12 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
   g.t0 = static_cast<int>(t0);
   g.t1 = static_cast<int>(t1);
   g.t2 = static_cast<int>(t2);
-  g.split = make_split(g.t0, g.t1, g.t2);
+  // longest tiles first: the short problem's before the long group's when its
+  // tiles take more K steps (e.g. dgrad-2, K = m_i, against weight gradients
+  // with K = n at few tokens)
+  auto steps = [](const KArgs& a) { return a.ksplit > 1 ? a.kchunk / BK : (a.K + BK - 1) / BK; };
+  const bool short_first = nl > 0 && has_short && steps(g.p[2]) > steps(g.p[0]);
+  g.split = make_split(g.t0, g.t1, g.t2, short_first);
   hipError_t e = hipErrorInvalidValue;
   if (tn == 192) {
     if (is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))

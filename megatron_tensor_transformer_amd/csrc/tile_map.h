@@ -11,7 +11,11 @@
 // many positions as the round-robin deal gives it, and works first through
 // the long-group tiles of its range, then the short-group ones: every XCD gets
 // its proportional share of both, the long tiles first so the short ones fill
-// in behind them.
+// in behind them.  ("Long group" names the problems' role in the launch, not
+// their K: when the short problem's tiles take more K steps than the long
+// group's, e.g. dgrad-2 with K = m_i against weight gradients with K = n at
+// few tokens, the launch sets short_first and each XCD runs its range's
+// short-problem tiles first.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,12 +35,14 @@ __host__ __device__ inline void xcd_range(int total, int xcd, int& begin, int& c
 // starts in the long group (long0) and how many long-group tiles it has
 // (nlong).  Computed once per launch on the host (it needs 64-bit divisions).
 struct XcdSplit {
-  int long0[8], nlong[8], short0[8];
+  int long0[8], nlong[8], short0[8], nshort[8];
+  int short_first;  // 1: each XCD runs its short-problem tiles before its long-group ones
 };
 
-__host__ __device__ inline XcdSplit make_split(int t0, int t1, int t2) {
+__host__ __device__ inline XcdSplit make_split(int t0, int t1, int t2, bool short_first = false) {
   const int64_t glong = static_cast<int64_t>(t0) + t1, total = glong + t2;
   XcdSplit s;
+  s.short_first = short_first ? 1 : 0;
   for (int x = 0; x < 8; ++x) {
     int begin, count;
     xcd_range(static_cast<int>(total), x, begin, count);
@@ -46,6 +52,7 @@ __host__ __device__ inline XcdSplit make_split(int t0, int t1, int t2) {
     s.long0[x] = a;
     s.nlong[x] = b - a;
     s.short0[x] = begin - a;
+    s.nshort[x] = count - (b - a);
   }
   return s;
 }
@@ -54,14 +61,26 @@ __host__ __device__ inline XcdSplit make_split(int t0, int t1, int t2) {
 // (the short problem); tile: index within that problem.
 __host__ __device__ inline void map_workgroup(const XcdSplit& s, int t0, int wg, int& prob, int& tile) {
   const int xcd = wg & 7, local = wg >> 3;
-  if (local < s.nlong[xcd]) {
-    const int k = s.long0[xcd] + local;
-    prob = k < t0 ? 0 : 1;
-    tile = k < t0 ? k : k - t0;
+  int lk;  // position among the XCD's long-group tiles, or -1 for a short one
+  if (!s.short_first) {
+    lk = local < s.nlong[xcd] ? local : -1;
+    if (lk < 0) {
+      prob = 2;
+      tile = s.short0[xcd] + (local - s.nlong[xcd]);
+      return;
+    }
   } else {
-    prob = 2;
-    tile = s.short0[xcd] + (local - s.nlong[xcd]);
+    const int nshort = s.nshort[xcd];
+    if (local < nshort) {
+      prob = 2;
+      tile = s.short0[xcd] + local;
+      return;
+    }
+    lk = local - nshort;
   }
+  const int k = s.long0[xcd] + lk;
+  prob = k < t0 ? 0 : 1;
+  tile = k < t0 ? k : k - t0;
 }
 
 // Attention launches: `heads` independent sequences of `nblk` blocks each, in

@@ -10,6 +10,8 @@ import subprocess
 
 import pytest
 
+import torch
+
 import megatron_tensor_transformer_amd as tp
 from conftest import ROOT
 
@@ -338,9 +340,28 @@ def test_sp_args_layout_matches_header(tmp_path):
 def test_gemm_tile_policy_knob(L):
     # host-only state: set, read back, reject other values, restore
     assert tp.gemm_tile_policy() == tp.GEMM_TILE_AUTO
-    for p in (tp.GEMM_TILE_256, tp.GEMM_TILE_192, tp.GEMM_TILE_AUTO):
+    for p in (tp.GEMM_TILE_256, tp.GEMM_TILE_192, tp.GEMM_STREAMK, tp.GEMM_TILE_AUTO):
         tp.set_gemm_tile_policy(p)
         assert tp.gemm_tile_policy() == p
-    for bad in (-1, 3, 192):
+    for bad in (-1, 4, 192):
         assert L.tpmlp_set_gemm_tile_policy(bad) == tp.ERR_ARG
     assert tp.gemm_tile_policy() == tp.GEMM_TILE_AUTO
+
+
+def test_workspace_query_covers_stream_k():
+    """With the K-split-tail policy the forward's workspace query asks for the
+    tail's partial tiles: n = 4352, d = m_i = 4096 gives both GEMMs 17 × 16 =
+    272 tiles (one round of 256 and 16 more), K = 4096 (64 steps), so the 16
+    tail tiles run as 16 pieces each, 256 partial tiles of 256 KiB; without
+    the tail neither GEMM needs a workspace."""
+    X = torch.empty((4352, 4096), dtype=torch.bfloat16)
+    A = torch.empty((1, 4096, 4096), dtype=torch.bfloat16)
+    try:
+        tp.set_gemm_tile_policy(tp.GEMM_TILE_256)
+        plain = tp.fwd_workspace_bytes(X, A)
+        tp.set_gemm_tile_policy(tp.GEMM_STREAMK)
+        sk = tp.fwd_workspace_bytes(X, A)
+    finally:
+        tp.set_gemm_tile_policy(tp.GEMM_TILE_AUTO)
+    assert plain == 0
+    assert sk == 16 * 16 * 256 * 256 * 4

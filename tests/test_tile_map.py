@@ -1,7 +1,9 @@
 """The GEMM launch's workgroup -> (problem, tile) map is a bijection onto the
 tiles of all its problems (a long group of up to two problems and a short
-one), for launches of any size, and gives every XCD a contiguous share of the
-long group and of the short problem.  The map is the
+one), for launches of any size, gives every XCD a contiguous share of the
+long group and of the short problem, and runs each XCD's tiles of one kind
+before the other's (the long group's first, or the short problem's with
+short_first).  The map is the
 host- and device-callable code of csrc/tile_map.h, compiled here for the host
 (no GPU involved)."""
 
@@ -23,6 +25,7 @@ int main() {
                        384, 576, 1000, 1536, 3072};
   int bad = 0, cases = 0;
   const int shapes[][2] = {{1, 0}, {1, 1}, {2, 3}, {72, 72}, {576, 576}, {0, 0}};
+  for (int sf = 0; sf < 2; ++sf)
   for (auto sh : shapes)
     for (int mult : {1, 3})
       for (int t2 : sizes) {
@@ -30,10 +33,11 @@ int main() {
         if (total == 0) continue;
         ++cases;
         const int t[3] = {t0, t1, t2};
-        const tpmlp::XcdSplit split = tpmlp::make_split(t0, t1, t2);
+        const tpmlp::XcdSplit split = tpmlp::make_split(t0, t1, t2, sf == 1);
         std::vector<std::vector<int>> seen(3);
         for (int p = 0; p < 3; ++p) seen[p].assign(t[p], 0);
         std::vector<int> lo(8, 1 << 30), hi(8, -1), n(8, 0), lo2(8, 1 << 30), hi2(8, -1), n2(8, 0);
+        std::vector<int> phase(8, 0);  // each XCD: first-kind tiles, then the other kind, never back
         for (int wg = 0; wg < total; ++wg) {
           int prob, tile;
           tpmlp::map_workgroup(split, t0, wg, prob, tile);
@@ -44,6 +48,9 @@ int main() {
             continue;
           }
           ++seen[prob][tile];
+          const bool first_kind = sf ? prob == 2 : prob < 2;
+          if (first_kind && phase[x]) ++bad;
+          if (!first_kind) phase[x] = 1;
           if (prob < 2) {  // index in the long group
             const int k = prob == 0 ? tile : t0 + tile;
             lo[x] = k < lo[x] ? k : lo[x]; hi[x] = k > hi[x] ? k : hi[x]; ++n[x];
