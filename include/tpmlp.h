@@ -493,21 +493,24 @@ int tpmlp_vocab_ce_bwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t
 /*
  * Tile width and schedule of the bf16 GEMMs, a tuning and testing knob
  * (process-wide; calls already enqueued are not affected).
- *   TPMLP_GEMM_TILE_AUTO (default): per launch, from its shapes, 256×192
- *     output tiles instead of 256×256 where they fill the GPU's 256 compute
- *     units in fewer rounds of tiles (one-kind launches with the plain, GeLU,
- *     GeLU' or bias epilogue that run without a K split; e.g. one shard of
- *     the 8.3B-shaped layer, n = 8192, m_i = 1536: 256 tiles instead of 192),
+ *   TPMLP_GEMM_TILE_AUTO (default): per launch, from its shapes, 256×192 or
+ *     256×128 output tiles instead of 256×256 where they fill the GPU's 256
+ *     compute units in fewer rounds of tiles (one-kind launches with the
+ *     plain, GeLU, GeLU' or bias epilogue that run without a K split; e.g.
+ *     one shard of the 8.3B-shaped layer, n = 8192, m_i = 1536: 256 tiles of
+ *     256×192 instead of 192; the single-shard layer's 2048×4096 products:
+ *     256 tiles of 256×128 instead of 128),
  *     or a K-split tail where a launch of one problem fills whole rounds and
  *     at most half of another (e.g. the GPT-1T-shaped shard's P = Y·B_i: 800
  *     tiles, 3 rounds and 32 more): each leftover tile runs as q equal K
  *     pieces (q·tiles ≤ 256) of fp32 partials in the workspace, added by a
  *     fix-up kernel in K order.
  *   TPMLP_GEMM_TILE_256: 256×256 tiles, no K-split tail.
- *   TPMLP_GEMM_TILE_192: 256×192 tiles wherever they are available.
+ *   TPMLP_GEMM_TILE_192, TPMLP_GEMM_TILE_128: 256×192 or 256×128 tiles
+ *     wherever they are available.
  *   TPMLP_GEMM_STREAMK: a K-split tail wherever it is available (the
  *     workspace queries then ask for its partial tiles, 256 KiB each).
- * 256×192 tiles give the same results as 256×256 bit for bit (each output
+ * Narrow tiles give the same results as 256×256 bit for bit (each output
  * element's K sum runs in the same order); a K-split tail adds the tail
  * tiles' K sums in q fp32 pieces (a different rounding, the same on every
  * run).  Returns TPMLP_OK, or TPMLP_ERR_ARG for another value.
@@ -516,6 +519,7 @@ int tpmlp_vocab_ce_bwd(hipStream_t stream, int dt, int64_t n, int64_t h, int64_t
 #define TPMLP_GEMM_TILE_256 1
 #define TPMLP_GEMM_TILE_192 2
 #define TPMLP_GEMM_STREAMK 3
+#define TPMLP_GEMM_TILE_128 4
 int tpmlp_set_gemm_tile_policy(int policy);
 int tpmlp_gemm_tile_policy(void);
 

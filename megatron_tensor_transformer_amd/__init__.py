@@ -403,8 +403,8 @@ def tpmlp_ln_sp(args, stream=None):
 
 
 # bf16 GEMM tile and schedule policy (process-wide): automatic, 256x256 only,
-# 256x192 wherever available, or a K-split tail wherever available
-GEMM_TILE_AUTO, GEMM_TILE_256, GEMM_TILE_192, GEMM_STREAMK = 0, 1, 2, 3
+# 256x192 / 256x128 tiles or a K-split tail wherever available
+GEMM_TILE_AUTO, GEMM_TILE_256, GEMM_TILE_192, GEMM_STREAMK, GEMM_TILE_128 = 0, 1, 2, 3, 4
 
 
 def set_gemm_tile_policy(policy):

@@ -160,12 +160,13 @@ extern "C" {
 int tpmlp_abi_version(void) { return TPMLP_ABI_VERSION; }
 
 static_assert(TPMLP_GEMM_TILE_AUTO == tpmlp::TILE_AUTO && TPMLP_GEMM_TILE_256 == tpmlp::TILE_256 &&
-                  TPMLP_GEMM_TILE_192 == tpmlp::TILE_192 && TPMLP_GEMM_STREAMK == tpmlp::TILE_STREAMK,
+                  TPMLP_GEMM_TILE_192 == tpmlp::TILE_192 && TPMLP_GEMM_STREAMK == tpmlp::TILE_STREAMK &&
+                  TPMLP_GEMM_TILE_128 == tpmlp::TILE_128,
               "tile policy values");
 
 int tpmlp_set_gemm_tile_policy(int policy) {
   if (policy != TPMLP_GEMM_TILE_AUTO && policy != TPMLP_GEMM_TILE_256 && policy != TPMLP_GEMM_TILE_192 &&
-      policy != TPMLP_GEMM_STREAMK)
+      policy != TPMLP_GEMM_STREAMK && policy != TPMLP_GEMM_TILE_128)
     return TPMLP_ERR_ARG;
   tpmlp::set_gemm_tile_policy(policy);
   return TPMLP_OK;

@@ -251,9 +251,13 @@ __device__ __forceinline__ void read_op(i32x4 (&fr)[NF], const uint32_t (&f)[4],
 __device__ __forceinline__ void wait_frags(i32x4 (&a)[FA], i32x4 (&b)[FB]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
 }
-// the same for the 256×192 tile's fragments (2 of A, 3 of B)
+// the same for the 256×192 tile's fragments (2 of A, 3 of B) and the
+// 256×128 tile's (2 and 2)
 __device__ __forceinline__ void wait_frags(i32x4 (&a)[2], i32x4 (&b)[3]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]));
+}
+__device__ __forceinline__ void wait_frags(i32x4 (&a)[2], i32x4 (&b)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]));
 }
 
 #define TPMLP_MFMA(ACC, BF, AF) \
@@ -294,11 +298,11 @@ struct StepCtx {
   int kremA, kremB, wave;
 };
 
-// The FA·FB MFMAs of slice S (8 for the 256×256 tile, 6 for 256×192).  After
-// MFMA Q come the next slice's reads Q and Q + FA·FB (for S = 3, slice 0 of
-// the next step, from its stages) and, at odd Q, one DMA load: in slice 1 of
-// A two steps ahead (a fourth A load of the 256×192 tile after MFMA 1 of
-// slice 2), in slice 3 of B two steps ahead.
+// The FA·FB MFMAs of slice S (8 for the 256×256 tile, 6 for 256×192, 4 for
+// 256×128).  After MFMA Q come the next slice's reads Q and Q + FA·FB (for
+// S = 3, slice 0 of the next step, from its stages) and, at odd Q, one DMA
+// load: of A two steps ahead in slice 1 (and, when slice 1 has fewer odd
+// slots than A has loads, in slice 2), of B two steps ahead in slice 3.
 template <int AO, int BO, int S, int FA_ = FA, int FB_ = FB, int NLB = NLOAD, int Q = 0>
 __device__ __forceinline__ void slice_body(f32x16 (&acc)[FA_][FB_], i32x4 (&ca)[FA_], i32x4 (&cb)[FB_],
                                            i32x4 (&na)[FA_], i32x4 (&nb)[FB_], const uint32_t (&pa)[4],
@@ -314,8 +318,8 @@ __device__ __forceinline__ void slice_body(f32x16 (&acc)[FA_][FB_], i32x4 (&ca)[
     if constexpr (S == 3 && Q + NQ < NR) next_read<AO, BO, 0, Q + NQ, FA_, FB_>(na, nb, pa, pb, s.nsa, s.nsb);
     if constexpr (S == 1 && (Q & 1) && (Q >> 1) < NLOAD)
       dma<AO, (Q >> 1)>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
-    if constexpr (S == 2 && NQ / 2 < NLOAD && Q == 1)
-      dma<AO, NQ / 2>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
+    if constexpr (S == 2 && (Q & 1) && NQ / 2 + (Q >> 1) < NLOAD)
+      dma<AO, NQ / 2 + (Q >> 1)>(s.rA, s.dA, la, s.koA, s.kremA, s.wave);
     if constexpr (S == 3 && (Q & 1) && (Q >> 1) < NLB)
       dma<BO, (Q >> 1), NLB>(s.rB, s.dB, lb, s.koB, s.kremB, s.wave);
     slice_body<AO, BO, S, FA_, FB_, NLB, Q + 1>(acc, ca, cb, na, nb, pa, pb, la, lb, s);
@@ -364,17 +368,19 @@ __device__ __forceinline__ uint32_t quad_addr(uint32_t qbase, int row, int chunk
   return qbase + row * QROW + (quad_slot(row, chunk) << 4) + half * 8;
 }
 
-// The 256×192 tile's epilogue (defined below).
-template <int EPI>
-__device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, int m0, int n0, TPMLP_LDS char* lds);
+// The 256×192 and 256×128 tiles' epilogue (defined below).
+template <int EPI, int TN>
+__device__ void epilogue_narrow(const KArgs& a, f32x16 (&acc)[2][TN / 64], int batch, int m0, int n0,
+                                TPMLP_LDS char* lds);
 
 // One output tile of problem a: 256×TN, TN = 256 (8 waves as 2×4, each 128×64:
-// 4×2 blocks) or TN = 192 (8 waves as 4×2, each 64×96: 2×3 blocks; its B
-// stage holds 192 rows and takes 3 DMA loads per wave).
+// 4×2 blocks), TN = 192 (8 waves as 4×2, each 64×96: 2×3 blocks; its B
+// stage holds 192 rows and takes 3 DMA loads per wave) or TN = 128 (4×2
+// waves of 64×64: 2×2 blocks; 2 B loads per wave).
 template <int AO, int BO, int EPI, int TN = BN>
 __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS char* lds) {
-  static_assert(TN == 256 || TN == 192, "tile width");
-  constexpr int FA_ = TN == 256 ? FA : 2, FB_ = TN == 256 ? FB : 3;
+  static_assert(TN == 256 || TN == 192 || TN == 128, "tile width");
+  constexpr int FA_ = TN == 256 ? FA : 2, FB_ = TN == 256 ? FB : TN / 64;
   constexpr int WN = TN / (32 * FB_);   // waves across N: 4 or 2
   constexpr int NLB = TN / 64;          // B loads per wave and stage: 4 or 3
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -463,8 +469,8 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // ------------------------------------------------------------------ epilogue
-  if constexpr (TN == 192) {
-    epilogue_n192<EPI>(a, acc, batch, m0, n0, lds);
+  if constexpr (TN != BN) {
+    epilogue_narrow<EPI, TN>(a, acc, batch, m0, n0, lds);
     return;
   } else {
   // Accumulator v of block (i, j) of lane L: row wm·128 + 32i + L%32,
@@ -760,26 +766,33 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, int tile, TPMLP_LDS ch
 }
 
 // ---------------------------------------------------------------------------
-// Epilogue of the 256×192 tile.  Each wave stages its 64×96 bf16 region in
-// LDS (rows of 256 B: chunk c of 8 columns of row r at 16-B slot c ^ (r % 16);
-// 16 KiB per wave), then all 8 waves store the whole 256×192 tile together:
-// a tile row is 384 B, three 128-B lines, and each wave-wide 16-B store
-// writes 8 whole lines.  Z and Y (the GeLU epilogues) take one pass each,
-// with a workgroup barrier before each pass's stores and after them.
-// Accumulator v of block (i, j) of lane L: row wm·64 + 32i + L%32, columns
-// wn·96 + 32j + 8·(v/4) + 4·(L/32) + v%4 (wm = wave / 2, wn = wave % 2).
-constexpr int N192_QROW = 256, N192_QBYTES = 64 * N192_QROW;
-static_assert(NWAVE * N192_QBYTES + NWAVE * 256 <= LDS_BYTES, "256x192 epilogue staging exceeds the LDS");
+// Epilogue of the 256×192 and 256×128 tiles.  Each wave stages its 64×(TN/2)
+// bf16 region in LDS (rows of 256 B: chunk c of 8 columns of row r at 16-B
+// slot c ^ (r % 16); 16 KiB per wave), then all 8 waves store the whole
+// 256×TN tile together: a tile row is 2·TN bytes (three or two 128-B lines),
+// and each wave-wide 16-B store writes 8 whole lines.  Z and Y (the GeLU
+// epilogues) take one pass each, with a workgroup barrier before each pass's
+// stores and after them.  Accumulator v of block (i, j) of lane L: row
+// wm·64 + 32i + L%32, columns wn·TN/2 + 32j + 8·(v/4) + 4·(L/32) + v%4
+// (wm = wave / 2, wn = wave % 2).
+constexpr int NARROW_QROW = 256, NARROW_QBYTES = 64 * NARROW_QROW;
+static_assert(NWAVE * NARROW_QBYTES + NWAVE * 256 <= LDS_BYTES, "narrow-tile epilogue staging exceeds the LDS");
 
-__device__ __forceinline__ uint32_t n192_addr(uint32_t qbase, int row, int chunk) {
-  return qbase + row * N192_QROW + ((chunk ^ (row & 15)) << 4);
+__device__ __forceinline__ uint32_t narrow_addr(uint32_t qbase, int row, int chunk) {
+  return qbase + row * NARROW_QROW + ((chunk ^ (row & 15)) << 4);
 }
 
-template <int EPI>
-__device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, int m0, int n0, TPMLP_LDS char* lds) {
+template <int EPI, int TN>
+__device__ void epilogue_narrow(const KArgs& a, f32x16 (&acc)[2][TN / 64], int batch, int m0, int n0,
+                                TPMLP_LDS char* lds) {
+  static_assert(TN == 192 || TN == 128, "narrow tile width");
   static_assert(EPI == EPI_STORE || EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE ||
                     EPI == EPI_GELU_GRAD,
-                "epilogue not available for the 256x192 tile");
+                "epilogue not available for the narrow tiles");
+  constexpr int NJ = TN / 64;        // 32-column blocks per wave
+  constexpr int CH = TN / 16;        // 16-B chunks per region row
+  constexpr int TCH = TN / 8;        // 16-B chunks per tile row
+  constexpr int ITER = 256 * TCH / NTHR;  // chunks stored per thread
   constexpr bool ZY = EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY;
   constexpr bool BIAS = EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE;
   constexpr bool GG = EPI == EPI_GELU_GRAD;
@@ -788,15 +801,15 @@ __device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, in
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int row_l = lane & 31, half = lane >> 5;
-  const uint32_t qbase = lds_base + wave * N192_QBYTES;
+  const uint32_t qbase = lds_base + wave * NARROW_QBYTES;
   const int64_t cbase = static_cast<int64_t>(batch) * a.sC;
-  const int qm0 = m0 + wm * 64, qn0 = n0 + wn * 96;
+  const int qm0 = m0 + wm * 64, qn0 = n0 + wn * (TN / 2);
   block_barrier();  // every wave is done with the main-loop stages
 
-  // column bias: the wave's 96 values, staged past the staging regions
-  const uint32_t bbase = lds_base + NWAVE * N192_QBYTES + wave * 256;
+  // column bias: the wave's TN/2 values, staged past the staging regions
+  const uint32_t bbase = lds_base + NWAVE * NARROW_QBYTES + wave * 256;
   if constexpr (BIAS) {
-    if (lane < 24) {
+    if (lane < TN / 8) {
       const int col = qn0 + lane * 4;
       const bf16* bias = a.bias + static_cast<int64_t>(batch) * a.sBias;
       const i32x2 b = col < a.N ? *reinterpret_cast<const i32x2*>(bias + col) : i32x2{0, 0};
@@ -813,10 +826,10 @@ __device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, in
       const int row = j * 4 + (lane >> 4);
       const int c = (lane & 15) ^ (row & 15);
       const int gr = qm0 + row, gc = qn0 + c * 8;
-      const uint32_t voff = (c < 12 && gr < a.M && gc < a.N)
+      const uint32_t voff = (c < CH && gr < a.M && gc < a.N)
                                 ? static_cast<uint32_t>((static_cast<int64_t>(gr) * a.ldc + gc) * 2)
                                 : OOB;
-      buffer_load_lds16(rZ, lds + wave * N192_QBYTES + j * 1024, voff);
+      buffer_load_lds16(rZ, lds + wave * NARROW_QBYTES + j * 1024, voff);
     }
     wait_vmcnt<0>();
   }
@@ -827,7 +840,7 @@ __device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, in
     for (int i = 0; i < 2; ++i) {
       const int row = i * 32 + row_l;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         i32x2 zr[4];
         if constexpr (BIAS) {
 #pragma unroll
@@ -838,7 +851,7 @@ __device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, in
         if constexpr (GG) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            asm volatile("ds_read_b64 %0, %1" : "=v"(zr[q]) : "v"(n192_addr(qbase, row, j * 4 + q) + half * 8));
+            asm volatile("ds_read_b64 %0, %1" : "=v"(zr[q]) : "v"(narrow_addr(qbase, row, j * 4 + q) + half * 8));
           asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(zr[0]), "+v"(zr[1]), "+v"(zr[2]), "+v"(zr[3])::"memory");
         }
         float v[16];
@@ -868,33 +881,33 @@ __device__ void epilogue_n192(const KArgs& a, f32x16 (&acc)[2][3], int batch, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const i32x2 pk = pack4_bf16(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-          asm volatile("ds_write_b64 %0, %1" ::"v"(n192_addr(qbase, row, j * 4 + q) + half * 8), "v"(pk)
+          asm volatile("ds_write_b64 %0, %1" ::"v"(narrow_addr(qbase, row, j * 4 + q) + half * 8), "v"(pk)
                        : "memory");
         }
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     block_barrier();  // every region of this pass is staged
-    // the tile: 256 rows × 24 chunks, 12 per thread; thread t, round it:
+    // the tile: 256 rows × TCH chunks, ITER per thread; thread t, round it:
     // chunk it·512 + t in row-major order
     bf16* C = static_cast<bf16*>(pass == 0 ? a.C : a.C2) + cbase;
 #pragma unroll
-    for (int it0 = 0; it0 < 12; it0 += 6) {
-      i32x4 w[6];
+    for (int it0 = 0; it0 < ITER; it0 += ITER / 2) {
+      i32x4 w[ITER / 2];
 #pragma unroll
-      for (int u = 0; u < 6; ++u) {
+      for (int u = 0; u < ITER / 2; ++u) {
         const int flat = (it0 + u) * NTHR + static_cast<int>(threadIdx.x);
-        const int R = flat / 24, c = flat - R * 24;
-        const int rw = (R >> 6) * 2 + (c >= 12 ? 1 : 0), rr = R & 63, cc = c >= 12 ? c - 12 : c;
-        const uint32_t ad = n192_addr(lds_base + rw * N192_QBYTES, rr, cc);
+        const int R = flat / TCH, c = flat - R * TCH;
+        const int rw = (R >> 6) * 2 + (c >= CH ? 1 : 0), rr = R & 63, cc = c >= CH ? c - CH : c;
+        const uint32_t ad = narrow_addr(lds_base + rw * NARROW_QBYTES, rr, cc);
         asm volatile("ds_read_b128 %0, %1" : "=v"(w[u]) : "v"(ad) : "memory");
       }
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5])::"memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int u = 0; u < 6; ++u) {
+      for (int u = 0; u < ITER / 2; ++u) {
+        asm volatile("" : "+v"(w[u]));
         const int flat = (it0 + u) * NTHR + static_cast<int>(threadIdx.x);
-        const int R = flat / 24, c = flat - R * 24;
+        const int R = flat / TCH, c = flat - R * TCH;
         const int gr = m0 + R, gc = n0 + c * 8;
         if (gr < a.M && gc < a.N)
           __builtin_nontemporal_store(w[u], reinterpret_cast<i32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc));
@@ -1237,7 +1250,7 @@ double out_bytes(const GemmKind& k) {
 // written and read plus the outputs at kFixBytesPerStep.
 void plan_stream_k(SplitPlan& pl, const GemmProblem* const (&pr)[3], const GemmKind* const (&kd)[3], int policy) {
   pl.sk_slot = -1;
-  if (policy == TILE_256 || policy == TILE_192) return;
+  if (policy == TILE_256 || policy == TILE_192 || policy == TILE_128) return;
   int live = -1, nlive = 0;
   for (int i = 0; i < 3; ++i)
     if (pr[i] != nullptr && !empty(*pr[i])) {
@@ -1373,12 +1386,33 @@ hipError_t fixup(const GemmProblem& p, int epi, const float* part, int S, hipStr
 // (P = Y·B_i, 24 steps, two rounds each), i.e. 0.9 of a step per step.  Only
 // shapes decide, so a call is reproducible.
 constexpr double k192StepFrac = 0.9, k192FixedSteps = 3.5;
+// 256×128 tiles: half the MFMA work and 3/4 of the operand bytes per step.
+// Measured on the single-shard layer's Z = X·A and dgrad-1 (2048×4096
+// outputs, 16 K steps; 256 tiles of 256×128 against 176 of 256×192, one round
+// each): 23.4 and 25.0 µs against 27.3 and 27.4 µs, i.e. about 0.85 of the
+// 256×192 round, which the constants reproduce.
+constexpr double k128StepFrac = 0.8, k128FixedSteps = 3.0;
 
 bool n192_kind(const GemmKind& k) {
   if (k.a_order != KMAJ) return false;
   if (k.b_order == MNMAJ)
     return k.epi == EPI_STORE || k.epi == EPI_GELU_ZY || k.epi == EPI_BIAS_GELU_ZY || k.epi == EPI_BIAS_STORE;
   return k.epi == EPI_STORE || k.epi == EPI_GELU_GRAD;
+}
+
+// A launch of 256×TN tiles (TN = 192 or 128) of one kind.
+template <int TN>
+hipError_t launch_narrow(const KGroup& g, const GemmKind& k, hipStream_t stream) {
+  auto is = [&](int ao, int bo, int epi) { return k.a_order == ao && k.b_order == bo && k.epi == epi; };
+  if (is(KMAJ, MNMAJ, EPI_GELU_ZY)) return launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY, TN>(g, stream);
+  if (is(KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
+    return launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, TN>(g, stream);
+  if (is(KMAJ, MNMAJ, EPI_STORE)) return launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE, TN>(g, stream);
+  if (is(KMAJ, MNMAJ, EPI_BIAS_STORE))
+    return launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_BIAS_STORE, TN>(g, stream);
+  if (is(KMAJ, KMAJ, EPI_GELU_GRAD)) return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD, TN>(g, stream);
+  if (is(KMAJ, KMAJ, EPI_STORE)) return launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE, TN>(g, stream);
+  return hipErrorInvalidValue;
 }
 
 // A launch planned with a K-split tail: the first sk_first tiles as whole
@@ -1496,18 +1530,24 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
   const int policy = g_tile_policy.load(std::memory_order_relaxed);
   if (policy != TILE_256 && same && n192_kind(k0) && plan.s[0] <= 1 && plan.s[1] <= 1 &&
       plan.s[2] <= 1) {
-    int64_t T256 = 0, T192 = 0;
+    int64_t T256 = 0, T192 = 0, T128 = 0;
     int ks = 0;
     for (int i = 0; i < 3; ++i) {
       if (slot[i] == nullptr || empty(sp[i]) || (i == 2 && !has_short) || (i < 2 && i >= nlong)) continue;
       T256 += tiles_of(sp[i]);
       T192 += tiles_of(sp[i], 192);
+      T128 += tiles_of(sp[i], 128);
       const int k = (sp[i].K + BK - 1) / BK;
       ks = k > ks ? k : ks;
     }
-    const double r256 = static_cast<double>((T256 + kCUs - 1) / kCUs), r192 = static_cast<double>((T192 + kCUs - 1) / kCUs);
-    const double c256 = r256 * (ks + kTileFixedSteps), c192 = r192 * (k192StepFrac * ks + k192FixedSteps);
-    if (policy == TILE_192 || c192 < 0.95 * c256) tn = 192;
+    auto rounds = [](int64_t T) { return static_cast<double>((T + kCUs - 1) / kCUs); };
+    const double c256 = rounds(T256) * (ks + kTileFixedSteps);
+    const double c192 = rounds(T192) * (k192StepFrac * ks + k192FixedSteps);
+    const double c128 = rounds(T128) * (k128StepFrac * ks + k128FixedSteps);
+    if (policy == TILE_192) tn = 192;
+    else if (policy == TILE_128) tn = 128;
+    else if (c192 < 0.95 * c256 && c192 <= c128) tn = 192;
+    else if (c128 < 0.95 * c256) tn = 128;
   }
   const int64_t t0 = nl > 0 ? tiles_of(*lp[0], tn) * plan.s[li[0]] : 0;
   const int64_t t1 = nl > 1 ? tiles_of(*lp[1], tn) * plan.s[li[1]] : 0;
@@ -1538,21 +1578,8 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
   const bool short_first = nl > 0 && has_short && steps(g.p[2]) > steps(g.p[0]);
   g.split = make_split(g.t0, g.t1, g.t2, short_first);
   hipError_t e = hipErrorInvalidValue;
-  if (tn == 192) {
-    if (is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
-      e = launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY, 192>(g, stream);
-    else if (is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
-      e = launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, 192>(g, stream);
-    else if (is(k0, KMAJ, MNMAJ, EPI_STORE))
-      e = launch_t<KMAJ, MNMAJ, EPI_STORE, KMAJ, MNMAJ, EPI_STORE, 192>(g, stream);
-    else if (is(k0, KMAJ, MNMAJ, EPI_BIAS_STORE))
-      e = launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_BIAS_STORE, 192>(g, stream);
-    else if (is(k0, KMAJ, KMAJ, EPI_GELU_GRAD))
-      e = launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD, 192>(g, stream);
-    else if (is(k0, KMAJ, KMAJ, EPI_STORE))
-      e = launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE, 192>(g, stream);
-    return e;  // never K-split: no fix-up
-  }
+  if (tn == 192) return launch_narrow<192>(g, k0, stream);  // narrow tiles are never K-split: no fix-up
+  if (tn == 128) return launch_narrow<128>(g, k0, stream);
   if (same && is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
     e = launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
   else if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))

@@ -62,14 +62,14 @@ struct GemmKind {
 // that would leave the machine idle run K-split (fp32 partials in ws, then a
 // fix-up kernel per split problem); with less (or none), nothing is split.
 // The bf16 GEMM's tile and schedule policy (process-wide): TILE_AUTO picks
-// 256×192 tiles or a K-split tail where a cost model of CU rounds favours
-// them; TILE_256 uses neither; TILE_192 takes 256×192 tiles wherever they are
-// available (launches of one kind with the plain, GeLU, bias or GeLU'
-// epilogue that run unsplit); TILE_STREAMK takes a K-split tail wherever it
+// 256×192 or 256×128 tiles or a K-split tail where a cost model of CU rounds
+// favours them; TILE_256 uses none of them; TILE_192 and TILE_128 take
+// 256×192 or 256×128 tiles wherever they are available (launches of one kind
+// with the plain, GeLU, bias or GeLU' epilogue that run unsplit); TILE_STREAMK takes a K-split tail wherever it
 // is available (launches of one problem, not fp32-output, whose 256×256 tiles
 // fill at least one whole round of the CUs and at most half of another) and
 // the workspace allows.
-enum TilePolicy { TILE_AUTO = 0, TILE_256 = 1, TILE_192 = 2, TILE_STREAMK = 3 };
+enum TilePolicy { TILE_AUTO = 0, TILE_256 = 1, TILE_192 = 2, TILE_STREAMK = 3, TILE_128 = 4 };
 void set_gemm_tile_policy(int policy);
 int gemm_tile_policy();
 

@@ -340,10 +340,10 @@ def test_sp_args_layout_matches_header(tmp_path):
 def test_gemm_tile_policy_knob(L):
     # host-only state: set, read back, reject other values, restore
     assert tp.gemm_tile_policy() == tp.GEMM_TILE_AUTO
-    for p in (tp.GEMM_TILE_256, tp.GEMM_TILE_192, tp.GEMM_STREAMK, tp.GEMM_TILE_AUTO):
+    for p in (tp.GEMM_TILE_256, tp.GEMM_TILE_192, tp.GEMM_STREAMK, tp.GEMM_TILE_128, tp.GEMM_TILE_AUTO):
         tp.set_gemm_tile_policy(p)
         assert tp.gemm_tile_policy() == p
-    for bad in (-1, 4, 192):
+    for bad in (-1, 5, 192):
         assert L.tpmlp_set_gemm_tile_policy(bad) == tp.ERR_ARG
     assert tp.gemm_tile_policy() == tp.GEMM_TILE_AUTO
 

@@ -1,12 +1,14 @@
-"""The bf16 GEMMs' 256×192 output tiles (tpmlp_set_gemm_tile_policy).
+"""The bf16 GEMMs' narrow output tiles, 256×192 and 256×128
+(tpmlp_set_gemm_tile_policy).
 
 Each output element's K sum runs in the same order with either tile width,
 so every result must equal the 256×256 tiles' bit for bit; the small shapes
 are also compared with the fp64 oracle.  Shapes have ragged edges in every
-dimension (M not a multiple of 256, N not a multiple of 192 or 8·24, K not a
+dimension (M not a multiple of 256, N not a multiple of 192 or 128, K not a
 multiple of 64) and include one shard of the 8.3B-shaped layer (n = 8192,
 d = 3072, m_i = 1536), where the automatic policy picks 256×192 for the
-forward GEMMs and dgrad-1.
+forward GEMMs and dgrad-1, and the single-shard layer (n = 2048, d = 1024,
+m = 4096), where it picks 256×128 for Z = X·A and dgrad-1.
 """
 
 import numpy as np
@@ -22,7 +24,7 @@ from gpu_util import dev, relerr, run_step, say, shard_cols, shard_rows
 
 pytestmark = pytest.mark.gpu
 
-POLICIES = (tp.GEMM_TILE_256, tp.GEMM_TILE_192, tp.GEMM_TILE_AUTO)
+POLICIES = (tp.GEMM_TILE_256, tp.GEMM_TILE_192, tp.GEMM_TILE_128, tp.GEMM_TILE_AUTO)
 
 
 @pytest.fixture(autouse=True)
@@ -48,7 +50,8 @@ def same_bits(a, b, name):
     (300, 264, 528, 2),      # N of GEMM1 = 264: one full and one 72-wide tile of 192
     (520, 392, 776, 1),      # K = 392 (6 steps + 8), N = 776 and 392
     (17, 1000, 2000, 2),     # a single ragged row block, K = 1000
-    (8192, 3072, 1536, 1),   # one shard of the 8.3B-shaped layer
+    (8192, 3072, 1536, 1),   # one shard of the 8.3B-shaped layer (256x192 tiles chosen)
+    (2048, 1024, 4096, 1),   # the single-shard layer (256x128 tiles chosen for GEMM1 and dgrad-1)
 ])
 def test_step_is_bit_identical_across_tile_widths(n, d, m, t):
     inp = mlp_inputs(n, d, m, t, dtype="bf16", seed=31)
@@ -87,12 +90,13 @@ def test_biased_forward_is_bit_identical_across_tile_widths(n, d, m, t):
     A_s, B_s = shard_cols(A, t), shard_rows(B, t)
     b1 = dev(bias["b1"]).reshape(t, m // t).contiguous()
     out = {}
-    for p in POLICIES[:2]:
+    for p in POLICIES[:3]:
         tp.set_gemm_tile_policy(p)
         out[p] = tp.mlp_fwd_bias(X, A_s, B_s, b1)
         torch.cuda.synchronize()
-    for name, a, b in zip("ZYP", out[POLICIES[0]], out[POLICIES[1]]):
-        same_bits(a, b, name)
+    for p in POLICIES[1:3]:
+        for name, a, b in zip("ZYP", out[POLICIES[0]], out[p]):
+            same_bits(a, b, f"{name} (policy {p})")
     fwd = om.tp_forward(inp["X"].f64, inp["A"].f64, inp["B"].f64, t, b1=bias["b1"].f64)
     Z, Y, P = out[tp.GEMM_TILE_192]
     for i in range(t):
@@ -112,12 +116,13 @@ def test_attention_layer_is_bit_identical_across_tile_widths(bias):
     Wq_s, Wp_s = shard_cols(Wq, t), shard_rows(Wp, t)
     bq = dev(inp["bqkv"]).reshape(t, 3 * d // t).contiguous() if bias else None
     out = {}
-    for p in POLICIES[:2]:
+    for p in POLICIES[:3]:
         tp.set_gemm_tile_policy(p)
         out[p] = tp.attn_fwd(X, Wq_s, Wp_s, s, b, d // heads, True, bqkv=bq)
         torch.cuda.synchronize()
-    for name, a, c in zip(("QKV", "O", "lse", "P"), out[POLICIES[0]], out[POLICIES[1]]):
-        same_bits(a, c, name)
+    for p in POLICIES[1:3]:
+        for name, a, c in zip(("QKV", "O", "lse", "P"), out[POLICIES[0]], out[p]):
+            same_bits(a, c, f"{name} (policy {p})")
     L = {k: v.f64 for k, v in inp.items()}
     f = oa.tp_forward(L["X"], L["Wqkv"], L["Wproj"], t, s, b, heads, True,
                       bqkv=L["bqkv"] if bias else None)
