@@ -45,6 +45,9 @@ LEGS = ("biased_step", "per_rank", "c2", "gpt1t_shard", "sp_region", "c5_block",
         "fp32_path")
 
 
+TILE_POLICIES = {"auto": 0, "256": 1, "192": 2, "tail": 3, "128": 4}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +63,11 @@ def parse():
                     help="also time the oracle once on every configuration (3x4 worked example, the "
                          "single-shard layer, the 8.3B-shaped layer, the GPT-1T-shaped shard, the h=4096 "
                          "sequence-parallel block); about a minute of host time")
+    ap.add_argument("--gemm-tile-policy", choices=sorted(TILE_POLICIES), default="auto",
+                    help="the bf16 GEMMs' tile and schedule policy (tpmlp_set_gemm_tile_policy): auto (the "
+                         "library's choice per launch), 256 (256x256 tiles only, no K-split tail), 192 or 128 "
+                         "(narrow tiles wherever available), tail (a K-split tail wherever available); for A/B "
+                         "timing, the results do not depend on it beyond the tail's fp32 rounding")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 512 MiB (read 512 MiB, write 512 MiB), "
                          "the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -761,6 +769,7 @@ def main():
     cfg = CONFIGS[WORKLOAD]
     n, d, m, t = cfg["n"], cfg["d"], cfg["m"], cfg["t"]
     mi = m // t
+    tp.set_gemm_tile_policy(TILE_POLICIES[args.gemm_tile_policy])
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     inp = config_inputs(WORKLOAD, seed=0)
@@ -858,7 +867,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, N(0,1e-4) grads)",
         "config": {"workload": "GPT-8.3B-shaped TP-MLP layer, h=3072, m=4h=12288, t=8 shards "
                                "resident on one GPU (A_i 3072x1536, B_i 1536x3072), n=b*s=8*1024",
-                   "n": n, "d": d, "m": m, "t": t, "m_i": mi, "parallelism": "tp8 simulated on 1 GPU"},
+                   "n": n, "d": d, "m": m, "t": t, "m_i": mi, "parallelism": "tp8 simulated on 1 GPU",
+                   "gemm_tile_policy": args.gemm_tile_policy},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "gemm_only": {"tflops": round(gemm_tflops, 2),
                       "pct_of_peak": round(100.0 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
