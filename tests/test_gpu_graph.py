@@ -50,11 +50,25 @@ def _step(X, A, B, G, o):
     tp.tpmlp_reduce_partials(o["dXp"], o["dX"])
 
 
-@pytest.mark.parametrize("dtype,n,d,m,t", [("bf16", 520, 264, 512, 4), ("f32", 130, 72, 96, 3),
-                                           # K-split products (the fix-up kernels are captured too)
-                                           ("bf16", 256, 2048, 512, 1)])
-def test_step_graph_replays_match_eager(dtype, n, d, m, t):
-    say(f"[gpu] graph capture {dtype} n={n} d={d} m={m} t={t}")
+@pytest.mark.parametrize("dtype,n,d,m,t,policy", [
+    ("bf16", 520, 264, 512, 4, tp.GEMM_TILE_AUTO), ("f32", 130, 72, 96, 3, tp.GEMM_TILE_AUTO),
+    # K-split products (the fix-up kernels are captured too)
+    ("bf16", 256, 2048, 512, 1, tp.GEMM_TILE_AUTO),
+    # the single-shard layer: 256x128 tiles for GEMM1 and dgrad-1, K-split P = Y·B
+    ("bf16", 2048, 1024, 4096, 1, tp.GEMM_TILE_AUTO),
+    # a K-split tail (16 tail tiles in 4 pieces) for GEMM1 and dgrad-1
+    ("bf16", 4352, 256, 4096, 1, tp.GEMM_STREAMK),
+])
+def test_step_graph_replays_match_eager(dtype, n, d, m, t, policy):
+    say(f"[gpu] graph capture {dtype} n={n} d={d} m={m} t={t} policy={policy}")
+    tp.set_gemm_tile_policy(policy)
+    try:
+        _graph_step(dtype, n, d, m, t)
+    finally:
+        tp.set_gemm_tile_policy(tp.GEMM_TILE_AUTO)
+
+
+def _graph_step(dtype, n, d, m, t):
     sets = []
     for seed in (21, 22, 23):
         inp = mlp_inputs(n, d, m, t, dtype=dtype, seed=seed)
