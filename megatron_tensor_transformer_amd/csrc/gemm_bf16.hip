@@ -782,13 +782,74 @@ __device__ __forceinline__ uint32_t narrow_addr(uint32_t qbase, int row, int chu
   return qbase + row * NARROW_QROW + ((chunk ^ (row & 15)) << 4);
 }
 
+// fp32 results of the 256×128 tile (the K-split's partial planes): each
+// wave stages its 64×64 fp32 region (rows of 256 B, 16-B chunk c of 4 floats
+// at slot c ^ (row % 16)), then the 8 waves store the 256×128 tile together,
+// 8 whole 128-B lines per wave-wide store.
+__device__ void epilogue_narrow_f32(const KArgs& a, f32x16 (&acc)[2][2], int batch, int m0, int n0,
+                                   TPMLP_LDS char* lds) {
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row_l = lane & 31, half = lane >> 5;
+  const uint32_t qbase = lds_base + wave * NARROW_QBYTES;
+  block_barrier();  // every wave is done with the main-loop stages
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = i * 32 + row_l;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[i][j][e]));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = v[4 * q + e];
+        // columns 32j + 8q + 4·half .. +3: chunk 8j + 2q + half of the region row
+        asm volatile("ds_write_b128 %0, %1" ::"v"(narrow_addr(qbase, row, 8 * j + 2 * q + half)), "v"(w)
+                     : "memory");
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  block_barrier();  // every region is staged
+  // the tile: 256 rows × 32 chunks of 4 floats, 16 per thread
+  float* C = static_cast<float*>(a.C) + static_cast<int64_t>(batch) * a.sC;
+#pragma unroll
+  for (int it0 = 0; it0 < 16; it0 += 8) {
+    f32x4 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int flat = (it0 + u) * NTHR + static_cast<int>(threadIdx.x);
+      const int R = flat >> 5, c = flat & 31;
+      const int rw = (R >> 6) * 2 + (c >> 4), rr = R & 63, cc = c & 15;
+      asm volatile("ds_read_b128 %0, %1" : "=v"(w[u]) : "v"(narrow_addr(lds_base + rw * NARROW_QBYTES, rr, cc))
+                   : "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      asm volatile("" : "+v"(w[u]));
+      const int flat = (it0 + u) * NTHR + static_cast<int>(threadIdx.x);
+      const int R = flat >> 5, c = flat & 31;
+      const int gr = m0 + R, gc = n0 + c * 4;
+      if (gr < a.M && gc < a.N) *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(gr) * a.ldc + gc) = w[u];
+    }
+  }
+}
+
 template <int EPI, int TN>
 __device__ void epilogue_narrow(const KArgs& a, f32x16 (&acc)[2][TN / 64], int batch, int m0, int n0,
                                 TPMLP_LDS char* lds) {
   static_assert(TN == 192 || TN == 128, "narrow tile width");
   static_assert(EPI == EPI_STORE || EPI == EPI_GELU_ZY || EPI == EPI_BIAS_GELU_ZY || EPI == EPI_BIAS_STORE ||
-                    EPI == EPI_GELU_GRAD,
+                    EPI == EPI_GELU_GRAD || (EPI == EPI_STORE_F32 && TN == 128),
                 "epilogue not available for the narrow tiles");
+  if constexpr (EPI == EPI_STORE_F32) {
+    epilogue_narrow_f32(a, acc, batch, m0, n0, lds);
+    return;
+  } else {
   constexpr int NJ = TN / 64;        // 32-column blocks per wave
   constexpr int CH = TN / 16;        // 16-B chunks per region row
   constexpr int TCH = TN / 8;        // 16-B chunks per tile row
@@ -915,6 +976,7 @@ __device__ void epilogue_narrow(const KArgs& a, f32x16 (&acc)[2][TN / 64], int b
     }
     if (pass + 1 < PASSES) block_barrier();  // the staging regions are read before the next pass writes them
   }
+  }  // not fp32
 }
 
 // The launch: problems 0 and 1 are of kind (AO0, BO0, EPI0), problem 2 of
@@ -986,9 +1048,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(KGroup g) {
   int prob, tile;
   map_workgroup(g.split, g.t0, blockIdx.x, prob, tile);
   if constexpr (TN != BN) {
-    // the 256×192 tile: launches of one kind, never K-split
-    static_assert(AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1, "one kind per 256x192 launch");
+    // narrow tiles: launches of one kind (fp32: a K-split's slices)
+    static_assert(AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1, "one kind per narrow-tile launch");
     KArgs a = g.p[prob];
+    if constexpr (EPI0 == EPI_STORE_F32) select_slice<AO0, BO0>(a, tile);
     gemm_tile<AO0, BO0, EPI0, TN>(a, tile, lds);
   } else if constexpr (AO0 == AO1 && BO0 == BO1 && EPI0 == EPI1) {
     KArgs a = g.p[prob];  // one copy: wide scalar loads at the problem's offset
@@ -1412,6 +1475,12 @@ hipError_t launch_narrow(const KGroup& g, const GemmKind& k, hipStream_t stream)
     return launch_t<KMAJ, MNMAJ, EPI_BIAS_STORE, KMAJ, MNMAJ, EPI_BIAS_STORE, TN>(g, stream);
   if (is(KMAJ, KMAJ, EPI_GELU_GRAD)) return launch_t<KMAJ, KMAJ, EPI_GELU_GRAD, KMAJ, KMAJ, EPI_GELU_GRAD, TN>(g, stream);
   if (is(KMAJ, KMAJ, EPI_STORE)) return launch_t<KMAJ, KMAJ, EPI_STORE, KMAJ, KMAJ, EPI_STORE, TN>(g, stream);
+  if constexpr (TN == 128) {
+    if (is(KMAJ, MNMAJ, EPI_STORE_F32))
+      return launch_t<KMAJ, MNMAJ, EPI_STORE_F32, KMAJ, MNMAJ, EPI_STORE_F32, TN>(g, stream);
+    if (is(KMAJ, KMAJ, EPI_STORE_F32))
+      return launch_t<KMAJ, KMAJ, EPI_STORE_F32, KMAJ, KMAJ, EPI_STORE_F32, TN>(g, stream);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -1548,6 +1617,20 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
     else if (policy == TILE_128) tn = 128;
     else if (c192 < 0.95 * c256 && c192 <= c128) tn = 192;
     else if (c128 < 0.95 * c256) tn = 128;
+  } else if (policy != TILE_256 && policy != TILE_192 && same && k0.epi == EPI_STORE_F32 && k0.a_order == KMAJ &&
+             nl + (has_short ? 1 : 0) == 1) {
+    // one K-split problem (its slices are fp32 stores): 256×128 tiles when
+    // its slices leave the CUs partly idle (the single-shard layer's P = Y·B:
+    // 32 tiles × 4 slices of 256×256, 64 × 4 of 256×128)
+    const int i = nl > 0 ? li[0] : 2;
+    const int S = plan.s[i];
+    if (S > 1) {
+      const int steps = ((sp[i].K + BK - 1) / BK + S - 1) / S;
+      auto rounds = [](int64_t T) { return static_cast<double>((T + kCUs - 1) / kCUs); };
+      const double c256 = rounds(tiles_of(sp[i]) * S) * (steps + kTileFixedSteps);
+      const double c128 = rounds(tiles_of(sp[i], 128) * S) * (k128StepFrac * steps + k128FixedSteps);
+      if (policy == TILE_128 || c128 < 0.95 * c256) tn = 128;
+    }
   }
   const int64_t t0 = nl > 0 ? tiles_of(*lp[0], tn) * plan.s[li[0]] : 0;
   const int64_t t1 = nl > 1 ? tiles_of(*lp[1], tn) * plan.s[li[1]] : 0;
@@ -1578,9 +1661,11 @@ hipError_t launch_gemm_bf16_group(const GemmProblem* longp, int nlong, const Gem
   const bool short_first = nl > 0 && has_short && steps(g.p[2]) > steps(g.p[0]);
   g.split = make_split(g.t0, g.t1, g.t2, short_first);
   hipError_t e = hipErrorInvalidValue;
-  if (tn == 192) return launch_narrow<192>(g, k0, stream);  // narrow tiles are never K-split: no fix-up
-  if (tn == 128) return launch_narrow<128>(g, k0, stream);
-  if (same && is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
+  if (tn == 192)
+    e = launch_narrow<192>(g, k0, stream);
+  else if (tn == 128)
+    e = launch_narrow<128>(g, k0, stream);  // (its fp32 kind: a K-split's slices, fixed up below)
+  else if (same && is(k0, KMAJ, MNMAJ, EPI_GELU_ZY))
     e = launch_t<KMAJ, MNMAJ, EPI_GELU_ZY, KMAJ, MNMAJ, EPI_GELU_ZY>(g, stream);
   else if (same && is(k0, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY))
     e = launch_t<KMAJ, MNMAJ, EPI_BIAS_GELU_ZY, KMAJ, MNMAJ, EPI_BIAS_GELU_ZY>(g, stream);
