@@ -90,13 +90,19 @@ def test_core_bf16(T, s, b, nh, dh, causal):
     compare_core(T, s, b, nh, dh, causal, "bf16")
 
 
+@pytest.mark.parametrize("T,s,b,nh,dh", [
+    (1, 320, 2, 2, 128),
+    (1, 384, 1, 3, 128),   # six key tiles, three workgroups of keys, three heads
+    (2, 200, 2, 1, 128),   # ragged: the last key tile holds 8 keys
+    (1, 384, 2, 2, 64),
+])
 @pytest.mark.parametrize("causal", [True, False])
-def test_core_bf16_growing_logits(causal):
+def test_core_bf16_growing_logits(causal, T, s, b, nh, dh):
     """Keys scaled by 2^⌊j/64⌋ (exact in bf16): every key tile doubles the
     logits' spread, so the row maxima grow by less than the forward's rescale
     threshold on the early tiles (P well above 1 against a stale reference)
-    and by more on the later ones (the reference moves mid-row)."""
-    T, s, b, nh, dh = 1, 320, 2, 2, 128
+    and by more on the later ones (the reference moves mid-row); the
+    backward's P and dS are then concentrated on few keys per row."""
     inp = qkv_inputs(T, s, b, nh, dh, dtype="bf16", seed=8)
     x = inp["qkv"].f32.reshape(T, s, b, nh, 3, dh).copy()
     x[:, :, :, :, 1, :] *= (2.0 ** (np.arange(s) // 64)).astype(np.float32)[None, :, None, None, None]
