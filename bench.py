@@ -43,6 +43,7 @@ METRIC = "TP-MLP shard fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
 WORKLOAD = "gpt8p3b_t8"
 LEGS = ("biased_step", "per_rank", "c2", "gpt1t_shard", "sp_region", "c5_block", "attention", "vocab_ce",
         "fp32_path")
+OPTIONAL_LEGS = ("library_yardsticks",)  # only when named in --legs
 
 
 TILE_POLICIES = {"auto": 0, "256": 1, "192": 2, "tail": 3, "128": 4}
@@ -56,7 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip every leg besides the headline step")
     ap.add_argument("--legs", default=None,
-                    help="comma-separated subset of the extra legs to run (default: all): " + ",".join(LEGS))
+                    help="comma-separated subset of the extra legs to run (default: all of " + ",".join(LEGS)
+                    + "); also " + ",".join(OPTIONAL_LEGS) + " (library kernels on the same shapes, as context)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--cpu-all-configs", action="store_true",
@@ -668,6 +670,104 @@ def leg_attention(tp, reps):
     return out
 
 
+def leg_library(reps):
+    """Library kernels on the shapes measured above, as context for their rates
+    (the libraries run as shipped; nothing of this package is involved):
+    - hipBLASLt through torch.bmm on the six products of the 8.3B-shaped layer
+      (t = 8 shards; each product's operands stored contiguous in the order it
+      reads them, so no transposed view reaches the library; bf16 outputs,
+      where the GEMM core writes dA_i and dB_i in fp32);
+    - torch's scaled_dot_product_attention, restricted to its flash and
+      memory-efficient kernels (never its math path), at the 8.3B attention
+      shape: b = 8, 24 heads of 128, s = 1024, causal, bf16, [b, heads, s, dh];
+      FLOP counted as in the attention leg (executed causal work);
+    - torch's device copy of the sequence-parallel kernels' byte counts, each
+      after the same 512 MiB cache flush as the sp_region leg."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    bf = torch.bfloat16
+    out = {}
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(bf)
+
+    t, n, d, mi = 8, 8192, 3072, 1536
+    prods = (("Z=X.A_i", (t, n, d), (t, d, mi)), ("P=Y.B_i", (t, n, mi), (t, mi, d)),
+             ("E=G.B_i^T", (t, n, d), (t, d, mi)), ("dA_i=X^T.D_i", (t, d, n), (t, n, mi)),
+             ("dB_i=Y_i^T.G", (t, mi, n), (t, n, d)), ("dX_i=D_i.A_i^T", (t, n, mi), (t, mi, d)))
+    gem = {}
+    total_ms = 0.0
+    for name, sa, sb in prods:
+        a, b = rnd(sa, 1.0), rnd(sb, 0.02)
+        c = torch.empty((t, sa[1], sb[2]), dtype=bf, device=dev)
+        fn = lambda: torch.bmm(a, b, out=c)  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        ms = _time_events(fn, reps)
+        med = float(np.median(ms))
+        fl = 2.0 * t * sa[1] * sa[2] * sb[2]
+        gem[name] = {"tflops_median": round(fl / (med * 1e-3) / 1e12, 2), **_stats(ms)}
+        total_ms += med
+        del a, b, c
+    flops = 12.0 * n * d * mi * t
+    gem["six_products"] = {"median_ms_sum": round(total_ms, 4),
+                           "tflops": round(flops / (total_ms * 1e-3) / 1e12, 2),
+                           "pct_of_peak": round(100.0 * flops / (total_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    out["hipblaslt_bmm_gpt8p3b_t8"] = gem
+    torch.cuda.empty_cache()
+
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    b, heads, s, dh = 8, 24, 1024, 128
+    q, k, v = rnd((b, heads, s, dh), 1.0), rnd((b, heads, s, dh), 1.0), rnd((b, heads, s, dh), 1.0)
+    go = rnd((b, heads, s, dh), 0.01)
+    core_f_exec = 4.0 * b * s * s * heads * dh * (s + 1) / (2.0 * s)
+    att = {"shape": f"b={b}, heads={heads}, s={s}, dh={dh}, causal, bf16"}
+    for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([be]):
+                qq, kk, vv = (x.detach().requires_grad_() for x in (q, k, v))
+
+                def fwd():
+                    return torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True)
+                o = fwd()
+
+                def bwd():
+                    torch.autograd.grad(o, (qq, kk, vv), go, retain_graph=True)
+                bwd()
+                torch.cuda.synchronize()
+                rf, rb = _time_events(fwd, reps), _time_events(bwd, reps)
+            rec = {}
+            for nm, ms, fl in (("fwd", rf, core_f_exec), ("bwd", rb, 2 * core_f_exec)):
+                med = float(np.median(ms))
+                rec[nm] = {"tflops_executed": round(fl / (med * 1e-3) / 1e12, 2), **_stats(ms)}
+            att[be.name.lower()] = rec
+            del o
+        except RuntimeError as ex:  # the backend has no kernel for this GPU or shape
+            att[be.name.lower()] = {"unavailable": str(ex).splitlines()[0][:200]}
+    out["sdpa_attention_core"] = att
+    del q, k, v, go
+    torch.cuda.empty_cache()
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    E = 2 * 4096 * 4096  # one [4096, 4096] bf16 tensor
+    cp = {}
+    for name, nbytes in (("33.5MB", E), ("168MB", 5 * E), ("185MB", 11 * E // 2)):
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        ms = _time_events(lambda: dst.copy_(src), reps, before=lambda: flush.zero_())
+        med = float(np.median(ms))
+        cp[name] = {"traffic_bytes": 2 * nbytes, "gbs_median": round(2 * nbytes / (med * 1e-3) / 1e9, 1), **_stats(ms)}
+        del src, dst
+    del flush
+    out["device_copy_after_flush"] = cp
+    return out
+
+
 def leg_vocab(tp, reps):
     """The logit layer and vocabulary-parallel cross-entropy of the 8.3B-shaped
     model: n = 8192 tokens, h = 3072, V = 51200 in t = 8 shards of 6400, bf16,
@@ -924,9 +1024,9 @@ def main():
     rec["roofline_reduce"]["cache_flushed"] = {
         "gbs_median": round(red_bytes / (float(np.median(red_flushed)) * 1e-3) / 1e9, 1), **_stats(red_flushed)}
     legs = set() if args.no_extra else set(LEGS if args.legs is None else args.legs.split(","))
-    unknown = legs - set(LEGS)
+    unknown = legs - set(LEGS) - set(OPTIONAL_LEGS)
     if unknown:
-        print(f"unknown legs: {sorted(unknown)}; known: {LEGS}", file=sys.stderr)
+        print(f"unknown legs: {sorted(unknown)}; known: {LEGS + OPTIONAL_LEGS}", file=sys.stderr)
         sys.exit(2)
     if "biased_step" in legs:
         rec["biased_step"] = leg_biased(tp, X, A_s, B_s, G, (Z, Y, P, O, D, dA, dB, dXp, dX), 10, flops)
@@ -944,7 +1044,7 @@ def main():
                               **leg_mlp_shard(tp, 2048, 25600, 12800, 10, seed=2)}
     for name, fn in (("sp_region", lambda: leg_sp(tp, 10)), ("c5_block", lambda: leg_c5_block(tp, 10)),
                      ("attention", lambda: leg_attention(tp, 10)), ("vocab_ce", lambda: leg_vocab(tp, 10)),
-                     ("fp32_path", lambda: leg_fp32(tp, 5))):
+                     ("fp32_path", lambda: leg_fp32(tp, 5)), ("library_yardsticks", lambda: leg_library(10))):
         if name in legs:
             torch.cuda.empty_cache()
             rec[name] = fn()
