@@ -347,6 +347,48 @@ __device__ __forceinline__ void lgkm_wait(i32x4& x, i32x4& y) {
   else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y)::"memory");
 }
 
+// Writes a wave's 32×DH result block, held as 32-row MFMA accumulators (lane
+// L: row L%32, columns 32d + 8(v/4) + 4·(L/32) + v%4), times `scale`, as bf16
+// rows dst + r·ld for r < nrows.  Stored directly, each 8-B piece would make a
+// store touch 32 rows; instead the wave stages the block in its own LDS region
+// `reg` (32·DH·2 bytes) and writes whole rows, 16 B per lane.  Staging layout:
+// 8-B unit k of row r at unit k ^ g(r), g(r) = r (dh 128) or r / 2 (dh 64), so
+// the 32 lanes of each half-wave write 32 distinct bank pairs; a 16-B read of
+// units 2m, 2m+1 finds them in one aligned slot, swapped when g(r) is odd.
+template <int DH>
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[DH / 32], float scale, uint32_t reg,
+                                                  bf16* dst, int64_t ld, int nrows, int lane) {
+  constexpr int RB = DH * 2, GS = DH == 128 ? 0 : 1;
+  constexpr int CPR = DH / 8, RPI = 64 / CPR, NS = 32 / RPI;  // 16-B chunks per row, rows per store
+  const int r32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int d = 0; d < DH / 32; ++d)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = f2bf(acc[d][4 * q4 + e] * scale);
+      const uint32_t ad = reg + r32 * RB + (((2 * (4 * d + q4) + hi) ^ (r32 >> GS)) << 3);
+      asm volatile("ds_write_b64 %0, %1" ::"v"(ad), "v"(__builtin_bit_cast(i32x2, w)) : "memory");
+    }
+  lds_wait();
+  const int mc = lane % CPR;
+  i32x4 v[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int R = i * RPI + lane / CPR;
+    v[i] = lds_rd128<0>(reg + R * RB + (((2 * mc) ^ (R >> GS)) & ~1) * 8);
+  }
+  lds_wait();
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    asm volatile("" : "+v"(v[i]));
+    const int R = i * RPI + lane / CPR;
+    if ((R >> GS) & 1) v[i] = i32x4{v[i][2], v[i][3], v[i][0], v[i][1]};
+    if (R < nrows) *reinterpret_cast<i32x4*>(dst + R * ld + 8 * mc) = v[i];
+  }
+}
+
 template <int DH, bool CAUSAL, bool GMASK>
 __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = AKV * DH * 2, RB = DH * 2;
@@ -559,24 +601,19 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   }
   if (j < nkv) step(ic<0>{}, j);
 
-  // o = oacc / l; lane holds row qrow, dh = 32d + 8(v/4) + 4·hi + v%4
-  if (qrow < a.s) {
+  // o = oacc / l, staged through the stage the last tile did not use (free
+  // since that tile's barrier: every wave had finished the tile before it,
+  // and no DMA went into it after), one 32-row region per wave
+  {
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    bf16* op = static_cast<bf16*>(a.o) + static_cast<int64_t>(T) * a.s * a.b * a.nh * DH +
-               (static_cast<int64_t>(qrow) * a.b + bi) * a.nh * DH + h * DH;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = f2bf(oacc[d][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * d + 8 * q4 + 4 * hi) = w;
-      }
-    if (hi == 0) {
-      const float lse = l > 0.f ? m * a.scale + logf(l) : -INFINITY;
-      a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + qrow] = lse;
-    }
+    bf16* ob = static_cast<bf16*>(a.o) + static_cast<int64_t>(T) * a.s * a.b * a.nh * DH +
+               (static_cast<int64_t>(q0) * a.b + bi) * a.nh * DH + h * DH;
+    store_rows_staged<DH>(oacc, inv, lds_base + (nkv & 1) * 2 * TILE + wave * 32 * RB, ob,
+                          static_cast<int64_t>(a.b) * a.nh * DH, a.s - q0, lane);
+  }
+  if (qrow < a.s && hi == 0) {
+    const float lse = l > 0.f ? m * a.scale + logf(l) : -INFINITY;
+    a.lse[((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s + qrow] = lse;
   }
 }
 
@@ -863,19 +900,12 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     step(ic<1>{}, j + 1);
   }
   if (j < nkv) step(ic<0>{}, j);
-  if (valid) {
-    bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(qrow) * a.b + bi) * row_len +
-               h * 3 * DH;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = f2bf(dq[d][4 * q4 + e] * a.scale);
-        *reinterpret_cast<bf16x4*>(op + 32 * d + 8 * q4 + 4 * hi) = w;
-      }
-  }
+  // dq, staged through the stage the last block did not use (free since its
+  // barrier), one 32-row region per wave
+  bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(q0) * a.b + bi) * row_len +
+             h * 3 * DH;
+  store_rows_staged<DH>(dq, a.scale, lds_base + (nkv & 1) * 2 * TILE + wave * 32 * RB, op,
+                        static_cast<int64_t>(a.b) * row_len, a.s - q0, lane);
 }
 
 // dk, dv: a workgroup takes 128 key rows, a wave 32, with k and v fragments in
@@ -1121,23 +1151,14 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
     step(ic<1>{}, j + 1);
   }
   if (j < nq) step(ic<0>{}, j);
-  if (valid) {
-    bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(krow) * a.b + bi) * row_len +
-               h * 3 * DH + DH;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 wk, wv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = f2bf(dk[d][4 * q4 + e] * a.scale);
-          wv[e] = f2bf(dv[d][4 * q4 + e]);
-        }
-        *reinterpret_cast<bf16x4*>(op + 32 * d + 8 * q4 + 4 * hi) = wk;
-        *reinterpret_cast<bf16x4*>(op + DH + 32 * d + 8 * q4 + 4 * hi) = wv;
-      }
-  }
+  // dk then dv, each staged through the wave's region of the stage the last
+  // block did not use (free since its barrier; the statistics have their own
+  // array), the second after the first one's reads have completed
+  bf16* op = static_cast<bf16*>(a.dqkv) + T * n * row_len + (static_cast<int64_t>(k0) * a.b + bi) * row_len +
+             h * 3 * DH + DH;
+  const uint32_t reg = lds_base + ((nq - j0) & 1) * 2 * TILE + wave * 32 * RB;
+  store_rows_staged<DH>(dk, a.scale, reg, op, static_cast<int64_t>(a.b) * row_len, a.s - k0, lane);
+  store_rows_staged<DH>(dv, 1.0f, reg, op + DH, static_cast<int64_t>(a.b) * row_len, a.s - k0, lane);
 }
 
 // fp32 backward: dq per query row, dk and dv per key row, two lanes per row
