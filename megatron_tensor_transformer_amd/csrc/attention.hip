@@ -422,24 +422,39 @@ __global__ __launch_bounds__(ATHR, 2) void attn_fwd_kernel(AttnArgs a) {
   const int64_t kcol = static_cast<int64_t>(h) * 3 * DH + DH;
   const TilePlan<DH, NW> kp = tile_plan<DH, NW>(a.b, bi, row_len, kcol, wave, lane);
   const TilePlan<DH, NW> vp = tile_plan<DH, NW>(a.b, bi, row_len, kcol + DH, wave, lane);
-  // prologue: K and V of block 0 into stage 0
+  // prologue: K and V of block 0 into stage 0, and the workgroup's 128 query
+  // rows (two 64-row tiles, rows past s zero-filled) into stage 1, which is
+  // free until the first step's barrier: whole rows per DMA load, where each
+  // lane loading its own fragments would touch 32 rows per load
   issue_tile<DH, NW>(rsrc, lds, kp, 0, stride, a.s, wave);
   issue_tile<DH, NW>(rsrc, lds + TILE, vp, 0, stride, a.s, wave);
-
-  // this lane's q fragments: row qrow, dh = 16c + 8·hi + 0..7
-  bf16x8 qf[NC];
   {
-    const bf16* qp = qkv + (static_cast<int64_t>(qrow) * a.b + bi) * row_len + h * 3 * DH + 8 * hi;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (qrow < a.s) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
-      else qf[c] = bf16x8{};
-    }
+    const TilePlan<DH, NW> qp = tile_plan<DH, NW>(a.b, bi, row_len, static_cast<int64_t>(h) * 3 * DH, wave, lane);
+    issue_tile<DH, NW>(rsrc, lds + 2 * TILE, qp, 2 * qb, stride, a.s, wave);
+    issue_tile<DH, NW>(rsrc, lds + 3 * TILE, qp, 2 * qb + 1, stride, a.s, wave);
   }
   // row-fragment offsets (row r32, chunk 2c + hi) and transposed-read addresses
   uint32_t ko[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) ko[c] = lds_base + kv_slot<DH>(r32, 2 * c + hi);
+
+  // this lane's q fragments: row qrow, dh = 16c + 8·hi + 0..7 (the wave's 32
+  // rows are rows 32·(wave % 2) .. of query tile wave / 2)
+  bf16x8 qf[NC];
+  {
+    wait_vmcnt<0>();
+    lds_barrier();
+    const uint32_t qoff = 2 * TILE + (wave >> 1) * TILE + (wave & 1) * 32 * RB;
+    i32x4 qr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qr[c] = lds_rd128<0>(ko[c] + qoff);
+    lds_wait();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      asm volatile("" : "+v"(qr[c]));
+      qf[c] = __builtin_bit_cast(bf16x8, qr[c]);
+    }
+  }
   uint32_t va[2 * ND];
   tr_addrs<DH, ND>(lds_base, lane, va);
 
