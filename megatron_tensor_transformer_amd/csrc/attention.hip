@@ -934,6 +934,7 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   constexpr int NC = DH / 16, ND = DH / 32;
   constexpr int NI = TILE / 1024 / 4;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) char kvmem[4 * TILE];  // the workgroup's 128 K rows, then V rows
   __shared__ __attribute__((aligned(16))) float stat[2][2][AKV];  // [stage][lse·log2(e) | δ][row]
   TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
   int T, bi, h, kb_idx;
@@ -970,6 +971,15 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   load_stat(j0, sv);
   load_tile<DH>(rq, lds, a.s, a.b, bi, row_len, qcol, j0, wave, lane);
   load_tile<DH>(rd, lds + TILE, a.s, a.b, bi, orow, dcol, j0, wave, lane);
+  // the workgroup's 128 keys: their K and V rows (two 64-row tiles each, rows
+  // past s zero-filled) by DMA into their own region, whole rows per load;
+  // each lane loading its own fragments would touch 32 rows per load, and
+  // with one workgroup per CU nothing else runs while they arrive
+  TPMLP_LDS char* kvl = (TPMLP_LDS char*)(kvmem);
+  load_tile<DH>(rq, kvl, a.s, a.b, bi, row_len, qcol + DH, 2 * kb_idx, wave, lane);
+  load_tile<DH>(rq, kvl + TILE, a.s, a.b, bi, row_len, qcol + DH, 2 * kb_idx + 1, wave, lane);
+  load_tile<DH>(rq, kvl + 2 * TILE, a.s, a.b, bi, row_len, qcol + 2 * DH, 2 * kb_idx, wave, lane);
+  load_tile<DH>(rq, kvl + 3 * TILE, a.s, a.b, bi, row_len, qcol + 2 * DH, 2 * kb_idx + 1, wave, lane);
 
   // k and v fragments of the lane's key, kept in AGPRs (an MFMA operand may
   // come from either register file; the VGPRs go to the S and dP
@@ -980,15 +990,6 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   const i32x4 mrs = GMASK ? make_rsrc(a.mask + (static_cast<int64_t>(a.b) + bi) * a.s * a.mw,
                                         static_cast<uint32_t>(static_cast<int64_t>(a.s) * a.mw * 4))
                              : i32x4{0, 0, 0, 0};
-  {
-    const bf16* kp = qkv + (static_cast<int64_t>(krow) * a.b + bi) * row_len + h * 3 * DH + DH + 8 * hi;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kf[c] = valid ? *reinterpret_cast<const i32x4*>(kp + 16 * c) : i32x4{0, 0, 0, 0};
-      vf[c] = valid ? *reinterpret_cast<const i32x4*>(kp + DH + 16 * c) : i32x4{0, 0, 0, 0};
-      asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
-    }
-  }
   f32x16 dk[ND], dv[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d)
@@ -1005,6 +1006,26 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   for (int c = 0; c < NC; ++c) ro[c] = lds_base + kv_slot<DH>(r32, 2 * c + hi);
   uint32_t va[NR];
   tr_addrs<DH, ND>(lds_base, lane, va);
+  {
+    // the wave's 32 keys are rows 32·(wave % 2) .. of K (V) tile wave / 2
+    lds_barrier();  // every wave's share of the K and V rows has landed
+    const uint32_t kvb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kvl)) + (wave >> 1) * TILE +
+                         (wave & 1) * 32 * RB;
+    i32x4 kr[NC], vr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kr[c] = lds_rd128<0>(kvb + kv_slot<DH>(r32, 2 * c + hi));
+      vr[c] = lds_rd128<2 * TILE>(kvb + kv_slot<DH>(r32, 2 * c + hi));
+    }
+    lds_wait();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      asm volatile("" : "+v"(kr[c]), "+v"(vr[c]));
+      kf[c] = kr[c];
+      vf[c] = vr[c];
+      asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
+    }
+  }
   // this lane's statistics: 4 consecutive query rows per 16-B read
   const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&stat[0][0][0])) + 16 * hi;
 
