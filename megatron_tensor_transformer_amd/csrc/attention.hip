@@ -73,6 +73,8 @@ __device__ __forceinline__ uint32_t kv_slot(int row, int chunk) {
 // word per 32-wide half tile through a buffer resource.
 __device__ uint32_t tpmlp_llvm_buffer_load_u32(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
     "llvm.amdgcn.raw.buffer.load.i32");
+__device__ i32x4 tpmlp_llvm_buffer_load_v4(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.v4i32");
 
 // The 16 bits of a 32-position mask word that belong to this lane's
 // accumulator entries: entry v = 4g + e is position 8g + 4·hi + e.
@@ -771,7 +773,63 @@ __global__ __launch_bounds__(ATHR, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   const bool valid = qrow < a.s;
   const int64_t srow = ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
   float dlt = 0.f;
-  {
+  if constexpr (!GMASK) {
+    // The wave's 32 rows of q, dO and o, loaded as whole rows (16-B chunk
+    // lane % CPR of row lane / CPR + RPI·i; rows past s read as zeros) and
+    // passed through the wave's region of stage 1 (free until the first
+    // step's barrier) into the fragment layout: lane (r32, hi) needs chunks
+    // 2c + hi of row r32.  Each lane loading its own chunks would make every
+    // load touch 32 rows.
+    constexpr int RB = DH * 2, CPR = DH / 8, RPI = 64 / CPR, NS = 32 / RPI;
+    const int rr = lane / CPR, ch = lane % CPR;
+    const i32x4 rdo = make_rsrc(static_cast<const bf16*>(a.dout) + T * n * orow, a.o_shard_bytes);
+    const i32x4 ro = make_rsrc(static_cast<const bf16*>(a.o) + T * n * orow, a.o_shard_bytes);
+    i32x4 lq[NS], ld[NS], lo[NS];
+    auto ooff = [&](int i) {
+      const int R = q0 + rr + RPI * i;
+      return R < a.s ? static_cast<int>(((static_cast<int64_t>(R) * a.b + bi) * orow + h * DH + 8 * ch) * 2)
+                     : static_cast<int>(AOOB);
+    };
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int R = q0 + rr + RPI * i;
+      const int64_t tok = static_cast<int64_t>(R) * a.b + bi;
+      lq[i] = tpmlp_llvm_buffer_load_v4(
+          rsrc, R < a.s ? static_cast<int>((tok * row_len + h * 3 * DH + 8 * ch) * 2) : static_cast<int>(AOOB), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) ld[i] = tpmlp_llvm_buffer_load_v4(rdo, ooff(i), 0, 0);
+    const uint32_t reg = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + 2 * TILE + wave * 32 * RB;
+    auto to_frags = [&](const i32x4(&x)[NS], bf16x8(&out)[NC]) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        asm volatile("ds_write_b128 %0, %1" ::"v"(reg + kv_slot<DH>(rr + RPI * i, ch)), "v"(x[i]) : "memory");
+      lds_wait();
+      i32x4 f[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) f[c] = lds_rd128<0>(reg + kv_slot<DH>(r32, 2 * c + hi));
+      lds_wait();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        asm volatile("" : "+v"(f[c]));
+        out[c] = __builtin_bit_cast(bf16x8, f[c]);
+      }
+    };
+    // o (needed only for δ) is loaded once q is staged, so that at most two
+    // of the three row sets are live at a time
+    bf16x8 of[NC];
+    to_frags(lq, qf);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) lo[i] = tpmlp_llvm_buffer_load_v4(ro, ooff(i), 0, 0);
+    to_frags(ld, df);
+    to_frags(lo, of);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = fmaf(bf2f(df[c][e]), bf2f(of[c][e]), dlt);
+  } else {
+    // (the general-mask kernel keeps per-lane fragment loads: the staged
+    // form's registers made it spill)
     const int64_t tok = static_cast<int64_t>(qrow) * a.b + bi;
     const bf16* qp = qkv + tok * row_len + h * 3 * DH + 8 * hi;
     const int64_t oo = T * n * orow + tok * orow + h * DH + 8 * hi;
