@@ -111,14 +111,14 @@ struct AttnArgs {
 // them; without the causal mask they are alike and go head by head (a head's
 // blocks run together and share its panel while it is in the L2).
 template <bool CAUSAL>
-__device__ __forceinline__ void attn_block(int nh, int b, int nblk, int& T, int& bi, int& h, int& p) {
+__device__ __forceinline__ void attn_block_at(int nh, int b, int nblk, int G, int wg, int& T, int& bi, int& h, int& p) {
   int flat;
   if constexpr (CAUSAL) {
-    heavy_first_block(static_cast<int>(gridDim.x) / nblk, nblk, static_cast<int>(blockIdx.x), flat, p);
+    heavy_first_block(G / nblk, nblk, wg, flat, p);
   } else {
     int begin, count;
-    xcd_range(static_cast<int>(gridDim.x), static_cast<int>(blockIdx.x & 7), begin, count);
-    const int x = begin + static_cast<int>(blockIdx.x >> 3);
+    xcd_range(G, wg & 7, begin, count);
+    const int x = begin + (wg >> 3);
     flat = x / nblk;
     p = x - flat * nblk;
   }
@@ -126,6 +126,10 @@ __device__ __forceinline__ void attn_block(int nh, int b, int nblk, int& T, int&
   flat /= nh;
   bi = flat % b;
   T = flat / b;
+}
+template <bool CAUSAL>
+__device__ __forceinline__ void attn_block(int nh, int b, int nblk, int& T, int& bi, int& h, int& p) {
+  attn_block_at<CAUSAL>(nh, b, nblk, static_cast<int>(gridDim.x), static_cast<int>(blockIdx.x), T, bi, h, p);
 }
 
 // Forward: the longest causal query blocks are the last in the sequence.
@@ -1255,6 +1259,327 @@ __global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   store_rows_staged<DH>(dv, 1.0f, reg, op + DH, static_cast<int64_t>(a.b) * row_len, a.s - k0, lane);
 }
 
+
+__device__ void tpmlp_llvm_buffer_store_v4(i32x4 vdata, i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.store.v4i32");
+
+// store_rows_staged with buffer stores: exactly 32·DH/512 store instructions
+// per call whatever nrows is (rows past it go past the buffer's range)
+template <int DH>
+__device__ __forceinline__ void store_rows_staged_buf(const f32x16 (&acc)[DH / 32], float scale, uint32_t reg,
+                                                      i32x4 rs, int64_t off0, int64_t ldb, int nrows, int lane) {
+  constexpr int RB = DH * 2, GS = DH == 128 ? 0 : 1;
+  constexpr int CPR = DH / 8, RPI = 64 / CPR, NS = 32 / RPI;
+  const int r32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int d = 0; d < DH / 32; ++d)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = f2bf(acc[d][4 * q4 + e] * scale);
+      const uint32_t ad = reg + r32 * RB + (((2 * (4 * d + q4) + hi) ^ (r32 >> GS)) << 3);
+      asm volatile("ds_write_b64 %0, %1" ::"v"(ad), "v"(__builtin_bit_cast(i32x2, w)) : "memory");
+    }
+  lds_wait();
+  const int mc = lane % CPR;
+  i32x4 v[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int R = i * RPI + lane / CPR;
+    v[i] = lds_rd128<0>(reg + R * RB + (((2 * mc) ^ (R >> GS)) & ~1) * 8);
+  }
+  lds_wait();
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    asm volatile("" : "+v"(v[i]));
+    const int R = i * RPI + lane / CPR;
+    if ((R >> GS) & 1) v[i] = i32x4{v[i][2], v[i][3], v[i][0], v[i][1]};
+    tpmlp_llvm_buffer_store_v4(v[i], rs, R < nrows ? static_cast<int>(off0 + R * ldb + 16 * mc) : static_cast<int>(AOOB),
+                               0, 0);
+  }
+}
+
+// dk/dv, persistent: gridDim.x = 8·W workgroups, workgroup (x = wg % 8,
+// l = wg / 8) takes the key blocks of XCD x at local positions l, 2W-1-l,
+// 2W+l, ... of the longest-first list (G blocks in all).  While a block runs,
+// the next block's K and V rows (from its first step) and its first query
+// tile and statistics (in its last step) are loaded, so the next block starts
+// without waiting for memory, and this block's stores stay in flight while it
+// starts: its first wait lets exactly the 2·NS stores be outstanding (loads
+// and stores leave the vector-memory counter in issue order).
+constexpr unsigned kDkdvPersistWG = 256;  // one workgroup per CU (8 XCDs × 32)
+
+template <int DH, bool CAUSAL>
+__global__ __launch_bounds__(ATHR, DH == 128 ? 1 : 2) void attn_bwd_dkdv_pkernel(AttnBwdArgs a, int G) {
+  static_assert(DH == 128, "the persistent dk/dv kernel is built for dh 128 (one workgroup per CU)");
+  constexpr int TILE = AKV * DH * 2;
+  constexpr int NC = DH / 16, ND = DH / 32;
+  constexpr int RB = DH * 2, NR = 2 * ND;
+  constexpr int NS = 32 / (64 / (DH / 8));
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) char kvmem[4 * TILE];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][AKV];
+  TPMLP_LDS char* lds = (TPMLP_LDS char*)(smem);
+  TPMLP_LDS char* kvl = (TPMLP_LDS char*)(kvmem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int64_t row_len = static_cast<int64_t>(a.nh) * 3 * DH, orow = static_cast<int64_t>(a.nh) * DH;
+  const int64_t n = static_cast<int64_t>(a.s) * a.b;
+  const int nq = (a.s + AKV - 1) / AKV;
+  const int W = static_cast<int>(gridDim.x) >> 3;
+  const int xcd = static_cast<int>(blockIdx.x) & 7, l = static_cast<int>(blockIdx.x) >> 3;
+  auto vblock = [&](int r) {
+    const int loc = (r & 1) ? (r + 1) * W - 1 - l : r * W + l;
+    return loc * 8 + xcd;
+  };
+  // a block: shard, batch entry, head, key block (everything else follows)
+  struct Blk {
+    int T, bi, h, kb;
+    __device__ int j0() const { return CAUSAL ? (kb * AQ) / AKV : 0; }
+    __device__ int64_t srow(const AttnBwdArgs& a) const {
+      return ((static_cast<int64_t>(T) * a.b + bi) * a.nh + h) * a.s;
+    }
+  };
+  auto make_blk = [&](int vb) {
+    Blk B;
+    attn_block_at<CAUSAL>(a.nh, a.b, a.nqb, G, vb, B.T, B.bi, B.h, B.kb);
+    return B;
+  };
+  auto rs_qkv = [&](const Blk& B) {
+    return make_rsrc(static_cast<const bf16*>(a.qkv) + B.T * n * row_len, a.qkv_shard_bytes);
+  };
+  auto rs_dout = [&](const Blk& B) {
+    return make_rsrc(static_cast<const bf16*>(a.dout) + B.T * n * orow, a.o_shard_bytes);
+  };
+  auto load_stat = [&](const Blk& B, int j, float& v) {
+    const int t = threadIdx.x & 63, qr = j * AKV + t;
+    const int64_t sr = B.srow(a);
+    if (threadIdx.x < 64) {
+      const float lv = qr < a.s ? a.lse[sr + qr] : 0.f;
+      v = lv == -INFINITY ? INFINITY : lv * 1.4426950408889634f;
+    } else if (threadIdx.x < 128) v = qr < a.s ? a.delta[sr + qr] : 0.f;
+  };
+  auto store_stat = [&](int st, float v) {
+    if (threadIdx.x < 128) stat[st][threadIdx.x >> 6][threadIdx.x & 63] = v;
+  };
+  auto load_kv = [&](const Blk& B) {
+    const i32x4 rq = rs_qkv(B);
+    const int64_t kc = static_cast<int64_t>(B.h) * 3 * DH + DH;
+    load_tile<DH>(rq, kvl, a.s, a.b, B.bi, row_len, kc, 2 * B.kb, wave, lane);
+    load_tile<DH>(rq, kvl + TILE, a.s, a.b, B.bi, row_len, kc, 2 * B.kb + 1, wave, lane);
+    load_tile<DH>(rq, kvl + 2 * TILE, a.s, a.b, B.bi, row_len, kc + DH, 2 * B.kb, wave, lane);
+    load_tile<DH>(rq, kvl + 3 * TILE, a.s, a.b, B.bi, row_len, kc + DH, 2 * B.kb + 1, wave, lane);
+  };
+  auto load_q = [&](const Blk& B, int j, TPMLP_LDS char* dst) {
+    load_tile<DH>(rs_qkv(B), dst, a.s, a.b, B.bi, row_len, static_cast<int64_t>(B.h) * 3 * DH, j, wave, lane);
+    load_tile<DH>(rs_dout(B), dst + TILE, a.s, a.b, B.bi, orow, static_cast<int64_t>(B.h) * DH, j, wave, lane);
+  };
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  uint32_t ro[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ro[c] = lds_base + kv_slot<DH>(r32, 2 * c + hi);
+  uint32_t va[NR];
+  tr_addrs<DH, ND>(lds_base, lane, va);
+  const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&stat[0][0][0])) + 16 * hi;
+  const uint32_t kvb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kvl)) + (wave >> 1) * TILE +
+                       (wave & 1) * 32 * RB;
+
+  Blk cur = make_blk(vblock(0));
+  bool has_next = vblock(1) < G;
+  Blk nxt = has_next ? make_blk(vblock(1)) : cur;
+  float sv = 0.f;
+  load_stat(cur, cur.j0(), sv);
+  load_q(cur, cur.j0(), lds);
+  load_kv(cur);
+  wait_vmcnt<0>();
+  store_stat(0, sv);
+  int st0 = 0;
+  i32x4 kf[NC], vf[NC];
+  f32x16 dk[ND], dv[ND];
+  for (int r = 0;; ++r) {
+    // this block's k and v fragments from the K/V rows in kvmem
+    lds_barrier();
+    {
+      i32x4 kr[NC], vr[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kr[c] = lds_rd128<0>(kvb + kv_slot<DH>(r32, 2 * c + hi));
+        vr[c] = lds_rd128<2 * TILE>(kvb + kv_slot<DH>(r32, 2 * c + hi));
+      }
+      lds_wait();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        asm volatile("" : "+v"(kr[c]), "+v"(vr[c]));
+        kf[c] = kr[c];
+        vf[c] = vr[c];
+        asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dk[d][v] = dv[d][v] = 0.f;
+    const int k0 = cur.kb * AQ + wave * 32, krow = k0 + r32, j0 = cur.j0();
+    const bool valid = krow < a.s;
+
+    auto step = [&](auto stc, int j, bool cont) {
+      constexpr int ST = decltype(stc)::value;
+      if (!cont) wait_vmcnt<0>();  // this wave's share of block j and its statistic
+      lds_wait();
+      lds_barrier();
+      const int t0 = j * AKV;
+      const bool masked = t0 + AKV > a.s || k0 + 31 >= a.s || (CAUSAL && t0 < k0 + 31);
+      const bool dead = k0 >= a.s || (CAUSAL && t0 + AKV - 1 < k0);
+      if (j + 1 < nq) {
+        load_stat(cur, j + 1, sv);
+        load_q(cur, j + 1, lds + (ST ^ 1) * 2 * TILE);
+      } else if (has_next) {
+        load_stat(nxt, nxt.j0(), sv);
+        load_q(nxt, nxt.j0(), lds + (ST ^ 1) * 2 * TILE);
+      }
+      // kvmem is free once every wave has its fragments (before this barrier)
+      if (j == j0 && has_next) load_kv(nxt);
+    if (!dead) static_for<0, 2>([&](auto uc) {
+      constexpr int U = decltype(uc)::value;
+      constexpr int QB = ST * 2 * TILE + U * 32 * RB, DB = QB + TILE;  // rows 32U.. of Q and dO
+      // statistics of the lane's 16 query rows (lse·log2(e), δ), read ahead
+      f32x4 ls[4], ds[4];
+      i32x4 sr[8];
+      static_for<0, 4>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        sr[g] = lds_rd128<((2 * ST + 0) * AKV + 32 * U + 8 * g) * 4>(sbase);
+        sr[4 + g] = lds_rd128<((2 * ST + 1) * AKV + 32 * U + 8 * g) * 4>(sbase);
+      });
+      // S = Q·Kᵀ and dP = dO·Vᵀ for the lane's key: slices read three ahead.
+      // The products are inline asm with VGPR accumulators (the compiler's
+      // form for this one-wave-per-SIMD kernel keeps them in AGPRs, and every
+      // VALU use below would first copy them out); the first slice starts
+      // from zero.
+      f32x16 sacc, pacc;
+      i32x4 qr[4], dr[4];
+      auto rd2 = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        qr[c % 4] = lds_rd128<QB>(ro[c]);
+        dr[c % 4] = lds_rd128<DB>(ro[c]);
+      };
+      static_for<0, (NC < 3 ? NC : 3)>(rd2);
+      static_for<0, NC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        constexpr int later = 2 * (NC - 1 - c < 2 ? NC - 1 - c : 2);
+        lgkm_wait<later>(qr[c % 4], dr[c % 4]);
+        if constexpr (c == 0) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(qr[0]), "a"(kf[0]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(pacc) : "v"(dr[0]), "a"(vf[0]));
+        } else {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qr[c % 4]), "a"(kf[c]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pacc) : "v"(dr[c % 4]), "a"(vf[c]));
+        }
+        if constexpr (c + 3 < NC) rd2(ic<c + 3>{});
+      });
+      // the VALU reads the results only after the MFMA pipeline has written
+      // them (the wait states the compiler inserts for its own MFMAs)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(sacc), "+v"(pacc));
+      // every LDS read above is complete (the last wait was for zero)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        asm volatile("" : "+v"(sr[g]), "+v"(sr[4 + g]));
+        ls[g] = __builtin_bit_cast(f32x4, sr[g]);
+        ds[g] = __builtin_bit_cast(f32x4, sr[4 + g]);
+      }
+      // the first two transposed blocks are read while P and dS are formed
+      i32x2 ta[NR], tb[NR];
+      tr_issue<DH, ND, DB>(va, ta);
+      tr_issue<DH, ND, QB>(va, tb);
+      // lane: key krow, query rows 64j + 32U + 8(v/4) + 4·hi + v%4; the
+      // mask runs only on tiles that reach past s, past this wave's keys'
+      // diagonal, or hold key rows past s
+      if (masked) {
+        const int lo = CAUSAL ? krow - t0 - 4 * hi : -1 << 30;
+        const int hi_ = valid ? a.s - t0 - 4 * hi : lo;
+        mask_range1(sacc, U, lo, hi_, -INFINITY);
+      }
+      f32x16 pv;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g + e;
+          pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[v], a.scale_log2, -ls[g][e]));
+          sacc[v] = pv[v] * (pacc[v] - ds[g][e]);  // dS
+        }
+      // dv += Pᵀ·dO and dk += dSᵀ·Q over the block's 32 query rows, 16 at a
+      // time; block g + 1's reads are in flight during block g's MFMAs
+      bf16x8 ft[ND];
+      tr_wait<NR, ND>(ta);
+      tr_frags<ND>(ta, ft);
+      {
+        const bf16x8 pf = pack_acc(pv, 0);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dv[d] = mfma(ft[d], pf, dv[d]);
+      }
+      tr_issue<DH, ND, DB + 16 * RB>(va, ta);
+      tr_wait<NR, ND>(tb);
+      tr_frags<ND>(tb, ft);
+      {
+        const bf16x8 sf = pack_acc(sacc, 0);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dk[d] = mfma(ft[d], sf, dk[d]);
+      }
+      tr_issue<DH, ND, QB + 16 * RB>(va, tb);
+      tr_wait<NR, ND>(ta);
+      tr_frags<ND>(ta, ft);
+      {
+        const bf16x8 pf = pack_acc(pv, 1);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dv[d] = mfma(ft[d], pf, dv[d]);
+      }
+      tr_wait<0, ND>(tb);
+      tr_frags<ND>(tb, ft);
+      {
+        const bf16x8 sf = pack_acc(sacc, 1);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dk[d] = mfma(ft[d], sf, dk[d]);
+      }
+    });
+      if (j + 1 < nq || has_next) store_stat(ST ^ 1, sv);
+    };
+    int j = j0;
+    bool cont = r > 0;
+    if (st0 == 0) {
+      for (; j + 1 < nq; j += 2) {
+        step(ic<0>{}, j, cont);
+        cont = false;
+        step(ic<1>{}, j + 1, false);
+      }
+      if (j < nq) step(ic<0>{}, j, cont);
+    } else {
+      for (; j + 1 < nq; j += 2) {
+        step(ic<1>{}, j, cont);
+        cont = false;
+        step(ic<0>{}, j + 1, false);
+      }
+      if (j < nq) step(ic<1>{}, j, cont);
+    }
+    const int stl = (st0 + (nq - j0) - 1) & 1;  // the last step's stage
+    lds_barrier();                                // every wave is done reading it
+    const uint32_t reg = lds_base + stl * 2 * TILE + wave * 32 * RB;
+    const i32x4 rw = make_rsrc(static_cast<bf16*>(a.dqkv) + cur.T * n * row_len, a.qkv_shard_bytes);
+    const int64_t off0 = ((static_cast<int64_t>(k0) * a.b + cur.bi) * row_len + cur.h * 3 * DH + DH) * 2;
+    store_rows_staged_buf<DH>(dk, a.scale, reg, rw, off0, static_cast<int64_t>(a.b) * row_len * 2, a.s - k0, lane);
+    store_rows_staged_buf<DH>(dv, 1.0f, reg, rw, off0 + DH * 2, static_cast<int64_t>(a.b) * row_len * 2, a.s - k0,
+                              lane);
+    if (!has_next) break;
+    // the next block's K/V rows, first query tile and statistics were issued
+    // before the 2·NS stores above
+    wait_vmcnt<2 * NS>();
+    cur = nxt;
+    st0 = stl ^ 1;
+    has_next = vblock(r + 2) < G;
+    if (has_next) nxt = make_blk(vblock(r + 2));
+  }
+}
+
 // fp32 backward: dq per query row, dk and dv per key row, two lanes per row
 // as in the forward (lane half j holds columns j·dh/2 ..).
 template <int DH, bool CAUSAL>
@@ -1373,7 +1698,14 @@ hipError_t launch_bwd_t(const AttnBwdArgs& a, int dt, hipStream_t stream) {
       hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, CAUSAL, false>), dim3(blocks), dim3(ATHR), 0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL, false>), dim3(blocks), dim3(ATHR), 0, stream, a);
+      // dh 128 (one workgroup per CU): the persistent kernel, one workgroup
+      // per CU walking at least two key blocks; the block count is a multiple
+      // of the 8 XCDs so that each XCD's share is its own list
+      if (DH == 128 && blocks % 8 == 0 && blocks >= 2u * kDkdvPersistWG)
+        hipLaunchKernelGGL((attn_bwd_dkdv_pkernel<128, CAUSAL>), dim3(kDkdvPersistWG), dim3(ATHR), 0, stream, a,
+                           static_cast<int>(blocks));
+      else
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, CAUSAL, false>), dim3(blocks), dim3(ATHR), 0, stream, a);
     }
   } else {
     const unsigned dblocks = static_cast<unsigned>((rows + 255) / 256);

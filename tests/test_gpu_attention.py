@@ -162,6 +162,28 @@ def test_core_rows_with_no_visible_key():
     assert np.all(np.isfinite(f64(dqkv)))
 
 
+@pytest.mark.parametrize("T,s,b,nh", [
+    (1, 256, 16, 16),   # 512 key blocks of 128 on 256 CUs: the persistent dk/dv kernel, two per workgroup
+    (2, 200, 8, 16),    # two shards, ragged: each sequence's last key block holds 72 keys
+    (1, 384, 16, 11),   # 528 blocks: some workgroups walk three
+])
+@pytest.mark.parametrize("causal", [True, False])
+def test_core_bf16_persistent_dkdv(T, s, b, nh, causal):
+    """dh 128 launches with at least 512 key blocks (a multiple of the 8 XCDs)
+    run dk/dv persistently: each workgroup walks several key blocks and loads
+    the next block's rows while the current one runs."""
+    compare_core(T, s, b, nh, 128, causal, "bf16", seed=11)
+
+
+def test_core_persistent_dkdv_deterministic_bitwise():
+    inp = qkv_inputs(1, 384, 16, 11, 128, dtype="bf16", seed=12)
+    r1 = run_core(inp, 1, 384, 16, 11, 128, True)
+    r2 = run_core(inp, 1, 384, 16, 11, 128, True)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
 def test_core_deterministic_bitwise():
     inp = qkv_inputs(2, 200, 2, 2, 128, dtype="bf16", seed=4)
     r1 = run_core(inp, 2, 200, 2, 2, 128, True)
