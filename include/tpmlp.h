@@ -416,6 +416,9 @@ int tpmlp_ln_sp(hipStream_t stream, const tpmlp_sp_args* a);
  *   16-byte aligned bases.
  * Workspace of the backward: tpmlp_attn_bwd_workspace_bytes(...) bytes (the
  * δ rows), 4-byte aligned.
+ * No atomics: every output is summed in a fixed order that depends only on
+ * the sizes (which kernels run, and how work is dealt to workgroups, too), so
+ * results are bit-reproducible.
  *
  * tpmlp_attn_core_fwd / _bwd run the attention core alone on a given QKV
  * (and O, lse, dO): QKV -> O, lse and (QKV, O, lse, dO) -> dQKV.
