@@ -147,9 +147,13 @@ def _graph_check(step, sets, order=(1, 2, 0, 1)):
             assert torch.equal(v, ref[k][name]), f"replay {rep} (input set {k}): {name} differs"
 
 
-@pytest.mark.parametrize("masked", [False, True])
-def test_attention_layer_graph(masked):
-    s, b, d, heads, t = 130, 2, 256, 2, 2
+@pytest.mark.parametrize("masked,shape", [
+    (False, (130, 2, 256, 2, 2)), (True, (130, 2, 256, 2, 2)),
+    # 512 key blocks of 128 with dh 128: the persistent dk/dv kernel is captured
+    (False, (256, 16, 2048, 16, 1)),
+])
+def test_attention_layer_graph(masked, shape):
+    s, b, d, heads, t = shape
     dh = d // heads
     say(f"[gpu] graph capture attention s={s} b={b} d={d} heads={heads} t={t} masked={masked}")
     sets = []
