@@ -150,6 +150,8 @@ __device__ __forceinline__ void load_tile(i32x4 rsrc, TPMLP_LDS char* tile, int 
   constexpr int NI = AKV * DH * 2 / 1024 / 4;   // 1-KiB DMA loads per wave
   constexpr int RPI = 1024 / (DH * 2);          // rows per load
   constexpr int CPR = DH / 8;                   // chunks per row
+  // the LDS destination (M0) from a scalar copy of the uniform wave index
+  const int ws = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
   for (int q = 0; q < NI; ++q) {
     const int I = wave * NI + q;
@@ -162,7 +164,7 @@ __device__ __forceinline__ void load_tile(i32x4 rsrc, TPMLP_LDS char* tile, int 
     const int r = j * AKV + row;
     const uint32_t voff =
         r < s ? static_cast<uint32_t>(((static_cast<int64_t>(r) * b + bi) * row_len + col + chunk * 8) * 2) : AOOB;
-    buffer_load_lds16(rsrc, tile + I * 1024, voff);
+    buffer_load_lds16(rsrc, tile + (ws * NI + q) * 1024, voff);
   }
 }
 
@@ -251,15 +253,16 @@ template <int DH, int NW = 4>
 __device__ __forceinline__ void issue_tile(i32x4 rsrc, TPMLP_LDS char* tile, const TilePlan<DH, NW>& p, int j,
                                            uint32_t stride, int s, int wave) {
   const uint32_t jo = static_cast<uint32_t>(j) * stride;
+  const int ws = __builtin_amdgcn_readfirstlane(wave);  // scalar LDS destinations (M0)
   if (j * AKV + AKV <= s) {  // the whole block is in range: no per-row check
 #pragma unroll
     for (int q = 0; q < TilePlan<DH, NW>::NI; ++q)
-      buffer_load_lds16(rsrc, tile + (wave * TilePlan<DH, NW>::NI + q) * 1024, p.voff[q] + jo);
+      buffer_load_lds16(rsrc, tile + (ws * TilePlan<DH, NW>::NI + q) * 1024, p.voff[q] + jo);
   } else {
 #pragma unroll
     for (int q = 0; q < TilePlan<DH, NW>::NI; ++q) {
       const uint32_t voff = j * AKV + p.row[q] < s ? p.voff[q] + jo : AOOB;
-      buffer_load_lds16(rsrc, tile + (wave * TilePlan<DH, NW>::NI + q) * 1024, voff);
+      buffer_load_lds16(rsrc, tile + (ws * TilePlan<DH, NW>::NI + q) * 1024, voff);
     }
   }
 }
