@@ -178,8 +178,10 @@ __device__ __forceinline__ void dma(i32x4 rsrc, TPMLP_LDS char* tile, const Load
   else
     ok = ((p.kseg + J * 16) & 63) + p.kq < krem;
   const uint32_t voff = ok ? p.base[J] + koff : OOB;
-  // both layouts: load (NL·wave + J) fills the tile's 1-KiB segment of that index
-  buffer_load_lds16(rsrc, tile + (wave * NL + J) * 1024, voff);
+  // both layouts: load (NL·wave + J) fills the tile's 1-KiB segment of that
+  // index; the LDS destination (M0) from a scalar copy of the uniform wave index
+  const int ws = __builtin_amdgcn_readfirstlane(wave);
+  buffer_load_lds16(rsrc, tile + (ws * NL + J) * 1024, voff);
 }
 
 template <int ORDER, int NL = NLOAD, int J = 0>
